@@ -1,0 +1,147 @@
+"""fp64 CPU oracle for the mLSTM recurrence and RetNet retention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, the package smoke check in
+``__graft_entry__.py`` and the CPU-baseline leg of ``bench.py`` may import
+this module.  The GPU library (``linear_recurrent_sequence_mlstm_amd``) never
+imports it and shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, one sequential loop over
+time per (batch, head), OpenMP across the independent (batch, head) pairs).
+This wrapper only converts inputs to contiguous float64 arrays, allocates the
+outputs and calls the C entry points through ctypes.  Inputs given as torch
+tensors (bf16 or fp32) are upcast exactly, so the oracle sees the very values
+the GPU receives.
+
+Parity status of each function (what pins it is listed in the tests):
+  mlstm_fwd        pinned (brute-force quadratic form, unstabilised direct
+                   recurrence, stabiliser-shift invariance, linear-attention
+                   special case, T=1 closed form, state carry)
+  mlstm_step       pinned (equals mlstm_fwd one token at a time, T=1 form)
+  retention_fwd    pinned (decay-matrix closed form of the RetNet page)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False, out: str | None = None, extra_flags=()) -> str:
+    """Compile oracle.c with gcc into a shared library; returns its path."""
+    out = out or _LIB
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(_SRC):
+        return out
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-Wall",
+           *extra_flags, _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _load(path: str | None = None):
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    lib = ctypes.CDLL(path or build())
+    P = ctypes.POINTER(ctypes.c_double)
+    i = ctypes.c_int
+    lib.oracle_mlstm_fwd.argtypes = [i, i, i, i, i, i, i] + [P] * 14
+    lib.oracle_mlstm_fwd.restype = i
+    lib.oracle_mlstm_step.argtypes = [i, i, i, i, i] + [P] * 11
+    lib.oracle_mlstm_step.restype = i
+    lib.oracle_retention_fwd.argtypes = [i, i, i, i, i] + [P] * 7
+    lib.oracle_retention_fwd.restype = i
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = i
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _f64(x):
+    """Contiguous float64 numpy copy of a numpy array or torch tensor (or None)."""
+    if x is None:
+        return None
+    if "torch" in sys.modules:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return np.ascontiguousarray(x.detach().to("cpu", torch.float64).numpy())
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def mlstm_fwd(q, k, v, i_pre, f_pre, o_pre=None, bias=None, C0=None, n0=None,
+              m0=None, num_blocks=1, normalise=True, m_shift=None, lib=None):
+    """Sequence form.  Shapes: q,k [B,H,T,dqk]; v [B,H,T,dv]; gates [B,H,T];
+    o_pre [B,H,T,dv] or None; bias [H] or None; C0 [B,H,nb,dqk/nb,dv/nb];
+    n0 [B,H,dqk]; m0 [B,H].  Returns (h, C, n, m) as float64 arrays."""
+    q, k, v, ip, fp = map(_f64, (q, k, v, i_pre, f_pre))
+    op, bs, c0, nn0, mm0, ms = map(_f64, (o_pre, bias, C0, n0, m0, m_shift))
+    B, H, T, dqk = q.shape
+    dv = v.shape[-1]
+    nb = int(num_blocks)
+    assert k.shape == q.shape and v.shape == (B, H, T, dv)
+    assert ip.shape == (B, H, T) and fp.shape == (B, H, T)
+    h = np.zeros((B, H, T, dv))
+    C = np.zeros((B, H, nb, dqk // nb, dv // nb))
+    n = np.zeros((B, H, dqk))
+    m = np.zeros((B, H))
+    rc = (lib or _load()).oracle_mlstm_fwd(
+        B, H, T, dqk, dv, nb, 1 if normalise else 0, _ptr(q), _ptr(k), _ptr(v),
+        _ptr(ip), _ptr(fp), _ptr(op), _ptr(bs), _ptr(c0), _ptr(nn0), _ptr(mm0),
+        _ptr(ms), _ptr(h), _ptr(C), _ptr(n), _ptr(m))
+    if rc != 0:
+        raise ValueError("oracle_mlstm_fwd failed with %d" % rc)
+    return h, C, n, m
+
+
+def mlstm_step(q, k, v, i_pre, f_pre, C, n, m, o_pre=None, bias=None,
+               num_blocks=1, lib=None):
+    """One decode step.  q,k [B,H,dqk]; v [B,H,dv]; gates [B,H]; C,n,m are
+    float64 arrays updated IN PLACE.  Returns h [B,H,dv] (float64)."""
+    q, k, v, ip, fp, op, bs = map(_f64, (q, k, v, i_pre, f_pre, o_pre, bias))
+    for a in (C, n, m):
+        assert isinstance(a, np.ndarray) and a.dtype == np.float64 and a.flags.c_contiguous
+    B, H, dqk = q.shape
+    dv = v.shape[-1]
+    h = np.zeros((B, H, dv))
+    rc = (lib or _load()).oracle_mlstm_step(
+        B, H, dqk, dv, int(num_blocks), _ptr(q), _ptr(k), _ptr(v), _ptr(ip),
+        _ptr(fp), _ptr(op), _ptr(bs), _ptr(C), _ptr(n), _ptr(m), _ptr(h))
+    if rc != 0:
+        raise ValueError("oracle_mlstm_step failed with %d" % rc)
+    return h
+
+
+def retention_fwd(q, k, v, gamma=None, S0=None, lib=None):
+    """Retention recurrence.  q,k [B,H,T,dk]; v [B,H,T,dv]; gamma [H] or None
+    (then 1 - 2^(-5-h)); S0 [B,H,dk,dv] or None.  Returns (out, S)."""
+    q, k, v, g, s0 = map(_f64, (q, k, v, gamma, S0))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    out = np.zeros((B, H, T, dv))
+    S = np.zeros((B, H, dk, dv))
+    rc = (lib or _load()).oracle_retention_fwd(
+        B, H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0),
+        _ptr(out), _ptr(S))
+    if rc != 0:
+        raise ValueError("oracle_retention_fwd failed with %d" % rc)
+    return out, S

@@ -1,0 +1,319 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Each test fixes part of the oracle with something independent of its code:
+  * brute-force quadratic (parallel) form, written from the unrolled
+    recurrence with its closed-form stabiliser          -> whole recurrence
+  * unstabilised direct recurrence in the natural C [d_v x d_qk] orientation
+    with exp/sigmoid gates, the block-diagonal memory as a mask on the full
+    matrix                                                -> stabiliser, layout
+  * invariance of h (and of the true state) to an arbitrary stabiliser shift
+  * f = 1, i = 1: causal linear attention by prefix sums
+  * T = 1 closed form
+  * split run with carried state == one run (checkpoint / resume)
+  * RetNet decay-matrix closed form ((Q K^T) * D) V  (RetNet page)
+  * gamma_h table of the RetNet page; xLSTM 7B state size of the xLSTM 7B page
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+RNG = np.random.default_rng
+
+
+def _inputs(rng, B, H, T, dqk, dv, *, f_mix=True, with_o=True, bias=True):
+    q = rng.standard_normal((B, H, T, dqk))
+    k = rng.standard_normal((B, H, T, dqk)) / np.sqrt(dqk)
+    v = rng.standard_normal((B, H, T, dv))
+    ip = rng.standard_normal((B, H, T))
+    if f_mix:
+        fp = np.where(rng.random((B, H, T)) < 0.7, rng.normal(3, 1, (B, H, T)),
+                      rng.normal(-2, 1, (B, H, T)))
+    else:
+        fp = rng.normal(3, 1, (B, H, T))
+    op = rng.standard_normal((B, H, T, dv)) if with_o else None
+    bs = rng.uniform(-0.5, 0.5, H) if bias else None
+    return q, k, v, ip, fp, op, bs
+
+
+def _state(rng, B, H, dqk, dv, nb):
+    C0 = rng.standard_normal((B, H, nb, dqk // nb, dv // nb)) * 0.3
+    n0 = rng.standard_normal((B, H, dqk)) * 0.3
+    m0 = rng.uniform(-2, 2, (B, H))
+    return C0, n0, m0
+
+
+def _relerr(a, b):
+    return np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300)
+
+
+# ---------------------------------------------------------------- brute force
+def brute_force(q, k, v, ip, fp, op, bs, nb, C0=None, n0=None, m0=None):
+    """Quadratic form of the recurrence for every (b, h).
+
+    With F_t = sum_{r<=t} log sigmoid(f_r), token s contributes to step t with
+    log-weight  F_t - F_s + i_s  and the initial state with  F_t + m_0.  The
+    stabiliser is the largest log-weight, M_t.  Returns h, the final
+    stabilised state (C, n) and M_T.
+    """
+    B, H, T, dqk = q.shape
+    dv = v.shape[-1]
+    dqb, dvb = dqk // nb, dv // nb
+    h = np.zeros((B, H, T, dv))
+    Cf = np.zeros((B, H, nb, dqb, dvb))
+    nf = np.zeros((B, H, dqk))
+    mf = np.zeros((B, H))
+    for b in range(B):
+        for hd in range(H):
+            lf = -np.logaddexp(0.0, -fp[b, hd])
+            F = np.cumsum(lf)
+            mi = 0.0 if m0 is None else m0[b, hd]
+            logD = F[:, None] - F[None, :] + ip[b, hd][None, :]
+            causal = np.tril(np.ones((T, T), dtype=bool))
+            logD = np.where(causal, logD, -np.inf)
+            log0 = F + mi
+            M = np.maximum(logD.max(axis=1), log0)
+            W = np.exp(logD - M[:, None])
+            w0 = np.exp(log0 - M)
+            qq, kk, vv = q[b, hd], k[b, hd], v[b, hd]
+            full = qq @ kk.T
+            den = (W * full).sum(axis=1) + bs_val(bs, hd) * np.exp(-M)
+            if n0 is not None:
+                den += w0 * (qq @ n0[b, hd])
+            num = np.zeros((T, dv))
+            for be in range(nb):
+                rs, cs = slice(be * dqb, (be + 1) * dqb), slice(be * dvb, (be + 1) * dvb)
+                A = qq[:, rs] @ kk[:, rs].T
+                num[:, cs] = (W * A) @ vv[:, cs]
+                if C0 is not None:
+                    num[:, cs] += w0[:, None] * (qq[:, rs] @ C0[b, hd, be])
+                Wl = W[-1]
+                Cf[b, hd, be] = (kk[:, rs] * Wl[:, None]).T @ vv[:, cs]
+                if C0 is not None:
+                    Cf[b, hd, be] += w0[-1] * C0[b, hd, be]
+            nf[b, hd] = (W[-1][:, None] * kk).sum(axis=0)
+            if n0 is not None:
+                nf[b, hd] += w0[-1] * n0[b, hd]
+            mf[b, hd] = M[-1]
+            o = 1.0 if op is None else 1.0 / (1.0 + np.exp(-op[b, hd]))
+            h[b, hd] = o * num / np.maximum(np.abs(den), np.exp(-M))[:, None]
+    return h, Cf, nf, mf
+
+
+def bs_val(bs, hd):
+    return 0.0 if bs is None else bs[hd]
+
+
+@pytest.mark.parametrize("nb,dqk,dv,T", [(1, 8, 12, 37), (2, 8, 12, 64), (4, 16, 8, 20), (1, 6, 6, 1)])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_pin_bruteforce_quadratic(nb, dqk, dv, T, with_state):
+    rng = RNG(10 + nb + T)
+    B, H = 2, 3
+    q, k, v, ip, fp, op, bs = _inputs(rng, B, H, T, dqk, dv)
+    st = _state(rng, B, H, dqk, dv, nb) if with_state else (None, None, None)
+    h, C, n, m = oracle.mlstm_fwd(q, k, v, ip, fp, op, bs, *st, num_blocks=nb)
+    hb, Cb, nbf, mb = brute_force(q, k, v, ip, fp, op, bs, nb, *st)
+    assert _relerr(h, hb) < 1e-12
+    assert np.max(np.abs(m - mb)) < 1e-12
+    assert _relerr(C, Cb) < 1e-12
+    assert _relerr(n, nbf) < 1e-12
+
+
+# ----------------------------------------------------------- unstabilised
+def direct_unstabilised(q, k, v, ip, fp, op, bs, nb, C0=None, n0=None, m0=None):
+    """C_t = f C + i v k^T (C is [d_v, d_qk], masked to the block diagonal),
+    n_t = f n + i k, h_t = o * C q / max(|n.q + bias|, 1); f = sigmoid,
+    i = exp, o = sigmoid, all without any stabiliser."""
+    B, H, T, dqk = q.shape
+    dv = v.shape[-1]
+    dqb, dvb = dqk // nb, dv // nb
+    mask = (np.arange(dv)[:, None] // dvb) == (np.arange(dqk)[None, :] // dqb)
+    h = np.zeros((B, H, T, dv))
+    for b in range(B):
+        for hd in range(H):
+            C = np.zeros((dv, dqk))
+            n = np.zeros(dqk)
+            if C0 is not None:
+                scale = np.exp(m0[b, hd])
+                for be in range(nb):
+                    C[be * dvb:(be + 1) * dvb, be * dqb:(be + 1) * dqb] = C0[b, hd, be].T * scale
+                n = n0[b, hd] * scale
+            for t in range(T):
+                f = 1.0 / (1.0 + np.exp(-fp[b, hd, t]))
+                i = np.exp(ip[b, hd, t])
+                C = f * C + i * np.outer(v[b, hd, t], k[b, hd, t]) * mask
+                n = f * n + i * k[b, hd, t]
+                o = 1.0 if op is None else 1.0 / (1.0 + np.exp(-op[b, hd, t]))
+                h[b, hd, t] = o * (C @ q[b, hd, t]) / max(abs(n @ q[b, hd, t] + bs_val(bs, hd)), 1.0)
+    return h
+
+
+@pytest.mark.parametrize("nb,dqk,dv", [(1, 8, 12), (2, 8, 12), (2, 16, 4)])
+def test_pin_unstabilised_direct(nb, dqk, dv):
+    rng = RNG(20 + nb + dqk)
+    B, H, T = 1, 4, 60
+    q, k, v, ip, fp, op, bs = _inputs(rng, B, H, T, dqk, dv)
+    h, *_ = oracle.mlstm_fwd(q, k, v, ip, fp, op, bs, num_blocks=nb)
+    assert _relerr(h, direct_unstabilised(q, k, v, ip, fp, op, bs, nb)) < 1e-11
+    st = _state(rng, B, H, dqk, dv, nb)
+    h, *_ = oracle.mlstm_fwd(q, k, v, ip, fp, op, bs, *st, num_blocks=nb)
+    assert _relerr(h, direct_unstabilised(q, k, v, ip, fp, op, bs, nb, *st)) < 1e-11
+
+
+def test_pin_unstabilised_cell_fp32_T60_workload():
+    """The single-cell fp32 workload itself (T = 60, no overflow without the
+    stabiliser) against the direct recurrence."""
+    from linear_recurrent_sequence_mlstm_amd.workloads import workload
+    x = workload("cell_fp32_T60")
+    h, *_ = oracle.mlstm_fwd(x.q, x.k, x.v, x.i_pre, x.f_pre, x.o_pre, x.bias)
+    f64 = lambda t: None if t is None else t.double().numpy()
+    hd = direct_unstabilised(*map(f64, (x.q, x.k, x.v, x.i_pre, x.f_pre, x.o_pre, x.bias)), 1)
+    assert _relerr(h, hd) < 1e-11
+
+
+# ------------------------------------------------------------ shift invariance
+def test_pin_stabiliser_shift_invariance():
+    rng = RNG(3)
+    B, H, T, dqk, dv, nb = 2, 2, 50, 8, 8, 2
+    q, k, v, ip, fp, op, bs = _inputs(rng, B, H, T, dqk, dv)
+    h, C, n, m = oracle.mlstm_fwd(q, k, v, ip, fp, op, bs, num_blocks=nb)
+    shift = rng.uniform(-5, 5, (B, H, T))
+    h2, C2, n2, m2 = oracle.mlstm_fwd(q, k, v, ip, fp, op, bs, num_blocks=nb, m_shift=shift)
+    assert _relerr(h2, h) < 1e-12
+    # the true (unstabilised) state is the same too
+    true = lambda S, mm: S * np.exp(mm)[:, :, None, None, None]
+    assert _relerr(true(C2, m2), true(C, m)) < 1e-11
+    assert np.max(np.abs(m2 - m)) > 1e-3  # the shift did move the stabiliser
+
+
+# ------------------------------------------------------------ special cases
+def test_pin_linear_attention_special_case():
+    """f = 1 (f_pre = +inf), i = 1 (i_pre = 0), no o: causal linear attention
+    h_t = sum_{s<=t} (q_t.k_s) v_s / max(|sum_{s<=t} q_t.k_s + b|, 1)."""
+    rng = RNG(4)
+    B, H, T, dqk, dv = 1, 2, 40, 6, 10
+    q, k, v, _, _, _, bs = _inputs(rng, B, H, T, dqk, dv)
+    ip = np.zeros((B, H, T))
+    fp = np.full((B, H, T), np.inf)
+    h, *_ = oracle.mlstm_fwd(q, k, v, ip, fp, None, bs)
+    KV = np.cumsum(k[..., :, None] * v[..., None, :], axis=2)  # [B,H,T,dqk,dv]
+    Z = np.cumsum(k, axis=2)
+    num = np.einsum("bhtr,bhtrc->bhtc", q, KV)
+    den = np.einsum("bhtr,bhtr->bht", q, Z) + bs[None, :, None]
+    ref = num / np.maximum(np.abs(den), 1.0)[..., None]
+    assert _relerr(h, ref) < 1e-12
+
+
+def test_pin_T1_closed_form():
+    rng = RNG(5)
+    B, H, dqk, dv = 3, 2, 8, 5
+    q, k, v, ip, fp, op, bs = _inputs(rng, B, H, 1, dqk, dv)
+    h, C, n, m = oracle.mlstm_fwd(q, k, v, ip, fp, op, bs)
+    i = np.exp(ip[..., 0])
+    qk = np.einsum("bhr,bhr->bh", q[:, :, 0], k[:, :, 0])
+    o = 1.0 / (1.0 + np.exp(-op[:, :, 0]))
+    ref = o * v[:, :, 0] * (i * qk / np.maximum(np.abs(i * qk + bs[None, :]), 1.0))[..., None]
+    assert _relerr(h[:, :, 0], ref) < 1e-14
+    lf = -np.logaddexp(0, -fp[..., 0])
+    assert np.max(np.abs(m - np.maximum(lf, ip[..., 0]))) < 1e-15
+
+
+def test_pin_state_carry_split_run():
+    rng = RNG(6)
+    B, H, T, dqk, dv, nb = 2, 2, 45, 8, 8, 2
+    q, k, v, ip, fp, op, bs = _inputs(rng, B, H, T, dqk, dv)
+    st = _state(rng, B, H, dqk, dv, nb)
+    h, C, n, m = oracle.mlstm_fwd(q, k, v, ip, fp, op, bs, *st, num_blocks=nb)
+    T1 = 17
+    sl = lambda a, s: None if a is None else a[:, :, s]
+    a = slice(0, T1)
+    b = slice(T1, T)
+    h1, C1, n1, m1 = oracle.mlstm_fwd(*(sl(x, a) for x in (q, k, v, ip, fp, op)), bs, *st, num_blocks=nb)
+    h2, C2, n2, m2 = oracle.mlstm_fwd(*(sl(x, b) for x in (q, k, v, ip, fp, op)), bs, C1, n1, m1, num_blocks=nb)
+    assert _relerr(np.concatenate([h1, h2], axis=2), h) < 1e-13
+    assert _relerr(C2, C) < 1e-13 and _relerr(n2, n) < 1e-13
+    assert np.max(np.abs(m2 - m)) < 1e-13
+
+
+def test_step_api_equals_sequence():
+    rng = RNG(7)
+    B, H, T, dqk, dv, nb = 2, 3, 12, 8, 12, 2
+    q, k, v, ip, fp, op, bs = _inputs(rng, B, H, T, dqk, dv)
+    h, C, n, m = oracle.mlstm_fwd(q, k, v, ip, fp, op, bs, num_blocks=nb)
+    Cs = np.zeros((B, H, nb, dqk // nb, dv // nb))
+    ns = np.zeros((B, H, dqk))
+    ms = np.zeros((B, H))
+    hs = np.stack([oracle.mlstm_step(q[:, :, t], k[:, :, t], v[:, :, t], ip[:, :, t], fp[:, :, t],
+                                     Cs, ns, ms, op[:, :, t], bs, num_blocks=nb)
+                   for t in range(T)], axis=2)
+    assert np.array_equal(hs, h)
+    assert np.array_equal(Cs, C) and np.array_equal(ns, n) and np.array_equal(ms, m)
+
+
+# ------------------------------------------------------------ retention
+def _gammas_golden():
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "retnet_gammas.txt")
+    rows = [l.split() for l in open(path) if l.strip() and not l.startswith("#")]
+    return np.array([float(g) for _, g in rows])
+
+
+def test_pin_retention_gamma_table():
+    g = _gammas_golden()
+    assert np.array_equal(g, 1.0 - 2.0 ** (-5.0 - np.arange(4)))
+    rng = RNG(8)
+    q, k, v = (rng.standard_normal((2, 4, 9, 5)) for _ in range(3))
+    a, Sa = oracle.retention_fwd(q, k, v)           # default gamma_h
+    b, Sb = oracle.retention_fwd(q, k, v, gamma=g)  # the page's values
+    assert np.array_equal(a, b) and np.array_equal(Sa, Sb)
+
+
+@pytest.mark.parametrize("with_state", [False, True])
+def test_pin_retention_decay_matrix_form(with_state):
+    """Parallel form of the RetNet page, ((Q K^T) * D) V with
+    D[n, m] = gamma^(n - m) for n >= m else 0, against the recurrence."""
+    rng = RNG(9)
+    B, H, T, dk, dv = 2, 4, 33, 6, 7
+    q, k, v = rng.standard_normal((B, H, T, dk)), rng.standard_normal((B, H, T, dk)), rng.standard_normal((B, H, T, dv))
+    S0 = rng.standard_normal((B, H, dk, dv)) if with_state else None
+    out, S = oracle.retention_fwd(q, k, v, S0=S0)
+    g = _gammas_golden()
+    nn, mm = np.meshgrid(np.arange(T), np.arange(T), indexing="ij")
+    for hd in range(H):
+        D = np.where(nn >= mm, g[hd] ** (nn - mm).astype(float), 0.0)
+        for b in range(B):
+            ref = ((q[b, hd] @ k[b, hd].T) * D) @ v[b, hd]
+            if S0 is not None:
+                ref += (g[hd] ** (np.arange(T) + 1.0))[:, None] * (q[b, hd] @ S0[b, hd])
+            assert _relerr(out[b, hd], ref) < 1e-12
+            Sref = (k[b, hd] * (g[hd] ** (T - 1.0 - np.arange(T)))[:, None]).T @ v[b, hd]
+            if S0 is not None:
+                Sref += g[hd] ** T * S0[b, hd]
+            assert _relerr(S[b, hd], Sref) < 1e-12
+
+
+def test_pin_retention_is_mlstm_special_case():
+    """i = 1 (i_pre = 0), f = gamma_h (f_pre = logit gamma_h), no normaliser:
+    the mLSTM oracle reduces to retention and its stabiliser stays at 0."""
+    rng = RNG(11)
+    B, H, T, d = 2, 4, 30, 6
+    q, k, v = (rng.standard_normal((B, H, T, d)) for _ in range(3))
+    g = _gammas_golden()
+    fp = np.broadcast_to(np.log(g / (1 - g))[None, :, None], (B, H, T)).copy()
+    h, C, n, m = oracle.mlstm_fwd(q, k, v, np.zeros((B, H, T)), fp, normalise=False)
+    out, S = oracle.retention_fwd(q, k, v)
+    assert _relerr(h, out) < 1e-13
+    assert _relerr(C[:, :, 0], S) < 1e-13
+    assert np.max(np.abs(m)) < 1e-13
+
+
+def test_pin_xlstm7b_state_size():
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "xlstm7b_state_size.txt")
+    kv = dict(l.split() for l in open(path) if l.strip() and not l.startswith("#"))
+    heads = int(kv["heads"])
+    dqk, dv = int(kv["qk_dim"]) // heads, int(kv["v_dim"]) // heads
+    assert (dqk, dv) == (256, 512)
+    per_head = dqk * dv + dqk  # C [d_qk, d_v] + n [d_qk]
+    total = int(kv["layers"]) * heads * per_head * int(kv["bytes_per_element"])
+    assert round(total / 2 ** 20, 1) == float(kv["printed_mib"])
