@@ -1,0 +1,152 @@
+/*
+ * libmlstm -- mLSTM matrix-memory recurrence and RetNet retention on AMD
+ * Instinct MI355X (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * The method.
+ *   Matrix memory, exponential input gate, log-space stabilised gating:
+ *     "mLSTM Model" page (DeepChrInteract-v2), section "Core idea" and its
+ *     display equation C_t = f_t C_{t-1} + i_t (v_t (x) k_t).
+ *   Normaliser with learnable bias and block-diagonal memory:
+ *     "Edifice.Recurrent.XLSTMv2" page, section "Key Improvements over
+ *     xLSTM v1", items 1 and 2 (normaliser read as the vector n_t = f n + i k
+ *     with readout n_t . q_t; the page prints a scalar form without q).
+ *   Retention (s_n = gamma s_{n-1} + K_n^T V_n, o_n = Q_n s_n) and
+ *   gamma_h = 1 - 2^(-5-h): "Edifice.Attention.RetNet" page, sections
+ *   "Key Innovation: Retention Mechanism" and "Multi-Scale Retention (MSR)";
+ *   the parallel, recurrent and chunkwise modes of its "Triple Paradigm".
+ *   In-place [B,H,K,V] state and chunk_size 64: burn-gdn2 config.rs,
+ *   Gdn2Mode::FusedRecurrent / Gdn2Mode::Chunk and Gdn2Config::chunk_size.
+ *
+ * Per (batch b, head h), with f = sigmoid(f_pre), i = exp(i_pre),
+ * o = sigmoid(o_pre) (or 1 when o_pre is NULL):
+ *     C_t = f_t C_{t-1} + i_t v_t k_t^T       n_t = f_t n_{t-1} + i_t k_t
+ *     h_t = o_t * (C_t q_t) / max(|n_t . q_t + bias_h|, 1)
+ * computed on the stabilised state S~ = C^T e^{-m}, n~ = n e^{-m} with
+ * m_t = max(log f_t + m_{t-1}, i_pre_t), m_0 = 0.  With num_blocks = nb > 1
+ * q, k, v are split into nb contiguous slices and C is block diagonal; gates,
+ * m, n and the denominator stay per head.
+ *
+ * Conventions for every entry point.
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major arrays.
+ *   - q, k, v, gate preactivations, o_pre and outputs h use the call's dtype;
+ *     states (C, n, m, S), norm_bias and gamma are always fp32.
+ *   - The caller owns every buffer.  The library allocates no memory and keeps
+ *     no pointer after returning.  Work is enqueued on `stream` (a
+ *     hipStream_t; NULL = default stream) and the call returns without
+ *     synchronising.
+ *   - Return value: 0 on success, a negative MLSTM_E_* code otherwise.  All
+ *     argument checks happen before anything is enqueued, so on error no
+ *     output has been touched.  mlstm_last_error() describes the last error of
+ *     the calling thread.
+ *   - Checks run on the host and need no GPU; MLSTM_E_HIP reports a failed
+ *     kernel launch.
+ */
+#ifndef MLSTM_H_
+#define MLSTM_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLSTM_ABI_VERSION 1
+
+typedef enum { MLSTM_F32 = 0, MLSTM_BF16 = 1 } mlstm_dtype;
+
+enum {
+  MLSTM_OK = 0,
+  MLSTM_E_NULL = -1,        /* a required pointer is NULL */
+  MLSTM_E_SHAPE = -2,       /* a size is out of range or inconsistent */
+  MLSTM_E_DTYPE = -3,       /* unknown dtype */
+  MLSTM_E_UNSUPPORTED = -4, /* valid request without a compiled kernel variant */
+  MLSTM_E_WORKSPACE = -5,   /* workspace missing or too small */
+  MLSTM_E_HIP = -6          /* the HIP runtime reported an error */
+};
+
+/* Version of this ABI (MLSTM_ABI_VERSION of the library that was built). */
+int mlstm_abi_version(void);
+
+/* Message for the last error returned on the calling thread ("" if none).
+ * The string stays valid until the next call on that thread. */
+const char* mlstm_last_error(void);
+
+/*
+ * Workspace size in bytes for mlstm_chunkwise_fwd with these arguments
+ * (0 if none is needed).  Returns 0 and sets the error message for invalid
+ * arguments; call mlstm_chunkwise_fwd to get the error code.
+ */
+size_t mlstm_chunkwise_workspace_bytes(int B, int H, int T, int d_qk, int d_v,
+                                       int num_blocks, int chunk,
+                                       mlstm_dtype dt);
+
+/*
+ * Chunkwise-parallel forward (prefill / training forward) over T tokens.
+ *   q, k     [B,H,T,d_qk]        dtype dt
+ *   v        [B,H,T,d_v]         dtype dt
+ *   i_pre    [B,H,T]             input-gate preactivation (i = exp(i_pre))
+ *   f_pre    [B,H,T]             forget-gate preactivation (f = sigmoid)
+ *   o_pre    [B,H,T,d_v] or NULL output-gate preactivation (o = sigmoid)
+ *   norm_bias [H] fp32 or NULL   normaliser bias (NULL = 0)
+ *   C0       [B,H,nb,d_qk/nb,d_v/nb] fp32 or NULL   initial S~ (NULL = 0)
+ *   n0       [B,H,d_qk] fp32 or NULL                initial n~ (NULL = 0)
+ *   m0       [B,H] fp32 or NULL                     initial m  (NULL = 0)
+ *   h        [B,H,T,d_v]         output, dtype dt
+ *   C_out, n_out, m_out          final stabilised state, same layouts as
+ *                                C0/n0/m0, or NULL to skip; each may alias
+ *                                its initial-state counterpart.
+ *   workspace, workspace_bytes   device scratch of at least
+ *                                mlstm_chunkwise_workspace_bytes(...) bytes,
+ *                                256-byte aligned; overwritten by the call.
+ * chunk is the chunk length L (64 for bf16; 16, 32 or 64 for fp32).
+ * Supported (d_qk, num_blocks): bf16 {(64,1),(64,2),(128,1),(256,1),(256,2)},
+ * fp32 {(64,1),(64,2)}; d_v must be a multiple of 64 (bf16 d_qk >= 128: of
+ * 128) whose per-block share is a multiple of 16.  Any T >= 1.
+ */
+int mlstm_chunkwise_fwd(int B, int H, int T, int d_qk, int d_v, int num_blocks,
+                        int chunk, mlstm_dtype dt, const void* q, const void* k,
+                        const void* v, const void* i_pre, const void* f_pre,
+                        const void* o_pre, const float* norm_bias,
+                        const float* C0, const float* n0, const float* m0,
+                        float* C_out, float* n_out, float* m_out, void* h,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Fused single-token decode step on every (b, h); the fp32 state is updated
+ * IN PLACE and the readout uses the updated state.
+ *   q, k  [B,H,d_qk]; v [B,H,d_v]; i_pre, f_pre [B,H]; o_pre [B,H,d_v] or
+ *   NULL (dtype dt); norm_bias [H] fp32 or NULL;
+ *   C [B,H,nb,d_qk/nb,d_v/nb], n [B,H,d_qk], m [B,H] fp32, read and written;
+ *   h [B,H,d_v] output (dtype dt).
+ * Requires d_v/4 to divide 256 and (d_qk/nb) % 8 == 0.
+ */
+int mlstm_step(int B, int H, int d_qk, int d_v, int num_blocks, mlstm_dtype dt,
+               const void* q, const void* k, const void* v, const void* i_pre,
+               const void* f_pre, const void* o_pre, const float* norm_bias,
+               float* C, float* n, float* m, void* h, void* stream);
+
+/* Workspace size in bytes for retention_chunkwise_fwd (0 if none). */
+size_t retention_chunkwise_workspace_bytes(int B, int H, int T, int d_k,
+                                           int d_v, int chunk, mlstm_dtype dt);
+
+/*
+ * RetNet retention, chunkwise form: out_t = sum_{s<=t} gamma_h^{t-s}
+ * (q_t . k_s) v_s + gamma_h^{t+1} q_t S0, i.e. the recurrence
+ * S_t = gamma_h S_{t-1} + k_t v_t^T, out_t = S_t^T q_t.  No normaliser, no
+ * gates, no stabiliser.
+ *   q, k [B,H,T,d_k]; v, out [B,H,T,d_v] (dtype dt);
+ *   gamma [H] fp32 in (0,1), or NULL for gamma_h = 1 - 2^(-5-h), h = 0..H-1;
+ *   S0, S_out [B,H,d_k,d_v] fp32 or NULL (S_out may alias S0).
+ * Supported d_k: bf16 {64, 128}, fp32 {64}; d_v as for mlstm_chunkwise_fwd.
+ */
+int retention_chunkwise_fwd(int B, int H, int T, int d_k, int d_v, int chunk,
+                            mlstm_dtype dt, const void* q, const void* k,
+                            const void* v, const float* gamma, const float* S0,
+                            float* S_out, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLSTM_H_ */

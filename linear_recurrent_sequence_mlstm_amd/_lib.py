@@ -1,0 +1,221 @@
+"""ctypes binding of libmlstm.so (C ABI in include/mlstm.h).
+
+Argument marshalling only: checks devices, dtypes, shapes and contiguity,
+allocates outputs and workspace as torch tensors (PyTorch provides device
+memory and the current stream), and calls the C entry points.  Every step of
+the computation runs in the HIP kernels; there is no fallback path, and a
+missing library raises an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmlstm.so")
+_lib = None
+
+F32, BF16 = 0, 1
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+
+# Every symbol declared in include/mlstm.h.
+EXPORTS = ("mlstm_abi_version", "mlstm_last_error", "mlstm_chunkwise_workspace_bytes",
+           "mlstm_chunkwise_fwd", "mlstm_step", "retention_chunkwise_workspace_bytes",
+           "retention_chunkwise_fwd")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libmlstm.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libmlstm.so is not built (%s); run `python -m "
+                           "linear_recurrent_sequence_mlstm_amd.build`" % _LIB_PATH)
+    L = ctypes.CDLL(_LIB_PATH)
+    i, sz, vp, fp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p
+    L.mlstm_abi_version.argtypes = []
+    L.mlstm_abi_version.restype = i
+    L.mlstm_last_error.argtypes = []
+    L.mlstm_last_error.restype = ctypes.c_char_p
+    L.mlstm_chunkwise_workspace_bytes.argtypes = [i] * 7 + [i]
+    L.mlstm_chunkwise_workspace_bytes.restype = sz
+    L.mlstm_chunkwise_fwd.argtypes = [i] * 8 + [vp] * 6 + [fp] * 7 + [vp, vp, sz, vp]
+    L.mlstm_chunkwise_fwd.restype = i
+    L.mlstm_step.argtypes = [i] * 6 + [vp] * 6 + [fp] * 4 + [vp, vp]
+    L.mlstm_step.restype = i
+    L.retention_chunkwise_workspace_bytes.argtypes = [i] * 6 + [i]
+    L.retention_chunkwise_workspace_bytes.restype = sz
+    L.retention_chunkwise_fwd.argtypes = [i] * 7 + [vp] * 3 + [fp] * 3 + [vp, vp, sz, vp]
+    L.retention_chunkwise_fwd.restype = i
+    _lib = L
+    return L
+
+
+def abi_version() -> int:
+    return lib().mlstm_abi_version()
+
+
+def last_error() -> str:
+    return lib().mlstm_last_error().decode()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise RuntimeError("%s failed (%d): %s" % (what, rc, last_error()))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def chunkwise_workspace_bytes(B, H, T, dqk, dv, num_blocks=1, chunk=64, dtype=torch.bfloat16) -> int:
+    return int(lib().mlstm_chunkwise_workspace_bytes(B, H, T, dqk, dv, num_blocks, chunk, _DT[dtype]))
+
+
+def retention_workspace_bytes(B, H, T, dk, dv, chunk=64, dtype=torch.bfloat16) -> int:
+    return int(lib().retention_chunkwise_workspace_bytes(B, H, T, dk, dv, chunk, _DT[dtype]))
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        return workspace
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def chunkwise_fwd(q, k, v, i_pre, f_pre, o_pre=None, bias=None, state=None, num_blocks=1,
+                  chunk=64, return_state=True, h=None, state_out=None, workspace=None):
+    """mlstm_chunkwise_fwd.  q,k [B,H,T,dqk]; v [B,H,T,dv]; i_pre,f_pre [B,H,T];
+    o_pre [B,H,T,dv] or None (all of one dtype, on one GPU); bias [H] fp32;
+    state = (C0 [B,H,nb,dqk/nb,dv/nb], n0 [B,H,dqk], m0 [B,H]) fp32 or None.
+    Returns (h, (C, n, m)) or (h, None)."""
+    B, H, T, dqk = q.shape
+    dv = v.shape[-1]
+    nb = int(num_blocks)
+    dev, dt = q.device, q.dtype
+    if dt not in _DT:
+        raise TypeError("unsupported dtype %s" % dt)
+    _need(k, "k", (B, H, T, dqk), dt, dev)
+    _need(v, "v", (B, H, T, dv), dt, dev)
+    _need(i_pre, "i_pre", (B, H, T), dt, dev)
+    _need(f_pre, "f_pre", (B, H, T), dt, dev)
+    _need(o_pre, "o_pre", (B, H, T, dv), dt, dev)
+    _need(bias, "bias", (H,), torch.float32, dev)
+    _need(q, "q", (B, H, T, dqk), dt, dev)
+    sshape = ((B, H, nb, dqk // nb, dv // nb), (B, H, dqk), (B, H))
+    C0 = n0 = m0 = None
+    if state is not None:
+        C0, n0, m0 = state
+        for t, nm, shp in zip((C0, n0, m0), ("C0", "n0", "m0"), sshape):
+            _need(t, nm, shp, torch.float32, dev)
+    if h is None:
+        h = torch.empty(B, H, T, dv, dtype=dt, device=dev)
+    _need(h, "h", (B, H, T, dv), dt, dev)
+    Co = no = mo = None
+    if return_state:
+        if state_out is not None:
+            Co, no, mo = state_out
+        else:
+            Co = torch.empty(sshape[0], dtype=torch.float32, device=dev)
+            no = torch.empty(sshape[1], dtype=torch.float32, device=dev)
+            mo = torch.empty(sshape[2], dtype=torch.float32, device=dev)
+        for t, nm, shp in zip((Co, no, mo), ("C_out", "n_out", "m_out"), sshape):
+            _need(t, nm, shp, torch.float32, dev)
+    L = lib()
+    nbytes = L.mlstm_chunkwise_workspace_bytes(B, H, T, dqk, dv, nb, chunk, _DT[dt])
+    if nbytes == 0:
+        _check(L.mlstm_chunkwise_fwd(B, H, T, dqk, dv, nb, chunk, _DT[dt], *([None] * 13),
+                                     None, None, 0, None), "mlstm_chunkwise_fwd")
+    ws = _workspace(nbytes, dev, workspace)
+    rc = L.mlstm_chunkwise_fwd(B, H, T, dqk, dv, nb, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(i_pre), _ptr(f_pre), _ptr(o_pre), _ptr(bias), _ptr(C0), _ptr(n0),
+                               _ptr(m0), _ptr(Co), _ptr(no), _ptr(mo), _ptr(h), _ptr(ws),
+                               ws.numel(), _stream(dev))
+    _check(rc, "mlstm_chunkwise_fwd")
+    return h, ((Co, no, mo) if return_state else None)
+
+
+def step(q, k, v, i_pre, f_pre, C, n, m, o_pre=None, bias=None, num_blocks=1, h=None):
+    """mlstm_step: one token per (b,h); C [B,H,nb,dqk/nb,dv/nb], n [B,H,dqk],
+    m [B,H] fp32 are updated in place.  Returns h [B,H,dv]."""
+    B, H, dqk = q.shape
+    dv = v.shape[-1]
+    nb = int(num_blocks)
+    dev, dt = q.device, q.dtype
+    if dt not in _DT:
+        raise TypeError("unsupported dtype %s" % dt)
+    _need(k, "k", (B, H, dqk), dt, dev)
+    _need(v, "v", (B, H, dv), dt, dev)
+    _need(i_pre, "i_pre", (B, H), dt, dev)
+    _need(f_pre, "f_pre", (B, H), dt, dev)
+    _need(o_pre, "o_pre", (B, H, dv), dt, dev)
+    _need(bias, "bias", (H,), torch.float32, dev)
+    _need(C, "C", (B, H, nb, dqk // nb, dv // nb), torch.float32, dev)
+    _need(n, "n", (B, H, dqk), torch.float32, dev)
+    _need(m, "m", (B, H), torch.float32, dev)
+    if h is None:
+        h = torch.empty(B, H, dv, dtype=dt, device=dev)
+    _need(h, "h", (B, H, dv), dt, dev)
+    rc = lib().mlstm_step(B, H, dqk, dv, nb, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre),
+                          _ptr(f_pre), _ptr(o_pre), _ptr(bias), _ptr(C), _ptr(n), _ptr(m), _ptr(h),
+                          _stream(dev))
+    _check(rc, "mlstm_step")
+    return h
+
+
+def retention_chunkwise_fwd(q, k, v, gamma=None, S0=None, chunk=64, return_state=True, out=None,
+                            S_out=None, workspace=None):
+    """retention_chunkwise_fwd.  q,k [B,H,T,dk]; v [B,H,T,dv]; gamma [H] fp32
+    or None (1 - 2^(-5-h)); S0 [B,H,dk,dv] fp32 or None.  Returns (out, S)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dt not in _DT:
+        raise TypeError("unsupported dtype %s" % dt)
+    _need(k, "k", (B, H, T, dk), dt, dev)
+    _need(v, "v", (B, H, T, dv), dt, dev)
+    _need(gamma, "gamma", (H,), torch.float32, dev)
+    _need(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty(B, H, T, dv, dtype=dt, device=dev)
+    _need(out, "out", (B, H, T, dv), dt, dev)
+    if return_state and S_out is None:
+        S_out = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    if return_state:
+        _need(S_out, "S_out", (B, H, dk, dv), torch.float32, dev)
+    L = lib()
+    nbytes = L.retention_chunkwise_workspace_bytes(B, H, T, dk, dv, chunk, _DT[dt])
+    if nbytes == 0:
+        _check(L.retention_chunkwise_fwd(B, H, T, dk, dv, chunk, _DT[dt], *([None] * 7), None, 0, None),
+               "retention_chunkwise_fwd")
+    ws = _workspace(nbytes, dev, workspace)
+    rc = L.retention_chunkwise_fwd(B, H, T, dk, dv, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(gamma), _ptr(S0), _ptr(S_out if return_state else None),
+                                   _ptr(out), _ptr(ws), ws.numel(), _stream(dev))
+    _check(rc, "retention_chunkwise_fwd")
+    return out, (S_out if return_state else None)

@@ -1,0 +1,239 @@
+// C ABI of libmlstm (declared in include/mlstm.h): argument checks, kernel
+// variant selection, workspace layout and launches on the caller's stream.
+// Every check runs before any HIP call, so invalid calls need no GPU and
+// touch no output.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/mlstm.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return MLSTM_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Optional tuning override: chunks per superchunk.
+int env_superchunk_chunks() {
+  const char* s = getenv("MLSTM_SUPERCHUNK_CHUNKS");
+  if (!s) return 0;
+  const int g = atoi(s);
+  return g > 0 ? g : 0;
+}
+
+int env_wave_cols() {
+  const char* s = getenv("MLSTM_WAVE_COLS");
+  if (!s) return 0;
+  const int w = atoi(s);
+  return (w == 16 || w == 32) ? w : 0;
+}
+
+struct Plan {
+  mlstm::ChunkVariant var;
+  int L, NC, G, NS, nslices;
+  size_t CS, nstate;
+  size_t off_scal, off_min, bytes;
+};
+
+// Checks shared by the mLSTM and retention chunkwise entry points and the
+// workspace queries; fills the plan.  Returns MLSTM_OK or an error code.
+int plan_chunkwise(int B, int H, int T, int dqk, int dv, int nb, int chunk, int dt, bool ret,
+                   Plan* pl) {
+  if (dt != MLSTM_F32 && dt != MLSTM_BF16) return fail(MLSTM_E_DTYPE, "unknown dtype %d", dt);
+  if (B < 1 || H < 1 || T < 1 || dqk < 1 || dv < 1 || nb < 1)
+    return fail(MLSTM_E_SHAPE, "sizes must be positive (B=%d H=%d T=%d d_qk=%d d_v=%d nb=%d)", B, H, T,
+                dqk, dv, nb);
+  if (dqk % nb || dv % nb)
+    return fail(MLSTM_E_SHAPE, "d_qk=%d and d_v=%d must be multiples of num_blocks=%d", dqk, dv, nb);
+  if ((long long)T * (dqk > dv ? dqk : dv) >= (1LL << 31))
+    return fail(MLSTM_E_SHAPE, "T * d too large (%d x %d)", T, dqk > dv ? dqk : dv);
+  if ((long long)B * H >= (1LL << 24)) return fail(MLSTM_E_SHAPE, "B * H too large");
+  if (chunk != 16 && chunk != 32 && chunk != 64)
+    return fail(MLSTM_E_SHAPE, "chunk must be 16, 32 or 64 (got %d)", chunk);
+  int wc = (dt == MLSTM_BF16 && dqk / nb >= 128) ? 32 : 16;
+  if (dt == MLSTM_BF16 && dqk == 256 && nb == 1 && env_wave_cols()) wc = env_wave_cols();
+  if (!mlstm::find_chunk_variant(dt, dqk, nb, wc, chunk, ret, &pl->var))
+    return fail(MLSTM_E_UNSUPPORTED,
+                "no kernel for dtype=%s d_qk=%d num_blocks=%d chunk=%d%s", dt ? "bf16" : "fp32", dqk, nb,
+                chunk, ret ? " (retention)" : "");
+  const int W = 4 * pl->var.wc;
+  if (dv % W || (dv / nb) % pl->var.wc)
+    return fail(MLSTM_E_UNSUPPORTED, "d_v=%d must be a multiple of %d with d_v/num_blocks a multiple of %d",
+                dv, W, pl->var.wc);
+  pl->L = chunk;
+  pl->nslices = dv / W;
+  pl->NC = (T + chunk - 1) / chunk;
+  // Superchunks: enough work-groups to fill 256 CUs at the occupancy the
+  // LDS footprint allows.
+  int per_cu = (int)(160 * 1024 / pl->var.lds_bytes);
+  if (per_cu < 1) per_cu = 1;
+  if (per_cu > 4) per_cu = 4;
+  const long long base = (long long)B * H * pl->nslices;
+  long long ns = (256LL * per_cu + base - 1) / base;
+  if (ns < 1) ns = 1;
+  if (ns > pl->NC) ns = pl->NC;
+  int G = (int)((pl->NC + ns - 1) / ns);
+  if (env_superchunk_chunks()) G = env_superchunk_chunks();
+  if (G > pl->NC) G = pl->NC;
+  pl->G = G;
+  pl->NS = (pl->NC + G - 1) / G;
+  pl->CS = (size_t)dqk * dv / nb;
+  pl->nstate = pl->CS + (ret ? 0 : dqk);
+  const size_t BH = (size_t)B * H;
+  pl->off_scal = align256(BH * pl->NS * pl->nstate * sizeof(float));
+  pl->off_min = pl->off_scal + align256(BH * pl->NS * 2 * sizeof(float));
+  pl->bytes = pl->off_min + align256(BH * pl->NS * sizeof(float));
+  return MLSTM_OK;
+}
+
+int launch(const Plan& pl, mlstm::ChunkParams& p, void* workspace, size_t workspace_bytes,
+           void* stream) {
+  if (!workspace) return fail(MLSTM_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", pl.bytes);
+  if (workspace_bytes < pl.bytes)
+    return fail(MLSTM_E_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, pl.bytes);
+  if ((size_t)workspace & 255) return fail(MLSTM_E_WORKSPACE, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  p.NC = pl.NC;
+  p.G = pl.G;
+  p.NS = pl.NS;
+  p.nslices = pl.nslices;
+  p.ws_state = reinterpret_cast<float*>(ws);
+  p.ws_scal = reinterpret_cast<float*>(ws + pl.off_scal);
+  p.ws_min = reinterpret_cast<float*>(ws + pl.off_min);
+  const hipError_t e = pl.var.launch(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLSTM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mlstm_abi_version(void) { return MLSTM_ABI_VERSION; }
+
+const char* mlstm_last_error(void) { return g_err; }
+
+size_t mlstm_chunkwise_workspace_bytes(int B, int H, int T, int d_qk, int d_v, int num_blocks, int chunk,
+                                       mlstm_dtype dt) {
+  Plan pl;
+  if (plan_chunkwise(B, H, T, d_qk, d_v, num_blocks, chunk, dt, false, &pl) != MLSTM_OK) return 0;
+  return pl.bytes;
+}
+
+size_t retention_chunkwise_workspace_bytes(int B, int H, int T, int d_k, int d_v, int chunk, mlstm_dtype dt) {
+  Plan pl;
+  if (plan_chunkwise(B, H, T, d_k, d_v, 1, chunk, dt, true, &pl) != MLSTM_OK) return 0;
+  return pl.bytes;
+}
+
+int mlstm_chunkwise_fwd(int B, int H, int T, int d_qk, int d_v, int num_blocks, int chunk, mlstm_dtype dt,
+                        const void* q, const void* k, const void* v, const void* i_pre, const void* f_pre,
+                        const void* o_pre, const float* norm_bias, const float* C0, const float* n0,
+                        const float* m0, float* C_out, float* n_out, float* m_out, void* h, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  Plan pl;
+  const int rc = plan_chunkwise(B, H, T, d_qk, d_v, num_blocks, chunk, dt, false, &pl);
+  if (rc != MLSTM_OK) return rc;
+  if (!q || !k || !v || !i_pre || !f_pre || !h)
+    return fail(MLSTM_E_NULL, "q, k, v, i_pre, f_pre and h are required");
+  mlstm::ChunkParams p{};
+  p.B = B;
+  p.H = H;
+  p.T = T;
+  p.DV = d_v;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.i_pre = i_pre;
+  p.f_pre = f_pre;
+  p.o_pre = o_pre;
+  p.bias = norm_bias;
+  p.ret_gamma = nullptr;
+  p.has_init = (C0 || n0 || m0) ? 1 : 0;
+  p.C0 = C0;
+  p.n0 = n0;
+  p.m0 = m0;
+  p.h = h;
+  p.C_out = C_out;
+  p.n_out = n_out;
+  p.m_out = m_out;
+  return launch(pl, p, workspace, workspace_bytes, stream);
+}
+
+int retention_chunkwise_fwd(int B, int H, int T, int d_k, int d_v, int chunk, mlstm_dtype dt, const void* q,
+                            const void* k, const void* v, const float* gamma, const float* S0, float* S_out,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan pl;
+  const int rc = plan_chunkwise(B, H, T, d_k, d_v, 1, chunk, dt, true, &pl);
+  if (rc != MLSTM_OK) return rc;
+  if (!q || !k || !v || !out) return fail(MLSTM_E_NULL, "q, k, v and out are required");
+  mlstm::ChunkParams p{};
+  p.B = B;
+  p.H = H;
+  p.T = T;
+  p.DV = d_v;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.ret_gamma = gamma;
+  p.has_init = S0 ? 1 : 0;
+  p.C0 = S0;
+  p.h = out;
+  p.C_out = S_out;
+  return launch(pl, p, workspace, workspace_bytes, stream);
+}
+
+int mlstm_step(int B, int H, int d_qk, int d_v, int num_blocks, mlstm_dtype dt, const void* q, const void* k,
+               const void* v, const void* i_pre, const void* f_pre, const void* o_pre, const float* norm_bias,
+               float* C, float* n, float* m, void* h, void* stream) {
+  if (dt != MLSTM_F32 && dt != MLSTM_BF16) return fail(MLSTM_E_DTYPE, "unknown dtype %d", dt);
+  if (B < 1 || H < 1 || d_qk < 1 || d_v < 1 || num_blocks < 1)
+    return fail(MLSTM_E_SHAPE, "sizes must be positive");
+  if (d_qk % num_blocks || d_v % num_blocks)
+    return fail(MLSTM_E_SHAPE, "d_qk=%d and d_v=%d must be multiples of num_blocks=%d", d_qk, d_v,
+                num_blocks);
+  if ((long long)B * H >= (1LL << 24)) return fail(MLSTM_E_SHAPE, "B * H too large");
+  if (!mlstm::step_supported(d_qk, d_v, num_blocks))
+    return fail(MLSTM_E_UNSUPPORTED, "no step kernel for d_qk=%d d_v=%d num_blocks=%d", d_qk, d_v, num_blocks);
+  if (!q || !k || !v || !i_pre || !f_pre || !C || !n || !m || !h)
+    return fail(MLSTM_E_NULL, "q, k, v, i_pre, f_pre, C, n, m and h are required");
+  mlstm::StepParams p{};
+  p.B = B;
+  p.H = H;
+  p.DQK = d_qk;
+  p.DV = d_v;
+  p.NB = num_blocks;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.i_pre = i_pre;
+  p.f_pre = f_pre;
+  p.o_pre = o_pre;
+  p.bias = norm_bias;
+  p.C = C;
+  p.n = n;
+  p.m = m;
+  p.h = h;
+  const hipError_t e = mlstm::launch_step(dt, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLSTM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

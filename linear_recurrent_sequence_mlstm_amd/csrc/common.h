@@ -1,0 +1,105 @@
+// Device helpers shared by the mLSTM / retention kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlstm {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// log(sigmoid(x)) = min(x, 0) - log1p(exp(-|x|)), in log2 units.
+__device__ __forceinline__ float log2_sigmoid(float x) {
+  return (fminf(x, 0.f) - log1pf(__expf(-fabsf(x)))) * kLog2e;
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __expf(-x)); }
+
+// MFMA traits: one 16x16 output tile, K elements of the contraction per
+// instruction, KL of them held by each lane.  Lane l holds A[l%16][KL*(l/16)+e],
+// B[KL*(l/16)+e][l%16] and D[4*(l/16)+i][l%16].
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<__bf16> {
+  static constexpr int K = 32;
+  static constexpr int KL = 8;
+  typedef bf16x8 frag;
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag load(const __bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+  }
+  __device__ __forceinline__ static frag zero() {
+    frag z;
+    for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.f;
+    return z;
+  }
+};
+
+template <>
+struct Mma<float> {
+  static constexpr int K = 4;
+  static constexpr int KL = 1;
+  typedef float frag;
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag load(const float* p) { return *p; }
+  __device__ __forceinline__ static frag zero() { return 0.f; }
+};
+
+// Vector of 16 bytes of element type T.
+template <typename T>
+struct Vec16 {
+  static constexpr int N = 16 / sizeof(T);
+  T v[N];
+};
+
+template <typename T>
+__device__ __forceinline__ Vec16<T> load16(const T* p) {
+  Vec16<T> r;
+  *reinterpret_cast<uint4*>(r.v) = *reinterpret_cast<const uint4*>(p);
+  return r;
+}
+
+template <typename T>
+__device__ __forceinline__ Vec16<T> zero16() {
+  Vec16<T> r;
+  *reinterpret_cast<uint4*>(r.v) = make_uint4(0, 0, 0, 0);
+  return r;
+}
+
+// Four consecutive elements to an 8- (bf16) or 16-byte (fp32) aligned address.
+__device__ __forceinline__ void store4(__bf16* dst, __bf16 a, __bf16 b, __bf16 c, __bf16 d) {
+  bf16x4 v;
+  v[0] = a;
+  v[1] = b;
+  v[2] = c;
+  v[3] = d;
+  *reinterpret_cast<bf16x4*>(dst) = v;
+}
+__device__ __forceinline__ void store4(float* dst, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
+}
+
+}  // namespace mlstm

@@ -1,0 +1,76 @@
+// Host-side view of the kernels: launch parameter blocks and variant lookup.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace mlstm {
+
+// Chunkwise forward (mLSTM or retention).  All pointers are device pointers.
+struct ChunkParams {
+  int B, H, T, DV;
+  int NC, G, NS, nslices;  // chunks, chunks per superchunk, superchunks, d_v slices
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* i_pre;
+  const void* f_pre;
+  const void* o_pre;
+  const float* bias;       // [H] or null
+  const float* ret_gamma;  // retention: [H] gamma_h, or null for 1 - 2^(-5-h)
+  float* ws_state;         // [B*H][NS][CS (+ d_qk)] superchunk start states
+  float* ws_scal;          // [B*H][NS][2] (total log2 decay, local log2 scale)
+  float* ws_min;           // [B*H][NS] stabiliser (log2) at superchunk starts
+  int has_init;
+  const float* C0;
+  const float* n0;
+  const float* m0;
+  void* h;
+  float* C_out;
+  float* n_out;
+  float* m_out;
+};
+
+struct ScanParams {
+  int NS;
+  size_t CS;
+  int DQK;
+  float* ws_state;
+  float* ws_scal;
+  float* ws_min;
+  int has_init;
+  const float* C0;
+  const float* n0;
+  const float* m0;
+};
+
+typedef hipError_t (*ChunkLaunchFn)(ChunkParams, hipStream_t);
+
+struct ChunkVariant {
+  ChunkLaunchFn launch;
+  size_t lds_bytes;
+  int wc;
+};
+
+// dtype: 0 = fp32, 1 = bf16.  wc = d_v columns per wave (work-group = 4 waves).
+bool find_chunk_variant(int dtype, int dqk, int nb, int wc, int L, bool ret, ChunkVariant* out);
+
+// Decode step.
+struct StepParams {
+  int B, H, DQK, DV, NB;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* i_pre;
+  const void* f_pre;
+  const void* o_pre;
+  const float* bias;
+  float* C;
+  float* n;
+  float* m;
+  void* h;
+};
+
+hipError_t launch_step(int dtype, const StepParams& p, hipStream_t stream);
+bool step_supported(int dqk, int dv, int nb);
+
+}  // namespace mlstm

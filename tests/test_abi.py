@@ -1,0 +1,79 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+that include/mlstm.h declares, and rejects invalid arguments with the
+documented error codes before touching the GPU (all pointers here are NULL or
+bogus host values that the library must never dereference)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_recurrent_sequence_mlstm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+E_NULL, E_SHAPE, E_DTYPE, E_UNSUPPORTED, E_WORKSPACE = -1, -2, -3, -4, -5
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "mlstm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_]+)\s*\(", src)) - {"sizeof"})
+
+
+def test_header_declares_the_exported_api():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert _lib.abi_version() == 1
+
+
+BOGUS = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _fwd(B=1, H=2, T=64, dqk=64, dv=64, nb=1, chunk=64, dt=1, ptr=BOGUS, ws=BOGUS, wsb=1 << 30):
+    L = _lib.lib()
+    p = [ptr] * 6 + [None] * 7
+    return L.mlstm_chunkwise_fwd(B, H, T, dqk, dv, nb, chunk, dt, *p, ptr, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), E_SHAPE), (dict(T=0), E_SHAPE), (dict(dqk=-1), E_SHAPE),
+    (dict(nb=3), E_SHAPE), (dict(dt=7), E_DTYPE), (dict(chunk=48), E_SHAPE),
+    (dict(dqk=96), E_UNSUPPORTED), (dict(dv=96), E_UNSUPPORTED), (dict(nb=4), E_UNSUPPORTED),
+    (dict(ptr=None), E_NULL), (dict(ws=None), E_WORKSPACE), (dict(wsb=16), E_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x1008)), E_WORKSPACE),
+])
+def test_chunkwise_validation(kw, code):
+    assert _fwd(**kw) == code
+    assert _lib.last_error() != ""
+
+
+def test_workspace_query():
+    L = _lib.lib()
+    n = L.mlstm_chunkwise_workspace_bytes(1, 8, 8192, 256, 512, 1, 64, 1)
+    assert n > 0 and n % 256 == 0
+    assert L.mlstm_chunkwise_workspace_bytes(1, 8, 8192, 96, 512, 1, 64, 1) == 0
+    assert L.retention_chunkwise_workspace_bytes(8, 4, 2048, 64, 64, 64, 1) > 0
+
+
+def test_step_validation():
+    L = _lib.lib()
+    P = [BOGUS] * 6 + [None] + [BOGUS] * 3 + [BOGUS, None]
+    P0 = [BOGUS] * 6 + [None] + [BOGUS] * 3
+    assert L.mlstm_step(0, 1, 64, 64, 1, 1, *P0, BOGUS, None) == E_SHAPE
+    assert L.mlstm_step(1, 1, 64, 64, 1, 5, *P0, BOGUS, None) == E_DTYPE
+    assert L.mlstm_step(1, 1, 64, 60, 1, 1, *P0, BOGUS, None) == E_UNSUPPORTED
+    assert L.mlstm_step(1, 1, 64, 64, 3, 1, *P0, BOGUS, None) == E_SHAPE
+    assert L.mlstm_step(1, 1, 64, 64, 1, 1, *([None] * 10), BOGUS, None) == E_NULL
+
+
+def test_retention_validation():
+    L = _lib.lib()
+    p = [BOGUS] * 3 + [None] * 3
+    assert L.retention_chunkwise_fwd(1, 1, 10, 256, 64, 64, 1, *p, BOGUS, BOGUS, 1 << 30, None) == E_UNSUPPORTED
+    assert L.retention_chunkwise_fwd(1, 1, 10, 64, 64, 64, 1, None, BOGUS, BOGUS, None, None, None,
+                                     BOGUS, BOGUS, 1 << 30, None) == E_NULL

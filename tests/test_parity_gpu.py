@@ -1,0 +1,235 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle on
+the same seeded inputs.
+
+Error metric: for every (batch, head) slice, max |y - y_ref| / max |y_ref|
+over all its elements; the test takes the largest over slices.  Bars: 1e-4
+for the fp32 path, 2e-2 for bf16 inputs.  Final states are compared after
+rescaling the stabilised state by e^{m_gpu - m_ref}; m itself to 1e-4
+absolute.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_recurrent_sequence_mlstm_amd import _lib as mlstm
+from linear_recurrent_sequence_mlstm_amd.workloads import mlstm_inputs, retention_inputs, workload
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+
+
+def slice_err(got, ref, lead=2):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    g = got.reshape(int(np.prod(got.shape[:lead])), -1)
+    r = ref.reshape(g.shape)
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    den = np.maximum(np.abs(r).max(axis=1), 1e-30)
+    return float((np.abs(g - r).max(axis=1) / den).max())
+
+
+def cpu(t):
+    return None if t is None else t.detach().to("cpu", torch.float64).numpy()
+
+
+def check_state(gpu_state, ref, tol, m_tol=1e-4):
+    C, n, m = (cpu(t) for t in gpu_state)
+    Cr, nr, mr = ref
+    assert np.max(np.abs(m - mr)) < m_tol
+    sc = np.exp(m - mr)
+    assert slice_err(C * sc[:, :, None, None, None], Cr) < tol
+    assert slice_err(n * sc[:, :, None], nr) < tol
+
+
+def run_both(x, dev, chunk=64, state=None, gpu_state=None):
+    g = x.to(dev)
+    h, st = mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, state=gpu_state,
+                                num_blocks=x.num_blocks, chunk=chunk)
+    torch.cuda.synchronize()
+    ref = oracle.mlstm_fwd(x.q, x.k, x.v, x.i_pre, x.f_pre, x.o_pre, x.bias,
+                           *(state if state is not None else (None, None, None)),
+                           num_blocks=x.num_blocks)
+    return h, st, ref
+
+
+# ---------------------------------------------------------------- fp32 cell
+@pytest.mark.parametrize("chunk", [64, 32, 16])
+def test_cell_fp32_T60_chunkwise(gpu, chunk):
+    x = workload("cell_fp32_T60")
+    h, st, ref = run_both(x, gpu, chunk=chunk)
+    assert slice_err(cpu(h), ref[0]) < TOL[torch.float32]
+    check_state(st, ref[1:], TOL[torch.float32])
+
+
+def test_cell_fp32_T60_step(gpu):
+    x = workload("cell_fp32_T60")
+    g = x.to(gpu)
+    B, H, T, dqk = x.q.shape
+    dv = x.v.shape[-1]
+    C = torch.zeros(B, H, 1, dqk, dv, device=gpu)
+    n = torch.zeros(B, H, dqk, device=gpu)
+    m = torch.zeros(B, H, device=gpu)
+    Cr, nr, mr = np.zeros((B, H, 1, dqk, dv)), np.zeros((B, H, dqk)), np.zeros((B, H))
+    for t in range(T):
+        h = mlstm.step(g.q[:, :, t].contiguous(), g.k[:, :, t].contiguous(), g.v[:, :, t].contiguous(),
+                       g.i_pre[:, :, t].contiguous(), g.f_pre[:, :, t].contiguous(), C, n, m,
+                       o_pre=g.o_pre[:, :, t].contiguous(), bias=g.bias)
+        hr = oracle.mlstm_step(x.q[:, :, t], x.k[:, :, t], x.v[:, :, t], x.i_pre[:, :, t],
+                               x.f_pre[:, :, t], Cr, nr, mr, o_pre=x.o_pre[:, :, t], bias=x.bias)
+        assert slice_err(cpu(h), hr) < TOL[torch.float32], t
+    check_state((C, n, m), (Cr, nr, mr), TOL[torch.float32])
+
+
+# ------------------------------------------------------------ bf16 chunkwise
+CASES = [
+    # B, H, T, dqk, dv, nb, with_o, bias, f_mix
+    (2, 2, 200, 64, 64, 1, True, "uniform", False),
+    (2, 2, 1, 64, 64, 1, True, "uniform", False),
+    (1, 2, 63, 64, 64, 1, False, None, False),
+    (1, 2, 64, 64, 64, 1, False, None, False),
+    (1, 2, 65, 64, 64, 1, False, None, True),
+    (2, 2, 777, 64, 64, 2, False, "uniform", True),
+    (1, 3, 1500, 64, 128, 2, True, "uniform", True),
+    (1, 2, 300, 128, 256, 1, True, "uniform", False),
+    (1, 2, 1000, 256, 512, 1, False, None, False),
+    (1, 1, 333, 256, 512, 1, True, "uniform", True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B%dH%dT%d_%dx%d_nb%d" % c[:6])
+def test_chunkwise_bf16(gpu, case):
+    B, H, T, dqk, dv, nb, with_o, bias, fmix = case
+    x = mlstm_inputs(B, H, T, dqk, dv, seed=7 + T, dtype="bf16", nb=nb, k_scale=dqk ** -0.5,
+                     f_mix=fmix, with_o=with_o, bias=bias)
+    h, st, ref = run_both(x, gpu)
+    assert slice_err(cpu(h), ref[0]) < TOL[torch.bfloat16]
+    check_state(st, ref[1:], TOL[torch.bfloat16])
+
+
+@pytest.mark.parametrize("dqk,dv,nb", [(64, 64, 1), (64, 64, 2), (256, 512, 1)])
+def test_chunkwise_initial_state_and_split_run(gpu, dqk, dv, nb):
+    """Run [0, T1) then [T1, T) carrying the state; both halves and the final
+    state must match the oracle's single run (the state is the checkpoint)."""
+    B, H, T, T1 = 1, 2, 900, 413
+    x = mlstm_inputs(B, H, T, dqk, dv, seed=31, dtype="bf16", nb=nb, k_scale=dqk ** -0.5,
+                     f_mix=True, with_o=True, bias="uniform")
+    ref = oracle.mlstm_fwd(x.q, x.k, x.v, x.i_pre, x.f_pre, x.o_pre, x.bias, num_blocks=nb)
+    g = x.to(gpu)
+    sl = lambda t, s: t[:, :, s].contiguous()
+    a, b = slice(0, T1), slice(T1, T)
+    h1, st1 = mlstm.chunkwise_fwd(sl(g.q, a), sl(g.k, a), sl(g.v, a), sl(g.i_pre, a), sl(g.f_pre, a),
+                                  sl(g.o_pre, a), g.bias, num_blocks=nb)
+    h2, st2 = mlstm.chunkwise_fwd(sl(g.q, b), sl(g.k, b), sl(g.v, b), sl(g.i_pre, b), sl(g.f_pre, b),
+                                  sl(g.o_pre, b), g.bias, state=st1, num_blocks=nb)
+    torch.cuda.synchronize()
+    assert slice_err(cpu(torch.cat([h1, h2], dim=2)), ref[0]) < TOL[torch.bfloat16]
+    check_state(st2, ref[1:], TOL[torch.bfloat16])
+    # in place: state_out aliasing the initial state
+    st_alias = tuple(t.clone() for t in st1)
+    h3, _ = mlstm.chunkwise_fwd(sl(g.q, b), sl(g.k, b), sl(g.v, b), sl(g.i_pre, b), sl(g.f_pre, b),
+                                sl(g.o_pre, b), g.bias, state=st_alias, state_out=st_alias, num_blocks=nb)
+    torch.cuda.synchronize()
+    assert torch.equal(h3, h2)
+    check_state(st_alias, ref[1:], TOL[torch.bfloat16])
+
+
+def test_chunkwise_deterministic_and_writes_every_output(gpu):
+    x = mlstm_inputs(1, 4, 1234, 256, 512, seed=5, dtype="bf16", k_scale=1 / 16).to(gpu)
+    outs = []
+    for _ in range(2):
+        h = torch.full((1, 4, 1234, 512), float("nan"), dtype=torch.bfloat16, device=gpu)
+        mlstm.chunkwise_fwd(x.q, x.k, x.v, x.i_pre, x.f_pre, h=h)
+        outs.append(h)
+    torch.cuda.synchronize()
+    assert not torch.isnan(outs[0]).any()
+    assert torch.equal(outs[0], outs[1])
+
+
+# ------------------------------------------------------------ retention
+@pytest.mark.parametrize("T,with_state", [(2048, False), (700, True), (50, False)])
+def test_retention_bf16(gpu, T, with_state):
+    B, H, d = 8 if T == 2048 else 2, 4, 64
+    q, k, v = retention_inputs(B, H, T, d, d, seed=1002)
+    S0 = torch.randn(B, H, d, d, generator=torch.Generator().manual_seed(3)) if with_state else None
+    out, S = mlstm.retention_chunkwise_fwd(q.to(gpu), k.to(gpu), v.to(gpu),
+                                           S0=None if S0 is None else S0.to(gpu))
+    torch.cuda.synchronize()
+    ref_out, ref_S = oracle.retention_fwd(q, k, v, S0=S0)
+    assert slice_err(cpu(out), ref_out) < TOL[torch.bfloat16]
+    assert slice_err(cpu(S), ref_S) < TOL[torch.bfloat16]
+
+
+def test_retention_decay_matrix_form_full_size(gpu):
+    """RetNet workload at full size against the page's parallel form
+    ((Q K^T) * D) V evaluated in fp64 on the CPU."""
+    q, k, v = workload("retnet_msr_T2048")
+    out, _ = mlstm.retention_chunkwise_fwd(q.to(gpu), k.to(gpu), v.to(gpu), return_state=False)
+    torch.cuda.synchronize()
+    B, H, T, _ = q.shape
+    t = torch.arange(T, dtype=torch.float64)
+    diff = (t[:, None] - t[None, :])
+    qd, kd, vd = q.double(), k.double(), v.double()
+    errs = []
+    for hd in range(H):
+        g = 1.0 - 2.0 ** (-5 - hd)
+        D = torch.where(diff >= 0, g ** diff.clamp(min=0), torch.zeros(()))
+        ref = ((qd[:, hd] @ kd[:, hd].transpose(1, 2)) * D) @ vd[:, hd]
+        errs.append(slice_err(cpu(out[:, hd]), ref.numpy(), lead=1))
+    assert max(errs) < TOL[torch.bfloat16]
+
+
+def test_retention_custom_gamma_fp32(gpu):
+    B, H, T, d = 1, 2, 130, 64
+    q, k, v = retention_inputs(B, H, T, d, d, seed=9, dtype="f32")
+    gamma = torch.tensor([0.9, 0.5])
+    out, S = mlstm.retention_chunkwise_fwd(q.to(gpu), k.to(gpu), v.to(gpu), gamma=gamma.to(gpu))
+    torch.cuda.synchronize()
+    ref_out, ref_S = oracle.retention_fwd(q, k, v, gamma=gamma)
+    assert slice_err(cpu(out), ref_out) < TOL[torch.float32]
+    assert slice_err(cpu(S), ref_S) < TOL[torch.float32]
+
+
+# ------------------------------------------------------------ decode step
+@pytest.mark.parametrize("B,H,dqk,dv,nb,with_o,bias", [
+    (3, 2, 64, 64, 1, True, "uniform"), (2, 4, 64, 64, 2, False, "uniform"),
+    (4, 2, 256, 512, 1, False, None), (2, 2, 128, 256, 2, True, "uniform"),
+])
+def test_step_bf16(gpu, B, H, dqk, dv, nb, with_o, bias):
+    from linear_recurrent_sequence_mlstm_amd.workloads import decode_inputs
+    S = 20
+    x = decode_inputs(S, B, H, dqk, dv, seed=77, nb=nb, k_scale=dqk ** -0.5, with_o=with_o, bias=bias)
+    g = x.to(gpu)
+    C = torch.zeros(B, H, nb, dqk // nb, dv // nb, device=gpu)
+    n = torch.zeros(B, H, dqk, device=gpu)
+    m = torch.zeros(B, H, device=gpu)
+    Cr, nr, mr = np.zeros((B, H, nb, dqk // nb, dv // nb)), np.zeros((B, H, dqk)), np.zeros((B, H))
+    for s in range(S):
+        h = mlstm.step(g.q[s], g.k[s], g.v[s], g.i_pre[s], g.f_pre[s], C, n, m,
+                       o_pre=None if g.o_pre is None else g.o_pre[s], bias=g.bias, num_blocks=nb)
+        hr = oracle.mlstm_step(x.q[s], x.k[s], x.v[s], x.i_pre[s], x.f_pre[s], Cr, nr, mr,
+                               o_pre=None if x.o_pre is None else x.o_pre[s], bias=x.bias, num_blocks=nb)
+        assert slice_err(cpu(h), hr) < TOL[torch.bfloat16], s
+    check_state((C, n, m), (Cr, nr, mr), TOL[torch.bfloat16])
+
+
+def test_step_matches_chunkwise(gpu):
+    """Decode steps continuing a chunkwise prefill equal the oracle on the
+    concatenated sequence (prefill state handed to the step kernel)."""
+    B, H, T, dqk, dv = 1, 2, 150, 64, 64
+    x = mlstm_inputs(B, H, T + 5, dqk, dv, seed=12, dtype="bf16", k_scale=1 / 8, bias="uniform")
+    ref = oracle.mlstm_fwd(x.q, x.k, x.v, x.i_pre, x.f_pre, None, x.bias)
+    g = x.to(gpu)
+    sl = lambda t: t[:, :, :T].contiguous()
+    h, (C, n, m) = mlstm.chunkwise_fwd(sl(g.q), sl(g.k), sl(g.v), sl(g.i_pre), sl(g.f_pre), bias=g.bias)
+    C = C.clone()
+    hs = []
+    for t in range(T, T + 5):
+        hs.append(mlstm.step(g.q[:, :, t].contiguous(), g.k[:, :, t].contiguous(), g.v[:, :, t].contiguous(),
+                             g.i_pre[:, :, t].contiguous(), g.f_pre[:, :, t].contiguous(), C, n, m,
+                             bias=g.bias).clone())
+    torch.cuda.synchronize()
+    full = torch.cat([h, torch.stack(hs, dim=2)], dim=2)
+    assert slice_err(cpu(full), ref[0]) < TOL[torch.bfloat16]
