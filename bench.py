@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the mLSTM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Step = one chunkwise prefill (mlstm_chunkwise_fwd) of the xLSTM-7B-shaped
+layer: B=1, 8 heads, d_qk=256, d_v=512, T=8192, chunk 64, bf16 q/k/v/gates,
+fp32 state, inputs resident in HBM.  K steps are timed between two device
+synchronisations; four input sets are rotated so that successive steps do not
+find their inputs in the 256 MB Infinity Cache.  ``value`` is prefill
+tokens/s = B*T*K / wall time.
+
+The decode part (``decode``) runs the xLSTM-7B-shaped fused decode step:
+B=256, 8 heads, fp32 state [256,8,256,512] (1 GiB) updated in place, 128 steps
+with a fresh bf16 token per step; it reports achieved HBM GB/s.
+
+``roofline`` is measured live: HIP events recorded by the library right before
+and after its main kernel (mlstm_set_profile_events) give that kernel's
+average duration over the timed steps; achieved = algorithmic bytes per
+launch / that duration.  ``cpu_baseline`` times the fp64 CPU oracle on the
+host cores on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "mLSTM prefill tokens/s (7B-shape, T=8192) + decode-step HBM GB/s, % roofline"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+
+
+def prefill_work(B, H, T, dqk, dv, L=64):
+    """Algorithmic bytes and flops of one chunkwise forward: every input read
+    once, h written once, final state written once; flops with dense LxL
+    intra-chunk tiles (2L(d_qk+d_v) + 4 d_qk d_v per token and head)."""
+    e = 2  # bf16
+    byts = B * H * T * (2 * dqk + dv) * e + B * H * T * 2 * e + B * H * T * dv * e
+    byts += B * H * (dqk * dv + dqk + 1) * 4
+    flops = B * H * T * (2 * L * (dqk + dv) + 4 * dqk * dv)
+    return byts, flops
+
+
+def decode_work(B, H, dqk, dv):
+    """Algorithmic bytes per decode step: fp32 C, n, m read and written once,
+    one bf16 token (q, k, v, i, f) read, h written."""
+    byts = 2 * B * H * (dqk * dv + dqk + 1) * 4
+    byts += B * H * (2 * dqk + dv + 2) * 2 + B * H * dv * 2
+    flops = B * H * (5 * dqk * dv + 4 * dqk)
+    return byts, flops
+
+
+def source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "linear_recurrent_sequence_mlstm_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel, sha):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def bench_prefill(torch, mlstm, x, args, dev):
+    spec = dict(B=1, H=8, T=8192, dqk=256, dv=512)
+    sets = [x.to(dev)]
+    for _ in range(3):  # distinct buffers with the same values
+        g = sets[0]
+        sets.append(type(g)(*(None if t is None else t.clone() for t in
+                              (g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias)), g.num_blocks, g.chunk))
+    B, H, T, dqk, dv = (spec[k] for k in ("B", "H", "T", "dqk", "dv"))
+    hs = [torch.empty(B, H, T, dv, dtype=torch.bfloat16, device=dev) for _ in sets]
+    st = (torch.empty(B, H, 1, dqk, dv, device=dev), torch.empty(B, H, dqk, device=dev),
+          torch.empty(B, H, device=dev))
+    ws = torch.empty(mlstm.chunkwise_workspace_bytes(B, H, T, dqk, dv), dtype=torch.uint8, device=dev)
+
+    def call(i):
+        g = sets[i % len(sets)]
+        mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, h=hs[i % len(sets)],
+                            state_out=st, workspace=ws)
+
+    for i in range(args.warmup):
+        call(i)
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in kev:  # create the HIP events before the timed region
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        mlstm.set_profile_events(*kev[i])
+        ev[i][0].record()
+        call(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mlstm.set_profile_events()
+    step_ms = sum(a.elapsed_time(b) for a, b in ev) / K
+    kern_ms = sum(a.elapsed_time(b) for a, b in kev) / K
+    byts, flops = prefill_work(B, H, T, dqk, dv)
+    return dict(spec=spec, wall=wall, K=K, step_ms=step_ms, kern_ms=kern_ms, bytes=byts, flops=flops,
+                tokens=B * T)
+
+
+def bench_decode(torch, mlstm, workload, args, dev):
+    d = workload("xlstm7b_decode_B256", steps=args.decode_steps).to(dev)
+    S, B, H, dqk = d.q.shape
+    dv = d.v.shape[-1]
+    C = torch.zeros(B, H, 1, dqk, dv, device=dev)
+    n = torch.zeros(B, H, dqk, device=dev)
+    m = torch.zeros(B, H, device=dev)
+    h = torch.empty(B, H, dv, dtype=torch.bfloat16, device=dev)
+
+    def call(s):
+        mlstm.step(d.q[s], d.k[s], d.v[s], d.i_pre[s], d.f_pre[s], C, n, m, bias=d.bias, h=h)
+
+    for s in range(min(args.warmup, S)):
+        call(s)
+    for t in (C, n, m):
+        t.zero_()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(S)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(S):
+        ev[s][0].record()
+        call(s)
+        ev[s][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = sum(a.elapsed_time(b) for a, b in ev) / S
+    byts, flops = decode_work(B, H, dqk, dv)
+    return dict(B=B, H=H, dqk=dqk, dv=dv, S=S, wall=wall, step_ms=step_ms, bytes=byts, flops=flops)
+
+
+def cpu_baseline(x, sample_tokens):
+    """The fp64 oracle on the host cores: all 8 heads of the prefill workload
+    (the same CPU tensors the GPU got) over its first ``sample_tokens`` tokens."""
+    import oracle
+    Ts = min(sample_tokens, x.q.shape[2])
+    sl = lambda t: None if t is None else t[:, :, :Ts].contiguous()
+    args = [sl(t) for t in (x.q, x.k, x.v, x.i_pre, x.f_pre)]
+    t0 = time.perf_counter()
+    oracle.mlstm_fwd(*args)
+    dt = time.perf_counter() - t0
+    B, H = x.q.shape[:2]
+    threads = min(oracle.num_threads(), B * H)
+    return dict(value=B * Ts / dt, unit="tokens/s", cores=threads, kind="oracle",
+                sample="xlstm7b_prefill_T8192, B=%d, all %d heads, first %d of 8192 tokens, fp64, "
+                       "%.1f s" % (B, H, Ts, dt))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the mLSTM heads shard across GPUs with no "
+              "communication, so the per-GPU figure is the whole story; got --gpus %d" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_recurrent_sequence_mlstm_amd import _lib as mlstm
+    from linear_recurrent_sequence_mlstm_amd.workloads import workload
+
+    dev = torch.device("cuda:0")
+    print("bench: prefill xlstm7b_prefill_T8192 steps=%d warmup=%d" % (args.steps, args.warmup),
+          file=sys.stderr, flush=True)
+    x = workload("xlstm7b_prefill_T8192")
+    pf = bench_prefill(torch, mlstm, x, args, dev)
+    print("bench: decode xlstm7b_decode_B256 steps=%d" % args.decode_steps, file=sys.stderr, flush=True)
+    dc = bench_decode(torch, mlstm, workload, args, dev)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(x, args.cpu_sample_tokens)
+
+    K = pf["K"]
+    value = pf["tokens"] * K / pf["wall"]
+    kern_s = pf["kern_ms"] * 1e-3
+    sha_cw = source_sha("chunkwise.hip", "common.h")
+    sha_st = source_sha("step.hip", "common.h")
+    roof = dict(bound="hbm", achieved=pf["bytes"] / kern_s / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_from_profiles("chunk_kernel_full", sha_cw)
+    roof["kernel"] = "chunk_kernel (per-chunk readout/update pass)"
+    roof["mfma_tflops"] = pf["flops"] / kern_s / 1e12
+    roof["mfma_frac"] = roof["mfma_tflops"] / MFMA_BF16_PEAK_TFLOPS
+    roof["algorithmic_bytes"] = pf["bytes"]
+    roof["algorithmic_flops"] = pf["flops"]
+    roof["kernel_ms"] = pf["kern_ms"]
+    dk_s = dc["step_ms"] * 1e-3
+    droof = dict(bound="hbm", achieved=dc["bytes"] / dk_s / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
+    droof["frac"] = droof["achieved"] / droof["peak"]
+    droof["traffic"] = traffic_from_profiles("step_kernel", sha_st)
+    droof["kernel"] = "step_kernel"
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": pf["wall"] / K * 1e3,
+        "gpu_ms_per_step": pf["step_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "xlstm7b_prefill_T8192", "B": 1, "H": 8, "T": 8192, "d_qk": 256,
+                   "d_v": 512, "chunk": 64, "state": "fp32", "input_sets_rotated": 4},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "decode": {
+            "workload": "xlstm7b_decode_B256",
+            "value": dc["bytes"] / dk_s / 1e9,
+            "unit": "GB/s",
+            "tokens_per_s": dc["B"] / dk_s,
+            "ms_per_step": dc["step_ms"],
+            "wall_ms_per_step": dc["wall"] / dc["S"] * 1e3,
+            "steps": dc["S"],
+            "roofline": droof,
+        },
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

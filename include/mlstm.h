@@ -72,6 +72,17 @@ int mlstm_abi_version(void);
 const char* mlstm_last_error(void);
 
 /*
+ * Profiling hook.  While set, every mlstm_chunkwise_fwd and
+ * retention_chunkwise_fwd call made on the calling thread records ev_start
+ * (a hipEvent_t) on its stream right before its main kernel (the per-chunk
+ * readout/update kernel) and ev_stop right after it, so that
+ * hipEventElapsedTime(ev_start, ev_stop) is that kernel's duration.  The
+ * caller owns the events.  (NULL, NULL) disables; giving only one of them is
+ * MLSTM_E_NULL.
+ */
+int mlstm_set_profile_events(void* ev_start, void* ev_stop);
+
+/*
  * Workspace size in bytes for mlstm_chunkwise_fwd with these arguments
  * (0 if none is needed).  Returns 0 and sets the error message for invalid
  * arguments; call mlstm_chunkwise_fwd to get the error code.

@@ -21,7 +21,8 @@ F32, BF16 = 0, 1
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 
 # Every symbol declared in include/mlstm.h.
-EXPORTS = ("mlstm_abi_version", "mlstm_last_error", "mlstm_chunkwise_workspace_bytes",
+EXPORTS = ("mlstm_abi_version", "mlstm_last_error", "mlstm_set_profile_events",
+           "mlstm_chunkwise_workspace_bytes",
            "mlstm_chunkwise_fwd", "mlstm_step", "retention_chunkwise_workspace_bytes",
            "retention_chunkwise_fwd")
 
@@ -44,6 +45,8 @@ def lib():
     L.mlstm_abi_version.restype = i
     L.mlstm_last_error.argtypes = []
     L.mlstm_last_error.restype = ctypes.c_char_p
+    L.mlstm_set_profile_events.argtypes = [vp, vp]
+    L.mlstm_set_profile_events.restype = i
     L.mlstm_chunkwise_workspace_bytes.argtypes = [i] * 7 + [i]
     L.mlstm_chunkwise_workspace_bytes.restype = sz
     L.mlstm_chunkwise_fwd.argtypes = [i] * 8 + [vp] * 6 + [fp] * 7 + [vp, vp, sz, vp]
@@ -64,6 +67,19 @@ def abi_version() -> int:
 
 def last_error() -> str:
     return lib().mlstm_last_error().decode()
+
+
+def set_profile_events(ev_start=None, ev_stop=None):
+    """Record two torch.cuda.Event objects (enable_timing=True) around the
+    main kernel of every following chunkwise call on this thread; call with
+    no arguments to stop."""
+    h0 = h1 = None
+    if ev_start is not None:
+        for ev in (ev_start, ev_stop):
+            if ev.cuda_event == 0:  # torch creates the HIP event on first record
+                ev.record()
+        h0, h1 = ctypes.c_void_p(ev_start.cuda_event), ctypes.c_void_p(ev_stop.cuda_event)
+    _check(lib().mlstm_set_profile_events(h0, h1), "mlstm_set_profile_events")
 
 
 def _check(rc: int, what: str):

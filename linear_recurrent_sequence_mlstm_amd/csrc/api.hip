@@ -14,6 +14,7 @@
 namespace {
 
 thread_local char g_err[512];
+thread_local hipEvent_t g_ev0 = nullptr, g_ev1 = nullptr;
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -117,7 +118,7 @@ int launch(const Plan& pl, mlstm::ChunkParams& p, void* workspace, size_t worksp
   p.ws_state = reinterpret_cast<float*>(ws);
   p.ws_scal = reinterpret_cast<float*>(ws + pl.off_scal);
   p.ws_min = reinterpret_cast<float*>(ws + pl.off_min);
-  const hipError_t e = pl.var.launch(p, static_cast<hipStream_t>(stream));
+  const hipError_t e = pl.var.launch(p, static_cast<hipStream_t>(stream), g_ev0, g_ev1);
   if (e != hipSuccess) return fail(MLSTM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -129,6 +130,14 @@ extern "C" {
 int mlstm_abi_version(void) { return MLSTM_ABI_VERSION; }
 
 const char* mlstm_last_error(void) { return g_err; }
+
+int mlstm_set_profile_events(void* ev_start, void* ev_stop) {
+  if ((ev_start == nullptr) != (ev_stop == nullptr))
+    return fail(MLSTM_E_NULL, "give both events or neither");
+  g_ev0 = static_cast<hipEvent_t>(ev_start);
+  g_ev1 = static_cast<hipEvent_t>(ev_stop);
+  return ok();
+}
 
 size_t mlstm_chunkwise_workspace_bytes(int B, int H, int T, int d_qk, int d_v, int num_blocks, int chunk,
                                        mlstm_dtype dt) {

@@ -51,6 +51,15 @@ __device__ __forceinline__ int perm_row<float>(int nt, int rho) {
   return nt * 16 + (rho & 3) * 4 + (rho >> 2);
 }
 
+// perm_row(nt, 4*lg + i) split into a lane part (depends on lg only) and a
+// wave-uniform part, so that state addresses need one lane offset.
+template <typename T>
+__device__ __forceinline__ int perm_row_lane(int lg) { return sizeof(T) == 2 ? lg * 8 : lg; }
+template <typename T>
+__device__ __forceinline__ constexpr int perm_row_uni(int nt, int i) {
+  return sizeof(T) == 2 ? (nt >> 1) * 32 + (nt & 1) * 4 + i : nt * 16 + i * 4;
+}
+
 // Readout A operand (rows = columns of d_v, k = features kk*K .. +K-1 of the
 // block) taken from the accumulator tiles of the state.
 template <typename T, int NT, int CT>
@@ -83,18 +92,24 @@ __device__ __forceinline__ bf16x8 scale_frag(bf16x8 x, const float* w) {
 }
 __device__ __forceinline__ float scale_frag(float x, const float* w) { return x * w[0]; }
 
-template <typename T, int DQK, int NB, int WC, int L>
+template <typename T, int DQK, int NB, int WC, int NRG, int L>
 struct ChunkCfg {
   static constexpr int K = Mma<T>::K;
   static constexpr int KL = Mma<T>::KL;
-  static constexpr int DQKB = DQK / NB;
-  static constexpr int NT = DQKB / 16;
-  static constexpr int CT = WC / 16;
-  static constexpr int W = 4 * WC;
-  static constexpr int NJT = L / 16;
-  static constexpr int NKL = L / K;
-  static constexpr int NKQ = DQK / K;
-  static constexpr int NKQB = DQKB / K;
+  static constexpr int NW = 4 * NRG;              // waves per work-group
+  static constexpr int NTH = 64 * NW;             // threads per work-group
+  static constexpr int DQKB = DQK / NB;           // rows of a memory block
+  static constexpr int RPW = DQKB / NRG;          // state rows per wave
+  static constexpr int NT = RPW / 16;             // state row tiles per wave
+  static constexpr int CT = WC / 16;              // state column tiles per wave
+  static constexpr int W = 4 * WC;                // d_v columns per work-group
+  static constexpr int NJT = L / 16;              // 16-token tiles per chunk
+  static constexpr int JPW = NJT / NRG;           // token tiles finished per wave
+  static constexpr int NKL = L / K;               // token k-blocks per chunk
+  static constexpr int NKQ = DQK / K;             // feature k-blocks of a head
+  static constexpr int NKQB = DQKB / K;           // feature k-blocks of a block
+  static constexpr int NKQR = RPW / K;            // feature k-blocks of a wave's rows
+  static constexpr int NTQK = NJT * (NJT + 1) / 2;  // causal score tiles
   static constexpr int VE = 16 / (int)sizeof(T);  // elements per 16 bytes
   static constexpr int PAD = VE;
   static constexpr int QS = DQK + PAD;            // row stride of sQ
@@ -103,13 +118,13 @@ struct ChunkCfg {
   static constexpr int NQU = L * DQK / VE;
   static constexpr int NKU = (L / 4) * (DQK / VE);
   static constexpr int NVU = (L / 4) * (W / VE);
-  static constexpr int QIT = (NQU + 255) / 256;
-  static constexpr int KIT = (NKU + 255) / 256;
-  static constexpr int VIT = (NVU + 255) / 256;
+  static constexpr int QIT = (NQU + NTH - 1) / NTH;
+  static constexpr int KIT = (NKU + NTH - 1) / NTH;
+  static constexpr int VIT = (NVU + NTH - 1) / NTH;
   static_assert(DQK % NB == 0, "d_qk % nb");
-  static_assert(DQKB % (2 * 16) == 0 || sizeof(T) == 4, "bf16 path needs 32-row blocks");
-  static_assert(DQKB % 16 == 0, "block rows multiple of 16");
+  static_assert(RPW % (sizeof(T) == 2 ? 32 : 16) == 0, "state rows per wave");
   static_assert(L % K == 0 && L % 16 == 0 && L <= 64, "chunk length");
+  static_assert(NJT % NRG == 0, "token tiles per row group");
   static_assert(WC % 16 == 0, "wave columns");
   static constexpr size_t lds_bytes(bool full, bool ret) {
     size_t b = 0;
@@ -120,34 +135,67 @@ struct ChunkCfg {
     if (full) {
       b += (size_t)L * QS * sizeof(T);           // sQ
       b += (size_t)NB * L * TS * sizeof(T);      // sP
-      b += 5 * L * 4;                            // den partials
+      b += (size_t)(NJT + 1) * L * 4;            // den partials
+      if (NRG > 1) b += (size_t)4 * NJT * CT * 64 * 16;  // readout exchange
     }
     return b;
   }
 };
 
-template <typename T, int DQK, int NB, int WC, int L, bool RET, bool FULL>
-__global__ __launch_bounds__(256) void chunk_kernel(ChunkParams p) {
-  using C = ChunkCfg<T, DQK, NB, WC, L>;
+// A operand of the score MFMA (rows = tokens, k = features f0 .. f0+KL-1) read
+// from the feature-major copy of K.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag load_k_rows(const T* sKt, int TS, int f0, int tok);
+template <>
+__device__ __forceinline__ bf16x8 load_k_rows<__bf16>(const __bf16* sKt, int TS, int f0, int tok) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = sKt[(f0 + e) * TS + tok];
+  return r;
+}
+template <>
+__device__ __forceinline__ float load_k_rows<float>(const float* sKt, int TS, int f0, int tok) {
+  return sKt[f0 * TS + tok];
+}
+
+// Main kernel.  FULL = true: pass 3 (readout, outputs, update).  FULL = false:
+// pass 1 (update only, from a zero state).
+//
+// Work-group = 4 column groups x NRG row groups of waves.  Wave (cg, rg) owns
+// columns [cg*WC, cg*WC+WC) of the work-group's d_v slice and state rows
+// [rg*RPW, rg*RPW+RPW) of their memory block.  With NRG = 2 the readout of a
+// column group is split over its two waves by rows; each wave finishes half of
+// the token tiles and the two partial sums meet in LDS (sX).
+template <typename T, int DQK, int NB, int WC, int NRG, int L, bool RET, bool FULL>
+__global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
+  using C = ChunkCfg<T, DQK, NB, WC, NRG, L>;
   using M = Mma<T>;
   typedef typename M::frag frag;
-  constexpr int K = C::K, KL = C::KL, DQKB = C::DQKB, NT = C::NT, CT = C::CT;
-  constexpr int W = C::W, NJT = C::NJT, NKL = C::NKL, NKQ = C::NKQ, NKQB = C::NKQB;
+  constexpr int K = C::K, KL = C::KL, DQKB = C::DQKB, NT = C::NT, CT = C::CT, NW = C::NW;
+  constexpr int NTH = C::NTH, RPW = C::RPW, JPW = C::JPW;
+  constexpr int W = C::W, NJT = C::NJT, NKL = C::NKL, NKQ = C::NKQ, NKQB = C::NKQB, NKQR = C::NKQR;
   constexpr int VE = C::VE, QS = C::QS, TS = C::TS;
+  constexpr unsigned ES = sizeof(T);
+  constexpr bool XCH = FULL && NRG > 1;
 
-  __shared__ __attribute__((aligned(16))) T sKt[DQK * TS];
-  __shared__ __attribute__((aligned(16))) T sVt[W * TS];
-  __shared__ __attribute__((aligned(16))) T sQ[FULL ? L * QS : 8];
+  __shared__ __attribute__((aligned(16))) T sKt[DQK * TS];  // K, feature-major
+  __shared__ __attribute__((aligned(16))) T sVt[W * TS];    // V slice, feature-major
+  __shared__ __attribute__((aligned(16))) T sQ[FULL ? L * QS : 8];   // Q, token-major
   __shared__ __attribute__((aligned(16))) T sP[FULL ? NB * L * TS : 8];
+  __shared__ __attribute__((aligned(16))) f32x4 sX[XCH ? 4 * NJT * CT * 64 : 1];
   __shared__ __attribute__((aligned(16))) T sNh[RET ? 8 : 2 * DQK];
   __shared__ float sNf[RET ? 4 : DQK];
   __shared__ float sA2[L], sM2[L], sRS[L], sCL[L], sBT[L], sW[L];
-  __shared__ float sDenPart[FULL ? 4 * L : 4];
+  __shared__ float sDenPart[FULL ? NJT * L : 4];
   __shared__ float sDenInter[FULL ? L : 4];
   __shared__ float sAlpha;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  // The wave index must be known to be wave-uniform: branches on it guard
+  // MFMA instructions, which do not honour a partial EXEC mask.
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cg = w & 3, rg = w >> 2;
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int BH = p.B * p.H;
   int idx = blockIdx.x;
   const int bh = idx % BH;
@@ -159,17 +207,24 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkParams p) {
   const size_t CS = (size_t)DQK * DV / NB;
   const size_t NSTATE = CS + (RET ? 0 : DQK);
 
-  const int wcol0 = slice * W + w * WC;  // first global d_v column of this wave
-  const int blk = wcol0 / DVB;           // memory block of this wave
-  const int wcl0 = wcol0 - blk * DVB;    // first column inside the block
-  const int rb0 = blk * DQKB;            // first feature row of the block
+  const int wcol0 = slice * W + cg * WC;  // first global d_v column of this wave
+  const int blk = wcol0 / DVB;            // memory block of this wave
+  const int wcl0 = wcol0 - blk * DVB;     // first column inside the block
+  const int rrow0 = rg * RPW;             // first state row of this wave inside the block
+  const int rb0 = blk * DQKB + rrow0;     // ... as a feature index of the head
+  const int jt0 = rg * JPW;               // first token tile finished by this wave
 
-  const T* __restrict__ gq = static_cast<const T*>(p.q) + (size_t)bh * T_ * DQK;
-  const T* __restrict__ gk = static_cast<const T*>(p.k) + (size_t)bh * T_ * DQK;
-  const T* __restrict__ gv = static_cast<const T*>(p.v) + (size_t)bh * T_ * DV;
-  const T* __restrict__ gi = RET ? nullptr : static_cast<const T*>(p.i_pre) + (size_t)bh * T_;
-  const T* __restrict__ gf = RET ? nullptr : static_cast<const T*>(p.f_pre) + (size_t)bh * T_;
-  const T* __restrict__ go = (FULL && p.o_pre) ? static_cast<const T*>(p.o_pre) + (size_t)bh * T_ * DV : nullptr;
+  // buffer resources over this (batch, head): reads past T return zero
+  const auto rq = make_rsrc(static_cast<const T*>(p.q) + (size_t)bh * T_ * DQK, (unsigned)T_ * DQK * ES);
+  const auto rk = make_rsrc(static_cast<const T*>(p.k) + (size_t)bh * T_ * DQK, (unsigned)T_ * DQK * ES);
+  const auto rv = make_rsrc(static_cast<const T*>(p.v) + (size_t)bh * T_ * DV, (unsigned)T_ * DV * ES);
+  const auto ri = make_rsrc(RET ? nullptr : static_cast<const T*>(p.i_pre) + (size_t)bh * T_,
+                            RET ? 0u : (unsigned)T_ * ES);
+  const auto rf = make_rsrc(RET ? nullptr : static_cast<const T*>(p.f_pre) + (size_t)bh * T_,
+                            RET ? 0u : (unsigned)T_ * ES);
+  const bool has_o = FULL && p.o_pre != nullptr;
+  const auto ro = make_rsrc(has_o ? static_cast<const T*>(p.o_pre) + (size_t)bh * T_ * DV : nullptr,
+                            has_o ? (unsigned)T_ * DV * ES : 0u);
   T* __restrict__ gh = FULL ? static_cast<T*>(p.h) + (size_t)bh * T_ * DV : nullptr;
   const float bias = (!RET && p.bias) ? p.bias[hd] : 0.f;
   float ret_lg2 = 0.f;
@@ -182,18 +237,17 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkParams p) {
   f32x4 st[NT][CT];
   const float* Sin = nullptr;
   if (FULL && (sc > 0 || p.has_init)) Sin = p.ws_state + ((size_t)bh * p.NS + sc) * NSTATE;
+  // state element (nt, ct, i) of this lane sits at soff + (uni(nt,i)*DVB + ct*16)
+  const int soff = blk * DQKB * DVB + (rrow0 + perm_row_lane<T>(lg)) * DVB + wcl0 + lr;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = perm_row<T>(nt, 4 * lg + i);
-        const int col = wcl0 + ct * 16 + lr;
-        st[nt][ct][i] = Sin ? Sin[(size_t)blk * DQKB * DVB + (size_t)row * DVB + col] : 0.f;
-      }
+      for (int i = 0; i < 4; ++i)
+        st[nt][ct][i] = Sin ? Sin[soff + perm_row_uni<T>(nt, i) * DVB + ct * 16] : 0.f;
   if constexpr (!RET) {
-    for (int r = tid; r < DQK; r += 256) {
+    for (int r = tid; r < DQK; r += NTH) {
       const float x = Sin ? Sin[CS + r] : 0.f;
       sNf[r] = x;
       const T hi = from_f32<T>(x);
@@ -203,60 +257,60 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkParams p) {
   }
   if constexpr (FULL) {
     // masked (l > j) tiles of P and their den partials are never written
-    for (int e = tid; e < NB * L * TS; e += 256) sP[e] = from_f32<T>(0.f);
-    for (int e = tid; e < 4 * L; e += 256) sDenPart[e] = 0.f;
+    for (int e = tid; e < NB * L * TS; e += NTH) sP[e] = from_f32<T>(0.f);
+    for (int e = tid; e < NJT * L; e += NTH) sDenPart[e] = 0.f;
   }
+  // The registers hold S^ = S~ / 2^{sig}: the per-chunk decay of the state is
+  // folded into sig (a wave-uniform scalar) instead of multiplying every
+  // state element; new contributions are weighted by 2^{-sig}, the readout by
+  // 2^{sig}.  When sig drops below -64 the registers are rescaled once.
+  float sig = 0.f;
   // stabiliser carried by wave 0 (log2 units)
   float m_prev = FULL ? p.ws_min[(size_t)bh * p.NS + sc] : -INFINITY;
   float a_total = 0.f;
 
   // ------------------------------------------------------ staging registers
-  Vec16<T> rq[FULL ? C::QIT : 1];
-  Vec16<T> rk[C::KIT][4];
-  Vec16<T> rv[C::VIT][4];
+  // All global loads are unconditional buffer loads (units past the end of a
+  // staging loop reload a valid unit and are not stored).  The next chunk's
+  // loads are issued during the current chunk and written to LDS at its end,
+  // so no staging register lives across a loop iteration.
+  Vec16<T> rgq[FULL ? C::QIT : 1];
+  Vec16<T> rgk[C::KIT][4];
+  Vec16<T> rgv[C::VIT][4];
   float rgi = 0.f, rgf = 0.f;
 
-  auto load_stage = [&](int c) {
-    const int t0 = c * L;
+  auto load_q = [&](int c) {
+    const unsigned t0 = (unsigned)c * L;
     if constexpr (FULL) {
 #pragma unroll
       for (int it = 0; it < C::QIT; ++it) {
-        const int u = tid + it * 256;
-        if (u < C::NQU) {
-          const int j = u / (DQK / VE), col = (u % (DQK / VE)) * VE;
-          rq[it] = (t0 + j < T_) ? load16(gq + (size_t)(t0 + j) * DQK + col) : zero16<T>();
-        }
+        const int u = (tid + it * NTH) % C::NQU;
+        const unsigned j = u / (DQK / VE), col = (u % (DQK / VE)) * VE;
+        rgq[it] = bload16<T>(rq, ((t0 + j) * DQK + col) * ES);
       }
     }
+  };
+
+  auto load_kv = [&](int c) {
+    const unsigned t0 = (unsigned)c * L;
 #pragma unroll
     for (int it = 0; it < C::KIT; ++it) {
-      const int u = tid + it * 256;
-      if (u < C::NKU) {
-        const int tg = u % (L / 4), fg = u / (L / 4);
+      const int u = (tid + it * NTH) % C::NKU;
+      const unsigned tg = u % (L / 4), fg = u / (L / 4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = t0 + 4 * tg + r;
-          rk[it][r] = (t < T_) ? load16(gk + (size_t)t * DQK + fg * VE) : zero16<T>();
-        }
-      }
+      for (int r = 0; r < 4; ++r) rgk[it][r] = bload16<T>(rk, ((t0 + 4 * tg + r) * DQK + fg * VE) * ES);
     }
 #pragma unroll
     for (int it = 0; it < C::VIT; ++it) {
-      const int u = tid + it * 256;
-      if (u < C::NVU) {
-        const int tg = u % (L / 4), fg = u / (L / 4);
+      const int u = (tid + it * NTH) % C::NVU;
+      const unsigned tg = u % (L / 4), fg = u / (L / 4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = t0 + 4 * tg + r;
-          rv[it][r] = (t < T_) ? load16(gv + (size_t)t * DV + slice * W + fg * VE) : zero16<T>();
-        }
-      }
+      for (int r = 0; r < 4; ++r)
+        rgv[it][r] = bload16<T>(rv, ((t0 + 4 * tg + r) * DV + slice * W + fg * VE) * ES);
     }
     if constexpr (!RET) {
-      if (w == 0 && lane < L && t0 + lane < T_) {
-        rgi = to_f32(gi[t0 + lane]);
-        rgf = to_f32(gf[t0 + lane]);
-      }
+      rgi = bload1<T>(ri, (t0 + (lane & (L - 1))) * ES);
+      rgf = bload1<T>(rf, (t0 + (lane & (L - 1))) * ES);
     }
   };
 
@@ -264,35 +318,33 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkParams p) {
     if constexpr (FULL) {
 #pragma unroll
       for (int it = 0; it < C::QIT; ++it) {
-        const int u = tid + it * 256;
+        const int u = tid + it * NTH;
         if (u < C::NQU) {
           const int j = u / (DQK / VE), col = (u % (DQK / VE)) * VE;
-          *reinterpret_cast<uint4*>(&sQ[j * QS + col]) = *reinterpret_cast<const uint4*>(rq[it].v);
+          *reinterpret_cast<uint4*>(&sQ[j * QS + col]) = *reinterpret_cast<const uint4*>(rgq[it].v);
         }
       }
     }
 #pragma unroll
     for (int it = 0; it < C::KIT; ++it) {
-      const int u = tid + it * 256;
+      const int u = tid + it * NTH;
       if (u < C::NKU) {
         const int tg = u % (L / 4), fg = u / (L / 4);
 #pragma unroll
-        for (int e = 0; e < VE; ++e) {
-          store4(&sKt[(fg * VE + e) * TS + 4 * tg], rk[it][0].v[e], rk[it][1].v[e], rk[it][2].v[e],
-                 rk[it][3].v[e]);
-        }
+        for (int e = 0; e < VE; ++e)
+          store4(&sKt[(fg * VE + e) * TS + 4 * tg], rgk[it][0].v[e], rgk[it][1].v[e], rgk[it][2].v[e],
+                 rgk[it][3].v[e]);
       }
     }
 #pragma unroll
     for (int it = 0; it < C::VIT; ++it) {
-      const int u = tid + it * 256;
+      const int u = tid + it * NTH;
       if (u < C::NVU) {
         const int tg = u % (L / 4), fg = u / (L / 4);
 #pragma unroll
-        for (int e = 0; e < VE; ++e) {
-          store4(&sVt[(fg * VE + e) * TS + 4 * tg], rv[it][0].v[e], rv[it][1].v[e], rv[it][2].v[e],
-                 rv[it][3].v[e]);
-        }
+        for (int e = 0; e < VE; ++e)
+          store4(&sVt[(fg * VE + e) * TS + 4 * tg], rgv[it][0].v[e], rgv[it][1].v[e], rgv[it][2].v[e],
+                 rgv[it][3].v[e]);
       }
     }
   };
@@ -335,167 +387,196 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkParams p) {
       sBT[lane] = bias * cl;
       sW[lane] = exp2_fast(a - ML);
     }
-    if (lane == 0) sAlpha = exp2_fast(m_prev - ML);
+    if (lane == 0) sAlpha = m_prev - ML;  // log2 of the state decay over the chunk
     m_prev = bL + ML;
     a_total += bL;
   };
 
-  load_stage(c_begin);
+  // Prime the first chunk.
+  load_q(c_begin);
+  load_kv(c_begin);
+  store_stage();
+  if (w == 0) gates(c_begin);
 
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * L;
-    store_stage();
-    if (w == 0) gates(c);
     __syncthreads();  // B1: chunk staged, gate factors ready
-    if (c + 1 < c_end) load_stage(c + 1);
+    const bool more = c + 1 < c_end;
+    // pass 1 prefetches at the top; pass 3 after its second barrier, so that
+    // the readout (its register peak) holds no staging registers
+    if (!FULL && more) load_kv(c + 1);
 
     // update of the state is needed unless this is the last chunk of a
     // superchunk whose end state nobody reads
-    const bool need_update = !FULL || (c + 1 < c_end) || (sc == p.NS - 1);
+    const bool need_update = !FULL || more || (sc == p.NS - 1);
 
-    frag vf[CT][NKL];  // V^T fragments of this wave's columns
+    frag vf[CT][NKL];  // V^T fragments of this wave's columns (loaded after phase B)
+    auto load_vf = [&]() {
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int kb = 0; kb < NKL; ++kb)
-        vf[ct][kb] = M::load(&sVt[(w * WC + ct * 16 + lr) * TS + kb * K + KL * lg]);
+        for (int kb = 0; kb < NKL; ++kb)
+          vf[ct][kb] = M::load(&sVt[(cg * WC + ct * 16 + lr) * TS + kb * K + KL * lg]);
+    };
+    if constexpr (!FULL) load_vf();
 
     if constexpr (FULL) {
       // ---------------------------------------------------------- phase B
-      f32x4 acc[NJT][CT];
-      f32x4 pt[NB][NJT];
-      f32x4 pn = {0.f, 0.f, 0.f, 0.f};
+      // causal score tiles (key tile lt, query tile jt), spread over the waves
 #pragma unroll
-      for (int jt = 0; jt < NJT; ++jt) {
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) acc[jt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int be = 0; be < NB; ++be) pt[be][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      const bool do_qk = w < NJT;
-      frag kf[NKQ];
-      if (do_qk) {
-        const int t = t0 + w * 16 + lr;
-#pragma unroll
-        for (int kb = 0; kb < NKQ; ++kb)
-          kf[kb] = (t < T_) ? M::load(gk + (size_t)t * DQK + kb * K + KL * lg) : M::zero();
-      }
-#pragma unroll
-      for (int jt = 0; jt < NJT; ++jt) {
-        frag qf[NKQ];
-#pragma unroll
-        for (int kb = 0; kb < NKQ; ++kb) qf[kb] = M::load(&sQ[(jt * 16 + lr) * QS + kb * K + KL * lg]);
-        // readout of the state at the chunk start: D[c][j] += S~[:, c] . q_j
-#pragma unroll
-        for (int be = 0; be < NB; ++be) {
-          if (be == blk) {
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-              for (int kk = 0; kk < NKQB; ++kk)
-                acc[jt][ct] = M::mma(StateFrag<T, NT, CT>::get(st, kk, ct), qf[be * NKQB + kk], acc[jt][ct]);
+      for (int ti = 0; ti < C::NTQK; ++ti) {
+        if (w == ti % NW) {
+          int lt = 0, jt = ti, rem = NJT;
+          while (jt >= rem) {  // tile index -> (lt, jt) with lt <= jt
+            jt -= rem;
+            ++lt;
+            --rem;
           }
-        }
-        // scores of key tile w against query tile jt, per memory block
-        if (do_qk && jt >= w) {
+          jt += lt;
+          f32x4 pt[NB];
 #pragma unroll
-          for (int be = 0; be < NB; ++be)
+          for (int be = 0; be < NB; ++be) {
+            pt[be] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < NKQB; ++kk)
-              pt[be][jt] = M::mma(kf[be * NKQB + kk], qf[be * NKQB + kk], pt[be][jt]);
+            for (int kk = 0; kk < NKQB; ++kk) {
+              const int kb = be * NKQB + kk;
+              const frag kf = load_k_rows<T>(sKt, TS, kb * K + KL * lg, lt * 16 + lr);
+              const frag qj = M::load(&sQ[(jt * 16 + lr) * QS + kb * K + KL * lg]);
+              pt[be] = M::mma(kf, qj, pt[be]);
+              if (kk & 1) __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          // decay factors, P to LDS, den partial sums
+          const int j = jt * 16 + lr;
+          const float m2 = sM2[j];
+          float fac[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int l = lt * 16 + 4 * lg + i;
+            fac[i] = (l <= j) ? exp2_fast(sA2[l] - m2) : 0.f;
+          }
+          float dsum = 0.f;
+#pragma unroll
+          for (int be = 0; be < NB; ++be) {
+            T pv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float x = pt[be][i] * fac[i];
+              dsum += x;
+              pv[i] = from_f32<T>(x);
+            }
+            store4(&sP[(be * L + j) * TS + lt * 16 + 4 * lg], pv[0], pv[1], pv[2], pv[3]);
+          }
+          dsum += __shfl_xor(dsum, 16, 64);
+          dsum += __shfl_xor(dsum, 32, 64);
+          if (lg == 0) sDenPart[lt * L + j] = dsum;
         }
-        // n~ . q_j for query tile jt == w, n~ split in hi + lo parts
-        if constexpr (!RET) {
-          if (jt == w) {
+      }
+      // n~ . q_j per query tile, n~ split in hi + lo parts (last waves)
+      if constexpr (!RET) {
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt) {
+          if (w == NW - 1 - (jt % NW)) {
+            f32x4 pn = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < NKQ; ++kb) {
               frag nf = M::load(&sNh[(lr & 1) * DQK + kb * K + KL * lg]);
               if (lr > 1) nf = M::zero();
-              pn = M::mma(nf, qf[kb], pn);
+              pn = M::mma(nf, M::load(&sQ[(jt * 16 + lr) * QS + kb * K + KL * lg]), pn);
+              if (kb & 1) __builtin_amdgcn_sched_barrier(0);
             }
+            if (lg == 0) sDenInter[jt * 16 + lr] = pn[0] + pn[1];
           }
         }
       }
-      // decay mask and factors, P to LDS, den partial sums
-      if (do_qk) {
-        float a2[4];
+      // readout of the state at the chunk start over this wave's rows:
+      // acc[jt][ct] = S~[rows, c]^T q_j
+      f32x4 acc[NJT][CT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a2[i] = sA2[w * 16 + 4 * lg + i];
+      for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
-        for (int jt = 0; jt < NJT; ++jt) {
-          if (jt >= w) {
-            const int j = jt * 16 + lr;
-            const float m2 = sM2[j];
-            float fac[4];
+        for (int ct = 0; ct < CT; ++ct) acc[jt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int kq0 = rb0 / K;  // first feature k-block of this wave's rows
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int l = w * 16 + 4 * lg + i;
-              fac[i] = (l <= j) ? exp2_fast(a2[i] - m2) : 0.f;
-            }
-            float dsum = 0.f;
+      for (int kk = 0; kk < NKQR; ++kk) {
+        frag qf[NJT];
 #pragma unroll
-            for (int be = 0; be < NB; ++be) {
-              T pv[4];
+        for (int jt = 0; jt < NJT; ++jt)
+          qf[jt] = M::load(&sQ[(jt * 16 + lr) * QS + (kq0 + kk) * K + KL * lg]);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const float x = pt[be][jt][i] * fac[i];
-                dsum += x;
-                pv[i] = from_f32<T>(x);
-              }
-              store4(&sP[(be * L + j) * TS + w * 16 + 4 * lg], pv[0], pv[1], pv[2], pv[3]);
-            }
-            dsum += __shfl_xor(dsum, 16, 64);
-            dsum += __shfl_xor(dsum, 32, 64);
-            if (lg == 0) sDenPart[w * L + j] = dsum;
-          }
+        for (int ct = 0; ct < CT; ++ct) {
+          const frag sf = StateFrag<T, NT, CT>::get(st, kk, ct);
+#pragma unroll
+          for (int jt = 0; jt < NJT; ++jt) acc[jt][ct] = M::mma(sf, qf[jt], acc[jt][ct]);
         }
-        if constexpr (!RET) {
-          if (lg == 0) sDenInter[w * 16 + lr] = pn[0] + pn[1];
-        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __syncthreads();  // B2: P and den partials ready
+      // hand the readout partials of the other row group's token tiles over
+      if constexpr (XCH) {
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt)
+          if (jt / JPW != rg)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) sX[((cg * NJT + jt) * CT + ct) * 64 + lane] = acc[jt][ct];
+      }
+      __syncthreads();  // B2: P, den partials and readout partials ready
+      if (more) {
+        load_kv(c + 1);
+        load_q(c + 1);
+      }
+      load_vf();
 
       // ---------------------------------------------------------- phase C
 #pragma unroll
-      for (int jt = 0; jt < NJT; ++jt) {
+      for (int jj = 0; jj < JPW; ++jj) {
+        const int jt = jt0 + jj;  // runtime, wave-uniform
+        f32x4 o_acc[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          // select acc[jt][ct] with a compile-time index
+          f32x4 a = acc[0][ct];
+#pragma unroll
+          for (int t = 1; t < NJT; ++t)
+            if (jt == t) a = acc[t][ct];
+          if constexpr (XCH) a += sX[((cg * NJT + jt) * CT + ct) * 64 + lane];
+          o_acc[ct] = a;
+        }
         const int j = jt * 16 + lr;
         const float rs = sRS[j];
+        const float rs_state = rs * exp2_fast(sig);
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) acc[jt][ct] *= rs;
+        for (int ct = 0; ct < CT; ++ct) o_acc[ct] *= rs_state;
 #pragma unroll
         for (int kb = 0; kb < NKL; ++kb) {
           if (kb * K <= jt * 16 + 15) {
             const frag pf = M::load(&sP[(blk * L + jt * 16 + lr) * TS + kb * K + KL * lg]);
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) acc[jt][ct] = M::mma(vf[ct][kb], pf, acc[jt][ct]);
+            for (int ct = 0; ct < CT; ++ct) o_acc[ct] = M::mma(vf[ct][kb], pf, o_acc[ct]);
           }
         }
+        float inv;
+        if constexpr (RET) {
+          inv = 1.f;
+        } else {
+          float den = rs * sDenInter[j] + sBT[j];
+#pragma unroll
+          for (int t = 0; t < NJT; ++t) den += sDenPart[t * L + j];
+          inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), sCL[j]));
+        }
         if (t0 + j < T_) {
-          float inv;
-          if constexpr (RET) {
-            inv = 1.f;
-          } else {
-            const float den = rs * sDenInter[j] + sDenPart[j] + sDenPart[L + j] + sDenPart[2 * L + j] +
-                              sDenPart[3 * L + j] + sBT[j];
-            inv = 1.f / fmaxf(fabsf(den), sCL[j]);
-          }
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) {
             const int col = wcol0 + ct * 16 + 4 * lg;
-            const size_t off = (size_t)(t0 + j) * DV + col;
             float o[4] = {1.f, 1.f, 1.f, 1.f};
-            if (go) {
+            if (has_o) {
+              bload4<T>(ro, ((unsigned)(t0 + j) * DV + col) * ES, o);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) o[i] = sigmoidf_(to_f32(go[off + i]));
+              for (int i = 0; i < 4; ++i) o[i] = sigmoidf_(o[i]);
             }
             T hv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) hv[i] = from_f32<T>(o[i] * acc[jt][ct][i] * inv);
-            if constexpr (sizeof(T) == 2) {
-              *reinterpret_cast<uint2*>(gh + off) = *reinterpret_cast<const uint2*>(hv);
-            } else {
-              *reinterpret_cast<uint4*>(gh + off) = *reinterpret_cast<const uint4*>(hv);
-            }
+            for (int i = 0; i < 4; ++i) hv[i] = from_f32<T>(o[i] * o_acc[ct][i] * inv);
+            store4(gh + (size_t)(t0 + j) * DV + col, hv[0], hv[1], hv[2], hv[3]);
           }
         }
       }
@@ -503,16 +584,23 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkParams p) {
 
     // ------------------------------------------------------- state update
     if (need_update) {
-      const float alpha = sAlpha;
+      const float la = sAlpha;
+      const float alpha = exp2_fast(la);
+      sig += la;
+      if (sig < -64.f) {  // wave-uniform: rescale the registers, rarely
+        const float f = exp2_fast(sig);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) st[nt][ct] *= alpha;
+          for (int ct = 0; ct < CT; ++ct) st[nt][ct] *= f;
+        sig = 0.f;
+      }
+      const float wscale = exp2_fast(-sig);
 #pragma unroll
       for (int kb = 0; kb < NKL; ++kb) {
         float wl[KL];
 #pragma unroll
-        for (int e = 0; e < KL; ++e) wl[e] = sW[kb * K + KL * lg + e];
+        for (int e = 0; e < KL; ++e) wl[e] = sW[kb * K + KL * lg + e] * wscale;
         frag wv[CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) wv[ct] = scale_frag(vf[ct][kb], wl);
@@ -524,13 +612,14 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkParams p) {
         }
       }
       if constexpr (!RET) {
-        for (int r = tid; r < DQK; r += 256) {
+        for (int r = tid; r < DQK; r += NTH) {
           float x = alpha * sNf[r];
 #pragma unroll
           for (int l = 0; l < L; l += VE) {
             const Vec16<T> kv = load16(&sKt[r * TS + l]);
 #pragma unroll
             for (int e = 0; e < VE; ++e) x += sW[l + e] * to_f32(kv.v[e]);
+            __builtin_amdgcn_sched_barrier(0);
           }
           sNf[r] = x;
           const T hi = from_f32<T>(x);
@@ -540,30 +629,32 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkParams p) {
       }
     }
     __syncthreads();  // B3: LDS free for the next chunk
+    if (more) {
+      store_stage();
+      if (w == 0) gates(c + 1);
+    }
   }
 
   // ---------------------------------------------------------------- outputs
   float* Sdst = nullptr;
   if (!FULL) Sdst = p.ws_state + ((size_t)bh * p.NS + sc + 1) * NSTATE;
-  else if (sc == p.NS - 1) Sdst = p.C_out;  // [B,H,NB,DQKB,DVB]
-  if (FULL && Sdst) Sdst += (size_t)bh * CS;
+  else if (sc == p.NS - 1 && p.C_out) Sdst = p.C_out + (size_t)bh * CS;  // [B,H,NB,DQKB,DVB]
   if (Sdst) {
+    const float f = exp2_fast(sig);
+    int so = soff;
+    asm volatile("" : "+v"(so));  // recompute addresses here, do not keep the prologue's
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = perm_row<T>(nt, 4 * lg + i);
-          const int col = wcl0 + ct * 16 + lr;
-          Sdst[(size_t)blk * DQKB * DVB + (size_t)row * DVB + col] = st[nt][ct][i];
-        }
+        for (int i = 0; i < 4; ++i) Sdst[so + perm_row_uni<T>(nt, i) * DVB + ct * 16] = st[nt][ct][i] * f;
   }
   if (slice == 0) {
     if (!FULL) {
       float* nd = p.ws_state + ((size_t)bh * p.NS + sc + 1) * NSTATE + CS;
       if constexpr (!RET)
-        for (int r = tid; r < DQK; r += 256) nd[r] = sNf[r];
+        for (int r = tid; r < DQK; r += NTH) nd[r] = sNf[r];
       if (tid == 0) {
         p.ws_scal[((size_t)bh * p.NS + sc) * 2 + 0] = a_total;
         p.ws_scal[((size_t)bh * p.NS + sc) * 2 + 1] = m_prev;
@@ -571,7 +662,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(ChunkParams p) {
     } else if (sc == p.NS - 1) {
       if constexpr (!RET) {
         if (p.n_out)
-          for (int r = tid; r < DQK; r += 256) p.n_out[(size_t)bh * DQK + r] = sNf[r];
+          for (int r = tid; r < DQK; r += NTH) p.n_out[(size_t)bh * DQK + r] = sNf[r];
       }
       if (tid == 0 && p.m_out) p.m_out[bh] = m_prev * kLn2;
     }
@@ -622,18 +713,19 @@ __global__ __launch_bounds__(256) void superchunk_scan_kernel(ScanParams p) {
   }
 }
 
-template <typename T, int DQK, int NB, int WC, int L, bool RET>
+template <typename T, int DQK, int NB, int WC, int NRG, int L, bool RET>
 size_t chunk_lds_bytes() {
-  return ChunkCfg<T, DQK, NB, WC, L>::lds_bytes(true, RET);
+  return ChunkCfg<T, DQK, NB, WC, NRG, L>::lds_bytes(true, RET);
 }
 
-template <typename T, int DQK, int NB, int WC, int L, bool RET>
-hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream) {
+template <typename T, int DQK, int NB, int WC, int NRG, int L, bool RET>
+hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  constexpr int NTH = 256 * NRG;
   const int BH = p.B * p.H;
   const size_t CS = (size_t)DQK * p.DV / NB;
   if (p.NS > 1) {
     dim3 g1((unsigned)(BH * p.nslices * (p.NS - 1)));
-    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, L, RET, false>), g1, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, L, RET, false>), g1, dim3(NTH), 0, stream, p);
   }
   ScanParams s;
   s.NS = p.NS;
@@ -650,34 +742,37 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream) {
   dim3 g2((unsigned)((nstate / 4 + 255) / 256), (unsigned)BH);
   hipLaunchKernelGGL((superchunk_scan_kernel<RET>), g2, dim3(256), 0, stream, s);
   dim3 g3((unsigned)(BH * p.nslices * p.NS));
-  hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, L, RET, true>), g3, dim3(256), 0, stream, p);
-  return hipGetLastError();
+  if (ev0) (void)hipEventRecord(ev0, stream);
+  hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, L, RET, true>), g3, dim3(NTH), 0, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (ev1) (void)hipEventRecord(ev1, stream);
+  return e;
 }
 
 // ------------------------------------------------------------ dispatch table
+// (dtype, d_qk, num_blocks, columns per wave, row groups, chunk, retention)
 #define MLSTM_CHUNK_VARIANTS(X)            \
-  X(__bf16, 64, 1, 16, 64, false)          \
-  X(__bf16, 64, 2, 16, 64, false)          \
-  X(__bf16, 64, 1, 16, 32, false)          \
-  X(__bf16, 128, 1, 32, 64, false)         \
-  X(__bf16, 256, 1, 32, 64, false)         \
-  X(__bf16, 256, 1, 16, 64, false)         \
-  X(__bf16, 256, 2, 16, 64, false)         \
-  X(float, 64, 1, 16, 64, false)           \
-  X(float, 64, 1, 16, 32, false)           \
-  X(float, 64, 1, 16, 16, false)           \
-  X(float, 64, 2, 16, 64, false)           \
-  X(__bf16, 64, 1, 16, 64, true)           \
-  X(__bf16, 64, 1, 16, 32, true)           \
-  X(__bf16, 128, 1, 32, 64, true)          \
-  X(float, 64, 1, 16, 64, true)
+  X(__bf16, 64, 1, 16, 1, 64, false)       \
+  X(__bf16, 64, 2, 16, 1, 64, false)       \
+  X(__bf16, 64, 1, 16, 1, 32, false)       \
+  X(__bf16, 128, 1, 32, 2, 64, false)      \
+  X(__bf16, 256, 1, 32, 2, 64, false)      \
+  X(__bf16, 256, 2, 16, 2, 64, false)      \
+  X(float, 64, 1, 16, 1, 64, false)        \
+  X(float, 64, 1, 16, 1, 32, false)        \
+  X(float, 64, 1, 16, 1, 16, false)        \
+  X(float, 64, 2, 16, 1, 64, false)        \
+  X(__bf16, 64, 1, 16, 1, 64, true)        \
+  X(__bf16, 64, 1, 16, 1, 32, true)        \
+  X(__bf16, 128, 1, 32, 2, 64, true)       \
+  X(float, 64, 1, 16, 1, 64, true)
 
 bool find_chunk_variant(int dtype, int dqk, int nb, int wc, int L, bool ret, ChunkVariant* out) {
-#define X(T_, DQK_, NB_, WC_, L_, RET_)                                                          \
+#define X(T_, DQK_, NB_, WC_, NRG_, L_, RET_)                                                    \
   if (dtype == (sizeof(T_) == 2 ? 1 : 0) && dqk == DQK_ && nb == NB_ && wc == WC_ && L == L_ && \
       ret == RET_) {                                                                             \
-    out->launch = &launch_chunkwise<T_, DQK_, NB_, WC_, L_, RET_>;                               \
-    out->lds_bytes = chunk_lds_bytes<T_, DQK_, NB_, WC_, L_, RET_>();                            \
+    out->launch = &launch_chunkwise<T_, DQK_, NB_, WC_, NRG_, L_, RET_>;                         \
+    out->lds_bytes = chunk_lds_bytes<T_, DQK_, NB_, WC_, NRG_, L_, RET_>();                      \
     out->wc = WC_;                                                                               \
     return true;                                                                                 \
   }

@@ -30,7 +30,7 @@ __device__ __forceinline__ float log2_sigmoid(float x) {
   return (fminf(x, 0.f) - log1pf(__expf(-fabsf(x)))) * kLog2e;
 }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __expf(-x)); }
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
 // MFMA traits: one 16x16 output tile, K elements of the contraction per
 // instruction, KL of them held by each lane.  Lane l holds A[l%16][KL*(l/16)+e],
@@ -87,6 +87,51 @@ __device__ __forceinline__ Vec16<T> zero16() {
   Vec16<T> r;
   *reinterpret_cast<uint4*>(r.v) = make_uint4(0, 0, 0, 0);
   return r;
+}
+
+// Buffer resource over [base, base + bytes): loads past the end return zero,
+// so masked (ragged-tail) loads need no branch.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <typename T>
+__device__ __forceinline__ Vec16<T> bload16(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
+  Vec16<T> v;
+  *reinterpret_cast<u32x4*>(v.v) = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+  return v;
+}
+
+// one element (bf16 or fp32) as float
+template <typename T>
+__device__ __forceinline__ float bload1(__amdgpu_buffer_rsrc_t r, unsigned byte_off);
+template <>
+__device__ __forceinline__ float bload1<float>(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+template <>
+__device__ __forceinline__ float bload1<__bf16>(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
+  return __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0) << 16);
+}
+
+// four consecutive elements as floats
+template <typename T>
+__device__ __forceinline__ void bload4(__amdgpu_buffer_rsrc_t r, unsigned byte_off, float (&x)[4]);
+template <>
+__device__ __forceinline__ void bload4<float>(__amdgpu_buffer_rsrc_t r, unsigned byte_off, float (&x)[4]) {
+  const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+  for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(u[i]);
+}
+template <>
+__device__ __forceinline__ void bload4<__bf16>(__amdgpu_buffer_rsrc_t r, unsigned byte_off, float (&x)[4]) {
+  const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
+  x[0] = __uint_as_float(u[0] << 16);
+  x[1] = __uint_as_float(u[0] & 0xffff0000u);
+  x[2] = __uint_as_float(u[1] << 16);
+  x[3] = __uint_as_float(u[1] & 0xffff0000u);
 }
 
 // Four consecutive elements to an 8- (bf16) or 16-byte (fp32) aligned address.

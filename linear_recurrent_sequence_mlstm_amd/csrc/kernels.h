@@ -43,7 +43,8 @@ struct ScanParams {
   const float* m0;
 };
 
-typedef hipError_t (*ChunkLaunchFn)(ChunkParams, hipStream_t);
+// ev0/ev1 (may be null) are recorded right before / after the main kernel.
+typedef hipError_t (*ChunkLaunchFn)(ChunkParams, hipStream_t, hipEvent_t ev0, hipEvent_t ev1);
 
 struct ChunkVariant {
   ChunkLaunchFn launch;

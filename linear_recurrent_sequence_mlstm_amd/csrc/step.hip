@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p, int tph, int pp
   }
   if (active) {
     const float cl2 = exp2_fast(-mn2);
-    const float inv = 1.f / fmaxf(fabsf(dot + bias * cl2), cl2);
+    const float inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(dot + bias * cl2), cl2));
     T hv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
