@@ -111,15 +111,29 @@ struct ChunkCfg {
   static constexpr int NKQR = RPW / K;            // feature k-blocks of a wave's rows
   static constexpr int NTQK = NJT * (NJT + 1) / 2;  // causal score tiles
   static constexpr int VE = 16 / (int)sizeof(T);  // elements per 16 bytes
-  static constexpr int PAD = VE;
-  static constexpr int QS = DQK + PAD;            // row stride of sQ
-  static constexpr int TS = L + PAD;              // row stride of sKt, sVt, sP
+  // Row strides (elements) of the token-major tiles: the smallest padding
+  // that makes a row step move the bank by one of the given residues (mod 64
+  // dwords).  Q/K (16-byte fragment reads, 16 rows) use 8 + 16i; V (only
+  // transposing reads, 4 rows x 32 bytes per 16 lanes) uses 12, 28, 36, 52.
+  // Both choices were the fastest in a sweep on MI355X.
+  static constexpr int pad_for(int row_elems, bool v) {
+    const int dw = row_elems * (int)sizeof(T) / 4;
+    int best = 64;
+    const int rq[4] = {8, 24, 40, 56}, rv[4] = {12, 28, 36, 52};
+    for (int i = 0; i < 4; ++i) {
+      const int r = v ? rv[i] : rq[i];
+      const int pad = ((r - dw % 64) % 64 + 64) % 64;
+      if (pad < best) best = pad;
+    }
+    return best * 4 / (int)sizeof(T);
+  }
+  static constexpr int QS = DQK + pad_for(DQK, false);  // sQ, sK
+  static constexpr int VS = W + pad_for(W, true);       // sV
+  static constexpr int PS = L + 16 / (int)sizeof(T);  // sP
   // staging units (16-byte loads) per chunk
   static constexpr int NQU = L * DQK / VE;
-  static constexpr int NKU = (L / 4) * (DQK / VE);
-  static constexpr int NVU = (L / 4) * (W / VE);
+  static constexpr int NVU = L * W / VE;
   static constexpr int QIT = (NQU + NTH - 1) / NTH;
-  static constexpr int KIT = (NKU + NTH - 1) / NTH;
   static constexpr int VIT = (NVU + NTH - 1) / NTH;
   static_assert(DQK % NB == 0, "d_qk % nb");
   static_assert(RPW % (sizeof(T) == 2 ? 32 : 16) == 0, "state rows per wave");
@@ -128,13 +142,13 @@ struct ChunkCfg {
   static_assert(WC % 16 == 0, "wave columns");
   static constexpr size_t lds_bytes(bool full, bool ret) {
     size_t b = 0;
-    b += (size_t)DQK * TS * sizeof(T);           // sKt
-    b += (size_t)W * TS * sizeof(T);             // sVt
+    b += (size_t)L * QS * sizeof(T);             // sK
+    b += (size_t)L * VS * sizeof(T);             // sV
     b += 6 * L * 4 + 16;                         // gate vectors
-    if (!ret) b += DQK * 4 + 2 * DQK * sizeof(T);  // n~
+    if (!ret) b += DQK * 4 + (full ? 16 * DQK * sizeof(T) : 0);  // n~
     if (full) {
       b += (size_t)L * QS * sizeof(T);           // sQ
-      b += (size_t)NB * L * TS * sizeof(T);      // sP
+      b += (size_t)NB * L * PS * sizeof(T);      // sP
       b += (size_t)(NJT + 1) * L * 4;            // den partials
       if (NRG > 1) b += (size_t)4 * NJT * CT * 64 * 16;  // readout exchange
     }
@@ -142,20 +156,26 @@ struct ChunkCfg {
   }
 };
 
-// A operand of the score MFMA (rows = tokens, k = features f0 .. f0+KL-1) read
-// from the feature-major copy of K.
-template <typename T>
-__device__ __forceinline__ typename Mma<T>::frag load_k_rows(const T* sKt, int TS, int f0, int tok);
-template <>
-__device__ __forceinline__ bf16x8 load_k_rows<__bf16>(const __bf16* sKt, int TS, int f0, int tok) {
+// MFMA fragment along the rows of a token-major tile: lane (lr, lg) gets rows
+// r0 + KL*lg + e (e < KL) of one column.
+//   bf16: two transposing reads; source lane lr addresses column csrc(lr),
+//         chosen by the caller so that output lane lr sees its column.
+//   fp32: one element, column ccol(lr).
+__device__ __forceinline__ bf16x8 frag_rows(const __bf16* tile, int RS, int r0, int lr, int csrc) {
+  const __bf16* p = tile + (r0 + (lr >> 2)) * RS + csrc;
+  const bf16x4 a = ds_read_tr16(p);
+  const bf16x4 b = ds_read_tr16(p + 4 * RS);
   bf16x8 r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = sKt[(f0 + e) * TS + tok];
+  for (int e = 0; e < 4; ++e) {
+    r[e] = a[e];
+    r[4 + e] = b[e];
+  }
   return r;
 }
-template <>
-__device__ __forceinline__ float load_k_rows<float>(const float* sKt, int TS, int f0, int tok) {
-  return sKt[f0 * TS + tok];
+__device__ __forceinline__ float frag_rows(const float* tile, int RS, int r0, int lr, int ccol) {
+  (void)lr;
+  return tile[r0 * RS + ccol];
 }
 
 // Main kernel.  FULL = true: pass 3 (readout, outputs, update).  FULL = false:
@@ -166,6 +186,8 @@ __device__ __forceinline__ float load_k_rows<float>(const float* sKt, int TS, in
 // [rg*RPW, rg*RPW+RPW) of their memory block.  With NRG = 2 the readout of a
 // column group is split over its two waves by rows; each wave finishes half of
 // the token tiles and the two partial sums meet in LDS (sX).
+// Q, K and V are staged token-major with plain 16-byte copies; the operands
+// that run along tokens (K^T and V^T) are read with transposing LDS reads.
 template <typename T, int DQK, int NB, int WC, int NRG, int L, bool RET, bool FULL>
 __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
   using C = ChunkCfg<T, DQK, NB, WC, NRG, L>;
@@ -174,16 +196,19 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
   constexpr int K = C::K, KL = C::KL, DQKB = C::DQKB, NT = C::NT, CT = C::CT, NW = C::NW;
   constexpr int NTH = C::NTH, RPW = C::RPW, JPW = C::JPW;
   constexpr int W = C::W, NJT = C::NJT, NKL = C::NKL, NKQ = C::NKQ, NKQB = C::NKQB, NKQR = C::NKQR;
-  constexpr int VE = C::VE, QS = C::QS, TS = C::TS;
+  constexpr int VE = C::VE, QS = C::QS, VS = C::VS, PS = C::PS;
   constexpr unsigned ES = sizeof(T);
   constexpr bool XCH = FULL && NRG > 1;
+  constexpr bool BF = sizeof(T) == 2;
 
-  __shared__ __attribute__((aligned(16))) T sKt[DQK * TS];  // K, feature-major
-  __shared__ __attribute__((aligned(16))) T sVt[W * TS];    // V slice, feature-major
+  __shared__ __attribute__((aligned(16))) T sK[L * QS];   // K, token-major
+  __shared__ __attribute__((aligned(16))) T sV[L * VS];   // V slice, token-major
   __shared__ __attribute__((aligned(16))) T sQ[FULL ? L * QS : 8];   // Q, token-major
-  __shared__ __attribute__((aligned(16))) T sP[FULL ? NB * L * TS : 8];
+  __shared__ __attribute__((aligned(16))) T sP[FULL ? NB * L * PS : 8];
   __shared__ __attribute__((aligned(16))) f32x4 sX[XCH ? 4 * NJT * CT * 64 : 1];
-  __shared__ __attribute__((aligned(16))) T sNh[RET ? 8 : 2 * DQK];
+  // n~ as a 16-row A-operand tile: row 0 = bf16 hi part, row 1 = lo part,
+  // rows 2..15 zero (fp32: row 0 = n~, row 1 zero)
+  __shared__ __attribute__((aligned(16))) T sNh[RET || !FULL ? 8 : 16 * DQK];
   __shared__ float sNf[RET ? 4 : DQK];
   __shared__ float sA2[L], sM2[L], sRS[L], sCL[L], sBT[L], sW[L];
   __shared__ float sDenPart[FULL ? NJT * L : 4];
@@ -196,19 +221,22 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int cg = w & 3, rg = w >> 2;
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  // Work-group coordinates.  Integer division by runtime values runs on the
+  // VALU; readfirstlane keeps the results (and the buffer descriptors built
+  // from them) in scalar registers, otherwise every buffer load would be
+  // wrapped in a waterfall loop.
   const int BH = p.B * p.H;
-  int idx = blockIdx.x;
-  const int bh = idx % BH;
-  idx /= BH;
-  const int slice = idx % p.nslices;
-  const int sc = idx / p.nslices;
-  const int hd = bh % p.H;
+  const int idx = blockIdx.x;
+  const int bh = __builtin_amdgcn_readfirstlane(idx % BH);
+  const int slice = __builtin_amdgcn_readfirstlane((idx / BH) % p.nslices);
+  const int sc = __builtin_amdgcn_readfirstlane((idx / BH) / p.nslices);
+  const int hd = __builtin_amdgcn_readfirstlane(bh % p.H);
   const int T_ = p.T, DV = p.DV, DVB = DV / NB;
   const size_t CS = (size_t)DQK * DV / NB;
   const size_t NSTATE = CS + (RET ? 0 : DQK);
 
   const int wcol0 = slice * W + cg * WC;  // first global d_v column of this wave
-  const int blk = wcol0 / DVB;            // memory block of this wave
+  const int blk = __builtin_amdgcn_readfirstlane(wcol0 / DVB);  // memory block of this wave
   const int wcl0 = wcol0 - blk * DVB;     // first column inside the block
   const int rrow0 = rg * RPW;             // first state row of this wave inside the block
   const int rb0 = blk * DQKB + rrow0;     // ... as a feature index of the head
@@ -233,6 +261,12 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
   const int c_begin = sc * p.G;
   const int c_end = FULL ? min(c_begin + p.G, p.NC) : c_begin + p.G;
 
+  // Source columns of the transposing reads.  K^T (update A operand): output
+  // lane lr must see feature rb0 + perm_row(nt, lr).  V^T (PV A operand and
+  // update B operand): output lane lr sees column cg*WC + ct*16 + lr.
+  const int kcol = BF ? rb0 + 8 * (lr & 3) : rb0;  // + perm part added per tile
+  const int vcol = BF ? cg * WC + 4 * (lr & 3) : cg * WC + lr;
+
   // ---------------------------------------------------------------- state in
   f32x4 st[NT][CT];
   const float* Sin = nullptr;
@@ -246,18 +280,24 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         st[nt][ct][i] = Sin ? Sin[soff + perm_row_uni<T>(nt, i) * DVB + ct * 16] : 0.f;
-  if constexpr (!RET) {
-    for (int r = tid; r < DQK; r += NTH) {
-      const float x = Sin ? Sin[CS + r] : 0.f;
-      sNf[r] = x;
+  // n~ in fp32 and as the hi/lo rows of the den tile
+  auto put_n = [&](int r, float x) __attribute__((always_inline)) {
+    sNf[r] = x;
+    if constexpr (FULL) {
       const T hi = from_f32<T>(x);
       sNh[r] = hi;
       sNh[DQK + r] = from_f32<T>(x - to_f32(hi));
     }
+  };
+  if constexpr (!RET) {
+    if constexpr (FULL)
+      for (int e = tid; e < 16 * DQK; e += NTH) sNh[e] = from_f32<T>(0.f);
+    __syncthreads();
+    for (int r = tid; r < DQK; r += NTH) put_n(r, Sin ? Sin[CS + r] : 0.f);
   }
   if constexpr (FULL) {
     // masked (l > j) tiles of P and their den partials are never written
-    for (int e = tid; e < NB * L * TS; e += NTH) sP[e] = from_f32<T>(0.f);
+    for (int e = tid; e < NB * L * PS; e += NTH) sP[e] = from_f32<T>(0.f);
     for (int e = tid; e < NJT * L; e += NTH) sDenPart[e] = 0.f;
   }
   // The registers hold S^ = S~ / 2^{sig}: the per-chunk decay of the state is
@@ -275,11 +315,11 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
   // loads are issued during the current chunk and written to LDS at its end,
   // so no staging register lives across a loop iteration.
   Vec16<T> rgq[FULL ? C::QIT : 1];
-  Vec16<T> rgk[C::KIT][4];
-  Vec16<T> rgv[C::VIT][4];
+  Vec16<T> rgk[C::QIT];
+  Vec16<T> rgv[C::VIT];
   float rgi = 0.f, rgf = 0.f;
 
-  auto load_q = [&](int c) {
+  auto load_q = [&](int c) __attribute__((always_inline)) {
     const unsigned t0 = (unsigned)c * L;
     if constexpr (FULL) {
 #pragma unroll
@@ -291,22 +331,19 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
     }
   };
 
-  auto load_kv = [&](int c) {
+  auto load_kv = [&](int c) __attribute__((always_inline)) {
     const unsigned t0 = (unsigned)c * L;
 #pragma unroll
-    for (int it = 0; it < C::KIT; ++it) {
-      const int u = (tid + it * NTH) % C::NKU;
-      const unsigned tg = u % (L / 4), fg = u / (L / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) rgk[it][r] = bload16<T>(rk, ((t0 + 4 * tg + r) * DQK + fg * VE) * ES);
+    for (int it = 0; it < C::QIT; ++it) {
+      const int u = (tid + it * NTH) % C::NQU;
+      const unsigned j = u / (DQK / VE), col = (u % (DQK / VE)) * VE;
+      rgk[it] = bload16<T>(rk, ((t0 + j) * DQK + col) * ES);
     }
 #pragma unroll
     for (int it = 0; it < C::VIT; ++it) {
       const int u = (tid + it * NTH) % C::NVU;
-      const unsigned tg = u % (L / 4), fg = u / (L / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        rgv[it][r] = bload16<T>(rv, ((t0 + 4 * tg + r) * DV + slice * W + fg * VE) * ES);
+      const unsigned j = u / (W / VE), col = (u % (W / VE)) * VE;
+      rgv[it] = bload16<T>(rv, ((t0 + j) * DV + slice * W + col) * ES);
     }
     if constexpr (!RET) {
       rgi = bload1<T>(ri, (t0 + (lane & (L - 1))) * ES);
@@ -314,43 +351,29 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
     }
   };
 
-  auto store_stage = [&]() {
-    if constexpr (FULL) {
+  auto store_stage = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int it = 0; it < C::QIT; ++it) {
-        const int u = tid + it * NTH;
-        if (u < C::NQU) {
-          const int j = u / (DQK / VE), col = (u % (DQK / VE)) * VE;
-          *reinterpret_cast<uint4*>(&sQ[j * QS + col]) = *reinterpret_cast<const uint4*>(rgq[it].v);
-        }
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < C::KIT; ++it) {
+    for (int it = 0; it < C::QIT; ++it) {
       const int u = tid + it * NTH;
-      if (u < C::NKU) {
-        const int tg = u % (L / 4), fg = u / (L / 4);
-#pragma unroll
-        for (int e = 0; e < VE; ++e)
-          store4(&sKt[(fg * VE + e) * TS + 4 * tg], rgk[it][0].v[e], rgk[it][1].v[e], rgk[it][2].v[e],
-                 rgk[it][3].v[e]);
+      if (u < C::NQU) {
+        const int j = u / (DQK / VE), col = (u % (DQK / VE)) * VE;
+        if constexpr (FULL)
+          *reinterpret_cast<uint4*>(&sQ[j * QS + col]) = *reinterpret_cast<const uint4*>(rgq[it].v);
+        *reinterpret_cast<uint4*>(&sK[j * QS + col]) = *reinterpret_cast<const uint4*>(rgk[it].v);
       }
     }
 #pragma unroll
     for (int it = 0; it < C::VIT; ++it) {
       const int u = tid + it * NTH;
       if (u < C::NVU) {
-        const int tg = u % (L / 4), fg = u / (L / 4);
-#pragma unroll
-        for (int e = 0; e < VE; ++e)
-          store4(&sVt[(fg * VE + e) * TS + 4 * tg], rgv[it][0].v[e], rgv[it][1].v[e], rgv[it][2].v[e],
-                 rgv[it][3].v[e]);
+        const int j = u / (W / VE), col = (u % (W / VE)) * VE;
+        *reinterpret_cast<uint4*>(&sV[j * VS + col]) = *reinterpret_cast<const uint4*>(rgv[it].v);
       }
     }
   };
 
   // Gate scan for one chunk on wave 0 (one lane per token).
-  auto gates = [&](int c) {
+  auto gates = [&](int c) __attribute__((always_inline)) {
     const int t0 = c * L;
     const bool valid = lane < L && t0 + lane < T_;
     float lf2, li2;
@@ -404,19 +427,21 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
     const bool more = c + 1 < c_end;
     // pass 1 prefetches at the top; pass 3 after its second barrier, so that
     // the readout (its register peak) holds no staging registers
-    if (!FULL && more) load_kv(c + 1);
+    if (!FULL && more) {
+      load_q(c + 1);
+      load_kv(c + 1);
+    }
 
     // update of the state is needed unless this is the last chunk of a
     // superchunk whose end state nobody reads
     const bool need_update = !FULL || more || (sc == p.NS - 1);
 
-    frag vf[CT][NKL];  // V^T fragments of this wave's columns (loaded after phase B)
-    auto load_vf = [&]() {
+    frag vf[CT][NKL];  // V^T fragments of this wave's columns
+    auto load_vf = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int kb = 0; kb < NKL; ++kb)
-          vf[ct][kb] = M::load(&sVt[(cg * WC + ct * 16 + lr) * TS + kb * K + KL * lg]);
+        for (int kb = 0; kb < NKL; ++kb) vf[ct][kb] = frag_rows(sV, VS, kb * K + KL * lg, lr, vcol + ct * 16);
     };
     if constexpr (!FULL) load_vf();
 
@@ -440,7 +465,7 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
 #pragma unroll
             for (int kk = 0; kk < NKQB; ++kk) {
               const int kb = be * NKQB + kk;
-              const frag kf = load_k_rows<T>(sKt, TS, kb * K + KL * lg, lt * 16 + lr);
+              const frag kf = M::load(&sK[(lt * 16 + lr) * QS + kb * K + KL * lg]);
               const frag qj = M::load(&sQ[(jt * 16 + lr) * QS + kb * K + KL * lg]);
               pt[be] = M::mma(kf, qj, pt[be]);
               if (kk & 1) __builtin_amdgcn_sched_barrier(0);
@@ -465,7 +490,7 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
               dsum += x;
               pv[i] = from_f32<T>(x);
             }
-            store4(&sP[(be * L + j) * TS + lt * 16 + 4 * lg], pv[0], pv[1], pv[2], pv[3]);
+            store4(&sP[(be * L + j) * PS + lt * 16 + 4 * lg], pv[0], pv[1], pv[2], pv[3]);
           }
           dsum += __shfl_xor(dsum, 16, 64);
           dsum += __shfl_xor(dsum, 32, 64);
@@ -480,8 +505,7 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
             f32x4 pn = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < NKQ; ++kb) {
-              frag nf = M::load(&sNh[(lr & 1) * DQK + kb * K + KL * lg]);
-              if (lr > 1) nf = M::zero();
+              const frag nf = M::load(&sNh[lr * DQK + kb * K + KL * lg]);
               pn = M::mma(nf, M::load(&sQ[(jt * 16 + lr) * QS + kb * K + KL * lg]), pn);
               if (kb & 1) __builtin_amdgcn_sched_barrier(0);
             }
@@ -549,7 +573,7 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
 #pragma unroll
         for (int kb = 0; kb < NKL; ++kb) {
           if (kb * K <= jt * 16 + 15) {
-            const frag pf = M::load(&sP[(blk * L + jt * 16 + lr) * TS + kb * K + KL * lg]);
+            const frag pf = M::load(&sP[(blk * L + jt * 16 + lr) * PS + kb * K + KL * lg]);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) o_acc[ct] = M::mma(vf[ct][kb], pf, o_acc[ct]);
           }
@@ -596,35 +620,62 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
         sig = 0.f;
       }
       const float wscale = exp2_fast(-sig);
+      // n~ gets sum_l w_l k_l.  With one memory block the K^T fragments of the
+      // update carry every feature of k: each is summed by one wave (tile nt
+      // goes to column group nt % 4).  With several blocks a work-group's waves
+      // need not cover all blocks, so a plain loop over sK does it.
+      constexpr bool NFRAG = !RET && NB == 1;
+      float dn[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) dn[nt] = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKL; ++kb) {
         float wl[KL];
 #pragma unroll
-        for (int e = 0; e < KL; ++e) wl[e] = sW[kb * K + KL * lg + e] * wscale;
+        for (int e = 0; e < KL; ++e) wl[e] = sW[kb * K + KL * lg + e];
+        float wls[KL];
+#pragma unroll
+        for (int e = 0; e < KL; ++e) wls[e] = wl[e] * wscale;
         frag wv[CT];
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) wv[ct] = scale_frag(vf[ct][kb], wl);
+        for (int ct = 0; ct < CT; ++ct) wv[ct] = scale_frag(vf[ct][kb], wls);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const frag ka = M::load(&sKt[(rb0 + perm_row<T>(nt, lr)) * TS + kb * K + KL * lg]);
+          const int kc = BF ? kcol + (nt >> 1) * 32 + (nt & 1) * 4 : kcol + perm_row<T>(nt, lr);
+          const frag ka = frag_rows(sK, QS, kb * K + KL * lg, lr, kc);
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) st[nt][ct] = M::mma(ka, wv[ct], st[nt][ct]);
+          if constexpr (NFRAG) {
+            if ((nt & 3) == cg) {
+#pragma unroll
+              for (int e = 0; e < KL; ++e) {
+                if constexpr (BF) dn[nt] += wl[e] * (float)ka[e];
+                else dn[nt] += wl[e] * ka;
+              }
+            }
+          }
+          if ((nt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if constexpr (!RET) {
+      if constexpr (!RET && !NFRAG) {
         for (int r = tid; r < DQK; r += NTH) {
           float x = alpha * sNf[r];
+          for (int l = 0; l < L; ++l) x += sW[l] * to_f32(sK[l * QS + r]);
+          put_n(r, x);
+        }
+      }
+      if constexpr (NFRAG) {
 #pragma unroll
-          for (int l = 0; l < L; l += VE) {
-            const Vec16<T> kv = load16(&sKt[r * TS + l]);
-#pragma unroll
-            for (int e = 0; e < VE; ++e) x += sW[l + e] * to_f32(kv.v[e]);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int nt = 0; nt < NT; ++nt) {
+          if ((nt & 3) == cg) {
+            float d = dn[nt];
+            d += __shfl_xor(d, 16, 64);
+            d += __shfl_xor(d, 32, 64);
+            if (lg == 0) {
+              const int r = rb0 + perm_row<T>(nt, lr);
+              put_n(r, alpha * sNf[r] + d);
+            }
           }
-          sNf[r] = x;
-          const T hi = from_f32<T>(x);
-          sNh[r] = hi;
-          sNh[DQK + r] = from_f32<T>(x - to_f32(hi));
         }
       }
     }

@@ -94,8 +94,15 @@ __device__ __forceinline__ Vec16<T> zero16() {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
+// Callers pass wave-uniform values; readfirstlane states that, so the
+// descriptor lives in scalar registers (a descriptor the compiler believes
+// divergent is used through a waterfall loop around every load).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  void* ub = reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
 template <typename T>
@@ -132,6 +139,18 @@ __device__ __forceinline__ void bload4<__bf16>(__amdgpu_buffer_rsrc_t r, unsigne
   x[1] = __uint_as_float(u[0] & 0xffff0000u);
   x[2] = __uint_as_float(u[1] << 16);
   x[3] = __uint_as_float(u[1] & 0xffff0000u);
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, output lane i holds element (i & 3) of the 4 elements that source lane
+// 4e + (i >> 2) addressed, for e = 0..3.  So if source lane s addresses row
+// r0 + (s >> 2), column c0 + 4 (s & 3) of a row-major tile, output lane i
+// receives column c0 + i of rows r0 .. r0+3: an MFMA fragment along the rows.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 ds_read_tr16(const __bf16* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(const_cast<__bf16*>(p)));
+  return __builtin_bit_cast(bf16x4, v);
 }
 
 // Four consecutive elements to an 8- (bf16) or 16-byte (fp32) aligned address.
