@@ -150,6 +150,21 @@ def bench_decode(torch, mlstm, workload, args, dev):
     return dict(B=B, H=H, dqk=dqk, dv=dv, S=S, wall=wall, step_ms=step_ms, bytes=byts, flops=flops)
 
 
+def copy_calibration(torch, dev, nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size (nbytes read, nbytes
+    written per launch).  Its rocprofv3 FETCH_SIZE / WRITE_SIZE readings give
+    the factors that turn those counters into HBM bytes for the kernels above."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    return dict(bytes_read=nbytes, bytes_written=nbytes, ms=dt * 1e3, GBps=2 * nbytes / dt / 1e9)
+
+
 def cpu_baseline(x, sample_tokens):
     """The fp64 oracle on the host cores: all 8 heads of the prefill workload
     (the same CPU tensors the GPU got) over its first ``sample_tokens`` tokens."""
@@ -175,6 +190,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=("prefill", "decode", "copy"),
+                    help="run one leg alone and print its raw figures (for profiler runs)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -188,6 +205,17 @@ def main():
     from linear_recurrent_sequence_mlstm_amd.workloads import workload
 
     dev = torch.device("cuda:0")
+    if args.only:
+        print("bench: only %s" % args.only, file=sys.stderr, flush=True)
+        if args.only == "prefill":
+            r = bench_prefill(torch, mlstm, workload("xlstm7b_prefill_T8192"), args, dev)
+            r.pop("spec")
+        elif args.only == "decode":
+            r = bench_decode(torch, mlstm, workload, args, dev)
+        else:
+            r = copy_calibration(torch, dev)
+        print(json.dumps(dict(leg=args.only, **r)))
+        return
     print("bench: prefill xlstm7b_prefill_T8192 steps=%d warmup=%d" % (args.steps, args.warmup),
           file=sys.stderr, flush=True)
     x = workload("xlstm7b_prefill_T8192")

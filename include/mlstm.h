@@ -111,8 +111,9 @@ size_t mlstm_chunkwise_workspace_bytes(int B, int H, int T, int d_qk, int d_v,
  *                                256-byte aligned; overwritten by the call.
  * chunk is the chunk length L (64 for bf16; 16, 32 or 64 for fp32).
  * Supported (d_qk, num_blocks): bf16 {(64,1),(64,2),(128,1),(256,1),(256,2)},
- * fp32 {(64,1),(64,2)}; d_v must be a multiple of 64 (bf16 d_qk >= 128: of
- * 128) whose per-block share is a multiple of 16.  Any T >= 1.
+ * fp32 {(64,1),(64,2)}.  d_v must be a multiple of 128 when d_qk/num_blocks
+ * >= 128 (bf16), else of 64, and d_v/num_blocks a multiple of 32 resp. 16.
+ * Any T >= 1.  Other combinations return MLSTM_E_UNSUPPORTED.
  */
 int mlstm_chunkwise_fwd(int B, int H, int T, int d_qk, int d_v, int num_blocks,
                         int chunk, mlstm_dtype dt, const void* q, const void* k,
@@ -129,7 +130,9 @@ int mlstm_chunkwise_fwd(int B, int H, int T, int d_qk, int d_v, int num_blocks,
  *   NULL (dtype dt); norm_bias [H] fp32 or NULL;
  *   C [B,H,nb,d_qk/nb,d_v/nb], n [B,H,d_qk], m [B,H] fp32, read and written;
  *   h [B,H,d_v] output (dtype dt).
- * Requires d_v/4 to divide 256 and (d_qk/nb) % 8 == 0.
+ * Requires d_v/nb a multiple of 4 and d_v a multiple of 32 up to 512, of 64
+ * up to 1024, of 128 up to 2048 or of 256 up to 4096; other shapes return
+ * MLSTM_E_UNSUPPORTED.
  */
 int mlstm_step(int B, int H, int d_qk, int d_v, int num_blocks, mlstm_dtype dt,
                const void* q, const void* k, const void* v, const void* i_pre,

@@ -39,13 +39,6 @@ int env_superchunk_chunks() {
   return g > 0 ? g : 0;
 }
 
-int env_wave_cols() {
-  const char* s = getenv("MLSTM_WAVE_COLS");
-  if (!s) return 0;
-  const int w = atoi(s);
-  return (w == 16 || w == 32) ? w : 0;
-}
-
 struct Plan {
   mlstm::ChunkVariant var;
   int L, NC, G, NS, nslices;
@@ -68,8 +61,7 @@ int plan_chunkwise(int B, int H, int T, int dqk, int dv, int nb, int chunk, int 
   if ((long long)B * H >= (1LL << 24)) return fail(MLSTM_E_SHAPE, "B * H too large");
   if (chunk != 16 && chunk != 32 && chunk != 64)
     return fail(MLSTM_E_SHAPE, "chunk must be 16, 32 or 64 (got %d)", chunk);
-  int wc = (dt == MLSTM_BF16 && dqk / nb >= 128) ? 32 : 16;
-  if (dt == MLSTM_BF16 && dqk == 256 && nb == 1 && env_wave_cols()) wc = env_wave_cols();
+  const int wc = (dt == MLSTM_BF16 && dqk / nb >= 128) ? 32 : 16;
   if (!mlstm::find_chunk_variant(dt, dqk, nb, wc, chunk, ret, &pl->var))
     return fail(MLSTM_E_UNSUPPORTED,
                 "no kernel for dtype=%s d_qk=%d num_blocks=%d chunk=%d%s", dt ? "bf16" : "fp32", dqk, nb,

@@ -132,25 +132,28 @@ __global__ __launch_bounds__(1024) void step_kernel(StepParams p) {
   }
 }
 
-// Row groups per (batch, head): aim at 256-512 threads per work-group.
-// MLSTM_STEP_RG (1, 2, 4, 8) overrides the choice for tuning.
+// Row groups per (batch, head): the most (up to 8) that keep the work-group
+// at <= 512 threads, else at <= 1024, with a whole number of waves (the n~.q
+// sum reduces per wave).  0 if no choice fits.  MLSTM_STEP_RG (1, 2, 4, 8)
+// overrides the choice for tuning when it fits.
 static int pick_rg(int dv) {
   const int tpc = dv / 4;
-  int rg = 1;
-  while (tpc * rg * 2 <= 512 && rg < 8) rg *= 2;
+  const auto fits = [tpc](int rg, int cap) { return tpc * rg <= cap && (tpc * rg) % 64 == 0; };
   const char* e = getenv("MLSTM_STEP_RG");
   if (e) {
     const int x = atoi(e);
-    if ((x == 1 || x == 2 || x == 4 || x == 8) && tpc * x <= 1024) rg = x;
+    if ((x == 1 || x == 2 || x == 4 || x == 8) && fits(x, 1024)) return x;
   }
-  return rg;
+  for (int cap : {512, 1024})
+    for (int rg = 8; rg >= 1; rg >>= 1)
+      if (fits(rg, cap)) return rg;
+  return 0;
 }
 
 bool step_supported(int dqk, int dv, int nb) {
   if (nb <= 0 || dqk % nb || dv % nb) return false;
   if (dv % 4 || (dv / nb) % 4) return false;
-  const int nth = dv / 4 * pick_rg(dv);
-  return nth % 64 == 0 && nth <= 1024;  // whole waves: the n~.q sum reduces per wave
+  return pick_rg(dv) > 0;
 }
 
 template <typename T>

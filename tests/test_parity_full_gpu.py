@@ -1,0 +1,85 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (default chunk and superchunk plan, caller-provided outputs
+and workspace), against the fp64 oracle on the same seeded inputs.
+
+Error metric and bars as in test_parity_gpu: per (batch, head) slice,
+max |y - y_ref| / max |y_ref|; 2e-2 for bf16 inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_recurrent_sequence_mlstm_amd import _lib as mlstm
+from linear_recurrent_sequence_mlstm_amd.workloads import workload
+
+from test_parity_gpu import TOL, check_state, cpu, slice_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _chunkwise_like_bench(g, dev):
+    B, H, T, dqk = g.q.shape
+    dv = g.v.shape[-1]
+    nb = g.num_blocks
+    h = torch.empty(B, H, T, dv, dtype=g.q.dtype, device=dev)
+    st = (torch.empty(B, H, nb, dqk // nb, dv // nb, device=dev), torch.empty(B, H, dqk, device=dev),
+          torch.empty(B, H, device=dev))
+    ws = torch.empty(mlstm.chunkwise_workspace_bytes(B, H, T, dqk, dv, nb, dtype=g.q.dtype),
+                     dtype=torch.uint8, device=dev)
+    mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, num_blocks=nb, h=h,
+                        state_out=st, workspace=ws)
+    torch.cuda.synchronize()
+    return h, st
+
+
+def test_xlstm7b_prefill_full_size(gpu):
+    """B=1, 8 heads, d_qk=256, d_v=512, T=8192: every output and the final state."""
+    x = workload("xlstm7b_prefill_T8192")
+    h, st = _chunkwise_like_bench(x.to(gpu), gpu)
+    ref = oracle.mlstm_fwd(x.q, x.k, x.v, x.i_pre, x.f_pre, x.o_pre, x.bias, num_blocks=x.num_blocks)
+    assert slice_err(cpu(h), ref[0]) < TOL[torch.bfloat16]
+    check_state(st, ref[1:], TOL[torch.bfloat16])
+
+
+def test_xlstm2_blockdiag_T65536_full_size(gpu):
+    """B=4, 4 heads, d=64 in two 32x32 blocks, T=65536, biased normaliser,
+    bimodal forget gates: every output and the final state."""
+    x = workload("xlstm2_blockdiag_T65536")
+    h, st = _chunkwise_like_bench(x.to(gpu), gpu)
+    ref = oracle.mlstm_fwd(x.q, x.k, x.v, x.i_pre, x.f_pre, x.o_pre, x.bias, num_blocks=x.num_blocks)
+    assert slice_err(cpu(h), ref[0]) < TOL[torch.bfloat16]
+    check_state(st, ref[1:], TOL[torch.bfloat16])
+
+
+def test_xlstm7b_decode_128_steps_sampled(gpu):
+    """B=256, 8 heads, 1 GiB fp32 state updated in place over 128 steps, as
+    the benchmark runs it.  The oracle follows 32 sampled (batch, head)
+    sequences (corners included): their h at every step and final state."""
+    d = workload("xlstm7b_decode_B256")
+    S, B, H, dqk = d.q.shape
+    dv = d.v.shape[-1]
+    g = d.to(gpu)
+    C = torch.zeros(B, H, 1, dqk, dv, device=gpu)
+    n = torch.zeros(B, H, dqk, device=gpu)
+    m = torch.zeros(B, H, device=gpu)
+    h = torch.empty(B, H, dv, dtype=torch.bfloat16, device=gpu)
+    rng = np.random.default_rng(4)
+    pairs = [(0, 0), (B - 1, H - 1), (B // 2, 3)] + [(int(b), int(hh)) for b, hh in
+                                                      zip(rng.integers(0, B, 29), rng.integers(0, H, 29))]
+    bi = torch.tensor([p[0] for p in pairs])
+    hi = torch.tensor([p[1] for p in pairs])
+    hs = []
+    for s in range(S):
+        mlstm.step(g.q[s], g.k[s], g.v[s], g.i_pre[s], g.f_pre[s], C, n, m, bias=g.bias, h=h)
+        hs.append(h[bi.to(gpu), hi.to(gpu)].clone())
+    torch.cuda.synchronize()
+    got = torch.stack(hs, dim=1)[None]  # [1, P, S, dv]
+    # sampled sequences as P heads of one batch: [1, P, S, d]
+    sel = lambda t: t[:, bi, hi].permute(1, 0, 2)[None].contiguous()
+    sel_g = lambda t: t[:, bi, hi].permute(1, 0)[None].contiguous()
+    bias = None if d.bias is None else d.bias[hi].contiguous()
+    ref = oracle.mlstm_fwd(sel(d.q), sel(d.k), sel(d.v), sel_g(d.i_pre), sel_g(d.f_pre), None, bias)
+    assert slice_err(cpu(got), ref[0]) < TOL[torch.bfloat16]
+    st = (C[bi.to(gpu), hi.to(gpu)][None], n[bi.to(gpu), hi.to(gpu)][None], m[bi.to(gpu), hi.to(gpu)][None])
+    check_state(st, ref[1:], TOL[torch.bfloat16])
