@@ -43,7 +43,7 @@ struct Plan {
   mlstm::ChunkVariant var;
   int L, NC, G, NS, nslices;
   size_t CS, nstate;
-  size_t off_scal, off_min, bytes;
+  size_t off_scal, off_min, off_w, bytes;
 };
 
 // Checks shared by the mLSTM and retention chunkwise entry points and the
@@ -84,6 +84,7 @@ int plan_chunkwise(int B, int H, int T, int dqk, int dv, int nb, int chunk, int 
   if (ns > pl->NC) ns = pl->NC;
   int G = (int)((pl->NC + ns - 1) / ns);
   if (env_superchunk_chunks()) G = env_superchunk_chunks();
+  if (G * chunk > 1024) G = 1024 / chunk;  // pass 1 holds the gate factors of <= 1024 tokens
   if (G > pl->NC) G = pl->NC;
   pl->G = G;
   pl->NS = (pl->NC + G - 1) / G;
@@ -92,7 +93,8 @@ int plan_chunkwise(int B, int H, int T, int dqk, int dv, int nb, int chunk, int 
   const size_t BH = (size_t)B * H;
   pl->off_scal = align256(BH * pl->NS * pl->nstate * sizeof(float));
   pl->off_min = pl->off_scal + align256(BH * pl->NS * 2 * sizeof(float));
-  pl->bytes = pl->off_min + align256(BH * pl->NS * sizeof(float));
+  pl->off_w = pl->off_min + align256(BH * pl->NS * sizeof(float));
+  pl->bytes = pl->off_w + (pl->NS > 1 ? align256(BH * (size_t)T * sizeof(float)) : 0);
   return MLSTM_OK;
 }
 
@@ -110,6 +112,7 @@ int launch(const Plan& pl, mlstm::ChunkParams& p, void* workspace, size_t worksp
   p.ws_state = reinterpret_cast<float*>(ws);
   p.ws_scal = reinterpret_cast<float*>(ws + pl.off_scal);
   p.ws_min = reinterpret_cast<float*>(ws + pl.off_min);
+  p.ws_w = reinterpret_cast<float*>(ws + pl.off_w);
   const hipError_t e = pl.var.launch(p, static_cast<hipStream_t>(stream), g_ev0, g_ev1);
   if (e != hipSuccess) return fail(MLSTM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -16,10 +16,11 @@
 //   S~   <- 2^{m_prev-M_L} S~ + sum_l 2^{a_l-M_L} k_l v_l^T;  m <- b_L + M_L
 // Retention is the same with i = 1, f = gamma_h and no normaliser.
 //
-// Three launches on the caller's stream:
-//   pass 1  every superchunk of G chunks but the last runs the state update
-//           from a zero state (m = -inf): its local end state dS, dn, its log
-//           scale mu and its total log decay A go to the workspace.
+// Four launches on the caller's stream:
+//   pass 1  every superchunk of G chunks but the last: its gate factors (one
+//           small kernel), then its local end state dS, dn from a zero state
+//           (m = -inf) as one dense product; dS, dn, the log scale mu and the
+//           total log decay A go to the workspace.
 //   pass 2  per state element, a scan over superchunks
 //           m' = max(A + m, mu); S' = 2^{A+m-m'} S + 2^{mu-m'} dS
 //           leaves the start state of every superchunk in the workspace.
@@ -32,6 +33,8 @@
 // fp32 state slice lives in registers as MFMA accumulator tiles for the whole
 // superchunk.  Its rows are stored in a permuted order (perm_row) so that the
 // accumulator registers are directly the A operand of the readout MFMA.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -92,6 +95,23 @@ __device__ __forceinline__ bf16x8 scale_frag(bf16x8 x, const float* w) {
 }
 __device__ __forceinline__ float scale_frag(float x, const float* w) { return x * w[0]; }
 
+// Row padding (elements) of a token-major LDS tile: the smallest padding that
+// makes a row step move the bank by one of the given residues (mod 64 dwords).
+// Tiles read with 16-byte fragment loads over 16 rows use 8 + 16i; tiles read
+// only with transposing reads (4 rows x 32 bytes per 16 lanes) use 12, 28, 36,
+// 52.  Both choices were the fastest in a sweep on MI355X.
+constexpr int lds_row_pad(int row_elems, int esize, bool transposing) {
+  const int dw = row_elems * esize / 4;
+  int best = 64;
+  const int rq[4] = {8, 24, 40, 56}, rv[4] = {12, 28, 36, 52};
+  for (int i = 0; i < 4; ++i) {
+    const int r = transposing ? rv[i] : rq[i];
+    const int pad = ((r - dw % 64) % 64 + 64) % 64;
+    if (pad < best) best = pad;
+  }
+  return best * 4 / esize;
+}
+
 template <typename T, int DQK, int NB, int WC, int NRG, int L>
 struct ChunkCfg {
   static constexpr int K = Mma<T>::K;
@@ -111,24 +131,9 @@ struct ChunkCfg {
   static constexpr int NKQR = RPW / K;            // feature k-blocks of a wave's rows
   static constexpr int NTQK = NJT * (NJT + 1) / 2;  // causal score tiles
   static constexpr int VE = 16 / (int)sizeof(T);  // elements per 16 bytes
-  // Row strides (elements) of the token-major tiles: the smallest padding
-  // that makes a row step move the bank by one of the given residues (mod 64
-  // dwords).  Q/K (16-byte fragment reads, 16 rows) use 8 + 16i; V (only
-  // transposing reads, 4 rows x 32 bytes per 16 lanes) uses 12, 28, 36, 52.
-  // Both choices were the fastest in a sweep on MI355X.
-  static constexpr int pad_for(int row_elems, bool v) {
-    const int dw = row_elems * (int)sizeof(T) / 4;
-    int best = 64;
-    const int rq[4] = {8, 24, 40, 56}, rv[4] = {12, 28, 36, 52};
-    for (int i = 0; i < 4; ++i) {
-      const int r = v ? rv[i] : rq[i];
-      const int pad = ((r - dw % 64) % 64 + 64) % 64;
-      if (pad < best) best = pad;
-    }
-    return best * 4 / (int)sizeof(T);
-  }
-  static constexpr int QS = DQK + pad_for(DQK, false);  // sQ, sK
-  static constexpr int VS = W + pad_for(W, true);       // sV
+  // row strides (elements) of the token-major tiles
+  static constexpr int QS = DQK + lds_row_pad(DQK, (int)sizeof(T), false);  // sQ, sK
+  static constexpr int VS = W + lds_row_pad(W, (int)sizeof(T), true);       // sV
   static constexpr int PS = L + 16 / (int)sizeof(T);  // sP
   // staging units (16-byte loads) per chunk
   static constexpr int NQU = L * DQK / VE;
@@ -140,18 +145,16 @@ struct ChunkCfg {
   static_assert(L % K == 0 && L % 16 == 0 && L <= 64, "chunk length");
   static_assert(NJT % NRG == 0, "token tiles per row group");
   static_assert(WC % 16 == 0, "wave columns");
-  static constexpr size_t lds_bytes(bool full, bool ret) {
+  static constexpr size_t lds_bytes(bool ret) {
     size_t b = 0;
     b += (size_t)L * QS * sizeof(T);             // sK
     b += (size_t)L * VS * sizeof(T);             // sV
     b += 6 * L * 4 + 16;                         // gate vectors
-    if (!ret) b += DQK * 4 + (full ? 16 * DQK * sizeof(T) : 0);  // n~
-    if (full) {
-      b += (size_t)L * QS * sizeof(T);           // sQ
-      b += (size_t)NB * L * PS * sizeof(T);      // sP
-      b += (size_t)(NJT + 1) * L * 4;            // den partials
-      if (NRG > 1) b += (size_t)4 * NJT * CT * 64 * 16;  // readout exchange
-    }
+    if (!ret) b += DQK * 4 + 16 * DQK * sizeof(T);  // n~
+    b += (size_t)L * QS * sizeof(T);             // sQ
+    b += (size_t)NB * L * PS * sizeof(T);        // sP
+    b += (size_t)(NJT + 1) * L * 4;              // den partials
+    if (NRG > 1) b += (size_t)4 * NJT * CT * 64 * 16;  // readout exchange
     return b;
   }
 };
@@ -178,8 +181,8 @@ __device__ __forceinline__ float frag_rows(const float* tile, int RS, int r0, in
   return tile[r0 * RS + ccol];
 }
 
-// Main kernel.  FULL = true: pass 3 (readout, outputs, update).  FULL = false:
-// pass 1 (update only, from a zero state).
+// Pass 3: per (batch*head, superchunk, d_v slice), the chunks of the
+// superchunk in order from its start state: readout, outputs, update.
 //
 // Work-group = 4 column groups x NRG row groups of waves.  Wave (cg, rg) owns
 // columns [cg*WC, cg*WC+WC) of the work-group's d_v slice and state rows
@@ -188,7 +191,7 @@ __device__ __forceinline__ float frag_rows(const float* tile, int RS, int r0, in
 // the token tiles and the two partial sums meet in LDS (sX).
 // Q, K and V are staged token-major with plain 16-byte copies; the operands
 // that run along tokens (K^T and V^T) are read with transposing LDS reads.
-template <typename T, int DQK, int NB, int WC, int NRG, int L, bool RET, bool FULL>
+template <typename T, int DQK, int NB, int WC, int NRG, int L, bool RET, bool HAS_O>
 __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
   using C = ChunkCfg<T, DQK, NB, WC, NRG, L>;
   using M = Mma<T>;
@@ -198,21 +201,21 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
   constexpr int W = C::W, NJT = C::NJT, NKL = C::NKL, NKQ = C::NKQ, NKQB = C::NKQB, NKQR = C::NKQR;
   constexpr int VE = C::VE, QS = C::QS, VS = C::VS, PS = C::PS;
   constexpr unsigned ES = sizeof(T);
-  constexpr bool XCH = FULL && NRG > 1;
+  constexpr bool XCH = NRG > 1;
   constexpr bool BF = sizeof(T) == 2;
 
   __shared__ __attribute__((aligned(16))) T sK[L * QS];   // K, token-major
   __shared__ __attribute__((aligned(16))) T sV[L * VS];   // V slice, token-major
-  __shared__ __attribute__((aligned(16))) T sQ[FULL ? L * QS : 8];   // Q, token-major
-  __shared__ __attribute__((aligned(16))) T sP[FULL ? NB * L * PS : 8];
+  __shared__ __attribute__((aligned(16))) T sQ[L * QS];   // Q, token-major
+  __shared__ __attribute__((aligned(16))) T sP[NB * L * PS];
   __shared__ __attribute__((aligned(16))) f32x4 sX[XCH ? 4 * NJT * CT * 64 : 1];
   // n~ as a 16-row A-operand tile: row 0 = bf16 hi part, row 1 = lo part,
   // rows 2..15 zero (fp32: row 0 = n~, row 1 zero)
-  __shared__ __attribute__((aligned(16))) T sNh[RET || !FULL ? 8 : 16 * DQK];
+  __shared__ __attribute__((aligned(16))) T sNh[RET ? 8 : 16 * DQK];
   __shared__ float sNf[RET ? 4 : DQK];
   __shared__ float sA2[L], sM2[L], sRS[L], sCL[L], sBT[L], sW[L];
-  __shared__ float sDenPart[FULL ? NJT * L : 4];
-  __shared__ float sDenInter[FULL ? L : 4];
+  __shared__ float sDenPart[NJT * L];
+  __shared__ float sDenInter[L];
   __shared__ float sAlpha;
 
   const int tid = threadIdx.x;
@@ -250,16 +253,16 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
                             RET ? 0u : (unsigned)T_ * ES);
   const auto rf = make_rsrc(RET ? nullptr : static_cast<const T*>(p.f_pre) + (size_t)bh * T_,
                             RET ? 0u : (unsigned)T_ * ES);
-  const bool has_o = FULL && p.o_pre != nullptr;
+  constexpr bool has_o = HAS_O;  // output gate present (o_pre not null)
   const auto ro = make_rsrc(has_o ? static_cast<const T*>(p.o_pre) + (size_t)bh * T_ * DV : nullptr,
                             has_o ? (unsigned)T_ * DV * ES : 0u);
-  T* __restrict__ gh = FULL ? static_cast<T*>(p.h) + (size_t)bh * T_ * DV : nullptr;
+  const auto rh = make_rsrc(static_cast<T*>(p.h) + (size_t)bh * T_ * DV, (unsigned)T_ * DV * ES);
   const float bias = (!RET && p.bias) ? p.bias[hd] : 0.f;
   float ret_lg2 = 0.f;
   if constexpr (RET) ret_lg2 = log2f(p.ret_gamma ? p.ret_gamma[hd] : 1.f - exp2f(-5.f - (float)hd));
 
   const int c_begin = sc * p.G;
-  const int c_end = FULL ? min(c_begin + p.G, p.NC) : c_begin + p.G;
+  const int c_end = min(c_begin + p.G, p.NC);
 
   // Source columns of the transposing reads.  K^T (update A operand): output
   // lane lr must see feature rb0 + perm_row(nt, lr).  V^T (PV A operand and
@@ -270,7 +273,7 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
   // ---------------------------------------------------------------- state in
   f32x4 st[NT][CT];
   const float* Sin = nullptr;
-  if (FULL && (sc > 0 || p.has_init)) Sin = p.ws_state + ((size_t)bh * p.NS + sc) * NSTATE;
+  if (sc > 0 || p.has_init) Sin = p.ws_state + ((size_t)bh * p.NS + sc) * NSTATE;
   // state element (nt, ct, i) of this lane sits at soff + (uni(nt,i)*DVB + ct*16)
   const int soff = blk * DQKB * DVB + (rrow0 + perm_row_lane<T>(lg)) * DVB + wcl0 + lr;
 #pragma unroll
@@ -283,51 +286,43 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
   // n~ in fp32 and as the hi/lo rows of the den tile
   auto put_n = [&](int r, float x) __attribute__((always_inline)) {
     sNf[r] = x;
-    if constexpr (FULL) {
-      const T hi = from_f32<T>(x);
-      sNh[r] = hi;
-      sNh[DQK + r] = from_f32<T>(x - to_f32(hi));
-    }
+    const T hi = from_f32<T>(x);
+    sNh[r] = hi;
+    sNh[DQK + r] = from_f32<T>(x - to_f32(hi));
   };
   if constexpr (!RET) {
-    if constexpr (FULL)
-      for (int e = tid; e < 16 * DQK; e += NTH) sNh[e] = from_f32<T>(0.f);
+    for (int e = tid; e < 16 * DQK; e += NTH) sNh[e] = from_f32<T>(0.f);
     __syncthreads();
     for (int r = tid; r < DQK; r += NTH) put_n(r, Sin ? Sin[CS + r] : 0.f);
   }
-  if constexpr (FULL) {
-    // masked (l > j) tiles of P and their den partials are never written
-    for (int e = tid; e < NB * L * PS; e += NTH) sP[e] = from_f32<T>(0.f);
-    for (int e = tid; e < NJT * L; e += NTH) sDenPart[e] = 0.f;
-  }
+  // masked (l > j) tiles of P and their den partials are never written
+  for (int e = tid; e < NB * L * PS; e += NTH) sP[e] = from_f32<T>(0.f);
+  for (int e = tid; e < NJT * L; e += NTH) sDenPart[e] = 0.f;
   // The registers hold S^ = S~ / 2^{sig}: the per-chunk decay of the state is
   // folded into sig (a wave-uniform scalar) instead of multiplying every
   // state element; new contributions are weighted by 2^{-sig}, the readout by
   // 2^{sig}.  When sig drops below -64 the registers are rescaled once.
   float sig = 0.f;
   // stabiliser carried by wave 0 (log2 units)
-  float m_prev = FULL ? p.ws_min[(size_t)bh * p.NS + sc] : -INFINITY;
-  float a_total = 0.f;
+  float m_prev = p.ws_min[(size_t)bh * p.NS + sc];
 
   // ------------------------------------------------------ staging registers
   // All global loads are unconditional buffer loads (units past the end of a
   // staging loop reload a valid unit and are not stored).  The next chunk's
   // loads are issued during the current chunk and written to LDS at its end,
   // so no staging register lives across a loop iteration.
-  Vec16<T> rgq[FULL ? C::QIT : 1];
+  Vec16<T> rgq[C::QIT];
   Vec16<T> rgk[C::QIT];
   Vec16<T> rgv[C::VIT];
   float rgi = 0.f, rgf = 0.f;
 
   auto load_q = [&](int c) __attribute__((always_inline)) {
     const unsigned t0 = (unsigned)c * L;
-    if constexpr (FULL) {
 #pragma unroll
-      for (int it = 0; it < C::QIT; ++it) {
-        const int u = (tid + it * NTH) % C::NQU;
-        const unsigned j = u / (DQK / VE), col = (u % (DQK / VE)) * VE;
-        rgq[it] = bload16<T>(rq, ((t0 + j) * DQK + col) * ES);
-      }
+    for (int it = 0; it < C::QIT; ++it) {
+      const int u = (tid + it * NTH) % C::NQU;
+      const unsigned j = u / (DQK / VE), col = (u % (DQK / VE)) * VE;
+      rgq[it] = bload16<T>(rq, ((t0 + j) * DQK + col) * ES);
     }
   };
 
@@ -357,8 +352,7 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
       const int u = tid + it * NTH;
       if (u < C::NQU) {
         const int j = u / (DQK / VE), col = (u % (DQK / VE)) * VE;
-        if constexpr (FULL)
-          *reinterpret_cast<uint4*>(&sQ[j * QS + col]) = *reinterpret_cast<const uint4*>(rgq[it].v);
+        *reinterpret_cast<uint4*>(&sQ[j * QS + col]) = *reinterpret_cast<const uint4*>(rgq[it].v);
         *reinterpret_cast<uint4*>(&sK[j * QS + col]) = *reinterpret_cast<const uint4*>(rgk[it].v);
       }
     }
@@ -412,7 +406,6 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
     }
     if (lane == 0) sAlpha = m_prev - ML;  // log2 of the state decay over the chunk
     m_prev = bL + ML;
-    a_total += bL;
   };
 
   // Prime the first chunk.
@@ -425,16 +418,9 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
     const int t0 = c * L;
     __syncthreads();  // B1: chunk staged, gate factors ready
     const bool more = c + 1 < c_end;
-    // pass 1 prefetches at the top; pass 3 after its second barrier, so that
-    // the readout (its register peak) holds no staging registers
-    if (!FULL && more) {
-      load_q(c + 1);
-      load_kv(c + 1);
-    }
-
     // update of the state is needed unless this is the last chunk of a
     // superchunk whose end state nobody reads
-    const bool need_update = !FULL || more || (sc == p.NS - 1);
+    const bool need_update = more || (sc == p.NS - 1);
 
     frag vf[CT][NKL];  // V^T fragments of this wave's columns
     auto load_vf = [&]() __attribute__((always_inline)) {
@@ -443,9 +429,7 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
 #pragma unroll
         for (int kb = 0; kb < NKL; ++kb) vf[ct][kb] = frag_rows(sV, VS, kb * K + KL * lg, lr, vcol + ct * 16);
     };
-    if constexpr (!FULL) load_vf();
-
-    if constexpr (FULL) {
+    {
       // ---------------------------------------------------------- phase B
       // causal score tiles (key tile lt, query tile jt), spread over the waves
 #pragma unroll
@@ -544,6 +528,17 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
             for (int ct = 0; ct < CT; ++ct) sX[((cg * NJT + jt) * CT + ct) * 64 + lane] = acc[jt][ct];
       }
       __syncthreads();  // B2: P, den partials and readout partials ready
+      // output-gate values of this wave's outputs, issued before the next
+      // chunk's loads so that using them does not wait for those
+      Raw4<T> oraw[has_o ? JPW : 1][has_o ? CT : 1];
+      if constexpr (has_o) {
+#pragma unroll
+        for (int jj = 0; jj < JPW; ++jj)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            oraw[jj][ct] = bload4_raw<T>(
+                ro, ((unsigned)(t0 + (jt0 + jj) * 16 + lr) * DV + wcol0 + ct * 16 + 4 * lg) * ES);
+      }
       if (more) {
         load_kv(c + 1);
         load_q(c + 1);
@@ -587,21 +582,18 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
           for (int t = 0; t < NJT; ++t) den += sDenPart[t * L + j];
           inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), sCL[j]));
         }
-        if (t0 + j < T_) {
+        // rows past T fall outside the output buffer and are dropped
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            const int col = wcol0 + ct * 16 + 4 * lg;
-            float o[4] = {1.f, 1.f, 1.f, 1.f};
-            if (has_o) {
-              bload4<T>(ro, ((unsigned)(t0 + j) * DV + col) * ES, o);
+        for (int ct = 0; ct < CT; ++ct) {
+          const int col = wcol0 + ct * 16 + 4 * lg;
+          float o[4] = {1.f, 1.f, 1.f, 1.f};
+          if constexpr (has_o) {
+            raw4_to_f32<T>(oraw[jj][ct], o);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) o[i] = sigmoidf_(o[i]);
-            }
-            T hv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) hv[i] = from_f32<T>(o[i] * o_acc[ct][i] * inv);
-            store4(gh + (size_t)(t0 + j) * DV + col, hv[0], hv[1], hv[2], hv[3]);
+            for (int i = 0; i < 4; ++i) o[i] = sigmoidf_(o[i]);
           }
+          bstore4<T>(rh, ((unsigned)(t0 + j) * DV + col) * ES, o[0] * o_acc[ct][0] * inv,
+                     o[1] * o_acc[ct][1] * inv, o[2] * o_acc[ct][2] * inv, o[3] * o_acc[ct][3] * inv);
         }
       }
     }
@@ -688,8 +680,7 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
 
   // ---------------------------------------------------------------- outputs
   float* Sdst = nullptr;
-  if (!FULL) Sdst = p.ws_state + ((size_t)bh * p.NS + sc + 1) * NSTATE;
-  else if (sc == p.NS - 1 && p.C_out) Sdst = p.C_out + (size_t)bh * CS;  // [B,H,NB,DQKB,DVB]
+  if (sc == p.NS - 1 && p.C_out) Sdst = p.C_out + (size_t)bh * CS;  // [B,H,NB,DQKB,DVB]
   if (Sdst) {
     const float f = exp2_fast(sig);
     int so = soff;
@@ -701,21 +692,391 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) Sdst[so + perm_row_uni<T>(nt, i) * DVB + ct * 16] = st[nt][ct][i] * f;
   }
-  if (slice == 0) {
-    if (!FULL) {
-      float* nd = p.ws_state + ((size_t)bh * p.NS + sc + 1) * NSTATE + CS;
-      if constexpr (!RET)
-        for (int r = tid; r < DQK; r += NTH) nd[r] = sNf[r];
-      if (tid == 0) {
-        p.ws_scal[((size_t)bh * p.NS + sc) * 2 + 0] = a_total;
-        p.ws_scal[((size_t)bh * p.NS + sc) * 2 + 1] = m_prev;
+  if (slice == 0 && sc == p.NS - 1) {
+    if constexpr (!RET) {
+      if (p.n_out)
+        for (int r = tid; r < DQK; r += NTH) p.n_out[(size_t)bh * DQK + r] = sNf[r];
+    }
+    if (tid == 0 && p.m_out) p.m_out[bh] = m_prev * kLn2;
+  }
+}
+
+// Pass 1a (superchunk_gate_kernel): the gate factors of every superchunk but
+// the last.  With b_t = sum_{r<=t} log2 sigmoid(f_r) and a_t = log2(i_t) - b_t
+// inside the superchunk (t = 0 .. G*L-1) and amax = max_t a_t, it writes
+// w_t = 2^{a_t - amax} for every token, the total log2 decay A = b_end and the
+// log2 scale mu = b_end + amax of the superchunk's local state (the stabiliser
+// the token recurrence reaches from m = -inf).  One work-group of 4 waves per
+// (batch*head, superchunk): the waves take 64-token groups in turn, scan them
+// with DPP, and the group totals meet in LDS.
+
+// inclusive prefix sum over the 64 lanes of a wave: rows of 16 lanes by
+// row shifts, then the row totals by row broadcasts (lanes without a source
+// add 0)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_or_zero(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  x += dpp_or_zero<0x111, 0xF>(x);  // row_shr:1
+  x += dpp_or_zero<0x112, 0xF>(x);  // row_shr:2
+  x += dpp_or_zero<0x114, 0xF>(x);  // row_shr:4
+  x += dpp_or_zero<0x118, 0xF>(x);  // row_shr:8
+  x += dpp_or_zero<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_or_zero<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+template <typename T, bool RET>
+__global__ __launch_bounds__(256) void superchunk_gate_kernel(ChunkParams p, int L) {
+  constexpr int GPW = 4;  // 64-token groups per wave, at most (superchunks of <= 1024 tokens)
+  __shared__ float stot[4 * GPW];
+  __shared__ float smax[4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int BH = p.B * p.H, T_ = p.T;
+  const int bh = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % BH));
+  const int sc = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / BH));
+  const int hd = bh % p.H;
+  const int GL = p.G * L, tb = sc * GL;
+  const int NG = (GL + 63) / 64;
+  constexpr unsigned ES = sizeof(T);
+  const auto ri = make_rsrc(RET ? nullptr : static_cast<const T*>(p.i_pre) + (size_t)bh * T_,
+                            RET ? 0u : (unsigned)T_ * ES);
+  const auto rf = make_rsrc(RET ? nullptr : static_cast<const T*>(p.f_pre) + (size_t)bh * T_,
+                            RET ? 0u : (unsigned)T_ * ES);
+  float ret_lg2 = 0.f;
+  if constexpr (RET) ret_lg2 = log2f(p.ret_gamma ? p.ret_gamma[hd] : 1.f - exp2f(-5.f - (float)hd));
+
+  float gi[GPW], gf[GPW], bl[GPW], li[GPW];
+#pragma unroll
+  for (int k = 0; k < GPW; ++k) {
+    const unsigned t = (unsigned)(tb + (w + 4 * k) * 64 + lane);
+    gi[k] = gf[k] = 0.f;
+    if constexpr (!RET) {
+      gi[k] = bload1<T>(ri, t * ES);
+      gf[k] = bload1<T>(rf, t * ES);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < GPW; ++k) {
+    const int g = w + 4 * k;
+    const int tl = g * 64 + lane;  // token within the superchunk
+    const bool valid = g < NG && tl < GL && tb + tl < T_;
+    float lf2;
+    if constexpr (RET) {
+      lf2 = valid ? ret_lg2 : 0.f;
+      li[k] = valid ? 0.f : -INFINITY;
+    } else {
+      lf2 = valid ? log2_sigmoid(gf[k]) : 0.f;
+      li[k] = valid ? gi[k] * kLog2e : -INFINITY;
+    }
+    bl[k] = wave_prefix_sum(lf2);
+    if (g < NG && lane == 63) stot[g] = bl[k];
+  }
+  __syncthreads();
+  float amax = -INFINITY, carry = 0.f;
+  int gdone = 0;
+#pragma unroll
+  for (int k = 0; k < GPW; ++k) {
+    const int g = w + 4 * k;
+    if (g < NG) {
+      for (; gdone < g; ++gdone) carry += stot[gdone];
+      const float a = li[k] - (carry + bl[k]);
+      amax = fmaxf(amax, a);
+      bl[k] = a;
+    }
+  }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 64));
+  if (lane == 0) smax[w] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+  float* wout = p.ws_w + (size_t)bh * T_ + tb;
+#pragma unroll
+  for (int k = 0; k < GPW; ++k) {
+    const int g = w + 4 * k;
+    const int tl = g * 64 + lane;
+    if (g < NG && tl < GL) wout[tl] = exp2_fast(bl[k] - amax);
+  }
+  if (tid == 0) {
+    float b_end = 0.f;
+    for (int g = 0; g < NG; ++g) b_end += stot[g];
+    p.ws_scal[((size_t)bh * p.NS + sc) * 2 + 0] = b_end;
+    p.ws_scal[((size_t)bh * p.NS + sc) * 2 + 1] = b_end + amax;
+  }
+}
+
+// Pass 1b (local_state_kernel): the local end state of every superchunk but
+// the last from the gate factors above:
+//   dS = sum_t w_t k_t v_t^T,   dn = sum_t w_t k_t.
+// Nothing chains from chunk to chunk, so this is one dense product (w.K)^T V
+// per superchunk and state tile.
+//
+// Work-group = 4 waves on a TR x TC tile of one memory block, WR x WCW waves
+// (4 x 1 when the tile has 64 or more rows: each wave owns TR/4 rows and all
+// TC columns).  K-steps of KS tokens run through a ring
+// of 4 LDS stages filled by direct global-to-LDS buffer loads issued 3 steps
+// ahead, so no staging registers hold data in flight.  A stage holds KS token
+// rows of K and of V, row-major with padded rows; one load instruction fills
+// 1 KB (lane l writes bytes 16l .. 16l+15), so each lane fetches the 16-byte
+// unit of the padded tile that lands in its slot, and pad slots read past the
+// end of the buffer (zero).  Both MFMA operands come from transposing LDS
+// reads; the K^T fragments are multiplied by w_t in registers (w of the whole
+// superchunk sits in LDS), which is also where dn is summed.
+template <typename T, int TR, int TC, int KS>
+struct LocalCfg {
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int VE = 16 / ES;
+  // row strides: residue 8 + 16i dwords (a 128-wide bf16 row pads to
+  // 288 bytes, so a 32-row region is exactly 9 KB)
+  static constexpr int RK = TR + lds_row_pad(TR, ES, false);
+  static constexpr int RV = TC + lds_row_pad(TC, ES, false);
+  static constexpr int UK = RK * ES / 16;  // 16-byte units per padded K row
+  static constexpr int UV = RV * ES / 16;
+  static constexpr int NIK = (KS * RK * ES + 1023) / 1024;  // load instructions per K region
+  static constexpr int NIV = (KS * RV * ES + 1023) / 1024;
+  static constexpr int NI = NIK + NIV;
+  static constexpr int JA = (NI + 3) / 4;  // instructions per wave (every wave issues JA)
+  static constexpr int STAGE = NI * 1024;  // bytes per stage: K region, then V region
+  static constexpr int WR = TR >= 64 ? 4 : TR / 16;  // waves along rows
+  static constexpr int WCW = 4 / WR;                  // waves along columns
+  static constexpr int MT = TR / WR / 16;             // 16-row tiles per wave
+  static constexpr int NTc = TC / WCW / 16;           // 16-column tiles per wave
+  static constexpr int GLMAX = 1024;                  // superchunk tokens (w in LDS)
+  static_assert(TR % (16 * WR) == 0 && TC % (16 * WCW) == 0 && WR * WCW == 4, "tile");
+  static_assert((RK * ES) % 16 == 0 && (RV * ES) % 16 == 0, "rows of whole 16-byte units");
+};
+
+// s_waitcnt with only a vmcnt limit (gfx9 encoding, expcnt and lgkmcnt left
+// at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// LDS accesses of this wave done, then a work-group barrier; the empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// fragment times per-k weights (KL consecutive k)
+__device__ __forceinline__ bf16x8 scale_frag8(bf16x8 x, const float (&w)[8], float (&dn)) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float kv = (float)x[e];
+    dn += w[e] * kv;
+    r[e] = (__bf16)(kv * w[e]);
+  }
+  return r;
+}
+
+template <typename T, int DQK, int NB, int TR, int TC, int L, bool RET>
+__global__ __launch_bounds__(256) void local_state_kernel(ChunkParams p) {
+  constexpr int KS = sizeof(T) == 2 ? 32 : 16;
+  using C = LocalCfg<T, TR, TC, KS>;
+  using M = Mma<T>;
+  typedef typename M::frag frag;
+  constexpr int K = M::K, KL = M::KL, RK = C::RK, RV = C::RV, VE = C::VE;
+  constexpr int MT = C::MT, NTc = C::NTc, NKL = KS / K, JA = C::JA, WR = C::WR, WCW = C::WCW;
+  constexpr int DQKB = DQK / NB, NRT = DQKB / TR;
+  constexpr unsigned ES = sizeof(T);
+  constexpr bool BF = sizeof(T) == 2;
+  static_assert(L % KS == 0, "superchunks of whole k-steps");
+
+  // ring of 4 stages (separate arrays, so that the compiler's own wait
+  // tracking tells their loads apart) and w of the superchunk
+  __shared__ __attribute__((aligned(1024))) unsigned char ring0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring2[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring3[C::STAGE];
+  __shared__ __attribute__((aligned(16))) float sw[C::GLMAX];
+  auto stage_ptr = [&](auto bidx) -> unsigned char* {
+    constexpr int b = decltype(bidx)::value;
+    if constexpr (b == 0) return ring0;
+    else if constexpr (b == 1) return ring1;
+    else if constexpr (b == 2) return ring2;
+    else return ring3;
+  };
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = w % WR, wcw = w / WR;
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int BH = p.B * p.H, DV = p.DV, DVB = DV / NB, T_ = p.T;
+  const int nct = DVB / TC;
+  const int ntile = NB * NRT * nct;
+  const int idx = blockIdx.x;
+  const int bh = __builtin_amdgcn_readfirstlane(idx % BH);
+  const int tile = __builtin_amdgcn_readfirstlane((idx / BH) % ntile);
+  const int sc = __builtin_amdgcn_readfirstlane((idx / BH) / ntile);
+  const int blk = tile / (NRT * nct), rt = (tile / nct) % NRT, ctl = tile % nct;
+  const int f0 = blk * DQKB + rt * TR;  // first feature (of the head) of the tile
+  const int c0 = blk * DVB + ctl * TC;  // first d_v column of the tile
+  const size_t CS = (size_t)DQK * DVB;
+  const size_t NSTATE = CS + (RET ? 0 : DQK);
+
+  const auto rk = make_rsrc(static_cast<const T*>(p.k) + (size_t)bh * T_ * DQK, (unsigned)T_ * DQK * ES);
+  const auto rv = make_rsrc(static_cast<const T*>(p.v) + (size_t)bh * T_ * DV, (unsigned)T_ * DV * ES);
+
+  const int GL = p.G * L;
+  const int tb = sc * GL;            // first token of the superchunk
+  const int NSTEP = p.G * (L / KS);  // k-steps of the superchunk
+
+  // per-lane byte offsets of the loaded units relative to the step's first
+  // token (the token part goes into the scalar offset); pad slots point past
+  // any buffer end.  Every wave issues exactly JA loads per step on every
+  // path, also past the last step (clamped to it; those stages are never
+  // read), so that the vm counter advances identically on all paths and the
+  // waits name exact counts; a wave with fewer than JA instructions in the
+  // stage repeats its previous one (same bytes to the same slot).
+  unsigned voff[JA];
+#pragma unroll
+  for (int j = 0; j < JA; ++j) {
+    const int i = w + 4 * j;
+    voff[j] = 0xFFFFFFF0u;
+    if (i < C::NIK) {
+      const int unit = i * 64 + lane, row = unit / C::UK, cu = unit % C::UK;
+      if (row < KS && cu < TR / VE) voff[j] = (unsigned)(row * DQK + f0 + cu * VE) * ES;
+    } else if (i < C::NI) {
+      const int unit = (i - C::NIK) * 64 + lane, row = unit / C::UV, cu = unit % C::UV;
+      if (row < KS && cu < TC / VE) voff[j] = (unsigned)(row * DV + c0 + cu * VE) * ES;
+    } else {
+      voff[j] = voff[j - 1];
+    }
+  }
+  auto issue = [&](int s_, auto bidx) __attribute__((always_inline)) {
+    unsigned char* st = stage_ptr(bidx);
+    const int s = min(s_, NSTEP - 1);
+    const unsigned t0 = (unsigned)(tb + s * KS);
+    const int sk = __builtin_amdgcn_readfirstlane((int)(t0 * DQK * ES));
+    const int sv = __builtin_amdgcn_readfirstlane((int)(t0 * DV * ES));
+#pragma unroll
+    for (int j = 0; j < JA; ++j) {
+      const int i0 = w + 4 * j;  // wave-uniform
+      const int i = i0 < C::NI ? i0 : i0 - 4;
+      const bool isk = i < C::NIK;
+      dma16_to_lds(isk ? rk : rv, st + i * 1024, voff[j], isk ? sk : sv);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  constexpr int NV = JA;  // vm operations of one step of one wave
+
+  // the first three steps in flight, then w of the superchunk into LDS
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  {
+    // w loads are issued before the ring loads, so waiting for them does not
+    // wait for the ring
+    const float* wsrc = p.ws_w + (size_t)bh * T_ + tb;
+    float wv[C::GLMAX / 256];
+#pragma unroll
+    for (int u = 0; u < C::GLMAX / 256; ++u) {
+      const int t = tid + 256 * u;
+      wv[u] = t < GL ? wsrc[t] : 0.f;
+    }
+    issue(0, I0{});
+    issue(1, I1{});
+    issue(2, I2{});
+#pragma unroll
+    for (int u = 0; u < C::GLMAX / 256; ++u) sw[tid + 256 * u] = wv[u];
+  }
+
+  const bool do_dn = !RET && ctl == 0 && wcw == 0;  // one column tile and wave per row sums dn
+  float dn[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) dn[mt] = 0.f;
+  f32x4 acc[MT][NTc];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTc; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // transposing-read source columns: output lane lr sees column base + lr
+  const int acol = BF ? wr * (TR / WR) + 4 * (lr & 3) : wr * (TR / WR) + lr;
+  const int bcol = BF ? wcw * (TC / WCW) + 4 * (lr & 3) : wcw * (TC / WCW) + lr;
+  auto mfma = [&](int c, auto bidx) __attribute__((always_inline)) {
+    const unsigned char* st = stage_ptr(bidx);
+    const T* sk = reinterpret_cast<const T*>(st);
+    const T* sv = reinterpret_cast<const T*>(st + C::NIK * 1024);
+#pragma unroll
+    for (int kb = 0; kb < NKL; ++kb) {
+      const int r0 = kb * K + KL * lg;  // first token of this lane's k elements
+      float wk[KL];
+#pragma unroll
+      for (int e = 0; e < KL; ++e) wk[e] = sw[c * KS + r0 + e];
+      frag af[MT], bfr[NTc];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) af[mt] = frag_rows(sk, RK, r0, lr, acol + mt * 16);
+#pragma unroll
+      for (int nt = 0; nt < NTc; ++nt) bfr[nt] = frag_rows(sv, RV, r0, lr, bcol + nt * 16);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if constexpr (BF) {
+          float d = 0.f;
+          af[mt] = scale_frag8(af[mt], wk, d);
+          dn[mt] += d;
+        } else {
+          dn[mt] += wk[0] * af[mt];
+          af[mt] *= wk[0];
+        }
       }
-    } else if (sc == p.NS - 1) {
-      if constexpr (!RET) {
-        if (p.n_out)
-          for (int r = tid; r < DQK; r += NTH) p.n_out[(size_t)bh * DQK + r] = sNf[r];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTc; ++nt) acc[mt][nt] = M::mma(af[mt], bfr[nt], acc[mt][nt]);
+    }
+  };
+
+  // ---- k-step c on stage b = c % 4: once this wave's loads of step c have
+  // landed, a barrier publishes the stage (and retires step c - 1's stage),
+  // step c + 3 goes into that freed stage, then the MFMAs of step c.  Steps
+  // past the end (the loop runs in groups of 4) only issue and wait.
+  auto body = [&](int c, auto bidx) __attribute__((always_inline)) {
+    constexpr int b = decltype(bidx)::value;
+    using B3 = std::integral_constant<int, (b + 3) % 4>;
+    wait_vmcnt<2 * NV>();
+    lds_barrier();
+    issue(c + 3, B3{});
+    if (c < NSTEP) mfma(c, bidx);
+  };
+  for (int c = 0; c < NSTEP; c += 4) {
+    body(c, I0{});
+    body(c + 1, I1{});
+    body(c + 2, I2{});
+    body(c + 3, I3{});
+  }
+  wait_vmcnt<0>();  // no load into the ring in flight past this point
+
+  // ---- outputs: slot sc + 1 of the workspace holds superchunk sc's local state
+  float* dst = p.ws_state + ((size_t)bh * p.NS + sc + 1) * NSTATE;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTc; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = rt * TR + wr * (TR / WR) + mt * 16 + 4 * lg + i;  // row within the block
+        const int cl = ctl * TC + wcw * (TC / WCW) + nt * 16 + lr;     // column within the block
+        dst[(size_t)blk * DQKB * DVB + (size_t)r * DVB + cl] = acc[mt][nt][i];
       }
-      if (tid == 0 && p.m_out) p.m_out[bh] = m_prev * kLn2;
+  if constexpr (!RET) {
+    if (do_dn) {
+      // lanes lr of the 4 lane groups hold partial sums of feature
+      // acol-row + mt*16 + lr over their k elements: fixed-order sum over them
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        float d = dn[mt];
+        d += __shfl_xor(d, 16, 64);
+        d += __shfl_xor(d, 32, 64);
+        if (lg == 0) dst[CS + f0 + wr * (TR / WR) + mt * 16 + lr] = d;
+      }
     }
   }
 }
@@ -766,7 +1127,7 @@ __global__ __launch_bounds__(256) void superchunk_scan_kernel(ScanParams p) {
 
 template <typename T, int DQK, int NB, int WC, int NRG, int L, bool RET>
 size_t chunk_lds_bytes() {
-  return ChunkCfg<T, DQK, NB, WC, NRG, L>::lds_bytes(true, RET);
+  return ChunkCfg<T, DQK, NB, WC, NRG, L>::lds_bytes(RET);
 }
 
 template <typename T, int DQK, int NB, int WC, int NRG, int L, bool RET>
@@ -775,8 +1136,20 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
   const int BH = p.B * p.H;
   const size_t CS = (size_t)DQK * p.DV / NB;
   if (p.NS > 1) {
-    dim3 g1((unsigned)(BH * p.nslices * (p.NS - 1)));
-    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, L, RET, false>), g1, dim3(NTH), 0, stream, p);
+    // pass 1 tiles: TR rows x TC columns of one memory block
+    constexpr int DQKB = DQK / NB;
+    constexpr int TCAP = sizeof(T) == 2 ? 128 : 64;
+    constexpr int TR = DQKB < TCAP ? DQKB : TCAP;
+    const int DVB = p.DV / NB;
+    const int TC = DVB % TCAP == 0 ? TCAP : DVB % 64 == 0 ? 64 : 32;
+    hipLaunchKernelGGL((superchunk_gate_kernel<T, RET>), dim3((unsigned)(BH * (p.NS - 1))), dim3(256), 0, stream, p, L);
+    const dim3 g1((unsigned)(BH * (p.NS - 1) * NB * (DQKB / TR) * (DVB / TC)));
+    if (TC == TCAP)
+      hipLaunchKernelGGL((local_state_kernel<T, DQK, NB, TR, TCAP, L, RET>), g1, dim3(256), 0, stream, p);
+    else if (TC == 64)
+      hipLaunchKernelGGL((local_state_kernel<T, DQK, NB, TR, 64, L, RET>), g1, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((local_state_kernel<T, DQK, NB, TR, 32, L, RET>), g1, dim3(256), 0, stream, p);
   }
   ScanParams s;
   s.NS = p.NS;
@@ -794,7 +1167,10 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
   hipLaunchKernelGGL((superchunk_scan_kernel<RET>), g2, dim3(256), 0, stream, s);
   dim3 g3((unsigned)(BH * p.nslices * p.NS));
   if (ev0) (void)hipEventRecord(ev0, stream);
-  hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, L, RET, true>), g3, dim3(NTH), 0, stream, p);
+  if (!RET && p.o_pre)
+    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, L, RET, !RET>), g3, dim3(NTH), 0, stream, p);
+  else
+    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, L, RET, false>), g3, dim3(NTH), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (ev1) (void)hipEventRecord(ev1, stream);
   return e;

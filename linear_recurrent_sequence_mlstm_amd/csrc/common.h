@@ -25,9 +25,15 @@ __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
 
-// log(sigmoid(x)) = min(x, 0) - log1p(exp(-|x|)), in log2 units.
+// log(sigmoid(x)) = min(x, 0) - log1p(exp(-|x|)), in log2 units.  log1p is
+// taken as log2(u) * e / (u - 1) with u = 1 + e (exact for e = 0 up to the
+// rounding of u; Goldberg's compensation), so hardware log2/exp2 suffice.
 __device__ __forceinline__ float log2_sigmoid(float x) {
-  return (fminf(x, 0.f) - log1pf(__expf(-fabsf(x)))) * kLog2e;
+  const float e = exp2_fast(-fabsf(x) * kLog2e);  // e^{-|x|} in (0, 1]
+  const float u = 1.f + e;
+  const float d = u - 1.f;
+  const float l = d == 0.f ? e * kLog2e : __builtin_amdgcn_logf(u) * (e * __builtin_amdgcn_rcpf(d));
+  return fminf(x, 0.f) * kLog2e - l;
 }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
@@ -124,6 +130,18 @@ __device__ __forceinline__ float bload1<__bf16>(__amdgpu_buffer_rsrc_t r, unsign
   return __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0) << 16);
 }
 
+// one element, raw bits (no conversion, so that the load need not complete
+// until the value is used)
+template <typename T>
+__device__ __forceinline__ unsigned bload1_raw(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
+  if constexpr (sizeof(T) == 2) return (unsigned)__builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0);
+  else return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
+}
+template <typename T>
+__device__ __forceinline__ float raw_to_f32(unsigned x) {
+  return __uint_as_float(sizeof(T) == 2 ? x << 16 : x);
+}
+
 // four consecutive elements as floats
 template <typename T>
 __device__ __forceinline__ void bload4(__amdgpu_buffer_rsrc_t r, unsigned byte_off, float (&x)[4]);
@@ -141,6 +159,54 @@ __device__ __forceinline__ void bload4<__bf16>(__amdgpu_buffer_rsrc_t r, unsigne
   x[3] = __uint_as_float(u[1] & 0xffff0000u);
 }
 
+// Four consecutive elements, raw bits (converted where used, so that the
+// load need not complete before then).
+template <typename T>
+struct Raw4;
+template <>
+struct Raw4<__bf16> {
+  u32x2 v;
+};
+template <>
+struct Raw4<float> {
+  u32x4 v;
+};
+template <typename T>
+__device__ __forceinline__ Raw4<T> bload4_raw(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
+  Raw4<T> x;
+  if constexpr (sizeof(T) == 2) x.v = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
+  else x.v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+  return x;
+}
+template <typename T>
+__device__ __forceinline__ void raw4_to_f32(const Raw4<T>& r, float (&x)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    x[0] = __uint_as_float(r.v[0] << 16);
+    x[1] = __uint_as_float(r.v[0] & 0xffff0000u);
+    x[2] = __uint_as_float(r.v[1] << 16);
+    x[3] = __uint_as_float(r.v[1] & 0xffff0000u);
+  } else {
+    for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(r.v[i]);
+  }
+}
+// Four consecutive elements converted to T and stored through a buffer
+// resource (stores past its end are dropped).
+template <typename T>
+__device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, unsigned byte_off, float a, float b, float c,
+                                        float d) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 v;
+    v[0] = (__bf16)a;
+    v[1] = (__bf16)b;
+    v[2] = (__bf16)c;
+    v[3] = (__bf16)d;
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, byte_off, 0, 0);
+  } else {
+    u32x4 v = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 0);
+  }
+}
+
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
 // lanes, output lane i holds element (i & 3) of the 4 elements that source lane
 // 4e + (i >> 2) addressed, for e = 0..3.  So if source lane s addresses row
@@ -151,6 +217,16 @@ __device__ __forceinline__ bf16x4 ds_read_tr16(const __bf16* p) {
   const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4*)(const_cast<__bf16*>(p)));
   return __builtin_bit_cast(bf16x4, v);
+}
+
+// Direct global-to-LDS load of 16 bytes per lane (gfx950 buffer_load_dwordx4
+// ... lds): lane l writes bytes [lds + 16 l, lds + 16 l + 16) of the wave-uniform
+// LDS address lds, read from voff + soff of the buffer (zero past its end).
+// It completes under vmcnt like any buffer load.  Kept in a device function:
+// the address-space cast must not appear in a kernel body that the host pass
+// also sees.
+__device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, unsigned voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
 // Four consecutive elements to an 8- (bf16) or 16-byte (fp32) aligned address.

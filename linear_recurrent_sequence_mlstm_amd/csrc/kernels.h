@@ -20,6 +20,7 @@ struct ChunkParams {
   float* ws_state;         // [B*H][NS][CS (+ d_qk)] superchunk start states
   float* ws_scal;          // [B*H][NS][2] (total log2 decay, local log2 scale)
   float* ws_min;           // [B*H][NS] stabiliser (log2) at superchunk starts
+  float* ws_w;             // [B*H][T] gate factors of the tokens in superchunks 0 .. NS-2
   int has_init;
   const float* C0;
   const float* n0;
