@@ -130,9 +130,9 @@ int mlstm_chunkwise_fwd(int B, int H, int T, int d_qk, int d_v, int num_blocks,
  *   NULL (dtype dt); norm_bias [H] fp32 or NULL;
  *   C [B,H,nb,d_qk/nb,d_v/nb], n [B,H,d_qk], m [B,H] fp32, read and written;
  *   h [B,H,d_v] output (dtype dt).
- * Requires d_v/nb a multiple of 4 and d_v a multiple of 32 up to 512, of 64
- * up to 1024, of 128 up to 2048 or of 256 up to 4096; other shapes return
- * MLSTM_E_UNSUPPORTED.
+ * Requires d_v a multiple of 16 and d_v/nb a multiple of 4; other shapes
+ * return MLSTM_E_UNSUPPORTED.  Two kernels are enqueued (the matrix state
+ * with the outputs, then n and m).
  */
 int mlstm_step(int B, int H, int d_qk, int d_v, int num_blocks, mlstm_dtype dt,
                const void* q, const void* k, const void* v, const void* i_pre,

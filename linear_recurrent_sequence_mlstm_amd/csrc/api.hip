@@ -43,7 +43,7 @@ struct Plan {
   mlstm::ChunkVariant var;
   int L, NC, G, NS, nslices;
   size_t CS, nstate;
-  size_t off_scal, off_min, off_w, bytes;
+  size_t off_scal, off_min, off_w, off_g, bytes;
 };
 
 // Checks shared by the mLSTM and retention chunkwise entry points and the
@@ -61,12 +61,11 @@ int plan_chunkwise(int B, int H, int T, int dqk, int dv, int nb, int chunk, int 
   if ((long long)B * H >= (1LL << 24)) return fail(MLSTM_E_SHAPE, "B * H too large");
   if (chunk != 16 && chunk != 32 && chunk != 64)
     return fail(MLSTM_E_SHAPE, "chunk must be 16, 32 or 64 (got %d)", chunk);
-  const int wc = (dt == MLSTM_BF16 && dqk / nb >= 128) ? 32 : 16;
-  if (!mlstm::find_chunk_variant(dt, dqk, nb, wc, chunk, ret, &pl->var))
+  if (!mlstm::find_chunk_variant(dt, dqk, nb, chunk, ret, &pl->var))
     return fail(MLSTM_E_UNSUPPORTED,
                 "no kernel for dtype=%s d_qk=%d num_blocks=%d chunk=%d%s", dt ? "bf16" : "fp32", dqk, nb,
                 chunk, ret ? " (retention)" : "");
-  const int W = 4 * pl->var.wc;
+  const int W = pl->var.w;
   if (dv % W || (dv / nb) % pl->var.wc)
     return fail(MLSTM_E_UNSUPPORTED, "d_v=%d must be a multiple of %d with d_v/num_blocks a multiple of %d",
                 dv, W, pl->var.wc);
@@ -94,7 +93,8 @@ int plan_chunkwise(int B, int H, int T, int dqk, int dv, int nb, int chunk, int 
   pl->off_scal = align256(BH * pl->NS * pl->nstate * sizeof(float));
   pl->off_min = pl->off_scal + align256(BH * pl->NS * 2 * sizeof(float));
   pl->off_w = pl->off_min + align256(BH * pl->NS * sizeof(float));
-  pl->bytes = pl->off_w + (pl->NS > 1 ? align256(BH * (size_t)T * sizeof(float)) : 0);
+  pl->off_g = pl->off_w + (pl->NS > 1 ? align256(BH * (size_t)T * sizeof(float)) : 0);
+  pl->bytes = pl->off_g + 3 * align256(BH * (size_t)pl->NC * chunk * sizeof(float));
   return MLSTM_OK;
 }
 
@@ -113,6 +113,10 @@ int launch(const Plan& pl, mlstm::ChunkParams& p, void* workspace, size_t worksp
   p.ws_scal = reinterpret_cast<float*>(ws + pl.off_scal);
   p.ws_min = reinterpret_cast<float*>(ws + pl.off_min);
   p.ws_w = reinterpret_cast<float*>(ws + pl.off_w);
+  const size_t gsz = align256((size_t)p.B * p.H * pl.NC * pl.L * sizeof(float));
+  p.ws_ga = reinterpret_cast<float*>(ws + pl.off_g);
+  p.ws_gg = reinterpret_cast<float*>(ws + pl.off_g + gsz);
+  p.ws_gb = reinterpret_cast<float*>(ws + pl.off_g + 2 * gsz);
   const hipError_t e = pl.var.launch(p, static_cast<hipStream_t>(stream), g_ev0, g_ev1);
   if (e != hipSuccess) return fail(MLSTM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

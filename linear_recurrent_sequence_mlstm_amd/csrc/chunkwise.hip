@@ -112,17 +112,30 @@ constexpr int lds_row_pad(int row_elems, int esize, bool transposing) {
   return best * 4 / esize;
 }
 
-template <typename T, int DQK, int NB, int WC, int NRG, int L>
+// Row padding (elements) that makes a row step move the bank by `res` dwords
+// (mod 64).
+constexpr int lds_pad_res(int row_elems, int esize, int res) {
+  const int dw = row_elems * esize / 4;
+  return (((res - dw % 64) % 64 + 64) % 64) * 4 / esize;
+}
+#ifndef MLSTM_P3_QRES
+#define MLSTM_P3_QRES 8
+#endif
+#ifndef MLSTM_P3_KRES
+#define MLSTM_P3_KRES 8
+#endif
+
+template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L>
 struct ChunkCfg {
   static constexpr int K = Mma<T>::K;
   static constexpr int KL = Mma<T>::KL;
-  static constexpr int NW = 4 * NRG;              // waves per work-group
+  static constexpr int NW = NCG * NRG;            // waves per work-group
   static constexpr int NTH = 64 * NW;             // threads per work-group
   static constexpr int DQKB = DQK / NB;           // rows of a memory block
   static constexpr int RPW = DQKB / NRG;          // state rows per wave
   static constexpr int NT = RPW / 16;             // state row tiles per wave
   static constexpr int CT = WC / 16;              // state column tiles per wave
-  static constexpr int W = 4 * WC;                // d_v columns per work-group
+  static constexpr int W = NCG * WC;              // d_v columns per work-group
   static constexpr int NJT = L / 16;              // 16-token tiles per chunk
   static constexpr int JPW = NJT / NRG;           // token tiles finished per wave
   static constexpr int NKL = L / K;               // token k-blocks per chunk
@@ -132,7 +145,10 @@ struct ChunkCfg {
   static constexpr int NTQK = NJT * (NJT + 1) / 2;  // causal score tiles
   static constexpr int VE = 16 / (int)sizeof(T);  // elements per 16 bytes
   // row strides (elements) of the token-major tiles
-  static constexpr int QS = DQK + lds_row_pad(DQK, (int)sizeof(T), false);  // sQ, sK
+  // sQ is read with 16-byte row fragments only; sK also with transposing
+  // reads (the update's K^T), so the two strides are chosen apart
+  static constexpr int QS = DQK + lds_pad_res(DQK, (int)sizeof(T), MLSTM_P3_QRES);  // sQ
+  static constexpr int KST = DQK + lds_pad_res(DQK, (int)sizeof(T), MLSTM_P3_KRES);  // sK
   static constexpr int VS = W + lds_row_pad(W, (int)sizeof(T), true);       // sV
   static constexpr int PS = L + 16 / (int)sizeof(T);  // sP
   // staging units (16-byte loads) per chunk
@@ -147,14 +163,14 @@ struct ChunkCfg {
   static_assert(WC % 16 == 0, "wave columns");
   static constexpr size_t lds_bytes(bool ret) {
     size_t b = 0;
-    b += (size_t)L * QS * sizeof(T);             // sK
+    b += (size_t)L * KST * sizeof(T);            // sK
     b += (size_t)L * VS * sizeof(T);             // sV
     b += 6 * L * 4 + 16;                         // gate vectors
     if (!ret) b += DQK * 4 + 16 * DQK * sizeof(T);  // n~
     b += (size_t)L * QS * sizeof(T);             // sQ
     b += (size_t)NB * L * PS * sizeof(T);        // sP
     b += (size_t)(NJT + 1) * L * 4;              // den partials
-    if (NRG > 1) b += (size_t)4 * NJT * CT * 64 * 16;  // readout exchange
+    if (NRG > 1) b += (size_t)NCG * NJT * CT * 64 * 16;  // readout exchange
     return b;
   }
 };
@@ -191,24 +207,24 @@ __device__ __forceinline__ float frag_rows(const float* tile, int RS, int r0, in
 // the token tiles and the two partial sums meet in LDS (sX).
 // Q, K and V are staged token-major with plain 16-byte copies; the operands
 // that run along tokens (K^T and V^T) are read with transposing LDS reads.
-template <typename T, int DQK, int NB, int WC, int NRG, int L, bool RET, bool HAS_O>
-__global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
-  using C = ChunkCfg<T, DQK, NB, WC, NRG, L>;
+template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET, bool HAS_O>
+__global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
+  using C = ChunkCfg<T, DQK, NB, WC, NRG, NCG, L>;
   using M = Mma<T>;
   typedef typename M::frag frag;
   constexpr int K = C::K, KL = C::KL, DQKB = C::DQKB, NT = C::NT, CT = C::CT, NW = C::NW;
   constexpr int NTH = C::NTH, RPW = C::RPW, JPW = C::JPW;
   constexpr int W = C::W, NJT = C::NJT, NKL = C::NKL, NKQ = C::NKQ, NKQB = C::NKQB, NKQR = C::NKQR;
-  constexpr int VE = C::VE, QS = C::QS, VS = C::VS, PS = C::PS;
+  constexpr int VE = C::VE, QS = C::QS, KST = C::KST, VS = C::VS, PS = C::PS;
   constexpr unsigned ES = sizeof(T);
   constexpr bool XCH = NRG > 1;
   constexpr bool BF = sizeof(T) == 2;
 
-  __shared__ __attribute__((aligned(16))) T sK[L * QS];   // K, token-major
+  __shared__ __attribute__((aligned(16))) T sK[L * KST];  // K, token-major
   __shared__ __attribute__((aligned(16))) T sV[L * VS];   // V slice, token-major
   __shared__ __attribute__((aligned(16))) T sQ[L * QS];   // Q, token-major
   __shared__ __attribute__((aligned(16))) T sP[NB * L * PS];
-  __shared__ __attribute__((aligned(16))) f32x4 sX[XCH ? 4 * NJT * CT * 64 : 1];
+  __shared__ __attribute__((aligned(16))) f32x4 sX[XCH ? NCG * NJT * CT * 64 : 1];
   // n~ as a 16-row A-operand tile: row 0 = bf16 hi part, row 1 = lo part,
   // rows 2..15 zero (fp32: row 0 = n~, row 1 zero)
   __shared__ __attribute__((aligned(16))) T sNh[RET ? 8 : 16 * DQK];
@@ -222,7 +238,7 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
   // The wave index must be known to be wave-uniform: branches on it guard
   // MFMA instructions, which do not honour a partial EXEC mask.
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int cg = w & 3, rg = w >> 2;
+  const int cg = w % NCG, rg = w / NCG;
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   // Work-group coordinates.  Integer division by runtime values runs on the
   // VALU; readfirstlane keeps the results (and the buffer descriptors built
@@ -249,17 +265,16 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
   const auto rq = make_rsrc(static_cast<const T*>(p.q) + (size_t)bh * T_ * DQK, (unsigned)T_ * DQK * ES);
   const auto rk = make_rsrc(static_cast<const T*>(p.k) + (size_t)bh * T_ * DQK, (unsigned)T_ * DQK * ES);
   const auto rv = make_rsrc(static_cast<const T*>(p.v) + (size_t)bh * T_ * DV, (unsigned)T_ * DV * ES);
-  const auto ri = make_rsrc(RET ? nullptr : static_cast<const T*>(p.i_pre) + (size_t)bh * T_,
-                            RET ? 0u : (unsigned)T_ * ES);
-  const auto rf = make_rsrc(RET ? nullptr : static_cast<const T*>(p.f_pre) + (size_t)bh * T_,
-                            RET ? 0u : (unsigned)T_ * ES);
+  // chunk-local gate logs of the gate kernel, over the padded sequence
+  const size_t NCL = (size_t)p.NC * L;
+  const auto rga_r = make_rsrc(p.ws_ga + (size_t)bh * NCL, (unsigned)NCL * 4u);
+  const auto rgg_r = make_rsrc(p.ws_gg + (size_t)bh * NCL, (unsigned)NCL * 4u);
+  const auto rgb_r = make_rsrc(p.ws_gb + (size_t)bh * NCL, (unsigned)NCL * 4u);
   constexpr bool has_o = HAS_O;  // output gate present (o_pre not null)
   const auto ro = make_rsrc(has_o ? static_cast<const T*>(p.o_pre) + (size_t)bh * T_ * DV : nullptr,
                             has_o ? (unsigned)T_ * DV * ES : 0u);
   const auto rh = make_rsrc(static_cast<T*>(p.h) + (size_t)bh * T_ * DV, (unsigned)T_ * DV * ES);
   const float bias = (!RET && p.bias) ? p.bias[hd] : 0.f;
-  float ret_lg2 = 0.f;
-  if constexpr (RET) ret_lg2 = log2f(p.ret_gamma ? p.ret_gamma[hd] : 1.f - exp2f(-5.f - (float)hd));
 
   const int c_begin = sc * p.G;
   const int c_end = min(c_begin + p.G, p.NC);
@@ -314,7 +329,7 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
   Vec16<T> rgq[C::QIT];
   Vec16<T> rgk[C::QIT];
   Vec16<T> rgv[C::VIT];
-  float rgi = 0.f, rgf = 0.f;
+  unsigned rga = 0, rgg = 0, rgb = 0;  // chunk-local gate logs of the next chunk (raw fp32)
 
   auto load_q = [&](int c) __attribute__((always_inline)) {
     const unsigned t0 = (unsigned)c * L;
@@ -340,20 +355,31 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
       const unsigned j = u / (W / VE), col = (u % (W / VE)) * VE;
       rgv[it] = bload16<T>(rv, ((t0 + j) * DV + slice * W + col) * ES);
     }
-    if constexpr (!RET) {
-      rgi = bload1<T>(ri, (t0 + (lane & (L - 1))) * ES);
-      rgf = bload1<T>(rf, (t0 + (lane & (L - 1))) * ES);
+    {
+      const unsigned o = (t0 + (unsigned)(lane & (L - 1))) * 4u;
+      rga = bload1_raw<float>(rga_r, o);
+      rgg = bload1_raw<float>(rgg_r, o);
+      rgb = bload1_raw<float>(rgb_r, o);
     }
   };
 
-  auto store_stage = [&]() __attribute__((always_inline)) {
+  auto store_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < C::QIT; ++it) {
       const int u = tid + it * NTH;
       if (u < C::NQU) {
         const int j = u / (DQK / VE), col = (u % (DQK / VE)) * VE;
         *reinterpret_cast<uint4*>(&sQ[j * QS + col]) = *reinterpret_cast<const uint4*>(rgq[it].v);
-        *reinterpret_cast<uint4*>(&sK[j * QS + col]) = *reinterpret_cast<const uint4*>(rgk[it].v);
+      }
+    }
+  };
+  auto store_kv = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < C::QIT; ++it) {
+      const int u = tid + it * NTH;
+      if (u < C::NQU) {
+        const int j = u / (DQK / VE), col = (u % (DQK / VE)) * VE;
+        *reinterpret_cast<uint4*>(&sK[j * KST + col]) = *reinterpret_cast<const uint4*>(rgk[it].v);
       }
     }
 #pragma unroll
@@ -366,34 +392,16 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
     }
   };
 
-  // Gate scan for one chunk on wave 0 (one lane per token).
+  // Gate factors of one chunk on wave 0 (one lane per token) from the
+  // chunk-local logs b_j, a_j, g_j of the gate kernel: only the chain through
+  // m_prev is left here.
   auto gates = [&](int c) __attribute__((always_inline)) {
-    const int t0 = c * L;
-    const bool valid = lane < L && t0 + lane < T_;
-    float lf2, li2;
-    if constexpr (RET) {
-      lf2 = valid ? ret_lg2 : 0.f;
-      li2 = valid ? 0.f : -INFINITY;
-    } else {
-      lf2 = valid ? log2_sigmoid(rgf) : 0.f;
-      li2 = valid ? rgi * kLog2e : -INFINITY;
-    }
-    float b = lf2;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const float y = __shfl_up(b, d, 64);
-      if (lane >= d) b += y;
-    }
-    const float a = li2 - b;
-    float g = a;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const float y = __shfl_up(g, d, 64);
-      if (lane >= d) g = fmaxf(g, y);
-    }
+    (void)c;
+    const float a = __uint_as_float(rga), g = __uint_as_float(rgg), b = __uint_as_float(rgb);
     const float Mj = fmaxf(m_prev, g);
-    const float ML = __shfl(Mj, L - 1, 64);
-    const float bL = __shfl(b, L - 1, 64);
+    const float gL = __uint_as_float(__builtin_amdgcn_readlane(rgg, L - 1));
+    const float bL = __uint_as_float(__builtin_amdgcn_readlane(rgb, L - 1));
+    const float ML = fmaxf(m_prev, gL);
     if (lane < L) {
       const float mj = b + Mj;
       const float cl = exp2_fast(-mj);
@@ -411,7 +419,8 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
   // Prime the first chunk.
   load_q(c_begin);
   load_kv(c_begin);
-  store_stage();
+  store_q();
+  store_kv();
   if (w == 0) gates(c_begin);
 
   for (int c = c_begin; c < c_end; ++c) {
@@ -449,7 +458,7 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
 #pragma unroll
             for (int kk = 0; kk < NKQB; ++kk) {
               const int kb = be * NKQB + kk;
-              const frag kf = M::load(&sK[(lt * 16 + lr) * QS + kb * K + KL * lg]);
+              const frag kf = M::load(&sK[(lt * 16 + lr) * KST + kb * K + KL * lg]);
               const frag qj = M::load(&sQ[(jt * 16 + lr) * QS + kb * K + KL * lg]);
               pt[be] = M::mma(kf, qj, pt[be]);
               if (kk & 1) __builtin_amdgcn_sched_barrier(0);
@@ -539,10 +548,9 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
             oraw[jj][ct] = bload4_raw<T>(
                 ro, ((unsigned)(t0 + (jt0 + jj) * 16 + lr) * DV + wcol0 + ct * 16 + 4 * lg) * ES);
       }
-      if (more) {
-        load_kv(c + 1);
-        load_q(c + 1);
-      }
+      // Q of the next chunk now (sQ is free after B2); its K and V after
+      // phase C, so that fewer staging registers are live at once
+      if (more) load_q(c + 1);
       load_vf();
 
       // ---------------------------------------------------------- phase C
@@ -598,6 +606,10 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
       }
     }
 
+    if (more) {
+      store_q();
+      load_kv(c + 1);
+    }
     // ------------------------------------------------------- state update
     if (need_update) {
       const float la = sAlpha;
@@ -634,11 +646,11 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const int kc = BF ? kcol + (nt >> 1) * 32 + (nt & 1) * 4 : kcol + perm_row<T>(nt, lr);
-          const frag ka = frag_rows(sK, QS, kb * K + KL * lg, lr, kc);
+          const frag ka = frag_rows(sK, KST, kb * K + KL * lg, lr, kc);
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) st[nt][ct] = M::mma(ka, wv[ct], st[nt][ct]);
           if constexpr (NFRAG) {
-            if ((nt & 3) == cg) {
+            if (nt % NCG == cg) {
 #pragma unroll
               for (int e = 0; e < KL; ++e) {
                 if constexpr (BF) dn[nt] += wl[e] * (float)ka[e];
@@ -652,14 +664,14 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
       if constexpr (!RET && !NFRAG) {
         for (int r = tid; r < DQK; r += NTH) {
           float x = alpha * sNf[r];
-          for (int l = 0; l < L; ++l) x += sW[l] * to_f32(sK[l * QS + r]);
+          for (int l = 0; l < L; ++l) x += sW[l] * to_f32(sK[l * KST + r]);
           put_n(r, x);
         }
       }
       if constexpr (NFRAG) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          if ((nt & 3) == cg) {
+          if (nt % NCG == cg) {
             float d = dn[nt];
             d += __shfl_xor(d, 16, 64);
             d += __shfl_xor(d, 32, 64);
@@ -673,7 +685,7 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
     }
     __syncthreads();  // B3: LDS free for the next chunk
     if (more) {
-      store_stage();
+      store_kv();
       if (w == 0) gates(c + 1);
     }
   }
@@ -701,29 +713,44 @@ __global__ __launch_bounds__(256 * NRG) void chunk_kernel(ChunkParams p) {
   }
 }
 
-// Pass 1a (superchunk_gate_kernel): the gate factors of every superchunk but
-// the last.  With b_t = sum_{r<=t} log2 sigmoid(f_r) and a_t = log2(i_t) - b_t
-// inside the superchunk (t = 0 .. G*L-1) and amax = max_t a_t, it writes
-// w_t = 2^{a_t - amax} for every token, the total log2 decay A = b_end and the
-// log2 scale mu = b_end + amax of the superchunk's local state (the stabiliser
-// the token recurrence reaches from m = -inf).  One work-group of 4 waves per
-// (batch*head, superchunk): the waves take 64-token groups in turn, scan them
-// with DPP, and the group totals meet in LDS.
+// Gate kernel (superchunk_gate_kernel), one work-group of 4 waves per
+// (batch*head, superchunk).  For every token, in base-2 logs:
+//   chunk-local, for pass 3 (chunks of L tokens, index j):
+//     b_j = sum_{r<=j} log2 sigmoid(f_r),  a_j = log2(i_j) - b_j,
+//     g_j = max_{r<=j} a_r
+//   superchunk-local, for pass 1 (every superchunk but the last, t = 0 .. G*L-1):
+//     w_t = 2^{a'_t - amax} with a'_t = log2(i_t) - sum_{r<=t} log2 sigmoid(f_r)
+//     and amax = max_t a'_t; the total log2 decay A = b'_end and the log2
+//     scale mu = b'_end + amax of the superchunk's local state (the stabiliser
+//     the token recurrence reaches from m = -inf).
+// Tokens past T count as f = 1, i = 0.  The waves take 64-token groups in
+// turn and scan them with DPP; the group totals meet in LDS.
 
-// inclusive prefix sum over the 64 lanes of a wave: rows of 16 lanes by
-// row shifts, then the row totals by row broadcasts (lanes without a source
-// add 0)
+// inclusive scans over lanes in segments of SEG = 16, 32 or 64 lanes: row
+// shifts inside rows of 16, then row broadcasts.  update_dpp with bound_ctrl
+// off hands lanes without a source (and lanes of rows outside the row mask)
+// the `old` operand, here the identity (checked on MI355X).
 template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_or_zero(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, false));
+__device__ __forceinline__ float dpp_or(float x, float identity) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(x), CTRL, ROWS, 0xF, false));
 }
-__device__ __forceinline__ float wave_prefix_sum(float x) {
-  x += dpp_or_zero<0x111, 0xF>(x);  // row_shr:1
-  x += dpp_or_zero<0x112, 0xF>(x);  // row_shr:2
-  x += dpp_or_zero<0x114, 0xF>(x);  // row_shr:4
-  x += dpp_or_zero<0x118, 0xF>(x);  // row_shr:8
-  x += dpp_or_zero<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
-  x += dpp_or_zero<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+__device__ __forceinline__ float seg_scan_sum(float x, int seg) {
+  x += dpp_or<0x111, 0xF>(x, 0.f);                  // row_shr:1
+  x += dpp_or<0x112, 0xF>(x, 0.f);                  // row_shr:2
+  x += dpp_or<0x114, 0xF>(x, 0.f);                  // row_shr:4
+  x += dpp_or<0x118, 0xF>(x, 0.f);                  // row_shr:8
+  if (seg >= 32) x += dpp_or<0x142, 0xA>(x, 0.f);  // row_bcast:15 into rows 1, 3
+  if (seg >= 64) x += dpp_or<0x143, 0xC>(x, 0.f);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+__device__ __forceinline__ float seg_scan_max(float x, int seg) {
+  x = fmaxf(x, dpp_or<0x111, 0xF>(x, -INFINITY));
+  x = fmaxf(x, dpp_or<0x112, 0xF>(x, -INFINITY));
+  x = fmaxf(x, dpp_or<0x114, 0xF>(x, -INFINITY));
+  x = fmaxf(x, dpp_or<0x118, 0xF>(x, -INFINITY));
+  if (seg >= 32) x = fmaxf(x, dpp_or<0x142, 0xA>(x, -INFINITY));
+  if (seg >= 64) x = fmaxf(x, dpp_or<0x143, 0xC>(x, -INFINITY));
   return x;
 }
 
@@ -739,7 +766,10 @@ __global__ __launch_bounds__(256) void superchunk_gate_kernel(ChunkParams p, int
   const int sc = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / BH));
   const int hd = bh % p.H;
   const int GL = p.G * L, tb = sc * GL;
-  const int NG = (GL + 63) / 64;
+  const int NCL = p.NC * L;                    // padded token count of a sequence
+  const int GLs = min(GL, NCL - tb);           // tokens of this superchunk (last may be short)
+  const int NG = (GLs + 63) / 64;
+  const bool local = sc < p.NS - 1;            // pass 1 needs this superchunk
   constexpr unsigned ES = sizeof(T);
   const auto ri = make_rsrc(RET ? nullptr : static_cast<const T*>(p.i_pre) + (size_t)bh * T_,
                             RET ? 0u : (unsigned)T_ * ES);
@@ -758,11 +788,12 @@ __global__ __launch_bounds__(256) void superchunk_gate_kernel(ChunkParams p, int
       gf[k] = bload1<T>(rf, t * ES);
     }
   }
+  const size_t gbase = (size_t)bh * NCL + tb;
 #pragma unroll
   for (int k = 0; k < GPW; ++k) {
     const int g = w + 4 * k;
     const int tl = g * 64 + lane;  // token within the superchunk
-    const bool valid = g < NG && tl < GL && tb + tl < T_;
+    const bool valid = g < NG && tl < GLs && tb + tl < T_;
     float lf2;
     if constexpr (RET) {
       lf2 = valid ? ret_lg2 : 0.f;
@@ -771,9 +802,19 @@ __global__ __launch_bounds__(256) void superchunk_gate_kernel(ChunkParams p, int
       lf2 = valid ? log2_sigmoid(gf[k]) : 0.f;
       li[k] = valid ? gi[k] * kLog2e : -INFINITY;
     }
-    bl[k] = wave_prefix_sum(lf2);
+    // chunk-local values for pass 3 (a chunk never straddles a 64-token group)
+    const float bc = seg_scan_sum(lf2, L);
+    const float ac = li[k] - bc;
+    const float gc = seg_scan_max(ac, L);
+    if (g < NG && tl < GLs) {
+      p.ws_ga[gbase + tl] = ac;
+      p.ws_gg[gbase + tl] = gc;
+      p.ws_gb[gbase + tl] = bc;
+    }
+    bl[k] = seg_scan_sum(lf2, 64);
     if (g < NG && lane == 63) stot[g] = bl[k];
   }
+  if (!local) return;  // work-group-uniform
   __syncthreads();
   float amax = -INFINITY, carry = 0.f;
   int gdone = 0;
@@ -1125,16 +1166,17 @@ __global__ __launch_bounds__(256) void superchunk_scan_kernel(ScanParams p) {
   }
 }
 
-template <typename T, int DQK, int NB, int WC, int NRG, int L, bool RET>
+template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET>
 size_t chunk_lds_bytes() {
-  return ChunkCfg<T, DQK, NB, WC, NRG, L>::lds_bytes(RET);
+  return ChunkCfg<T, DQK, NB, WC, NRG, NCG, L>::lds_bytes(RET);
 }
 
-template <typename T, int DQK, int NB, int WC, int NRG, int L, bool RET>
+template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET>
 hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  constexpr int NTH = 256 * NRG;
+  constexpr int NTH = 64 * NCG * NRG;
   const int BH = p.B * p.H;
   const size_t CS = (size_t)DQK * p.DV / NB;
+  hipLaunchKernelGGL((superchunk_gate_kernel<T, RET>), dim3((unsigned)(BH * p.NS)), dim3(256), 0, stream, p, L);
   if (p.NS > 1) {
     // pass 1 tiles: TR rows x TC columns of one memory block
     constexpr int DQKB = DQK / NB;
@@ -1142,7 +1184,6 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
     constexpr int TR = DQKB < TCAP ? DQKB : TCAP;
     const int DVB = p.DV / NB;
     const int TC = DVB % TCAP == 0 ? TCAP : DVB % 64 == 0 ? 64 : 32;
-    hipLaunchKernelGGL((superchunk_gate_kernel<T, RET>), dim3((unsigned)(BH * (p.NS - 1))), dim3(256), 0, stream, p, L);
     const dim3 g1((unsigned)(BH * (p.NS - 1) * NB * (DQKB / TR) * (DVB / TC)));
     if (TC == TCAP)
       hipLaunchKernelGGL((local_state_kernel<T, DQK, NB, TR, TCAP, L, RET>), g1, dim3(256), 0, stream, p);
@@ -1168,39 +1209,41 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
   dim3 g3((unsigned)(BH * p.nslices * p.NS));
   if (ev0) (void)hipEventRecord(ev0, stream);
   if (!RET && p.o_pre)
-    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, L, RET, !RET>), g3, dim3(NTH), 0, stream, p);
+    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, !RET>), g3, dim3(NTH), 0, stream, p);
   else
-    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, L, RET, false>), g3, dim3(NTH), 0, stream, p);
+    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, false>), g3, dim3(NTH), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (ev1) (void)hipEventRecord(ev1, stream);
   return e;
 }
 
 // ------------------------------------------------------------ dispatch table
-// (dtype, d_qk, num_blocks, columns per wave, row groups, chunk, retention)
-#define MLSTM_CHUNK_VARIANTS(X)            \
-  X(__bf16, 64, 1, 16, 1, 64, false)       \
-  X(__bf16, 64, 2, 16, 1, 64, false)       \
-  X(__bf16, 64, 1, 16, 1, 32, false)       \
-  X(__bf16, 128, 1, 32, 2, 64, false)      \
-  X(__bf16, 256, 1, 32, 2, 64, false)      \
-  X(__bf16, 256, 2, 16, 2, 64, false)      \
-  X(float, 64, 1, 16, 1, 64, false)        \
-  X(float, 64, 1, 16, 1, 32, false)        \
-  X(float, 64, 1, 16, 1, 16, false)        \
-  X(float, 64, 2, 16, 1, 64, false)        \
-  X(__bf16, 64, 1, 16, 1, 64, true)        \
-  X(__bf16, 64, 1, 16, 1, 32, true)        \
-  X(__bf16, 128, 1, 32, 2, 64, true)       \
-  X(float, 64, 1, 16, 1, 64, true)
+// (dtype, d_qk, num_blocks, columns per wave, row groups, column groups,
+//  chunk, retention); one variant per (dtype, d_qk, num_blocks, chunk,
+//  retention)
+#define MLSTM_CHUNK_VARIANTS(X)             \
+  X(__bf16, 64, 1, 16, 1, 4, 64, false)     \
+  X(__bf16, 64, 2, 16, 1, 4, 64, false)     \
+  X(__bf16, 64, 1, 16, 1, 4, 32, false)     \
+  X(__bf16, 128, 1, 32, 2, 4, 64, false)    \
+  X(__bf16, 256, 1, 32, 2, 4, 64, false)    \
+  X(__bf16, 256, 2, 16, 2, 4, 64, false)    \
+  X(float, 64, 1, 16, 1, 4, 64, false)      \
+  X(float, 64, 1, 16, 1, 4, 32, false)      \
+  X(float, 64, 1, 16, 1, 4, 16, false)      \
+  X(float, 64, 2, 16, 1, 4, 64, false)      \
+  X(__bf16, 64, 1, 16, 1, 4, 64, true)      \
+  X(__bf16, 64, 1, 16, 1, 4, 32, true)      \
+  X(__bf16, 128, 1, 32, 2, 4, 64, true)     \
+  X(float, 64, 1, 16, 1, 4, 64, true)
 
-bool find_chunk_variant(int dtype, int dqk, int nb, int wc, int L, bool ret, ChunkVariant* out) {
-#define X(T_, DQK_, NB_, WC_, NRG_, L_, RET_)                                                    \
-  if (dtype == (sizeof(T_) == 2 ? 1 : 0) && dqk == DQK_ && nb == NB_ && wc == WC_ && L == L_ && \
-      ret == RET_) {                                                                             \
-    out->launch = &launch_chunkwise<T_, DQK_, NB_, WC_, NRG_, L_, RET_>;                         \
-    out->lds_bytes = chunk_lds_bytes<T_, DQK_, NB_, WC_, NRG_, L_, RET_>();                      \
+bool find_chunk_variant(int dtype, int dqk, int nb, int L, bool ret, ChunkVariant* out) {
+#define X(T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_)                                              \
+  if (dtype == (sizeof(T_) == 2 ? 1 : 0) && dqk == DQK_ && nb == NB_ && L == L_ && ret == RET_) { \
+    out->launch = &launch_chunkwise<T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_>;                   \
+    out->lds_bytes = chunk_lds_bytes<T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_>();                \
     out->wc = WC_;                                                                               \
+    out->w = NCG_ * WC_;                                                                         \
     return true;                                                                                 \
   }
   MLSTM_CHUNK_VARIANTS(X)

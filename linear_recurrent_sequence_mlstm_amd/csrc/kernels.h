@@ -21,6 +21,9 @@ struct ChunkParams {
   float* ws_scal;          // [B*H][NS][2] (total log2 decay, local log2 scale)
   float* ws_min;           // [B*H][NS] stabiliser (log2) at superchunk starts
   float* ws_w;             // [B*H][T] gate factors of the tokens in superchunks 0 .. NS-2
+  float* ws_ga;            // [B*H][NC*L] chunk-local log2 gate sums a_j, prefix maxima g_j,
+  float* ws_gg;            //   forget-gate sums b_j (gate kernel -> pass 3)
+  float* ws_gb;
   int has_init;
   const float* C0;
   const float* n0;
@@ -50,11 +53,12 @@ typedef hipError_t (*ChunkLaunchFn)(ChunkParams, hipStream_t, hipEvent_t ev0, hi
 struct ChunkVariant {
   ChunkLaunchFn launch;
   size_t lds_bytes;
-  int wc;
+  int wc;  // d_v columns per wave
+  int w;   // d_v columns per work-group (the d_v slice)
 };
 
-// dtype: 0 = fp32, 1 = bf16.  wc = d_v columns per wave (work-group = 4 waves).
-bool find_chunk_variant(int dtype, int dqk, int nb, int wc, int L, bool ret, ChunkVariant* out);
+// dtype: 0 = fp32, 1 = bf16.
+bool find_chunk_variant(int dtype, int dqk, int nb, int L, bool ret, ChunkVariant* out);
 
 // Decode step.
 struct StepParams {

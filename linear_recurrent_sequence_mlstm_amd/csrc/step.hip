@@ -11,13 +11,16 @@
 //   h   = o * (S~^T q) / max(|n~.q + bias 2^{-m'}|, 2^{-m'})
 // The readout uses the updated state.
 //
-// Thread layout: one work-group per (batch, head).  Its threads form
-// RG row groups x (d_v / 4) column threads; thread (g, t) owns columns
-// 4t..4t+3 and rows g, g+RG, ... of its memory block, so every state element
-// is read and written exactly once with 16-byte accesses, and consecutive
-// threads touch consecutive 16-byte words of a row.  The RG partial readout
-// sums of a column meet in LDS.  Many short work-groups keep the HBM
-// streams of the whole chip in flight.
+// Two launches.  step_kernel streams the matrix state: work-group (b*h,
+// slice) owns a slice of WS columns and all rows, so its readout columns are
+// complete and it writes h for them.  The updated normaliser enters only
+// through n~'.q = f' (n~.q) + i' (k.q), computed from the old n~, so no
+// work-group depends on another's writes; step_norm_kernel then updates n~
+// and m in place.  Thread (g, t) of a slice owns columns 4t..4t+3 and rows
+// g, g+RG, ... of their memory block: every state element is read and written
+// once with 16-byte accesses, consecutive threads touch consecutive 16-byte
+// words of a row, and short work-groups keep the HBM streams of the whole
+// chip busy.  The RG partial sums of a column meet in LDS.
 #include <stdlib.h>
 
 #include "common.h"
@@ -25,58 +28,89 @@
 
 namespace mlstm {
 
+// gate factors of one (batch, head) in log2 units
+struct StepGates {
+  float mn2, fdec, iw;
+};
+template <typename T>
+__device__ __forceinline__ StepGates step_gates(const StepParams& p, int bh) {
+  const float lf2 = log2_sigmoid(to_f32(static_cast<const T*>(p.f_pre)[bh]));
+  const float li2 = to_f32(static_cast<const T*>(p.i_pre)[bh]) * kLog2e;
+  const float m2 = p.m[bh] * kLog2e;
+  StepGates s;
+  s.mn2 = fmaxf(lf2 + m2, li2);
+  s.fdec = exp2_fast(lf2 + m2 - s.mn2);
+  s.iw = exp2_fast(li2 - s.mn2);
+  return s;
+}
+
 template <typename T, int RG>
-__global__ __launch_bounds__(1024) void step_kernel(StepParams p) {
+__global__ __launch_bounds__(512) void step_kernel(StepParams p, int WS) {
   extern __shared__ float smem[];
   const int DQK = p.DQK, DV = p.DV, NB = p.NB;
   const int DQKB = DQK / NB, DVB = DV / NB;
-  const int TPC = DV / 4;  // column threads
+  const int TPC = WS / 4;  // column threads
   const int nth = TPC * RG;
-  const int tid = threadIdx.x;
+  const int nsl = DV / WS;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int g = tid / TPC, t = tid - g * TPC;
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x / nsl, slice = blockIdx.x - bh * nsl;
   float* sq = smem;              // [DQK]
   float* sk = sq + DQK;          // [DQK]
-  float* sacc = sk + DQK;        // [RG][DV]
-  float* sred = sacc + RG * DV;  // [nth / 64]
+  float* sacc = sk + DQK;        // [RG][WS]
+  float* sred = sacc + RG * WS;  // [2][nth / 64]
 
-  const T* q = static_cast<const T*>(p.q);
-  const T* k = static_cast<const T*>(p.k);
-  const T* v = static_cast<const T*>(p.v);
-  const T* ip = static_cast<const T*>(p.i_pre);
-  const T* fp = static_cast<const T*>(p.f_pre);
-  const T* op = static_cast<const T*>(p.o_pre);
-  T* h = static_cast<T*>(p.h);
+  const T* q = static_cast<const T*>(p.q) + (size_t)bh * DQK;
+  const T* k = static_cast<const T*>(p.k) + (size_t)bh * DQK;
+  const T* v = static_cast<const T*>(p.v) + (size_t)bh * DV;
 
-  const float lf2 = log2_sigmoid(to_f32(fp[bh]));
-  const float li2 = to_f32(ip[bh]) * kLog2e;
-  const float m2 = p.m[bh] * kLog2e;
-  const float mn2 = fmaxf(lf2 + m2, li2);
-  const float fdec = exp2_fast(lf2 + m2 - mn2);
-  const float iw = exp2_fast(li2 - mn2);
+  const int col = slice * WS + t * 4;
+  const int blk = col / DVB, cl = col - blk * DVB;
+  float* S = p.C + (size_t)bh * DQK * DVB + (size_t)blk * DQKB * DVB + cl;
+  constexpr int U = 16;  // rows in flight per thread (16 x 16 B loads)
+  f32x4 s[U];
+  // the first batch of state rows goes out before anything else
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int r = g + u * RG;
+    if (r < DQKB) s[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (size_t)r * DVB));
+  }
+  const StepGates gt = step_gates<T>(p, bh);
   const float bias = p.bias ? p.bias[bh % p.H] : 0.f;
+  // q, k to LDS; n~.q and k.q over the head
+  float nq = 0.f, kq = 0.f;
   for (int r = tid; r < DQK; r += nth) {
-    sq[r] = to_f32(q[(size_t)bh * DQK + r]);
-    sk[r] = to_f32(k[(size_t)bh * DQK + r]);
+    const float qr = to_f32(q[r]), kr = to_f32(k[r]);
+    sq[r] = qr;
+    sk[r] = kr;
+    nq += p.n[(size_t)bh * DQK + r] * qr;
+    kq += kr * qr;
+  }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) {
+    nq += __shfl_xor(nq, d, 64);
+    kq += __shfl_xor(kq, d, 64);
+  }
+  if (lane == 0) {
+    sred[tid >> 6] = nq;
+    sred[nth / 64 + (tid >> 6)] = kq;
   }
   __syncthreads();
 
-  const int col = t * 4;
-  const int blk = col / DVB, cl = col - blk * DVB;
   float vv[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) vv[i] = iw * to_f32(v[(size_t)bh * DV + col + i]);
-  float* S = p.C + (size_t)bh * DQK * DVB + (size_t)blk * DQKB * DVB + cl;
+  for (int i = 0; i < 4; ++i) vv[i] = gt.iw * to_f32(v[col + i]);
   const float* kb = sk + blk * DQKB;
   const float* qb = sq + blk * DQKB;
+  const float fdec = gt.fdec;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 16;  // rows in flight per thread (16 x 16 B loads)
   for (int r0 = g; r0 < DQKB; r0 += U * RG) {
-    f32x4 s[U];
+    if (r0 != g) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int r = r0 + u * RG;
-      if (r < DQKB) s[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (size_t)r * DVB));
+      for (int u = 0; u < U; ++u) {
+        const int r = r0 + u * RG;
+        if (r < DQKB) s[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (size_t)r * DVB));
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -95,85 +129,98 @@ __global__ __launch_bounds__(1024) void step_kernel(StepParams p) {
       }
     }
   }
-  // n~ update and n~.q over the whole work-group
-  float dot = 0.f;
-  for (int r = tid; r < DQK; r += nth) {
-    float* np = p.n + (size_t)bh * DQK + r;
-    const float nn = fdec * *np + iw * sk[r];
-    *np = nn;
-    dot += nn * sq[r];
-  }
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) dot += __shfl_xor(dot, d, 64);
-  if ((tid & 63) == 0) sred[tid >> 6] = dot;
   if constexpr (RG > 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sacc[g * DV + col + i] = acc[i];
+    for (int i = 0; i < 4; ++i) sacc[g * WS + t * 4 + i] = acc[i];
   }
   __syncthreads();
   if (g == 0) {
-    dot = 0.f;
-    for (int i = 0; i < nth / 64; ++i) dot += sred[i];
+    float n_q = 0.f, k_q = 0.f;
+    for (int i = 0; i < nth / 64; ++i) {
+      n_q += sred[i];
+      k_q += sred[nth / 64 + i];
+    }
     if constexpr (RG > 1) {
       for (int gg = 1; gg < RG; ++gg)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += sacc[gg * DV + col + i];
+        for (int i = 0; i < 4; ++i) acc[i] += sacc[gg * WS + t * 4 + i];
     }
-    const float cl2 = exp2_fast(-mn2);
-    const float inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(dot + bias * cl2), cl2));
+    const float cl2 = exp2_fast(-gt.mn2);
+    const float den = fdec * n_q + gt.iw * k_q + bias * cl2;  // n~' . q + bias 2^{-m'}
+    const float inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), cl2));
+    const T* op = static_cast<const T*>(p.o_pre);
     T hv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float o = op ? sigmoidf_(to_f32(op[(size_t)bh * DV + col + i])) : 1.f;
       hv[i] = from_f32<T>(o * acc[i] * inv);
     }
-    store4(h + (size_t)bh * DV + col, hv[0], hv[1], hv[2], hv[3]);
-    if (t == 0) p.m[bh] = mn2 * kLn2;
+    store4(static_cast<T*>(p.h) + (size_t)bh * DV + col, hv[0], hv[1], hv[2], hv[3]);
   }
 }
 
-// Row groups per (batch, head): the most (up to 8) that keep the work-group
-// at <= 512 threads, else at <= 1024, with a whole number of waves (the n~.q
-// sum reduces per wave).  0 if no choice fits.  MLSTM_STEP_RG (1, 2, 4, 8)
-// overrides the choice for tuning when it fits.
-static int pick_rg(int dv) {
-  const int tpc = dv / 4;
+// n~ <- f' n~ + i' k and m <- m' in place, after step_kernel has read them.
+template <typename T>
+__global__ __launch_bounds__(256) void step_norm_kernel(StepParams p) {
+  const int bh = blockIdx.x;
+  const StepGates gt = step_gates<T>(p, bh);
+  const T* k = static_cast<const T*>(p.k) + (size_t)bh * p.DQK;
+  float* n = p.n + (size_t)bh * p.DQK;
+  for (int r = threadIdx.x; r < p.DQK; r += 256) n[r] = gt.fdec * n[r] + gt.iw * to_f32(k[r]);
+  __syncthreads();  // every thread has read m
+  if (threadIdx.x == 0) p.m[bh] = gt.mn2 * kLn2;
+}
+
+// Slice width: the largest of 128, 64, 32, 16 columns that divides d_v.
+static int pick_ws(int dv) {
+  for (int ws : {128, 64, 32, 16})
+    if (dv % ws == 0) return ws;
+  return 0;
+}
+// Row groups: the most (up to 16) that keep the work-group at <= 512
+// threads with a whole number of waves (the dot products reduce per wave).
+// MLSTM_STEP_RG (1 .. 16, a power of two) overrides the choice for tuning
+// when it fits.
+static int pick_rg(int ws) {
+  const int tpc = ws / 4;
   const auto fits = [tpc](int rg, int cap) { return tpc * rg <= cap && (tpc * rg) % 64 == 0; };
   const char* e = getenv("MLSTM_STEP_RG");
   if (e) {
     const int x = atoi(e);
-    if ((x == 1 || x == 2 || x == 4 || x == 8) && fits(x, 1024)) return x;
+    if ((x == 1 || x == 2 || x == 4 || x == 8 || x == 16) && fits(x, 512)) return x;
   }
-  for (int cap : {512, 1024})
-    for (int rg = 8; rg >= 1; rg >>= 1)
-      if (fits(rg, cap)) return rg;
+  for (int rg = 16; rg >= 1; rg >>= 1)
+    if (fits(rg, 512)) return rg;
   return 0;
 }
 
 bool step_supported(int dqk, int dv, int nb) {
   if (nb <= 0 || dqk % nb || dv % nb) return false;
-  if (dv % 4 || (dv / nb) % 4) return false;
-  return pick_rg(dv) > 0;
+  if ((dv / nb) % 4 || pick_ws(dv) == 0) return false;
+  return pick_rg(pick_ws(dv)) > 0;
 }
 
 template <typename T>
-static hipError_t launch_rg(const StepParams& p, int rg, hipStream_t stream) {
-  const int tpc = p.DV / 4;
-  const dim3 grid((unsigned)(p.B * p.H));
+static hipError_t launch_rg(const StepParams& p, int ws, int rg, hipStream_t stream) {
+  const int tpc = ws / 4;
+  const dim3 grid((unsigned)(p.B * p.H * (p.DV / ws)));
   const dim3 block((unsigned)(tpc * rg));
-  const size_t smem = ((size_t)2 * p.DQK + (size_t)rg * p.DV + 16) * sizeof(float);
+  const size_t smem = ((size_t)2 * p.DQK + (size_t)rg * ws + 2 * 16) * sizeof(float);
   switch (rg) {
-    case 1: hipLaunchKernelGGL((step_kernel<T, 1>), grid, block, smem, stream, p); break;
-    case 2: hipLaunchKernelGGL((step_kernel<T, 2>), grid, block, smem, stream, p); break;
-    case 4: hipLaunchKernelGGL((step_kernel<T, 4>), grid, block, smem, stream, p); break;
-    default: hipLaunchKernelGGL((step_kernel<T, 8>), grid, block, smem, stream, p); break;
+    case 1: hipLaunchKernelGGL((step_kernel<T, 1>), grid, block, smem, stream, p, ws); break;
+    case 2: hipLaunchKernelGGL((step_kernel<T, 2>), grid, block, smem, stream, p, ws); break;
+    case 4: hipLaunchKernelGGL((step_kernel<T, 4>), grid, block, smem, stream, p, ws); break;
+    case 8: hipLaunchKernelGGL((step_kernel<T, 8>), grid, block, smem, stream, p, ws); break;
+    default: hipLaunchKernelGGL((step_kernel<T, 16>), grid, block, smem, stream, p, ws); break;
   }
+  hipLaunchKernelGGL((step_norm_kernel<T>), dim3((unsigned)(p.B * p.H)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_step(int dtype, const StepParams& p, hipStream_t stream) {
-  const int rg = pick_rg(p.DV);
-  return dtype == 1 ? launch_rg<__bf16>(p, rg, stream) : launch_rg<float>(p, rg, stream);
+  const int ws = pick_ws(p.DV);
+  const int rg = pick_rg(ws);
+  return dtype == 1 ? launch_rg<__bf16>(p, ws, rg, stream) : launch_rg<float>(p, ws, rg, stream);
 }
 
 }  // namespace mlstm
