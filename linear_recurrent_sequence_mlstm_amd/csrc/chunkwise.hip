@@ -151,6 +151,10 @@ struct ChunkCfg {
   static constexpr int KST = DQK + lds_pad_res(DQK, (int)sizeof(T), MLSTM_P3_KRES);  // sK
   static constexpr int VS = W + lds_row_pad(W, (int)sizeof(T), true);       // sV
   static constexpr int PS = L + 16 / (int)sizeof(T);  // sP
+  // bf16 outputs are staged in LDS (sH, token-major) and written as whole
+  // 16-byte units of the work-group's row segment
+  static constexpr bool HST = sizeof(T) == 2;
+  static constexpr int HS = W + 16 / (int)sizeof(T);
   // staging units (16-byte loads) per chunk
   static constexpr int NQU = L * DQK / VE;
   static constexpr int NVU = L * W / VE;
@@ -171,6 +175,7 @@ struct ChunkCfg {
     b += (size_t)NB * L * PS * sizeof(T);        // sP
     b += (size_t)(NJT + 1) * L * 4;              // den partials
     if (NRG > 1) b += (size_t)NCG * NJT * CT * 64 * 16;  // readout exchange
+    if (HST) b += (size_t)L * HS * sizeof(T);    // sH
     return b;
   }
 };
@@ -215,7 +220,8 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   constexpr int K = C::K, KL = C::KL, DQKB = C::DQKB, NT = C::NT, CT = C::CT, NW = C::NW;
   constexpr int NTH = C::NTH, RPW = C::RPW, JPW = C::JPW;
   constexpr int W = C::W, NJT = C::NJT, NKL = C::NKL, NKQ = C::NKQ, NKQB = C::NKQB, NKQR = C::NKQR;
-  constexpr int VE = C::VE, QS = C::QS, KST = C::KST, VS = C::VS, PS = C::PS;
+  constexpr int VE = C::VE, QS = C::QS, KST = C::KST, VS = C::VS, PS = C::PS, HS = C::HS;
+  constexpr bool HST = C::HST;
   constexpr unsigned ES = sizeof(T);
   constexpr bool XCH = NRG > 1;
   constexpr bool BF = sizeof(T) == 2;
@@ -225,6 +231,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   __shared__ __attribute__((aligned(16))) T sQ[L * QS];   // Q, token-major
   __shared__ __attribute__((aligned(16))) T sP[NB * L * PS];
   __shared__ __attribute__((aligned(16))) f32x4 sX[XCH ? NCG * NJT * CT * 64 : 1];
+  __shared__ __attribute__((aligned(16))) T sH[HST ? L * HS : 8];  // outputs of the chunk
   // n~ as a 16-row A-operand tile: row 0 = bf16 hi part, row 1 = lo part,
   // rows 2..15 zero (fp32: row 0 = n~, row 1 zero)
   __shared__ __attribute__((aligned(16))) T sNh[RET ? 8 : 16 * DQK];
@@ -600,8 +607,14 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = sigmoidf_(o[i]);
           }
-          bstore4<T>(rh, ((unsigned)(t0 + j) * DV + col) * ES, o[0] * o_acc[ct][0] * inv,
-                     o[1] * o_acc[ct][1] * inv, o[2] * o_acc[ct][2] * inv, o[3] * o_acc[ct][3] * inv);
+          float hv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hv[i] = o[i] * o_acc[ct][i] * inv;
+          if constexpr (HST)
+            store4(&sH[j * HS + cg * WC + ct * 16 + 4 * lg], from_f32<T>(hv[0]), from_f32<T>(hv[1]),
+                   from_f32<T>(hv[2]), from_f32<T>(hv[3]));
+          else
+            bstore4<T>(rh, ((unsigned)(t0 + j) * DV + col) * ES, hv[0], hv[1], hv[2], hv[3]);
         }
       }
     }
@@ -684,6 +697,17 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
       }
     }
     __syncthreads();  // B3: LDS free for the next chunk
+    if constexpr (HST) {
+      // the chunk's outputs, whole 16-byte units per lane (rows past T are
+      // dropped by the buffer range)
+      constexpr int UR = W / VE;  // units per token row
+#pragma unroll
+      for (int u = tid; u < L * UR; u += NTH) {
+        const int j = u / UR, cu = u % UR;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(&sH[j * HS + cu * VE]);
+        __builtin_amdgcn_raw_buffer_store_b128(x, rh, ((unsigned)(t0 + j) * DV + slice * W + cu * VE) * ES, 0, 0);
+      }
+    }
     if (more) {
       store_kv();
       if (w == 0) gates(c + 1);

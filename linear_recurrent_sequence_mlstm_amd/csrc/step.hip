@@ -160,15 +160,27 @@ __global__ __launch_bounds__(512) void step_kernel(StepParams p, int WS) {
 }
 
 // n~ <- f' n~ + i' k and m <- m' in place, after step_kernel has read them.
+// A work-group owns RPB = max(1, 256 / d_qk) whole rows (b, h), so every
+// reader of a row's m is in the work-group that rewrites it, after a barrier;
+// all loads of a thread are issued before any result is needed.
 template <typename T>
-__global__ __launch_bounds__(256) void step_norm_kernel(StepParams p) {
-  const int bh = blockIdx.x;
-  const StepGates gt = step_gates<T>(p, bh);
-  const T* k = static_cast<const T*>(p.k) + (size_t)bh * p.DQK;
-  float* n = p.n + (size_t)bh * p.DQK;
-  for (int r = threadIdx.x; r < p.DQK; r += 256) n[r] = gt.fdec * n[r] + gt.iw * to_f32(k[r]);
-  __syncthreads();  // every thread has read m
-  if (threadIdx.x == 0) p.m[bh] = gt.mn2 * kLn2;
+__global__ __launch_bounds__(256) void step_norm_kernel(StepParams p, int RPB) {
+  const int DQK = p.DQK, BH = p.B * p.H;
+  const int bh0 = blockIdx.x * RPB;
+  const int nrow = min(RPB, BH - bh0);
+  for (int e = threadIdx.x; e < nrow * DQK; e += 256) {
+    const int bh = bh0 + e / DQK;
+    const size_t idx = (size_t)bh0 * DQK + e;
+    const float nv = p.n[idx];
+    const float kv = to_f32(static_cast<const T*>(p.k)[idx]);
+    const StepGates gt = step_gates<T>(p, bh);
+    p.n[idx] = gt.fdec * nv + gt.iw * kv;
+  }
+  __syncthreads();  // every read of m in this work-group is done
+  if (threadIdx.x < nrow) {
+    const StepGates gt = step_gates<T>(p, bh0 + threadIdx.x);
+    p.m[bh0 + threadIdx.x] = gt.mn2 * kLn2;
+  }
 }
 
 // Slice width: the largest of 128, 64, 32, 16 columns that divides d_v.
@@ -213,7 +225,9 @@ static hipError_t launch_rg(const StepParams& p, int ws, int rg, hipStream_t str
     case 8: hipLaunchKernelGGL((step_kernel<T, 8>), grid, block, smem, stream, p, ws); break;
     default: hipLaunchKernelGGL((step_kernel<T, 16>), grid, block, smem, stream, p, ws); break;
   }
-  hipLaunchKernelGGL((step_norm_kernel<T>), dim3((unsigned)(p.B * p.H)), dim3(256), 0, stream, p);
+  const int rpb = p.DQK >= 256 ? 1 : 256 / p.DQK;
+  const int nwg = (p.B * p.H + rpb - 1) / rpb;
+  hipLaunchKernelGGL((step_norm_kernel<T>), dim3((unsigned)nwg), dim3(256), 0, stream, p, rpb);
   return hipGetLastError();
 }
 
