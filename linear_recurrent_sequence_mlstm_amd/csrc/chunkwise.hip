@@ -96,17 +96,16 @@ __device__ __forceinline__ bf16x8 scale_frag(bf16x8 x, const float* w) {
 __device__ __forceinline__ float scale_frag(float x, const float* w) { return x * w[0]; }
 
 // Row padding (elements) of a token-major LDS tile: the smallest padding that
-// makes a row step move the bank by one of the given residues (mod 64 dwords).
-// Tiles read with 16-byte fragment loads over 16 rows use 8 + 16i; tiles read
-// only with transposing reads (4 rows x 32 bytes per 16 lanes) use 12, 28, 36,
-// 52.  Both choices were the fastest in a sweep on MI355X.
-constexpr int lds_row_pad(int row_elems, int esize, bool transposing) {
+// makes a row step move the bank by 8 + 16i dwords (mod 64).  In a sweep on
+// MI355X these residues were the fastest both for 16-byte fragment loads
+// over 16 rows and for transposing reads in the frag_rows layout (16 lanes
+// over 16 consecutive rows, 32 contiguous bytes per row).
+constexpr int lds_row_pad(int row_elems, int esize) {
   const int dw = row_elems * esize / 4;
   int best = 64;
-  const int rq[4] = {8, 24, 40, 56}, rv[4] = {12, 28, 36, 52};
+  const int rq[4] = {8, 24, 40, 56};
   for (int i = 0; i < 4; ++i) {
-    const int r = transposing ? rv[i] : rq[i];
-    const int pad = ((r - dw % 64) % 64 + 64) % 64;
+    const int pad = ((rq[i] - dw % 64) % 64 + 64) % 64;
     if (pad < best) best = pad;
   }
   return best * 4 / esize;
@@ -122,7 +121,7 @@ constexpr int lds_pad_res(int row_elems, int esize, int res) {
 #define MLSTM_P3_QRES 8
 #endif
 #ifndef MLSTM_P3_KRES
-#define MLSTM_P3_KRES 8
+#define MLSTM_P3_KRES 24
 #endif
 
 template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L>
@@ -146,10 +145,11 @@ struct ChunkCfg {
   static constexpr int VE = 16 / (int)sizeof(T);  // elements per 16 bytes
   // row strides (elements) of the token-major tiles
   // sQ is read with 16-byte row fragments only; sK also with transposing
-  // reads (the update's K^T), so the two strides are chosen apart
+  // reads (the update's K^T, 16-byte spaced 8-byte runs per row), whose
+  // bank spread is best at residue 24
   static constexpr int QS = DQK + lds_pad_res(DQK, (int)sizeof(T), MLSTM_P3_QRES);  // sQ
   static constexpr int KST = DQK + lds_pad_res(DQK, (int)sizeof(T), MLSTM_P3_KRES);  // sK
-  static constexpr int VS = W + lds_row_pad(W, (int)sizeof(T), true);       // sV
+  static constexpr int VS = W + lds_row_pad(W, (int)sizeof(T));  // sV
   static constexpr int PS = L + 16 / (int)sizeof(T);  // sP
   // bf16 outputs are staged in LDS (sH, token-major) and written as whole
   // 16-byte units of the work-group's row segment
@@ -180,15 +180,33 @@ struct ChunkCfg {
   }
 };
 
+// Row (token) inside a K-row block of element e of lane group lg, for MFMA
+// operands whose k index runs along tokens.  bf16: lane group lg takes rows
+// 4lg .. 4lg+3 and 16+4lg .. 16+4lg+3, so that the 16 lanes of one
+// transposing read cover 16 consecutive rows (fewer LDS bank conflicts than
+// 8 consecutive rows per lane group).  The contraction does not care which k
+// is which token as long as both operands agree, so every operand along
+// tokens (K^T, V^T, P rows, the weights w) uses this order.  fp32: row lg.
+template <typename T>
+__device__ __forceinline__ constexpr int krow(int lg, int e) {
+  return sizeof(T) == 2 ? 4 * lg + (e & 3) + 16 * (e >> 2) : lg + e;
+}
+// Position of token t (t % 4 == 0) in a P row stored so that a 16-byte row
+// fragment at 8 lg holds the tokens krow(lg, 0..7) of its block.
+template <typename T>
+__device__ __forceinline__ constexpr int kpos4(int t) {
+  return sizeof(T) == 2 ? (t & ~31) + 8 * ((t >> 2) & 3) + 4 * ((t >> 4) & 1) : t;
+}
+
 // MFMA fragment along the rows of a token-major tile: lane (lr, lg) gets rows
-// r0 + KL*lg + e (e < KL) of one column.
+// kb0 + krow(lg, e) of one column.
 //   bf16: two transposing reads; source lane lr addresses column csrc(lr),
 //         chosen by the caller so that output lane lr sees its column.
 //   fp32: one element, column ccol(lr).
-__device__ __forceinline__ bf16x8 frag_rows(const __bf16* tile, int RS, int r0, int lr, int csrc) {
-  const __bf16* p = tile + (r0 + (lr >> 2)) * RS + csrc;
+__device__ __forceinline__ bf16x8 frag_rows(const __bf16* tile, int RS, int kb0, int lg, int lr, int csrc) {
+  const __bf16* p = tile + (kb0 + 4 * lg + (lr >> 2)) * RS + csrc;
   const bf16x4 a = ds_read_tr16(p);
-  const bf16x4 b = ds_read_tr16(p + 4 * RS);
+  const bf16x4 b = ds_read_tr16(p + 16 * RS);
   bf16x8 r;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -197,9 +215,9 @@ __device__ __forceinline__ bf16x8 frag_rows(const __bf16* tile, int RS, int r0, 
   }
   return r;
 }
-__device__ __forceinline__ float frag_rows(const float* tile, int RS, int r0, int lr, int ccol) {
+__device__ __forceinline__ float frag_rows(const float* tile, int RS, int kb0, int lg, int lr, int ccol) {
   (void)lr;
-  return tile[r0 * RS + ccol];
+  return tile[(kb0 + lg) * RS + ccol];
 }
 
 // Pass 3: per (batch*head, superchunk, d_v slice), the chunks of the
@@ -443,7 +461,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int kb = 0; kb < NKL; ++kb) vf[ct][kb] = frag_rows(sV, VS, kb * K + KL * lg, lr, vcol + ct * 16);
+        for (int kb = 0; kb < NKL; ++kb) vf[ct][kb] = frag_rows(sV, VS, kb * K, lg, lr, vcol + ct * 16);
     };
     {
       // ---------------------------------------------------------- phase B
@@ -490,7 +508,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
               dsum += x;
               pv[i] = from_f32<T>(x);
             }
-            store4(&sP[(be * L + j) * PS + lt * 16 + 4 * lg], pv[0], pv[1], pv[2], pv[3]);
+            store4(&sP[(be * L + j) * PS + kpos4<T>(lt * 16 + 4 * lg)], pv[0], pv[1], pv[2], pv[3]);
           }
           dsum += __shfl_xor(dsum, 16, 64);
           dsum += __shfl_xor(dsum, 32, 64);
@@ -642,35 +660,20 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
       // goes to column group nt % 4).  With several blocks a work-group's waves
       // need not cover all blocks, so a plain loop over sK does it.
       constexpr bool NFRAG = !RET && NB == 1;
-      float dn[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) dn[nt] = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKL; ++kb) {
-        float wl[KL];
-#pragma unroll
-        for (int e = 0; e < KL; ++e) wl[e] = sW[kb * K + KL * lg + e];
         float wls[KL];
 #pragma unroll
-        for (int e = 0; e < KL; ++e) wls[e] = wl[e] * wscale;
+        for (int e = 0; e < KL; ++e) wls[e] = sW[kb * K + krow<T>(lg, e)] * wscale;
         frag wv[CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) wv[ct] = scale_frag(vf[ct][kb], wls);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const int kc = BF ? kcol + (nt >> 1) * 32 + (nt & 1) * 4 : kcol + perm_row<T>(nt, lr);
-          const frag ka = frag_rows(sK, KST, kb * K + KL * lg, lr, kc);
+          const frag ka = frag_rows(sK, KST, kb * K, lg, lr, kc);
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) st[nt][ct] = M::mma(ka, wv[ct], st[nt][ct]);
-          if constexpr (NFRAG) {
-            if (nt % NCG == cg) {
-#pragma unroll
-              for (int e = 0; e < KL; ++e) {
-                if constexpr (BF) dn[nt] += wl[e] * (float)ka[e];
-                else dn[nt] += wl[e] * ka;
-              }
-            }
-          }
           if ((nt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -682,15 +685,39 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
         }
       }
       if constexpr (NFRAG) {
+        // rows of tiles nt = cg, cg + NCG, ...: their K^T fragments are read
+        // again here, all before the first is used, so that no branch splits
+        // the MFMA loop above
+        constexpr int NJ = (NT + NCG - 1) / NCG;
+        float d[NJ];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          if (nt % NCG == cg) {
-            float d = dn[nt];
-            d += __shfl_xor(d, 16, 64);
-            d += __shfl_xor(d, 32, 64);
+        for (int j = 0; j < NJ; ++j) {
+          d[j] = 0.f;
+          const int nt = j * NCG + cg;  // wave-uniform
+          if (NT % NCG == 0 || nt < NT) {
+#pragma unroll
+            for (int kb = 0; kb < NKL; ++kb) {
+              const int kc = BF ? kcol + (nt >> 1) * 32 + (nt & 1) * 4 : kcol + perm_row<T>(nt, lr);
+              const frag ka = frag_rows(sK, KST, kb * K, lg, lr, kc);
+#pragma unroll
+              for (int e = 0; e < KL; ++e) {
+                const float wl = sW[kb * K + krow<T>(lg, e)];
+                if constexpr (BF) d[j] += wl * (float)ka[e];
+                else d[j] += wl * ka;
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int nt = j * NCG + cg;
+          if (NT % NCG == 0 || nt < NT) {
+            float x = d[j];
+            x += __shfl_xor(x, 16, 64);
+            x += __shfl_xor(x, 32, 64);
             if (lg == 0) {
               const int r = rb0 + perm_row<T>(nt, lr);
-              put_n(r, alpha * sNf[r] + d);
+              put_n(r, alpha * sNf[r] + x);
             }
           }
         }
@@ -895,8 +922,8 @@ struct LocalCfg {
   static constexpr int VE = 16 / ES;
   // row strides: residue 8 + 16i dwords (a 128-wide bf16 row pads to
   // 288 bytes, so a 32-row region is exactly 9 KB)
-  static constexpr int RK = TR + lds_row_pad(TR, ES, false);
-  static constexpr int RV = TC + lds_row_pad(TC, ES, false);
+  static constexpr int RK = TR + lds_row_pad(TR, ES);
+  static constexpr int RV = TC + lds_row_pad(TC, ES);
   static constexpr int UK = RK * ES / 16;  // 16-byte units per padded K row
   static constexpr int UV = RV * ES / 16;
   static constexpr int NIK = (KS * RK * ES + 1023) / 1024;  // load instructions per K region
@@ -1072,15 +1099,14 @@ __global__ __launch_bounds__(256) void local_state_kernel(ChunkParams p) {
     const T* sv = reinterpret_cast<const T*>(st + C::NIK * 1024);
 #pragma unroll
     for (int kb = 0; kb < NKL; ++kb) {
-      const int r0 = kb * K + KL * lg;  // first token of this lane's k elements
       float wk[KL];
 #pragma unroll
-      for (int e = 0; e < KL; ++e) wk[e] = sw[c * KS + r0 + e];
+      for (int e = 0; e < KL; ++e) wk[e] = sw[c * KS + kb * K + krow<T>(lg, e)];
       frag af[MT], bfr[NTc];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) af[mt] = frag_rows(sk, RK, r0, lr, acol + mt * 16);
+      for (int mt = 0; mt < MT; ++mt) af[mt] = frag_rows(sk, RK, kb * K, lg, lr, acol + mt * 16);
 #pragma unroll
-      for (int nt = 0; nt < NTc; ++nt) bfr[nt] = frag_rows(sv, RV, r0, lr, bcol + nt * 16);
+      for (int nt = 0; nt < NTc; ++nt) bfr[nt] = frag_rows(sv, RV, kb * K, lg, lr, bcol + nt * 16);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if constexpr (BF) {
