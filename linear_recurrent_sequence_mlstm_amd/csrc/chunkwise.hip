@@ -142,6 +142,13 @@ struct ChunkCfg {
   static constexpr int NKQB = DQKB / K;           // feature k-blocks of a block
   static constexpr int NKQR = RPW / K;            // feature k-blocks of a wave's rows
   static constexpr int NTQK = NJT * (NJT + 1) / 2;  // causal score tiles
+  static constexpr int NUMAX = (NTQK + NCG * NRG - 1) / (NCG * NRG);  // score tiles per wave
+  static_assert(NUMAX <= 3, "at most three score tiles per wave");
+  // With one memory block, n~.q_j for query tile j is summed by wave j
+  // together with its first score tile (0, j), which reads the same Q rows;
+  // else in a loop of its own.
+  static constexpr bool FUSED_NQ = NB == 1;
+  static_assert(NJT <= NCG * NRG, "a wave per query tile");
   static constexpr int VE = 16 / (int)sizeof(T);  // elements per 16 bytes
   // row strides (elements) of the token-major tiles
   // sQ is read with 16-byte row fragments only; sK also with transposing
@@ -163,14 +170,14 @@ struct ChunkCfg {
   static_assert(DQK % NB == 0, "d_qk % nb");
   static_assert(RPW % (sizeof(T) == 2 ? 32 : 16) == 0, "state rows per wave");
   static_assert(L % K == 0 && L % 16 == 0 && L <= 64, "chunk length");
-  static_assert(NJT % NRG == 0, "token tiles per row group");
+  static_assert(NJT % NRG == 0 && NRG <= 2, "token tiles per row group");
   static_assert(WC % 16 == 0, "wave columns");
   static constexpr size_t lds_bytes(bool ret) {
     size_t b = 0;
     b += (size_t)L * KST * sizeof(T);            // sK
     b += (size_t)L * VS * sizeof(T);             // sV
     b += 6 * L * 4 + 16;                         // gate vectors
-    if (!ret) b += DQK * 4 + 16 * DQK * sizeof(T);  // n~
+    if (!ret) b += DQK * 4 + 2 * DQK * sizeof(T);  // n~
     b += (size_t)L * QS * sizeof(T);             // sQ
     b += (size_t)NB * L * PS * sizeof(T);        // sP
     b += (size_t)(NJT + 1) * L * 4;              // den partials
@@ -250,9 +257,10 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   __shared__ __attribute__((aligned(16))) T sP[NB * L * PS];
   __shared__ __attribute__((aligned(16))) f32x4 sX[XCH ? NCG * NJT * CT * 64 : 1];
   __shared__ __attribute__((aligned(16))) T sH[HST ? L * HS : 8];  // outputs of the chunk
-  // n~ as a 16-row A-operand tile: row 0 = bf16 hi part, row 1 = lo part,
-  // rows 2..15 zero (fp32: row 0 = n~, row 1 zero)
-  __shared__ __attribute__((aligned(16))) T sNh[RET ? 8 : 16 * DQK];
+  // n~ as rows 0 and 1 of a 16-row A-operand tile (rows 2..15 are zero and
+  // not stored): row 0 = bf16 hi part, row 1 = lo part (fp32: row 0 = n~,
+  // row 1 zero)
+  __shared__ __attribute__((aligned(16))) T sNh[RET ? 8 : 2 * DQK];
   __shared__ float sNf[RET ? 4 : DQK];
   __shared__ float sA2[L], sM2[L], sRS[L], sCL[L], sBT[L], sW[L];
   __shared__ float sDenPart[NJT * L];
@@ -331,8 +339,6 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
     sNh[DQK + r] = from_f32<T>(x - to_f32(hi));
   };
   if constexpr (!RET) {
-    for (int e = tid; e < 16 * DQK; e += NTH) sNh[e] = from_f32<T>(0.f);
-    __syncthreads();
     for (int r = tid; r < DQK; r += NTH) put_n(r, Sin ? Sin[CS + r] : 0.f);
   }
   // masked (l > j) tiles of P and their den partials are never written
@@ -465,37 +471,71 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
     };
     {
       // ---------------------------------------------------------- phase B
-      // causal score tiles (key tile lt, query tile jt), spread over the waves
+      // causal score tiles (key tile lt, query tile jt): the k-th tile of
+      // wave w is k NW + w, or k NW + NW - 1 - w for odd k (so that with
+      // NTQK < 2 NW the second tiles go to the last waves, not to waves
+      // 0 .. NJT-1, which also sum n~.q); a wave's tiles are computed
+      // interleaved
+      auto tile_of = [](int ti, int& lt, int& jt) __attribute__((always_inline)) {
+        lt = 0;
+        jt = ti;
+        int rem = NJT;
+        while (jt >= rem) {  // tile index -> (lt, jt) with lt <= jt
+          jt -= rem;
+          ++lt;
+          --rem;
+        }
+        jt += lt;
+      };
+      auto tile_idx = [&](int k) __attribute__((always_inline)) { return k * NW + ((k & 1) ? NW - 1 - w : w); };
+      // rows 0 (hi) and 1 (lo) of the n~ tile; zero in rows 2..15
+      auto n_frag = [&](int kb) __attribute__((always_inline)) {
+        const frag f = M::load(&sNh[(lr & 1) * DQK + kb * K + KL * lg]);
+        return lr < 2 ? f : M::zero();
+      };
+      auto scores = [&](auto nuc, auto wnc) __attribute__((always_inline)) {
+        constexpr int NU = decltype(nuc)::value;
+        constexpr bool WN = decltype(wnc)::value;  // also n~ . q of query tile jt[0]
+        int lt[NU], jt[NU];
 #pragma unroll
-      for (int ti = 0; ti < C::NTQK; ++ti) {
-        if (w == ti % NW) {
-          int lt = 0, jt = ti, rem = NJT;
-          while (jt >= rem) {  // tile index -> (lt, jt) with lt <= jt
-            jt -= rem;
-            ++lt;
-            --rem;
-          }
-          jt += lt;
-          f32x4 pt[NB];
+        for (int u = 0; u < NU; ++u) tile_of(tile_idx(u), lt[u], jt[u]);
+        f32x4 pt[NU][NB];
+        f32x4 pn = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int be = 0; be < NB; ++be) {
-            pt[be] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int be = 0; be < NB; ++be) {
 #pragma unroll
-            for (int kk = 0; kk < NKQB; ++kk) {
-              const int kb = be * NKQB + kk;
-              const frag kf = M::load(&sK[(lt * 16 + lr) * KST + kb * K + KL * lg]);
-              const frag qj = M::load(&sQ[(jt * 16 + lr) * QS + kb * K + KL * lg]);
-              pt[be] = M::mma(kf, qj, pt[be]);
-              if (kk & 1) __builtin_amdgcn_sched_barrier(0);
+          for (int u = 0; u < NU; ++u) pt[u][be] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < NKQB; ++kk) {
+            const int kb = be * NKQB + kk;
+            frag kf[NU], qj[NU];
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+              kf[u] = M::load(&sK[(lt[u] * 16 + lr) * KST + kb * K + KL * lg]);
+              qj[u] = M::load(&sQ[(jt[u] * 16 + lr) * QS + kb * K + KL * lg]);
             }
+            frag nf;
+            if constexpr (WN) nf = n_frag(kb);
+#pragma unroll
+            for (int u = 0; u < NU; ++u) pt[u][be] = M::mma(kf[u], qj[u], pt[u][be]);
+            if constexpr (WN) pn = M::mma(nf, qj[0], pn);
+            if (kk & 1) __builtin_amdgcn_sched_barrier(0);
           }
-          // decay factors, P to LDS, den partial sums
-          const int j = jt * 16 + lr;
+        }
+        if constexpr (WN) {
+          if (lg == 0) sDenInter[jt[0] * 16 + lr] = pn[0] + pn[1];
+        }
+        // decay factors, P to LDS, den partial sums (of the fp32 products:
+        // summing the bf16-rounded P instead loses too much where the
+        // normaliser cancels)
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const int j = jt[u] * 16 + lr;
           const float m2 = sM2[j];
           float fac[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int l = lt * 16 + 4 * lg + i;
+            const int l = lt[u] * 16 + 4 * lg + i;
             fac[i] = (l <= j) ? exp2_fast(sA2[l] - m2) : 0.f;
           }
           float dsum = 0.f;
@@ -504,27 +544,46 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
             T pv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float x = pt[be][i] * fac[i];
+              const float x = pt[u][be][i] * fac[i];
               dsum += x;
               pv[i] = from_f32<T>(x);
             }
-            store4(&sP[(be * L + j) * PS + kpos4<T>(lt * 16 + 4 * lg)], pv[0], pv[1], pv[2], pv[3]);
+            store4(&sP[(be * L + j) * PS + kpos4<T>(lt[u] * 16 + 4 * lg)], pv[0], pv[1], pv[2], pv[3]);
           }
           dsum += __shfl_xor(dsum, 16, 64);
           dsum += __shfl_xor(dsum, 32, 64);
-          if (lg == 0) sDenPart[lt * L + j] = dsum;
+          if (lg == 0) sDenPart[lt[u] * L + j] = dsum;
+        }
+      };
+      {
+        int nu = 0;  // tiles of this wave (wave-uniform)
+#pragma unroll
+        for (int k = 0; k < C::NUMAX; ++k) nu += tile_idx(k) < C::NTQK ? 1 : 0;
+        auto run = [&](auto wnc) __attribute__((always_inline)) {
+          if (nu == 3) {
+            if constexpr (C::NUMAX >= 3) scores(std::integral_constant<int, 3>{}, wnc);
+          } else if (nu == 2) {
+            if constexpr (C::NUMAX >= 2) scores(std::integral_constant<int, 2>{}, wnc);
+          } else if (nu == 1) {
+            scores(std::integral_constant<int, 1>{}, wnc);
+          }
+        };
+        if constexpr (!RET && C::FUSED_NQ) {
+          if (w < NJT) run(std::true_type{});  // first tile (0, w): query tile w
+          else run(std::false_type{});
+        } else {
+          run(std::false_type{});
         }
       }
-      // n~ . q_j per query tile, n~ split in hi + lo parts (last waves)
-      if constexpr (!RET) {
+      // n~ . q_j per query tile in a loop of its own (several memory blocks)
+      if constexpr (!RET && !C::FUSED_NQ) {
 #pragma unroll
         for (int jt = 0; jt < NJT; ++jt) {
           if (w == NW - 1 - (jt % NW)) {
             f32x4 pn = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < NKQ; ++kb) {
-              const frag nf = M::load(&sNh[lr * DQK + kb * K + KL * lg]);
-              pn = M::mma(nf, M::load(&sQ[(jt * 16 + lr) * QS + kb * K + KL * lg]), pn);
+              pn = M::mma(n_frag(kb), M::load(&sQ[(jt * 16 + lr) * QS + kb * K + KL * lg]), pn);
               if (kb & 1) __builtin_amdgcn_sched_barrier(0);
             }
             if (lg == 0) sDenInter[jt * 16 + lr] = pn[0] + pn[1];
@@ -554,12 +613,18 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
       // hand the readout partials of the other row group's token tiles over
+      // (the row group is a compile-time constant in each copy of the code)
       if constexpr (XCH) {
+        auto exchange = [&](auto rgc) __attribute__((always_inline)) {
+          constexpr int RG = decltype(rgc)::value;
 #pragma unroll
-        for (int jt = 0; jt < NJT; ++jt)
-          if (jt / JPW != rg)
+          for (int jt = 0; jt < NJT; ++jt)
+            if (jt / JPW != RG)
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) sX[((cg * NJT + jt) * CT + ct) * 64 + lane] = acc[jt][ct];
+              for (int ct = 0; ct < CT; ++ct) sX[((cg * NJT + jt) * CT + ct) * 64 + lane] = acc[jt][ct];
+        };
+        if (rg == 0) exchange(std::integral_constant<int, 0>{});
+        else exchange(std::integral_constant<int, 1>{});
       }
       __syncthreads();  // B2: P, den partials and readout partials ready
       // output-gate values of this wave's outputs, issued before the next
@@ -579,62 +644,66 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
       load_vf();
 
       // ---------------------------------------------------------- phase C
+      // one copy of the code per row group, so that the token tiles (and the
+      // accumulators they select) are compile-time constants
+      auto phase_c = [&](auto rgc) __attribute__((always_inline)) {
+        constexpr int JT0 = decltype(rgc)::value * JPW;
 #pragma unroll
-      for (int jj = 0; jj < JPW; ++jj) {
-        const int jt = jt0 + jj;  // runtime, wave-uniform
-        f32x4 o_acc[CT];
+        for (int jj = 0; jj < JPW; ++jj) {
+          const int jt = JT0 + jj;  // compile-time after unrolling
+          f32x4 o_acc[CT];
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          // select acc[jt][ct] with a compile-time index
-          f32x4 a = acc[0][ct];
+          for (int ct = 0; ct < CT; ++ct) {
+            f32x4 a = acc[jt][ct];
+            if constexpr (XCH) a += sX[((cg * NJT + jt) * CT + ct) * 64 + lane];
+            o_acc[ct] = a;
+          }
+          const int j = jt * 16 + lr;
+          const float rs = sRS[j];
+          const float rs_state = rs * exp2_fast(sig);
 #pragma unroll
-          for (int t = 1; t < NJT; ++t)
-            if (jt == t) a = acc[t][ct];
-          if constexpr (XCH) a += sX[((cg * NJT + jt) * CT + ct) * 64 + lane];
-          o_acc[ct] = a;
-        }
-        const int j = jt * 16 + lr;
-        const float rs = sRS[j];
-        const float rs_state = rs * exp2_fast(sig);
+          for (int ct = 0; ct < CT; ++ct) o_acc[ct] *= rs_state;
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) o_acc[ct] *= rs_state;
+          for (int kb = 0; kb < NKL; ++kb) {
+            if (kb * K <= jt * 16 + 15) {
+              const frag pf = M::load(&sP[(blk * L + jt * 16 + lr) * PS + kb * K + KL * lg]);
 #pragma unroll
-        for (int kb = 0; kb < NKL; ++kb) {
-          if (kb * K <= jt * 16 + 15) {
-            const frag pf = M::load(&sP[(blk * L + jt * 16 + lr) * PS + kb * K + KL * lg]);
+              for (int ct = 0; ct < CT; ++ct) o_acc[ct] = M::mma(vf[ct][kb], pf, o_acc[ct]);
+            }
+          }
+          float inv;
+          if constexpr (RET) {
+            inv = 1.f;
+          } else {
+            float den = rs * sDenInter[j] + sBT[j];
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) o_acc[ct] = M::mma(vf[ct][kb], pf, o_acc[ct]);
+            for (int t = 0; t < NJT; ++t) den += sDenPart[t * L + j];
+            inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), sCL[j]));
+          }
+          // rows past T fall outside the output buffer and are dropped
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const int col = wcol0 + ct * 16 + 4 * lg;
+            float o[4] = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (has_o) {
+              raw4_to_f32<T>(oraw[jj][ct], o);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) o[i] = sigmoidf_(o[i]);
+            }
+            float hv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hv[i] = o[i] * o_acc[ct][i] * inv;
+            if constexpr (HST)
+              store4(&sH[j * HS + cg * WC + ct * 16 + 4 * lg], from_f32<T>(hv[0]), from_f32<T>(hv[1]),
+                     from_f32<T>(hv[2]), from_f32<T>(hv[3]));
+            else
+              bstore4<T>(rh, ((unsigned)(t0 + j) * DV + col) * ES, hv[0], hv[1], hv[2], hv[3]);
           }
         }
-        float inv;
-        if constexpr (RET) {
-          inv = 1.f;
-        } else {
-          float den = rs * sDenInter[j] + sBT[j];
-#pragma unroll
-          for (int t = 0; t < NJT; ++t) den += sDenPart[t * L + j];
-          inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), sCL[j]));
-        }
-        // rows past T fall outside the output buffer and are dropped
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const int col = wcol0 + ct * 16 + 4 * lg;
-          float o[4] = {1.f, 1.f, 1.f, 1.f};
-          if constexpr (has_o) {
-            raw4_to_f32<T>(oraw[jj][ct], o);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = sigmoidf_(o[i]);
-          }
-          float hv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) hv[i] = o[i] * o_acc[ct][i] * inv;
-          if constexpr (HST)
-            store4(&sH[j * HS + cg * WC + ct * 16 + 4 * lg], from_f32<T>(hv[0]), from_f32<T>(hv[1]),
-                   from_f32<T>(hv[2]), from_f32<T>(hv[3]));
-          else
-            bstore4<T>(rh, ((unsigned)(t0 + j) * DV + col) * ES, hv[0], hv[1], hv[2], hv[3]);
-        }
-      }
+      };
+      if constexpr (NRG == 1) phase_c(std::integral_constant<int, 0>{});
+      else if (rg == 0) phase_c(std::integral_constant<int, 0>{});
+      else phase_c(std::integral_constant<int, 1>{});
     }
 
     if (more) {
