@@ -137,6 +137,9 @@ struct ChunkCfg {
   static constexpr int W = NCG * WC;              // d_v columns per work-group
   static constexpr int NJT = L / 16;              // 16-token tiles per chunk
   static constexpr int JPW = NJT / NRG;           // token tiles finished per wave
+  // jj-th token tile finished by row group g (snake order) and its owner
+  static constexpr int jt_of(int g, int jj) { return jj * NRG + ((jj & 1) ? NRG - 1 - g : g); }
+  static constexpr int owner_of(int jt) { return ((jt / NRG) & 1) ? NRG - 1 - jt % NRG : jt % NRG; }
   static constexpr int NKL = L / K;               // token k-blocks per chunk
   static constexpr int NKQ = DQK / K;             // feature k-blocks of a head
   static constexpr int NKQB = DQKB / K;           // feature k-blocks of a block
@@ -292,7 +295,9 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   const int wcl0 = wcol0 - blk * DVB;     // first column inside the block
   const int rrow0 = rg * RPW;             // first state row of this wave inside the block
   const int rb0 = blk * DQKB + rrow0;     // ... as a feature index of the head
-  const int jt0 = rg * JPW;               // first token tile finished by this wave
+  // Token tiles finished by the waves of row group g: jj-th = jt_of(g, jj),
+  // snake order (0 and 3 for one row group, 1 and 2 for the other with four
+  // tiles), so that both groups get the same share of causal P V work.
 
   // buffer resources over this (batch, head): reads past T return zero
   const auto rq = make_rsrc(static_cast<const T*>(p.q) + (size_t)bh * T_ * DQK, (unsigned)T_ * DQK * ES);
@@ -499,6 +504,18 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
         int lt[NU], jt[NU];
 #pragma unroll
         for (int u = 0; u < NU; ++u) tile_of(tile_idx(u), lt[u], jt[u]);
+        // decay factors of the tiles first: they do not wait for the MFMAs
+        float fac[NU][4];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const int j = jt[u] * 16 + lr;
+          const float m2 = sM2[j];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int l = lt[u] * 16 + 4 * lg + i;
+            fac[u][i] = (l <= j) ? exp2_fast(sA2[l] - m2) : 0.f;
+          }
+        }
         f32x4 pt[NU][NB];
         f32x4 pn = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -525,33 +542,24 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
         if constexpr (WN) {
           if (lg == 0) sDenInter[jt[0] * 16 + lr] = pn[0] + pn[1];
         }
-        // decay factors, P to LDS, den partial sums (of the fp32 products:
-        // summing the bf16-rounded P instead loses too much where the
-        // normaliser cancels)
+        // P to LDS, den partial sums (of the fp32 products: summing the
+        // bf16-rounded P instead loses too much where the normaliser cancels)
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
           const int j = jt[u] * 16 + lr;
-          const float m2 = sM2[j];
-          float fac[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int l = lt[u] * 16 + 4 * lg + i;
-            fac[i] = (l <= j) ? exp2_fast(sA2[l] - m2) : 0.f;
-          }
           float dsum = 0.f;
 #pragma unroll
           for (int be = 0; be < NB; ++be) {
             T pv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float x = pt[u][be][i] * fac[i];
+              const float x = pt[u][be][i] * fac[u][i];
               dsum += x;
               pv[i] = from_f32<T>(x);
             }
             store4(&sP[(be * L + j) * PS + kpos4<T>(lt[u] * 16 + 4 * lg)], pv[0], pv[1], pv[2], pv[3]);
           }
-          dsum += __shfl_xor(dsum, 16, 64);
-          dsum += __shfl_xor(dsum, 32, 64);
+          dsum = sum_lane_groups(dsum);
           if (lg == 0) sDenPart[lt[u] * L + j] = dsum;
         }
       };
@@ -619,7 +627,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
           constexpr int RG = decltype(rgc)::value;
 #pragma unroll
           for (int jt = 0; jt < NJT; ++jt)
-            if (jt / JPW != RG)
+            if (C::owner_of(jt) != RG)
 #pragma unroll
               for (int ct = 0; ct < CT; ++ct) sX[((cg * NJT + jt) * CT + ct) * 64 + lane] = acc[jt][ct];
         };
@@ -636,7 +644,8 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct)
             oraw[jj][ct] = bload4_raw<T>(
-                ro, ((unsigned)(t0 + (jt0 + jj) * 16 + lr) * DV + wcol0 + ct * 16 + 4 * lg) * ES);
+                ro, ((unsigned)(t0 + (jj * NRG + ((jj & 1) ? NRG - 1 - rg : rg)) * 16 + lr) * DV + wcol0 +
+                     ct * 16 + 4 * lg) * ES);
       }
       // Q of the next chunk now (sQ is free after B2); its K and V after
       // phase C, so that fewer staging registers are live at once
@@ -647,10 +656,10 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
       // one copy of the code per row group, so that the token tiles (and the
       // accumulators they select) are compile-time constants
       auto phase_c = [&](auto rgc) __attribute__((always_inline)) {
-        constexpr int JT0 = decltype(rgc)::value * JPW;
+        constexpr int RG = decltype(rgc)::value;
 #pragma unroll
         for (int jj = 0; jj < JPW; ++jj) {
-          const int jt = JT0 + jj;  // compile-time after unrolling
+          const int jt = C::jt_of(RG, jj);  // compile-time after unrolling
           f32x4 o_acc[CT];
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) {
@@ -781,9 +790,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
         for (int j = 0; j < NJ; ++j) {
           const int nt = j * NCG + cg;
           if (NT % NCG == 0 || nt < NT) {
-            float x = d[j];
-            x += __shfl_xor(x, 16, 64);
-            x += __shfl_xor(x, 32, 64);
+            const float x = sum_lane_groups(d[j]);
             if (lg == 0) {
               const int r = rb0 + perm_row<T>(nt, lr);
               put_n(r, alpha * sNf[r] + x);
@@ -1232,9 +1239,7 @@ __global__ __launch_bounds__(256) void local_state_kernel(ChunkParams p) {
       // acol-row + mt*16 + lr over their k elements: fixed-order sum over them
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        float d = dn[mt];
-        d += __shfl_xor(d, 16, 64);
-        d += __shfl_xor(d, 32, 64);
+        const float d = sum_lane_groups(dn[mt]);
         if (lg == 0) dst[CS + f0 + wr * (TR / WR) + mt * 16 + lr] = d;
       }
     }

@@ -74,6 +74,15 @@ struct Mma<float> {
   __device__ __forceinline__ static frag zero() { return 0.f; }
 };
 
+// Sum over the four 16-lane groups of a wave, valid in lanes 0..15 (gfx950
+// lane swaps: lanes 32..63 meet lanes 0..31, then lanes 16..31 meet 0..15).
+__device__ __forceinline__ float sum_lane_groups(float x) {
+  const unsigned u = __float_as_uint(x);
+  const float s = x + __uint_as_float(__builtin_amdgcn_permlane32_swap(u, u, false, false)[1]);
+  const unsigned v = __float_as_uint(s);
+  return s + __uint_as_float(__builtin_amdgcn_permlane16_swap(v, v, false, false)[1]);
+}
+
 // Vector of 16 bytes of element type T.
 template <typename T>
 struct Vec16 {
