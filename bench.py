@@ -234,7 +234,7 @@ def main():
     sha_st = source_sha("step.hip", "common.h")
     roof = dict(bound="hbm", achieved=pf["bytes"] / kern_s / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic_from_profiles("chunk_kernel_full", sha_cw)
+    roof["traffic"] = traffic_from_profiles("chunk_kernel", sha_cw)
     roof["kernel"] = "chunk_kernel (per-chunk readout/update pass)"
     roof["mfma_tflops"] = pf["flops"] / kern_s / 1e12
     roof["mfma_frac"] = roof["mfma_tflops"] / MFMA_BF16_PEAK_TFLOPS

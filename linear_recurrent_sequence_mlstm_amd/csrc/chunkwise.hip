@@ -70,13 +70,10 @@ struct StateFrag;
 template <int NT, int CT>
 struct StateFrag<__bf16, NT, CT> {
   __device__ __forceinline__ static bf16x8 get(const f32x4 (&st)[NT][CT], int kk, int ct) {
-    bf16x8 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      r[i] = (__bf16)st[2 * kk][ct][i];
-      r[4 + i] = (__bf16)st[2 * kk + 1][ct][i];
-    }
-    return r;
+    const f32x4 a = st[2 * kk][ct], b = st[2 * kk + 1][ct];
+    const u32x4 r = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                     pack_bf16x2(b[2], b[3])};
+    return __builtin_bit_cast(bf16x8, r);
   }
 };
 template <int NT, int CT>
@@ -88,10 +85,10 @@ struct StateFrag<float, NT, CT> {
 
 // fragment scaled by per-k weights (weights for k = base .. base+KL-1)
 __device__ __forceinline__ bf16x8 scale_frag(bf16x8 x, const float* w) {
-  bf16x8 r;
+  u32x4 r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (__bf16)((float)x[e] * w[e]);
-  return r;
+  for (int q = 0; q < 4; ++q) r[q] = pack_bf16x2((float)x[2 * q] * w[2 * q], (float)x[2 * q + 1] * w[2 * q + 1]);
+  return __builtin_bit_cast(bf16x8, r);
 }
 __device__ __forceinline__ float scale_frag(float x, const float* w) { return x * w[0]; }
 
@@ -550,14 +547,13 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
           float dsum = 0.f;
 #pragma unroll
           for (int be = 0; be < NB; ++be) {
-            T pv[4];
+            float x[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float x = pt[u][be][i] * fac[u][i];
-              dsum += x;
-              pv[i] = from_f32<T>(x);
+              x[i] = pt[u][be][i] * fac[u][i];
+              dsum += x[i];
             }
-            store4(&sP[(be * L + j) * PS + kpos4<T>(lt[u] * 16 + 4 * lg)], pv[0], pv[1], pv[2], pv[3]);
+            store4f(&sP[(be * L + j) * PS + kpos4<T>(lt[u] * 16 + 4 * lg)], x[0], x[1], x[2], x[3]);
           }
           dsum = sum_lane_groups(dsum);
           if (lg == 0) sDenPart[lt[u] * L + j] = dsum;
@@ -703,8 +699,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) hv[i] = o[i] * o_acc[ct][i] * inv;
             if constexpr (HST)
-              store4(&sH[j * HS + cg * WC + ct * 16 + 4 * lg], from_f32<T>(hv[0]), from_f32<T>(hv[1]),
-                     from_f32<T>(hv[2]), from_f32<T>(hv[3]));
+              store4f(&sH[j * HS + cg * WC + ct * 16 + 4 * lg], hv[0], hv[1], hv[2], hv[3]);
             else
               bstore4<T>(rh, ((unsigned)(t0 + j) * DV + col) * ES, hv[0], hv[1], hv[2], hv[3]);
           }
@@ -1032,17 +1027,8 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// fragment times per-k weights (KL consecutive k)
-__device__ __forceinline__ bf16x8 scale_frag8(bf16x8 x, const float (&w)[8], float (&dn)) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float kv = (float)x[e];
-    dn += w[e] * kv;
-    r[e] = (__bf16)(kv * w[e]);
-  }
-  return r;
-}
+// fragment times per-k weights, rounded back to bf16 in pairs
+__device__ __forceinline__ bf16x8 scale_frag8(bf16x8 x, const float (&w)[8]) { return scale_frag(x, w); }
 
 template <typename T, int DQK, int NB, int TR, int TC, int L, bool RET>
 __global__ __launch_bounds__(256) void local_state_kernel(ChunkParams p) {
@@ -1135,7 +1121,7 @@ __global__ __launch_bounds__(256) void local_state_kernel(ChunkParams p) {
   };
   constexpr int NV = JA;  // vm operations of one step of one wave
 
-  // the first three steps in flight, then w of the superchunk into LDS
+  // the first four steps in flight, then w of the superchunk into LDS
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
@@ -1153,14 +1139,20 @@ __global__ __launch_bounds__(256) void local_state_kernel(ChunkParams p) {
     issue(0, I0{});
     issue(1, I1{});
     issue(2, I2{});
+    issue(3, I3{});
 #pragma unroll
     for (int u = 0; u < C::GLMAX / 256; ++u) sw[tid + 256 * u] = wv[u];
   }
 
-  const bool do_dn = !RET && ctl == 0 && wcw == 0;  // one column tile and wave per row sums dn
-  float dn[MT];
+  // dn = sum_t w_t k_t by MFMA: the scaled K^T fragments times an all-ones B
+  // operand put the row sums into every column of dacc (rows 4 lg + i).  All
+  // waves compute it (no branch in the k-loop); one column tile and wave per
+  // row stores it.
+  const bool do_dn = !RET && ctl == 0 && wcw == 0;
+  f32x4 dacc[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) dn[mt] = 0.f;
+  for (int mt = 0; mt < MT; ++mt) dacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const frag ones = M::ones();
   f32x4 acc[MT][NTc];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -1169,55 +1161,78 @@ __global__ __launch_bounds__(256) void local_state_kernel(ChunkParams p) {
   // transposing-read source columns: output lane lr sees column base + lr
   const int acol = BF ? wr * (TR / WR) + 4 * (lr & 3) : wr * (TR / WR) + lr;
   const int bcol = BF ? wcw * (TC / WCW) + 4 * (lr & 3) : wcw * (TC / WCW) + lr;
-  auto mfma = [&](int c, auto bidx) __attribute__((always_inline)) {
+  // fragments of one k-step: A = K^T (scaled by w in registers), B = V^T
+  struct StepFrags {
+    frag af[NKL][MT];
+    frag bf[NKL][NTc];
+  };
+  auto load_step = [&](auto bidx, StepFrags& f) __attribute__((always_inline)) {
     const unsigned char* st = stage_ptr(bidx);
     const T* sk = reinterpret_cast<const T*>(st);
     const T* sv = reinterpret_cast<const T*>(st + C::NIK * 1024);
 #pragma unroll
     for (int kb = 0; kb < NKL; ++kb) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) f.af[kb][mt] = frag_rows(sk, RK, kb * K, lg, lr, acol + mt * 16);
+#pragma unroll
+      for (int nt = 0; nt < NTc; ++nt) f.bf[kb][nt] = frag_rows(sv, RV, kb * K, lg, lr, bcol + nt * 16);
+    }
+  };
+  auto scale_step = [&](int c, StepFrags& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < NKL; ++kb) {
       float wk[KL];
 #pragma unroll
       for (int e = 0; e < KL; ++e) wk[e] = sw[c * KS + kb * K + krow<T>(lg, e)];
-      frag af[MT], bfr[NTc];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) af[mt] = frag_rows(sk, RK, kb * K, lg, lr, acol + mt * 16);
-#pragma unroll
-      for (int nt = 0; nt < NTc; ++nt) bfr[nt] = frag_rows(sv, RV, kb * K, lg, lr, bcol + nt * 16);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        if constexpr (BF) {
-          float d = 0.f;
-          af[mt] = scale_frag8(af[mt], wk, d);
-          dn[mt] += d;
-        } else {
-          dn[mt] += wk[0] * af[mt];
-          af[mt] *= wk[0];
-        }
+        if constexpr (BF) f.af[kb][mt] = scale_frag8(f.af[kb][mt], wk);
+        else f.af[kb][mt] *= wk[0];
       }
+    }
+  };
+  auto mma_step = [&](const StepFrags& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < NKL; ++kb)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NTc; ++nt) acc[mt][nt] = M::mma(af[mt], bfr[nt], acc[mt][nt]);
+        for (int nt = 0; nt < NTc; ++nt) acc[mt][nt] = M::mma(f.af[kb][mt], f.bf[kb][nt], acc[mt][nt]);
+    if constexpr (!RET) {
+#pragma unroll
+      for (int kb = 0; kb < NKL; ++kb)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) dacc[mt] = M::mma(f.af[kb][mt], ones, dacc[mt]);
     }
   };
 
-  // ---- k-step c on stage b = c % 4: once this wave's loads of step c have
-  // landed, a barrier publishes the stage (and retires step c - 1's stage),
-  // step c + 3 goes into that freed stage, then the MFMAs of step c.  Steps
-  // past the end (the loop runs in groups of 4) only issue and wait.
-  auto body = [&](int c, auto bidx) __attribute__((always_inline)) {
+  // ---- Software pipeline over k-steps, stage of step c = c % 4.  Step 0's
+  // fragments are in registers before the loop.  Iteration c: once this
+  // wave's loads of step c + 1 have landed, a barrier publishes that stage
+  // (and guarantees every wave has read step c's stage into registers, so
+  // step c + 4 can go into it), then step c + 1's fragments are read while
+  // the MFMAs of step c run, and scaled by w after them.  Steps past the end
+  // (the loop runs in groups of 4) only issue and wait.
+  StepFrags F0, F1;
+  wait_vmcnt<3 * NV>();  // step 0 landed
+  lds_barrier();
+  load_step(I0{}, F0);
+  scale_step(0, F0);
+  auto body = [&](int c, auto bidx, StepFrags& cur, StepFrags& nxt) __attribute__((always_inline)) {
     constexpr int b = decltype(bidx)::value;
-    using B3 = std::integral_constant<int, (b + 3) % 4>;
+    using B1 = std::integral_constant<int, (b + 1) % 4>;
     wait_vmcnt<2 * NV>();
     lds_barrier();
-    issue(c + 3, B3{});
-    if (c < NSTEP) mfma(c, bidx);
+    issue(c + 4, bidx);
+    if (c + 1 < NSTEP) load_step(B1{}, nxt);
+    if (c < NSTEP) mma_step(cur);
+    if (c + 1 < NSTEP) scale_step(c + 1, nxt);
   };
   for (int c = 0; c < NSTEP; c += 4) {
-    body(c, I0{});
-    body(c + 1, I1{});
-    body(c + 2, I2{});
-    body(c + 3, I3{});
+    body(c, I0{}, F0, F1);
+    body(c + 1, I1{}, F1, F0);
+    body(c + 2, I2{}, F0, F1);
+    body(c + 3, I3{}, F1, F0);
   }
   wait_vmcnt<0>();  // no load into the ring in flight past this point
 
@@ -1234,14 +1249,11 @@ __global__ __launch_bounds__(256) void local_state_kernel(ChunkParams p) {
         dst[(size_t)blk * DQKB * DVB + (size_t)r * DVB + cl] = acc[mt][nt][i];
       }
   if constexpr (!RET) {
-    if (do_dn) {
-      // lanes lr of the 4 lane groups hold partial sums of feature
-      // acol-row + mt*16 + lr over their k elements: fixed-order sum over them
+    if (do_dn && lr == 0) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const float d = sum_lane_groups(dn[mt]);
-        if (lg == 0) dst[CS + f0 + wr * (TR / WR) + mt * 16 + lr] = d;
-      }
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[CS + f0 + wr * (TR / WR) + mt * 16 + 4 * lg + i] = dacc[mt][i];
     }
   }
 }

@@ -7,8 +7,10 @@ namespace mlstm {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -60,6 +62,11 @@ struct Mma<__bf16> {
     for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.f;
     return z;
   }
+  __device__ __forceinline__ static frag ones() {
+    frag z;
+    for (int e = 0; e < 8; ++e) z[e] = (__bf16)1.f;
+    return z;
+  }
 };
 
 template <>
@@ -72,6 +79,7 @@ struct Mma<float> {
   }
   __device__ __forceinline__ static frag load(const float* p) { return *p; }
   __device__ __forceinline__ static frag zero() { return 0.f; }
+  __device__ __forceinline__ static frag ones() { return 1.f; }
 };
 
 // Sum over the four 16-lane groups of a wave, valid in lanes 0..15 (gfx950
@@ -238,6 +246,13 @@ __device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
+// Two floats to a packed pair of bf16 (first one in the low half): one
+// v_cvt_pk_bf16_f32, where element-wise conversions would also need a permute.
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+  const f32x2 f = {a, b};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
+}
+
 // Four consecutive elements to an 8- (bf16) or 16-byte (fp32) aligned address.
 __device__ __forceinline__ void store4(__bf16* dst, __bf16 a, __bf16 b, __bf16 c, __bf16 d) {
   bf16x4 v;
@@ -250,5 +265,11 @@ __device__ __forceinline__ void store4(__bf16* dst, __bf16 a, __bf16 b, __bf16 c
 __device__ __forceinline__ void store4(float* dst, float a, float b, float c, float d) {
   *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
 }
+// Four floats rounded to T, stored as in store4 (bf16: two packed converts).
+__device__ __forceinline__ void store4f(__bf16* dst, float a, float b, float c, float d) {
+  const u32x2 v = {pack_bf16x2(a, b), pack_bf16x2(c, d)};
+  *reinterpret_cast<u32x2*>(dst) = v;
+}
+__device__ __forceinline__ void store4f(float* dst, float a, float b, float c, float d) { store4(dst, a, b, c, d); }
 
 }  // namespace mlstm
