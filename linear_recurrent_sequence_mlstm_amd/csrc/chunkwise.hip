@@ -176,7 +176,7 @@ struct ChunkCfg {
     size_t b = 0;
     b += (size_t)L * KST * sizeof(T);            // sK
     b += (size_t)L * VS * sizeof(T);             // sV
-    b += 6 * L * 4 + 16;                         // gate vectors
+    b += 2 * 6 * L * 4 + 16;                     // gate vectors, two sets
     if (!ret) b += DQK * 4 + 2 * DQK * sizeof(T);  // n~
     b += (size_t)L * QS * sizeof(T);             // sQ
     b += (size_t)NB * L * PS * sizeof(T);        // sP
@@ -262,10 +262,12 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   // row 1 zero)
   __shared__ __attribute__((aligned(16))) T sNh[RET ? 8 : 2 * DQK];
   __shared__ float sNf[RET ? 4 : DQK];
-  __shared__ float sA2[L], sM2[L], sRS[L], sCL[L], sBT[L], sW[L];
+  // gate vectors, two sets: wave 0 fills the next chunk's while the other
+  // waves still read the current chunk's
+  __shared__ float sA2b[2][L], sM2b[2][L], sRSb[2][L], sCLb[2][L], sBTb[2][L], sWb[2][L];
   __shared__ float sDenPart[NJT * L];
   __shared__ float sDenInter[L];
-  __shared__ float sAlpha;
+  __shared__ float sAlphab[2];
 
   const int tid = threadIdx.x;
   // The wave index must be known to be wave-uniform: branches on it guard
@@ -428,8 +430,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   // Gate factors of one chunk on wave 0 (one lane per token) from the
   // chunk-local logs b_j, a_j, g_j of the gate kernel: only the chain through
   // m_prev is left here.
-  auto gates = [&](int c) __attribute__((always_inline)) {
-    (void)c;
+  auto gates = [&](int gb) __attribute__((always_inline)) {
     const float a = __uint_as_float(rga), g = __uint_as_float(rgg), b = __uint_as_float(rgb);
     const float Mj = fmaxf(m_prev, g);
     const float gL = __uint_as_float(__builtin_amdgcn_readlane(rgg, L - 1));
@@ -438,14 +439,14 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
     if (lane < L) {
       const float mj = b + Mj;
       const float cl = exp2_fast(-mj);
-      sA2[lane] = a;
-      sM2[lane] = Mj;
-      sRS[lane] = exp2_fast(m_prev - Mj);
-      sCL[lane] = cl;
-      sBT[lane] = bias * cl;
-      sW[lane] = exp2_fast(a - ML);
+      sA2b[gb][lane] = a;
+      sM2b[gb][lane] = Mj;
+      sRSb[gb][lane] = exp2_fast(m_prev - Mj);
+      sCLb[gb][lane] = cl;
+      sBTb[gb][lane] = bias * cl;
+      sWb[gb][lane] = exp2_fast(a - ML);
     }
-    if (lane == 0) sAlpha = m_prev - ML;  // log2 of the state decay over the chunk
+    if (lane == 0) sAlphab[gb] = m_prev - ML;  // log2 of the state decay over the chunk
     m_prev = bL + ML;
   };
 
@@ -454,12 +455,35 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   load_kv(c_begin);
   store_q();
   store_kv();
-  if (w == 0) gates(c_begin);
+  if (w == 0) gates(0);
+
+  // The chunk's outputs from sH, whole 16-byte units per lane (rows past T
+  // are dropped by the buffer range).  Issued after the next chunk's B1, where
+  // the waves have slack, and once more after the loop.
+  auto store_h = [&](int tc) __attribute__((always_inline)) {
+    if constexpr (HST) {
+      constexpr int UR = W / VE;  // units per token row
+#pragma unroll
+      for (int u = tid; u < L * UR; u += NTH) {
+        const int j = u / UR, cu = u % UR;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(&sH[j * HS + cu * VE]);
+        __builtin_amdgcn_raw_buffer_store_b128(x, rh, ((unsigned)(tc + j) * DV + slice * W + cu * VE) * ES, 0, 0);
+      }
+    }
+  };
 
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * L;
     __syncthreads();  // B1: chunk staged, gate factors ready
+    if (c > c_begin) store_h(t0 - L);
     const bool more = c + 1 < c_end;
+    const int pb = (c - c_begin) & 1;  // gate vector set of this chunk
+    const float* sA2 = sA2b[pb];
+    const float* sM2 = sM2b[pb];
+    const float* sRS = sRSb[pb];
+    const float* sCL = sCLb[pb];
+    const float* sBT = sBTb[pb];
+    const float* sW = sWb[pb];
     // update of the state is needed unless this is the last chunk of a
     // superchunk whose end state nobody reads
     const bool need_update = more || (sc == p.NS - 1);
@@ -716,7 +740,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
     }
     // ------------------------------------------------------- state update
     if (need_update) {
-      const float la = sAlpha;
+      const float la = sAlphab[pb];
       const float alpha = exp2_fast(la);
       sig += la;
       if (sig < -64.f) {  // wave-uniform: rescale the registers, rarely
@@ -794,23 +818,13 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
         }
       }
     }
+    // the next chunk's gate vectors into the other set (its loads were
+    // issued before the update)
+    if (more && w == 0) gates(pb ^ 1);
     __syncthreads();  // B3: LDS free for the next chunk
-    if constexpr (HST) {
-      // the chunk's outputs, whole 16-byte units per lane (rows past T are
-      // dropped by the buffer range)
-      constexpr int UR = W / VE;  // units per token row
-#pragma unroll
-      for (int u = tid; u < L * UR; u += NTH) {
-        const int j = u / UR, cu = u % UR;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(&sH[j * HS + cu * VE]);
-        __builtin_amdgcn_raw_buffer_store_b128(x, rh, ((unsigned)(t0 + j) * DV + slice * W + cu * VE) * ES, 0, 0);
-      }
-    }
-    if (more) {
-      store_kv();
-      if (w == 0) gates(c + 1);
-    }
+    if (more) store_kv();
   }
+  store_h((c_end - 1) * L);
 
   // ---------------------------------------------------------------- outputs
   float* Sdst = nullptr;
