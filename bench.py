@@ -77,6 +77,44 @@ def traffic_from_profiles(kernel, sha):
     return rec.get("bytes_per_launch")
 
 
+class _KernelEvents:
+    """Pairs of HIP events for the library's profile hooks, created without
+    the system-scope fence (hipEventDisableSystemFence): a timing event with
+    that fence costs several microseconds of idle GPU per record here, which
+    would show up in the timed steps.  They still order with the stream."""
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.pairs = []
+        for _ in range(n):
+            pair = []
+            for _ in range(2):
+                e = ctypes.c_void_p()
+                rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(self.FLAGS))
+                if rc != 0:
+                    raise RuntimeError("hipEventCreateWithFlags failed (%d)" % rc)
+                pair.append(e)
+            self.pairs.append(tuple(pair))
+
+    def mean_ms(self):
+        tot = 0.0
+        for a, b in self.pairs:
+            ms = self.ct.c_float()
+            rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b)
+            if rc != 0:
+                raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+            tot += ms.value
+        return tot / len(self.pairs)
+
+    def close(self):
+        for pair in self.pairs:
+            for e in pair:
+                self.hip.hipEventDestroy(e)
+
+
 def bench_prefill(torch, mlstm, x, args, dev):
     spec = dict(B=1, H=8, T=8192, dqk=256, dv=512)
     sets = [x.to(dev)]
@@ -98,23 +136,22 @@ def bench_prefill(torch, mlstm, x, args, dev):
     for i in range(args.warmup):
         call(i)
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    for a, b in kev:  # create the HIP events before the timed region
-        a.record()
-        b.record()
+    kev = _KernelEvents(K)  # around the main kernel of every timed step
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    L = mlstm.lib()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record()
     for i in range(K):
-        mlstm.set_profile_events(*kev[i])
-        ev[i][0].record()
+        L.mlstm_set_profile_events(*kev.pairs[i])
         call(i)
-        ev[i][1].record()
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     mlstm.set_profile_events()
-    step_ms = sum(a.elapsed_time(b) for a, b in ev) / K
-    kern_ms = sum(a.elapsed_time(b) for a, b in kev) / K
+    step_ms = e0.elapsed_time(e1) / K
+    kern_ms = kev.mean_ms()
+    kev.close()
     byts, flops = prefill_work(B, H, T, dqk, dv)
     return dict(spec=spec, wall=wall, K=K, step_ms=step_ms, kern_ms=kern_ms, bytes=byts, flops=flops,
                 tokens=B * T)
@@ -136,16 +173,19 @@ def bench_decode(torch, mlstm, workload, args, dev):
         call(s)
     for t in (C, n, m):
         t.zero_()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(S)]
+    ev = _KernelEvents(S)  # around every step (both launches of a step)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rec = ev.hip.hipEventRecord
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(S):
-        ev[s][0].record()
+        rec(ev.pairs[s][0], ev.ct.c_void_p(stream))
         call(s)
-        ev[s][1].record()
+        rec(ev.pairs[s][1], ev.ct.c_void_p(stream))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = sum(a.elapsed_time(b) for a, b in ev) / S
+    step_ms = ev.mean_ms()
+    ev.close()
     byts, flops = decode_work(B, H, dqk, dv)
     return dict(B=B, H=H, dqk=dqk, dv=dv, S=S, wall=wall, step_ms=step_ms, bytes=byts, flops=flops)
 
@@ -185,8 +225,8 @@ def cpu_baseline(x, sample_tokens):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
