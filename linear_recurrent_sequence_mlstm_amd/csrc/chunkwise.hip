@@ -114,6 +114,9 @@ constexpr int lds_pad_res(int row_elems, int esize, int res) {
   const int dw = row_elems * esize / 4;
   return (((res - dw % 64) % 64 + 64) % 64) * 4 / esize;
 }
+#ifndef MLSTM_P1_ROWS
+#define MLSTM_P1_ROWS 256  // most state rows of a bf16 pass-1 tile
+#endif
 #ifndef MLSTM_P3_QRES
 #define MLSTM_P3_QRES 8
 #endif
@@ -680,18 +683,11 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
 #pragma unroll
         for (int jj = 0; jj < JPW; ++jj) {
           const int jt = C::jt_of(RG, jj);  // compile-time after unrolling
+          // intra-chunk part first, from zero: its MFMAs do not wait for the
+          // exchanged readout partials
           f32x4 o_acc[CT];
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            f32x4 a = acc[jt][ct];
-            if constexpr (XCH) a += sX[((cg * NJT + jt) * CT + ct) * 64 + lane];
-            o_acc[ct] = a;
-          }
-          const int j = jt * 16 + lr;
-          const float rs = sRS[j];
-          const float rs_state = rs * exp2_fast(sig);
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) o_acc[ct] *= rs_state;
+          for (int ct = 0; ct < CT; ++ct) o_acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kb = 0; kb < NKL; ++kb) {
             if (kb * K <= jt * 16 + 15) {
@@ -699,6 +695,15 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
 #pragma unroll
               for (int ct = 0; ct < CT; ++ct) o_acc[ct] = M::mma(vf[ct][kb], pf, o_acc[ct]);
             }
+          }
+          const int j = jt * 16 + lr;
+          const float rs = sRS[j];
+          const float rs_state = rs * exp2_fast(sig);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            f32x4 a = acc[jt][ct];
+            if constexpr (XCH) a += sX[((cg * NJT + jt) * CT + ct) * 64 + lane];
+            o_acc[ct] += rs_state * a;
           }
           float inv;
           if constexpr (RET) {
@@ -734,24 +739,43 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
       else phase_c(std::integral_constant<int, 1>{});
     }
 
+    // The update's B operands, w (x) V^T with w scaled by 2^-sig, are formed
+    // after the next chunk's staging loads and before the update, so that
+    // their LDS reads and VALU work do not sit between the update's K^T reads
+    // and its MFMAs.  The register scale sig is decided first: when it would
+    // drop below -64 the state is rescaled to sig = 0 before the update.
+    const float la = sAlphab[pb];
+    const float sig_new = sig + la;
+    const bool rescale = sig_new < -64.f;  // wave-uniform, rare
     if (more) {
       store_q();
       load_kv(c + 1);
     }
+    frag wv[CT][NKL];
+    if (need_update) {
+      const float wscale = exp2_fast(rescale ? 0.f : -sig_new);
+#pragma unroll
+      for (int kb = 0; kb < NKL; ++kb) {
+        float wls[KL];
+#pragma unroll
+        for (int e = 0; e < KL; ++e) wls[e] = sW[kb * K + krow<T>(lg, e)] * wscale;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) wv[ct][kb] = scale_frag(vf[ct][kb], wls);
+      }
+    }
     // ------------------------------------------------------- state update
     if (need_update) {
-      const float la = sAlphab[pb];
       const float alpha = exp2_fast(la);
-      sig += la;
-      if (sig < -64.f) {  // wave-uniform: rescale the registers, rarely
-        const float f = exp2_fast(sig);
+      if (rescale) {
+        const float f = exp2_fast(sig_new);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) st[nt][ct] *= f;
         sig = 0.f;
+      } else {
+        sig = sig_new;
       }
-      const float wscale = exp2_fast(-sig);
       // n~ gets sum_l w_l k_l.  With one memory block the K^T fragments of the
       // update carry every feature of k: each is summed by one wave (tile nt
       // goes to column group nt % 4).  With several blocks a work-group's waves
@@ -759,18 +783,12 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
       constexpr bool NFRAG = !RET && NB == 1;
 #pragma unroll
       for (int kb = 0; kb < NKL; ++kb) {
-        float wls[KL];
-#pragma unroll
-        for (int e = 0; e < KL; ++e) wls[e] = sW[kb * K + krow<T>(lg, e)] * wscale;
-        frag wv[CT];
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) wv[ct] = scale_frag(vf[ct][kb], wls);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const int kc = BF ? kcol + (nt >> 1) * 32 + (nt & 1) * 4 : kcol + perm_row<T>(nt, lr);
           const frag ka = frag_rows(sK, KST, kb * K, lg, lr, kc);
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) st[nt][ct] = M::mma(ka, wv[ct], st[nt][ct]);
+          for (int ct = 0; ct < CT; ++ct) st[nt][ct] = M::mma(ka, wv[ct][kb], st[nt][ct]);
           if ((nt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -1001,8 +1019,9 @@ __global__ __launch_bounds__(256) void superchunk_gate_kernel(ChunkParams p, int
 // end of the buffer (zero).  Both MFMA operands come from transposing LDS
 // reads; the K^T fragments are multiplied by w_t in registers (w of the whole
 // superchunk sits in LDS), which is also where dn is summed.
-template <typename T, int TR, int TC, int KS>
+template <typename T, int TR, int TC, int KS, int NWP>
 struct LocalCfg {
+  static constexpr int NTH = 64 * NWP;  // threads per work-group
   static constexpr int ES = (int)sizeof(T);
   static constexpr int VE = 16 / ES;
   // row strides: residue 8 + 16i dwords (a 128-wide bf16 row pads to
@@ -1014,14 +1033,15 @@ struct LocalCfg {
   static constexpr int NIK = (KS * RK * ES + 1023) / 1024;  // load instructions per K region
   static constexpr int NIV = (KS * RV * ES + 1023) / 1024;
   static constexpr int NI = NIK + NIV;
-  static constexpr int JA = (NI + 3) / 4;  // instructions per wave (every wave issues JA)
+  static constexpr int JA = (NI + NWP - 1) / NWP;  // instructions per wave (every wave issues JA)
   static constexpr int STAGE = NI * 1024;  // bytes per stage: K region, then V region
-  static constexpr int WR = TR >= 64 ? 4 : TR / 16;  // waves along rows
-  static constexpr int WCW = 4 / WR;                  // waves along columns
+  static constexpr int WR = TR >= 16 * NWP ? NWP : TR / 16;  // waves along rows
+  static constexpr int WCW = NWP / WR;                         // waves along columns
   static constexpr int MT = TR / WR / 16;             // 16-row tiles per wave
   static constexpr int NTc = TC / WCW / 16;           // 16-column tiles per wave
   static constexpr int GLMAX = 1024;                  // superchunk tokens (w in LDS)
-  static_assert(TR % (16 * WR) == 0 && TC % (16 * WCW) == 0 && WR * WCW == 4, "tile");
+  static_assert(TR % (16 * WR) == 0 && TC % (16 * WCW) == 0 && WR * WCW == NWP, "tile");
+  static_assert(GLMAX % NTH == 0, "w staging");
   static_assert((RK * ES) % 16 == 0 && (RV * ES) % 16 == 0, "rows of whole 16-byte units");
 };
 
@@ -1044,10 +1064,11 @@ __device__ __forceinline__ void lds_barrier() {
 // fragment times per-k weights, rounded back to bf16 in pairs
 __device__ __forceinline__ bf16x8 scale_frag8(bf16x8 x, const float (&w)[8]) { return scale_frag(x, w); }
 
-template <typename T, int DQK, int NB, int TR, int TC, int L, bool RET>
-__global__ __launch_bounds__(256) void local_state_kernel(ChunkParams p) {
+template <typename T, int DQK, int NB, int TR, int TC, int L, bool RET, int NWP>
+__global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
   constexpr int KS = sizeof(T) == 2 ? 32 : 16;
-  using C = LocalCfg<T, TR, TC, KS>;
+  using C = LocalCfg<T, TR, TC, KS, NWP>;
+  constexpr int NTH = C::NTH;
   using M = Mma<T>;
   typedef typename M::frag frag;
   constexpr int K = M::K, KL = M::KL, RK = C::RK, RV = C::RV, VE = C::VE;
@@ -1106,7 +1127,7 @@ __global__ __launch_bounds__(256) void local_state_kernel(ChunkParams p) {
   unsigned voff[JA];
 #pragma unroll
   for (int j = 0; j < JA; ++j) {
-    const int i = w + 4 * j;
+    const int i = w + NWP * j;
     voff[j] = 0xFFFFFFF0u;
     if (i < C::NIK) {
       const int unit = i * 64 + lane, row = unit / C::UK, cu = unit % C::UK;
@@ -1126,8 +1147,8 @@ __global__ __launch_bounds__(256) void local_state_kernel(ChunkParams p) {
     const int sv = __builtin_amdgcn_readfirstlane((int)(t0 * DV * ES));
 #pragma unroll
     for (int j = 0; j < JA; ++j) {
-      const int i0 = w + 4 * j;  // wave-uniform
-      const int i = i0 < C::NI ? i0 : i0 - 4;
+      const int i0 = w + NWP * j;  // wave-uniform
+      const int i = i0 < C::NI ? i0 : i0 - NWP;
       const bool isk = i < C::NIK;
       dma16_to_lds(isk ? rk : rv, st + i * 1024, voff[j], isk ? sk : sv);
     }
@@ -1144,10 +1165,10 @@ __global__ __launch_bounds__(256) void local_state_kernel(ChunkParams p) {
     // w loads are issued before the ring loads, so waiting for them does not
     // wait for the ring
     const float* wsrc = p.ws_w + (size_t)bh * T_ + tb;
-    float wv[C::GLMAX / 256];
+    float wv[C::GLMAX / NTH];
 #pragma unroll
-    for (int u = 0; u < C::GLMAX / 256; ++u) {
-      const int t = tid + 256 * u;
+    for (int u = 0; u < C::GLMAX / NTH; ++u) {
+      const int t = tid + NTH * u;
       wv[u] = t < GL ? wsrc[t] : 0.f;
     }
     issue(0, I0{});
@@ -1155,7 +1176,7 @@ __global__ __launch_bounds__(256) void local_state_kernel(ChunkParams p) {
     issue(2, I2{});
     issue(3, I3{});
 #pragma unroll
-    for (int u = 0; u < C::GLMAX / 256; ++u) sw[tid + 256 * u] = wv[u];
+    for (int u = 0; u < C::GLMAX / NTH; ++u) sw[tid + NTH * u] = wv[u];
   }
 
   // dn = sum_t w_t k_t by MFMA: the scaled K^T fragments times an all-ones B
@@ -1328,19 +1349,25 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
   const size_t CS = (size_t)DQK * p.DV / NB;
   hipLaunchKernelGGL((superchunk_gate_kernel<T, RET>), dim3((unsigned)(BH * p.NS)), dim3(256), 0, stream, p, L);
   if (p.NS > 1) {
-    // pass 1 tiles: TR rows x TC columns of one memory block
+    // pass 1 tiles: TR rows x TC columns of one memory block.  bf16 tiles
+    // take up to 256 rows (8 waves, one work-group per CU): every k-step's
+    // V rows then serve twice the MFMA work of a 128-row tile, which halves
+    // the redundant L2-to-LDS traffic that bounds this pass.
     constexpr int DQKB = DQK / NB;
+    constexpr int RCAP = sizeof(T) == 2 ? MLSTM_P1_ROWS : 64;
+    constexpr int TR = DQKB < RCAP ? DQKB : RCAP;
+    constexpr int NWP = TR >= 256 ? 8 : 4;
     constexpr int TCAP = sizeof(T) == 2 ? 128 : 64;
-    constexpr int TR = DQKB < TCAP ? DQKB : TCAP;
     const int DVB = p.DV / NB;
     const int TC = DVB % TCAP == 0 ? TCAP : DVB % 64 == 0 ? 64 : 32;
     const dim3 g1((unsigned)(BH * (p.NS - 1) * NB * (DQKB / TR) * (DVB / TC)));
+    const dim3 b1(64 * NWP);
     if (TC == TCAP)
-      hipLaunchKernelGGL((local_state_kernel<T, DQK, NB, TR, TCAP, L, RET>), g1, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((local_state_kernel<T, DQK, NB, TR, TCAP, L, RET, NWP>), g1, b1, 0, stream, p);
     else if (TC == 64)
-      hipLaunchKernelGGL((local_state_kernel<T, DQK, NB, TR, 64, L, RET>), g1, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((local_state_kernel<T, DQK, NB, TR, 64, L, RET, NWP>), g1, b1, 0, stream, p);
     else
-      hipLaunchKernelGGL((local_state_kernel<T, DQK, NB, TR, 32, L, RET>), g1, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((local_state_kernel<T, DQK, NB, TR, 32, L, RET, NWP>), g1, b1, 0, stream, p);
   }
   ScanParams s;
   s.NS = p.NS;
