@@ -1253,22 +1253,33 @@ __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
   lds_barrier();
   load_step(I0{}, F0);
   scale_step(0, F0);
-  auto body = [&](int c, auto bidx, StepFrags& cur, StepFrags& nxt) __attribute__((always_inline)) {
+  // body<true>: steps c and c + 1 both exist (no branch, so the next step's
+  // fragment reads can overlap this step's MFMAs); body<false>: the last
+  // group of 4, where either may be past the end.
+  auto body = [&](auto fullc, int c, auto bidx, StepFrags& cur, StepFrags& nxt) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(fullc)::value;
     constexpr int b = decltype(bidx)::value;
     using B1 = std::integral_constant<int, (b + 1) % 4>;
     wait_vmcnt<2 * NV>();
     lds_barrier();
     issue(c + 4, bidx);
-    if (c + 1 < NSTEP) load_step(B1{}, nxt);
-    if (c < NSTEP) mma_step(cur);
-    if (c + 1 < NSTEP) scale_step(c + 1, nxt);
+    if (FULL || c + 1 < NSTEP) load_step(B1{}, nxt);
+    if (FULL || c < NSTEP) mma_step(cur);
+    if (FULL || c + 1 < NSTEP) scale_step(c + 1, nxt);
   };
-  for (int c = 0; c < NSTEP; c += 4) {
-    body(c, I0{}, F0, F1);
-    body(c + 1, I1{}, F1, F0);
-    body(c + 2, I2{}, F0, F1);
-    body(c + 3, I3{}, F1, F0);
+  using Full = std::true_type;
+  using Tail = std::false_type;
+  int c = 0;
+  for (; c + 4 < NSTEP; c += 4) {
+    body(Full{}, c, I0{}, F0, F1);
+    body(Full{}, c + 1, I1{}, F1, F0);
+    body(Full{}, c + 2, I2{}, F0, F1);
+    body(Full{}, c + 3, I3{}, F1, F0);
   }
+  body(Tail{}, c, I0{}, F0, F1);
+  body(Tail{}, c + 1, I1{}, F1, F0);
+  body(Tail{}, c + 2, I2{}, F0, F1);
+  body(Tail{}, c + 3, I3{}, F1, F0);
   wait_vmcnt<0>();  // no load into the ring in flight past this point
 
   // ---- outputs: slot sc + 1 of the workspace holds superchunk sc's local state
