@@ -43,7 +43,7 @@ struct Plan {
   mlstm::ChunkVariant var;
   int L, NC, G, NS, nslices;
   size_t CS, nstate;
-  size_t off_scal, off_min, off_w, off_g, bytes;
+  size_t off_scal, off_min, off_g, bytes;
 };
 
 // Checks shared by the mLSTM and retention chunkwise entry points and the
@@ -92,8 +92,7 @@ int plan_chunkwise(int B, int H, int T, int dqk, int dv, int nb, int chunk, int 
   const size_t BH = (size_t)B * H;
   pl->off_scal = align256(BH * pl->NS * pl->nstate * sizeof(float));
   pl->off_min = pl->off_scal + align256(BH * pl->NS * 2 * sizeof(float));
-  pl->off_w = pl->off_min + align256(BH * pl->NS * sizeof(float));
-  pl->off_g = pl->off_w + (pl->NS > 1 ? align256(BH * (size_t)T * sizeof(float)) : 0);
+  pl->off_g = pl->off_min + align256(BH * pl->NS * sizeof(float));
   pl->bytes = pl->off_g + 3 * align256(BH * (size_t)pl->NC * chunk * sizeof(float));
   return MLSTM_OK;
 }
@@ -112,7 +111,6 @@ int launch(const Plan& pl, mlstm::ChunkParams& p, void* workspace, size_t worksp
   p.ws_state = reinterpret_cast<float*>(ws);
   p.ws_scal = reinterpret_cast<float*>(ws + pl.off_scal);
   p.ws_min = reinterpret_cast<float*>(ws + pl.off_min);
-  p.ws_w = reinterpret_cast<float*>(ws + pl.off_w);
   const size_t gsz = align256((size_t)p.B * p.H * pl.NC * pl.L * sizeof(float));
   p.ws_ga = reinterpret_cast<float*>(ws + pl.off_g);
   p.ws_gg = reinterpret_cast<float*>(ws + pl.off_g + gsz);

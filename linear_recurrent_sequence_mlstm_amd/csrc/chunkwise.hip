@@ -867,8 +867,23 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   }
 }
 
-// Gate kernel (superchunk_gate_kernel), one work-group of 4 waves per
-// (batch*head, superchunk).  For every token, in base-2 logs:
+// s_waitcnt with only a vmcnt limit (gfx9 encoding, expcnt and lgkmcnt left
+// at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// LDS accesses of this wave done, then a work-group barrier; the empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Gates, per (batch*head, superchunk).  For every token, in base-2 logs:
 //   chunk-local, for pass 3 (chunks of L tokens, index j):
 //     b_j = sum_{r<=j} log2 sigmoid(f_r),  a_j = log2(i_j) - b_j,
 //     g_j = max_{r<=j} a_r
@@ -877,8 +892,13 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
 //     and amax = max_t a'_t; the total log2 decay A = b'_end and the log2
 //     scale mu = b'_end + amax of the superchunk's local state (the stabiliser
 //     the token recurrence reaches from m = -inf).
-// Tokens past T count as f = 1, i = 0.  The waves take 64-token groups in
-// turn and scan them with DPP; the group totals meet in LDS.
+// Tokens past T count as f = 1, i = 0.  The waves of a work-group take
+// 64-token groups in turn and scan them with DPP; the group totals meet in
+// LDS.  With several superchunks this runs inside pass 1: extra work-groups
+// write the chunk-local arrays and the scan scalars, and every state tile's
+// work-group computes w_t of its own superchunk (a few KB of gate inputs,
+// read by each tile) while its first k-steps are in flight.  With one
+// superchunk a stand-alone kernel writes the chunk-local arrays.
 
 // inclusive scans over lanes in segments of SEG = 16, 32 or 64 lanes: row
 // shifts inside rows of 16, then row broadcasts.  update_dpp with bound_ctrl
@@ -908,44 +928,56 @@ __device__ __forceinline__ float seg_scan_max(float x, int seg) {
   return x;
 }
 
-template <typename T, bool RET>
-__global__ __launch_bounds__(256) void superchunk_gate_kernel(ChunkParams p, int L) {
-  constexpr int GPW = 4;  // 64-token groups per wave, at most (superchunks of <= 1024 tokens)
-  __shared__ float stot[4 * GPW];
-  __shared__ float smax[4];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int BH = p.B * p.H, T_ = p.T;
-  const int bh = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % BH));
-  const int sc = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / BH));
-  const int hd = bh % p.H;
-  const int GL = p.G * L, tb = sc * GL;
-  const int NCL = p.NC * L;                    // padded token count of a sequence
-  const int GLs = min(GL, NCL - tb);           // tokens of this superchunk (last may be short)
-  const int NG = (GLs + 63) / 64;
-  const bool local = sc < p.NS - 1;            // pass 1 needs this superchunk
+// Gate inputs of one superchunk for wave w of NWG: 64-token groups w, w + NWG, ...
+template <int NWG>
+struct GateRegs {
+  static constexpr int GPW = 16 / NWG;  // superchunks of at most 1024 tokens
+  float gi[GPW], gf[GPW];
+};
+
+template <typename T, bool RET, int NWG>
+__device__ __forceinline__ void gate_loads(const ChunkParams& p, int L, int bh, int sc, int w, int lane,
+                                           GateRegs<NWG>& r) {
   constexpr unsigned ES = sizeof(T);
+  const int T_ = p.T, tb = sc * p.G * L;
   const auto ri = make_rsrc(RET ? nullptr : static_cast<const T*>(p.i_pre) + (size_t)bh * T_,
                             RET ? 0u : (unsigned)T_ * ES);
   const auto rf = make_rsrc(RET ? nullptr : static_cast<const T*>(p.f_pre) + (size_t)bh * T_,
                             RET ? 0u : (unsigned)T_ * ES);
+#pragma unroll
+  for (int k = 0; k < GateRegs<NWG>::GPW; ++k) {
+    const unsigned t = (unsigned)(tb + (w + NWG * k) * 64 + lane);
+    r.gi[k] = r.gf[k] = 0.f;
+    if constexpr (!RET) {
+      r.gi[k] = bload1<T>(ri, t * ES);
+      r.gf[k] = bload1<T>(rf, t * ES);
+    }
+  }
+}
+
+// From the loaded gates of superchunk sc (all NWG waves of the work-group
+// take part; LDS-only barriers inside).  WRITE: store the chunk-local logs
+// for pass 3 and, for superchunks but the last, the scan scalars.  WANT_W:
+// the superchunk weights w_t into sw (LDS, 1024 floats).  stot: 16 floats,
+// smax: NWG floats of LDS.
+template <typename T, bool RET, int NWG, bool WRITE, bool WANT_W>
+__device__ __forceinline__ void gate_compute(const ChunkParams& p, int L, int bh, int sc, int w, int lane, int tid,
+                                             const GateRegs<NWG>& r, float* sw, float* stot, float* smax) {
+  constexpr int GPW = GateRegs<NWG>::GPW;
+  const int T_ = p.T, hd = bh % p.H;
+  const int GL = p.G * L, tb = sc * GL;
+  const int NCL = p.NC * L;           // padded token count of a sequence
+  const int GLs = min(GL, NCL - tb);  // tokens of this superchunk (last may be short)
+  const int NG = (GLs + 63) / 64;
+  const bool local = sc < p.NS - 1;   // pass 1 needs this superchunk
   float ret_lg2 = 0.f;
   if constexpr (RET) ret_lg2 = log2f(p.ret_gamma ? p.ret_gamma[hd] : 1.f - exp2f(-5.f - (float)hd));
 
-  float gi[GPW], gf[GPW], bl[GPW], li[GPW];
-#pragma unroll
-  for (int k = 0; k < GPW; ++k) {
-    const unsigned t = (unsigned)(tb + (w + 4 * k) * 64 + lane);
-    gi[k] = gf[k] = 0.f;
-    if constexpr (!RET) {
-      gi[k] = bload1<T>(ri, t * ES);
-      gf[k] = bload1<T>(rf, t * ES);
-    }
-  }
+  float bl[GPW], li[GPW];
   const size_t gbase = (size_t)bh * NCL + tb;
 #pragma unroll
   for (int k = 0; k < GPW; ++k) {
-    const int g = w + 4 * k;
+    const int g = w + NWG * k;
     const int tl = g * 64 + lane;  // token within the superchunk
     const bool valid = g < NG && tl < GLs && tb + tl < T_;
     float lf2;
@@ -953,28 +985,30 @@ __global__ __launch_bounds__(256) void superchunk_gate_kernel(ChunkParams p, int
       lf2 = valid ? ret_lg2 : 0.f;
       li[k] = valid ? 0.f : -INFINITY;
     } else {
-      lf2 = valid ? log2_sigmoid(gf[k]) : 0.f;
-      li[k] = valid ? gi[k] * kLog2e : -INFINITY;
+      lf2 = valid ? log2_sigmoid(r.gf[k]) : 0.f;
+      li[k] = valid ? r.gi[k] * kLog2e : -INFINITY;
     }
-    // chunk-local values for pass 3 (a chunk never straddles a 64-token group)
-    const float bc = seg_scan_sum(lf2, L);
-    const float ac = li[k] - bc;
-    const float gc = seg_scan_max(ac, L);
-    if (g < NG && tl < GLs) {
-      p.ws_ga[gbase + tl] = ac;
-      p.ws_gg[gbase + tl] = gc;
-      p.ws_gb[gbase + tl] = bc;
+    if constexpr (WRITE) {
+      // chunk-local values for pass 3 (a chunk never straddles a 64-token group)
+      const float bc = seg_scan_sum(lf2, L);
+      const float ac = li[k] - bc;
+      const float gc = seg_scan_max(ac, L);
+      if (g < NG && tl < GLs) {
+        p.ws_ga[gbase + tl] = ac;
+        p.ws_gg[gbase + tl] = gc;
+        p.ws_gb[gbase + tl] = bc;
+      }
     }
     bl[k] = seg_scan_sum(lf2, 64);
     if (g < NG && lane == 63) stot[g] = bl[k];
   }
   if (!local) return;  // work-group-uniform
-  __syncthreads();
+  lds_barrier();
   float amax = -INFINITY, carry = 0.f;
   int gdone = 0;
 #pragma unroll
   for (int k = 0; k < GPW; ++k) {
-    const int g = w + 4 * k;
+    const int g = w + NWG * k;
     if (g < NG) {
       for (; gdone < g; ++gdone) carry += stot[gdone];
       const float a = li[k] - (carry + bl[k]);
@@ -985,21 +1019,40 @@ __global__ __launch_bounds__(256) void superchunk_gate_kernel(ChunkParams p, int
 #pragma unroll
   for (int d = 32; d > 0; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 64));
   if (lane == 0) smax[w] = amax;
-  __syncthreads();
-  amax = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
-  float* wout = p.ws_w + (size_t)bh * T_ + tb;
+  lds_barrier();
+  amax = smax[0];
 #pragma unroll
-  for (int k = 0; k < GPW; ++k) {
-    const int g = w + 4 * k;
-    const int tl = g * 64 + lane;
-    if (g < NG && tl < GL) wout[tl] = exp2_fast(bl[k] - amax);
+  for (int i = 1; i < NWG; ++i) amax = fmaxf(amax, smax[i]);
+  if constexpr (WANT_W) {
+#pragma unroll
+    for (int k = 0; k < GPW; ++k) {
+      const int g = w + NWG * k;
+      const int tl = g * 64 + lane;  // < 1024
+      sw[tl] = (g < NG && tl < GL) ? exp2_fast(bl[k] - amax) : 0.f;
+    }
   }
-  if (tid == 0) {
+  if (WRITE && tid == 0) {
     float b_end = 0.f;
     for (int g = 0; g < NG; ++g) b_end += stot[g];
     p.ws_scal[((size_t)bh * p.NS + sc) * 2 + 0] = b_end;
     p.ws_scal[((size_t)bh * p.NS + sc) * 2 + 1] = b_end + amax;
   }
+}
+
+// Stand-alone gate pass for a plan with one superchunk (no pass 1): one
+// work-group of 4 waves per (batch*head) writes the chunk-local logs.
+template <typename T, bool RET>
+__global__ __launch_bounds__(256) void superchunk_gate_kernel(ChunkParams p, int L) {
+  __shared__ float stot[16];
+  __shared__ float smax[4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int BH = p.B * p.H;
+  const int bh = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % BH));
+  const int sc = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / BH));
+  GateRegs<4> r;
+  gate_loads<T, RET, 4>(p, L, bh, sc, w, lane, r);
+  gate_compute<T, RET, 4, true, false>(p, L, bh, sc, w, lane, tid, r, nullptr, stot, smax);
 }
 
 // Pass 1b (local_state_kernel): the local end state of every superchunk but
@@ -1008,9 +1061,9 @@ __global__ __launch_bounds__(256) void superchunk_gate_kernel(ChunkParams p, int
 // Nothing chains from chunk to chunk, so this is one dense product (w.K)^T V
 // per superchunk and state tile.
 //
-// Work-group = 4 waves on a TR x TC tile of one memory block, WR x WCW waves
-// (4 x 1 when the tile has 64 or more rows: each wave owns TR/4 rows and all
-// TC columns).  K-steps of KS tokens run through a ring
+// Work-group = NWP waves (8 for 256-row tiles, else 4) on a TR x TC tile of
+// one memory block, WR x WCW waves (NWP x 1 when the tile has 16 NWP or more
+// rows: each wave owns TR/NWP rows and all TC columns).  K-steps of KS tokens run through a ring
 // of 4 LDS stages filled by direct global-to-LDS buffer loads issued 3 steps
 // ahead, so no staging registers hold data in flight.  A stage holds KS token
 // rows of K and of V, row-major with padded rows; one load instruction fills
@@ -1018,7 +1071,7 @@ __global__ __launch_bounds__(256) void superchunk_gate_kernel(ChunkParams p, int
 // unit of the padded tile that lands in its slot, and pad slots read past the
 // end of the buffer (zero).  Both MFMA operands come from transposing LDS
 // reads; the K^T fragments are multiplied by w_t in registers (w of the whole
-// superchunk sits in LDS), which is also where dn is summed.
+// superchunk sits in LDS), and dn comes from the same scaled fragments.
 template <typename T, int TR, int TC, int KS, int NWP>
 struct LocalCfg {
   static constexpr int NTH = 64 * NWP;  // threads per work-group
@@ -1045,22 +1098,6 @@ struct LocalCfg {
   static_assert((RK * ES) % 16 == 0 && (RV * ES) % 16 == 0, "rows of whole 16-byte units");
 };
 
-// s_waitcnt with only a vmcnt limit (gfx9 encoding, expcnt and lgkmcnt left
-// at their no-wait maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-// LDS accesses of this wave done, then a work-group barrier; the empty asm
-// statements keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // fragment times per-k weights, rounded back to bf16 in pairs
 __device__ __forceinline__ bf16x8 scale_frag8(bf16x8 x, const float (&w)[8]) { return scale_frag(x, w); }
 
@@ -1085,6 +1122,8 @@ __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring2[C::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char ring3[C::STAGE];
   __shared__ __attribute__((aligned(16))) float sw[C::GLMAX];
+  __shared__ float stot[16];
+  __shared__ float smax[NWP];
   auto stage_ptr = [&](auto bidx) -> unsigned char* {
     constexpr int b = decltype(bidx)::value;
     if constexpr (b == 0) return ring0;
@@ -1101,6 +1140,18 @@ __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
   const int nct = DVB / TC;
   const int ntile = NB * NRT * nct;
   const int idx = blockIdx.x;
+  const int ncomp = BH * (p.NS - 1) * ntile;
+  if (idx >= ncomp) {
+    // gate work-groups, one per (batch*head, superchunk): the chunk-local
+    // logs of pass 3 and the scan scalars of pass 2
+    const int j = idx - ncomp;
+    const int gbh = __builtin_amdgcn_readfirstlane(j % BH);
+    const int gsc = __builtin_amdgcn_readfirstlane(j / BH);
+    GateRegs<NWP> r;
+    gate_loads<T, RET, NWP>(p, L, gbh, gsc, w, lane, r);
+    gate_compute<T, RET, NWP, true, false>(p, L, gbh, gsc, w, lane, tid, r, nullptr, stot, smax);
+    return;
+  }
   const int bh = __builtin_amdgcn_readfirstlane(idx % BH);
   const int tile = __builtin_amdgcn_readfirstlane((idx / BH) % ntile);
   const int sc = __builtin_amdgcn_readfirstlane((idx / BH) / ntile);
@@ -1156,27 +1207,21 @@ __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
   };
   constexpr int NV = JA;  // vm operations of one step of one wave
 
-  // the first four steps in flight, then w of the superchunk into LDS
+  // gate inputs, then the first four steps in flight, then w of the
+  // superchunk into LDS (the gate loads are issued first, so waiting for
+  // them does not wait for the ring)
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
   {
-    // w loads are issued before the ring loads, so waiting for them does not
-    // wait for the ring
-    const float* wsrc = p.ws_w + (size_t)bh * T_ + tb;
-    float wv[C::GLMAX / NTH];
-#pragma unroll
-    for (int u = 0; u < C::GLMAX / NTH; ++u) {
-      const int t = tid + NTH * u;
-      wv[u] = t < GL ? wsrc[t] : 0.f;
-    }
+    GateRegs<NWP> r;
+    gate_loads<T, RET, NWP>(p, L, bh, sc, w, lane, r);
     issue(0, I0{});
     issue(1, I1{});
     issue(2, I2{});
     issue(3, I3{});
-#pragma unroll
-    for (int u = 0; u < C::GLMAX / NTH; ++u) sw[tid + NTH * u] = wv[u];
+    gate_compute<T, RET, NWP, false, true>(p, L, bh, sc, w, lane, tid, r, sw, stot, smax);
   }
 
   // dn = sum_t w_t k_t by MFMA: the scaled K^T fragments times an all-ones B
@@ -1358,12 +1403,14 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
   constexpr int NTH = 64 * NCG * NRG;
   const int BH = p.B * p.H;
   const size_t CS = (size_t)DQK * p.DV / NB;
-  hipLaunchKernelGGL((superchunk_gate_kernel<T, RET>), dim3((unsigned)(BH * p.NS)), dim3(256), 0, stream, p, L);
-  if (p.NS > 1) {
+  if (p.NS == 1)
+    hipLaunchKernelGGL((superchunk_gate_kernel<T, RET>), dim3((unsigned)BH), dim3(256), 0, stream, p, L);
+  else {
     // pass 1 tiles: TR rows x TC columns of one memory block.  bf16 tiles
     // take up to 256 rows (8 waves, one work-group per CU): every k-step's
     // V rows then serve twice the MFMA work of a 128-row tile, which halves
-    // the redundant L2-to-LDS traffic that bounds this pass.
+    // the redundant L2-to-LDS traffic that bounds this pass.  The gate
+    // work-groups (one per batch*head and superchunk) follow the tiles.
     constexpr int DQKB = DQK / NB;
     constexpr int RCAP = sizeof(T) == 2 ? MLSTM_P1_ROWS : 64;
     constexpr int TR = DQKB < RCAP ? DQKB : RCAP;
@@ -1371,7 +1418,7 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
     constexpr int TCAP = sizeof(T) == 2 ? 128 : 64;
     const int DVB = p.DV / NB;
     const int TC = DVB % TCAP == 0 ? TCAP : DVB % 64 == 0 ? 64 : 32;
-    const dim3 g1((unsigned)(BH * (p.NS - 1) * NB * (DQKB / TR) * (DVB / TC)));
+    const dim3 g1((unsigned)(BH * (p.NS - 1) * NB * (DQKB / TR) * (DVB / TC) + BH * p.NS));
     const dim3 b1(64 * NWP);
     if (TC == TCAP)
       hipLaunchKernelGGL((local_state_kernel<T, DQK, NB, TR, TCAP, L, RET, NWP>), g1, b1, 0, stream, p);

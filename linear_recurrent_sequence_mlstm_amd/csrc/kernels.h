@@ -20,9 +20,8 @@ struct ChunkParams {
   float* ws_state;         // [B*H][NS][CS (+ d_qk)] superchunk start states
   float* ws_scal;          // [B*H][NS][2] (total log2 decay, local log2 scale)
   float* ws_min;           // [B*H][NS] stabiliser (log2) at superchunk starts
-  float* ws_w;             // [B*H][T] gate factors of the tokens in superchunks 0 .. NS-2
   float* ws_ga;            // [B*H][NC*L] chunk-local log2 gate sums a_j, prefix maxima g_j,
-  float* ws_gg;            //   forget-gate sums b_j (gate kernel -> pass 3)
+  float* ws_gg;            //   forget-gate sums b_j (gate pass -> pass 3)
   float* ws_gb;
   int has_init;
   const float* C0;
