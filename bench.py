@@ -14,6 +14,11 @@ The decode part (``decode``) runs the xLSTM-7B-shaped fused decode step:
 B=256, 8 heads, fp32 state [256,8,256,512] (1 GiB) updated in place, 128 steps
 with a fresh bf16 token per step; it reports achieved HBM GB/s.
 
+``variants`` times the other two chunkwise workloads through the same
+kernels (RetNet retention B=8 H=4 d=64 T=2048; xLSTM-v2 block-diagonal B=4
+H=4 d=64 nb=2 T=65536): tokens/s over the whole call and its algorithmic
+bytes against HBM.
+
 ``roofline`` is measured live: HIP events recorded by the library right before
 and after its main kernel (mlstm_set_profile_events) give that kernel's
 average duration over the timed steps; achieved = algorithmic bytes per
@@ -190,6 +195,85 @@ def bench_decode(torch, mlstm, workload, args, dev):
     return dict(B=B, H=H, dqk=dqk, dv=dv, S=S, wall=wall, step_ms=step_ms, bytes=byts, flops=flops)
 
 
+def retention_work(B, H, T, dk, dv, L=64):
+    """Algorithmic bytes and flops of one retention forward: q, k, v read
+    once, the output written once, the final fp32 state written once."""
+    byts = B * H * T * (2 * dk + 2 * dv) * 2 + B * H * dk * dv * 4
+    flops = B * H * T * (2 * L * (dk + dv) + 4 * dk * dv)
+    return byts, flops
+
+
+def bench_variants(torch, mlstm, workload, args, dev):
+    """The retention and block-diagonal workloads through the same chunkwise
+    kernels: fence-free events around every call (all launches of it) and
+    the library's events around its main kernel.  Enough distinct input sets
+    rotate that the inputs do not stay in the 256 MB Infinity Cache."""
+    out = []
+    L = mlstm.lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def timed(call, nsets, K, W):
+        for i in range(W):
+            call(i % nsets)
+        ev = _KernelEvents(K)
+        kev = _KernelEvents(K)
+        rec = ev.hip.hipEventRecord
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            L.mlstm_set_profile_events(*kev.pairs[i])
+            rec(ev.pairs[i][0], ev.ct.c_void_p(stream))
+            call(i % nsets)
+            rec(ev.pairs[i][1], ev.ct.c_void_p(stream))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        mlstm.set_profile_events()
+        r = dict(call_ms=ev.mean_ms(), kernel_ms=kev.mean_ms(), wall_ms=wall / K * 1e3)
+        ev.close()
+        kev.close()
+        return r
+
+    # RetNet multi-scale retention: B=8, H=4, d=64, T=2048 (34 MB per call)
+    q, k, v = workload("retnet_msr_T2048")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    sets = [tuple(t.to(dev) for t in (q, k, v)) for _ in range(8)]
+    outs = [torch.empty(B, H, T, dv, dtype=q.dtype, device=dev) for _ in sets]
+    S = torch.empty(B, H, dk, dv, device=dev)
+    ws = torch.empty(mlstm.retention_workspace_bytes(B, H, T, dk, dv), dtype=torch.uint8, device=dev)
+    r = timed(lambda i: mlstm.retention_chunkwise_fwd(*sets[i], out=outs[i], S_out=S, workspace=ws),
+              len(sets), args.variant_steps, args.variant_steps)
+    byts, flops = retention_work(B, H, T, dk, dv)
+    out.append(dict(workload="retnet_msr_T2048", B=B, H=H, T=T, d_k=dk, d_v=dv, **r, bytes=byts, flops=flops,
+                    tokens=B * T))
+    del sets, outs, S, ws
+
+    # xLSTM-v2 block-diagonal: B=4, H=4, d=64, nb=2, T=65536 (541 MB per call)
+    x = workload("xlstm2_blockdiag_T65536")
+    B, H, T, dqk = x.q.shape
+    dv = x.v.shape[-1]
+    sets = [x.to(dev), x.to(dev)]
+    hs = [torch.empty(B, H, T, dv, dtype=x.q.dtype, device=dev) for _ in sets]
+    nb = x.num_blocks
+    st = (torch.empty(B, H, nb, dqk // nb, dv // nb, device=dev), torch.empty(B, H, dqk, device=dev),
+          torch.empty(B, H, device=dev))
+    ws = torch.empty(mlstm.chunkwise_workspace_bytes(B, H, T, dqk, dv, nb), dtype=torch.uint8, device=dev)
+
+    def call(i):
+        g = sets[i]
+        mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, num_blocks=nb, h=hs[i],
+                            state_out=st, workspace=ws)
+
+    r = timed(call, len(sets), args.variant_steps, args.variant_steps)
+    byts, flops = prefill_work(B, H, T, dqk, dv)
+    # block-diagonal: the state and its products are nb times smaller
+    byts -= B * H * (dqk * dv - dqk * dv // nb) * 4
+    flops -= B * H * T * 4 * (dqk * dv - dqk * dv // nb)
+    out.append(dict(workload="xlstm2_blockdiag_T65536", B=B, H=H, T=T, d_qk=dqk, d_v=dv, num_blocks=nb, **r,
+                    bytes=byts, flops=flops, tokens=B * T))
+    return out
+
+
 def copy_calibration(torch, dev, nbytes=1 << 30, reps=3):
     """A plain device-to-device copy of known size (nbytes read, nbytes
     written per launch).  Its rocprofv3 FETCH_SIZE / WRITE_SIZE readings give
@@ -222,6 +306,20 @@ def cpu_baseline(x, sample_tokens):
                        "%.1f s" % (B, H, Ts, dt))
 
 
+def variant_line(v):
+    """One retention / block-diagonal record: throughput of the whole call
+    and the HBM and MFMA rooflines of its algorithmic work."""
+    s = v["call_ms"] * 1e-3
+    gbs = v["bytes"] / s / 1e9
+    keep = {k: v[k] for k in v if k not in ("call_ms", "kernel_ms", "wall_ms", "bytes", "flops", "tokens")}
+    return dict(keep, value=v["tokens"] / s, unit="tokens/s", ms_per_call=v["call_ms"],
+                wall_ms_per_call=v["wall_ms"], main_kernel_ms=v["kernel_ms"],
+                roofline=dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
+                              traffic=None, kernel="whole call (all launches)",
+                              mfma_frac=v["flops"] / s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                              algorithmic_bytes=v["bytes"], algorithmic_flops=v["flops"]))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,7 +328,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=("prefill", "decode", "copy"),
+    ap.add_argument("--variant-steps", type=int, default=100,
+                    help="timed calls of the retention and block-diagonal workloads (0: skip them)")
+    ap.add_argument("--only", choices=("prefill", "decode", "copy", "variants"),
                     help="run one leg alone and print its raw figures (for profiler runs)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -252,6 +352,8 @@ def main():
             r.pop("spec")
         elif args.only == "decode":
             r = bench_decode(torch, mlstm, workload, args, dev)
+        elif args.only == "variants":
+            r = dict(variants=bench_variants(torch, mlstm, workload, args, dev))
         else:
             r = copy_calibration(torch, dev)
         print(json.dumps(dict(leg=args.only, **r)))
@@ -262,6 +364,11 @@ def main():
     pf = bench_prefill(torch, mlstm, x, args, dev)
     print("bench: decode xlstm7b_decode_B256 steps=%d" % args.decode_steps, file=sys.stderr, flush=True)
     dc = bench_decode(torch, mlstm, workload, args, dev)
+    var = []
+    if args.variant_steps > 0:
+        print("bench: retention and block-diagonal workloads, %d calls each" % args.variant_steps,
+              file=sys.stderr, flush=True)
+        var = bench_variants(torch, mlstm, workload, args, dev)
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -314,6 +421,7 @@ def main():
             "steps": dc["S"],
             "roofline": droof,
         },
+        "variants": [variant_line(v) for v in var],
     }
     print(json.dumps(out))
 

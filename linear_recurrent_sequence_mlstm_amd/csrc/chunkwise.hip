@@ -1373,23 +1373,41 @@ __global__ __launch_bounds__(256) void superchunk_scan_kernel(ScanParams p) {
     S = make_float4(x[0], x[1], x[2], x[3]);
     *reinterpret_cast<float4*>(base + e0) = S;
   }
+  // Superchunks go in windows of SW: all local states and scalars of a
+  // window are loaded before any of its start states is stored (each into
+  // the slot its local state was read from), so the loads' latencies
+  // overlap instead of queueing behind the stores.
+  constexpr int SW = 8;
   float m = m0;
-  for (int sc = 1; sc < p.NS; ++sc) {
-    const float A = p.ws_scal[((size_t)bh * p.NS + sc - 1) * 2 + 0];
-    const float mu = p.ws_scal[((size_t)bh * p.NS + sc - 1) * 2 + 1];
-    const float mn = fmaxf(A + m, mu);
-    const float fa = exp2_fast(A + m - mn), fb = exp2_fast(mu - mn);
-    if (active) {
-      float4* ptr = reinterpret_cast<float4*>(base + (size_t)sc * NSTATE + e0);
-      const float4 d = *ptr;
-      S.x = fa * S.x + fb * d.x;
-      S.y = fa * S.y + fb * d.y;
-      S.z = fa * S.z + fb * d.z;
-      S.w = fa * S.w + fb * d.w;
-      *ptr = S;
+  for (int s0 = 1; s0 < p.NS; s0 += SW) {
+    float A[SW], mu[SW];
+    float4 d[SW];
+#pragma unroll
+    for (int j = 0; j < SW; ++j) {
+      const int sc = s0 + j;
+      A[j] = mu[j] = 0.f;
+      d[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (sc < p.NS) {
+        A[j] = p.ws_scal[((size_t)bh * p.NS + sc - 1) * 2 + 0];
+        mu[j] = p.ws_scal[((size_t)bh * p.NS + sc - 1) * 2 + 1];
+        if (active) d[j] = *reinterpret_cast<const float4*>(base + (size_t)sc * NSTATE + e0);
+      }
     }
-    m = mn;
-    if (writer) p.ws_min[(size_t)bh * p.NS + sc] = mn;
+#pragma unroll
+    for (int j = 0; j < SW; ++j) {
+      const int sc = s0 + j;
+      if (sc < p.NS) {
+        const float mn = fmaxf(A[j] + m, mu[j]);
+        const float fa = exp2_fast(A[j] + m - mn), fb = exp2_fast(mu[j] - mn);
+        S.x = fa * S.x + fb * d[j].x;
+        S.y = fa * S.y + fb * d[j].y;
+        S.z = fa * S.z + fb * d[j].z;
+        S.w = fa * S.w + fb * d[j].w;
+        if (active) *reinterpret_cast<float4*>(base + (size_t)sc * NSTATE + e0) = S;
+        m = mn;
+        if (writer) p.ws_min[(size_t)bh * p.NS + sc] = mn;
+      }
+    }
   }
 }
 
