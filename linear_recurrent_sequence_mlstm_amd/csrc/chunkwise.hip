@@ -157,8 +157,13 @@ struct ChunkCfg {
   // sQ is read with 16-byte row fragments only; sK also with transposing
   // reads (the update's K^T, 16-byte spaced 8-byte runs per row), whose
   // bank spread is best at residue 24
-  static constexpr int QS = DQK + lds_pad_res(DQK, (int)sizeof(T), MLSTM_P3_QRES);  // sQ
-  static constexpr int KST = DQK + lds_pad_res(DQK, (int)sizeof(T), MLSTM_P3_KRES);  // sK
+  // (heads narrower than 128 take the smallest padding of the same residue
+  // family instead: there the tuned residues would nearly double the row
+  // and halve the work-groups that fit on a CU)
+  static constexpr int QS = DQK + (DQK >= 128 ? lds_pad_res(DQK, (int)sizeof(T), MLSTM_P3_QRES)
+                                              : lds_row_pad(DQK, (int)sizeof(T)));  // sQ
+  static constexpr int KST = DQK + (DQK >= 128 ? lds_pad_res(DQK, (int)sizeof(T), MLSTM_P3_KRES)
+                                               : lds_row_pad(DQK, (int)sizeof(T)));  // sK
   static constexpr int VS = W + lds_row_pad(W, (int)sizeof(T));  // sV
   static constexpr int PS = L + 16 / (int)sizeof(T);  // sP
   // bf16 outputs are staged in LDS (sH, token-major) and written as whole
