@@ -14,10 +14,10 @@ The decode part (``decode``) runs the xLSTM-7B-shaped fused decode step:
 B=256, 8 heads, fp32 state [256,8,256,512] (1 GiB) updated in place, 128 steps
 with a fresh bf16 token per step; it reports achieved HBM GB/s.
 
-``variants`` times the other two chunkwise workloads through the same
-kernels (RetNet retention B=8 H=4 d=64 T=2048; xLSTM-v2 block-diagonal B=4
-H=4 d=64 nb=2 T=65536): tokens/s over the whole call and its algorithmic
-bytes against HBM.
+``variants`` times the other chunkwise workloads through the same kernels
+(RetNet retention B=8 H=4 d=64 T=2048; xLSTM-v2 block-diagonal B=4 H=4 d=64
+nb=2 T=65536) and the retention decode step on the RetNet shape: tokens/s
+per call and its algorithmic bytes against HBM.
 
 ``roofline`` is measured live: HIP events recorded by the library right before
 and after its main kernel (mlstm_set_profile_events) give that kernel's
@@ -212,25 +212,28 @@ def bench_variants(torch, mlstm, workload, args, dev):
     L = mlstm.lib()
     stream = torch.cuda.current_stream(dev).cuda_stream
 
-    def timed(call, nsets, K, W):
+    def timed(call, nsets, K, W, chunkwise=True):
+        # chunkwise calls also record the library's events around pass 3
         for i in range(W):
             call(i % nsets)
         ev = _KernelEvents(K)
-        kev = _KernelEvents(K)
+        kev = _KernelEvents(K) if chunkwise else None
         rec = ev.hip.hipEventRecord
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
-            L.mlstm_set_profile_events(*kev.pairs[i])
+            if kev:
+                L.mlstm_set_profile_events(*kev.pairs[i])
             rec(ev.pairs[i][0], ev.ct.c_void_p(stream))
             call(i % nsets)
             rec(ev.pairs[i][1], ev.ct.c_void_p(stream))
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         mlstm.set_profile_events()
-        r = dict(call_ms=ev.mean_ms(), kernel_ms=kev.mean_ms(), wall_ms=wall / K * 1e3)
+        r = dict(call_ms=ev.mean_ms(), kernel_ms=kev.mean_ms() if kev else ev.mean_ms(), wall_ms=wall / K * 1e3)
         ev.close()
-        kev.close()
+        if kev:
+            kev.close()
         return r
 
     # RetNet multi-scale retention: B=8, H=4, d=64, T=2048 (34 MB per call)
@@ -247,6 +250,19 @@ def bench_variants(torch, mlstm, workload, args, dev):
     out.append(dict(workload="retnet_msr_T2048", B=B, H=H, T=T, d_k=dk, d_v=dv, **r, bytes=byts, flops=flops,
                     tokens=B * T))
     del sets, outs, S, ws
+
+    # retention decode on the same workload: its first D tokens, one call
+    # of retention_step each, state updated in place
+    D = min(128, T)
+    q, k, v = workload("retnet_msr_T2048")
+    toks = [tuple(t[:, :, s].contiguous().to(dev) for t in (q, k, v)) for s in range(D)]
+    S = torch.zeros(B, H, dk, dv, device=dev)
+    o = torch.empty(B, H, dv, dtype=q.dtype, device=dev)
+    r = timed(lambda i: mlstm.retention_step(*toks[i], S, out=o), D, D, D, chunkwise=False)
+    byts = 2 * B * H * dk * dv * 4 + B * H * (2 * dk + 2 * dv) * 2
+    out.append(dict(workload="retnet_msr_decode_B8", B=B, H=H, d_k=dk, d_v=dv, steps=D, **r, bytes=byts,
+                    flops=B * H * 4 * dk * dv, tokens=B))
+    del toks, S, o
 
     # xLSTM-v2 block-diagonal: B=4, H=4, d=64, nb=2, T=65536 (541 MB per call)
     x = workload("xlstm2_blockdiag_T65536")

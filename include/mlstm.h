@@ -159,6 +159,23 @@ int retention_chunkwise_fwd(int B, int H, int T, int d_k, int d_v, int chunk,
                             float* S_out, void* out, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/*
+ * RetNet retention, one decode step on every (b, h), in the recurrent form of
+ * the "Edifice.Attention.RetNet" page ("Key Innovation: Retention
+ * Mechanism"; recurrent mode of "Triple Paradigm"):
+ *     S <- gamma_h S + k v^T     (IN PLACE),     out = S^T q
+ * (the readout uses the updated state, as one token of
+ * retention_chunkwise_fwd does).
+ *   q, k [B,H,d_k]; v, out [B,H,d_v] (dtype dt);
+ *   gamma [H] fp32, or NULL for gamma_h = 1 - 2^(-5-h), h = 0..H-1;
+ *   S [B,H,d_k,d_v] fp32, read and written.
+ * Requires d_v a multiple of 16 (any d_k >= 1); other shapes return
+ * MLSTM_E_UNSUPPORTED.  One kernel is enqueued.
+ */
+int retention_step(int B, int H, int d_k, int d_v, mlstm_dtype dt,
+                   const void* q, const void* k, const void* v,
+                   const float* gamma, float* S, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ _DT = {torch.float32: F32, torch.bfloat16: BF16}
 EXPORTS = ("mlstm_abi_version", "mlstm_last_error", "mlstm_set_profile_events",
            "mlstm_chunkwise_workspace_bytes",
            "mlstm_chunkwise_fwd", "mlstm_step", "retention_chunkwise_workspace_bytes",
-           "retention_chunkwise_fwd")
+           "retention_chunkwise_fwd", "retention_step")
 
 
 def library_path() -> str:
@@ -57,6 +57,8 @@ def lib():
     L.retention_chunkwise_workspace_bytes.restype = sz
     L.retention_chunkwise_fwd.argtypes = [i] * 7 + [vp] * 3 + [fp] * 3 + [vp, vp, sz, vp]
     L.retention_chunkwise_fwd.restype = i
+    L.retention_step.argtypes = [i] * 5 + [vp] * 3 + [fp] * 2 + [vp, vp]
+    L.retention_step.restype = i
     _lib = L
     return L
 
@@ -235,3 +237,25 @@ def retention_chunkwise_fwd(q, k, v, gamma=None, S0=None, chunk=64, return_state
                                    _ptr(out), _ptr(ws), ws.numel(), _stream(dev))
     _check(rc, "retention_chunkwise_fwd")
     return out, (S_out if return_state else None)
+
+
+def retention_step(q, k, v, S, gamma=None, out=None):
+    """retention_step: one token per (b,h); q,k [B,H,dk]; v [B,H,dv];
+    S [B,H,dk,dv] fp32 updated in place (S = gamma S + k v^T); gamma [H]
+    fp32 or None (1 - 2^(-5-h)).  Returns out = S^T q [B,H,dv]."""
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dt not in _DT:
+        raise TypeError("unsupported dtype %s" % dt)
+    _need(k, "k", (B, H, dk), dt, dev)
+    _need(v, "v", (B, H, dv), dt, dev)
+    _need(gamma, "gamma", (H,), torch.float32, dev)
+    _need(S, "S", (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty(B, H, dv, dtype=dt, device=dev)
+    _need(out, "out", (B, H, dv), dt, dev)
+    rc = lib().retention_step(B, H, dk, dv, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(S),
+                              _ptr(out), _stream(dev))
+    _check(rc, "retention_step")
+    return out

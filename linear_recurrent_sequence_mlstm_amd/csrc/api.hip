@@ -242,4 +242,29 @@ int mlstm_step(int B, int H, int d_qk, int d_v, int num_blocks, mlstm_dtype dt, 
   return ok();
 }
 
+int retention_step(int B, int H, int d_k, int d_v, mlstm_dtype dt, const void* q, const void* k, const void* v,
+                   const float* gamma, float* S, void* out, void* stream) {
+  if (dt != MLSTM_F32 && dt != MLSTM_BF16) return fail(MLSTM_E_DTYPE, "unknown dtype %d", dt);
+  if (B < 1 || H < 1 || d_k < 1 || d_v < 1) return fail(MLSTM_E_SHAPE, "sizes must be positive");
+  if ((long long)B * H >= (1LL << 24)) return fail(MLSTM_E_SHAPE, "B * H too large");
+  if (!mlstm::step_supported(d_k, d_v, 1))
+    return fail(MLSTM_E_UNSUPPORTED, "no retention step kernel for d_k=%d d_v=%d", d_k, d_v);
+  if (!q || !k || !v || !S || !out) return fail(MLSTM_E_NULL, "q, k, v, S and out are required");
+  mlstm::StepParams p{};
+  p.B = B;
+  p.H = H;
+  p.DQK = d_k;
+  p.DV = d_v;
+  p.NB = 1;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.C = S;
+  p.h = out;
+  p.gamma = gamma;
+  const hipError_t e = mlstm::launch_retention_step(dt, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLSTM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

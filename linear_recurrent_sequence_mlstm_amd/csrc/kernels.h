@@ -73,9 +73,12 @@ struct StepParams {
   float* n;
   float* m;
   void* h;
+  const float* gamma;  // retention: [H] decay, or null for 1 - 2^(-5-h)
 };
 
 hipError_t launch_step(int dtype, const StepParams& p, hipStream_t stream);
+// Retention decode: C is S [B,H,d_k,d_v]; q, k, v, h and gamma are read.
+hipError_t launch_retention_step(int dtype, const StepParams& p, hipStream_t stream);
 bool step_supported(int dqk, int dv, int nb);
 
 }  // namespace mlstm

@@ -11,6 +11,11 @@
 //   h   = o * (S~^T q) / max(|n~.q + bias 2^{-m'}|, 2^{-m'})
 // The readout uses the updated state.
 //
+// Retention decode (recurrent form of the "Edifice.Attention.RetNet" page,
+// "Key Innovation: Retention Mechanism", one step of its recurrent mode in
+// "Triple Paradigm"): the same kernel with f' = gamma_h, i' = 1 and no
+// normaliser, output gate or stabiliser:  S <- gamma_h S + k v^T, o = S^T q.
+//
 // Two launches.  step_kernel streams the matrix state: work-group (b*h,
 // slice) owns a slice of WS columns and all rows, so its readout columns are
 // complete and it writes h for them.  The updated normaliser enters only
@@ -32,8 +37,16 @@ namespace mlstm {
 struct StepGates {
   float mn2, fdec, iw;
 };
-template <typename T>
+template <typename T, bool RET = false>
 __device__ __forceinline__ StepGates step_gates(const StepParams& p, int bh) {
+  if constexpr (RET) {
+    const int hd = bh % p.H;
+    StepGates s;
+    s.mn2 = 0.f;
+    s.fdec = p.gamma ? p.gamma[hd] : 1.f - exp2f(-5.f - (float)hd);
+    s.iw = 1.f;
+    return s;
+  }
   const float lf2 = log2_sigmoid(to_f32(static_cast<const T*>(p.f_pre)[bh]));
   const float li2 = to_f32(static_cast<const T*>(p.i_pre)[bh]) * kLog2e;
   const float m2 = p.m[bh] * kLog2e;
@@ -44,7 +57,7 @@ __device__ __forceinline__ StepGates step_gates(const StepParams& p, int bh) {
   return s;
 }
 
-template <typename T, int RG>
+template <typename T, int RG, bool RET>
 __global__ __launch_bounds__(512) void step_kernel(StepParams p, int WS) {
   extern __shared__ float smem[];
   const int DQK = p.DQK, DV = p.DV, NB = p.NB;
@@ -75,25 +88,29 @@ __global__ __launch_bounds__(512) void step_kernel(StepParams p, int WS) {
     const int r = g + u * RG;
     if (r < DQKB) s[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (size_t)r * DVB));
   }
-  const StepGates gt = step_gates<T>(p, bh);
-  const float bias = p.bias ? p.bias[bh % p.H] : 0.f;
+  const StepGates gt = step_gates<T, RET>(p, bh);
+  const float bias = (!RET && p.bias) ? p.bias[bh % p.H] : 0.f;
   // q, k to LDS; n~.q and k.q over the head
   float nq = 0.f, kq = 0.f;
   for (int r = tid; r < DQK; r += nth) {
     const float qr = to_f32(q[r]), kr = to_f32(k[r]);
     sq[r] = qr;
     sk[r] = kr;
-    nq += p.n[(size_t)bh * DQK + r] * qr;
-    kq += kr * qr;
+    if constexpr (!RET) {
+      nq += p.n[(size_t)bh * DQK + r] * qr;
+      kq += kr * qr;
+    }
   }
+  if constexpr (!RET) {
 #pragma unroll
-  for (int d = 32; d > 0; d >>= 1) {
-    nq += __shfl_xor(nq, d, 64);
-    kq += __shfl_xor(kq, d, 64);
-  }
-  if (lane == 0) {
-    sred[tid >> 6] = nq;
-    sred[nth / 64 + (tid >> 6)] = kq;
+    for (int d = 32; d > 0; d >>= 1) {
+      nq += __shfl_xor(nq, d, 64);
+      kq += __shfl_xor(kq, d, 64);
+    }
+    if (lane == 0) {
+      sred[tid >> 6] = nq;
+      sred[nth / 64 + (tid >> 6)] = kq;
+    }
   }
   __syncthreads();
 
@@ -135,15 +152,20 @@ __global__ __launch_bounds__(512) void step_kernel(StepParams p, int WS) {
   }
   __syncthreads();
   if (g == 0) {
-    float n_q = 0.f, k_q = 0.f;
-    for (int i = 0; i < nth / 64; ++i) {
-      n_q += sred[i];
-      k_q += sred[nth / 64 + i];
-    }
     if constexpr (RG > 1) {
       for (int gg = 1; gg < RG; ++gg)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] += sacc[gg * WS + t * 4 + i];
+    }
+    if constexpr (RET) {
+      store4(static_cast<T*>(p.h) + (size_t)bh * DV + col, from_f32<T>(acc[0]), from_f32<T>(acc[1]),
+             from_f32<T>(acc[2]), from_f32<T>(acc[3]));
+      return;
+    }
+    float n_q = 0.f, k_q = 0.f;
+    for (int i = 0; i < nth / 64; ++i) {
+      n_q += sred[i];
+      k_q += sred[nth / 64 + i];
     }
     const float cl2 = exp2_fast(-gt.mn2);
     const float den = fdec * n_q + gt.iw * k_q + bias * cl2;  // n~' . q + bias 2^{-m'}
@@ -212,19 +234,20 @@ bool step_supported(int dqk, int dv, int nb) {
   return pick_rg(pick_ws(dv)) > 0;
 }
 
-template <typename T>
+template <typename T, bool RET>
 static hipError_t launch_rg(const StepParams& p, int ws, int rg, hipStream_t stream) {
   const int tpc = ws / 4;
   const dim3 grid((unsigned)(p.B * p.H * (p.DV / ws)));
   const dim3 block((unsigned)(tpc * rg));
   const size_t smem = ((size_t)2 * p.DQK + (size_t)rg * ws + 2 * 16) * sizeof(float);
   switch (rg) {
-    case 1: hipLaunchKernelGGL((step_kernel<T, 1>), grid, block, smem, stream, p, ws); break;
-    case 2: hipLaunchKernelGGL((step_kernel<T, 2>), grid, block, smem, stream, p, ws); break;
-    case 4: hipLaunchKernelGGL((step_kernel<T, 4>), grid, block, smem, stream, p, ws); break;
-    case 8: hipLaunchKernelGGL((step_kernel<T, 8>), grid, block, smem, stream, p, ws); break;
-    default: hipLaunchKernelGGL((step_kernel<T, 16>), grid, block, smem, stream, p, ws); break;
+    case 1: hipLaunchKernelGGL((step_kernel<T, 1, RET>), grid, block, smem, stream, p, ws); break;
+    case 2: hipLaunchKernelGGL((step_kernel<T, 2, RET>), grid, block, smem, stream, p, ws); break;
+    case 4: hipLaunchKernelGGL((step_kernel<T, 4, RET>), grid, block, smem, stream, p, ws); break;
+    case 8: hipLaunchKernelGGL((step_kernel<T, 8, RET>), grid, block, smem, stream, p, ws); break;
+    default: hipLaunchKernelGGL((step_kernel<T, 16, RET>), grid, block, smem, stream, p, ws); break;
   }
+  if constexpr (RET) return hipGetLastError();  // no normaliser or stabiliser
   const int rpb = p.DQK >= 256 ? 1 : 256 / p.DQK;
   const int nwg = (p.B * p.H + rpb - 1) / rpb;
   hipLaunchKernelGGL((step_norm_kernel<T>), dim3((unsigned)nwg), dim3(256), 0, stream, p, rpb);
@@ -234,7 +257,13 @@ static hipError_t launch_rg(const StepParams& p, int ws, int rg, hipStream_t str
 hipError_t launch_step(int dtype, const StepParams& p, hipStream_t stream) {
   const int ws = pick_ws(p.DV);
   const int rg = pick_rg(ws);
-  return dtype == 1 ? launch_rg<__bf16>(p, ws, rg, stream) : launch_rg<float>(p, ws, rg, stream);
+  return dtype == 1 ? launch_rg<__bf16, false>(p, ws, rg, stream) : launch_rg<float, false>(p, ws, rg, stream);
+}
+
+hipError_t launch_retention_step(int dtype, const StepParams& p, hipStream_t stream) {
+  const int ws = pick_ws(p.DV);
+  const int rg = pick_rg(ws);
+  return dtype == 1 ? launch_rg<__bf16, true>(p, ws, rg, stream) : launch_rg<float, true>(p, ws, rg, stream);
 }
 
 }  // namespace mlstm

@@ -73,6 +73,17 @@ def test_step_validation():
     assert L.mlstm_step(1, 1, 64, 64, 1, 1, *([None] * 10), BOGUS, None) == E_NULL
 
 
+def test_retention_step_validation():
+    L = _lib.lib()
+    assert L.retention_step(0, 1, 64, 64, 1, BOGUS, BOGUS, BOGUS, None, BOGUS, BOGUS, None) == E_SHAPE
+    assert L.retention_step(1, 1, 64, 64, 9, BOGUS, BOGUS, BOGUS, None, BOGUS, BOGUS, None) == E_DTYPE
+    for dv in (8, 24, 100):  # d_v must be a multiple of 16
+        assert L.retention_step(1, 1, 64, dv, 1, BOGUS, BOGUS, BOGUS, None, BOGUS, BOGUS, None) == E_UNSUPPORTED
+    assert L.retention_step(1, 1, 64, 64, 1, BOGUS, None, BOGUS, None, BOGUS, BOGUS, None) == E_NULL
+    assert L.retention_step(1, 1, 64, 64, 1, BOGUS, BOGUS, BOGUS, None, None, BOGUS, None) == E_NULL
+    assert _lib.last_error() != ""
+
+
 def test_retention_validation():
     L = _lib.lib()
     p = [BOGUS] * 3 + [None] * 3

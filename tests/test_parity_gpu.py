@@ -192,6 +192,48 @@ def test_retention_custom_gamma_fp32(gpu):
     assert slice_err(cpu(S), ref_S) < TOL[torch.float32]
 
 
+@pytest.mark.parametrize("B,H,dk,dv,dtype,custom_gamma", [
+    (8, 4, 64, 64, "bf16", False), (2, 3, 128, 256, "f32", True), (3, 2, 256, 512, "bf16", True),
+])
+def test_retention_step(gpu, B, H, dk, dv, dtype, custom_gamma):
+    """T decode steps from a random state, token by token through
+    retention_step, against the oracle's retention recurrence over the same
+    T tokens: every step's output and the final state."""
+    T = 40
+    q, k, v = retention_inputs(B, H, T, dk, dv, seed=21, dtype=dtype)
+    S0 = torch.randn(B, H, dk, dv, generator=torch.Generator().manual_seed(5)) * 0.1
+    gamma = torch.linspace(0.6, 0.99, H) if custom_gamma else None
+    S = S0.to(gpu).contiguous()
+    g = None if gamma is None else gamma.to(gpu)
+    outs = []
+    for t in range(T):
+        o = mlstm.retention_step(q[:, :, t].contiguous().to(gpu), k[:, :, t].contiguous().to(gpu),
+                                 v[:, :, t].contiguous().to(gpu), S, gamma=g)
+        outs.append(cpu(o))
+    torch.cuda.synchronize()
+    ref_out, ref_S = oracle.retention_fwd(q, k, v, gamma=gamma, S0=S0)
+    got = np.stack(outs, axis=2)
+    tol = TOL[torch.bfloat16 if dtype == "bf16" else torch.float32]
+    assert slice_err(got, ref_out) < tol
+    assert slice_err(cpu(S), ref_S) < tol
+
+
+def test_retention_step_matches_chunkwise(gpu):
+    """Prefill by retention_chunkwise_fwd, then steps, equals one chunkwise
+    call over the whole sequence (the state hand-over of the two paths)."""
+    B, H, T, T1, d = 2, 4, 100, 70, 64
+    q, k, v = (t.to(gpu) for t in retention_inputs(B, H, T, d, d, seed=8))
+    out_all, S_all = mlstm.retention_chunkwise_fwd(q, k, v)
+    _, S = mlstm.retention_chunkwise_fwd(q[:, :, :T1].contiguous(), k[:, :, :T1].contiguous(),
+                                         v[:, :, :T1].contiguous())
+    outs = [mlstm.retention_step(q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous(), S)
+            for t in range(T1, T)]
+    torch.cuda.synchronize()
+    got = np.stack([cpu(o) for o in outs], axis=2)
+    assert slice_err(got, cpu(out_all[:, :, T1:])) < TOL[torch.bfloat16]
+    assert slice_err(cpu(S), cpu(S_all)) < TOL[torch.bfloat16]
+
+
 # ------------------------------------------------------------ decode step
 @pytest.mark.parametrize("B,H,dqk,dv,nb,with_o,bias", [
     (3, 2, 64, 64, 1, True, "uniform"), (2, 4, 64, 64, 2, False, "uniform"),
