@@ -16,8 +16,9 @@ with a fresh bf16 token per step; it reports achieved HBM GB/s.
 
 ``variants`` times the other chunkwise workloads through the same kernels
 (RetNet retention B=8 H=4 d=64 T=2048; xLSTM-v2 block-diagonal B=4 H=4 d=64
-nb=2 T=65536) and the retention decode step on the RetNet shape: tokens/s
-per call and its algorithmic bytes against HBM.
+nb=2 T=65536; the 7B prefill with an output gate) and the retention decode
+step on the RetNet shape: tokens/s per call and its algorithmic bytes
+against HBM.
 
 ``roofline`` is measured live: HIP events recorded by the library right before
 and after its main kernel (mlstm_set_profile_events) give that kernel's
@@ -263,6 +264,28 @@ def bench_variants(torch, mlstm, workload, args, dev):
     out.append(dict(workload="retnet_msr_decode_B8", B=B, H=H, d_k=dk, d_v=dv, steps=D, **r, bytes=byts,
                     flops=B * H * 4 * dk * dv, tokens=B))
     del toks, S, o
+
+    # the 7B prefill with an output gate o = sigmoid(o_pre) [B,H,T,d_v] read too
+    x = workload("xlstm7b_prefill_T8192", with_o=True)
+    B, H, T, dqk = x.q.shape
+    dv = x.v.shape[-1]
+    sets = [x.to(dev), x.to(dev)]
+    hs = [torch.empty(B, H, T, dv, dtype=x.q.dtype, device=dev) for _ in sets]
+    st = (torch.empty(B, H, 1, dqk, dv, device=dev), torch.empty(B, H, dqk, device=dev),
+          torch.empty(B, H, device=dev))
+    ws = torch.empty(mlstm.chunkwise_workspace_bytes(B, H, T, dqk, dv), dtype=torch.uint8, device=dev)
+
+    def call_o(i):
+        g = sets[i]
+        mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, h=hs[i], state_out=st,
+                            workspace=ws)
+
+    r = timed(call_o, len(sets), args.variant_steps, args.variant_steps)
+    byts, flops = prefill_work(B, H, T, dqk, dv)
+    byts += B * H * T * dv * 2
+    out.append(dict(workload="xlstm7b_prefill_T8192_with_o", B=B, H=H, T=T, d_qk=dqk, d_v=dv, **r,
+                    bytes=byts, flops=flops, tokens=B * T))
+    del sets, hs, st, ws
 
     # xLSTM-v2 block-diagonal: B=4, H=4, d=64, nb=2, T=65536 (541 MB per call)
     x = workload("xlstm2_blockdiag_T65536")

@@ -496,6 +496,19 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
     // superchunk whose end state nobody reads
     const bool need_update = more || (sc == p.NS - 1);
 
+    // output-gate values of this wave's outputs, issued at the chunk start
+    // so that phase B hides their latency (phase C uses them)
+    Raw4<T> oraw[has_o ? JPW : 1][has_o ? CT : 1];
+    if constexpr (has_o) {
+#pragma unroll
+      for (int jj = 0; jj < JPW; ++jj)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          oraw[jj][ct] = bload4_raw<T>(
+              ro, ((unsigned)(t0 + (jj * NRG + ((jj & 1) ? NRG - 1 - rg : rg)) * 16 + lr) * DV + wcol0 +
+                   ct * 16 + 4 * lg) * ES);
+    }
+
     frag vf[CT][NKL];  // V^T fragments of this wave's columns
     auto load_vf = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -663,18 +676,6 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
         else exchange(std::integral_constant<int, 1>{});
       }
       __syncthreads();  // B2: P, den partials and readout partials ready
-      // output-gate values of this wave's outputs, issued before the next
-      // chunk's loads so that using them does not wait for those
-      Raw4<T> oraw[has_o ? JPW : 1][has_o ? CT : 1];
-      if constexpr (has_o) {
-#pragma unroll
-        for (int jj = 0; jj < JPW; ++jj)
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct)
-            oraw[jj][ct] = bload4_raw<T>(
-                ro, ((unsigned)(t0 + (jj * NRG + ((jj & 1) ? NRG - 1 - rg : rg)) * 16 + lr) * DV + wcol0 +
-                     ct * 16 + 4 * lg) * ES);
-      }
       // Q of the next chunk now (sQ is free after B2); its K and V after
       // phase C, so that fewer staging registers are live at once
       if (more) load_q(c + 1);
