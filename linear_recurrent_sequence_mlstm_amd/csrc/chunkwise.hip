@@ -601,7 +601,12 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
             store4f(&sP[(be * L + j) * PS + kpos4<T>(lt[u] * 16 + 4 * lg)], x[0], x[1], x[2], x[3]);
           }
           dsum = sum_lane_groups(dsum);
-          if (lg == 0) sDenPart[lt[u] * L + j] = dsum;
+          // the store index is formed here, not hoisted out of the chunk loop
+          // (kept live across the loop it would be spilled, and its reload
+          // would wait for the h stores in flight)
+          int jd = lt[u] * L + j;
+          asm volatile("" : "+v"(jd));
+          if (lg == 0) sDenPart[jd] = dsum;
         }
       };
       {
