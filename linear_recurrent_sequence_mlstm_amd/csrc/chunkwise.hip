@@ -406,10 +406,18 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
     }
   };
 
+  // With the output gate the staging indices are formed at each use:
+  // hoisted out of the chunk loop they would stay live across it, and that
+  // variant would spill (whose reloads wait for every load in flight).
+  // Without it, hoisting them measures faster.
+  auto fresh = [](int& u) __attribute__((always_inline)) {
+    if constexpr (HAS_O) asm volatile("" : "+v"(u));
+  };
   auto store_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < C::QIT; ++it) {
-      const int u = tid + it * NTH;
+      int u = tid + it * NTH;
+      fresh(u);
       if (u < C::NQU) {
         const int j = u / (DQK / VE), col = (u % (DQK / VE)) * VE;
         *reinterpret_cast<uint4*>(&sQ[j * QS + col]) = *reinterpret_cast<const uint4*>(rgq[it].v);
@@ -419,7 +427,8 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   auto store_kv = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < C::QIT; ++it) {
-      const int u = tid + it * NTH;
+      int u = tid + it * NTH;
+      fresh(u);
       if (u < C::NQU) {
         const int j = u / (DQK / VE), col = (u % (DQK / VE)) * VE;
         *reinterpret_cast<uint4*>(&sK[j * KST + col]) = *reinterpret_cast<const uint4*>(rgk[it].v);
@@ -427,7 +436,8 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
     }
 #pragma unroll
     for (int it = 0; it < C::VIT; ++it) {
-      const int u = tid + it * NTH;
+      int u = tid + it * NTH;
+      fresh(u);
       if (u < C::NVU) {
         const int j = u / (W / VE), col = (u % (W / VE)) * VE;
         *reinterpret_cast<uint4*>(&sV[j * VS + col]) = *reinterpret_cast<const uint4*>(rgv[it].v);
