@@ -16,11 +16,12 @@
 //   S~   <- 2^{m_prev-M_L} S~ + sum_l 2^{a_l-M_L} k_l v_l^T;  m <- b_L + M_L
 // Retention is the same with i = 1, f = gamma_h and no normaliser.
 //
-// Four launches on the caller's stream:
-//   pass 1  every superchunk of G chunks but the last: its gate factors (one
-//           small kernel), then its local end state dS, dn from a zero state
-//           (m = -inf) as one dense product; dS, dn, the log scale mu and the
-//           total log decay A go to the workspace.
+// Three launches on the caller's stream:
+//   pass 1  the gate logs of every superchunk of G chunks (extra work-groups)
+//           and, for every superchunk but the last, its local end state dS,
+//           dn from a zero state (m = -inf) as one dense product; dS, dn, the
+//           log scale mu and the total log decay A go to the workspace.  With
+//           a single superchunk a small gate kernel replaces it.
 //   pass 2  per state element, a scan over superchunks
 //           m' = max(A + m, mu); S' = 2^{A+m-m'} S + 2^{mu-m'} dS
 //           leaves the start state of every superchunk in the workspace.
@@ -28,11 +29,12 @@
 //           chunks sequentially from its start state: readout, intra-chunk
 //           product, output, state update.
 //
-// Work-group: 4 waves of 64.  A work-group owns W = 4*WC columns of d_v; wave
-// w owns WC of them and all d_qk/NB rows of the memory block they lie in.  The
-// fp32 state slice lives in registers as MFMA accumulator tiles for the whole
-// superchunk.  Its rows are stored in a permuted order (perm_row) so that the
-// accumulator registers are directly the A operand of the readout MFMA.
+// Pass 3 work-group: 4 column groups x NRG row groups of waves.  It owns
+// W = 4*WC columns of d_v; wave (cg, rg) owns WC of them and d_qk/NB/NRG rows
+// of the memory block they lie in.  The fp32 state slice lives in registers
+// as MFMA accumulator tiles for the whole superchunk.  Its rows are stored in
+// a permuted order (perm_row) so that the accumulator registers are directly
+// the A operand of the readout MFMA.
 #include <type_traits>
 
 #include "common.h"
@@ -310,7 +312,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   const auto rq = make_rsrc(static_cast<const T*>(p.q) + (size_t)bh * T_ * DQK, (unsigned)T_ * DQK * ES);
   const auto rk = make_rsrc(static_cast<const T*>(p.k) + (size_t)bh * T_ * DQK, (unsigned)T_ * DQK * ES);
   const auto rv = make_rsrc(static_cast<const T*>(p.v) + (size_t)bh * T_ * DV, (unsigned)T_ * DV * ES);
-  // chunk-local gate logs of the gate kernel, over the padded sequence
+  // chunk-local gate logs of the gate pass, over the padded sequence
   const size_t NCL = (size_t)p.NC * L;
   const auto rga_r = make_rsrc(p.ws_ga + (size_t)bh * NCL, (unsigned)NCL * 4u);
   const auto rgg_r = make_rsrc(p.ws_gg + (size_t)bh * NCL, (unsigned)NCL * 4u);
@@ -446,7 +448,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   };
 
   // Gate factors of one chunk on wave 0 (one lane per token) from the
-  // chunk-local logs b_j, a_j, g_j of the gate kernel: only the chain through
+  // chunk-local logs b_j, a_j, g_j of the gate pass: only the chain through
   // m_prev is left here.
   auto gates = [&](int gb) __attribute__((always_inline)) {
     const float a = __uint_as_float(rga), g = __uint_as_float(rgg), b = __uint_as_float(rgb);
