@@ -1124,8 +1124,13 @@ struct LocalCfg {
 // fragment times per-k weights, rounded back to bf16 in pairs
 __device__ __forceinline__ bf16x8 scale_frag8(bf16x8 x, const float (&w)[8]) { return scale_frag(x, w); }
 
-template <typename T, int DQK, int NB, int TR, int TC, int L, bool RET, int NWP>
+// NBS: memory blocks of the stored state.  NBS = NB tiles each block; with
+// NB = 1 < NBS (blocks narrower than 64 rows) a tile spans the whole head,
+// its product covers every block pair, and only the diagonal blocks are
+// stored (the off-diagonal MFMA work is cheaper than tiles of 32 rows).
+template <typename T, int DQK, int NB, int TR, int TC, int L, bool RET, int NWP, int NBS = NB>
 __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
+  static_assert(NBS == NB || NB == 1, "whole-head tiles store several blocks");
   constexpr int KS = sizeof(T) == 2 ? 32 : 16;
   using C = LocalCfg<T, TR, TC, KS, NWP>;
   constexpr int NTH = C::NTH;
@@ -1181,7 +1186,7 @@ __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
   const int blk = tile / (NRT * nct), rt = (tile / nct) % NRT, ctl = tile % nct;
   const int f0 = blk * DQKB + rt * TR;  // first feature (of the head) of the tile
   const int c0 = blk * DVB + ctl * TC;  // first d_v column of the tile
-  const size_t CS = (size_t)DQK * DVB;
+  const size_t CS = (size_t)DQK * (DV / NBS);
   const size_t NSTATE = CS + (RET ? 0 : DQK);
 
   const auto rk = make_rsrc(static_cast<const T*>(p.k) + (size_t)bh * T_ * DQK, (unsigned)T_ * DQK * ES);
@@ -1360,7 +1365,17 @@ __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
       for (int i = 0; i < 4; ++i) {
         const int r = rt * TR + wr * (TR / WR) + mt * 16 + 4 * lg + i;  // row within the block
         const int cl = ctl * TC + wcw * (TC / WCW) + nt * 16 + lr;     // column within the block
-        dst[(size_t)blk * DQKB * DVB + (size_t)r * DVB + cl] = acc[mt][nt][i];
+        if constexpr (NBS == NB) {
+          dst[(size_t)blk * DQKB * DVB + (size_t)r * DVB + cl] = acc[mt][nt][i];
+        } else {
+          // whole-head tile: row r and column cl of the head; keep the
+          // diagonal blocks
+          constexpr int RB = DQK / NBS;
+          const int DVS = DV / NBS;
+          const int bs = r / RB;
+          if (bs == cl / DVS)
+            dst[(size_t)bs * RB * DVS + (size_t)(r - bs * RB) * DVS + (cl - bs * DVS)] = acc[mt][nt][i];
+        }
       }
   if constexpr (!RET) {
     if (do_dn && lr == 0) {
@@ -1452,21 +1467,24 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
     // V rows then serve twice the MFMA work of a 128-row tile, which halves
     // the redundant L2-to-LDS traffic that bounds this pass.  The gate
     // work-groups (one per batch*head and superchunk) follow the tiles.
-    constexpr int DQKB = DQK / NB;
+    // Blocks narrower than 64 rows: whole-head tiles (NBC = 1), diagonal
+    // blocks stored.
+    constexpr int NBC = (NB > 1 && DQK / NB < 64) ? 1 : NB;  // blocks of the tiling
+    constexpr int DQKB = DQK / NBC;
     constexpr int RCAP = sizeof(T) == 2 ? MLSTM_P1_ROWS : 64;
     constexpr int TR = DQKB < RCAP ? DQKB : RCAP;
     constexpr int NWP = TR >= 256 ? 8 : 4;
     constexpr int TCAP = sizeof(T) == 2 ? 128 : 64;
-    const int DVB = p.DV / NB;
+    const int DVB = p.DV / NBC;
     const int TC = DVB % TCAP == 0 ? TCAP : DVB % 64 == 0 ? 64 : 32;
-    const dim3 g1((unsigned)(BH * (p.NS - 1) * NB * (DQKB / TR) * (DVB / TC) + BH * p.NS));
+    const dim3 g1((unsigned)(BH * (p.NS - 1) * NBC * (DQKB / TR) * (DVB / TC) + BH * p.NS));
     const dim3 b1(64 * NWP);
     if (TC == TCAP)
-      hipLaunchKernelGGL((local_state_kernel<T, DQK, NB, TR, TCAP, L, RET, NWP>), g1, b1, 0, stream, p);
+      hipLaunchKernelGGL((local_state_kernel<T, DQK, NBC, TR, TCAP, L, RET, NWP, NB>), g1, b1, 0, stream, p);
     else if (TC == 64)
-      hipLaunchKernelGGL((local_state_kernel<T, DQK, NB, TR, 64, L, RET, NWP>), g1, b1, 0, stream, p);
+      hipLaunchKernelGGL((local_state_kernel<T, DQK, NBC, TR, 64, L, RET, NWP, NB>), g1, b1, 0, stream, p);
     else
-      hipLaunchKernelGGL((local_state_kernel<T, DQK, NB, TR, 32, L, RET, NWP>), g1, b1, 0, stream, p);
+      hipLaunchKernelGGL((local_state_kernel<T, DQK, NBC, TR, 32, L, RET, NWP, NB>), g1, b1, 0, stream, p);
   }
   ScanParams s;
   s.NS = p.NS;
