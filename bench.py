@@ -15,10 +15,10 @@ B=256, 8 heads, fp32 state [256,8,256,512] (1 GiB) updated in place, 128 steps
 with a fresh bf16 token per step; it reports achieved HBM GB/s.
 
 ``variants`` times the other chunkwise workloads through the same kernels
-(RetNet retention B=8 H=4 d=64 T=2048; xLSTM-v2 block-diagonal B=4 H=4 d=64
-nb=2 T=65536; the 7B prefill with an output gate) and the retention decode
-step on the RetNet shape: tokens/s per call and its algorithmic bytes
-against HBM.
+(RetNet retention B=8 H=4 d=64 T=2048, also with its per-head group norm
+fused; xLSTM-v2 block-diagonal B=4 H=4 d=64 nb=2 T=65536; the 7B prefill
+with an output gate) and the retention decode step on the RetNet shape:
+tokens/s per call and its algorithmic bytes against HBM.
 
 ``roofline`` is measured live: HIP events recorded by the library right before
 and after its main kernel (mlstm_set_profile_events) give that kernel's
@@ -250,7 +250,15 @@ def bench_variants(torch, mlstm, workload, args, dev):
     byts, flops = retention_work(B, H, T, dk, dv)
     out.append(dict(workload="retnet_msr_T2048", B=B, H=H, T=T, d_k=dk, d_v=dv, **r, bytes=byts, flops=flops,
                     tokens=B * T))
-    del sets, outs, S, ws
+    # the same with the per-head group norm fused into the output write
+    gw = torch.ones(H * dv, device=dev)
+    gb = torch.zeros(H * dv, device=dev)
+    r = timed(lambda i: mlstm.retention_chunkwise_fwd(*sets[i], out=outs[i], S_out=S, workspace=ws,
+                                                      groupnorm=(gw, gb, 1e-5)),
+              len(sets), args.variant_steps, args.variant_steps)
+    out.append(dict(workload="retnet_msr_T2048_groupnorm", B=B, H=H, T=T, d_k=dk, d_v=dv, **r,
+                    bytes=byts + 2 * H * dv * 4, flops=flops, tokens=B * T))
+    del sets, outs, S, ws, gw, gb
 
     # retention decode on the same workload: its first D tokens, one call
     # of retention_step each, state updated in place

@@ -160,6 +160,29 @@ int retention_chunkwise_fwd(int B, int H, int T, int d_k, int d_v, int chunk,
                             size_t workspace_bytes, void* stream);
 
 /*
+ * retention_chunkwise_fwd with the per-head group norm of the "Multi-Scale
+ * Retention (MSR)" section of the "Edifice.Attention.RetNet" page fused into
+ * the output write: each output row of each head is normalised over its d_v
+ * channels,
+ *     out = (y - mean(y)) / sqrt(var(y) + gn_eps) * gn_weight + gn_bias
+ * with y the retention output, mean and (biased) variance over the row, and
+ * per-channel gn_weight, gn_bias [H*d_v] fp32 (NULL: 1 and 0), as a group
+ * norm with one group per head over the H*d_v channels.  Statistics are
+ * taken in fp32 before rounding to dt.  Same arguments, workspace and
+ * S0/S_out as retention_chunkwise_fwd; gn_eps > 0.  Requires d_v = 64 for
+ * d_k = 64 and d_v = 128 for d_k = 128 (one work-group holds a whole row);
+ * other shapes return MLSTM_E_UNSUPPORTED.
+ */
+int retention_chunkwise_groupnorm_fwd(int B, int H, int T, int d_k, int d_v,
+                                      int chunk, mlstm_dtype dt, const void* q,
+                                      const void* k, const void* v,
+                                      const float* gamma, const float* S0,
+                                      float* S_out, const float* gn_weight,
+                                      const float* gn_bias, float gn_eps,
+                                      void* out, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/*
  * RetNet retention, one decode step on every (b, h), in the recurrent form of
  * the "Edifice.Attention.RetNet" page ("Key Innovation: Retention
  * Mechanism"; recurrent mode of "Triple Paradigm"):

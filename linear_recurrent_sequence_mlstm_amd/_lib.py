@@ -24,7 +24,7 @@ _DT = {torch.float32: F32, torch.bfloat16: BF16}
 EXPORTS = ("mlstm_abi_version", "mlstm_last_error", "mlstm_set_profile_events",
            "mlstm_chunkwise_workspace_bytes",
            "mlstm_chunkwise_fwd", "mlstm_step", "retention_chunkwise_workspace_bytes",
-           "retention_chunkwise_fwd", "retention_step")
+           "retention_chunkwise_fwd", "retention_chunkwise_groupnorm_fwd", "retention_step")
 
 
 def library_path() -> str:
@@ -57,6 +57,9 @@ def lib():
     L.retention_chunkwise_workspace_bytes.restype = sz
     L.retention_chunkwise_fwd.argtypes = [i] * 7 + [vp] * 3 + [fp] * 3 + [vp, vp, sz, vp]
     L.retention_chunkwise_fwd.restype = i
+    L.retention_chunkwise_groupnorm_fwd.argtypes = ([i] * 7 + [vp] * 3 + [fp] * 5 + [ctypes.c_float] +
+                                                    [vp, vp, sz, vp])
+    L.retention_chunkwise_groupnorm_fwd.restype = i
     L.retention_step.argtypes = [i] * 5 + [vp] * 3 + [fp] * 2 + [vp, vp]
     L.retention_step.restype = i
     _lib = L
@@ -207,9 +210,11 @@ def step(q, k, v, i_pre, f_pre, C, n, m, o_pre=None, bias=None, num_blocks=1, h=
 
 
 def retention_chunkwise_fwd(q, k, v, gamma=None, S0=None, chunk=64, return_state=True, out=None,
-                            S_out=None, workspace=None):
+                            S_out=None, workspace=None, groupnorm=None):
     """retention_chunkwise_fwd.  q,k [B,H,T,dk]; v [B,H,T,dv]; gamma [H] fp32
-    or None (1 - 2^(-5-h)); S0 [B,H,dk,dv] fp32 or None.  Returns (out, S)."""
+    or None (1 - 2^(-5-h)); S0 [B,H,dk,dv] fp32 or None.  Returns (out, S).
+    groupnorm = (weight [H*dv] or None, bias [H*dv] or None, eps) fuses the
+    per-head group norm of the outputs (retention_chunkwise_groupnorm_fwd)."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
@@ -232,6 +237,16 @@ def retention_chunkwise_fwd(q, k, v, gamma=None, S0=None, chunk=64, return_state
         _check(L.retention_chunkwise_fwd(B, H, T, dk, dv, chunk, _DT[dt], *([None] * 7), None, 0, None),
                "retention_chunkwise_fwd")
     ws = _workspace(nbytes, dev, workspace)
+    if groupnorm is not None:
+        gw, gb, eps = groupnorm
+        _need(gw, "gn_weight", (H * dv,), torch.float32, dev)
+        _need(gb, "gn_bias", (H * dv,), torch.float32, dev)
+        rc = L.retention_chunkwise_groupnorm_fwd(B, H, T, dk, dv, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v),
+                                                 _ptr(gamma), _ptr(S0), _ptr(S_out if return_state else None),
+                                                 _ptr(gw), _ptr(gb), float(eps), _ptr(out), _ptr(ws),
+                                                 ws.numel(), _stream(dev))
+        _check(rc, "retention_chunkwise_groupnorm_fwd")
+        return out, (S_out if return_state else None)
     rc = L.retention_chunkwise_fwd(B, H, T, dk, dv, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v),
                                    _ptr(gamma), _ptr(S0), _ptr(S_out if return_state else None),
                                    _ptr(out), _ptr(ws), ws.numel(), _stream(dev))

@@ -206,6 +206,40 @@ int retention_chunkwise_fwd(int B, int H, int T, int d_k, int d_v, int chunk, ml
   return launch(pl, p, workspace, workspace_bytes, stream);
 }
 
+int retention_chunkwise_groupnorm_fwd(int B, int H, int T, int d_k, int d_v, int chunk, mlstm_dtype dt,
+                                      const void* q, const void* k, const void* v, const float* gamma,
+                                      const float* S0, float* S_out, const float* gn_weight,
+                                      const float* gn_bias, float gn_eps, void* out, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  Plan pl;
+  const int rc = plan_chunkwise(B, H, T, d_k, d_v, 1, chunk, dt, true, &pl);
+  if (rc != MLSTM_OK) return rc;
+  mlstm::ChunkVariant gv;
+  if (!mlstm::find_retention_groupnorm_variant(dt, d_k, chunk, &gv) || d_v != gv.w)
+    return fail(MLSTM_E_UNSUPPORTED, "fused group norm needs d_v = %d for d_k=%d (got d_v=%d)",
+                mlstm::find_retention_groupnorm_variant(dt, d_k, chunk, &gv) ? gv.w : 0, d_k, d_v);
+  if (!(gn_eps > 0.f)) return fail(MLSTM_E_SHAPE, "gn_eps must be positive (got %g)", (double)gn_eps);
+  if (!q || !k || !v || !out) return fail(MLSTM_E_NULL, "q, k, v and out are required");
+  pl.var.launch = gv.launch;  // same plan and workspace as without the norm
+  mlstm::ChunkParams p{};
+  p.B = B;
+  p.H = H;
+  p.T = T;
+  p.DV = d_v;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.ret_gamma = gamma;
+  p.has_init = S0 ? 1 : 0;
+  p.C0 = S0;
+  p.h = out;
+  p.C_out = S_out;
+  p.gn_w = gn_weight;
+  p.gn_b = gn_bias;
+  p.gn_eps = gn_eps;
+  return launch(pl, p, workspace, workspace_bytes, stream);
+}
+
 int mlstm_step(int B, int H, int d_qk, int d_v, int num_blocks, mlstm_dtype dt, const void* q, const void* k,
                const void* v, const void* i_pre, const void* f_pre, const void* o_pre, const float* norm_bias,
                float* C, float* n, float* m, void* h, void* stream) {

@@ -126,7 +126,7 @@ constexpr int lds_pad_res(int row_elems, int esize, int res) {
 #define MLSTM_P3_KRES 24
 #endif
 
-template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L>
+template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool GN = false>
 struct ChunkCfg {
   static constexpr int K = Mma<T>::K;
   static constexpr int KL = Mma<T>::KL;
@@ -169,9 +169,11 @@ struct ChunkCfg {
   static constexpr int VS = W + lds_row_pad(W, (int)sizeof(T));  // sV
   static constexpr int PS = L + 16 / (int)sizeof(T);  // sP
   // bf16 outputs are staged in LDS (sH, token-major) and written as whole
-  // 16-byte units of the work-group's row segment
-  static constexpr bool HST = sizeof(T) == 2;
-  static constexpr int HS = W + 16 / (int)sizeof(T);
+  // 16-byte units of the work-group's row segment.  With the fused group
+  // norm (GN) every output is staged, in fp32, and normalised per row.
+  static constexpr bool HST = sizeof(T) == 2 || GN;
+  using HT = typename std::conditional<GN, float, T>::type;  // staging type
+  static constexpr int HS = W + 16 / (int)sizeof(HT);
   // staging units (16-byte loads) per chunk
   static constexpr int NQU = L * DQK / VE;
   static constexpr int NVU = L * W / VE;
@@ -192,7 +194,7 @@ struct ChunkCfg {
     b += (size_t)NB * L * PS * sizeof(T);        // sP
     b += (size_t)(NJT + 1) * L * 4;              // den partials
     if (NRG > 1) b += (size_t)NCG * NJT * CT * 64 * 16;  // readout exchange
-    if (HST) b += (size_t)L * HS * sizeof(T);    // sH
+    if (HST) b += (size_t)L * HS * sizeof(HT);   // sH
     return b;
   }
 };
@@ -247,9 +249,9 @@ __device__ __forceinline__ float frag_rows(const float* tile, int RS, int kb0, i
 // the token tiles and the two partial sums meet in LDS (sX).
 // Q, K and V are staged token-major with plain 16-byte copies; the operands
 // that run along tokens (K^T and V^T) are read with transposing LDS reads.
-template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET, bool HAS_O>
+template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET, bool HAS_O, bool GN = false>
 __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
-  using C = ChunkCfg<T, DQK, NB, WC, NRG, NCG, L>;
+  using C = ChunkCfg<T, DQK, NB, WC, NRG, NCG, L, GN>;
   using M = Mma<T>;
   typedef typename M::frag frag;
   constexpr int K = C::K, KL = C::KL, DQKB = C::DQKB, NT = C::NT, CT = C::CT, NW = C::NW;
@@ -266,7 +268,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   __shared__ __attribute__((aligned(16))) T sQ[L * QS];   // Q, token-major
   __shared__ __attribute__((aligned(16))) T sP[NB * L * PS];
   __shared__ __attribute__((aligned(16))) f32x4 sX[XCH ? NCG * NJT * CT * 64 : 1];
-  __shared__ __attribute__((aligned(16))) T sH[HST ? L * HS : 8];  // outputs of the chunk
+  __shared__ __attribute__((aligned(16))) typename C::HT sH[HST ? L * HS : 8];  // outputs of the chunk
   // n~ as rows 0 and 1 of a 16-row A-operand tile (rows 2..15 are zero and
   // not stored): row 0 = bf16 hi part, row 1 = lo part (fp32: row 0 = n~,
   // row 1 zero)
@@ -480,8 +482,50 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   // The chunk's outputs from sH, whole 16-byte units per lane (rows past T
   // are dropped by the buffer range).  Issued after the next chunk's B1, where
   // the waves have slack, and once more after the loop.
+  // group norm: a thread's units always have the same 4 columns (NTH is a
+  // multiple of the units per row), so its affine parameters load once
+  float gnw[GN ? 4 : 1], gnb[GN ? 4 : 1];
+  if constexpr (GN) {
+    const int col = (tid % (W / 4)) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gnw[i] = p.gn_w ? p.gn_w[hd * DV + col + i] : 1.f;
+      gnb[i] = p.gn_b ? p.gn_b[hd * DV + col + i] : 0.f;
+    }
+  }
   auto store_h = [&](int tc) __attribute__((always_inline)) {
-    if constexpr (HST) {
+    if constexpr (GN) {
+      // Group norm of each output row over the head's d_v channels (the
+      // work-group holds the whole row, W = d_v): a group of UR consecutive
+      // lanes owns a row, 4 fp32 values per lane; mean, then the biased
+      // variance of the centred values; y = (x - mean) rsqrt(var + eps) w + b.
+      constexpr int UR = W / 4;
+      static_assert((UR & (UR - 1)) == 0 && UR <= 64 && NTH % UR == 0, "row groups of lanes");
+#pragma unroll
+      for (int u0 = 0; u0 < L * UR; u0 += NTH) {
+        const int u = u0 + tid;
+        const int j = u / UR, cu = u % UR;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&sH[j * HS + cu * 4]);
+        float sm = (x[0] + x[1]) + (x[2] + x[3]);
+#pragma unroll
+        for (int d = 1; d < UR; d <<= 1) sm += __shfl_xor(sm, d, 64);
+        const float mean = sm * (1.f / W);
+        float dx[4], sq = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dx[i] = x[i] - mean;
+          sq += dx[i] * dx[i];
+        }
+#pragma unroll
+        for (int d = 1; d < UR; d <<= 1) sq += __shfl_xor(sq, d, 64);
+        const float rstd = rsqrtf(sq * (1.f / W) + p.gn_eps);
+        const int col = cu * 4;
+        float y[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = dx[i] * rstd * gnw[i] + gnb[i];
+        bstore4<T>(rh, ((unsigned)(tc + j) * DV + col) * ES, y[0], y[1], y[2], y[3]);
+      }
+    } else if constexpr (HST) {
       constexpr int UR = W / VE;  // units per token row
 #pragma unroll
       for (int u = tid; u < L * UR; u += NTH) {
@@ -1449,12 +1493,12 @@ __global__ __launch_bounds__(256) void superchunk_scan_kernel(ScanParams p) {
   }
 }
 
-template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET>
+template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET, bool GN>
 size_t chunk_lds_bytes() {
-  return ChunkCfg<T, DQK, NB, WC, NRG, NCG, L>::lds_bytes(RET);
+  return ChunkCfg<T, DQK, NB, WC, NRG, NCG, L, GN>::lds_bytes(RET);
 }
 
-template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET>
+template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET, bool GN>
 hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   constexpr int NTH = 64 * NCG * NRG;
   const int BH = p.B * p.H;
@@ -1502,7 +1546,9 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
   hipLaunchKernelGGL((superchunk_scan_kernel<RET>), g2, dim3(256), 0, stream, s);
   dim3 g3((unsigned)(BH * p.nslices * p.NS));
   if (ev0) (void)hipEventRecord(ev0, stream);
-  if (!RET && p.o_pre)
+  if constexpr (GN)
+    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, false, true>), g3, dim3(NTH), 0, stream, p);
+  else if (!RET && p.o_pre)
     hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, !RET>), g3, dim3(NTH), 0, stream, p);
   else
     hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, false>), g3, dim3(NTH), 0, stream, p);
@@ -1534,8 +1580,26 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
 bool find_chunk_variant(int dtype, int dqk, int nb, int L, bool ret, ChunkVariant* out) {
 #define X(T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_)                                              \
   if (dtype == (sizeof(T_) == 2 ? 1 : 0) && dqk == DQK_ && nb == NB_ && L == L_ && ret == RET_) { \
-    out->launch = &launch_chunkwise<T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_>;                   \
-    out->lds_bytes = chunk_lds_bytes<T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_>();                \
+    out->launch = &launch_chunkwise<T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_, false>;            \
+    out->lds_bytes = chunk_lds_bytes<T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_, false>();         \
+    out->wc = WC_;                                                                               \
+    out->w = NCG_ * WC_;                                                                         \
+    return true;                                                                                 \
+  }
+  MLSTM_CHUNK_VARIANTS(X)
+#undef X
+  return false;
+}
+
+// Retention with the per-head group norm fused into the output store (the
+// "Multi-Scale Retention (MSR)" section of the "Edifice.Attention.RetNet"
+// page normalises each head's output with a group norm): the retention
+// variants above, with d_v equal to their slice width.
+bool find_retention_groupnorm_variant(int dtype, int dqk, int L, ChunkVariant* out) {
+#define X(T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_)                                              \
+  if (RET_ && dtype == (sizeof(T_) == 2 ? 1 : 0) && dqk == DQK_ && NB_ == 1 && L == L_) {        \
+    out->launch = &launch_chunkwise<T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_, RET_>;             \
+    out->lds_bytes = chunk_lds_bytes<T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_, RET_>();          \
     out->wc = WC_;                                                                               \
     out->w = NCG_ * WC_;                                                                         \
     return true;                                                                                 \

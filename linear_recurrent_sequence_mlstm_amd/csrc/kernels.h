@@ -31,6 +31,11 @@ struct ChunkParams {
   float* C_out;
   float* n_out;
   float* m_out;
+  // fused group norm of retention outputs: [H*d_v] weight and bias (null:
+  // 1 and 0) and epsilon
+  const float* gn_w;
+  const float* gn_b;
+  float gn_eps;
 };
 
 struct ScanParams {
@@ -58,6 +63,8 @@ struct ChunkVariant {
 
 // dtype: 0 = fp32, 1 = bf16.
 bool find_chunk_variant(int dtype, int dqk, int nb, int L, bool ret, ChunkVariant* out);
+// Retention with the group norm of each head's output fused (d_v = out->w).
+bool find_retention_groupnorm_variant(int dtype, int dqk, int L, ChunkVariant* out);
 
 // Decode step.
 struct StepParams {

@@ -18,6 +18,8 @@ Parity status of each function (what pins it is listed in the tests):
                    special case, T=1 closed form, state carry)
   mlstm_step       pinned (equals mlstm_fwd one token at a time, T=1 form)
   retention_fwd    pinned (decay-matrix closed form of the RetNet page)
+  groupnorm        pinned (torch's group_norm in fp64; zero mean and
+                   var/(var+eps) variance of every normalised row)
 """
 from __future__ import annotations
 
@@ -129,6 +131,25 @@ def mlstm_step(q, k, v, i_pre, f_pre, C, n, m, o_pre=None, bias=None,
     if rc != 0:
         raise ValueError("oracle_mlstm_step failed with %d" % rc)
     return h
+
+
+def groupnorm(y, weight=None, bias=None, eps=1e-5):
+    """Per-head group norm of retention outputs ("Multi-Scale Retention
+    (MSR)" section of the "Edifice.Attention.RetNet" page: a group norm
+    normalises each head's output).  y [B,H,T,dv]; one group per head over
+    its dv channels, per token: (y - mean) / sqrt(var + eps) with the mean
+    and biased variance over those dv values, then the per-channel affine
+    weight, bias [H*dv] (None: 1, 0).  Plain numpy in fp64."""
+    y = _f64(y)
+    B, H, T, dv = y.shape
+    mean = y.mean(axis=3, keepdims=True)
+    var = ((y - mean) ** 2).mean(axis=3, keepdims=True)
+    out = (y - mean) / np.sqrt(var + eps)
+    if weight is not None:
+        out = out * _f64(weight).reshape(1, H, 1, dv)
+    if bias is not None:
+        out = out + _f64(bias).reshape(1, H, 1, dv)
+    return out
 
 
 def retention_fwd(q, k, v, gamma=None, S0=None, lib=None):

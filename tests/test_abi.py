@@ -84,6 +84,17 @@ def test_retention_step_validation():
     assert _lib.last_error() != ""
 
 
+def test_retention_groupnorm_validation():
+    L = _lib.lib()
+    f = ctypes.c_float
+    args = lambda dv=64, eps=1e-5, q=BOGUS: [1, 1, 10, 64, dv, 64, 1, q, BOGUS, BOGUS, None, None, None,
+                                            None, None, f(eps), BOGUS, BOGUS, 1 << 30, None]
+    assert L.retention_chunkwise_groupnorm_fwd(*args(dv=128)) == E_UNSUPPORTED  # d_v must be 64 at d_k 64
+    assert L.retention_chunkwise_groupnorm_fwd(*args(eps=0.0)) == E_SHAPE
+    assert L.retention_chunkwise_groupnorm_fwd(*args(q=None)) == E_NULL
+    assert _lib.last_error() != ""
+
+
 def test_retention_validation():
     L = _lib.lib()
     p = [BOGUS] * 3 + [None] * 3

@@ -317,3 +317,32 @@ def test_pin_xlstm7b_state_size():
     per_head = dqk * dv + dqk  # C [d_qk, d_v] + n [d_qk]
     total = int(kv["layers"]) * heads * per_head * int(kv["bytes_per_element"])
     assert round(total / 2 ** 20, 1) == float(kv["printed_mib"])
+
+
+# ---------------------------------------------------------------- group norm
+def test_pin_groupnorm_is_torch_group_norm():
+    """The per-head group norm equals torch's group_norm routine (fp64, one
+    group per head over the H*dv channels of each token)."""
+    import torch
+    g = torch.Generator().manual_seed(17)
+    B, H, T, dv = 2, 3, 5, 8
+    y = torch.randn(B, H, T, dv, generator=g, dtype=torch.float64) * 3 + 1
+    w = torch.randn(H * dv, generator=g, dtype=torch.float64)
+    b = torch.randn(H * dv, generator=g, dtype=torch.float64)
+    got = oracle.groupnorm(y, w, b, eps=1e-3)
+    x = y.permute(0, 2, 1, 3).reshape(B * T, H * dv)
+    ref = torch.nn.functional.group_norm(x, H, w, b, eps=1e-3)
+    ref = ref.reshape(B, T, H, dv).permute(0, 2, 1, 3).numpy()
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_pin_groupnorm_row_moments():
+    """Without the affine part every normalised row has mean 0 and variance
+    var / (var + eps) exactly."""
+    rng = np.random.default_rng(3)
+    y = rng.normal(size=(1, 2, 7, 16)) * np.array([0.5, 4.0]).reshape(1, 2, 1, 1)
+    eps = 1e-2
+    out = oracle.groupnorm(y, eps=eps)
+    var = y.var(axis=3)
+    assert np.max(np.abs(out.mean(axis=3))) < 1e-12
+    assert np.max(np.abs(out.var(axis=3) - var / (var + eps))) < 1e-12

@@ -192,6 +192,34 @@ def test_retention_custom_gamma_fp32(gpu):
     assert slice_err(cpu(S), ref_S) < TOL[torch.float32]
 
 
+@pytest.mark.parametrize("B,H,T,dk,dtype,with_state,affine", [
+    (8, 4, 2048, 64, "bf16", False, True),   # the RetNet workload's shape
+    (2, 3, 130, 64, "bf16", True, False),    # ragged tail, initial state
+    (1, 2, 100, 64, "f32", True, True),
+    (2, 2, 200, 128, "bf16", False, True),
+])
+def test_retention_groupnorm(gpu, B, H, T, dk, dtype, with_state, affine):
+    """Retention with the per-head group norm fused into the output write
+    against the oracle's retention followed by its group norm; the final
+    state is unaffected by the norm."""
+    dv = dk
+    q, k, v = retention_inputs(B, H, T, dk, dv, seed=31, dtype=dtype)
+    g = torch.Generator().manual_seed(6)
+    S0 = torch.randn(B, H, dk, dv, generator=g) * 0.1 if with_state else None
+    w = torch.rand(H * dv, generator=g) + 0.5 if affine else None
+    b = torch.randn(H * dv, generator=g) * 0.1 if affine else None
+    gamma = torch.linspace(0.7, 0.99, H) if dtype == "f32" else None
+    dv_ = lambda t: None if t is None else t.to(gpu)
+    out, S = mlstm.retention_chunkwise_fwd(q.to(gpu), k.to(gpu), v.to(gpu), gamma=dv_(gamma), S0=dv_(S0),
+                                           groupnorm=(dv_(w), dv_(b), 1e-5))
+    torch.cuda.synchronize()
+    ref_y, ref_S = oracle.retention_fwd(q, k, v, gamma=gamma, S0=S0)
+    ref = oracle.groupnorm(ref_y, w, b, eps=1e-5)
+    tol = TOL[torch.bfloat16 if dtype == "bf16" else torch.float32]
+    assert slice_err(cpu(out), ref) < tol
+    assert slice_err(cpu(S), ref_S) < tol
+
+
 @pytest.mark.parametrize("B,H,dk,dv,dtype,custom_gamma", [
     (8, 4, 64, 64, "bf16", False), (2, 3, 128, 256, "f32", True), (3, 2, 256, 512, "bf16", True),
 ])
