@@ -58,7 +58,7 @@ def _load(path: str | None = None):
     i = ctypes.c_int
     lib.oracle_mlstm_fwd.argtypes = [i, i, i, i, i, i, i] + [P] * 14
     lib.oracle_mlstm_fwd.restype = i
-    lib.oracle_mlstm_step.argtypes = [i, i, i, i, i] + [P] * 11
+    lib.oracle_mlstm_step.argtypes = [i, i, i, i, i, i] + [P] * 11
     lib.oracle_mlstm_step.restype = i
     lib.oracle_retention_fwd.argtypes = [i, i, i, i, i] + [P] * 7
     lib.oracle_retention_fwd.restype = i
@@ -90,14 +90,27 @@ def num_threads() -> int:
     return _load().oracle_num_threads()
 
 
+# normaliser readings (see oracle.c, cell_step): the vector n . q used
+# throughout, the scalar n = f n + i the XLSTMv2 page prints, and a
+# per-block vector normaliser for the block-diagonal memory
+NORM_MODES = {"vector": 1, "scalar": 2, "block": 3}
+
+
 def mlstm_fwd(q, k, v, i_pre, f_pre, o_pre=None, bias=None, C0=None, n0=None,
-              m0=None, num_blocks=1, normalise=True, m_shift=None, lib=None):
+              m0=None, num_blocks=1, normalise=True, m_shift=None, lib=None,
+              norm_mode="vector"):
     """Sequence form.  Shapes: q,k [B,H,T,dqk]; v [B,H,T,dv]; gates [B,H,T];
     o_pre [B,H,T,dv] or None; bias [H] or None; C0 [B,H,nb,dqk/nb,dv/nb];
-    n0 [B,H,dqk]; m0 [B,H].  Returns (h, C, n, m) as float64 arrays."""
+    n0 [B,H,dqk] ([B,H] with norm_mode "scalar"); m0 [B,H].
+    Returns (h, C, n, m) as float64 arrays (n [B,H] in scalar mode)."""
     q, k, v, ip, fp = map(_f64, (q, k, v, i_pre, f_pre))
     op, bs, c0, nn0, mm0, ms = map(_f64, (o_pre, bias, C0, n0, m0, m_shift))
     B, H, T, dqk = q.shape
+    mode = NORM_MODES[norm_mode] if normalise else 0
+    if mode == 2 and nn0 is not None:
+        e = np.zeros((B, H, dqk))
+        e[:, :, 0] = nn0.reshape(B, H)
+        nn0 = e
     dv = v.shape[-1]
     nb = int(num_blocks)
     assert k.shape == q.shape and v.shape == (B, H, T, dv)
@@ -107,29 +120,37 @@ def mlstm_fwd(q, k, v, i_pre, f_pre, o_pre=None, bias=None, C0=None, n0=None,
     n = np.zeros((B, H, dqk))
     m = np.zeros((B, H))
     rc = (lib or _load()).oracle_mlstm_fwd(
-        B, H, T, dqk, dv, nb, 1 if normalise else 0, _ptr(q), _ptr(k), _ptr(v),
+        B, H, T, dqk, dv, nb, mode, _ptr(q), _ptr(k), _ptr(v),
         _ptr(ip), _ptr(fp), _ptr(op), _ptr(bs), _ptr(c0), _ptr(nn0), _ptr(mm0),
         _ptr(ms), _ptr(h), _ptr(C), _ptr(n), _ptr(m))
     if rc != 0:
         raise ValueError("oracle_mlstm_fwd failed with %d" % rc)
-    return h, C, n, m
+    return h, C, (n[:, :, 0].copy() if mode == 2 else n), m
 
 
 def mlstm_step(q, k, v, i_pre, f_pre, C, n, m, o_pre=None, bias=None,
-               num_blocks=1, lib=None):
+               num_blocks=1, lib=None, norm_mode="vector"):
     """One decode step.  q,k [B,H,dqk]; v [B,H,dv]; gates [B,H]; C,n,m are
-    float64 arrays updated IN PLACE.  Returns h [B,H,dv] (float64)."""
+    float64 arrays updated IN PLACE (n [B,H] with norm_mode "scalar").
+    Returns h [B,H,dv] (float64)."""
     q, k, v, ip, fp, op, bs = map(_f64, (q, k, v, i_pre, f_pre, o_pre, bias))
     for a in (C, n, m):
         assert isinstance(a, np.ndarray) and a.dtype == np.float64 and a.flags.c_contiguous
     B, H, dqk = q.shape
     dv = v.shape[-1]
+    mode = NORM_MODES[norm_mode]
+    nn = n
+    if mode == 2:
+        nn = np.zeros((B, H, dqk))
+        nn[:, :, 0] = n.reshape(B, H)
     h = np.zeros((B, H, dv))
     rc = (lib or _load()).oracle_mlstm_step(
-        B, H, dqk, dv, int(num_blocks), _ptr(q), _ptr(k), _ptr(v), _ptr(ip),
-        _ptr(fp), _ptr(op), _ptr(bs), _ptr(C), _ptr(n), _ptr(m), _ptr(h))
+        B, H, dqk, dv, int(num_blocks), mode, _ptr(q), _ptr(k), _ptr(v), _ptr(ip),
+        _ptr(fp), _ptr(op), _ptr(bs), _ptr(C), _ptr(nn), _ptr(m), _ptr(h))
     if rc != 0:
         raise ValueError("oracle_mlstm_step failed with %d" % rc)
+    if mode == 2:
+        n.reshape(B, H)[...] = nn[:, :, 0]
     return h
 
 

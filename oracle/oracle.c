@@ -62,7 +62,17 @@ static double sigmoid(double x) {
  * S: [nb][dqkb][dvb]; n: [dqk]; *m: scalar.  Writes h[dv].
  * shift: extra amount added to the stabiliser after the max rule (0 for the
  * plain oracle; the shift-invariance test passes non-zero values).
- * normalise == 0 gives the retention special case h = o * S~^T q.
+ * normalise selects the normaliser:
+ *   0  none: the retention special case h = o * S~^T q;
+ *   1  vector n~ = f' n~ + i' k, denominator |n~ . q + bias e^{-m}| per head
+ *      (the reading used throughout);
+ *   2  scalar n~ = f' n~ + i' kept in n[0], denominator |n~ + bias e^{-m}|:
+ *      the normaliser exactly as the "Edifice.Recurrent.XLSTMv2" page prints
+ *      it in "Key Improvements over xLSTM v1", item 2 (no k, no q);
+ *   3  vector n~ as in 1, but each memory block divides by its own
+ *      |n~_beta . q_beta + bias e^{-m}| (a per-block normaliser for the
+ *      block-diagonal memory of item 1).
+ * The floor max(., e^{-m}) is the page's max(., 1) in stabilised units.
  */
 static void cell_step(int dqk, int dv, int nb, const double* q, const double* k,
                       const double* v, double i_pre, double f_pre,
@@ -84,16 +94,25 @@ static void cell_step(int dqk, int dv, int nb, const double* q, const double* k,
       for (int c = 0; c < dvb; ++c)
         Sb[(size_t)r * dvb + c] = fdec * Sb[(size_t)r * dvb + c] + iw * kb[r] * vb[c];
   }
-  /* n~ = f' n~ + i' k (full head). */
-  for (int r = 0; r < dqk; ++r) n[r] = fdec * n[r] + iw * k[r];
+  /* n~ = f' n~ + i' k (full head), or the scalar n~ = f' n~ + i'. */
+  if (normalise == 2) n[0] = fdec * n[0] + iw;
+  else
+    for (int r = 0; r < dqk; ++r) n[r] = fdec * n[r] + iw * k[r];
   /* Readout with the updated state: num_beta = S~_beta^T q_beta. */
   double den = 0.0;
-  for (int r = 0; r < dqk; ++r) den += n[r] * q[r];
+  if (normalise == 2) den = n[0];
+  else
+    for (int r = 0; r < dqk; ++r) den += n[r] * q[r];
   const double floor_ = exp(-m_new);
-  const double denom = fmax(fabs(den + bias * floor_), floor_);
+  double denom = fmax(fabs(den + bias * floor_), floor_);
   for (int b = 0; b < nb; ++b) {
     const double* Sb = S + (size_t)b * dqkb * dvb;
     const double* qb = q + (size_t)b * dqkb;
+    if (normalise == 3) {
+      double db = 0.0;
+      for (int r = 0; r < dqkb; ++r) db += n[(size_t)b * dqkb + r] * qb[r];
+      denom = fmax(fabs(db + bias * floor_), floor_);
+    }
     for (int c = 0; c < dvb; ++c) {
       double num = 0.0;
       for (int r = 0; r < dqkb; ++r) num += Sb[(size_t)r * dvb + c] * qb[r];
@@ -169,7 +188,7 @@ int oracle_mlstm_fwd(int B, int H, int T, int dqk, int dv, int nb, int normalise
  * (the in-place carried state of the burn-gdn2 Gdn2Mode::FusedRecurrent doc).
  * q,k [B,H,dqk]; v,o_pre,h [B,H,dv]; i_pre,f_pre [B,H]; C,n,m as above.
  */
-int oracle_mlstm_step(int B, int H, int dqk, int dv, int nb,
+int oracle_mlstm_step(int B, int H, int dqk, int dv, int nb, int normalise,
                       const double* q, const double* k, const double* v,
                       const double* i_pre, const double* f_pre,
                       const double* o_pre, const double* bias, double* C,
@@ -183,7 +202,7 @@ int oracle_mlstm_step(int B, int H, int dqk, int dv, int nb,
     const int hd = (int)(bh % H);
     cell_step(dqk, dv, nb, q + bh * dqk, k + bh * dqk, v + bh * dv, i_pre[bh],
               f_pre[bh], o_pre ? o_pre + bh * dv : NULL, bias ? bias[hd] : 0.0,
-              1, 0.0, C + bh * csz, n + bh * dqk, m + bh, h + bh * dv);
+              normalise, 0.0, C + bh * csz, n + bh * dqk, m + bh, h + bh * dv);
   }
   return 0;
 }

@@ -346,3 +346,95 @@ def test_pin_groupnorm_row_moments():
     var = y.var(axis=3)
     assert np.max(np.abs(out.mean(axis=3))) < 1e-12
     assert np.max(np.abs(out.var(axis=3) - var / (var + eps))) < 1e-12
+
+
+# ------------------------------------------- alternative normaliser readings
+def direct_unstabilised_scalar(q, k, v, ip, fp, op, bs, nb):
+    """The XLSTMv2 page's printed normaliser: scalar n_t = f n + i, readout
+    h_t = o * C q / max(|n + bias|, 1), no stabiliser."""
+    B, H, T, dqk = q.shape
+    dv = v.shape[-1]
+    dqb, dvb = dqk // nb, dv // nb
+    mask = (np.arange(dv)[:, None] // dvb) == (np.arange(dqk)[None, :] // dqb)
+    h = np.zeros((B, H, T, dv))
+    for b in range(B):
+        for hd in range(H):
+            C = np.zeros((dv, dqk))
+            n = 0.0
+            for t in range(T):
+                f = 1.0 / (1.0 + np.exp(-fp[b, hd, t]))
+                i = np.exp(ip[b, hd, t])
+                C = f * C + i * np.outer(v[b, hd, t], k[b, hd, t]) * mask
+                n = f * n + i
+                o = 1.0 if op is None else 1.0 / (1.0 + np.exp(-op[b, hd, t]))
+                h[b, hd, t] = o * (C @ q[b, hd, t]) / max(abs(n + bs_val(bs, hd)), 1.0)
+    return h
+
+
+@pytest.mark.parametrize("nb", [1, 2])
+def test_pin_scalar_normaliser_unstabilised(nb):
+    """Scalar normaliser: the stabilised oracle against the direct
+    recurrence without a stabiliser (T = 60 does not overflow)."""
+    rng = RNG(70 + nb)
+    q, k, v, ip, fp, op, bs = _inputs(rng, 1, 3, 60, 8, 12)
+    h, C, n, m = oracle.mlstm_fwd(q, k, v, ip, fp, op, bs, num_blocks=nb, norm_mode="scalar")
+    assert n.shape == (1, 3)
+    assert _relerr(h, direct_unstabilised_scalar(q, k, v, ip, fp, op, bs, nb)) < 1e-11
+
+
+def test_pin_scalar_normaliser_running_mean():
+    """f = 1, i = 1 (f_pre large, i_pre = 0): n_t = t + 1, so with bias b the
+    output is the causal sum of (q_t . k_s) v_s divided by max(|t + 1 + b|, 1)."""
+    rng = RNG(77)
+    B, H, T, d = 1, 2, 30, 6
+    q, k, v = (rng.standard_normal((B, H, T, d)) for _ in range(3))
+    ip = np.zeros((B, H, T))
+    fp = np.full((B, H, T), 50.0)  # sigmoid(50) = 1 - 2e-22
+    bs = np.array([-3.5, 0.25])
+    h, *_ = oracle.mlstm_fwd(q, k, v, ip, fp, None, bs, norm_mode="scalar")
+    for hd in range(H):
+        S = np.tril(q[0, hd] @ k[0, hd].T) @ v[0, hd]
+        den = np.maximum(np.abs(np.arange(1, T + 1) + bs[hd]), 1.0)
+        assert _relerr(h[0, hd], S / den[:, None]) < 1e-12
+
+
+def test_pin_scalar_normaliser_state_carry():
+    """Scalar normaliser: a split run carrying (C, n, m) equals one run, and
+    the decode step equals the sequence form token by token."""
+    rng = RNG(78)
+    q, k, v, ip, fp, op, bs = _inputs(rng, 2, 2, 41, 8, 8)
+    h, C, n, m = oracle.mlstm_fwd(q, k, v, ip, fp, op, bs, norm_mode="scalar")
+    a = lambda x, s: None if x is None else x[:, :, s]
+    h1, C1, n1, m1 = oracle.mlstm_fwd(*(a(x, slice(0, 17)) for x in (q, k, v, ip, fp, op)), bs,
+                                      norm_mode="scalar")
+    h2, C2, n2, m2 = oracle.mlstm_fwd(*(a(x, slice(17, None)) for x in (q, k, v, ip, fp, op)), bs,
+                                      C1, n1, m1, norm_mode="scalar")
+    assert _relerr(np.concatenate([h1, h2], axis=2), h) < 1e-12
+    assert _relerr(C2, C) < 1e-12 and _relerr(n2, n) < 1e-12 and _relerr(m2, m) < 1e-12
+    Cs, ns, ms = np.zeros_like(C), np.zeros_like(n), np.zeros_like(m)
+    for t in range(q.shape[2]):
+        ht = oracle.mlstm_step(q[:, :, t], k[:, :, t], v[:, :, t], ip[:, :, t], fp[:, :, t], Cs, ns, ms,
+                               op[:, :, t], bs, norm_mode="scalar")
+        assert _relerr(ht, h[:, :, t]) < 1e-12
+    assert _relerr(ns, n) < 1e-12
+
+
+@pytest.mark.parametrize("nb", [2, 4])
+def test_pin_block_normaliser_is_independent_cells(nb):
+    """Per-block normaliser: block beta of the output, state and normaliser
+    equals a stand-alone single-block cell on the beta slices of q, k, v (the
+    same gates); with one block it is the vector normaliser."""
+    rng = RNG(80 + nb)
+    dqk, dv = 16, 8
+    q, k, v, ip, fp, op, bs = _inputs(rng, 1, 2, 33, dqk, dv)
+    h, C, n, m = oracle.mlstm_fwd(q, k, v, ip, fp, op, bs, num_blocks=nb, norm_mode="block")
+    dqb, dvb = dqk // nb, dv // nb
+    for be in range(nb):
+        rs, cs = slice(be * dqb, (be + 1) * dqb), slice(be * dvb, (be + 1) * dvb)
+        hb, Cb, nbk, mb = oracle.mlstm_fwd(q[..., rs], k[..., rs], v[..., cs], ip, fp, op[..., cs], bs)
+        assert _relerr(h[..., cs], hb) < 1e-12
+        assert _relerr(C[:, :, be], Cb[:, :, 0]) < 1e-12
+        assert _relerr(n[..., rs], nbk) < 1e-12 and _relerr(m, mb) < 1e-12
+    h1, *_ = oracle.mlstm_fwd(q, k, v, ip, fp, op, bs, norm_mode="block")
+    h0, *_ = oracle.mlstm_fwd(q, k, v, ip, fp, op, bs)
+    assert _relerr(h1, h0) == 0.0
