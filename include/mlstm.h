@@ -124,6 +124,34 @@ int mlstm_chunkwise_fwd(int B, int H, int T, int d_qk, int d_v, int num_blocks,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Normaliser readings (norm_mode of the _ex entry points).
+ *   MLSTM_NORM_VECTOR  n_t = f n + i k_t, denominator |n_t . q_t + bias| (the
+ *                      reading of every other entry point);
+ *   MLSTM_NORM_SCALAR  n_t = f n + i (one scalar per head), denominator
+ *                      |n_t + bias|: the normaliser exactly as the
+ *                      "Edifice.Recurrent.XLSTMv2" page prints it in "Key
+ *                      Improvements over xLSTM v1", item 2 (no k, no q).
+ * Both take max(., 1) as on that page (in stabilised units).
+ */
+#define MLSTM_NORM_VECTOR 0
+#define MLSTM_NORM_SCALAR 1
+
+/*
+ * mlstm_chunkwise_fwd with a choice of normaliser.  With MLSTM_NORM_SCALAR
+ * n0 and n_out are [B,H] fp32 (one value per head); everything else, the
+ * supported shapes and the workspace size are those of mlstm_chunkwise_fwd.
+ * Unknown modes return MLSTM_E_UNSUPPORTED.
+ */
+int mlstm_chunkwise_fwd_ex(int B, int H, int T, int d_qk, int d_v, int num_blocks,
+                           int chunk, mlstm_dtype dt, int norm_mode,
+                           const void* q, const void* k, const void* v,
+                           const void* i_pre, const void* f_pre,
+                           const void* o_pre, const float* norm_bias,
+                           const float* C0, const float* n0, const float* m0,
+                           float* C_out, float* n_out, float* m_out, void* h,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Fused single-token decode step on every (b, h); the fp32 state is updated
  * IN PLACE and the readout uses the updated state.
  *   q, k  [B,H,d_qk]; v [B,H,d_v]; i_pre, f_pre [B,H]; o_pre [B,H,d_v] or
@@ -138,6 +166,17 @@ int mlstm_step(int B, int H, int d_qk, int d_v, int num_blocks, mlstm_dtype dt,
                const void* q, const void* k, const void* v, const void* i_pre,
                const void* f_pre, const void* o_pre, const float* norm_bias,
                float* C, float* n, float* m, void* h, void* stream);
+
+/*
+ * mlstm_step with a choice of normaliser (see MLSTM_NORM_*).  With
+ * MLSTM_NORM_SCALAR n is [B,H] fp32.  Unknown modes return
+ * MLSTM_E_UNSUPPORTED.
+ */
+int mlstm_step_ex(int B, int H, int d_qk, int d_v, int num_blocks, mlstm_dtype dt,
+                  int norm_mode, const void* q, const void* k, const void* v,
+                  const void* i_pre, const void* f_pre, const void* o_pre,
+                  const float* norm_bias, float* C, float* n, float* m,
+                  void* h, void* stream);
 
 /* Workspace size in bytes for retention_chunkwise_fwd (0 if none). */
 size_t retention_chunkwise_workspace_bytes(int B, int H, int T, int d_k,

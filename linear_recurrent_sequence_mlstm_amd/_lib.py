@@ -23,7 +23,8 @@ _DT = {torch.float32: F32, torch.bfloat16: BF16}
 # Every symbol declared in include/mlstm.h.
 EXPORTS = ("mlstm_abi_version", "mlstm_last_error", "mlstm_set_profile_events",
            "mlstm_chunkwise_workspace_bytes",
-           "mlstm_chunkwise_fwd", "mlstm_step", "retention_chunkwise_workspace_bytes",
+           "mlstm_chunkwise_fwd", "mlstm_chunkwise_fwd_ex", "mlstm_step", "mlstm_step_ex",
+           "retention_chunkwise_workspace_bytes",
            "retention_chunkwise_fwd", "retention_chunkwise_groupnorm_fwd", "retention_step")
 
 
@@ -53,6 +54,10 @@ def lib():
     L.mlstm_chunkwise_fwd.restype = i
     L.mlstm_step.argtypes = [i] * 6 + [vp] * 6 + [fp] * 4 + [vp, vp]
     L.mlstm_step.restype = i
+    L.mlstm_chunkwise_fwd_ex.argtypes = [i] * 9 + [vp] * 6 + [fp] * 7 + [vp, vp, sz, vp]
+    L.mlstm_chunkwise_fwd_ex.restype = i
+    L.mlstm_step_ex.argtypes = [i] * 7 + [vp] * 6 + [fp] * 4 + [vp, vp]
+    L.mlstm_step_ex.restype = i
     L.retention_chunkwise_workspace_bytes.argtypes = [i] * 6 + [i]
     L.retention_chunkwise_workspace_bytes.restype = sz
     L.retention_chunkwise_fwd.argtypes = [i] * 7 + [vp] * 3 + [fp] * 3 + [vp, vp, sz, vp]
@@ -129,12 +134,18 @@ def _workspace(nbytes, device, workspace):
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
+# normaliser readings of the _ex entry points (MLSTM_NORM_* in mlstm.h)
+NORM_MODES = {"vector": 0, "scalar": 1}
+
+
 def chunkwise_fwd(q, k, v, i_pre, f_pre, o_pre=None, bias=None, state=None, num_blocks=1,
-                  chunk=64, return_state=True, h=None, state_out=None, workspace=None):
-    """mlstm_chunkwise_fwd.  q,k [B,H,T,dqk]; v [B,H,T,dv]; i_pre,f_pre [B,H,T];
+                  chunk=64, return_state=True, h=None, state_out=None, workspace=None,
+                  norm_mode="vector"):
+    """mlstm_chunkwise_fwd(_ex).  q,k [B,H,T,dqk]; v [B,H,T,dv]; i_pre,f_pre [B,H,T];
     o_pre [B,H,T,dv] or None (all of one dtype, on one GPU); bias [H] fp32;
-    state = (C0 [B,H,nb,dqk/nb,dv/nb], n0 [B,H,dqk], m0 [B,H]) fp32 or None.
-    Returns (h, (C, n, m)) or (h, None)."""
+    state = (C0 [B,H,nb,dqk/nb,dv/nb], n0 [B,H,dqk] ([B,H] for norm_mode
+    "scalar"), m0 [B,H]) fp32 or None.  Returns (h, (C, n, m)) or (h, None)."""
+    mode = NORM_MODES[norm_mode]
     B, H, T, dqk = q.shape
     dv = v.shape[-1]
     nb = int(num_blocks)
@@ -148,7 +159,7 @@ def chunkwise_fwd(q, k, v, i_pre, f_pre, o_pre=None, bias=None, state=None, num_
     _need(o_pre, "o_pre", (B, H, T, dv), dt, dev)
     _need(bias, "bias", (H,), torch.float32, dev)
     _need(q, "q", (B, H, T, dqk), dt, dev)
-    sshape = ((B, H, nb, dqk // nb, dv // nb), (B, H, dqk), (B, H))
+    sshape = ((B, H, nb, dqk // nb, dv // nb), (B, H, dqk) if mode == 0 else (B, H), (B, H))
     C0 = n0 = m0 = None
     if state is not None:
         C0, n0, m0 = state
@@ -173,17 +184,20 @@ def chunkwise_fwd(q, k, v, i_pre, f_pre, o_pre=None, bias=None, state=None, num_
         _check(L.mlstm_chunkwise_fwd(B, H, T, dqk, dv, nb, chunk, _DT[dt], *([None] * 13),
                                      None, None, 0, None), "mlstm_chunkwise_fwd")
     ws = _workspace(nbytes, dev, workspace)
-    rc = L.mlstm_chunkwise_fwd(B, H, T, dqk, dv, nb, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v),
-                               _ptr(i_pre), _ptr(f_pre), _ptr(o_pre), _ptr(bias), _ptr(C0), _ptr(n0),
-                               _ptr(m0), _ptr(Co), _ptr(no), _ptr(mo), _ptr(h), _ptr(ws),
-                               ws.numel(), _stream(dev))
-    _check(rc, "mlstm_chunkwise_fwd")
+    rc = L.mlstm_chunkwise_fwd_ex(B, H, T, dqk, dv, nb, chunk, _DT[dt], mode, _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(i_pre), _ptr(f_pre), _ptr(o_pre), _ptr(bias), _ptr(C0), _ptr(n0),
+                                  _ptr(m0), _ptr(Co), _ptr(no), _ptr(mo), _ptr(h), _ptr(ws),
+                                  ws.numel(), _stream(dev))
+    _check(rc, "mlstm_chunkwise_fwd_ex")
     return h, ((Co, no, mo) if return_state else None)
 
 
-def step(q, k, v, i_pre, f_pre, C, n, m, o_pre=None, bias=None, num_blocks=1, h=None):
-    """mlstm_step: one token per (b,h); C [B,H,nb,dqk/nb,dv/nb], n [B,H,dqk],
-    m [B,H] fp32 are updated in place.  Returns h [B,H,dv]."""
+def step(q, k, v, i_pre, f_pre, C, n, m, o_pre=None, bias=None, num_blocks=1, h=None,
+         norm_mode="vector"):
+    """mlstm_step(_ex): one token per (b,h); C [B,H,nb,dqk/nb,dv/nb], n [B,H,dqk]
+    ([B,H] for norm_mode "scalar"), m [B,H] fp32 are updated in place.
+    Returns h [B,H,dv]."""
+    mode = NORM_MODES[norm_mode]
     B, H, dqk = q.shape
     dv = v.shape[-1]
     nb = int(num_blocks)
@@ -197,15 +211,15 @@ def step(q, k, v, i_pre, f_pre, C, n, m, o_pre=None, bias=None, num_blocks=1, h=
     _need(o_pre, "o_pre", (B, H, dv), dt, dev)
     _need(bias, "bias", (H,), torch.float32, dev)
     _need(C, "C", (B, H, nb, dqk // nb, dv // nb), torch.float32, dev)
-    _need(n, "n", (B, H, dqk), torch.float32, dev)
+    _need(n, "n", (B, H, dqk) if mode == 0 else (B, H), torch.float32, dev)
     _need(m, "m", (B, H), torch.float32, dev)
     if h is None:
         h = torch.empty(B, H, dv, dtype=dt, device=dev)
     _need(h, "h", (B, H, dv), dt, dev)
-    rc = lib().mlstm_step(B, H, dqk, dv, nb, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre),
-                          _ptr(f_pre), _ptr(o_pre), _ptr(bias), _ptr(C), _ptr(n), _ptr(m), _ptr(h),
-                          _stream(dev))
-    _check(rc, "mlstm_step")
+    rc = lib().mlstm_step_ex(B, H, dqk, dv, nb, _DT[dt], mode, _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre),
+                             _ptr(f_pre), _ptr(o_pre), _ptr(bias), _ptr(C), _ptr(n), _ptr(m), _ptr(h),
+                             _stream(dev))
+    _check(rc, "mlstm_step_ex")
     return h
 
 

@@ -154,11 +154,27 @@ int mlstm_chunkwise_fwd(int B, int H, int T, int d_qk, int d_v, int num_blocks, 
                         const void* o_pre, const float* norm_bias, const float* C0, const float* n0,
                         const float* m0, float* C_out, float* n_out, float* m_out, void* h, void* workspace,
                         size_t workspace_bytes, void* stream) {
+  return mlstm_chunkwise_fwd_ex(B, H, T, d_qk, d_v, num_blocks, chunk, dt, MLSTM_NORM_VECTOR, q, k, v, i_pre,
+                                f_pre, o_pre, norm_bias, C0, n0, m0, C_out, n_out, m_out, h, workspace,
+                                workspace_bytes, stream);
+}
+
+int mlstm_chunkwise_fwd_ex(int B, int H, int T, int d_qk, int d_v, int num_blocks, int chunk, mlstm_dtype dt,
+                           int norm_mode, const void* q, const void* k, const void* v, const void* i_pre,
+                           const void* f_pre, const void* o_pre, const float* norm_bias, const float* C0,
+                           const float* n0, const float* m0, float* C_out, float* n_out, float* m_out, void* h,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (norm_mode != MLSTM_NORM_VECTOR && norm_mode != MLSTM_NORM_SCALAR)
+    return fail(MLSTM_E_UNSUPPORTED, "unknown norm_mode %d", norm_mode);
   Plan pl;
   const int rc = plan_chunkwise(B, H, T, d_qk, d_v, num_blocks, chunk, dt, false, &pl);
   if (rc != MLSTM_OK) return rc;
   if (!q || !k || !v || !i_pre || !f_pre || !h)
     return fail(MLSTM_E_NULL, "q, k, v, i_pre, f_pre and h are required");
+  if (norm_mode == MLSTM_NORM_SCALAR) {
+    if (!pl.var.launch_scalar_norm) return fail(MLSTM_E_UNSUPPORTED, "no scalar-normaliser kernel");
+    pl.var.launch = pl.var.launch_scalar_norm;  // same plan and workspace
+  }
   mlstm::ChunkParams p{};
   p.B = B;
   p.H = H;
@@ -243,6 +259,15 @@ int retention_chunkwise_groupnorm_fwd(int B, int H, int T, int d_k, int d_v, int
 int mlstm_step(int B, int H, int d_qk, int d_v, int num_blocks, mlstm_dtype dt, const void* q, const void* k,
                const void* v, const void* i_pre, const void* f_pre, const void* o_pre, const float* norm_bias,
                float* C, float* n, float* m, void* h, void* stream) {
+  return mlstm_step_ex(B, H, d_qk, d_v, num_blocks, dt, MLSTM_NORM_VECTOR, q, k, v, i_pre, f_pre, o_pre,
+                       norm_bias, C, n, m, h, stream);
+}
+
+int mlstm_step_ex(int B, int H, int d_qk, int d_v, int num_blocks, mlstm_dtype dt, int norm_mode, const void* q,
+                  const void* k, const void* v, const void* i_pre, const void* f_pre, const void* o_pre,
+                  const float* norm_bias, float* C, float* n, float* m, void* h, void* stream) {
+  if (norm_mode != MLSTM_NORM_VECTOR && norm_mode != MLSTM_NORM_SCALAR)
+    return fail(MLSTM_E_UNSUPPORTED, "unknown norm_mode %d", norm_mode);
   if (dt != MLSTM_F32 && dt != MLSTM_BF16) return fail(MLSTM_E_DTYPE, "unknown dtype %d", dt);
   if (B < 1 || H < 1 || d_qk < 1 || d_v < 1 || num_blocks < 1)
     return fail(MLSTM_E_SHAPE, "sizes must be positive");
@@ -271,7 +296,7 @@ int mlstm_step(int B, int H, int d_qk, int d_v, int num_blocks, mlstm_dtype dt, 
   p.n = n;
   p.m = m;
   p.h = h;
-  const hipError_t e = mlstm::launch_step(dt, p, static_cast<hipStream_t>(stream));
+  const hipError_t e = mlstm::launch_step(dt, p, static_cast<hipStream_t>(stream), norm_mode == MLSTM_NORM_SCALAR);
   if (e != hipSuccess) return fail(MLSTM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

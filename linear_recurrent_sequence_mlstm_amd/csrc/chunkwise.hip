@@ -249,7 +249,10 @@ __device__ __forceinline__ float frag_rows(const float* tile, int RS, int kb0, i
 // the token tiles and the two partial sums meet in LDS (sX).
 // Q, K and V are staged token-major with plain 16-byte copies; the operands
 // that run along tokens (K^T and V^T) are read with transposing LDS reads.
-template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET, bool HAS_O, bool GN = false>
+// SN: the scalar normaliser n~ = f' n~ + i' (kept in n~[0], the other
+// entries zero), denominator |n~ + bias 2^{-m}| instead of |n~ . q + ...|.
+template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET, bool HAS_O, bool GN = false,
+          bool SN = false>
 __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   using C = ChunkCfg<T, DQK, NB, WC, NRG, NCG, L, GN>;
   using M = Mma<T>;
@@ -262,6 +265,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   constexpr unsigned ES = sizeof(T);
   constexpr bool XCH = NRG > 1;
   constexpr bool BF = sizeof(T) == 2;
+  constexpr bool VN = !RET && !SN;  // vector normaliser
 
   __shared__ __attribute__((aligned(16))) T sK[L * KST];  // K, token-major
   __shared__ __attribute__((aligned(16))) T sV[L * VS];   // V slice, token-major
@@ -652,7 +656,11 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               x[i] = pt[u][be][i] * fac[u][i];
-              dsum += x[i];
+              if constexpr (SN) {
+                if (be == 0) dsum += fac[u][i];  // the decay weights alone
+              } else {
+                dsum += x[i];
+              }
             }
             store4f(&sP[(be * L + j) * PS + kpos4<T>(lt[u] * 16 + 4 * lg)], x[0], x[1], x[2], x[3]);
           }
@@ -678,15 +686,18 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
             scores(std::integral_constant<int, 1>{}, wnc);
           }
         };
-        if constexpr (!RET && C::FUSED_NQ) {
+        if constexpr (VN && C::FUSED_NQ) {
           if (w < NJT) run(std::true_type{});  // first tile (0, w): query tile w
           else run(std::false_type{});
         } else {
           run(std::false_type{});
         }
       }
+      if constexpr (SN) {  // the inter part of the denominator is n~ itself
+        if (w == NW - 1 && lane < L) sDenInter[lane] = sNf[0];
+      }
       // n~ . q_j per query tile in a loop of its own (several memory blocks)
-      if constexpr (!RET && !C::FUSED_NQ) {
+      if constexpr (VN && !C::FUSED_NQ) {
 #pragma unroll
         for (int jt = 0; jt < NJT; ++jt) {
           if (w == NW - 1 - (jt % NW)) {
@@ -847,7 +858,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
       // update carry every feature of k: each is summed by one wave (tile nt
       // goes to column group nt % 4).  With several blocks a work-group's waves
       // need not cover all blocks, so a plain loop over sK does it.
-      constexpr bool NFRAG = !RET && NB == 1;
+      constexpr bool NFRAG = VN && NB == 1;
 #pragma unroll
       for (int kb = 0; kb < NKL; ++kb) {
 #pragma unroll
@@ -859,11 +870,19 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
           if ((nt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if constexpr (!RET && !NFRAG) {
+      if constexpr (VN && !NFRAG) {
         for (int r = tid; r < DQK; r += NTH) {
           float x = alpha * sNf[r];
           for (int l = 0; l < L; ++l) x += sW[l] * to_f32(sK[l * KST + r]);
           put_n(r, x);
+        }
+      }
+      if constexpr (SN) {  // n~ <- alpha n~ + sum_l w_l, summed by the last wave
+        if (w == NW - 1) {
+          float x = lane < L ? sW[lane] : 0.f;
+#pragma unroll
+          for (int d = 32; d > 0; d >>= 1) x += __shfl_xor(x, d, 64);
+          if (lane == 0) put_n(0, alpha * sNf[0] + x);
         }
       }
       if constexpr (NFRAG) {
@@ -927,8 +946,13 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   }
   if (slice == 0 && sc == p.NS - 1) {
     if constexpr (!RET) {
-      if (p.n_out)
-        for (int r = tid; r < DQK; r += NTH) p.n_out[(size_t)bh * DQK + r] = sNf[r];
+      if (p.n_out) {
+        if constexpr (SN) {
+          if (tid == 0) p.n_out[bh] = sNf[0];
+        } else {
+          for (int r = tid; r < DQK; r += NTH) p.n_out[(size_t)bh * DQK + r] = sNf[r];
+        }
+      }
     }
     if (tid == 0 && p.m_out) p.m_out[bh] = m_prev * kLn2;
   }
@@ -1172,7 +1196,8 @@ __device__ __forceinline__ bf16x8 scale_frag8(bf16x8 x, const float (&w)[8]) { r
 // NB = 1 < NBS (blocks narrower than 64 rows) a tile spans the whole head,
 // its product covers every block pair, and only the diagonal blocks are
 // stored (the off-diagonal MFMA work is cheaper than tiles of 32 rows).
-template <typename T, int DQK, int NB, int TR, int TC, int L, bool RET, int NWP, int NBS = NB>
+// SN: scalar normaliser, dn = sum_t w_t in dn[0] (the other entries zero).
+template <typename T, int DQK, int NB, int TR, int TC, int L, bool RET, int NWP, int NBS = NB, bool SN = false>
 __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
   static_assert(NBS == NB || NB == 1, "whole-head tiles store several blocks");
   constexpr int KS = sizeof(T) == 2 ? 32 : 16;
@@ -1350,7 +1375,7 @@ __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NTc; ++nt) acc[mt][nt] = M::mma(f.af[kb][mt], f.bf[kb][nt], acc[mt][nt]);
-    if constexpr (!RET) {
+    if constexpr (!RET && !SN) {
 #pragma unroll
       for (int kb = 0; kb < NKL; ++kb)
 #pragma unroll
@@ -1421,12 +1446,31 @@ __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
             dst[(size_t)bs * RB * DVS + (size_t)(r - bs * RB) * DVS + (cl - bs * DVS)] = acc[mt][nt][i];
         }
       }
-  if constexpr (!RET) {
+  if constexpr (!RET && !SN) {
     if (do_dn && lr == 0) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) dst[CS + f0 + wr * (TR / WR) + mt * 16 + 4 * lg + i] = dacc[mt][i];
+    }
+  }
+  if constexpr (SN) {
+    // the scalar sum_t w_t (w of the whole superchunk sits in LDS, zero past
+    // its end) into dn[0], zeros in this tile's other dn rows
+    float ws = 0.f;
+    if (do_dn && f0 == 0 && wr == 0) {
+      for (int t = lane; t < C::GLMAX; t += 64) ws += sw[t];
+#pragma unroll
+      for (int d = 32; d > 0; d >>= 1) ws += __shfl_xor(ws, d, 64);
+    }
+    if (do_dn && lr == 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = f0 + wr * (TR / WR) + mt * 16 + 4 * lg + i;
+          dst[CS + r] = r == 0 ? ws : 0.f;
+        }
     }
   }
 }
@@ -1450,6 +1494,7 @@ __global__ __launch_bounds__(256) void superchunk_scan_kernel(ScanParams p) {
     for (int i = 0; i < 4; ++i) {
       const size_t e = e0 + i;
       if (e < p.CS) x[i] = p.C0 ? p.C0[(size_t)bh * p.CS + e] : 0.f;
+      else if (p.scalar_n) x[i] = (p.n0 && e == p.CS) ? p.n0[bh] : 0.f;  // n0 [B,H]
       else x[i] = p.n0 ? p.n0[(size_t)bh * p.DQK + (e - p.CS)] : 0.f;
     }
     S = make_float4(x[0], x[1], x[2], x[3]);
@@ -1498,7 +1543,7 @@ size_t chunk_lds_bytes() {
   return ChunkCfg<T, DQK, NB, WC, NRG, NCG, L, GN>::lds_bytes(RET);
 }
 
-template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET, bool GN>
+template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET, bool GN, bool SN = false>
 hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   constexpr int NTH = 64 * NCG * NRG;
   const int BH = p.B * p.H;
@@ -1524,11 +1569,11 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
     const dim3 g1((unsigned)(BH * (p.NS - 1) * NBC * (DQKB / TR) * (DVB / TC) + BH * p.NS));
     const dim3 b1(64 * NWP);
     if (TC == TCAP)
-      hipLaunchKernelGGL((local_state_kernel<T, DQK, NBC, TR, TCAP, L, RET, NWP, NB>), g1, b1, 0, stream, p);
+      hipLaunchKernelGGL((local_state_kernel<T, DQK, NBC, TR, TCAP, L, RET, NWP, NB, SN>), g1, b1, 0, stream, p);
     else if (TC == 64)
-      hipLaunchKernelGGL((local_state_kernel<T, DQK, NBC, TR, 64, L, RET, NWP, NB>), g1, b1, 0, stream, p);
+      hipLaunchKernelGGL((local_state_kernel<T, DQK, NBC, TR, 64, L, RET, NWP, NB, SN>), g1, b1, 0, stream, p);
     else
-      hipLaunchKernelGGL((local_state_kernel<T, DQK, NBC, TR, 32, L, RET, NWP, NB>), g1, b1, 0, stream, p);
+      hipLaunchKernelGGL((local_state_kernel<T, DQK, NBC, TR, 32, L, RET, NWP, NB, SN>), g1, b1, 0, stream, p);
   }
   ScanParams s;
   s.NS = p.NS;
@@ -1541,6 +1586,7 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
   s.C0 = p.C0;
   s.n0 = p.n0;
   s.m0 = p.m0;
+  s.scalar_n = SN ? 1 : 0;
   const size_t nstate = CS + (RET ? 0 : DQK);
   dim3 g2((unsigned)((nstate / 4 + 255) / 256), (unsigned)BH);
   hipLaunchKernelGGL((superchunk_scan_kernel<RET>), g2, dim3(256), 0, stream, s);
@@ -1549,9 +1595,11 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
   if constexpr (GN)
     hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, false, true>), g3, dim3(NTH), 0, stream, p);
   else if (!RET && p.o_pre)
-    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, !RET>), g3, dim3(NTH), 0, stream, p);
+    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, !RET, false, SN>), g3, dim3(NTH), 0, stream,
+                       p);
   else
-    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, false>), g3, dim3(NTH), 0, stream, p);
+    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, false, false, SN>), g3, dim3(NTH), 0,
+                       stream, p);
   const hipError_t e = hipGetLastError();
   if (ev1) (void)hipEventRecord(ev1, stream);
   return e;
@@ -1577,10 +1625,18 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
   X(__bf16, 128, 1, 32, 2, 4, 64, true)     \
   X(float, 64, 1, 16, 1, 4, 64, true)
 
+// the scalar-normaliser launcher of an mLSTM variant (none for retention)
+template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET>
+constexpr ChunkLaunchFn scalar_norm_launcher() {
+  if constexpr (RET) return nullptr;
+  else return &launch_chunkwise<T, DQK, NB, WC, NRG, NCG, L, RET, false, true>;
+}
+
 bool find_chunk_variant(int dtype, int dqk, int nb, int L, bool ret, ChunkVariant* out) {
 #define X(T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_)                                              \
   if (dtype == (sizeof(T_) == 2 ? 1 : 0) && dqk == DQK_ && nb == NB_ && L == L_ && ret == RET_) { \
     out->launch = &launch_chunkwise<T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_, false>;            \
+    out->launch_scalar_norm = scalar_norm_launcher<T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_>();  \
     out->lds_bytes = chunk_lds_bytes<T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_, false>();         \
     out->wc = WC_;                                                                               \
     out->w = NCG_ * WC_;                                                                         \
@@ -1599,6 +1655,7 @@ bool find_retention_groupnorm_variant(int dtype, int dqk, int L, ChunkVariant* o
 #define X(T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_)                                              \
   if (RET_ && dtype == (sizeof(T_) == 2 ? 1 : 0) && dqk == DQK_ && NB_ == 1 && L == L_) {        \
     out->launch = &launch_chunkwise<T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_, RET_>;             \
+    out->launch_scalar_norm = nullptr;                                                           \
     out->lds_bytes = chunk_lds_bytes<T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_, RET_>();          \
     out->wc = WC_;                                                                               \
     out->w = NCG_ * WC_;                                                                         \

@@ -49,6 +49,7 @@ struct ScanParams {
   const float* C0;
   const float* n0;
   const float* m0;
+  int scalar_n;  // n0 is [B,H] (scalar normaliser)
 };
 
 // ev0/ev1 (may be null) are recorded right before / after the main kernel.
@@ -56,6 +57,7 @@ typedef hipError_t (*ChunkLaunchFn)(ChunkParams, hipStream_t, hipEvent_t ev0, hi
 
 struct ChunkVariant {
   ChunkLaunchFn launch;
+  ChunkLaunchFn launch_scalar_norm;  // mLSTM with the scalar normaliser (null: none)
   size_t lds_bytes;
   int wc;  // d_v columns per wave
   int w;   // d_v columns per work-group (the d_v slice)
@@ -83,7 +85,8 @@ struct StepParams {
   const float* gamma;  // retention: [H] decay, or null for 1 - 2^(-5-h)
 };
 
-hipError_t launch_step(int dtype, const StepParams& p, hipStream_t stream);
+// scalar_norm: n is [B,H] and the denominator is |n~ + bias 2^{-m}|
+hipError_t launch_step(int dtype, const StepParams& p, hipStream_t stream, bool scalar_norm = false);
 // Retention decode: C is S [B,H,d_k,d_v]; q, k, v, h and gamma are read.
 hipError_t launch_retention_step(int dtype, const StepParams& p, hipStream_t stream);
 bool step_supported(int dqk, int dv, int nb);

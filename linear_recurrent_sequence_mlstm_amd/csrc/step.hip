@@ -57,7 +57,9 @@ __device__ __forceinline__ StepGates step_gates(const StepParams& p, int bh) {
   return s;
 }
 
-template <typename T, int RG, bool RET>
+// SN: the scalar normaliser n~ = f' n~ + i' (n [B,H]), denominator
+// |n~ + bias 2^{-m'}| (no k, no q).
+template <typename T, int RG, bool RET, bool SN = false>
 __global__ __launch_bounds__(512) void step_kernel(StepParams p, int WS) {
   extern __shared__ float smem[];
   const int DQK = p.DQK, DV = p.DV, NB = p.NB;
@@ -96,12 +98,12 @@ __global__ __launch_bounds__(512) void step_kernel(StepParams p, int WS) {
     const float qr = to_f32(q[r]), kr = to_f32(k[r]);
     sq[r] = qr;
     sk[r] = kr;
-    if constexpr (!RET) {
+    if constexpr (!RET && !SN) {
       nq += p.n[(size_t)bh * DQK + r] * qr;
       kq += kr * qr;
     }
   }
-  if constexpr (!RET) {
+  if constexpr (!RET && !SN) {
 #pragma unroll
     for (int d = 32; d > 0; d >>= 1) {
       nq += __shfl_xor(nq, d, 64);
@@ -163,9 +165,14 @@ __global__ __launch_bounds__(512) void step_kernel(StepParams p, int WS) {
       return;
     }
     float n_q = 0.f, k_q = 0.f;
-    for (int i = 0; i < nth / 64; ++i) {
-      n_q += sred[i];
-      k_q += sred[nth / 64 + i];
+    if constexpr (SN) {
+      n_q = p.n[bh];  // the old scalar n~; its new value is f' n~ + i'
+      k_q = 1.f;
+    } else {
+      for (int i = 0; i < nth / 64; ++i) {
+        n_q += sred[i];
+        k_q += sred[nth / 64 + i];
+      }
     }
     const float cl2 = exp2_fast(-gt.mn2);
     const float den = fdec * n_q + gt.iw * k_q + bias * cl2;  // n~' . q + bias 2^{-m'}
@@ -185,16 +192,16 @@ __global__ __launch_bounds__(512) void step_kernel(StepParams p, int WS) {
 // A work-group owns RPB = max(1, 256 / d_qk) whole rows (b, h), so every
 // reader of a row's m is in the work-group that rewrites it, after a barrier;
 // all loads of a thread are issued before any result is needed.
-template <typename T>
+template <typename T, bool SN = false>
 __global__ __launch_bounds__(256) void step_norm_kernel(StepParams p, int RPB) {
-  const int DQK = p.DQK, BH = p.B * p.H;
+  const int DQK = SN ? 1 : p.DQK, BH = p.B * p.H;  // normaliser entries per row
   const int bh0 = blockIdx.x * RPB;
   const int nrow = min(RPB, BH - bh0);
   for (int e = threadIdx.x; e < nrow * DQK; e += 256) {
     const int bh = bh0 + e / DQK;
     const size_t idx = (size_t)bh0 * DQK + e;
     const float nv = p.n[idx];
-    const float kv = to_f32(static_cast<const T*>(p.k)[idx]);
+    const float kv = SN ? 1.f : to_f32(static_cast<const T*>(p.k)[idx]);
     const StepGates gt = step_gates<T>(p, bh);
     p.n[idx] = gt.fdec * nv + gt.iw * kv;
   }
@@ -234,29 +241,33 @@ bool step_supported(int dqk, int dv, int nb) {
   return pick_rg(pick_ws(dv)) > 0;
 }
 
-template <typename T, bool RET>
+template <typename T, bool RET, bool SN = false>
 static hipError_t launch_rg(const StepParams& p, int ws, int rg, hipStream_t stream) {
   const int tpc = ws / 4;
   const dim3 grid((unsigned)(p.B * p.H * (p.DV / ws)));
   const dim3 block((unsigned)(tpc * rg));
   const size_t smem = ((size_t)2 * p.DQK + (size_t)rg * ws + 2 * 16) * sizeof(float);
   switch (rg) {
-    case 1: hipLaunchKernelGGL((step_kernel<T, 1, RET>), grid, block, smem, stream, p, ws); break;
-    case 2: hipLaunchKernelGGL((step_kernel<T, 2, RET>), grid, block, smem, stream, p, ws); break;
-    case 4: hipLaunchKernelGGL((step_kernel<T, 4, RET>), grid, block, smem, stream, p, ws); break;
-    case 8: hipLaunchKernelGGL((step_kernel<T, 8, RET>), grid, block, smem, stream, p, ws); break;
-    default: hipLaunchKernelGGL((step_kernel<T, 16, RET>), grid, block, smem, stream, p, ws); break;
+    case 1: hipLaunchKernelGGL((step_kernel<T, 1, RET, SN>), grid, block, smem, stream, p, ws); break;
+    case 2: hipLaunchKernelGGL((step_kernel<T, 2, RET, SN>), grid, block, smem, stream, p, ws); break;
+    case 4: hipLaunchKernelGGL((step_kernel<T, 4, RET, SN>), grid, block, smem, stream, p, ws); break;
+    case 8: hipLaunchKernelGGL((step_kernel<T, 8, RET, SN>), grid, block, smem, stream, p, ws); break;
+    default: hipLaunchKernelGGL((step_kernel<T, 16, RET, SN>), grid, block, smem, stream, p, ws); break;
   }
   if constexpr (RET) return hipGetLastError();  // no normaliser or stabiliser
-  const int rpb = p.DQK >= 256 ? 1 : 256 / p.DQK;
+  const int nent = SN ? 1 : p.DQK;  // normaliser entries per (b, h)
+  const int rpb = nent >= 256 ? 1 : 256 / nent;
   const int nwg = (p.B * p.H + rpb - 1) / rpb;
-  hipLaunchKernelGGL((step_norm_kernel<T>), dim3((unsigned)nwg), dim3(256), 0, stream, p, rpb);
+  hipLaunchKernelGGL((step_norm_kernel<T, SN>), dim3((unsigned)nwg), dim3(256), 0, stream, p, rpb);
   return hipGetLastError();
 }
 
-hipError_t launch_step(int dtype, const StepParams& p, hipStream_t stream) {
+hipError_t launch_step(int dtype, const StepParams& p, hipStream_t stream, bool scalar_norm) {
   const int ws = pick_ws(p.DV);
   const int rg = pick_rg(ws);
+  if (scalar_norm)
+    return dtype == 1 ? launch_rg<__bf16, false, true>(p, ws, rg, stream)
+                      : launch_rg<float, false, true>(p, ws, rg, stream);
   return dtype == 1 ? launch_rg<__bf16, false>(p, ws, rg, stream) : launch_rg<float, false>(p, ws, rg, stream);
 }
 

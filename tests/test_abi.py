@@ -60,6 +60,18 @@ def test_workspace_query():
     assert L.retention_chunkwise_workspace_bytes(8, 4, 2048, 64, 64, 64, 1) > 0
 
 
+def test_norm_mode_validation():
+    L = _lib.lib()
+    p = [BOGUS] * 6 + [None] * 7
+    assert L.mlstm_chunkwise_fwd_ex(1, 2, 64, 64, 64, 1, 64, 1, 7, *p, BOGUS, BOGUS, 1 << 30, None) == E_UNSUPPORTED
+    assert L.mlstm_chunkwise_fwd_ex(1, 2, 64, 64, 64, 1, 64, 1, 1, *p[:-1], None, None, BOGUS, 1 << 30,
+                                    None) == E_NULL
+    P0 = [BOGUS] * 6 + [None] + [BOGUS] * 3
+    assert L.mlstm_step_ex(1, 1, 64, 64, 1, 1, 9, *P0, BOGUS, None) == E_UNSUPPORTED
+    assert L.mlstm_step_ex(1, 1, 64, 60, 1, 1, 1, *P0, BOGUS, None) == E_UNSUPPORTED
+    assert _lib.last_error() != ""
+
+
 def test_step_validation():
     L = _lib.lib()
     P = [BOGUS] * 6 + [None] + [BOGUS] * 3 + [BOGUS, None]

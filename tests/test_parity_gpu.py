@@ -148,6 +148,67 @@ def test_chunkwise_deterministic_and_writes_every_output(gpu):
     assert torch.equal(outs[0], outs[1])
 
 
+# ------------------------------------------------- scalar normaliser reading
+@pytest.mark.parametrize("case", [
+    dict(B=1, H=2, T=300, dqk=256, dv=512, nb=1, dtype="bf16", f_mix=True, with_o=False, bias="uniform"),
+    dict(B=2, H=2, T=200, dqk=64, dv=64, nb=2, dtype="bf16", f_mix=True, with_o=True, bias="uniform"),
+    dict(B=1, H=3, T=100, dqk=64, dv=64, nb=1, dtype="f32", f_mix=False, with_o=True, bias="uniform"),
+])
+def test_chunkwise_scalar_normaliser(gpu, case):
+    """norm_mode "scalar" (the XLSTMv2 page's printed n = f n + i): outputs
+    and final (C, n, m) against the oracle's scalar mode, from an initial
+    state carried over from a first run."""
+    c = dict(case)
+    dt = c.pop("dtype")
+    x = mlstm_inputs(**c, dtype=dt, seed=41, k_scale=0.125)
+    T1 = c["T"] // 3
+    cut = lambda t, s: None if t is None else t[:, :, s].contiguous()
+    xa = type(x)(*(cut(t, slice(0, T1)) for t in (x.q, x.k, x.v, x.i_pre, x.f_pre, x.o_pre)), x.bias,
+                 x.num_blocks, x.chunk)
+    xb = type(x)(*(cut(t, slice(T1, None)) for t in (x.q, x.k, x.v, x.i_pre, x.f_pre, x.o_pre)), x.bias,
+                 x.num_blocks, x.chunk)
+    ga, gb = xa.to(gpu), xb.to(gpu)
+    ha, sta = mlstm.chunkwise_fwd(ga.q, ga.k, ga.v, ga.i_pre, ga.f_pre, ga.o_pre, ga.bias,
+                                  num_blocks=x.num_blocks, norm_mode="scalar")
+    assert tuple(sta[1].shape) == (x.q.shape[0], x.q.shape[1])
+    hb, stb = mlstm.chunkwise_fwd(gb.q, gb.k, gb.v, gb.i_pre, gb.f_pre, gb.o_pre, gb.bias, state=sta,
+                                  num_blocks=x.num_blocks, norm_mode="scalar")
+    torch.cuda.synchronize()
+    ref = oracle.mlstm_fwd(x.q, x.k, x.v, x.i_pre, x.f_pre, x.o_pre, x.bias, num_blocks=x.num_blocks,
+                           norm_mode="scalar")
+    tol = TOL[torch.bfloat16 if dt == "bf16" else torch.float32]
+    assert slice_err(np.concatenate([cpu(ha), cpu(hb)], axis=2), ref[0]) < tol
+    C, n, m = (cpu(t) for t in stb)
+    Cr, nr, mr = ref[1:]
+    assert np.max(np.abs(m - mr)) < 1e-4
+    sc = np.exp(m - mr)
+    assert slice_err(C * sc[:, :, None, None, None], Cr) < tol
+    assert np.max(np.abs(n * sc - nr) / np.maximum(np.abs(nr), 1e-30)) < tol
+
+
+def test_step_scalar_normaliser(gpu):
+    """Decode steps in scalar mode after a scalar-mode prefill equal one
+    oracle run over the whole sequence."""
+    B, H, T, T1, dqk, dv = 2, 3, 90, 60, 64, 128
+    x = mlstm_inputs(B, H, T, dqk, dv, dtype="bf16", seed=42, k_scale=0.125, with_o=True, bias="uniform")
+    g = x.to(gpu)
+    cut = lambda t: None if t is None else t[:, :, :T1].contiguous()
+    _, (C, n, m) = mlstm.chunkwise_fwd(*(cut(t) for t in (g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre)), g.bias,
+                                       norm_mode="scalar")
+    outs = []
+    for t in range(T1, T):
+        tok = lambda a: a[:, :, t].contiguous()
+        outs.append(cpu(mlstm.step(tok(g.q), tok(g.k), tok(g.v), tok(g.i_pre), tok(g.f_pre), C, n, m,
+                                   o_pre=tok(g.o_pre), bias=g.bias, norm_mode="scalar")))
+    torch.cuda.synchronize()
+    ref = oracle.mlstm_fwd(x.q, x.k, x.v, x.i_pre, x.f_pre, x.o_pre, x.bias, norm_mode="scalar")
+    assert slice_err(np.stack(outs, axis=2), ref[0][:, :, T1:]) < TOL[torch.bfloat16]
+    mm = cpu(m)
+    assert np.max(np.abs(mm - ref[3])) < 1e-4
+    nn_ = cpu(n) * np.exp(mm - ref[3])
+    assert np.max(np.abs(nn_ - ref[2]) / np.abs(ref[2])) < TOL[torch.bfloat16]
+
+
 # ------------------------------------------------------------ retention
 @pytest.mark.parametrize("T,with_state", [(2048, False), (700, True), (50, False)])
 def test_retention_bf16(gpu, T, with_state):
