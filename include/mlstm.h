@@ -130,11 +130,17 @@ int mlstm_chunkwise_fwd(int B, int H, int T, int d_qk, int d_v, int num_blocks,
  *   MLSTM_NORM_SCALAR  n_t = f n + i (one scalar per head), denominator
  *                      |n_t + bias|: the normaliser exactly as the
  *                      "Edifice.Recurrent.XLSTMv2" page prints it in "Key
- *                      Improvements over xLSTM v1", item 2 (no k, no q).
- * Both take max(., 1) as on that page (in stabilised units).
+ *                      Improvements over xLSTM v1", item 2 (no k, no q);
+ *   MLSTM_NORM_BLOCK   n_t as for VECTOR, but memory block b divides by its
+ *                      own |n_t,b . q_t,b + bias| over the block's features
+ *                      (the block-diagonal memory of item 1 read as
+ *                      independent cells; the same as VECTOR with one block;
+ *                      the decode step takes at most 8 blocks).
+ * All take max(., 1) as on that page (in stabilised units).
  */
 #define MLSTM_NORM_VECTOR 0
 #define MLSTM_NORM_SCALAR 1
+#define MLSTM_NORM_BLOCK 2
 
 /*
  * mlstm_chunkwise_fwd with a choice of normaliser.  With MLSTM_NORM_SCALAR

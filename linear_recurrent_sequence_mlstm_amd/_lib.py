@@ -135,7 +135,7 @@ def _workspace(nbytes, device, workspace):
 
 
 # normaliser readings of the _ex entry points (MLSTM_NORM_* in mlstm.h)
-NORM_MODES = {"vector": 0, "scalar": 1}
+NORM_MODES = {"vector": 0, "scalar": 1, "block": 2}
 
 
 def chunkwise_fwd(q, k, v, i_pre, f_pre, o_pre=None, bias=None, state=None, num_blocks=1,
@@ -159,7 +159,8 @@ def chunkwise_fwd(q, k, v, i_pre, f_pre, o_pre=None, bias=None, state=None, num_
     _need(o_pre, "o_pre", (B, H, T, dv), dt, dev)
     _need(bias, "bias", (H,), torch.float32, dev)
     _need(q, "q", (B, H, T, dqk), dt, dev)
-    sshape = ((B, H, nb, dqk // nb, dv // nb), (B, H, dqk) if mode == 0 else (B, H), (B, H))
+    scalar_n = mode == NORM_MODES["scalar"]  # n is [B,H] only for the scalar normaliser
+    sshape = ((B, H, nb, dqk // nb, dv // nb), (B, H) if scalar_n else (B, H, dqk), (B, H))
     C0 = n0 = m0 = None
     if state is not None:
         C0, n0, m0 = state
@@ -211,7 +212,7 @@ def step(q, k, v, i_pre, f_pre, C, n, m, o_pre=None, bias=None, num_blocks=1, h=
     _need(o_pre, "o_pre", (B, H, dv), dt, dev)
     _need(bias, "bias", (H,), torch.float32, dev)
     _need(C, "C", (B, H, nb, dqk // nb, dv // nb), torch.float32, dev)
-    _need(n, "n", (B, H, dqk) if mode == 0 else (B, H), torch.float32, dev)
+    _need(n, "n", (B, H) if mode == NORM_MODES["scalar"] else (B, H, dqk), torch.float32, dev)
     _need(m, "m", (B, H), torch.float32, dev)
     if h is None:
         h = torch.empty(B, H, dv, dtype=dt, device=dev)

@@ -164,7 +164,7 @@ int mlstm_chunkwise_fwd_ex(int B, int H, int T, int d_qk, int d_v, int num_block
                            const void* f_pre, const void* o_pre, const float* norm_bias, const float* C0,
                            const float* n0, const float* m0, float* C_out, float* n_out, float* m_out, void* h,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  if (norm_mode != MLSTM_NORM_VECTOR && norm_mode != MLSTM_NORM_SCALAR)
+  if (norm_mode != MLSTM_NORM_VECTOR && norm_mode != MLSTM_NORM_SCALAR && norm_mode != MLSTM_NORM_BLOCK)
     return fail(MLSTM_E_UNSUPPORTED, "unknown norm_mode %d", norm_mode);
   Plan pl;
   const int rc = plan_chunkwise(B, H, T, d_qk, d_v, num_blocks, chunk, dt, false, &pl);
@@ -174,6 +174,10 @@ int mlstm_chunkwise_fwd_ex(int B, int H, int T, int d_qk, int d_v, int num_block
   if (norm_mode == MLSTM_NORM_SCALAR) {
     if (!pl.var.launch_scalar_norm) return fail(MLSTM_E_UNSUPPORTED, "no scalar-normaliser kernel");
     pl.var.launch = pl.var.launch_scalar_norm;  // same plan and workspace
+  }
+  if (norm_mode == MLSTM_NORM_BLOCK && num_blocks > 1) {  // one block: the vector normaliser
+    if (!pl.var.launch_block_norm) return fail(MLSTM_E_UNSUPPORTED, "no per-block-normaliser kernel");
+    pl.var.launch = pl.var.launch_block_norm;
   }
   mlstm::ChunkParams p{};
   p.B = B;
@@ -266,8 +270,10 @@ int mlstm_step(int B, int H, int d_qk, int d_v, int num_blocks, mlstm_dtype dt, 
 int mlstm_step_ex(int B, int H, int d_qk, int d_v, int num_blocks, mlstm_dtype dt, int norm_mode, const void* q,
                   const void* k, const void* v, const void* i_pre, const void* f_pre, const void* o_pre,
                   const float* norm_bias, float* C, float* n, float* m, void* h, void* stream) {
-  if (norm_mode != MLSTM_NORM_VECTOR && norm_mode != MLSTM_NORM_SCALAR)
+  if (norm_mode != MLSTM_NORM_VECTOR && norm_mode != MLSTM_NORM_SCALAR && norm_mode != MLSTM_NORM_BLOCK)
     return fail(MLSTM_E_UNSUPPORTED, "unknown norm_mode %d", norm_mode);
+  if (norm_mode == MLSTM_NORM_BLOCK && num_blocks > 8)
+    return fail(MLSTM_E_UNSUPPORTED, "per-block normaliser decode supports at most 8 blocks (got %d)", num_blocks);
   if (dt != MLSTM_F32 && dt != MLSTM_BF16) return fail(MLSTM_E_DTYPE, "unknown dtype %d", dt);
   if (B < 1 || H < 1 || d_qk < 1 || d_v < 1 || num_blocks < 1)
     return fail(MLSTM_E_SHAPE, "sizes must be positive");
@@ -296,7 +302,7 @@ int mlstm_step_ex(int B, int H, int d_qk, int d_v, int num_blocks, mlstm_dtype d
   p.n = n;
   p.m = m;
   p.h = h;
-  const hipError_t e = mlstm::launch_step(dt, p, static_cast<hipStream_t>(stream), norm_mode == MLSTM_NORM_SCALAR);
+  const hipError_t e = mlstm::launch_step(dt, p, static_cast<hipStream_t>(stream), norm_mode);
   if (e != hipSuccess) return fail(MLSTM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

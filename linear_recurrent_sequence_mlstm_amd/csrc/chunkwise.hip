@@ -126,7 +126,7 @@ constexpr int lds_pad_res(int row_elems, int esize, int res) {
 #define MLSTM_P3_KRES 24
 #endif
 
-template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool GN = false>
+template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool GN = false, bool PB = false>
 struct ChunkCfg {
   static constexpr int K = Mma<T>::K;
   static constexpr int KL = Mma<T>::KL;
@@ -192,7 +192,7 @@ struct ChunkCfg {
     if (!ret) b += DQK * 4 + 2 * DQK * sizeof(T);  // n~
     b += (size_t)L * QS * sizeof(T);             // sQ
     b += (size_t)NB * L * PS * sizeof(T);        // sP
-    b += (size_t)(NJT + 1) * L * 4;              // den partials
+    b += (size_t)(PB ? NB : 1) * (NJT + 1) * L * 4;  // den partials
     if (NRG > 1) b += (size_t)NCG * NJT * CT * 64 * 16;  // readout exchange
     if (HST) b += (size_t)L * HS * sizeof(HT);   // sH
     return b;
@@ -251,10 +251,12 @@ __device__ __forceinline__ float frag_rows(const float* tile, int RS, int kb0, i
 // that run along tokens (K^T and V^T) are read with transposing LDS reads.
 // SN: the scalar normaliser n~ = f' n~ + i' (kept in n~[0], the other
 // entries zero), denominator |n~ + bias 2^{-m}| instead of |n~ . q + ...|.
+// PB: one denominator per memory block, |n~_b . q_b + ...| over the block's
+// features (NB > 1).
 template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET, bool HAS_O, bool GN = false,
-          bool SN = false>
+          bool SN = false, bool PB = false>
 __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
-  using C = ChunkCfg<T, DQK, NB, WC, NRG, NCG, L, GN>;
+  using C = ChunkCfg<T, DQK, NB, WC, NRG, NCG, L, GN, PB>;
   using M = Mma<T>;
   typedef typename M::frag frag;
   constexpr int K = C::K, KL = C::KL, DQKB = C::DQKB, NT = C::NT, CT = C::CT, NW = C::NW;
@@ -266,6 +268,8 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   constexpr bool XCH = NRG > 1;
   constexpr bool BF = sizeof(T) == 2;
   constexpr bool VN = !RET && !SN;  // vector normaliser
+  static_assert(!PB || (NB > 1 && VN), "per-block denominators need blocks and the vector normaliser");
+  constexpr int NDB = PB ? NB : 1;  // denominators per head
 
   __shared__ __attribute__((aligned(16))) T sK[L * KST];  // K, token-major
   __shared__ __attribute__((aligned(16))) T sV[L * VS];   // V slice, token-major
@@ -281,8 +285,8 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   // gate vectors, two sets: wave 0 fills the next chunk's while the other
   // waves still read the current chunk's
   __shared__ float sA2b[2][L], sM2b[2][L], sRSb[2][L], sCLb[2][L], sBTb[2][L], sWb[2][L];
-  __shared__ float sDenPart[NJT * L];
-  __shared__ float sDenInter[L];
+  __shared__ float sDenPart[NDB * NJT * L];
+  __shared__ float sDenInter[NDB * L];
   __shared__ float sAlphab[2];
 
   const int tid = threadIdx.x;
@@ -363,7 +367,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   }
   // masked (l > j) tiles of P and their den partials are never written
   for (int e = tid; e < NB * L * PS; e += NTH) sP[e] = from_f32<T>(0.f);
-  for (int e = tid; e < NJT * L; e += NTH) sDenPart[e] = 0.f;
+  for (int e = tid; e < NDB * NJT * L; e += NTH) sDenPart[e] = 0.f;
   // The registers hold S^ = S~ / 2^{sig}: the per-chunk decay of the state is
   // folded into sig (a wave-uniform scalar) instead of multiplying every
   // state element; new contributions are weighted by 2^{-sig}, the readout by
@@ -649,7 +653,9 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
           const int j = jt[u] * 16 + lr;
-          float dsum = 0.f;
+          float dsum[NDB];
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) dsum[db] = 0.f;
 #pragma unroll
           for (int be = 0; be < NB; ++be) {
             float x[4];
@@ -657,20 +663,23 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
             for (int i = 0; i < 4; ++i) {
               x[i] = pt[u][be][i] * fac[u][i];
               if constexpr (SN) {
-                if (be == 0) dsum += fac[u][i];  // the decay weights alone
+                if (be == 0) dsum[0] += fac[u][i];  // the decay weights alone
               } else {
-                dsum += x[i];
+                dsum[PB ? be : 0] += x[i];
               }
             }
             store4f(&sP[(be * L + j) * PS + kpos4<T>(lt[u] * 16 + 4 * lg)], x[0], x[1], x[2], x[3]);
           }
-          dsum = sum_lane_groups(dsum);
-          // the store index is formed here, not hoisted out of the chunk loop
-          // (kept live across the loop it would be spilled, and its reload
-          // would wait for the h stores in flight)
-          int jd = lt[u] * L + j;
-          asm volatile("" : "+v"(jd));
-          if (lg == 0) sDenPart[jd] = dsum;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const float ds = sum_lane_groups(dsum[db]);
+            // the store index is formed here, not hoisted out of the chunk
+            // loop (kept live across the loop it would be spilled, and its
+            // reload would wait for the h stores in flight)
+            int jd = (db * NJT + lt[u]) * L + j;
+            asm volatile("" : "+v"(jd));
+            if (lg == 0) sDenPart[jd] = ds;
+          }
         }
       };
       {
@@ -701,13 +710,18 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
 #pragma unroll
         for (int jt = 0; jt < NJT; ++jt) {
           if (w == NW - 1 - (jt % NW)) {
-            f32x4 pn = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < NKQ; ++kb) {
-              pn = M::mma(n_frag(kb), M::load(&sQ[(jt * 16 + lr) * QS + kb * K + KL * lg]), pn);
-              if (kb & 1) __builtin_amdgcn_sched_barrier(0);
+            for (int db = 0; db < NDB; ++db) {
+              f32x4 pn = {0.f, 0.f, 0.f, 0.f};
+              constexpr int KPB = NKQ / NDB;  // feature k-blocks per denominator
+#pragma unroll
+              for (int kk = 0; kk < KPB; ++kk) {
+                const int kb = db * KPB + kk;
+                pn = M::mma(n_frag(kb), M::load(&sQ[(jt * 16 + lr) * QS + kb * K + KL * lg]), pn);
+                if (kk & 1) __builtin_amdgcn_sched_barrier(0);
+              }
+              if (lg == 0) sDenInter[db * L + jt * 16 + lr] = pn[0] + pn[1];
             }
-            if (lg == 0) sDenInter[jt * 16 + lr] = pn[0] + pn[1];
           }
         }
       }
@@ -787,9 +801,10 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
           if constexpr (RET) {
             inv = 1.f;
           } else {
-            float den = rs * sDenInter[j] + sBT[j];
+            const int db = PB ? blk : 0;  // this wave's columns lie in block blk
+            float den = rs * sDenInter[db * L + j] + sBT[j];
 #pragma unroll
-            for (int t = 0; t < NJT; ++t) den += sDenPart[t * L + j];
+            for (int t = 0; t < NJT; ++t) den += sDenPart[(db * NJT + t) * L + j];
             inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), sCL[j]));
           }
           // rows past T fall outside the output buffer and are dropped
@@ -1543,7 +1558,8 @@ size_t chunk_lds_bytes() {
   return ChunkCfg<T, DQK, NB, WC, NRG, NCG, L, GN>::lds_bytes(RET);
 }
 
-template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET, bool GN, bool SN = false>
+template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET, bool GN, bool SN = false,
+          bool PB = false>
 hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   constexpr int NTH = 64 * NCG * NRG;
   const int BH = p.B * p.H;
@@ -1595,10 +1611,10 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
   if constexpr (GN)
     hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, false, true>), g3, dim3(NTH), 0, stream, p);
   else if (!RET && p.o_pre)
-    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, !RET, false, SN>), g3, dim3(NTH), 0, stream,
-                       p);
+    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, !RET, false, SN, PB>), g3, dim3(NTH), 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, false, false, SN>), g3, dim3(NTH), 0,
+    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, false, false, SN, PB>), g3, dim3(NTH), 0,
                        stream, p);
   const hipError_t e = hipGetLastError();
   if (ev1) (void)hipEventRecord(ev1, stream);
@@ -1631,12 +1647,19 @@ constexpr ChunkLaunchFn scalar_norm_launcher() {
   if constexpr (RET) return nullptr;
   else return &launch_chunkwise<T, DQK, NB, WC, NRG, NCG, L, RET, false, true>;
 }
+// the per-block-normaliser launcher of a block-diagonal mLSTM variant
+template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET>
+constexpr ChunkLaunchFn block_norm_launcher() {
+  if constexpr (RET || NB == 1) return nullptr;
+  else return &launch_chunkwise<T, DQK, NB, WC, NRG, NCG, L, RET, false, false, true>;
+}
 
 bool find_chunk_variant(int dtype, int dqk, int nb, int L, bool ret, ChunkVariant* out) {
 #define X(T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_)                                              \
   if (dtype == (sizeof(T_) == 2 ? 1 : 0) && dqk == DQK_ && nb == NB_ && L == L_ && ret == RET_) { \
     out->launch = &launch_chunkwise<T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_, false>;            \
     out->launch_scalar_norm = scalar_norm_launcher<T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_>();  \
+    out->launch_block_norm = block_norm_launcher<T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_>();    \
     out->lds_bytes = chunk_lds_bytes<T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_, false>();         \
     out->wc = WC_;                                                                               \
     out->w = NCG_ * WC_;                                                                         \
@@ -1656,6 +1679,7 @@ bool find_retention_groupnorm_variant(int dtype, int dqk, int L, ChunkVariant* o
   if (RET_ && dtype == (sizeof(T_) == 2 ? 1 : 0) && dqk == DQK_ && NB_ == 1 && L == L_) {        \
     out->launch = &launch_chunkwise<T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_, RET_>;             \
     out->launch_scalar_norm = nullptr;                                                           \
+    out->launch_block_norm = nullptr;                                                            \
     out->lds_bytes = chunk_lds_bytes<T_, DQK_, NB_, WC_, NRG_, NCG_, L_, RET_, RET_>();          \
     out->wc = WC_;                                                                               \
     out->w = NCG_ * WC_;                                                                         \

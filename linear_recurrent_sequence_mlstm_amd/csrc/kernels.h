@@ -58,6 +58,7 @@ typedef hipError_t (*ChunkLaunchFn)(ChunkParams, hipStream_t, hipEvent_t ev0, hi
 struct ChunkVariant {
   ChunkLaunchFn launch;
   ChunkLaunchFn launch_scalar_norm;  // mLSTM with the scalar normaliser (null: none)
+  ChunkLaunchFn launch_block_norm;   // mLSTM, one denominator per memory block (null: none)
   size_t lds_bytes;
   int wc;  // d_v columns per wave
   int w;   // d_v columns per work-group (the d_v slice)
@@ -85,8 +86,9 @@ struct StepParams {
   const float* gamma;  // retention: [H] decay, or null for 1 - 2^(-5-h)
 };
 
-// scalar_norm: n is [B,H] and the denominator is |n~ + bias 2^{-m}|
-hipError_t launch_step(int dtype, const StepParams& p, hipStream_t stream, bool scalar_norm = false);
+// norm_mode: 0 vector, 1 scalar (n is [B,H], denominator |n~ + bias 2^{-m}|),
+// 2 one denominator per memory block
+hipError_t launch_step(int dtype, const StepParams& p, hipStream_t stream, int norm_mode = 0);
 // Retention decode: C is S [B,H,d_k,d_v]; q, k, v, h and gamma are read.
 hipError_t launch_retention_step(int dtype, const StepParams& p, hipStream_t stream);
 bool step_supported(int dqk, int dv, int nb);

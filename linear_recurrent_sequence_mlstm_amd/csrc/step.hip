@@ -58,8 +58,10 @@ __device__ __forceinline__ StepGates step_gates(const StepParams& p, int bh) {
 }
 
 // SN: the scalar normaliser n~ = f' n~ + i' (n [B,H]), denominator
-// |n~ + bias 2^{-m'}| (no k, no q).
-template <typename T, int RG, bool RET, bool SN = false>
+// |n~ + bias 2^{-m'}| (no k, no q).  PB: one denominator per memory block
+// (at most kStepMaxBlocks blocks).
+constexpr int kStepMaxBlocks = 8;
+template <typename T, int RG, bool RET, bool SN = false, bool PB = false>
 __global__ __launch_bounds__(512) void step_kernel(StepParams p, int WS) {
   extern __shared__ float smem[];
   const int DQK = p.DQK, DV = p.DV, NB = p.NB;
@@ -73,7 +75,8 @@ __global__ __launch_bounds__(512) void step_kernel(StepParams p, int WS) {
   float* sq = smem;              // [DQK]
   float* sk = sq + DQK;          // [DQK]
   float* sacc = sk + DQK;        // [RG][WS]
-  float* sred = sacc + RG * WS;  // [2][nth / 64]
+  float* sred = sacc + RG * WS;  // [2][nth / 64], per block with PB
+  constexpr int NBA = PB ? kStepMaxBlocks : 1;
 
   const T* q = static_cast<const T*>(p.q) + (size_t)bh * DQK;
   const T* k = static_cast<const T*>(p.k) + (size_t)bh * DQK;
@@ -93,25 +96,40 @@ __global__ __launch_bounds__(512) void step_kernel(StepParams p, int WS) {
   const StepGates gt = step_gates<T, RET>(p, bh);
   const float bias = (!RET && p.bias) ? p.bias[bh % p.H] : 0.f;
   // q, k to LDS; n~.q and k.q over the head
-  float nq = 0.f, kq = 0.f;
+  float nqa[NBA], kqa[NBA];  // per block with PB (registers: fixed indices only)
+#pragma unroll
+  for (int bb = 0; bb < NBA; ++bb) nqa[bb] = kqa[bb] = 0.f;
   for (int r = tid; r < DQK; r += nth) {
     const float qr = to_f32(q[r]), kr = to_f32(k[r]);
     sq[r] = qr;
     sk[r] = kr;
     if constexpr (!RET && !SN) {
-      nq += p.n[(size_t)bh * DQK + r] * qr;
-      kq += kr * qr;
+      const float nx = p.n[(size_t)bh * DQK + r] * qr, kx = kr * qr;
+      const int rb = PB ? r / DQKB : 0;
+#pragma unroll
+      for (int bb = 0; bb < NBA; ++bb)
+        if (bb == rb) {
+          nqa[bb] += nx;
+          kqa[bb] += kx;
+        }
     }
   }
   if constexpr (!RET && !SN) {
+    const int nw = nth / 64;
 #pragma unroll
-    for (int d = 32; d > 0; d >>= 1) {
-      nq += __shfl_xor(nq, d, 64);
-      kq += __shfl_xor(kq, d, 64);
-    }
-    if (lane == 0) {
-      sred[tid >> 6] = nq;
-      sred[nth / 64 + (tid >> 6)] = kq;
+    for (int bb = 0; bb < NBA; ++bb) {
+      if (bb < (PB ? NB : 1)) {
+        float nq = nqa[bb], kq = kqa[bb];
+#pragma unroll
+        for (int d = 32; d > 0; d >>= 1) {
+          nq += __shfl_xor(nq, d, 64);
+          kq += __shfl_xor(kq, d, 64);
+        }
+        if (lane == 0) {
+          sred[2 * bb * nw + (tid >> 6)] = nq;
+          sred[(2 * bb + 1) * nw + (tid >> 6)] = kq;
+        }
+      }
     }
   }
   __syncthreads();
@@ -169,9 +187,10 @@ __global__ __launch_bounds__(512) void step_kernel(StepParams p, int WS) {
       n_q = p.n[bh];  // the old scalar n~; its new value is f' n~ + i'
       k_q = 1.f;
     } else {
-      for (int i = 0; i < nth / 64; ++i) {
-        n_q += sred[i];
-        k_q += sred[nth / 64 + i];
+      const int nw = nth / 64, db = PB ? blk : 0;  // this thread's columns lie in block blk
+      for (int i = 0; i < nw; ++i) {
+        n_q += sred[2 * db * nw + i];
+        k_q += sred[(2 * db + 1) * nw + i];
       }
     }
     const float cl2 = exp2_fast(-gt.mn2);
@@ -241,18 +260,18 @@ bool step_supported(int dqk, int dv, int nb) {
   return pick_rg(pick_ws(dv)) > 0;
 }
 
-template <typename T, bool RET, bool SN = false>
+template <typename T, bool RET, bool SN = false, bool PB = false>
 static hipError_t launch_rg(const StepParams& p, int ws, int rg, hipStream_t stream) {
   const int tpc = ws / 4;
   const dim3 grid((unsigned)(p.B * p.H * (p.DV / ws)));
   const dim3 block((unsigned)(tpc * rg));
-  const size_t smem = ((size_t)2 * p.DQK + (size_t)rg * ws + 2 * 16) * sizeof(float);
+  const size_t smem = ((size_t)2 * p.DQK + (size_t)rg * ws + 2 * 16 * (PB ? kStepMaxBlocks : 1)) * sizeof(float);
   switch (rg) {
-    case 1: hipLaunchKernelGGL((step_kernel<T, 1, RET, SN>), grid, block, smem, stream, p, ws); break;
-    case 2: hipLaunchKernelGGL((step_kernel<T, 2, RET, SN>), grid, block, smem, stream, p, ws); break;
-    case 4: hipLaunchKernelGGL((step_kernel<T, 4, RET, SN>), grid, block, smem, stream, p, ws); break;
-    case 8: hipLaunchKernelGGL((step_kernel<T, 8, RET, SN>), grid, block, smem, stream, p, ws); break;
-    default: hipLaunchKernelGGL((step_kernel<T, 16, RET, SN>), grid, block, smem, stream, p, ws); break;
+    case 1: hipLaunchKernelGGL((step_kernel<T, 1, RET, SN, PB>), grid, block, smem, stream, p, ws); break;
+    case 2: hipLaunchKernelGGL((step_kernel<T, 2, RET, SN, PB>), grid, block, smem, stream, p, ws); break;
+    case 4: hipLaunchKernelGGL((step_kernel<T, 4, RET, SN, PB>), grid, block, smem, stream, p, ws); break;
+    case 8: hipLaunchKernelGGL((step_kernel<T, 8, RET, SN, PB>), grid, block, smem, stream, p, ws); break;
+    default: hipLaunchKernelGGL((step_kernel<T, 16, RET, SN, PB>), grid, block, smem, stream, p, ws); break;
   }
   if constexpr (RET) return hipGetLastError();  // no normaliser or stabiliser
   const int nent = SN ? 1 : p.DQK;  // normaliser entries per (b, h)
@@ -262,12 +281,15 @@ static hipError_t launch_rg(const StepParams& p, int ws, int rg, hipStream_t str
   return hipGetLastError();
 }
 
-hipError_t launch_step(int dtype, const StepParams& p, hipStream_t stream, bool scalar_norm) {
+hipError_t launch_step(int dtype, const StepParams& p, hipStream_t stream, int norm_mode) {
   const int ws = pick_ws(p.DV);
   const int rg = pick_rg(ws);
-  if (scalar_norm)
+  if (norm_mode == 1)
     return dtype == 1 ? launch_rg<__bf16, false, true>(p, ws, rg, stream)
                       : launch_rg<float, false, true>(p, ws, rg, stream);
+  if (norm_mode == 2 && p.NB > 1)
+    return dtype == 1 ? launch_rg<__bf16, false, false, true>(p, ws, rg, stream)
+                      : launch_rg<float, false, false, true>(p, ws, rg, stream);
   return dtype == 1 ? launch_rg<__bf16, false>(p, ws, rg, stream) : launch_rg<float, false>(p, ws, rg, stream);
 }
 

@@ -69,6 +69,7 @@ def test_norm_mode_validation():
     P0 = [BOGUS] * 6 + [None] + [BOGUS] * 3
     assert L.mlstm_step_ex(1, 1, 64, 64, 1, 1, 9, *P0, BOGUS, None) == E_UNSUPPORTED
     assert L.mlstm_step_ex(1, 1, 64, 60, 1, 1, 1, *P0, BOGUS, None) == E_UNSUPPORTED
+    assert L.mlstm_step_ex(1, 1, 64, 64, 16, 1, 2, *P0, BOGUS, None) == E_UNSUPPORTED  # > 8 blocks
     assert _lib.last_error() != ""
 
 

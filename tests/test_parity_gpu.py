@@ -209,6 +209,45 @@ def test_step_scalar_normaliser(gpu):
     assert np.max(np.abs(nn_ - ref[2]) / np.abs(ref[2])) < TOL[torch.bfloat16]
 
 
+# ------------------------------------------------ per-block normaliser reading
+@pytest.mark.parametrize("B,H,T,dqk,dv,dtype", [(2, 2, 150, 64, 64, "bf16"), (1, 2, 130, 256, 512, "bf16"),
+                                                 (1, 2, 70, 64, 64, "f32")])
+def test_chunkwise_block_normaliser(gpu, B, H, T, dqk, dv, dtype):
+    """norm_mode "block" with two memory blocks against the oracle's
+    per-block mode (each block its own denominator), outputs and state."""
+    x = mlstm_inputs(B, H, T, dqk, dv, dtype=dtype, seed=51, nb=2, k_scale=0.125, f_mix=True,
+                     with_o=True, bias="uniform")
+    g = x.to(gpu)
+    h, st = mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, num_blocks=2,
+                                norm_mode="block")
+    torch.cuda.synchronize()
+    assert tuple(st[1].shape) == (B, H, dqk)  # the per-block reading keeps the vector n
+    ref = oracle.mlstm_fwd(x.q, x.k, x.v, x.i_pre, x.f_pre, x.o_pre, x.bias, num_blocks=2, norm_mode="block")
+    tol = TOL[torch.bfloat16 if dtype == "bf16" else torch.float32]
+    assert slice_err(cpu(h), ref[0]) < tol
+    check_state(st, ref[1:], tol)
+
+
+def test_step_block_normaliser(gpu):
+    """Decode steps in per-block mode from a per-block prefill equal one
+    oracle run."""
+    B, H, T, T1, dqk, dv = 2, 2, 50, 30, 64, 128
+    x = mlstm_inputs(B, H, T, dqk, dv, dtype="bf16", seed=52, nb=2, k_scale=0.125, bias="uniform")
+    g = x.to(gpu)
+    cut = lambda t: None if t is None else t[:, :, :T1].contiguous()
+    _, (C, n, m) = mlstm.chunkwise_fwd(*(cut(t) for t in (g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre)), g.bias,
+                                       num_blocks=2, norm_mode="block")
+    outs = []
+    for t in range(T1, T):
+        tok = lambda a: a[:, :, t].contiguous()
+        outs.append(cpu(mlstm.step(tok(g.q), tok(g.k), tok(g.v), tok(g.i_pre), tok(g.f_pre), C, n, m,
+                                   bias=g.bias, num_blocks=2, norm_mode="block")))
+    torch.cuda.synchronize()
+    ref = oracle.mlstm_fwd(x.q, x.k, x.v, x.i_pre, x.f_pre, x.o_pre, x.bias, num_blocks=2, norm_mode="block")
+    assert slice_err(np.stack(outs, axis=2), ref[0][:, :, T1:]) < TOL[torch.bfloat16]
+    check_state((C, n, m), ref[1:], TOL[torch.bfloat16])
+
+
 # ------------------------------------------------------------ retention
 @pytest.mark.parametrize("T,with_state", [(2048, False), (700, True), (50, False)])
 def test_retention_bf16(gpu, T, with_state):
