@@ -16,9 +16,10 @@ with a fresh bf16 token per step; it reports achieved HBM GB/s.
 
 ``variants`` times the other chunkwise workloads through the same kernels
 (RetNet retention B=8 H=4 d=64 T=2048, also with its per-head group norm
-fused; xLSTM-v2 block-diagonal B=4 H=4 d=64 nb=2 T=65536; the 7B prefill
-with an output gate) and the retention decode step on the RetNet shape:
-tokens/s per call and its algorithmic bytes against HBM.
+fused; xLSTM-v2 block-diagonal B=4 H=4 d=64 nb=2 T=65536, also with per-block
+denominators; the 7B prefill with an output gate, and with the scalar
+normaliser) and the retention decode step on the RetNet shape: tokens/s per
+call and its algorithmic bytes against HBM.
 
 ``roofline`` is measured live: HIP events recorded by the library right before
 and after its main kernel (mlstm_set_profile_events) give that kernel's
@@ -293,7 +294,20 @@ def bench_variants(torch, mlstm, workload, args, dev):
     byts += B * H * T * dv * 2
     out.append(dict(workload="xlstm7b_prefill_T8192_with_o", B=B, H=H, T=T, d_qk=dqk, d_v=dv, **r,
                     bytes=byts, flops=flops, tokens=B * T))
-    del sets, hs, st, ws
+
+    # the same workload (no output gate) with the scalar normaliser reading
+    st_s = (st[0], torch.empty(B, H, device=dev), st[2])
+
+    def call_s(i):
+        g = sets[i]
+        mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, None, g.bias, h=hs[i], state_out=st_s, workspace=ws,
+                            norm_mode="scalar")
+
+    r = timed(call_s, len(sets), args.variant_steps, args.variant_steps)
+    byts, flops = prefill_work(B, H, T, dqk, dv)
+    out.append(dict(workload="xlstm7b_prefill_T8192_scalar_norm", B=B, H=H, T=T, d_qk=dqk, d_v=dv, **r,
+                    bytes=byts - B * H * (dqk - 1) * 4, flops=flops, tokens=B * T))
+    del sets, hs, st, st_s, ws
 
     # xLSTM-v2 block-diagonal: B=4, H=4, d=64, nb=2, T=65536 (541 MB per call)
     x = workload("xlstm2_blockdiag_T65536")
@@ -318,6 +332,16 @@ def bench_variants(torch, mlstm, workload, args, dev):
     flops -= B * H * T * 4 * (dqk * dv - dqk * dv // nb)
     out.append(dict(workload="xlstm2_blockdiag_T65536", B=B, H=H, T=T, d_qk=dqk, d_v=dv, num_blocks=nb, **r,
                     bytes=byts, flops=flops, tokens=B * T))
+
+    # the same with one denominator per memory block
+    def call_b(i):
+        g = sets[i]
+        mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, num_blocks=nb, h=hs[i],
+                            state_out=st, workspace=ws, norm_mode="block")
+
+    r = timed(call_b, len(sets), args.variant_steps, args.variant_steps)
+    out.append(dict(workload="xlstm2_blockdiag_T65536_block_norm", B=B, H=H, T=T, d_qk=dqk, d_v=dv,
+                    num_blocks=nb, **r, bytes=byts, flops=flops, tokens=B * T))
     return out
 
 
