@@ -251,3 +251,191 @@ int oracle_retention_fwd(int B, int H, int T, int dk, int dv, const double* q,
   }
   return bad ? -2 : 0;
 }
+
+/*
+ * Backward pass of the mLSTM sequence form (vector normaliser, one memory
+ * block): the gradients of L = sum_t dh_t . h_t with respect to every input,
+ * by the chain rule applied to the recurrence above, one step at a time from
+ * t = T-1 down to 0.  Training runs the parallel or chunked forms (section
+ * "Triple Paradigm" of the "Edifice.Attention.RetNet" page; the chunked-scan
+ * mode of Gdn2Mode on the "burn-gdn2" page); they compute this same function,
+ * so its gradient is fixed by the recurrence alone.
+ *
+ * In true (unstabilised) units, with S_t = f_t S_{t-1} + i_t k_t v_t^T,
+ * n_t = f_t n_{t-1} + i_t k_t, z_t = n_t . q_t + bias, h_t = o_t * S_t^T q_t
+ * / max(|z_t|, 1), and G_t, g_t the total gradients of L with respect to
+ * S_t and n_t (everything from step t on):
+ *   G_t = f_{t+1} G_{t+1} + q_t dnum_t^T,  g_t = f_{t+1} g_{t+1} + dz_t q_t,
+ *   dnum_t = o_t * dh_t / max(|z_t|, 1),
+ *   dz_t = -(o_t * dh_t) . (S_t^T q_t) / max(|z_t|,1)^2 * sign(z_t) when |z_t| > 1, else 0,
+ *   dq_t = S_t dnum_t + n_t dz_t,
+ *   dk_t = i_t (G_t v_t + g_t),  dv_t = i_t G_t^T k_t,
+ *   d i_pre_t = i_t (k_t . G_t v_t + k_t . g_t)           (i = exp(i_pre)),
+ *   d log f_t = f_t (<G_t, S_{t-1}> + g_t . n_{t-1}),
+ *   d f_pre_t = d log f_t * sigmoid(-f_pre_t)            (log f = log sigmoid(f_pre)),
+ *   d o_pre_t = dh_t * (S_t^T q_t / max(|z_t|,1)) * o_t (1 - o_t),
+ *   d bias = sum_t dz_t,  dC0 = f_1 G_1 (as gradient of the initial S), dn0 likewise.
+ * It runs on the stabilised state: G~_t = e^{m_t} G_t, g~_t = e^{m_t} g_t,
+ * which turns the factors above into the f' = e^{lf + m_{t-1} - m_t} and
+ * i' = e^{li - m_t} of the forward step and makes dnum, dz use the stabilised
+ * denominator max(|z~|, e^{-m}).  The initial-state gradients are returned for
+ * the stabilised C0, n0 (d/dC0~ = e^{m0} d/dC0 = f'_1 G~_1).
+ *
+ * The forward states S~_{t-1}, S~_t are needed at every step; they are
+ * recomputed per segment of SEG steps from a saved state at each segment start
+ * (checkpoints), so memory stays O((T/SEG + SEG) d_qk d_v).
+ *
+ * dh [B,H,T,d_v] in; outputs (any may be NULL): dq, dk [B,H,T,d_qk]; dv, do_pre
+ * [B,H,T,d_v]; di, df [B,H,T]; dbias [H] (summed over B); dC0 [B,H,d_qk,d_v];
+ * dn0 [B,H,d_qk].  Returns 0, -1 for bad sizes, -2 when out of memory.
+ */
+int oracle_mlstm_bwd(int B, int H, int T, int dqk, int dv, const double* q,
+                     const double* k, const double* v, const double* i_pre,
+                     const double* f_pre, const double* o_pre, const double* bias,
+                     const double* C0, const double* n0, const double* m0,
+                     const double* dh, double* dq, double* dk, double* dvo,
+                     double* di, double* df, double* do_pre, double* dbias,
+                     double* dC0, double* dn0) {
+  if (B < 0 || H < 0 || T < 0 || dqk <= 0 || dv <= 0) return -1;
+  const size_t csz = (size_t)dqk * dv;
+  const size_t ssz = csz + (size_t)dqk + 1; /* one saved state: S~, n~, m */
+  const long BH = (long)B * H;
+  int SEG = 1;
+  while ((long)SEG * SEG < T) ++SEG;
+  const int NSEG = T > 0 ? (T + SEG - 1) / SEG : 0;
+  double* dbias_bh = (double*)calloc(BH > 0 ? (size_t)BH : 1, sizeof(double));
+  if (!dbias_bh) return -2;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < BH; ++bh) {
+    const int hd = (int)(bh % H);
+    const double bs = bias ? bias[hd] : 0.0;
+    /* ckpt[s]: state before segment s; seg[j]: state after step s*SEG + j */
+    double* ckpt = (double*)malloc((size_t)(NSEG + 1) * ssz * sizeof(double));
+    double* seg = (double*)malloc((size_t)(SEG + 1) * ssz * sizeof(double));
+    double* G = (double*)calloc(csz, sizeof(double));
+    double* g = (double*)calloc((size_t)dqk, sizeof(double));
+    double* hbuf = (double*)malloc((size_t)dv * sizeof(double));
+    double* dn = (double*)malloc((size_t)dv * sizeof(double));
+    double* Gv = (double*)malloc((size_t)dqk * sizeof(double));
+    if (!ckpt || !seg || !G || !g || !hbuf || !dn || !Gv) {
+      free(ckpt), free(seg), free(G), free(g), free(hbuf), free(dn), free(Gv);
+#pragma omp atomic write
+      bad = 1;
+      continue;
+    }
+    /* forward sweep: the state at every segment start */
+    double* s0 = ckpt;
+    if (C0) memcpy(s0, C0 + bh * csz, csz * sizeof(double));
+    else memset(s0, 0, csz * sizeof(double));
+    if (n0) memcpy(s0 + csz, n0 + bh * dqk, (size_t)dqk * sizeof(double));
+    else memset(s0 + csz, 0, (size_t)dqk * sizeof(double));
+    s0[csz + dqk] = m0 ? m0[bh] : 0.0;
+    for (int s = 0; s < NSEG; ++s) {
+      double* cur = ckpt + (size_t)(s + 1) * ssz;
+      memcpy(cur, ckpt + (size_t)s * ssz, ssz * sizeof(double));
+      for (int t = s * SEG; t < T && t < (s + 1) * SEG; ++t) {
+        const size_t tok = (size_t)bh * T + t;
+        cell_step(dqk, dv, 1, q + tok * dqk, k + tok * dqk, v + tok * dv, i_pre[tok],
+                  f_pre[tok], o_pre ? o_pre + tok * dv : NULL, bs, 1, 0.0, cur,
+                  cur + csz, cur + csz + dqk, hbuf);
+      }
+    }
+    double dbias_acc = 0.0;
+    for (int s = NSEG - 1; s >= 0; --s) {
+      /* recompute the segment: seg[0] = state before it, seg[j+1] after step j */
+      const int t0 = s * SEG, t1 = (s + 1) * SEG < T ? (s + 1) * SEG : T;
+      memcpy(seg, ckpt + (size_t)s * ssz, ssz * sizeof(double));
+      for (int t = t0; t < t1; ++t) {
+        const size_t tok = (size_t)bh * T + t;
+        double* nxt = seg + (size_t)(t - t0 + 1) * ssz;
+        memcpy(nxt, seg + (size_t)(t - t0) * ssz, ssz * sizeof(double));
+        cell_step(dqk, dv, 1, q + tok * dqk, k + tok * dqk, v + tok * dv, i_pre[tok],
+                  f_pre[tok], o_pre ? o_pre + tok * dv : NULL, bs, 1, 0.0, nxt,
+                  nxt + csz, nxt + csz + dqk, hbuf);
+      }
+      for (int t = t1 - 1; t >= t0; --t) {
+        const size_t tok = (size_t)bh * T + t;
+        const double* Sp = seg + (size_t)(t - t0) * ssz; /* S~_{t-1}, n~_{t-1}, m_{t-1} */
+        const double* St = Sp + ssz;                     /* S~_t, n~_t, m_t */
+        const double* np_ = Sp + csz;
+        const double* nt = St + csz;
+        const double mp = Sp[csz + dqk], mt = St[csz + dqk];
+        const double* qt = q + tok * dqk;
+        const double* kt = k + tok * dqk;
+        const double* vt = v + tok * dv;
+        const double* dht = dh + tok * dv;
+        /* readout at t on the updated state */
+        double zt = 0.0;
+        for (int r = 0; r < dqk; ++r) zt += nt[r] * qt[r];
+        const double fl = exp(-mt);
+        zt += bs * fl;
+        const double den = fmax(fabs(zt), fl);
+        double sdy = 0.0; /* (o * dh) . y */
+        for (int c = 0; c < dv; ++c) {
+          double num = 0.0;
+          for (int r = 0; r < dqk; ++r) num += St[(size_t)r * dv + c] * qt[r];
+          const double y = num / den;
+          const double o = o_pre ? sigmoid(o_pre[tok * dv + c]) : 1.0;
+          if (do_pre && o_pre) do_pre[tok * dv + c] = dht[c] * y * o * (1.0 - o);
+          dn[c] = o * dht[c] / den;
+          sdy += o * dht[c] * y;
+        }
+        const double dz = fabs(zt) > fl ? -sdy / den * (zt > 0 ? 1.0 : -1.0) : 0.0;
+        dbias_acc += dz * fl;
+        /* dq_t = S~_t dn + n~_t dz */
+        if (dq)
+          for (int r = 0; r < dqk; ++r) {
+            double a = nt[r] * dz;
+            for (int c = 0; c < dv; ++c) a += St[(size_t)r * dv + c] * dn[c];
+            dq[tok * dqk + r] = a;
+          }
+        /* total gradients of the state at t */
+        for (int r = 0; r < dqk; ++r) {
+          for (int c = 0; c < dv; ++c) G[(size_t)r * dv + c] += qt[r] * dn[c];
+          g[r] += qt[r] * dz;
+        }
+        /* through S~_t = f' S~_{t-1} + i' k v^T */
+        const double lf = log_sigmoid(f_pre[tok]);
+        const double fdec = exp(lf + mp - mt), iw = exp(i_pre[tok] - mt);
+        double kGv = 0.0, kg = 0.0, dlf = 0.0;
+        for (int r = 0; r < dqk; ++r) {
+          double a = 0.0;
+          for (int c = 0; c < dv; ++c) a += G[(size_t)r * dv + c] * vt[c];
+          Gv[r] = a;
+          kGv += kt[r] * a;
+          kg += kt[r] * g[r];
+          double b = np_[r] * g[r];
+          for (int c = 0; c < dv; ++c) b += G[(size_t)r * dv + c] * Sp[(size_t)r * dv + c];
+          dlf += b;
+        }
+        dlf *= fdec;
+        if (dk)
+          for (int r = 0; r < dqk; ++r) dk[tok * dqk + r] = iw * (Gv[r] + g[r]);
+        if (dvo)
+          for (int c = 0; c < dv; ++c) {
+            double a = 0.0;
+            for (int r = 0; r < dqk; ++r) a += G[(size_t)r * dv + c] * kt[r];
+            dvo[tok * dv + c] = iw * a;
+          }
+        if (di) di[tok] = iw * (kGv + kg);
+        if (df) df[tok] = dlf * sigmoid(-f_pre[tok]);
+        /* on to step t-1: G~_{t-1} = f' G~_t */
+        for (size_t e = 0; e < csz; ++e) G[e] *= fdec;
+        for (int r = 0; r < dqk; ++r) g[r] *= fdec;
+      }
+    }
+    if (dC0) memcpy(dC0 + bh * csz, G, csz * sizeof(double));
+    if (dn0) memcpy(dn0 + bh * dqk, g, (size_t)dqk * sizeof(double));
+    dbias_bh[bh] = dbias_acc;
+    free(ckpt), free(seg), free(G), free(g), free(hbuf), free(dn), free(Gv);
+  }
+  if (dbias)
+    for (int hd = 0; hd < H; ++hd) {
+      double a = 0.0;
+      for (int b = 0; b < B; ++b) a += dbias_bh[(long)b * H + hd];
+      dbias[hd] = a;
+    }
+  free(dbias_bh);
+  return bad ? -2 : 0;
+}

@@ -1,0 +1,124 @@
+"""Pins of the oracle's backward pass (oracle.mlstm_bwd) against facts that do
+not come from its code:
+  * central finite differences of the oracle's forward (L = sum dh * h) for
+    every input, initial state included, with the denominator floor active on
+    some tokens and not on others;
+  * torch autograd through an unstabilised fp64 recurrence written here from
+    the cell's definition (C_t = f C + i k v^T, n_t = f n + i k,
+    h = o * C^T q / max(|n.q + bias|, 1)), at lengths on both sides of the
+    oracle's checkpoint segment.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+
+def _case(seed, B, H, T, dqk, dv, with_o=True, bias=True, init=True, kscale=1.0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, T, dqk))
+    k = rng.standard_normal((B, H, T, dqk)) / np.sqrt(dqk) * kscale
+    v = rng.standard_normal((B, H, T, dv))
+    ip = rng.standard_normal((B, H, T))
+    fp = np.where(rng.random((B, H, T)) < 0.7, rng.normal(3, 1, (B, H, T)),
+                  rng.normal(-2, 1, (B, H, T)))
+    op = rng.standard_normal((B, H, T, dv)) if with_o else None
+    bs = rng.uniform(-0.5, 0.5, H) if bias else None
+    C0 = rng.standard_normal((B, H, dqk, dv)) * 0.3 if init else None
+    n0 = rng.standard_normal((B, H, dqk)) * 0.3 if init else None
+    m0 = rng.uniform(-2, 2, (B, H)) if init else None
+    dh = rng.standard_normal((B, H, T, dv))
+    return dict(q=q, k=k, v=v, i_pre=ip, f_pre=fp, o_pre=op, bias=bs, C0=C0, n0=n0, m0=m0), dh
+
+
+def _fwd(a):
+    B, H, T, dqk = a["q"].shape
+    dv = a["v"].shape[-1]
+    C0 = None if a["C0"] is None else a["C0"].reshape(B, H, 1, dqk, dv)
+    return oracle.mlstm_fwd(a["q"], a["k"], a["v"], a["i_pre"], a["f_pre"], a["o_pre"],
+                            a["bias"], C0, a["n0"], a["m0"])[0]
+
+
+def _torch_h(t):
+    """Unstabilised recurrence in true units, fp64, differentiable."""
+    q, k, v, ip, fp = t["q"], t["k"], t["v"], t["i_pre"], t["f_pre"]
+    B, H, T, dqk = q.shape
+    dv = v.shape[-1]
+    if t["C0"] is not None:
+        C = t["C0"] * torch.exp(t["m0"])[..., None, None]
+        n = t["n0"] * torch.exp(t["m0"])[..., None]
+    else:
+        C = torch.zeros(B, H, dqk, dv, dtype=torch.float64)
+        n = torch.zeros(B, H, dqk, dtype=torch.float64)
+    bias = t["bias"] if t["bias"] is not None else torch.zeros(H, dtype=torch.float64)
+    hs, zs = [], []
+    for s in range(T):
+        f = torch.sigmoid(fp[:, :, s])[..., None]
+        i = torch.exp(ip[:, :, s])[..., None]
+        C = f[..., None] * C + (i * k[:, :, s])[..., :, None] * v[:, :, s][..., None, :]
+        n = f * n + i * k[:, :, s]
+        num = (C * q[:, :, s][..., :, None]).sum(-2)
+        z = (n * q[:, :, s]).sum(-1) + bias
+        den = torch.clamp(z.abs(), min=1.0)
+        o = torch.sigmoid(t["o_pre"][:, :, s]) if t["o_pre"] is not None else 1.0
+        hs.append(o * num / den[..., None])
+        zs.append(z.detach())
+    return torch.stack(hs, 2), torch.stack(zs, 2)
+
+
+GRAD_OF = dict(q="dq", k="dk", v="dv", i_pre="di", f_pre="df", o_pre="do", bias="dbias",
+               C0="dC0", n0="dn0")
+
+
+def _relerr(a, b):
+    return np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300)
+
+
+def test_bwd_pin_finite_differences():
+    a, dh = _case(11, 1, 2, 9, 4, 3, kscale=3.0)
+    # both sides of the denominator floor occur, none within reach of the kink
+    _, z = _torch_h({n: (None if x is None else torch.from_numpy(x)) for n, x in a.items()})
+    z = z.numpy()
+    assert (np.abs(z) > 1).any() and (np.abs(z) < 1).any()
+    assert np.min(np.abs(np.abs(z) - 1)) > 1e-3
+    g = oracle.mlstm_bwd(dh=dh, **a)
+    eps = 1e-6
+    for name, gname in GRAD_OF.items():
+        x = a[name]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            lp = np.sum(dh * _fwd(a))
+            x[idx] = keep - eps
+            lm = np.sum(dh * _fwd(a))
+            x[idx] = keep
+            fd[idx] = (lp - lm) / (2 * eps)
+        err = _relerr(g[gname], fd)
+        assert err < 1e-6, (name, err)
+
+
+@pytest.mark.parametrize("T,with_o,bias,init", [(1, True, True, True), (17, False, True, False),
+                                                (40, True, False, True), (64, True, True, False)])
+def test_bwd_pin_torch_autograd(T, with_o, bias, init):
+    a, dh = _case(100 + T, 2, 2, T, 8, 6, with_o=with_o, bias=bias, init=init, kscale=2.0)
+    g = oracle.mlstm_bwd(dh=dh, **a)
+    t = {n: (None if x is None else torch.tensor(x, requires_grad=True)) for n, x in a.items()}
+    h, _ = _torch_h(t)
+    h_or = _fwd(a)
+    assert _relerr(h_or, h.detach().numpy()) < 1e-12
+    (h * torch.from_numpy(dh)).sum().backward()
+    for name, gname in GRAD_OF.items():
+        if t[name] is None or name == "m0":
+            continue
+        err = _relerr(g[gname], t[name].grad.numpy())
+        assert err < 1e-10, (name, T, err)
+    if not init:  # gradient of a zero initial state is still returned
+        C0 = torch.zeros(2, 2, 8, 6, dtype=torch.float64, requires_grad=True)
+        n0 = torch.zeros(2, 2, 8, dtype=torch.float64, requires_grad=True)
+        t2 = dict(t, C0=C0, n0=n0, m0=torch.zeros(2, 2, dtype=torch.float64))
+        h2, _ = _torch_h(t2)
+        (h2 * torch.from_numpy(dh)).sum().backward()
+        assert _relerr(g["dC0"], C0.grad.numpy()) < 1e-10
+        assert _relerr(g["dn0"], n0.grad.numpy()) < 1e-10
