@@ -244,6 +244,54 @@ int retention_step(int B, int H, int d_k, int d_v, mlstm_dtype dt,
                    const void* q, const void* k, const void* v,
                    const float* gamma, float* S, void* out, void* stream);
 
+/*
+ * Workspace size in bytes for mlstm_chunkwise_bwd (0, with the error message
+ * set, for arguments it does not take).
+ */
+size_t mlstm_chunkwise_bwd_workspace_bytes(int B, int H, int T, int d_qk, int d_v,
+                                           int num_blocks, int chunk, mlstm_dtype dt);
+
+/*
+ * Chunkwise backward pass of the mLSTM (vector normaliser): the gradients of
+ * L = sum(dh * h) for h = mlstm_chunkwise_fwd(...) with the same inputs and
+ * initial state (vector normaliser).  The pages run training on the parallel and chunked forms
+ * ("Triple Paradigm" section of the "Edifice.Attention.RetNet" page; the
+ * chunked-scan mode of Gdn2Mode on the "burn-gdn2" page); this is the
+ * gradient of the same chunkwise computation, recomputing the stabiliser, the
+ * chunk states and the outputs from the inputs (nothing is kept from the
+ * forward call).
+ *   q, k, v, i_pre, f_pre, o_pre, norm_bias, C0, n0, m0   as passed to the
+ *                  forward (o_pre, norm_bias, C0, n0, m0 may be NULL);
+ *   dh       [B,H,T,d_v]  gradient of the loss with respect to h (dtype dt);
+ *   dq, dk   [B,H,T,d_qk], dv [B,H,T,d_v], di_pre, df_pre [B,H,T]  outputs,
+ *                  dtype dt (gradients of q, k, v and of the gate
+ *                  preactivations i_pre, f_pre);
+ *   do_pre   [B,H,T,d_v] dtype dt: gradient of o_pre; required exactly when
+ *                  o_pre is given, else NULL;
+ *   dbias    [H] fp32 or NULL: gradient of norm_bias, summed over the batch;
+ *   dC0 [B,H,d_qk,d_v], dn0 [B,H,d_qk] fp32 or NULL: gradients of the
+ *                  stabilised initial state C0, n0 (also for a zero state).
+ *                  The gradient of m0 is <dC0, C0> + <dn0, n0>.
+ * The final state gets no incoming gradient (the loss is taken on h only).
+ * Requires num_blocks = 1, chunk = 64, d_v a multiple of 64 and d_qk in
+ * {64, 128, 256} (bf16) or 64 (fp32); other shapes return
+ * MLSTM_E_UNSUPPORTED.  workspace: at least mlstm_chunkwise_bwd_workspace_bytes
+ * bytes, 256-byte aligned (it holds the start state of every chunk and the
+ * backward state at every chunk end, fp32: 2 (d_qk d_v + d_qk) 4 bytes per
+ * chunk and batch*head).  Enqueues the forward's state passes and six
+ * backward kernels on stream; profile events set by mlstm_set_profile_events
+ * bracket the six backward kernels.
+ */
+int mlstm_chunkwise_bwd(int B, int H, int T, int d_qk, int d_v, int num_blocks,
+                        int chunk, mlstm_dtype dt, const void* q, const void* k,
+                        const void* v, const void* i_pre, const void* f_pre,
+                        const void* o_pre, const float* norm_bias,
+                        const float* C0, const float* n0, const float* m0,
+                        const void* dh, void* dq, void* dk,
+                        void* dv, void* di_pre, void* df_pre, void* do_pre,
+                        float* dbias, float* dC0, float* dn0, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,7 +49,7 @@ struct Plan {
 // Checks shared by the mLSTM and retention chunkwise entry points and the
 // workspace queries; fills the plan.  Returns MLSTM_OK or an error code.
 int plan_chunkwise(int B, int H, int T, int dqk, int dv, int nb, int chunk, int dt, bool ret,
-                   Plan* pl) {
+                   Plan* pl, bool chunk_states = false) {
   if (dt != MLSTM_F32 && dt != MLSTM_BF16) return fail(MLSTM_E_DTYPE, "unknown dtype %d", dt);
   if (B < 1 || H < 1 || T < 1 || dqk < 1 || dv < 1 || nb < 1)
     return fail(MLSTM_E_SHAPE, "sizes must be positive (B=%d H=%d T=%d d_qk=%d d_v=%d nb=%d)", B, H, T,
@@ -83,6 +83,7 @@ int plan_chunkwise(int B, int H, int T, int dqk, int dv, int nb, int chunk, int 
   if (ns > pl->NC) ns = pl->NC;
   int G = (int)((pl->NC + ns - 1) / ns);
   if (env_superchunk_chunks()) G = env_superchunk_chunks();
+  if (chunk_states) G = 1;  // the backward pass needs every chunk's start state
   if (G * chunk > 1024) G = 1024 / chunk;  // pass 1 holds the gate factors of <= 1024 tokens
   if (G > pl->NC) G = pl->NC;
   pl->G = G;
@@ -120,9 +121,158 @@ int launch(const Plan& pl, mlstm::ChunkParams& p, void* workspace, size_t worksp
   return ok();
 }
 
+// Backward workspace: the forward plan with one chunk per superchunk, then
+// the backward's own arrays.
+struct BwdPlan {
+  Plan fwd;
+  size_t off_U, off_P, off_Pt, off_D, off_Dt, off_rden, off_dz, off_db, off_dbh, off_qdq, off_kdki, off_kdk, bytes;
+};
+
+int plan_bwd(int B, int H, int T, int dqk, int dv, int nb, int chunk, int dt, BwdPlan* bp) {
+  const int rc = plan_chunkwise(B, H, T, dqk, dv, nb, chunk, dt, false, &bp->fwd, true);
+  if (rc != MLSTM_OK) return rc;
+  if (nb != 1) return fail(MLSTM_E_UNSUPPORTED, "the backward pass takes num_blocks = 1 (got %d)", nb);
+  if (chunk != 64) return fail(MLSTM_E_UNSUPPORTED, "the backward pass takes chunk = 64 (got %d)", chunk);
+  if (!mlstm::bwd_supported(dt, dqk, dv))
+    return fail(MLSTM_E_UNSUPPORTED, "no backward kernel for dtype=%s d_qk=%d d_v=%d", dt ? "bf16" : "fp32", dqk,
+                dv);
+  const size_t BH = (size_t)B * H, NC = bp->fwd.NC, NCL = NC * 64, es = dt ? 2 : 4;
+  size_t o = align256(bp->fwd.bytes);
+  bp->off_U = o;
+  o += align256(BH * NC * ((size_t)dqk * dv + dqk) * 4);
+  const size_t tile = align256(BH * NC * 64 * 64 * es);
+  bp->off_P = o;
+  bp->off_Pt = o + tile;
+  bp->off_D = o + 2 * tile;
+  bp->off_Dt = o + 3 * tile;
+  o += 4 * tile;
+  bp->off_rden = o;
+  o += align256(BH * NCL * 4);
+  bp->off_dz = o;
+  o += align256(BH * NCL * 4);
+  bp->off_db = o;
+  o += align256(BH * NC * 4);
+  bp->off_dbh = o;
+  o += align256(BH * 4);
+  bp->off_qdq = o;
+  o += align256(BH * NCL * 4);
+  bp->off_kdki = o;
+  o += align256(BH * NCL * 4);
+  bp->off_kdk = o;
+  o += align256(BH * NCL * (dqk / 64) * 4);
+  bp->bytes = o;
+  return MLSTM_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t mlstm_chunkwise_bwd_workspace_bytes(int B, int H, int T, int d_qk, int d_v, int num_blocks, int chunk,
+                                           mlstm_dtype dt) {
+  BwdPlan bp;
+  if (plan_bwd(B, H, T, d_qk, d_v, num_blocks, chunk, dt, &bp) != MLSTM_OK) return 0;
+  return bp.bytes;
+}
+
+int mlstm_chunkwise_bwd(int B, int H, int T, int d_qk, int d_v, int num_blocks, int chunk, mlstm_dtype dt,
+                        const void* q, const void* k, const void* v, const void* i_pre, const void* f_pre,
+                        const void* o_pre, const float* norm_bias, const float* C0, const float* n0,
+                        const float* m0, const void* dh, void* dq, void* dk, void* dv,
+                        void* di_pre, void* df_pre, void* do_pre, float* dbias, float* dC0, float* dn0,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  BwdPlan bp;
+  const int rc = plan_bwd(B, H, T, d_qk, d_v, num_blocks, chunk, dt, &bp);
+  if (rc != MLSTM_OK) return rc;
+  if (!q || !k || !v || !i_pre || !f_pre || !dh)
+    return fail(MLSTM_E_NULL, "q, k, v, i_pre, f_pre and dh are required");
+  if (!dq || !dk || !dv || !di_pre || !df_pre) return fail(MLSTM_E_NULL, "dq, dk, dv, di_pre and df_pre are required");
+  if ((o_pre == nullptr) != (do_pre == nullptr)) return fail(MLSTM_E_NULL, "do_pre is required exactly when o_pre is given");
+  if (!workspace) return fail(MLSTM_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", bp.bytes);
+  if (workspace_bytes < bp.bytes)
+    return fail(MLSTM_E_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, bp.bytes);
+  if ((size_t)workspace & 255) return fail(MLSTM_E_WORKSPACE, "workspace must be 256-byte aligned");
+  const Plan& pl = bp.fwd;
+  char* ws = static_cast<char*>(workspace);
+  // forward state passes only (h = NULL skips the output pass)
+  mlstm::ChunkParams p{};
+  p.B = B;
+  p.H = H;
+  p.T = T;
+  p.DV = d_v;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.i_pre = i_pre;
+  p.f_pre = f_pre;
+  p.o_pre = o_pre;
+  p.bias = norm_bias;
+  p.has_init = (C0 || n0 || m0) ? 1 : 0;
+  p.C0 = C0;
+  p.n0 = n0;
+  p.m0 = m0;
+  p.h = nullptr;
+  p.NC = pl.NC;
+  p.G = pl.G;
+  p.NS = pl.NS;
+  p.nslices = pl.nslices;
+  p.ws_state = reinterpret_cast<float*>(ws);
+  p.ws_scal = reinterpret_cast<float*>(ws + pl.off_scal);
+  p.ws_min = reinterpret_cast<float*>(ws + pl.off_min);
+  const size_t gsz = align256((size_t)B * H * pl.NC * pl.L * sizeof(float));
+  p.ws_ga = reinterpret_cast<float*>(ws + pl.off_g);
+  p.ws_gg = reinterpret_cast<float*>(ws + pl.off_g + gsz);
+  p.ws_gb = reinterpret_cast<float*>(ws + pl.off_g + 2 * gsz);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = pl.var.launch(p, st, nullptr, nullptr);
+  if (e != hipSuccess) return fail(MLSTM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  mlstm::BwdParams b{};
+  b.B = B;
+  b.H = H;
+  b.T = T;
+  b.DQK = d_qk;
+  b.DV = d_v;
+  b.NC = pl.NC;
+  b.q = q;
+  b.k = k;
+  b.v = v;
+  b.f_pre = f_pre;
+  b.o_pre = o_pre;
+  b.bias = norm_bias;
+  b.dh = dh;
+  b.has_init = p.has_init;
+  b.ws_state = p.ws_state;
+  b.ws_min = p.ws_min;
+  b.ws_ga = p.ws_ga;
+  b.ws_gg = p.ws_gg;
+  b.ws_gb = p.ws_gb;
+  b.wsP = ws + bp.off_P;
+  b.wsPt = ws + bp.off_Pt;
+  b.wsD = ws + bp.off_D;
+  b.wsDt = ws + bp.off_Dt;
+  b.ws_rden = reinterpret_cast<float*>(ws + bp.off_rden);
+  b.ws_dz = reinterpret_cast<float*>(ws + bp.off_dz);
+  b.ws_dbias = reinterpret_cast<float*>(ws + bp.off_db);
+  b.ws_dbias_bh = reinterpret_cast<float*>(ws + bp.off_dbh);
+  b.ws_U = reinterpret_cast<float*>(ws + bp.off_U);
+  b.ws_qdq = reinterpret_cast<float*>(ws + bp.off_qdq);
+  b.ws_kdki = reinterpret_cast<float*>(ws + bp.off_kdki);
+  b.ws_kdk = reinterpret_cast<float*>(ws + bp.off_kdk);
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  b.di = di_pre;
+  b.df = df_pre;
+  b.d_o = do_pre;
+  b.dbias = dbias;
+  b.dC0 = dC0;
+  b.dn0 = dn0;
+  if (g_ev0) (void)hipEventRecord(g_ev0, st);
+  e = mlstm::launch_bwd(dt, b, st);
+  if (g_ev1) (void)hipEventRecord(g_ev1, st);
+  if (e != hipSuccess) return fail(MLSTM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
 
 int mlstm_abi_version(void) { return MLSTM_ABI_VERSION; }
 

@@ -1,0 +1,834 @@
+// Chunkwise backward pass of the mLSTM recurrence (vector normaliser, one
+// memory block, chunks of 64 tokens): gradients of sum(dh * h) with respect to
+// q, k, v, the gate preactivations, the output gate, the normaliser bias and
+// the initial state.
+//
+// The forward's state passes (gates, pass 1, pass 2), run with one chunk per
+// superchunk, leave in the workspace the stabilised start state (S~, n~) and
+// stabiliser m of every chunk and the chunk-local gate logs a_j, g_j, b_j (log2
+// units).  From these, per chunk with M_j = max(m_prev, g_j) and M_L its
+// chunk-end value (the forward's own weights):
+//   E_jl = 2^{a_l - M_j} (l <= j),  alpha_j = 2^{m_prev - M_j},
+//   w_j = 2^{a_j - M_L},  e^{-m_j} = 2^{-(b_j + M_j)},
+//   dn~_j = o_j dh_j / den~_j,  dz~_j = -(dh_j . h_j) sign(z~_j) / den~_j when
+//     |z~_j| > e^{-m_j} (else 0),  D'_jl = E_jl (dn~_j . v_l + dz~_j),
+//   dq_j = sum_l D'_jl k_l + alpha_j (S~_prev dn~_j + n~_prev dz~_j),
+//   dk_j = sum_l D'_lj q_l + w_j (G_c v_j + g_c),
+//   dv_j = sum_l E_lj (q_l . k_j) dn~_l + w_j G_c^T k_j,
+// with (G_c, g_c) the backward state at the end of chunk c from the reverse
+// chunk scan  G_{c-1} = 2^{m_prev - M_L} G_c + sum_j alpha_j q_j [dn~_j, dz~_j]^T.
+// q and k enter h only through e^{F_t} q_t and e^{i_t - F_t} k_t (F the
+// cumulative log forget gate), so d i_pre_t = k_t . dk_t and d log f_t is the
+// reverse cumulative sum of q_s . dq_s - k_s . dk_s over s >= t.
+//
+// Kernels (all on the caller's stream, after the forward's state passes):
+//   bwd_scores_kernel  per (batch*head, chunk): Q K^T, the denominators, the
+//                      readout (recomputed), dN V^T; writes P = E.(Q K^T) and
+//                      D' (and transposes), 1/den~, dz~, d o_pre and a bias
+//                      partial.
+//   bwd_dq_kernel      per (batch*head, chunk, 64 features): dq and the chunk's
+//                      local backward state sum_j alpha_j q_j [dn~_j, dz~_j]^T.
+//   bwd_scan_kernel    reverse scan of the local backward states over chunks
+//                      (in place: slot c ends up holding G_c), initial-state
+//                      gradients.
+//   bwd_dkv_kernel     per (batch*head, chunk, 64 features of dk or 64 columns
+//                      of dv): dk, dv.
+//   bwd_gate_kernel    per batch*head: d i_pre, d f_pre (reverse cumulative
+//                      sum), the bias partial of the sequence.
+//   bwd_bias_kernel    d bias summed over the batch.
+//
+// Tiles: 4 waves of 64 lanes own 16 rows each of a 64 x 64 output tile; both
+// MFMA operands sit in LDS with the contraction index contiguous (operands
+// that run the other way are transposed while they are staged).
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace mlstm {
+
+namespace {
+
+constexpr int BL = 64;  // chunk length of the backward pass
+
+template <typename T>
+struct BT {
+  static constexpr int LD = 64 + 16 / (int)sizeof(T);  // LDS row stride (elements)
+};
+
+// acc[n] += A[16 w + r][k] Bt[16 n + c][k] over k in [0, 64) (A, Bt in LDS,
+// row stride BT<T>::LD).  acc[n][i] is row 16 w + 4 lg + i, column 16 n + lr.
+template <typename T>
+__device__ __forceinline__ void mma64(f32x4 (&acc)[4], const T* A, const T* Bt, int w, int lane,
+                                      int lda = BT<T>::LD) {
+  constexpr int LD = BT<T>::LD, K = Mma<T>::K, KL = Mma<T>::KL;
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int k0 = 0; k0 < 64; k0 += K) {
+    const typename Mma<T>::frag a = Mma<T>::load(A + (16 * w + lr) * lda + k0 + KL * lg);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const typename Mma<T>::frag b = Mma<T>::load(Bt + (16 * n + lr) * LD + k0 + KL * lg);
+      acc[n] = Mma<T>::mma(a, b, acc[n]);
+    }
+  }
+}
+
+// dn~ = o dh / den~ for one element (the same expression in every kernel, so
+// that each rounds it identically)
+__device__ __forceinline__ float dn_of(float dh, float o, float rden) { return (dh * o) * rden; }
+
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[4]) {
+#pragma unroll
+  for (int n = 0; n < 4; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// 16 consecutive elements of type S as floats (bytes past the buffer: zero).
+template <typename S>
+__device__ __forceinline__ void load16f(__amdgpu_buffer_rsrc_t r, unsigned byte_off, float (&x)[16]) {
+  if constexpr (sizeof(S) == 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off + 16 * h, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[8 * h + 2 * e] = __uint_as_float(u[e] << 16);
+        x[8 * h + 2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off + 16 * h, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * h + e] = __uint_as_float(u[e]);
+    }
+  }
+}
+
+// Thread tid of 256 covers row tid >> 2, columns 16 (tid & 3) .. +15 of a 64 x 64 tile.
+template <typename T>
+__device__ __forceinline__ void st_row16(T* s, int r, int c0, const float (&x)[16]) {
+  constexpr int LD = BT<T>::LD;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(x[8 * h + 2 * e], x[8 * h + 2 * e + 1]);
+      *reinterpret_cast<u32x4*>(s + r * LD + c0 + 8 * h) = u;
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      *reinterpret_cast<float4*>(s + r * LD + c0 + 4 * h) =
+          make_float4(x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]);
+  }
+}
+template <typename T>
+__device__ __forceinline__ void st_col16(T* s, int r, int c0, const float (&x)[16]) {
+  constexpr int LD = BT<T>::LD;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s[(c0 + e) * LD + r] = from_f32<T>(x[e]);
+}
+
+// Stabiliser quantities of one chunk into LDS (threads 0..63): a_j, M_j,
+// alpha_j, e^{-m_j}, w_j; returns nothing, sets *sdec to 2^{m_prev - M_L}.
+__device__ __forceinline__ void load_chunk_gates(const BwdParams& p, int bh, int c, int tid, float* sa, float* sM,
+                                                 float* sal, float* sem, float* sw) {
+  if (tid < BL) {
+    const size_t tg = (size_t)bh * p.NC * BL + (size_t)c * BL + tid;
+    const float mp = p.ws_min[(size_t)bh * p.NC + c];
+    const float a = p.ws_ga[tg];
+    const float M = fmaxf(mp, p.ws_gg[tg]);
+    const float ML = fmaxf(mp, p.ws_gg[(size_t)bh * p.NC * BL + (size_t)c * BL + BL - 1]);
+    sa[tid] = a;
+    sM[tid] = M;
+    sal[tid] = exp2_fast(mp - M);
+    sem[tid] = exp2_fast(-(p.ws_gb[tg] + M));
+    sw[tid] = exp2_fast(a - ML);
+  }
+}
+
+// ---------------------------------------------------------------- kernel 1
+// The chunk's readout is recomputed here in fp32 (num~ = alpha Q S~_prev +
+// P V) so that dh . h enters dz~ as sum_l P_jl D_jl + alpha_j dn~_j . (S~^T q_j)
+// with the very P, D and dn~ that D' and the dq/dk/dv products use: where the
+// denominator nearly cancels the direct term, rounding h (or any operand) on
+// one side only would leave the cancellation residue in the gradient.
+template <typename T, int DQK>
+__global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
+  constexpr int LD = BT<T>::LD;
+  constexpr int LDQ = DQK + 16 / (int)sizeof(T);
+  constexpr unsigned ES = sizeof(T);
+  __shared__ __attribute__((aligned(16))) T sQ[BL * LDQ];  // Q, token-major
+  __shared__ __attribute__((aligned(16))) T sX[BL * LD];   // K slices, then dN slices  [j][.]
+  __shared__ __attribute__((aligned(16))) T sY[BL * LD];   // V slices                  [l][c]
+  __shared__ __attribute__((aligned(16))) T sVt[BL * LD];  // V^T slices                [c][l]
+  __shared__ __attribute__((aligned(16))) T sP[BL * LD];   // P                         [j][l]
+  __shared__ __attribute__((aligned(16))) T sSt[BL * LD];  // S~^T tiles                [c][d]
+  // bf16: S~ - bf16(S~), so that the state enters the readout to ~2^-16
+  // (the initial state is exact fp32 input)
+  __shared__ __attribute__((aligned(16))) T sSl[sizeof(T) == 2 ? BL * LD : 8];
+  // bf16: dn~ - bf16(dn~), likewise for D and dh . h (a near-cancelling
+  // dn~ . (v_l - y_j) must not see dn~ rounded)
+  __shared__ __attribute__((aligned(16))) T sXl[sizeof(T) == 2 ? BL * LD : 8];
+  __shared__ float sa[BL], sM[BL], sal[BL], sem[BL], sw[BL];
+  __shared__ float sqn[BL], srow[BL], sden[BL], ssg[BL], sdz[BL];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int bh = blockIdx.x / p.NC, c = blockIdx.x % p.NC;
+  const int hd = bh % p.H;
+  const int r = tid >> 2, c0 = 16 * (tid & 3);
+  const int t0 = c * BL;
+  const size_t NST = (size_t)DQK * p.DV + DQK;
+  load_chunk_gates(p, bh, c, tid, sa, sM, sal, sem, sw);
+
+  const bool has_state = p.has_init || c > 0;
+  const float* Sp = p.ws_state + ((size_t)bh * p.NC + c) * NST;
+  const float* nprev = Sp + (size_t)DQK * p.DV;
+  const auto rq = make_rsrc(static_cast<const T*>(p.q) + (size_t)bh * p.T * DQK, (unsigned)(p.T * DQK) * ES);
+  const auto rk = make_rsrc(static_cast<const T*>(p.k) + (size_t)bh * p.T * DQK, (unsigned)(p.T * DQK) * ES);
+
+  // S = Q K^T over feature slices of 64 (Q kept whole); q_j . n~_prev alongside
+  f32x4 accP[4];
+  zero_acc(accP);
+  float qn = 0.f;
+  for (int ds = 0; ds < DQK / 64; ++ds) {
+    float x[16], y[16];
+    load16f<T>(rq, ((unsigned)(t0 + r) * DQK + ds * 64 + c0) * ES, x);
+    load16f<T>(rk, ((unsigned)(t0 + r) * DQK + ds * 64 + c0) * ES, y);
+    if (has_state) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) qn += x[e] * nprev[ds * 64 + c0 + e];
+    }
+    __syncthreads();
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4 u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(x[8 * h + 2 * e], x[8 * h + 2 * e + 1]);
+        *reinterpret_cast<u32x4*>(sQ + r * LDQ + ds * 64 + c0 + 8 * h) = u;
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        *reinterpret_cast<float4*>(sQ + r * LDQ + ds * 64 + c0 + 4 * h) =
+            make_float4(x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]);
+    }
+    st_row16<T>(sX, r, c0, y);
+    __syncthreads();
+    mma64<T>(accP, sQ + ds * 64, sX, w, lane, LDQ);
+  }
+  qn += __shfl_xor(qn, 1, 64);
+  qn += __shfl_xor(qn, 2, 64);
+  if ((tid & 3) == 0) sqn[r] = qn;
+
+  // P = E . S (kept in fp32 registers), its row sums; P and P^T to the
+  // workspace, P to LDS for the readout
+  T* Pw = static_cast<T*>(p.wsP) + ((size_t)bh * p.NC + c) * BL * BL;
+  T* Ptw = static_cast<T*>(p.wsPt) + ((size_t)bh * p.NC + c) * BL * BL;
+  float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int l = 16 * n + lr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 16 * w + 4 * lg + i;
+      const float e = l <= j ? exp2_fast(sa[l] - sM[j]) : 0.f;
+      accP[n][i] *= e;
+      rs[i] += accP[n][i];
+      Pw[j * BL + l] = from_f32<T>(accP[n][i]);
+      sP[j * LD + l] = from_f32<T>(accP[n][i]);
+    }
+    store4f(Ptw + l * BL + 16 * w + 4 * lg, accP[n][0], accP[n][1], accP[n][2], accP[n][3]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) rs[i] += __shfl_xor(rs[i], d, 64);
+    if (lr == 0) srow[16 * w + 4 * lg + i] = rs[i];
+  }
+  __syncthreads();
+  if (tid < BL) {
+    const float bias = p.bias ? p.bias[hd] : 0.f;
+    const float z = srow[tid] + sal[tid] * sqn[tid] + bias * sem[tid];
+    const float den = fmaxf(fabsf(z), sem[tid]);
+    sden[tid] = 1.f / den;
+    ssg[tid] = fabsf(z) > sem[tid] ? (z > 0.f ? 1.f : -1.f) : 0.f;
+  }
+  __syncthreads();
+
+  // over d_v slices: D = dN V^T, the readout num~ = alpha Q S~ + P V, and
+  // dn~ . (Q S~) for dh . h; d o_pre from the recomputed outputs
+  const auto rv = make_rsrc(static_cast<const T*>(p.v) + (size_t)bh * p.T * p.DV, (unsigned)(p.T * p.DV) * ES);
+  const auto rdh = make_rsrc(static_cast<const T*>(p.dh) + (size_t)bh * p.T * p.DV, (unsigned)(p.T * p.DV) * ES);
+  const auto ro = make_rsrc(p.o_pre ? static_cast<const T*>(p.o_pre) + (size_t)bh * p.T * p.DV : nullptr,
+                            p.o_pre ? (unsigned)(p.T * p.DV) * ES : 0u);
+  T* dow = p.d_o ? static_cast<T*>(p.d_o) + (size_t)bh * p.T * p.DV : nullptr;
+  const float rden = sden[r];
+  f32x4 accD[4];
+  zero_acc(accD);
+  float sint[4] = {0.f, 0.f, 0.f, 0.f};  // rows 16 w + 4 lg + i: dn~ . (Q S~) partials
+  for (int cs = 0; cs < p.DV / 64; ++cs) {
+    {
+      const unsigned off = ((unsigned)(t0 + r) * p.DV + cs * 64 + c0) * ES;
+      float g[16], x[16], vv[16];
+      load16f<T>(rdh, off, g);
+      load16f<T>(rv, off, vv);
+      if (p.o_pre) {
+        load16f<T>(ro, off, x);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) g[e] = dn_of(g[e], sigmoidf_(x[e]), rden);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) g[e] = dn_of(g[e], 1.f, rden);
+      }
+      __syncthreads();  // the previous slice's operands are consumed
+      st_row16<T>(sX, r, c0, g);
+      st_row16<T>(sY, r, c0, vv);
+      st_col16<T>(sVt, r, c0, vv);
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) g[e] -= to_f32(from_f32<T>(g[e]));
+        st_row16<T>(sXl, r, c0, g);
+      }
+    }
+    f32x4 accI[4], accN[4];
+    zero_acc(accI);
+    zero_acc(accN);
+    if (has_state) {
+      for (int ds = 0; ds < DQK / 64; ++ds) {
+        float sv[16];
+        const float* src = Sp + (size_t)(ds * 64 + r) * p.DV + cs * 64 + c0;
+#pragma unroll
+        for (int e = 0; e < 16; e += 4) {
+          const float4 u = *reinterpret_cast<const float4*>(src + e);
+          sv[e] = u.x, sv[e + 1] = u.y, sv[e + 2] = u.z, sv[e + 3] = u.w;
+        }
+        if (ds > 0) __syncthreads();  // previous tile consumed
+        st_col16<T>(sSt, r, c0, sv);
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sv[e] -= to_f32(from_f32<T>(sv[e]));
+          st_col16<T>(sSl, r, c0, sv);
+        }
+        __syncthreads();
+        mma64<T>(accI, sQ + ds * 64, sSt, w, lane, LDQ);  // sum_d q_jd S~_dc
+        if constexpr (sizeof(T) == 2) mma64<T>(accI, sQ + ds * 64, sSl, w, lane, LDQ);
+      }
+    } else {
+      __syncthreads();
+    }
+    mma64<T>(accD, sX, sY, w, lane);   // sum_c dn~_jc v_lc
+    if constexpr (sizeof(T) == 2) mma64<T>(accD, sXl, sY, w, lane);
+    mma64<T>(accN, sP, sVt, w, lane);  // sum_l P_jl v_lc
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int col = 16 * n + lr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 16 * w + 4 * lg + i;
+        float dnv = to_f32(sX[j * LD + col]);
+        if constexpr (sizeof(T) == 2) dnv += to_f32(sXl[j * LD + col]);
+        sint[i] += dnv * accI[n][i];
+        if (p.o_pre && t0 + j < p.T) {
+          const size_t e = (size_t)(t0 + j) * p.DV + cs * 64 + col;
+          const float y = (sal[j] * accI[n][i] + accN[n][i]) * sden[j];
+          const float o = sigmoidf_(to_f32(static_cast<const T*>(p.o_pre)[(size_t)bh * p.T * p.DV + e]));
+          const float g = to_f32(static_cast<const T*>(p.dh)[(size_t)bh * p.T * p.DV + e]);
+          dow[e] = from_f32<T>(g * y * (o * (1.f - o)));
+        }
+      }
+    }
+  }
+  // dh . h = dn~ . num~ = sum_l P_jl D_jl + alpha_j dn~_j . (Q S~)_j
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float a = 0.f, b = sint[i];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) a += accP[n][i] * accD[n][i];
+    const int j = 16 * w + 4 * lg + i;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      a += __shfl_xor(a, d, 64);
+      b += __shfl_xor(b, d, 64);
+    }
+    if (lr == 0) {
+      sdz[j] = -(a + sal[j] * b) * ssg[j] * sden[j];
+      srow[j] = b;  // dn~_j . (Q S~)_j
+    }
+  }
+  __syncthreads();
+  // q_j . dq_j and the in-chunk part of k_j . dk_j from the fp32 products
+  // (D'_jl (q_j . k_l) = (D_jl + dz~_j) P_jl):
+  //   q_j . dq_j = sum_l D'_jl S_jl + alpha_j (dn~_j . (Q S~)_j + dz~_j q_j . n~),
+  //   k_j . dk_j = sum_l D'_lj S_lj + w_j k_j . (G_c v_j + g_c)  (last term later)
+  {
+    float rsum[4] = {0.f, 0.f, 0.f, 0.f}, csum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = (accD[n][i] + sdz[16 * w + 4 * lg + i]) * accP[n][i];
+        rsum[i] += x;
+        csum[n] += x;
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) rsum[i] += __shfl_xor(rsum[i], d, 64);
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      csum[n] += __shfl_xor(csum[n], 16, 64);
+      csum[n] += __shfl_xor(csum[n], 32, 64);
+    }
+    __syncthreads();  // srow (dn~ . (Q S~)) is read below, scol reuses sX
+    float* scol = reinterpret_cast<float*>(sX);  // [4 waves][64 columns]
+    if (lg == 0) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) scol[w * 64 + 16 * n + lr] = csum[n];
+    }
+    if (lr == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 16 * w + 4 * lg + i;
+        sqn[j] = rsum[i] + sal[j] * (srow[j] + sdz[j] * sqn[j]);
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < BL) {
+    const float dz = sdz[tid];
+    const size_t tg = (size_t)bh * p.NC * BL + (size_t)c * BL + tid;
+    const float* scol = reinterpret_cast<const float*>(sX);
+    p.ws_qdq[tg] = sqn[tid];
+    p.ws_kdki[tg] = scol[tid] + scol[64 + tid] + scol[128 + tid] + scol[192 + tid];
+    p.ws_rden[tg] = sden[tid];
+    p.ws_dz[tg] = dz;
+    float bsum = (t0 + tid < p.T) ? sem[tid] * dz : 0.f;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) bsum += __shfl_xor(bsum, d, 64);
+    if (tid == 0) p.ws_dbias[(size_t)bh * p.NC + c] = bsum;
+  }
+
+  // D' = E . (dN V^T + dz~) and its transpose
+  T* Dw = static_cast<T*>(p.wsD) + ((size_t)bh * p.NC + c) * BL * BL;
+  T* Dtw = static_cast<T*>(p.wsDt) + ((size_t)bh * p.NC + c) * BL * BL;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int l = 16 * n + lr;
+    float dv4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 16 * w + 4 * lg + i;
+      const float e = l <= j ? exp2_fast(sa[l] - sM[j]) : 0.f;
+      dv4[i] = e * (accD[n][i] + sdz[j]);
+      Dw[j * BL + l] = from_f32<T>(dv4[i]);
+    }
+    store4f(Dtw + l * BL + 16 * w + 4 * lg, dv4[0], dv4[1], dv4[2], dv4[3]);
+  }
+}
+
+// ---------------------------------------------------------------- kernel 2
+template <typename T, int DQK>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
+  constexpr int LD = BT<T>::LD;
+  constexpr unsigned ES = sizeof(T);
+  constexpr int NDT = DQK / 64;
+  __shared__ __attribute__((aligned(16))) T sA[BL * LD];   // D', then dN slices   [j][.]
+  __shared__ __attribute__((aligned(16))) T sB[BL * LD];   // K^T, then S~ slices  [d][.]
+  __shared__ __attribute__((aligned(16))) T sC[BL * LD];   // alpha dN^T slices    [c][j]
+  __shared__ __attribute__((aligned(16))) T sQt[BL * LD];  // Q^T of the tile      [d][j]
+  __shared__ float sa[BL], sM[BL], sal[BL], sem[BL], sw[BL], sden[BL], sdz[BL], snp[64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int dt = blockIdx.x % NDT;
+  const int bc = blockIdx.x / NDT;
+  const int bh = bc / p.NC, c = bc % p.NC;
+  const int r = tid >> 2, c0 = 16 * (tid & 3);
+  const int t0 = c * BL;
+  const size_t NST = (size_t)DQK * p.DV + DQK;
+  load_chunk_gates(p, bh, c, tid, sa, sM, sal, sem, sw);
+  const bool has_state = p.has_init || c > 0;
+  const float* Sp = p.ws_state + ((size_t)bh * p.NC + c) * NST;
+  if (tid < BL) {
+    const size_t tg = (size_t)bh * p.NC * BL + (size_t)c * BL + tid;
+    sden[tid] = p.ws_rden[tg];
+    sdz[tid] = p.ws_dz[tg];
+    snp[tid] = has_state ? Sp[(size_t)DQK * p.DV + dt * 64 + tid] : 0.f;
+  }
+  const auto rq = make_rsrc(static_cast<const T*>(p.q) + (size_t)bh * p.T * DQK, (unsigned)(p.T * DQK) * ES);
+  const auto rk = make_rsrc(static_cast<const T*>(p.k) + (size_t)bh * p.T * DQK, (unsigned)(p.T * DQK) * ES);
+  {
+    float x[16], y[16], d[16];
+    load16f<T>(rq, ((unsigned)(t0 + r) * DQK + dt * 64 + c0) * ES, x);
+    load16f<T>(rk, ((unsigned)(t0 + r) * DQK + dt * 64 + c0) * ES, y);
+    const T* Dw = static_cast<const T*>(p.wsD) + ((size_t)bh * p.NC + c) * BL * BL;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) d[e] = to_f32(Dw[r * BL + c0 + e]);
+    st_col16<T>(sQt, r, c0, x);
+    st_col16<T>(sB, r, c0, y);
+    st_row16<T>(sA, r, c0, d);
+  }
+  __syncthreads();
+  f32x4 acc[4], accx[4];
+  zero_acc(acc);
+  zero_acc(accx);
+  mma64<T>(acc, sA, sB, w, lane);  // sum_l D'_jl k_l
+
+  const auto rdh = make_rsrc(static_cast<const T*>(p.dh) + (size_t)bh * p.T * p.DV, (unsigned)(p.T * p.DV) * ES);
+  const auto ro = make_rsrc(p.o_pre ? static_cast<const T*>(p.o_pre) + (size_t)bh * p.T * p.DV : nullptr,
+                            p.o_pre ? (unsigned)(p.T * p.DV) * ES : 0u);
+  float* Uw = p.ws_U + ((size_t)bh * p.NC + c) * NST;
+  const float rden = sden[r], alr = sal[r];
+  for (int cs = 0; cs < p.DV / 64; ++cs) {
+    float g[16], x[16], s[16];
+    const unsigned off = ((unsigned)(t0 + r) * p.DV + cs * 64 + c0) * ES;
+    load16f<T>(rdh, off, g);
+    if (p.o_pre) {
+      load16f<T>(ro, off, x);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) g[e] = dn_of(g[e], sigmoidf_(x[e]), rden);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) g[e] = dn_of(g[e], 1.f, rden);
+    }
+    if (has_state) {
+      const float* src = Sp + (size_t)(dt * 64 + r) * p.DV + cs * 64 + c0;
+#pragma unroll
+      for (int e = 0; e < 16; e += 4) {
+        const float4 u = *reinterpret_cast<const float4*>(src + e);
+        s[e] = u.x, s[e + 1] = u.y, s[e + 2] = u.z, s[e + 3] = u.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = 0.f;
+    }
+    __syncthreads();  // previous slice's operands are consumed
+    st_row16<T>(sA, r, c0, g);
+    st_row16<T>(sB, r, c0, s);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) x[e] = g[e] * alr;
+    st_col16<T>(sC, r, c0, x);
+    __syncthreads();
+    mma64<T>(accx, sA, sB, w, lane);  // sum_c dN_jc S~_dc
+    f32x4 u[4];
+    zero_acc(u);
+    mma64<T>(u, sQt, sC, w, lane);  // U_dc = sum_j q_jd alpha_j dN_jc
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        Uw[(size_t)(dt * 64 + 16 * w + 4 * lg + i) * p.DV + cs * 64 + 16 * n + lr] = u[n][i];
+  }
+  if (tid < 64) {  // normaliser column: sum_j q_jd alpha_j dz~_j
+    float a = 0.f;
+    for (int j = 0; j < BL; ++j) a += to_f32(sQt[tid * LD + j]) * sal[j] * sdz[j];
+    Uw[(size_t)DQK * p.DV + dt * 64 + tid] = a;
+  }
+  // dq = intra + alpha (S~ dn~ + n~ dz~); q . dq partial
+  T* dqw = static_cast<T*>(p.dq) + (size_t)bh * p.T * DQK;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int d = 16 * n + lr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 16 * w + 4 * lg + i;
+      const float v = acc[n][i] + sal[j] * (accx[n][i] + sdz[j] * snp[d]);
+      if (t0 + j < p.T) dqw[(size_t)(t0 + j) * DQK + dt * 64 + d] = from_f32<T>(v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- kernel 3
+// Thread = 4 consecutive entries of the backward state; chunks in reverse,
+// in windows of SW whose local states are all loaded before any is replaced.
+__global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p, int DQK) {
+  const int bh = blockIdx.y;
+  const size_t NST = (size_t)DQK * p.DV + DQK;
+  const size_t e0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const bool active = e0 < NST;
+  float* base = p.ws_U + (size_t)bh * p.NC * NST;
+  const float* gg = p.ws_gg + (size_t)bh * p.NC * BL;
+  const float* mn = p.ws_min + (size_t)bh * p.NC;
+  float4 G = make_float4(0.f, 0.f, 0.f, 0.f);
+  constexpr int SW = 8;
+  for (int c1 = p.NC - 1; c1 >= 0; c1 -= SW) {
+    float4 u[SW];
+    float dec[SW];
+#pragma unroll
+    for (int j = 0; j < SW; ++j) {
+      const int c = c1 - j;
+      u[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      dec[j] = 0.f;
+      if (c >= 0) {
+        const float mp = mn[c];
+        dec[j] = exp2_fast(mp - fmaxf(mp, gg[(size_t)c * BL + BL - 1]));
+        if (active) u[j] = *reinterpret_cast<const float4*>(base + (size_t)c * NST + e0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < SW; ++j) {
+      const int c = c1 - j;
+      if (c >= 0) {
+        if (active) *reinterpret_cast<float4*>(base + (size_t)c * NST + e0) = G;
+        const float f = c == p.NC - 1 ? 0.f : dec[j];
+        G.x = f * G.x + u[j].x;
+        G.y = f * G.y + u[j].y;
+        G.z = f * G.z + u[j].z;
+        G.w = f * G.w + u[j].w;
+      }
+    }
+  }
+  if (active) {
+    const size_t CS = (size_t)DQK * p.DV;
+    const float g4[4] = {G.x, G.y, G.z, G.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t e = e0 + i;
+      if (e < CS) {
+        if (p.dC0) p.dC0[(size_t)bh * CS + e] = g4[i];
+      } else if (e < NST) {
+        if (p.dn0) p.dn0[(size_t)bh * DQK + (e - CS)] = g4[i];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- kernel 4
+template <typename T, int DQK>
+__global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
+  constexpr int LD = BT<T>::LD;
+  constexpr unsigned ES = sizeof(T);
+  constexpr int NDT = DQK / 64;
+  __shared__ __attribute__((aligned(16))) T sA[BL * LD];
+  __shared__ __attribute__((aligned(16))) T sB[BL * LD];
+  __shared__ __attribute__((aligned(16))) T sK[BL * LD];  // dk tiles: K of the tile [j][d]
+  __shared__ float sa[BL], sM[BL], sal[BL], sem[BL], sw[BL], sg[64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int NVT = p.DV / 64;
+  const int tile = blockIdx.x % (NDT + NVT);
+  const int bc = blockIdx.x / (NDT + NVT);
+  const int bh = bc / p.NC, c = bc % p.NC;
+  const int r = tid >> 2, c0 = 16 * (tid & 3);
+  const int t0 = c * BL;
+  const size_t NST = (size_t)DQK * p.DV + DQK;
+  load_chunk_gates(p, bh, c, tid, sa, sM, sal, sem, sw);
+  const float* Gc = p.ws_U + ((size_t)bh * p.NC + c) * NST;  // G_c, then g_c
+  const auto rq = make_rsrc(static_cast<const T*>(p.q) + (size_t)bh * p.T * DQK, (unsigned)(p.T * DQK) * ES);
+  const auto rk = make_rsrc(static_cast<const T*>(p.k) + (size_t)bh * p.T * DQK, (unsigned)(p.T * DQK) * ES);
+  const auto rv = make_rsrc(static_cast<const T*>(p.v) + (size_t)bh * p.T * p.DV, (unsigned)(p.T * p.DV) * ES);
+  f32x4 acc[4], accx[4];
+  zero_acc(acc);
+  zero_acc(accx);
+  if (tile < NDT) {
+    // dk_j = sum_l D'_lj q_l + w_j (G_c v_j + g_c), features [64 dt, 64 dt + 64)
+    const int dt = tile;
+    if (tid < 64) sg[tid] = Gc[(size_t)DQK * p.DV + dt * 64 + tid];
+    {
+      float x[16], y[16], d[16];
+      load16f<T>(rq, ((unsigned)(t0 + r) * DQK + dt * 64 + c0) * ES, x);
+      load16f<T>(rk, ((unsigned)(t0 + r) * DQK + dt * 64 + c0) * ES, y);
+      const T* Dt = static_cast<const T*>(p.wsDt) + ((size_t)bh * p.NC + c) * BL * BL;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) d[e] = to_f32(Dt[r * BL + c0 + e]);
+      st_row16<T>(sA, r, c0, d);
+      st_col16<T>(sB, r, c0, x);
+      st_row16<T>(sK, r, c0, y);
+    }
+    __syncthreads();
+    mma64<T>(acc, sA, sB, w, lane);
+    for (int cs = 0; cs < p.DV / 64; ++cs) {
+      float vv[16], s[16];
+      load16f<T>(rv, ((unsigned)(t0 + r) * p.DV + cs * 64 + c0) * ES, vv);
+      const float* src = Gc + (size_t)(dt * 64 + r) * p.DV + cs * 64 + c0;
+#pragma unroll
+      for (int e = 0; e < 16; e += 4) {
+        const float4 u = *reinterpret_cast<const float4*>(src + e);
+        s[e] = u.x, s[e + 1] = u.y, s[e + 2] = u.z, s[e + 3] = u.w;
+      }
+      __syncthreads();
+      st_row16<T>(sA, r, c0, vv);
+      st_row16<T>(sB, r, c0, s);
+      __syncthreads();
+      mma64<T>(accx, sA, sB, w, lane);  // sum_c v_jc G_dc
+    }
+    T* dkw = static_cast<T*>(p.dk) + (size_t)bh * p.T * DQK;
+    float kd[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int d = 16 * n + lr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 16 * w + 4 * lg + i;
+        const float x = sw[j] * (accx[n][i] + sg[d]);
+        const float v = acc[n][i] + x;
+        if (t0 + j < p.T) dkw[(size_t)(t0 + j) * DQK + dt * 64 + d] = from_f32<T>(v);
+        kd[i] += to_f32(sK[j * LD + d]) * x;  // w_j k_j . (G_c v_j + g_c)
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) kd[i] += __shfl_xor(kd[i], d, 64);
+      if (lr == 0) p.ws_kdk[((size_t)bh * p.NC * BL + (size_t)c * BL + 16 * w + 4 * lg + i) * NDT + dt] = kd[i];
+    }
+  } else {
+    // dv_j = sum_l P_lj dn~_l + w_j G_c^T k_j, columns [64 ct, 64 ct + 64)
+    const int ct = tile - NDT;
+    const auto rdh = make_rsrc(static_cast<const T*>(p.dh) + (size_t)bh * p.T * p.DV, (unsigned)(p.T * p.DV) * ES);
+    const auto ro = make_rsrc(p.o_pre ? static_cast<const T*>(p.o_pre) + (size_t)bh * p.T * p.DV : nullptr,
+                              p.o_pre ? (unsigned)(p.T * p.DV) * ES : 0u);
+    {
+      const float rden = p.ws_rden[(size_t)bh * p.NC * BL + (size_t)c * BL + r];
+      float g[16], x[16], d[16];
+      const unsigned off = ((unsigned)(t0 + r) * p.DV + ct * 64 + c0) * ES;
+      load16f<T>(rdh, off, g);
+      if (p.o_pre) {
+        load16f<T>(ro, off, x);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) g[e] = dn_of(g[e], sigmoidf_(x[e]), rden);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) g[e] = dn_of(g[e], 1.f, rden);
+      }
+      const T* Pt = static_cast<const T*>(p.wsPt) + ((size_t)bh * p.NC + c) * BL * BL;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) d[e] = to_f32(Pt[r * BL + c0 + e]);
+      st_row16<T>(sA, r, c0, d);
+      st_col16<T>(sB, r, c0, g);
+    }
+    __syncthreads();
+    mma64<T>(acc, sA, sB, w, lane);  // sum_l P_lj dn~_lc
+    for (int ds = 0; ds < NDT; ++ds) {
+      float y[16], s[16];
+      load16f<T>(rk, ((unsigned)(t0 + r) * DQK + ds * 64 + c0) * ES, y);
+      const float* src = Gc + (size_t)(ds * 64 + r) * p.DV + ct * 64 + c0;
+#pragma unroll
+      for (int e = 0; e < 16; e += 4) {
+        const float4 u = *reinterpret_cast<const float4*>(src + e);
+        s[e] = u.x, s[e + 1] = u.y, s[e + 2] = u.z, s[e + 3] = u.w;
+      }
+      __syncthreads();
+      st_row16<T>(sA, r, c0, y);
+      st_col16<T>(sB, r, c0, s);  // G^T [c][d]
+      __syncthreads();
+      mma64<T>(accx, sA, sB, w, lane);  // sum_d k_jd G_dc
+    }
+    T* dvw = static_cast<T*>(p.dv) + (size_t)bh * p.T * p.DV;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int col = 16 * n + lr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 16 * w + 4 * lg + i;
+        const float v = acc[n][i] + sw[j] * accx[n][i];
+        if (t0 + j < p.T) dvw[(size_t)(t0 + j) * p.DV + ct * 64 + col] = from_f32<T>(v);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- kernel 5
+// Per batch*head: d i_pre_t = k_t . dk_t; d log f_t = sum_{s >= t} (q_s . dq_s -
+// k_s . dk_s), in blocks of 256 tokens from the end; d f_pre = d log f *
+// sigmoid(-f_pre).  Also the sequence's bias partial.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_gate_kernel(BwdParams p, int NDT) {
+  __shared__ float swt[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int bh = blockIdx.x;
+  const size_t tb = (size_t)bh * p.NC * BL;
+  const T* fpre = static_cast<const T*>(p.f_pre) + (size_t)bh * p.T;
+  T* diw = static_cast<T*>(p.di) + (size_t)bh * p.T;
+  T* dfw = static_cast<T*>(p.df) + (size_t)bh * p.T;
+  float carry = 0.f;
+  for (int b0 = ((p.T - 1) / 256) * 256; b0 >= 0; b0 -= 256) {
+    const int t = b0 + 255 - tid;  // thread 0 takes the last token of the block
+    float kdk = 0.f, dF = 0.f;
+    if (t < p.T) {
+      kdk = p.ws_kdki[tb + t];
+      for (int d = 0; d < NDT; ++d) kdk += p.ws_kdk[(tb + t) * NDT + d];
+      dF = p.ws_qdq[tb + t] - kdk;
+    }
+    // inclusive prefix sum in thread order = suffix sum in token order
+    float s = dF;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float y = __shfl_up(s, d, 64);
+      if (lane >= d) s += y;
+    }
+    if (lane == 63) swt[w] = s;
+    __syncthreads();
+    float before = carry;
+    for (int i = 0; i < w; ++i) before += swt[i];
+    float total = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) total += swt[i];
+    __syncthreads();
+    if (t < p.T) {
+      const float dlf = before + s;
+      const float f = to_f32(fpre[t]);
+      diw[t] = from_f32<T>(kdk);
+      dfw[t] = from_f32<T>(dlf * sigmoidf_(-f));
+    }
+    carry += total;
+  }
+  if (tid < 64) {
+    float a = 0.f;
+    for (int c = tid; c < p.NC; c += 64) a += p.ws_dbias[(size_t)bh * p.NC + c];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) a += __shfl_xor(a, d, 64);
+    if (tid == 0) p.ws_dbias_bh[bh] = a;
+  }
+}
+
+__global__ void bwd_bias_kernel(BwdParams p) {
+  for (int hd = threadIdx.x; hd < p.H; hd += blockDim.x) {
+    float a = 0.f;
+    for (int b = 0; b < p.B; ++b) a += p.ws_dbias_bh[(size_t)b * p.H + hd];
+    p.dbias[hd] = a;
+  }
+}
+
+template <typename T, int DQK>
+hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
+  const unsigned BH = (unsigned)(p.B * p.H);
+  const unsigned nch = BH * (unsigned)p.NC;
+  hipLaunchKernelGGL((bwd_scores_kernel<T, DQK>), dim3(nch), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, DQK>), dim3(nch * (DQK / 64)), dim3(256), 0, stream, p);
+  const size_t NST = (size_t)DQK * p.DV + DQK;
+  hipLaunchKernelGGL(bwd_scan_kernel, dim3((unsigned)((NST / 4 + 255) / 256), BH), dim3(256), 0, stream, p, DQK);
+  hipLaunchKernelGGL((bwd_dkv_kernel<T, DQK>), dim3(nch * (DQK / 64 + p.DV / 64)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_gate_kernel<T>), dim3(BH), dim3(256), 0, stream, p, DQK / 64);
+  if (p.dbias) hipLaunchKernelGGL(bwd_bias_kernel, dim3(1), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_supported(int dtype, int dqk, int dv) {
+  if (dv % 64) return false;
+  if (dtype == 1) return dqk == 64 || dqk == 128 || dqk == 256;
+  return dqk == 64;
+}
+
+hipError_t launch_bwd(int dtype, const BwdParams& p, hipStream_t stream) {
+  if (dtype == 1) {
+    if (p.DQK == 64) return launch_bwd_t<__bf16, 64>(p, stream);
+    if (p.DQK == 128) return launch_bwd_t<__bf16, 128>(p, stream);
+    if (p.DQK == 256) return launch_bwd_t<__bf16, 256>(p, stream);
+  } else if (p.DQK == 64) {
+    return launch_bwd_t<float, 64>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mlstm

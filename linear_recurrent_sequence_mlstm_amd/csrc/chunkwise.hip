@@ -1606,6 +1606,7 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
   const size_t nstate = CS + (RET ? 0 : DQK);
   dim3 g2((unsigned)((nstate / 4 + 255) / 256), (unsigned)BH);
   hipLaunchKernelGGL((superchunk_scan_kernel<RET>), g2, dim3(256), 0, stream, s);
+  if (!p.h) return hipGetLastError();  // state passes only (the backward's recompute)
   dim3 g3((unsigned)(BH * p.nslices * p.NS));
   if (ev0) (void)hipEventRecord(ev0, stream);
   if constexpr (GN)

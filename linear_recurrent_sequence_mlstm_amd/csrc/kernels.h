@@ -93,4 +93,47 @@ hipError_t launch_step(int dtype, const StepParams& p, hipStream_t stream, int n
 hipError_t launch_retention_step(int dtype, const StepParams& p, hipStream_t stream);
 bool step_supported(int dqk, int dv, int nb);
 
+// Chunkwise backward (mLSTM, vector normaliser, one memory block, chunks of
+// 64 tokens).  The ws_* forward pointers are those of a forward plan with one
+// chunk per superchunk after its state passes ran.
+struct BwdParams {
+  int B, H, T, DQK, DV, NC;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* f_pre;
+  const void* o_pre;
+  const float* bias;
+  const void* dh;
+  int has_init;
+  const float* ws_state;  // [B*H][NC][d_qk d_v + d_qk] chunk start states
+  const float* ws_min;    // [B*H][NC] stabiliser (log2) at chunk starts
+  const float* ws_ga;     // [B*H][NC*64] a_j, prefix maxima g_j, b_j (log2)
+  const float* ws_gg;
+  const float* ws_gb;
+  void* wsP;   // [B*H][NC][64][64] E.(Q K^T), and transposed
+  void* wsPt;
+  void* wsD;   // [B*H][NC][64][64] D', and transposed
+  void* wsDt;
+  float* ws_rden;     // [B*H][NC*64] 1 / den~
+  float* ws_dz;       // [B*H][NC*64] dz~
+  float* ws_dbias;    // [B*H][NC] bias partials of the chunks
+  float* ws_dbias_bh; // [B*H]
+  float* ws_U;        // [B*H][NC][d_qk d_v + d_qk] local, then scanned, backward states
+  float* ws_qdq;      // [B*H][NC*64] q . dq
+  float* ws_kdki;     // [B*H][NC*64] in-chunk part of k . dk
+  float* ws_kdk;      // [B*H][NC*64][d_qk/64] partials of the rest of k . dk
+  void* dq;
+  void* dk;
+  void* dv;
+  void* di;
+  void* df;
+  void* d_o;
+  float* dbias;
+  float* dC0;
+  float* dn0;
+};
+bool bwd_supported(int dtype, int dqk, int dv);
+hipError_t launch_bwd(int dtype, const BwdParams& p, hipStream_t stream);
+
 }  // namespace mlstm

@@ -178,3 +178,10 @@ def workload(name: str, **override):
                         f_mix=spec.get("f_mix", False),
                         with_o=spec.get("with_o", False), bias=spec.get("bias"),
                         chunk=spec.get("chunk", 64))
+
+
+def grad_output(shape, *, seed, dtype="bf16", scale=1.0) -> torch.Tensor:
+    """Seeded incoming gradient dh ~ N(0, 1) * scale of the given shape, cast
+    to dtype (the loss sum(dh * h) of a backward pass)."""
+    g = torch.Generator().manual_seed(int(seed))
+    return (torch.randn(*shape, generator=g) * scale).to(_DT[dtype]).contiguous()
