@@ -18,8 +18,9 @@ with a fresh bf16 token per step; it reports achieved HBM GB/s.
 (RetNet retention B=8 H=4 d=64 T=2048, also with its per-head group norm
 fused; xLSTM-v2 block-diagonal B=4 H=4 d=64 nb=2 T=65536, also with per-block
 denominators; the 7B prefill with an output gate, and with the scalar
-normaliser) and the retention decode step on the RetNet shape: tokens/s per
-call and its algorithmic bytes against HBM.
+normaliser), the retention decode step on the RetNet shape, and the backward
+pass of the 7B prefill workload: tokens/s per call and its algorithmic bytes
+against HBM (``backward`` runs that last one alone).
 
 ``roofline`` is measured live: HIP events recorded by the library right before
 and after its main kernel (mlstm_set_profile_events) give that kernel's
@@ -205,7 +206,21 @@ def retention_work(B, H, T, dk, dv, L=64):
     return byts, flops
 
 
-def bench_variants(torch, mlstm, workload, args, dev):
+def backward_work(B, H, T, dqk, dv, L=64):
+    """Algorithmic bytes and flops of one chunkwise backward: q, k, v, dh and
+    the gates read once, dq, dk, dv and the gate gradients written once, the
+    fp32 initial-state gradient written once; flops of the products the
+    chunkwise backward performs, the recompute of the chunk states included:
+    12 d_qk d_v + 6 L (d_qk + d_v) per token and head (six state-sized
+    products, three L x L x d_qk and three L x L x d_v ones)."""
+    e = 2
+    byts = B * H * T * (2 * dqk + 2 * dv + 2) * e + B * H * T * (2 * dqk + dv + 2) * e
+    byts += B * H * (dqk * dv + dqk) * 4
+    flops = B * H * T * (12 * dqk * dv + 6 * L * (dqk + dv))
+    return byts, flops
+
+
+def bench_variants(torch, mlstm, workload, args, dev, only_backward=False):
     """The retention and block-diagonal workloads through the same chunkwise
     kernels: fence-free events around every call (all launches of it) and
     the library's events around its main kernel.  Enough distinct input sets
@@ -237,6 +252,31 @@ def bench_variants(torch, mlstm, workload, args, dev):
         if kev:
             kev.close()
         return r
+
+    # backward pass of the 7B prefill workload (state passes recomputed,
+    # gradients of all inputs and of the initial state); the library's events
+    # bracket its six backward kernels
+    from linear_recurrent_sequence_mlstm_amd.workloads import grad_output
+    x = workload("xlstm7b_prefill_T8192")
+    B, H, T, dqk = x.q.shape
+    dv = x.v.shape[-1]
+    sets = [x.to(dev), x.to(dev)]
+    dhs = [grad_output((B, H, T, dv), seed=7000 + i).to(dev) for i in range(len(sets))]
+    ws = torch.empty(mlstm.lib().mlstm_chunkwise_bwd_workspace_bytes(B, H, T, dqk, dv, 1, 64, mlstm.BF16),
+                     dtype=torch.uint8, device=dev)
+
+    def call_bwd(i):
+        g = sets[i]
+        mlstm.chunkwise_bwd(g.q, g.k, g.v, g.i_pre, g.f_pre, dhs[i], None, g.bias, workspace=ws)
+
+    nb_steps = max(1, args.variant_steps // 4)
+    r = timed(call_bwd, len(sets), nb_steps, nb_steps)
+    byts, flops = backward_work(B, H, T, dqk, dv)
+    out.append(dict(workload="xlstm7b_prefill_T8192_backward", B=B, H=H, T=T, d_qk=dqk, d_v=dv, **r,
+                    bytes=byts, flops=flops, tokens=B * T))
+    del sets, dhs, ws
+    if only_backward:
+        return out
 
     # RetNet multi-scale retention: B=8, H=4, d=64, T=2048 (34 MB per call)
     q, k, v = workload("retnet_msr_T2048")
@@ -401,7 +441,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variant-steps", type=int, default=100,
                     help="timed calls of the retention and block-diagonal workloads (0: skip them)")
-    ap.add_argument("--only", choices=("prefill", "decode", "copy", "variants"),
+    ap.add_argument("--only", choices=("prefill", "decode", "copy", "variants", "backward"),
                     help="run one leg alone and print its raw figures (for profiler runs)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -425,6 +465,8 @@ def main():
             r = bench_decode(torch, mlstm, workload, args, dev)
         elif args.only == "variants":
             r = dict(variants=bench_variants(torch, mlstm, workload, args, dev))
+        elif args.only == "backward":
+            r = dict(variants=bench_variants(torch, mlstm, workload, args, dev, only_backward=True))
         else:
             r = copy_calibration(torch, dev)
         print(json.dumps(dict(leg=args.only, **r)))

@@ -278,9 +278,9 @@ size_t mlstm_chunkwise_bwd_workspace_bytes(int B, int H, int T, int d_qk, int d_
  * MLSTM_E_UNSUPPORTED.  workspace: at least mlstm_chunkwise_bwd_workspace_bytes
  * bytes, 256-byte aligned (it holds the start state of every chunk and the
  * backward state at every chunk end, fp32: 2 (d_qk d_v + d_qk) 4 bytes per
- * chunk and batch*head).  Enqueues the forward's state passes and six
+ * chunk and batch*head).  Enqueues the forward's state passes and eight
  * backward kernels on stream; profile events set by mlstm_set_profile_events
- * bracket the six backward kernels.
+ * bracket the backward kernels.
  */
 int mlstm_chunkwise_bwd(int B, int H, int T, int d_qk, int d_v, int num_blocks,
                         int chunk, mlstm_dtype dt, const void* q, const void* k,

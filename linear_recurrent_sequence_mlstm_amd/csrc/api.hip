@@ -153,7 +153,7 @@ int plan_bwd(int B, int H, int T, int dqk, int dv, int nb, int chunk, int dt, Bw
   bp->off_db = o;
   o += align256(BH * NC * 4);
   bp->off_dbh = o;
-  o += align256(BH * 4);
+  o += align256(BH * NC * 4);
   bp->off_qdq = o;
   o += align256(BH * NCL * 4);
   bp->off_kdki = o;
@@ -253,7 +253,7 @@ int mlstm_chunkwise_bwd(int B, int H, int T, int d_qk, int d_v, int num_blocks, 
   b.ws_rden = reinterpret_cast<float*>(ws + bp.off_rden);
   b.ws_dz = reinterpret_cast<float*>(ws + bp.off_dz);
   b.ws_dbias = reinterpret_cast<float*>(ws + bp.off_db);
-  b.ws_dbias_bh = reinterpret_cast<float*>(ws + bp.off_dbh);
+  b.ws_ctot = reinterpret_cast<float*>(ws + bp.off_dbh);
   b.ws_U = reinterpret_cast<float*>(ws + bp.off_U);
   b.ws_qdq = reinterpret_cast<float*>(ws + bp.off_qdq);
   b.ws_kdki = reinterpret_cast<float*>(ws + bp.off_kdki);

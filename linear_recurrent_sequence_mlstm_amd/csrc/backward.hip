@@ -33,9 +33,10 @@
 //                      gradients.
 //   bwd_dkv_kernel     per (batch*head, chunk, 64 features of dk or 64 columns
 //                      of dv): dk, dv.
-//   bwd_gate_kernel    per batch*head: d i_pre, d f_pre (reverse cumulative
-//                      sum), the bias partial of the sequence.
-//   bwd_bias_kernel    d bias summed over the batch.
+//   bwd_gate_total_kernel, bwd_gate_kernel  per (batch*head, chunk): d i_pre,
+//                      d f_pre (reverse cumulative sum: chunk totals, then
+//                      suffix sums with the later chunks' totals).
+//   bwd_bias_kernel    d bias summed over the batch and the chunks.
 //
 // Tiles: 4 waves of 64 lanes own 16 rows each of a 64 x 64 output tile; both
 // MFMA operands sit in LDS with the contraction index contiguous (operands
@@ -737,63 +738,58 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- kernel 5
-// Per batch*head: d i_pre_t = k_t . dk_t; d log f_t = sum_{s >= t} (q_s . dq_s -
-// k_s . dk_s), in blocks of 256 tokens from the end; d f_pre = d log f *
-// sigmoid(-f_pre).  Also the sequence's bias partial.
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_gate_kernel(BwdParams p, int NDT) {
-  __shared__ float swt[4];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int bh = blockIdx.x;
-  const size_t tb = (size_t)bh * p.NC * BL;
-  const T* fpre = static_cast<const T*>(p.f_pre) + (size_t)bh * p.T;
-  T* diw = static_cast<T*>(p.di) + (size_t)bh * p.T;
-  T* dfw = static_cast<T*>(p.df) + (size_t)bh * p.T;
-  float carry = 0.f;
-  for (int b0 = ((p.T - 1) / 256) * 256; b0 >= 0; b0 -= 256) {
-    const int t = b0 + 255 - tid;  // thread 0 takes the last token of the block
-    float kdk = 0.f, dF = 0.f;
-    if (t < p.T) {
-      kdk = p.ws_kdki[tb + t];
-      for (int d = 0; d < NDT; ++d) kdk += p.ws_kdk[(tb + t) * NDT + d];
-      dF = p.ws_qdq[tb + t] - kdk;
-    }
-    // inclusive prefix sum in thread order = suffix sum in token order
-    float s = dF;
+// d i_pre_t = k_t . dk_t; d log f_t = sum_{s >= t} (q_s . dq_s - k_s . dk_s);
+// d f_pre = d log f * sigmoid(-f_pre).  Two passes over (batch*head, chunk)
+// work-groups of one wave: the chunk totals of q.dq - k.dk, then each chunk's
+// in-chunk suffix sums plus the totals of the chunks after it.
+__global__ __launch_bounds__(64) void bwd_gate_total_kernel(BwdParams p, int NDT) {
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x / p.NC, c = blockIdx.x % p.NC;
+  const size_t tg = (size_t)bh * p.NC * BL + (size_t)c * BL + lane;
+  float kdk = p.ws_kdki[tg];
+  for (int d = 0; d < NDT; ++d) kdk += p.ws_kdk[tg * NDT + d];
+  float dF = c * BL + lane < p.T ? p.ws_qdq[tg] - kdk : 0.f;
+  p.ws_kdki[tg] = kdk;  // k . dk, complete
+  p.ws_qdq[tg] = dF;    // q . dq - k . dk
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const float y = __shfl_up(s, d, 64);
-      if (lane >= d) s += y;
-    }
-    if (lane == 63) swt[w] = s;
-    __syncthreads();
-    float before = carry;
-    for (int i = 0; i < w; ++i) before += swt[i];
-    float total = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) total += swt[i];
-    __syncthreads();
-    if (t < p.T) {
-      const float dlf = before + s;
-      const float f = to_f32(fpre[t]);
-      diw[t] = from_f32<T>(kdk);
-      dfw[t] = from_f32<T>(dlf * sigmoidf_(-f));
-    }
-    carry += total;
-  }
-  if (tid < 64) {
-    float a = 0.f;
-    for (int c = tid; c < p.NC; c += 64) a += p.ws_dbias[(size_t)bh * p.NC + c];
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) a += __shfl_xor(a, d, 64);
-    if (tid == 0) p.ws_dbias_bh[bh] = a;
-  }
+  for (int d = 1; d < 64; d <<= 1) dF += __shfl_xor(dF, d, 64);
+  if (lane == 0) p.ws_ctot[(size_t)bh * p.NC + c] = dF;
 }
 
+template <typename T>
+__global__ __launch_bounds__(64) void bwd_gate_kernel(BwdParams p) {
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x / p.NC, c = blockIdx.x % p.NC;
+  const size_t tg = (size_t)bh * p.NC * BL + (size_t)c * BL + lane;
+  float carry = 0.f;
+  for (int c2 = c + 1 + lane; c2 < p.NC; c2 += 64) carry += p.ws_ctot[(size_t)bh * p.NC + c2];
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) carry += __shfl_xor(carry, d, 64);
+  // suffix sum within the chunk: lane 63 - l takes token l
+  const int l = 63 - lane;
+  const size_t tl = (size_t)bh * p.NC * BL + (size_t)c * BL + l;
+  float s = p.ws_qdq[tl];
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float y = __shfl_up(s, d, 64);
+    if (lane >= d) s += y;
+  }
+  const int t = c * BL + l;
+  if (t < p.T) {
+    const size_t o = (size_t)bh * p.T + t;
+    const float f = to_f32(static_cast<const T*>(p.f_pre)[o]);
+    static_cast<T*>(p.di)[o] = from_f32<T>(p.ws_kdki[tl]);
+    static_cast<T*>(p.df)[o] = from_f32<T>((carry + s) * sigmoidf_(-f));
+  }
+  (void)tg;
+}
+
+// d bias_h = sum over the batch and the chunks of the bias partials
 __global__ void bwd_bias_kernel(BwdParams p) {
   for (int hd = threadIdx.x; hd < p.H; hd += blockDim.x) {
     float a = 0.f;
-    for (int b = 0; b < p.B; ++b) a += p.ws_dbias_bh[(size_t)b * p.H + hd];
+    for (int b = 0; b < p.B; ++b)
+      for (int c = 0; c < p.NC; ++c) a += p.ws_dbias[((size_t)b * p.H + hd) * p.NC + c];
     p.dbias[hd] = a;
   }
 }
@@ -807,7 +803,8 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   const size_t NST = (size_t)DQK * p.DV + DQK;
   hipLaunchKernelGGL(bwd_scan_kernel, dim3((unsigned)((NST / 4 + 255) / 256), BH), dim3(256), 0, stream, p, DQK);
   hipLaunchKernelGGL((bwd_dkv_kernel<T, DQK>), dim3(nch * (DQK / 64 + p.DV / 64)), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL((bwd_gate_kernel<T>), dim3(BH), dim3(256), 0, stream, p, DQK / 64);
+  hipLaunchKernelGGL(bwd_gate_total_kernel, dim3(nch), dim3(64), 0, stream, p, DQK / 64);
+  hipLaunchKernelGGL((bwd_gate_kernel<T>), dim3(nch), dim3(64), 0, stream, p);
   if (p.dbias) hipLaunchKernelGGL(bwd_bias_kernel, dim3(1), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

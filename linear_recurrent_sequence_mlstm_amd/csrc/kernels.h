@@ -118,7 +118,7 @@ struct BwdParams {
   float* ws_rden;     // [B*H][NC*64] 1 / den~
   float* ws_dz;       // [B*H][NC*64] dz~
   float* ws_dbias;    // [B*H][NC] bias partials of the chunks
-  float* ws_dbias_bh; // [B*H]
+  float* ws_ctot;     // [B*H][NC] chunk totals of q . dq - k . dk
   float* ws_U;        // [B*H][NC][d_qk d_v + d_qk] local, then scanned, backward states
   float* ws_qdq;      // [B*H][NC*64] q . dq
   float* ws_kdki;     // [B*H][NC*64] in-chunk part of k . dk
