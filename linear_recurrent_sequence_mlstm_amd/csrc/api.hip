@@ -49,7 +49,7 @@ struct Plan {
 // Checks shared by the mLSTM and retention chunkwise entry points and the
 // workspace queries; fills the plan.  Returns MLSTM_OK or an error code.
 int plan_chunkwise(int B, int H, int T, int dqk, int dv, int nb, int chunk, int dt, bool ret,
-                   Plan* pl, bool chunk_states = false) {
+                   Plan* pl) {
   if (dt != MLSTM_F32 && dt != MLSTM_BF16) return fail(MLSTM_E_DTYPE, "unknown dtype %d", dt);
   if (B < 1 || H < 1 || T < 1 || dqk < 1 || dv < 1 || nb < 1)
     return fail(MLSTM_E_SHAPE, "sizes must be positive (B=%d H=%d T=%d d_qk=%d d_v=%d nb=%d)", B, H, T,
@@ -83,7 +83,6 @@ int plan_chunkwise(int B, int H, int T, int dqk, int dv, int nb, int chunk, int 
   if (ns > pl->NC) ns = pl->NC;
   int G = (int)((pl->NC + ns - 1) / ns);
   if (env_superchunk_chunks()) G = env_superchunk_chunks();
-  if (chunk_states) G = 1;  // the backward pass needs every chunk's start state
   if (G * chunk > 1024) G = 1024 / chunk;  // pass 1 holds the gate factors of <= 1024 tokens
   if (G > pl->NC) G = pl->NC;
   pl->G = G;
@@ -125,11 +124,12 @@ int launch(const Plan& pl, mlstm::ChunkParams& p, void* workspace, size_t worksp
 // the backward's own arrays.
 struct BwdPlan {
   Plan fwd;
-  size_t off_U, off_P, off_Pt, off_D, off_Dt, off_rden, off_dz, off_db, off_dbh, off_qdq, off_kdki, off_kdk, bytes;
+  size_t off_cst, off_cmin, off_U, off_P, off_Pt, off_D, off_Dt, off_rden, off_dz, off_db, off_dbh, off_qdq, off_kdki,
+      off_kdk, bytes;
 };
 
 int plan_bwd(int B, int H, int T, int dqk, int dv, int nb, int chunk, int dt, BwdPlan* bp) {
-  const int rc = plan_chunkwise(B, H, T, dqk, dv, nb, chunk, dt, false, &bp->fwd, true);
+  const int rc = plan_chunkwise(B, H, T, dqk, dv, nb, chunk, dt, false, &bp->fwd);
   if (rc != MLSTM_OK) return rc;
   if (nb != 1) return fail(MLSTM_E_UNSUPPORTED, "the backward pass takes num_blocks = 1 (got %d)", nb);
   if (chunk != 64) return fail(MLSTM_E_UNSUPPORTED, "the backward pass takes chunk = 64 (got %d)", chunk);
@@ -138,6 +138,10 @@ int plan_bwd(int B, int H, int T, int dqk, int dv, int nb, int chunk, int dt, Bw
                 dv);
   const size_t BH = (size_t)B * H, NC = bp->fwd.NC, NCL = NC * 64, es = dt ? 2 : 4;
   size_t o = align256(bp->fwd.bytes);
+  bp->off_cst = o;
+  o += align256(BH * NC * ((size_t)dqk * dv + dqk) * 4);
+  bp->off_cmin = o;
+  o += align256(BH * NC * 4);
   bp->off_U = o;
   o += align256(BH * NC * ((size_t)dqk * dv + dqk) * 4);
   const size_t tile = align256(BH * NC * 64 * 64 * es);
@@ -233,6 +237,8 @@ int mlstm_chunkwise_bwd(int B, int H, int T, int d_qk, int d_v, int num_blocks, 
   b.DQK = d_qk;
   b.DV = d_v;
   b.NC = pl.NC;
+  b.G = pl.G;
+  b.NS = pl.NS;
   b.q = q;
   b.k = k;
   b.v = v;
@@ -241,8 +247,10 @@ int mlstm_chunkwise_bwd(int B, int H, int T, int d_qk, int d_v, int num_blocks, 
   b.bias = norm_bias;
   b.dh = dh;
   b.has_init = p.has_init;
-  b.ws_state = p.ws_state;
-  b.ws_min = p.ws_min;
+  b.sc_state = p.ws_state;
+  b.sc_min = p.ws_min;
+  b.ws_state = reinterpret_cast<float*>(ws + bp.off_cst);
+  b.ws_min = reinterpret_cast<float*>(ws + bp.off_cmin);
   b.ws_ga = p.ws_ga;
   b.ws_gg = p.ws_gg;
   b.ws_gb = p.ws_gb;

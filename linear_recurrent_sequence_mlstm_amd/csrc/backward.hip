@@ -3,10 +3,10 @@
 // q, k, v, the gate preactivations, the output gate, the normaliser bias and
 // the initial state.
 //
-// The forward's state passes (gates, pass 1, pass 2), run with one chunk per
-// superchunk, leave in the workspace the stabilised start state (S~, n~) and
-// stabiliser m of every chunk and the chunk-local gate logs a_j, g_j, b_j (log2
-// units).  From these, per chunk with M_j = max(m_prev, g_j) and M_L its
+// The forward's state passes (gates, pass 1, pass 2) leave in the workspace
+// the superchunk start states and the chunk-local gate logs a_j, g_j, b_j (log2
+// units); bwd_chunk_states_kernel expands them into the stabilised start state
+// (S~, n~) and stabiliser m of every chunk.  From these, per chunk with M_j = max(m_prev, g_j) and M_L its
 // chunk-end value (the forward's own weights):
 //   E_jl = 2^{a_l - M_j} (l <= j),  alpha_j = 2^{m_prev - M_j},
 //   w_j = 2^{a_j - M_L},  e^{-m_j} = 2^{-(b_j + M_j)},
@@ -22,6 +22,8 @@
 // reverse cumulative sum of q_s . dq_s - k_s . dk_s over s >= t.
 //
 // Kernels (all on the caller's stream, after the forward's state passes):
+//   bwd_chunk_states_kernel  per (batch*head, superchunk, 64 x 64 state tile):
+//                      every chunk's start state.
 //   bwd_scores_kernel  per (batch*head, chunk): Q K^T, the denominators, the
 //                      readout (recomputed), dN V^T; writes P = E.(Q K^T) and
 //                      D' (and transposes), 1/den~, dz~, d o_pre and a bias
@@ -107,6 +109,15 @@ __device__ __forceinline__ void load16f(__amdgpu_buffer_rsrc_t r, unsigned byte_
   }
 }
 
+// 16 consecutive fp32 values (in bounds).
+__device__ __forceinline__ void ld16(const float* src, float (&x)[16]) {
+#pragma unroll
+  for (int e = 0; e < 16; e += 4) {
+    const float4 u = *reinterpret_cast<const float4*>(src + e);
+    x[e] = u.x, x[e + 1] = u.y, x[e + 2] = u.z, x[e + 3] = u.w;
+  }
+}
+
 // Thread tid of 256 covers row tid >> 2, columns 16 (tid & 3) .. +15 of a 64 x 64 tile.
 template <typename T>
 __device__ __forceinline__ void st_row16(T* s, int r, int c0, const float (&x)[16]) {
@@ -148,6 +159,115 @@ __device__ __forceinline__ void load_chunk_gates(const BwdParams& p, int bh, int
     sal[tid] = exp2_fast(mp - M);
     sem[tid] = exp2_fast(-(p.ws_gb[tg] + M));
     sw[tid] = exp2_fast(a - ML);
+  }
+}
+
+// ---------------------------------------------------------------- kernel 0
+// Every chunk's start state from the superchunk start states of the
+// forward's passes 1-2: per (batch*head, superchunk, 64 x 64 state tile) the
+// superchunk's chunks in order, the tile in registers (MFMA layout: rows
+// d = 16 w + 4 lg + i, columns c = 16 n + lr):
+//   write S~ (and, column tile 0, n~ and m) as chunk c's start state,
+//   S~ <- 2^{m - M_L} S~ + (w . K_c)^T V_c,  n~ <- 2^{m - M_L} n~ + sum_l w_l k_l,
+//   m <- b_L + M_L,  with M_L = max(m, g_L) and w_l = 2^{a_l - M_L}
+// (the forward's state update; K and V of the next chunk load during the
+// current one's product).
+template <typename T, int DQK>
+__global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
+  constexpr int LD = BT<T>::LD;
+  constexpr unsigned ES = sizeof(T);
+  constexpr int NDT = DQK / 64;
+  __shared__ __attribute__((aligned(16))) T sKt[BL * LD];  // (w . K)^T  [d][l]
+  __shared__ __attribute__((aligned(16))) T sVt[BL * LD];  // V^T        [c][l]
+  __shared__ float sw[BL];
+  __shared__ float sdec;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int NVT = p.DV / 64;
+  const int ct = blockIdx.x % NVT;
+  const int dt = (blockIdx.x / NVT) % NDT;
+  const int bs = blockIdx.x / (NVT * NDT);
+  const int bh = bs / p.NS, sc = bs % p.NS;
+  const int r = tid >> 2, c0 = 16 * (tid & 3);
+  const size_t NST = (size_t)DQK * p.DV + DQK;
+  const bool lead = ct == 0;  // writes n~ and m as well
+  const size_t NCL = (size_t)p.NC * BL;
+  // superchunk start state (slot 0 holds the initial state only if given)
+  f32x4 acc[4];
+  zero_acc(acc);
+  // n~[64 dt + r] lives in thread 4 r of the lead work-group
+  float nn = 0.f;
+  const bool has = p.has_init || sc > 0;
+  const float* S0 = p.sc_state + ((size_t)bh * p.NS + sc) * NST;
+  if (has) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[n][i] = S0[(size_t)(dt * 64 + 16 * w + 4 * lg + i) * p.DV + ct * 64 + 16 * n + lr];
+    if (lead) nn = S0[(size_t)DQK * p.DV + dt * 64 + r];
+  }
+  float m = p.sc_min[(size_t)bh * p.NS + sc];  // meaningful in threads below 64
+  const int cb = sc * p.G, ce = min(p.NC, cb + p.G);
+  const auto rk = make_rsrc(static_cast<const T*>(p.k) + (size_t)bh * p.T * DQK, (unsigned)(p.T * DQK) * ES);
+  const auto rv = make_rsrc(static_cast<const T*>(p.v) + (size_t)bh * p.T * p.DV, (unsigned)(p.T * p.DV) * ES);
+  float kx[16], vx[16];
+  load16f<T>(rk, ((unsigned)(cb * BL + r) * DQK + dt * 64 + c0) * ES, kx);
+  load16f<T>(rv, ((unsigned)(cb * BL + r) * p.DV + ct * 64 + c0) * ES, vx);
+  // gate logs of the chunk to update next, one chunk ahead
+  float ga = 0.f, gL = 0.f, bL = 0.f;
+  if (tid < BL) {
+    const size_t tg = (size_t)bh * NCL + (size_t)cb * BL;
+    ga = p.ws_ga[tg + tid];
+    gL = p.ws_gg[tg + BL - 1];
+    bL = p.ws_gb[tg + BL - 1];
+  }
+  for (int c = cb; c < ce; ++c) {
+    float* St = p.ws_state + ((size_t)bh * p.NC + c) * NST;
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) St[(size_t)(dt * 64 + 16 * w + 4 * lg + i) * p.DV + ct * 64 + 16 * n + lr] = acc[n][i];
+    if (lead && (tid & 3) == 0) St[(size_t)DQK * p.DV + dt * 64 + r] = nn;
+    if (lead && dt == 0 && tid == 0) p.ws_min[(size_t)bh * p.NC + c] = m;
+    if (c + 1 == ce) break;  // the next superchunk starts from its own start state
+    __syncthreads();  // previous chunk's operands are consumed
+    if (tid < BL) {
+      const float ML = fmaxf(m, gL);
+      sw[tid] = exp2_fast(ga - ML);
+      if (tid == 0) sdec = exp2_fast(m - ML);
+      m = bL + ML;
+      if (c + 2 < ce) {
+        const size_t tg = (size_t)bh * NCL + (size_t)(c + 1) * BL;
+        ga = p.ws_ga[tg + tid];
+        gL = p.ws_gg[tg + BL - 1];
+        bL = p.ws_gb[tg + BL - 1];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) kx[e] *= sw[r];
+    st_col16<T>(sKt, r, c0, kx);
+    st_col16<T>(sVt, r, c0, vx);
+    if (c + 2 < ce) {
+      load16f<T>(rk, ((unsigned)((c + 1) * BL + r) * DQK + dt * 64 + c0) * ES, kx);
+      load16f<T>(rv, ((unsigned)((c + 1) * BL + r) * p.DV + ct * 64 + c0) * ES, vx);
+    }
+    __syncthreads();
+    const float dec = sdec;
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[n][i] *= dec;
+    mma64<T>(acc, sKt, sVt, w, lane);
+    if (lead) {  // n~[64 dt + r] += sum_l w_l k_l, four threads per row
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) a += to_f32(sKt[r * LD + 16 * (tid & 3) + e]);
+      a += __shfl_xor(a, 1, 64);
+      a += __shfl_xor(a, 2, 64);
+      nn = dec * nn + a;
+    }
   }
 }
 
@@ -273,42 +393,42 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
   f32x4 accD[4];
   zero_acc(accD);
   float sint[4] = {0.f, 0.f, 0.f, 0.f};  // rows 16 w + 4 lg + i: dn~ . (Q S~) partials
-  for (int cs = 0; cs < p.DV / 64; ++cs) {
-    {
-      const unsigned off = ((unsigned)(t0 + r) * p.DV + cs * 64 + c0) * ES;
-      float g[16], x[16], vv[16];
-      load16f<T>(rdh, off, g);
-      load16f<T>(rv, off, vv);
-      if (p.o_pre) {
-        load16f<T>(ro, off, x);
+  // Global loads run one step ahead: slice cs + 1's dh, o_pre, v and the next
+  // S~ tile are in flight while the current ones are multiplied.
+  const int NCS = p.DV / 64;
+  constexpr int NDS = DQK / 64;
+  float g[16], x[16], vv[16], sv[16];
+  auto load_slice = [&](int cs) {
+    const unsigned off = ((unsigned)(t0 + r) * p.DV + cs * 64 + c0) * ES;
+    load16f<T>(rdh, off, g);
+    load16f<T>(rv, off, vv);
+    if (p.o_pre) load16f<T>(ro, off, x);
+  };
+  load_slice(0);
+  if (has_state) ld16(Sp + (size_t)r * p.DV + c0, sv);
+  for (int cs = 0; cs < NCS; ++cs) {
+    if (p.o_pre) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) g[e] = dn_of(g[e], sigmoidf_(x[e]), rden);
-      } else {
+      for (int e = 0; e < 16; ++e) g[e] = dn_of(g[e], sigmoidf_(x[e]), rden);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) g[e] = dn_of(g[e], 1.f, rden);
-      }
-      __syncthreads();  // the previous slice's operands are consumed
-      st_row16<T>(sX, r, c0, g);
-      st_row16<T>(sY, r, c0, vv);
-      st_col16<T>(sVt, r, c0, vv);
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) g[e] -= to_f32(from_f32<T>(g[e]));
-        st_row16<T>(sXl, r, c0, g);
-      }
+      for (int e = 0; e < 16; ++e) g[e] = dn_of(g[e], 1.f, rden);
     }
+    __syncthreads();  // the previous slice's operands are consumed
+    st_row16<T>(sX, r, c0, g);
+    st_row16<T>(sY, r, c0, vv);
+    st_col16<T>(sVt, r, c0, vv);
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) g[e] -= to_f32(from_f32<T>(g[e]));
+      st_row16<T>(sXl, r, c0, g);
+    }
+    if (cs + 1 < NCS) load_slice(cs + 1);
     f32x4 accI[4], accN[4];
     zero_acc(accI);
     zero_acc(accN);
     if (has_state) {
-      for (int ds = 0; ds < DQK / 64; ++ds) {
-        float sv[16];
-        const float* src = Sp + (size_t)(ds * 64 + r) * p.DV + cs * 64 + c0;
-#pragma unroll
-        for (int e = 0; e < 16; e += 4) {
-          const float4 u = *reinterpret_cast<const float4*>(src + e);
-          sv[e] = u.x, sv[e + 1] = u.y, sv[e + 2] = u.z, sv[e + 3] = u.w;
-        }
+      for (int ds = 0; ds < NDS; ++ds) {
         if (ds > 0) __syncthreads();  // previous tile consumed
         st_col16<T>(sSt, r, c0, sv);
         if constexpr (sizeof(T) == 2) {
@@ -316,6 +436,8 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
           for (int e = 0; e < 16; ++e) sv[e] -= to_f32(from_f32<T>(sv[e]));
           st_col16<T>(sSl, r, c0, sv);
         }
+        if (ds + 1 < NDS) ld16(Sp + (size_t)((ds + 1) * 64 + r) * p.DV + cs * 64 + c0, sv);
+        else if (cs + 1 < NCS) ld16(Sp + (size_t)r * p.DV + (cs + 1) * 64 + c0, sv);
         __syncthreads();
         mma64<T>(accI, sQ + ds * 64, sSt, w, lane, LDQ);  // sum_d q_jd S~_dc
         if constexpr (sizeof(T) == 2) mma64<T>(accI, sQ + ds * 64, sSl, w, lane, LDQ);
@@ -487,35 +609,34 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
                             p.o_pre ? (unsigned)(p.T * p.DV) * ES : 0u);
   float* Uw = p.ws_U + ((size_t)bh * p.NC + c) * NST;
   const float rden = sden[r], alr = sal[r];
-  for (int cs = 0; cs < p.DV / 64; ++cs) {
-    float g[16], x[16], s[16];
+  const int NCS = p.DV / 64;
+  float g[16], x[16], sv[16];  // one slice ahead (see the scores kernel)
+  auto load_slice = [&](int cs) {
     const unsigned off = ((unsigned)(t0 + r) * p.DV + cs * 64 + c0) * ES;
     load16f<T>(rdh, off, g);
+    if (p.o_pre) load16f<T>(ro, off, x);
+    if (has_state) ld16(Sp + (size_t)(dt * 64 + r) * p.DV + cs * 64 + c0, sv);
+  };
+  if (!has_state) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sv[e] = 0.f;
+  }
+  load_slice(0);
+  for (int cs = 0; cs < NCS; ++cs) {
     if (p.o_pre) {
-      load16f<T>(ro, off, x);
 #pragma unroll
       for (int e = 0; e < 16; ++e) g[e] = dn_of(g[e], sigmoidf_(x[e]), rden);
     } else {
 #pragma unroll
       for (int e = 0; e < 16; ++e) g[e] = dn_of(g[e], 1.f, rden);
     }
-    if (has_state) {
-      const float* src = Sp + (size_t)(dt * 64 + r) * p.DV + cs * 64 + c0;
-#pragma unroll
-      for (int e = 0; e < 16; e += 4) {
-        const float4 u = *reinterpret_cast<const float4*>(src + e);
-        s[e] = u.x, s[e + 1] = u.y, s[e + 2] = u.z, s[e + 3] = u.w;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] = 0.f;
-    }
     __syncthreads();  // previous slice's operands are consumed
     st_row16<T>(sA, r, c0, g);
-    st_row16<T>(sB, r, c0, s);
+    st_row16<T>(sB, r, c0, sv);
 #pragma unroll
     for (int e = 0; e < 16; ++e) x[e] = g[e] * alr;
     st_col16<T>(sC, r, c0, x);
+    if (cs + 1 < NCS) load_slice(cs + 1);
     __syncthreads();
     mma64<T>(accx, sA, sB, w, lane);  // sum_c dN_jc S~_dc
     f32x4 u[4];
@@ -646,18 +767,18 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
     }
     __syncthreads();
     mma64<T>(acc, sA, sB, w, lane);
-    for (int cs = 0; cs < p.DV / 64; ++cs) {
-      float vv[16], s[16];
-      load16f<T>(rv, ((unsigned)(t0 + r) * p.DV + cs * 64 + c0) * ES, vv);
-      const float* src = Gc + (size_t)(dt * 64 + r) * p.DV + cs * 64 + c0;
-#pragma unroll
-      for (int e = 0; e < 16; e += 4) {
-        const float4 u = *reinterpret_cast<const float4*>(src + e);
-        s[e] = u.x, s[e + 1] = u.y, s[e + 2] = u.z, s[e + 3] = u.w;
-      }
+    const int NCS = p.DV / 64;
+    float vv[16], sv[16];  // one slice ahead
+    load16f<T>(rv, ((unsigned)(t0 + r) * p.DV + c0) * ES, vv);
+    ld16(Gc + (size_t)(dt * 64 + r) * p.DV + c0, sv);
+    for (int cs = 0; cs < NCS; ++cs) {
       __syncthreads();
       st_row16<T>(sA, r, c0, vv);
-      st_row16<T>(sB, r, c0, s);
+      st_row16<T>(sB, r, c0, sv);
+      if (cs + 1 < NCS) {
+        load16f<T>(rv, ((unsigned)(t0 + r) * p.DV + (cs + 1) * 64 + c0) * ES, vv);
+        ld16(Gc + (size_t)(dt * 64 + r) * p.DV + (cs + 1) * 64 + c0, sv);
+      }
       __syncthreads();
       mma64<T>(accx, sA, sB, w, lane);  // sum_c v_jc G_dc
     }
@@ -708,18 +829,17 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
     }
     __syncthreads();
     mma64<T>(acc, sA, sB, w, lane);  // sum_l P_lj dn~_lc
+    float y[16], sv[16];  // one feature slice ahead
+    load16f<T>(rk, ((unsigned)(t0 + r) * DQK + c0) * ES, y);
+    ld16(Gc + (size_t)r * p.DV + ct * 64 + c0, sv);
     for (int ds = 0; ds < NDT; ++ds) {
-      float y[16], s[16];
-      load16f<T>(rk, ((unsigned)(t0 + r) * DQK + ds * 64 + c0) * ES, y);
-      const float* src = Gc + (size_t)(ds * 64 + r) * p.DV + ct * 64 + c0;
-#pragma unroll
-      for (int e = 0; e < 16; e += 4) {
-        const float4 u = *reinterpret_cast<const float4*>(src + e);
-        s[e] = u.x, s[e + 1] = u.y, s[e + 2] = u.z, s[e + 3] = u.w;
-      }
       __syncthreads();
       st_row16<T>(sA, r, c0, y);
-      st_col16<T>(sB, r, c0, s);  // G^T [c][d]
+      st_col16<T>(sB, r, c0, sv);  // G^T [c][d]
+      if (ds + 1 < NDT) {
+        load16f<T>(rk, ((unsigned)(t0 + r) * DQK + (ds + 1) * 64 + c0) * ES, y);
+        ld16(Gc + (size_t)((ds + 1) * 64 + r) * p.DV + ct * 64 + c0, sv);
+      }
       __syncthreads();
       mma64<T>(accx, sA, sB, w, lane);  // sum_d k_jd G_dc
     }
@@ -798,6 +918,8 @@ template <typename T, int DQK>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   const unsigned BH = (unsigned)(p.B * p.H);
   const unsigned nch = BH * (unsigned)p.NC;
+  hipLaunchKernelGGL((bwd_chunk_states_kernel<T, DQK>), dim3(BH * p.NS * (DQK / 64) * (p.DV / 64)), dim3(256), 0,
+                     stream, p);
   hipLaunchKernelGGL((bwd_scores_kernel<T, DQK>), dim3(nch), dim3(256), 0, stream, p);
   hipLaunchKernelGGL((bwd_dq_kernel<T, DQK>), dim3(nch * (DQK / 64)), dim3(256), 0, stream, p);
   const size_t NST = (size_t)DQK * p.DV + DQK;

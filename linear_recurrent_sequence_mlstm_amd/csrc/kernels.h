@@ -94,10 +94,9 @@ hipError_t launch_retention_step(int dtype, const StepParams& p, hipStream_t str
 bool step_supported(int dqk, int dv, int nb);
 
 // Chunkwise backward (mLSTM, vector normaliser, one memory block, chunks of
-// 64 tokens).  The ws_* forward pointers are those of a forward plan with one
-// chunk per superchunk after its state passes ran.
+// 64 tokens), after the forward plan's state passes ran.
 struct BwdParams {
-  int B, H, T, DQK, DV, NC;
+  int B, H, T, DQK, DV, NC, G, NS;
   const void* q;
   const void* k;
   const void* v;
@@ -106,8 +105,10 @@ struct BwdParams {
   const float* bias;
   const void* dh;
   int has_init;
-  const float* ws_state;  // [B*H][NC][d_qk d_v + d_qk] chunk start states
-  const float* ws_min;    // [B*H][NC] stabiliser (log2) at chunk starts
+  const float* sc_state;  // [B*H][NS][d_qk d_v + d_qk] superchunk start states (forward pass 2)
+  const float* sc_min;    // [B*H][NS] stabiliser (log2) at superchunk starts
+  float* ws_state;        // [B*H][NC][d_qk d_v + d_qk] chunk start states
+  float* ws_min;          // [B*H][NC] stabiliser (log2) at chunk starts
   const float* ws_ga;     // [B*H][NC*64] a_j, prefix maxima g_j, b_j (log2)
   const float* ws_gg;
   const float* ws_gb;
