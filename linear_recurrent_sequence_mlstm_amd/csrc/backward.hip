@@ -40,9 +40,10 @@
 //                      suffix sums with the later chunks' totals).
 //   bwd_bias_kernel    d bias summed over the batch and the chunks.
 //
-// Tiles: 4 waves of 64 lanes own 16 rows each of a 64 x 64 output tile; both
-// MFMA operands sit in LDS with the contraction index contiguous (operands
-// that run the other way are transposed while they are staged).
+// Tiles: 4 waves of 64 lanes own 16 rows each of a 64 x 64 output tile.
+// Every operand is staged in LDS as it lies in memory (16-byte row stores);
+// one whose contraction index runs along its rows is read with transposing
+// LDS reads (mma64x).
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -59,19 +60,61 @@ struct BT {
   static constexpr int LD = 64 + 16 / (int)sizeof(T);  // LDS row stride (elements)
 };
 
-// acc[n] += A[16 w + r][k] Bt[16 n + c][k] over k in [0, 64) (A, Bt in LDS,
-// row stride BT<T>::LD).  acc[n][i] is row 16 w + 4 lg + i, column 16 n + lr.
-template <typename T>
-__device__ __forceinline__ void mma64(f32x4 (&acc)[4], const T* A, const T* Bt, int w, int lane,
-                                      int lda = BT<T>::LD) {
-  constexpr int LD = BT<T>::LD, K = Mma<T>::K, KL = Mma<T>::KL;
+// MFMA operand fragments with the contraction index k in the order
+// krow(lg, e) = 4 lg + (e & 3) + 16 (e >> 2) within each 32-wide k block (bf16;
+// fp32: k = lg), so that an operand stored with k along its columns (row-major,
+// k contiguous: two 8-byte reads) and one stored with k along its rows (two
+// transposing ds_read_b64_tr_b16) agree on which k is which.
+__device__ __forceinline__ bf16x8 frag_kcols(const __bf16* t, int ld, int row, int k0, int lg, int lr) {
+  (void)lr;
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(t + row * ld + k0 + 4 * lg);
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(t + row * ld + k0 + 16 + 4 * lg);
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = a[e];
+    r[4 + e] = b[e];
+  }
+  return r;
+}
+// rows k of column col0 + lr: source lane lr addresses row k0 + 4 lg + lr/4,
+// columns col0 + 4 (lr & 3) .. +3, so that output lane lr receives column col0 + lr
+__device__ __forceinline__ bf16x8 frag_krows(const __bf16* t, int ld, int col0, int k0, int lg, int lr) {
+  const __bf16* p = t + (k0 + 4 * lg + (lr >> 2)) * ld + col0 + 4 * (lr & 3);
+  const bf16x4 a = ds_read_tr16(p);
+  const bf16x4 b = ds_read_tr16(p + 16 * ld);
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = a[e];
+    r[4 + e] = b[e];
+  }
+  return r;
+}
+__device__ __forceinline__ float frag_kcols(const float* t, int ld, int row, int k0, int lg, int lr) {
+  (void)lr;
+  return t[row * ld + k0 + lg];
+}
+__device__ __forceinline__ float frag_krows(const float* t, int ld, int col0, int k0, int lg, int lr) {
+  return t[(k0 + lg) * ld + col0 + lr];
+}
+
+// acc[n] += A B over k in [0, 64) for the wave's rows 16 w .. +15 and all 64
+// columns.  A (rows m, contraction k): AR ? stored [k][m] : stored [m][k];
+// B (contraction k, columns n): BR ? stored [k][n] : stored [n][k].
+// acc[n][i] is row 16 w + 4 lg + i, column 16 n + lr.
+template <typename T, bool AR, bool BR>
+__device__ __forceinline__ void mma64x(f32x4 (&acc)[4], const T* A, int lda, const T* B, int ldb, int w, int lane) {
+  constexpr int K = Mma<T>::K;
   const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
   for (int k0 = 0; k0 < 64; k0 += K) {
-    const typename Mma<T>::frag a = Mma<T>::load(A + (16 * w + lr) * lda + k0 + KL * lg);
+    const typename Mma<T>::frag a =
+        AR ? frag_krows(A, lda, 16 * w, k0, lg, lr) : frag_kcols(A, lda, 16 * w + lr, k0, lg, lr);
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-      const typename Mma<T>::frag b = Mma<T>::load(Bt + (16 * n + lr) * LD + k0 + KL * lg);
+      const typename Mma<T>::frag b =
+          BR ? frag_krows(B, ldb, 16 * n, k0, lg, lr) : frag_kcols(B, ldb, 16 * n + lr, k0, lg, lr);
       acc[n] = Mma<T>::mma(a, b, acc[n]);
     }
   }
@@ -137,13 +180,6 @@ __device__ __forceinline__ void st_row16(T* s, int r, int c0, const float (&x)[1
           make_float4(x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]);
   }
 }
-template <typename T>
-__device__ __forceinline__ void st_col16(T* s, int r, int c0, const float (&x)[16]) {
-  constexpr int LD = BT<T>::LD;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) s[(c0 + e) * LD + r] = from_f32<T>(x[e]);
-}
-
 // Stabiliser quantities of one chunk into LDS (threads 0..63): a_j, M_j,
 // alpha_j, e^{-m_j}, w_j; returns nothing, sets *sdec to 2^{m_prev - M_L}.
 __device__ __forceinline__ void load_chunk_gates(const BwdParams& p, int bh, int c, int tid, float* sa, float* sM,
@@ -177,8 +213,8 @@ __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
   constexpr int LD = BT<T>::LD;
   constexpr unsigned ES = sizeof(T);
   constexpr int NDT = DQK / 64;
-  __shared__ __attribute__((aligned(16))) T sKt[BL * LD];  // (w . K)^T  [d][l]
-  __shared__ __attribute__((aligned(16))) T sVt[BL * LD];  // V^T        [c][l]
+  __shared__ __attribute__((aligned(16))) T sK[BL * LD];  // w . K, token-major [l][d]
+  __shared__ __attribute__((aligned(16))) T sV[BL * LD];  // V, token-major     [l][c]
   __shared__ float sw[BL];
   __shared__ float sdec;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -193,7 +229,9 @@ __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
   const size_t NST = (size_t)DQK * p.DV + DQK;
   const bool lead = ct == 0;  // writes n~ and m as well
   const size_t NCL = (size_t)p.NC * BL;
-  // superchunk start state (slot 0 holds the initial state only if given)
+  // The tile is held transposed, so that each lane owns 4 consecutive state
+  // columns: acc[n][i] = S~[64 dt + 16 n + lr][64 ct + 16 w + 4 lg + i].
+  const size_t toff = (size_t)(dt * 64 + lr) * p.DV + ct * 64 + 16 * w + 4 * lg;
   f32x4 acc[4];
   zero_acc(acc);
   // n~[64 dt + r] lives in thread 4 r of the lead work-group
@@ -202,9 +240,10 @@ __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
   const float* S0 = p.sc_state + ((size_t)bh * p.NS + sc) * NST;
   if (has) {
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[n][i] = S0[(size_t)(dt * 64 + 16 * w + 4 * lg + i) * p.DV + ct * 64 + 16 * n + lr];
+    for (int n = 0; n < 4; ++n) {
+      const float4 u = *reinterpret_cast<const float4*>(S0 + toff + (size_t)16 * n * p.DV);
+      acc[n] = f32x4{u.x, u.y, u.z, u.w};
+    }
     if (lead) nn = S0[(size_t)DQK * p.DV + dt * 64 + r];
   }
   float m = p.sc_min[(size_t)bh * p.NS + sc];  // meaningful in threads below 64
@@ -226,8 +265,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
     float* St = p.ws_state + ((size_t)bh * p.NC + c) * NST;
 #pragma unroll
     for (int n = 0; n < 4; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) St[(size_t)(dt * 64 + 16 * w + 4 * lg + i) * p.DV + ct * 64 + 16 * n + lr] = acc[n][i];
+      *reinterpret_cast<float4*>(St + toff + (size_t)16 * n * p.DV) = make_float4(acc[n][0], acc[n][1], acc[n][2], acc[n][3]);
     if (lead && (tid & 3) == 0) St[(size_t)DQK * p.DV + dt * 64 + r] = nn;
     if (lead && dt == 0 && tid == 0) p.ws_min[(size_t)bh * p.NC + c] = m;
     if (c + 1 == ce) break;  // the next superchunk starts from its own start state
@@ -245,10 +283,11 @@ __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
       }
     }
     __syncthreads();
+    const float wr = sw[r];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) kx[e] *= sw[r];
-    st_col16<T>(sKt, r, c0, kx);
-    st_col16<T>(sVt, r, c0, vx);
+    for (int e = 0; e < 16; ++e) kx[e] *= wr;
+    st_row16<T>(sK, r, c0, kx);
+    st_row16<T>(sV, r, c0, vx);
     if (c + 2 < ce) {
       load16f<T>(rk, ((unsigned)((c + 1) * BL + r) * DQK + dt * 64 + c0) * ES, kx);
       load16f<T>(rv, ((unsigned)((c + 1) * BL + r) * p.DV + ct * 64 + c0) * ES, vx);
@@ -259,11 +298,11 @@ __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
     for (int n = 0; n < 4; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[n][i] *= dec;
-    mma64<T>(acc, sKt, sVt, w, lane);
+    mma64x<T, true, true>(acc, sV, LD, sK, LD, w, lane);  // S~^T += V^T (w . K)
     if (lead) {  // n~[64 dt + r] += sum_l w_l k_l, four threads per row
       float a = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) a += to_f32(sKt[r * LD + 16 * (tid & 3) + e]);
+      for (int e = 0; e < 16; ++e) a += to_f32(sK[(16 * (tid & 3) + e) * LD + r]);
       a += __shfl_xor(a, 1, 64);
       a += __shfl_xor(a, 2, 64);
       nn = dec * nn + a;
@@ -285,9 +324,8 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) T sQ[BL * LDQ];  // Q, token-major
   __shared__ __attribute__((aligned(16))) T sX[BL * LD];   // K slices, then dN slices  [j][.]
   __shared__ __attribute__((aligned(16))) T sY[BL * LD];   // V slices                  [l][c]
-  __shared__ __attribute__((aligned(16))) T sVt[BL * LD];  // V^T slices                [c][l]
   __shared__ __attribute__((aligned(16))) T sP[BL * LD];   // P                         [j][l]
-  __shared__ __attribute__((aligned(16))) T sSt[BL * LD];  // S~^T tiles                [c][d]
+  __shared__ __attribute__((aligned(16))) T sSt[BL * LD];  // S~ tiles                  [d][c]
   // bf16: S~ - bf16(S~), so that the state enters the readout to ~2^-16
   // (the initial state is exact fp32 input)
   __shared__ __attribute__((aligned(16))) T sSl[sizeof(T) == 2 ? BL * LD : 8];
@@ -341,7 +379,7 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
     }
     st_row16<T>(sX, r, c0, y);
     __syncthreads();
-    mma64<T>(accP, sQ + ds * 64, sX, w, lane, LDQ);
+    mma64x<T, false, false>(accP, sQ + ds * 64, LDQ, sX, LD, w, lane);
   }
   qn += __shfl_xor(qn, 1, 64);
   qn += __shfl_xor(qn, 2, 64);
@@ -417,7 +455,6 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
     __syncthreads();  // the previous slice's operands are consumed
     st_row16<T>(sX, r, c0, g);
     st_row16<T>(sY, r, c0, vv);
-    st_col16<T>(sVt, r, c0, vv);
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) g[e] -= to_f32(from_f32<T>(g[e]));
@@ -430,24 +467,24 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
     if (has_state) {
       for (int ds = 0; ds < NDS; ++ds) {
         if (ds > 0) __syncthreads();  // previous tile consumed
-        st_col16<T>(sSt, r, c0, sv);
+        st_row16<T>(sSt, r, c0, sv);
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) sv[e] -= to_f32(from_f32<T>(sv[e]));
-          st_col16<T>(sSl, r, c0, sv);
+          st_row16<T>(sSl, r, c0, sv);
         }
         if (ds + 1 < NDS) ld16(Sp + (size_t)((ds + 1) * 64 + r) * p.DV + cs * 64 + c0, sv);
         else if (cs + 1 < NCS) ld16(Sp + (size_t)r * p.DV + (cs + 1) * 64 + c0, sv);
         __syncthreads();
-        mma64<T>(accI, sQ + ds * 64, sSt, w, lane, LDQ);  // sum_d q_jd S~_dc
-        if constexpr (sizeof(T) == 2) mma64<T>(accI, sQ + ds * 64, sSl, w, lane, LDQ);
+        mma64x<T, false, true>(accI, sQ + ds * 64, LDQ, sSt, LD, w, lane);  // sum_d q_jd S~_dc
+        if constexpr (sizeof(T) == 2) mma64x<T, false, true>(accI, sQ + ds * 64, LDQ, sSl, LD, w, lane);
       }
     } else {
       __syncthreads();
     }
-    mma64<T>(accD, sX, sY, w, lane);   // sum_c dn~_jc v_lc
-    if constexpr (sizeof(T) == 2) mma64<T>(accD, sXl, sY, w, lane);
-    mma64<T>(accN, sP, sVt, w, lane);  // sum_l P_jl v_lc
+    mma64x<T, false, false>(accD, sX, LD, sY, LD, w, lane);  // sum_c dn~_jc v_lc
+    if constexpr (sizeof(T) == 2) mma64x<T, false, false>(accD, sXl, LD, sY, LD, w, lane);
+    mma64x<T, false, true>(accN, sP, LD, sY, LD, w, lane);  // sum_l P_jl v_lc
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       const int col = 16 * n + lr;
@@ -562,10 +599,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   constexpr int LD = BT<T>::LD;
   constexpr unsigned ES = sizeof(T);
   constexpr int NDT = DQK / 64;
-  __shared__ __attribute__((aligned(16))) T sA[BL * LD];   // D', then dN slices   [j][.]
-  __shared__ __attribute__((aligned(16))) T sB[BL * LD];   // K^T, then S~ slices  [d][.]
-  __shared__ __attribute__((aligned(16))) T sC[BL * LD];   // alpha dN^T slices    [c][j]
-  __shared__ __attribute__((aligned(16))) T sQt[BL * LD];  // Q^T of the tile      [d][j]
+  __shared__ __attribute__((aligned(16))) T sA[BL * LD];  // D', then dN slices     [j][.]
+  __shared__ __attribute__((aligned(16))) T sB[BL * LD];  // K tile, then S~ slices [l][d], [d][c]
+  __shared__ __attribute__((aligned(16))) T sC[BL * LD];  // alpha dN slices        [j][c]
+  __shared__ __attribute__((aligned(16))) T sQ[BL * LD];  // Q of the tile          [j][d]
   __shared__ float sa[BL], sM[BL], sal[BL], sem[BL], sw[BL], sden[BL], sdz[BL], snp[64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -594,15 +631,15 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     const T* Dw = static_cast<const T*>(p.wsD) + ((size_t)bh * p.NC + c) * BL * BL;
 #pragma unroll
     for (int e = 0; e < 16; ++e) d[e] = to_f32(Dw[r * BL + c0 + e]);
-    st_col16<T>(sQt, r, c0, x);
-    st_col16<T>(sB, r, c0, y);
+    st_row16<T>(sQ, r, c0, x);
+    st_row16<T>(sB, r, c0, y);
     st_row16<T>(sA, r, c0, d);
   }
   __syncthreads();
   f32x4 acc[4], accx[4];
   zero_acc(acc);
   zero_acc(accx);
-  mma64<T>(acc, sA, sB, w, lane);  // sum_l D'_jl k_l
+  mma64x<T, false, true>(acc, sA, LD, sB, LD, w, lane);  // sum_l D'_jl k_l
 
   const auto rdh = make_rsrc(static_cast<const T*>(p.dh) + (size_t)bh * p.T * p.DV, (unsigned)(p.T * p.DV) * ES);
   const auto ro = make_rsrc(p.o_pre ? static_cast<const T*>(p.o_pre) + (size_t)bh * p.T * p.DV : nullptr,
@@ -635,13 +672,13 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     st_row16<T>(sB, r, c0, sv);
 #pragma unroll
     for (int e = 0; e < 16; ++e) x[e] = g[e] * alr;
-    st_col16<T>(sC, r, c0, x);
+    st_row16<T>(sC, r, c0, x);
     if (cs + 1 < NCS) load_slice(cs + 1);
     __syncthreads();
-    mma64<T>(accx, sA, sB, w, lane);  // sum_c dN_jc S~_dc
+    mma64x<T, false, false>(accx, sA, LD, sB, LD, w, lane);  // sum_c dN_jc S~_dc
     f32x4 u[4];
     zero_acc(u);
-    mma64<T>(u, sQt, sC, w, lane);  // U_dc = sum_j q_jd alpha_j dN_jc
+    mma64x<T, true, true>(u, sQ, LD, sC, LD, w, lane);  // U_dc = sum_j q_jd alpha_j dN_jc
 #pragma unroll
     for (int n = 0; n < 4; ++n)
 #pragma unroll
@@ -650,7 +687,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   }
   if (tid < 64) {  // normaliser column: sum_j q_jd alpha_j dz~_j
     float a = 0.f;
-    for (int j = 0; j < BL; ++j) a += to_f32(sQt[tid * LD + j]) * sal[j] * sdz[j];
+    for (int j = 0; j < BL; ++j) a += to_f32(sQ[j * LD + tid]) * sal[j] * sdz[j];
     Uw[(size_t)DQK * p.DV + dt * 64 + tid] = a;
   }
   // dq = intra + alpha (S~ dn~ + n~ dz~); q . dq partial
@@ -762,11 +799,11 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) d[e] = to_f32(Dt[r * BL + c0 + e]);
       st_row16<T>(sA, r, c0, d);
-      st_col16<T>(sB, r, c0, x);
+      st_row16<T>(sB, r, c0, x);  // Q [l][d]
       st_row16<T>(sK, r, c0, y);
     }
     __syncthreads();
-    mma64<T>(acc, sA, sB, w, lane);
+    mma64x<T, false, true>(acc, sA, LD, sB, LD, w, lane);  // sum_l D'_lj q_ld
     const int NCS = p.DV / 64;
     float vv[16], sv[16];  // one slice ahead
     load16f<T>(rv, ((unsigned)(t0 + r) * p.DV + c0) * ES, vv);
@@ -780,7 +817,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
         ld16(Gc + (size_t)(dt * 64 + r) * p.DV + (cs + 1) * 64 + c0, sv);
       }
       __syncthreads();
-      mma64<T>(accx, sA, sB, w, lane);  // sum_c v_jc G_dc
+      mma64x<T, false, false>(accx, sA, LD, sB, LD, w, lane);  // sum_c v_jc G_dc
     }
     T* dkw = static_cast<T*>(p.dk) + (size_t)bh * p.T * DQK;
     float kd[4] = {0.f, 0.f, 0.f, 0.f};
@@ -825,23 +862,23 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) d[e] = to_f32(Pt[r * BL + c0 + e]);
       st_row16<T>(sA, r, c0, d);
-      st_col16<T>(sB, r, c0, g);
+      st_row16<T>(sB, r, c0, g);  // dN [l][c]
     }
     __syncthreads();
-    mma64<T>(acc, sA, sB, w, lane);  // sum_l P_lj dn~_lc
+    mma64x<T, false, true>(acc, sA, LD, sB, LD, w, lane);  // sum_l P_lj dn~_lc
     float y[16], sv[16];  // one feature slice ahead
     load16f<T>(rk, ((unsigned)(t0 + r) * DQK + c0) * ES, y);
     ld16(Gc + (size_t)r * p.DV + ct * 64 + c0, sv);
     for (int ds = 0; ds < NDT; ++ds) {
       __syncthreads();
       st_row16<T>(sA, r, c0, y);
-      st_col16<T>(sB, r, c0, sv);  // G^T [c][d]
+      st_row16<T>(sB, r, c0, sv);  // G [d][c]
       if (ds + 1 < NDT) {
         load16f<T>(rk, ((unsigned)(t0 + r) * DQK + (ds + 1) * 64 + c0) * ES, y);
         ld16(Gc + (size_t)((ds + 1) * 64 + r) * p.DV + ct * 64 + c0, sv);
       }
       __syncthreads();
-      mma64<T>(accx, sA, sB, w, lane);  // sum_d k_jd G_dc
+      mma64x<T, false, true>(accx, sA, LD, sB, LD, w, lane);  // sum_d k_jd G_dc
     }
     T* dvw = static_cast<T*>(p.dv) + (size_t)bh * p.T * p.DV;
 #pragma unroll
