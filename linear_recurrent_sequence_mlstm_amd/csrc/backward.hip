@@ -603,6 +603,12 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) T sB[BL * LD];  // K tile, then S~ slices [l][d], [d][c]
   __shared__ __attribute__((aligned(16))) T sC[BL * LD];  // alpha dN slices        [j][c]
   __shared__ __attribute__((aligned(16))) T sQ[BL * LD];  // Q of the tile          [j][d]
+  // bf16 lo parts, x - bf16(x), of S~, dN and alpha dN: dq's S~ dn~ and the
+  // local backward state then see dn~ as the scores kernel does (hi + lo), so
+  // the near-cancellation of dn~ . v against dz~ holds in them too
+  __shared__ __attribute__((aligned(16))) T sBl[sizeof(T) == 2 ? BL * LD : 8];
+  __shared__ __attribute__((aligned(16))) T sAl[sizeof(T) == 2 ? BL * LD : 8];
+  __shared__ __attribute__((aligned(16))) T sCl[sizeof(T) == 2 ? BL * LD : 8];
   __shared__ float sa[BL], sM[BL], sal[BL], sem[BL], sw[BL], sden[BL], sdz[BL], snp[64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -673,12 +679,28 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) x[e] = g[e] * alr;
     st_row16<T>(sC, r, c0, x);
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        sv[e] -= to_f32(from_f32<T>(sv[e]));
+        g[e] -= to_f32(from_f32<T>(g[e]));
+        x[e] -= to_f32(from_f32<T>(x[e]));
+      }
+      st_row16<T>(sBl, r, c0, sv);
+      st_row16<T>(sAl, r, c0, g);
+      st_row16<T>(sCl, r, c0, x);
+    }
     if (cs + 1 < NCS) load_slice(cs + 1);
     __syncthreads();
     mma64x<T, false, false>(accx, sA, LD, sB, LD, w, lane);  // sum_c dN_jc S~_dc
+    if constexpr (sizeof(T) == 2) {
+      mma64x<T, false, false>(accx, sA, LD, sBl, LD, w, lane);
+      mma64x<T, false, false>(accx, sAl, LD, sB, LD, w, lane);
+    }
     f32x4 u[4];
     zero_acc(u);
     mma64x<T, true, true>(u, sQ, LD, sC, LD, w, lane);  // U_dc = sum_j q_jd alpha_j dN_jc
+    if constexpr (sizeof(T) == 2) mma64x<T, true, true>(u, sQ, LD, sCl, LD, w, lane);
 #pragma unroll
     for (int n = 0; n < 4; ++n)
 #pragma unroll
@@ -768,6 +790,8 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) T sA[BL * LD];
   __shared__ __attribute__((aligned(16))) T sB[BL * LD];
   __shared__ __attribute__((aligned(16))) T sK[BL * LD];  // dk tiles: K of the tile [j][d]
+  // bf16 dk tiles: G - bf16(G), so that k . dk (hence d i_pre, d f_pre) sees G to ~2^-16
+  __shared__ __attribute__((aligned(16))) T sBl[sizeof(T) == 2 ? BL * LD : 8];
   __shared__ float sa[BL], sM[BL], sal[BL], sem[BL], sw[BL], sg[64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -812,12 +836,18 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
       __syncthreads();
       st_row16<T>(sA, r, c0, vv);
       st_row16<T>(sB, r, c0, sv);
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sv[e] -= to_f32(from_f32<T>(sv[e]));
+        st_row16<T>(sBl, r, c0, sv);
+      }
       if (cs + 1 < NCS) {
         load16f<T>(rv, ((unsigned)(t0 + r) * p.DV + (cs + 1) * 64 + c0) * ES, vv);
         ld16(Gc + (size_t)(dt * 64 + r) * p.DV + (cs + 1) * 64 + c0, sv);
       }
       __syncthreads();
       mma64x<T, false, false>(accx, sA, LD, sB, LD, w, lane);  // sum_c v_jc G_dc
+      if constexpr (sizeof(T) == 2) mma64x<T, false, false>(accx, sA, LD, sBl, LD, w, lane);
     }
     T* dkw = static_cast<T*>(p.dk) + (size_t)bh * p.T * DQK;
     float kd[4] = {0.f, 0.f, 0.f, 0.f};

@@ -100,3 +100,57 @@ def test_bwd_xlstm7b_head_shape(gpu):
     x = workload("xlstm7b_prefill_T8192", T=160, H=2)
     out, ref = run_bwd(x, gpu, seed=2005)
     check(out, ref, TOL[torch.bfloat16])
+
+
+def test_bwd_xlstm7b_full_T8192_window(gpu):
+    """The 7B prefill workload at full size (B=1, H=8, T=8192: the launch
+    configuration bench.py times), dh non-zero on the last W = 320 tokens
+    only.  Window tokens: every gradient against the oracle's backward over
+    the window, started from the oracle's own state after the first T - W
+    tokens.  Prefix tokens: dq is exactly zero, and the last prefix token's dk
+    and dv follow from the window's initial-state gradient
+    (dk = i' (dC0 v + dn0), dv = i' dC0^T k with i' = e^{i_pre - m}).
+
+    The gradient jumps where |n.q + bias| crosses the floor 1 (the max in the
+    denominator), and the GPU's states differ from fp64 by about 2e-3, so a
+    token within that distance of the floor may take the other branch.  At
+    tokens whose margin ||z| / floor - 1| (from the oracle, stepping through
+    the window) is below 2e-2, dh is set to zero: there dh . h = 0, so dz~ = 0
+    on both sides whichever branch each takes."""
+    x = workload("xlstm7b_prefill_T8192")
+    B, H, T, dqk = x.q.shape
+    dv = x.v.shape[-1]
+    W = 320
+    cut = lambda t, a, b: t[:, :, a:b].contiguous()
+    _, C, n, m = oracle.mlstm_fwd(*(cut(t, 0, T - W) for t in (x.q, x.k, x.v, x.i_pre, x.f_pre)))
+    # margins to the denominator floor over the window
+    Cs, ns, ms = C.copy(), n.copy(), m.copy()
+    qn, kn, vn, ipn, fpn = (cpu(t) for t in (x.q, x.k, x.v, x.i_pre, x.f_pre))
+    near = np.zeros((B, H, W), dtype=bool)
+    for s in range(W):
+        t = T - W + s
+        oracle.mlstm_step(qn[:, :, t], kn[:, :, t], vn[:, :, t], ipn[:, :, t], fpn[:, :, t], Cs, ns, ms)
+        z = np.einsum("bhd,bhd->bh", ns, qn[:, :, t])
+        near[:, :, s] = np.abs(np.abs(z) * np.exp(ms) - 1) < 2e-2
+    dh = grad_output((B, H, T, dv), seed=2006)
+    dh[:, :, :T - W] = 0
+    dh[:, :, T - W:][torch.from_numpy(near)] = 0
+    print("window tokens near the floor (dh zeroed): %d of %d" % (int(near.sum()), near.size), flush=True)
+    g = x.to(gpu)
+    out = mlstm.chunkwise_bwd(g.q, g.k, g.v, g.i_pre, g.f_pre, dh.to(gpu))
+    torch.cuda.synchronize()
+    win = [cut(t, T - W, T) for t in (x.q, x.k, x.v, x.i_pre, x.f_pre)]
+    ref = oracle.mlstm_bwd(*win, cut(dh, T - W, T), C0=C.reshape(B, H, dqk, dv), n0=n, m0=m)
+    errs = {nm: slice_err(cpu(out[nm])[:, :, T - W:], ref[nm]) for nm in ("dq", "dk", "dv", "di", "df")}
+    print({k: "%.2e" % v for k, v in errs.items()}, flush=True)
+    assert all(v < TOL[torch.bfloat16] for v in errs.values()), errs
+    assert float(out["dq"][:, :, :T - W].abs().max()) == 0.0
+    t = T - W - 1
+    iw = np.exp(ipn[:, :, t] - m)  # e^{i_pre - m} with m after token t
+    dC0 = ref["dC0"]
+    dk_ref = iw[..., None] * (np.einsum("bhdc,bhc->bhd", dC0, vn[:, :, t]) + ref["dn0"])
+    dv_ref = iw[..., None] * np.einsum("bhdc,bhd->bhc", dC0, kn[:, :, t])
+    e_k = slice_err(cpu(out["dk"])[:, :, t], dk_ref)
+    e_v = slice_err(cpu(out["dv"])[:, :, t], dv_ref)
+    print("last prefix token: dk %.2e dv %.2e" % (e_k, e_v), flush=True)
+    assert e_k < TOL[torch.bfloat16] and e_v < TOL[torch.bfloat16], (e_k, e_v)
