@@ -154,3 +154,15 @@ def test_bwd_xlstm7b_full_T8192_window(gpu):
     e_v = slice_err(cpu(out["dv"])[:, :, t], dv_ref)
     print("last prefix token: dk %.2e dv %.2e" % (e_k, e_v), flush=True)
     assert e_k < TOL[torch.bfloat16] and e_v < TOL[torch.bfloat16], (e_k, e_v)
+
+
+@pytest.mark.parametrize("G,dtype", [(2, "bf16"), (3, "bf16"), (3, "f32")])
+def test_bwd_multichunk_superchunks(gpu, monkeypatch, G, dtype):
+    """Superchunks of G chunks (the plan's override), so that the chunk-state
+    walk steps through several chunks from each superchunk start state, with
+    an initial state and a ragged tail."""
+    monkeypatch.setenv("MLSTM_SUPERCHUNK_CHUNKS", str(G))
+    x = mlstm_inputs(1, 2, 7 * 64 - 9, 64, 128, seed=2400 + G, dtype=dtype, k_scale=1 / 8, f_mix=True,
+                     with_o=True, bias="uniform")
+    out, ref = run_bwd(x, gpu, seed=2500 + G, state=_state(1, 2, 64, 128, 2600 + G))
+    check(out, ref, TOL[x.q.dtype])
