@@ -23,6 +23,8 @@ Parity status of each function (what pins it is listed in the tests):
   mlstm_bwd        pinned (central finite differences of mlstm_fwd for every
                    input; torch autograd through an unstabilised fp64
                    recurrence written in the test)
+  retention_bwd    pinned (central finite differences of retention_fwd;
+                   torch autograd through the decay-matrix parallel form)
 """
 from __future__ import annotations
 
@@ -67,6 +69,8 @@ def _load(path: str | None = None):
     lib.oracle_retention_fwd.restype = i
     lib.oracle_mlstm_bwd.argtypes = [i, i, i, i, i] + [P] * 20
     lib.oracle_mlstm_bwd.restype = i
+    lib.oracle_retention_bwd.argtypes = [i, i, i, i, i] + [P] * 10
+    lib.oracle_retention_bwd.restype = i
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i
     if path is None:
@@ -221,4 +225,19 @@ def mlstm_bwd(q, k, v, i_pre, f_pre, dh, o_pre=None, bias=None, C0=None, n0=None
         _ptr(out["do"]), _ptr(out["dbias"]), _ptr(out["dC0"]), _ptr(out["dn0"]))
     if rc != 0:
         raise ValueError("oracle_mlstm_bwd failed with %d" % rc)
+    return out
+
+
+def retention_bwd(q, k, v, dout, gamma=None, S0=None, lib=None):
+    """Gradients of sum(dout * out) for out = retention_fwd(q, k, v, gamma,
+    S0)[0].  Returns a dict of float64 arrays dq, dk, dv and dS0 [B,H,dk,dv]."""
+    q, k, v, g, s0, go = map(_f64, (q, k, v, gamma, S0, dout))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v), dS0=np.zeros((B, H, dk, dv)))
+    rc = (lib or _load()).oracle_retention_bwd(
+        B, H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(go), _ptr(out["dq"]),
+        _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dS0"]))
+    if rc != 0:
+        raise ValueError("oracle_retention_bwd failed with %d" % rc)
     return out

@@ -439,3 +439,79 @@ int oracle_mlstm_bwd(int B, int H, int T, int dqk, int dv, const double* q,
   free(dbias_bh);
   return bad ? -2 : 0;
 }
+
+/*
+ * Backward pass of retention (recurrent form above): the gradients of
+ * L = sum_t dout_t . out_t.  With G_t the total gradient of L with respect to
+ * the state after token t,
+ *   G_t = gamma G_{t+1} + q_t dout_t^T,
+ *   dq_t = S_t dout_t,  dk_t = G_t v_t,  dv_t = G_t^T k_t,
+ *   dS0 = gamma G_0 (gradient of the initial state).
+ * dq comes from a forward sweep over the states, dk, dv, dS0 from a reverse
+ * sweep over G.  gamma may be NULL (1 - 2^(-5-h)); S0 may be NULL (zero).
+ * Outputs may be NULL.  Returns 0, -1 for bad sizes, -2 when out of memory.
+ */
+int oracle_retention_bwd(int B, int H, int T, int dk, int dv, const double* q,
+                         const double* k, const double* v, const double* gamma,
+                         const double* S0, const double* dout, double* dq,
+                         double* dk_out, double* dv_out, double* dS0) {
+  if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0) return -1;
+  const size_t ssz = (size_t)dk * dv;
+  const long BH = (long)B * H;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < BH; ++bh) {
+    const int hd = (int)(bh % H);
+    const double g = gamma ? gamma[hd] : 1.0 - ldexp(1.0, -5 - hd);
+    double* S = (double*)malloc(ssz * sizeof(double));
+    if (!S) {
+#pragma omp atomic write
+      bad = 1;
+      continue;
+    }
+    /* forward sweep: S_t, dq_t = S_t dout_t */
+    if (S0) memcpy(S, S0 + bh * ssz, ssz * sizeof(double));
+    else memset(S, 0, ssz * sizeof(double));
+    for (int t = 0; t < T; ++t) {
+      const size_t tok = (size_t)bh * T + t;
+      const double* kt = k + tok * dk;
+      const double* vt = v + tok * dv;
+      const double* gt = dout + tok * dv;
+      for (int r = 0; r < dk; ++r)
+        for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] = g * S[(size_t)r * dv + c] + kt[r] * vt[c];
+      if (dq)
+        for (int r = 0; r < dk; ++r) {
+          double a = 0.0;
+          for (int c = 0; c < dv; ++c) a += S[(size_t)r * dv + c] * gt[c];
+          dq[tok * dk + r] = a;
+        }
+    }
+    /* reverse sweep: G_t = gamma G_{t+1} + q_t dout_t^T (S reused as G) */
+    memset(S, 0, ssz * sizeof(double));
+    for (int t = T - 1; t >= 0; --t) {
+      const size_t tok = (size_t)bh * T + t;
+      const double* qt = q + tok * dk;
+      const double* kt = k + tok * dk;
+      const double* vt = v + tok * dv;
+      const double* gt = dout + tok * dv;
+      for (int r = 0; r < dk; ++r)
+        for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] = g * S[(size_t)r * dv + c] + qt[r] * gt[c];
+      if (dk_out)
+        for (int r = 0; r < dk; ++r) {
+          double a = 0.0;
+          for (int c = 0; c < dv; ++c) a += S[(size_t)r * dv + c] * vt[c];
+          dk_out[tok * dk + r] = a;
+        }
+      if (dv_out)
+        for (int c = 0; c < dv; ++c) {
+          double a = 0.0;
+          for (int r = 0; r < dk; ++r) a += S[(size_t)r * dv + c] * kt[r];
+          dv_out[tok * dv + c] = a;
+        }
+    }
+    if (dS0)
+      for (size_t e = 0; e < ssz; ++e) dS0[bh * ssz + e] = g * S[e];
+    free(S);
+  }
+  return bad ? -2 : 0;
+}

@@ -122,3 +122,44 @@ def test_bwd_pin_torch_autograd(T, with_o, bias, init):
         (h2 * torch.from_numpy(dh)).sum().backward()
         assert _relerr(g["dC0"], C0.grad.numpy()) < 1e-10
         assert _relerr(g["dn0"], n0.grad.numpy()) < 1e-10
+
+
+def test_retention_bwd_pin_finite_differences():
+    rng = np.random.default_rng(21)
+    B, H, T, dk, dv = 1, 2, 7, 3, 4
+    a = dict(q=rng.standard_normal((B, H, T, dk)), k=rng.standard_normal((B, H, T, dk)),
+             v=rng.standard_normal((B, H, T, dv)), S0=rng.standard_normal((B, H, dk, dv)))
+    gamma = np.array([0.9, 0.7])
+    do = rng.standard_normal((B, H, T, dv))
+    g = oracle.retention_bwd(a["q"], a["k"], a["v"], do, gamma, a["S0"])
+    eps = 1e-6
+    for name, gname in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("S0", "dS0")):
+        x = a[name]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            lp = np.sum(do * oracle.retention_fwd(a["q"], a["k"], a["v"], gamma, a["S0"])[0])
+            x[idx] = keep - eps
+            lm = np.sum(do * oracle.retention_fwd(a["q"], a["k"], a["v"], gamma, a["S0"])[0])
+            x[idx] = keep
+            fd[idx] = (lp - lm) / (2 * eps)
+        assert _relerr(g[gname], fd) < 1e-7, name
+
+
+def test_retention_bwd_pin_parallel_form_autograd():
+    """Autograd through the decay-matrix parallel form ((Q K^T) * D) V of the
+    RetNet page ("Key Innovation: Retention Mechanism"), default gammas."""
+    rng = np.random.default_rng(22)
+    B, H, T, dk, dv = 2, 3, 40, 8, 6
+    q, k, v, do = (rng.standard_normal(s) for s in ((B, H, T, dk), (B, H, T, dk), (B, H, T, dv), (B, H, T, dv)))
+    g = oracle.retention_bwd(q, k, v, do)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    gam = torch.tensor([1 - 2.0 ** (-5 - h) for h in range(H)], dtype=torch.float64)
+    n = torch.arange(T, dtype=torch.float64)
+    expo = (n[:, None] - n[None, :])
+    D = torch.where(expo >= 0, gam[:, None, None] ** expo.clamp(min=0), torch.zeros(()))
+    out = ((tq @ tk.transpose(-1, -2)) * D) @ tv
+    (out * torch.from_numpy(do)).sum().backward()
+    for t, nm in ((tq, "dq"), (tk, "dk"), (tv, "dv")):
+        assert _relerr(g[nm], t.grad.numpy()) < 1e-10, nm
