@@ -51,6 +51,12 @@ static double log_sigmoid(double x) {
   return x - log1p(exp(x));
 }
 
+/* gamma_h of the RetNet page ("Multi-Scale Retention (MSR)"): given, or
+ * 1 - 2^(-5-h) with 0-based h. */
+static double ret_gamma(const double* gamma, int hd) {
+  return gamma ? gamma[hd] : 1.0 - ldexp(1.0, -5 - hd);
+}
+
 static double sigmoid(double x) {
   if (x >= 0.0) return 1.0 / (1.0 + exp(-x));
   double e = exp(x);
@@ -222,7 +228,7 @@ int oracle_retention_fwd(int B, int H, int T, int dk, int dv, const double* q,
 #pragma omp parallel for schedule(dynamic, 1)
   for (long bh = 0; bh < BH; ++bh) {
     const int hd = (int)(bh % H);
-    const double g = gamma ? gamma[hd] : 1.0 - ldexp(1.0, -5 - hd);
+    const double g = ret_gamma(gamma, hd);
     double* S = (double*)malloc(ssz * sizeof(double));
     if (!S) {
 #pragma omp atomic write
@@ -462,7 +468,7 @@ int oracle_retention_bwd(int B, int H, int T, int dk, int dv, const double* q,
 #pragma omp parallel for schedule(dynamic, 1)
   for (long bh = 0; bh < BH; ++bh) {
     const int hd = (int)(bh % H);
-    const double g = gamma ? gamma[hd] : 1.0 - ldexp(1.0, -5 - hd);
+    const double g = ret_gamma(gamma, hd);
     double* S = (double*)malloc(ssz * sizeof(double));
     if (!S) {
 #pragma omp atomic write
@@ -478,7 +484,7 @@ int oracle_retention_bwd(int B, int H, int T, int dk, int dv, const double* q,
       const double* vt = v + tok * dv;
       const double* gt = dout + tok * dv;
       for (int r = 0; r < dk; ++r)
-        for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] = g * S[(size_t)r * dv + c] + kt[r] * vt[c];
+        for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] = kt[r] * vt[c] + g * S[(size_t)r * dv + c];
       if (dq)
         for (int r = 0; r < dk; ++r) {
           double a = 0.0;
