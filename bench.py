@@ -19,8 +19,9 @@ with a fresh bf16 token per step; it reports achieved HBM GB/s.
 fused; xLSTM-v2 block-diagonal B=4 H=4 d=64 nb=2 T=65536, also with per-block
 denominators; the 7B prefill with an output gate, and with the scalar
 normaliser), the retention decode step on the RetNet shape, and the backward
-pass of the 7B prefill workload: tokens/s per call and its algorithmic bytes
-against HBM (``backward`` runs that last one alone).
+passes of the 7B prefill and of the RetNet workloads: tokens/s per call and
+its algorithmic bytes against HBM (``backward`` runs the two backward
+passes alone).
 
 ``roofline`` is measured live: HIP events recorded by the library right before
 and after its main kernel (mlstm_set_profile_events) give that kernel's
@@ -220,6 +221,16 @@ def backward_work(B, H, T, dqk, dv, L=64):
     return byts, flops
 
 
+def retention_backward_work(B, H, T, dk, dv, L=64):
+    """Algorithmic bytes and flops of one retention backward: q, k, v and dout
+    read once, dq, dk, dv written once, the fp32 initial-state gradient
+    written once; flops of the chunkwise products, the state recompute
+    included: 10 d_k d_v + 2L (3 d_k + 2 d_v) per token and head."""
+    byts = B * H * T * (2 * dk + 2 * dv) * 2 + B * H * T * (2 * dk + dv) * 2 + B * H * dk * dv * 4
+    flops = B * H * T * (10 * dk * dv + 2 * L * (3 * dk + 2 * dv))
+    return byts, flops
+
+
 def bench_variants(torch, mlstm, workload, args, dev, only_backward=False):
     """The retention and block-diagonal workloads through the same chunkwise
     kernels: fence-free events around every call (all launches of it) and
@@ -275,6 +286,21 @@ def bench_variants(torch, mlstm, workload, args, dev, only_backward=False):
     out.append(dict(workload="xlstm7b_prefill_T8192_backward", B=B, H=H, T=T, d_qk=dqk, d_v=dv, **r,
                     bytes=byts, flops=flops, tokens=B * T))
     del sets, dhs, ws
+
+    # retention backward on the RetNet workload (B=8, H=4, d=64, T=2048)
+    q, k, v = workload("retnet_msr_T2048")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    rsets = [tuple(t.to(dev) for t in (q, k, v)) for _ in range(4)]
+    douts = [grad_output((B, H, T, dv), seed=7100 + i, scale=1 / 8).to(dev) for i in range(len(rsets))]
+    ws = torch.empty(mlstm.lib().retention_chunkwise_bwd_workspace_bytes(B, H, T, dk, dv, 64, mlstm.BF16),
+                     dtype=torch.uint8, device=dev)
+    r = timed(lambda i: mlstm.retention_chunkwise_bwd(*rsets[i], douts[i], workspace=ws), len(rsets),
+              args.variant_steps, args.variant_steps)
+    byts, flops = retention_backward_work(B, H, T, dk, dv)
+    out.append(dict(workload="retnet_msr_T2048_backward", B=B, H=H, T=T, d_k=dk, d_v=dv, **r, bytes=byts,
+                    flops=flops, tokens=B * T))
+    del rsets, douts, ws
     if only_backward:
         return out
 

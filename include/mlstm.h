@@ -292,6 +292,36 @@ int mlstm_chunkwise_bwd(int B, int H, int T, int d_qk, int d_v, int num_blocks,
                         float* dbias, float* dC0, float* dn0, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* Workspace size in bytes for retention_chunkwise_bwd (0 for arguments it
+ * does not take, with the error message set). */
+size_t retention_chunkwise_bwd_workspace_bytes(int B, int H, int T, int d_k, int d_v,
+                                               int chunk, mlstm_dtype dt);
+
+/*
+ * Chunkwise backward pass of RetNet retention: the gradients of
+ * L = sum(dout * out) for out = retention_chunkwise_fwd(...) with the same
+ * q, k, v, gamma and S0.  The RetNet page trains with the parallel form
+ * ("Triple Paradigm": parallel mode is the training mode); this is the
+ * gradient of the same function, computed chunkwise:
+ *     dq_t = S_t dout_t,  dk_t = G_t v_t,  dv_t = G_t^T k_t,
+ *     G_t = gamma_h G_{t+1} + q_t dout_t^T,  dS0 = gamma_h G_0.
+ *   q, k [B,H,T,d_k]; v, dout [B,H,T,d_v] (dtype dt); gamma [H] fp32 or NULL
+ *   (1 - 2^(-5-h)); S0 [B,H,d_k,d_v] fp32 or NULL (zero);
+ *   dq, dk [B,H,T,d_k], dv [B,H,T,d_v] outputs, dtype dt;
+ *   dS0 [B,H,d_k,d_v] fp32 or NULL: gradient of S0 (also for a zero S0).
+ * Requires chunk = 64, d_v a multiple of 64 and d_k in {64, 128} (bf16) or 64
+ * (fp32); other shapes return MLSTM_E_UNSUPPORTED.  workspace: at least
+ * retention_chunkwise_bwd_workspace_bytes bytes, 256-byte aligned.  Enqueues
+ * the forward's state passes and the backward kernels of mlstm_chunkwise_bwd
+ * (without the gate and bias ones) on stream.
+ */
+int retention_chunkwise_bwd(int B, int H, int T, int d_k, int d_v, int chunk,
+                            mlstm_dtype dt, const void* q, const void* k,
+                            const void* v, const float* gamma, const float* S0,
+                            const void* dout, void* dq, void* dk, void* dv,
+                            float* dS0, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,7 +7,7 @@ that ABI.  Import is cheap: the library is loaded on first use and its absence
 raises an error (there is no fallback path).
 """
 
-__all__ = ["chunkwise_fwd", "chunkwise_bwd", "step", "retention_chunkwise_fwd",
+__all__ = ["chunkwise_fwd", "chunkwise_bwd", "step", "retention_chunkwise_fwd", "retention_chunkwise_bwd",
            "chunkwise_workspace_bytes", "abi_version", "library_path"]
 
 

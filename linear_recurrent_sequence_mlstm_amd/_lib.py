@@ -26,7 +26,8 @@ EXPORTS = ("mlstm_abi_version", "mlstm_last_error", "mlstm_set_profile_events",
            "mlstm_chunkwise_fwd", "mlstm_chunkwise_fwd_ex", "mlstm_step", "mlstm_step_ex",
            "retention_chunkwise_workspace_bytes",
            "retention_chunkwise_fwd", "retention_chunkwise_groupnorm_fwd", "retention_step",
-           "mlstm_chunkwise_bwd_workspace_bytes", "mlstm_chunkwise_bwd")
+           "mlstm_chunkwise_bwd_workspace_bytes", "mlstm_chunkwise_bwd",
+           "retention_chunkwise_bwd_workspace_bytes", "retention_chunkwise_bwd")
 
 
 def library_path() -> str:
@@ -73,6 +74,10 @@ def lib():
     L.mlstm_chunkwise_bwd.argtypes = ([i] * 8 + [vp] * 6 + [fp] * 4 + [vp] + [vp] * 6 + [fp] * 3 +
                                       [vp, sz, vp])
     L.mlstm_chunkwise_bwd.restype = i
+    L.retention_chunkwise_bwd_workspace_bytes.argtypes = [i] * 7
+    L.retention_chunkwise_bwd_workspace_bytes.restype = sz
+    L.retention_chunkwise_bwd.argtypes = [i] * 7 + [vp] * 3 + [fp] * 2 + [vp] * 4 + [fp] + [vp, sz, vp]
+    L.retention_chunkwise_bwd.restype = i
     _lib = L
     return L
 
@@ -341,4 +346,34 @@ def chunkwise_bwd(q, k, v, i_pre, f_pre, dh, o_pre=None, bias=None, state=None, 
                                _ptr(out["df"]), _ptr(out["do"]), _ptr(out["dbias"]), _ptr(out["dC0"]),
                                _ptr(out["dn0"]), _ptr(ws), ws.numel(), _stream(dev))
     _check(rc, "mlstm_chunkwise_bwd")
+    return out
+
+
+def retention_chunkwise_bwd(q, k, v, dout, gamma=None, S0=None, chunk=64, state_grad=True, workspace=None):
+    """retention_chunkwise_bwd: gradients of sum(dout * out) for out =
+    retention_chunkwise_fwd(q, k, v, gamma, S0).  Returns a dict with dq, dk,
+    dv and, with state_grad, dS0 [B,H,dk,dv] fp32."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dt not in _DT:
+        raise TypeError("unsupported dtype %s" % dt)
+    _need(q, "q", (B, H, T, dk), dt, dev)
+    _need(k, "k", (B, H, T, dk), dt, dev)
+    _need(v, "v", (B, H, T, dv), dt, dev)
+    _need(dout, "dout", (B, H, T, dv), dt, dev)
+    _need(gamma, "gamma", (H,), torch.float32, dev)
+    _need(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dS0=torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev) if state_grad else None)
+    L = lib()
+    nbytes = L.retention_chunkwise_bwd_workspace_bytes(B, H, T, dk, dv, chunk, _DT[dt])
+    if nbytes == 0:
+        _check(L.retention_chunkwise_bwd(B, H, T, dk, dv, chunk, _DT[dt], *([None] * 10), None, 0, None),
+               "retention_chunkwise_bwd")
+    ws = _workspace(nbytes, dev, workspace)
+    rc = L.retention_chunkwise_bwd(B, H, T, dk, dv, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
+                                   _ptr(S0), _ptr(dout), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                   _ptr(out["dS0"]), _ptr(ws), ws.numel(), _stream(dev))
+    _check(rc, "retention_chunkwise_bwd")
     return out

@@ -128,8 +128,8 @@ struct BwdPlan {
       off_kdk, bytes;
 };
 
-int plan_bwd(int B, int H, int T, int dqk, int dv, int nb, int chunk, int dt, BwdPlan* bp) {
-  const int rc = plan_chunkwise(B, H, T, dqk, dv, nb, chunk, dt, false, &bp->fwd);
+int plan_bwd(int B, int H, int T, int dqk, int dv, int nb, int chunk, int dt, BwdPlan* bp, bool ret = false) {
+  const int rc = plan_chunkwise(B, H, T, dqk, dv, nb, chunk, dt, ret, &bp->fwd);
   if (rc != MLSTM_OK) return rc;
   if (nb != 1) return fail(MLSTM_E_UNSUPPORTED, "the backward pass takes num_blocks = 1 (got %d)", nb);
   if (chunk != 64) return fail(MLSTM_E_UNSUPPORTED, "the backward pass takes chunk = 64 (got %d)", chunk);
@@ -239,6 +239,7 @@ int mlstm_chunkwise_bwd(int B, int H, int T, int d_qk, int d_v, int num_blocks, 
   b.NC = pl.NC;
   b.G = pl.G;
   b.NS = pl.NS;
+  b.sc_nst = pl.nstate;
   b.q = q;
   b.k = k;
   b.v = v;
@@ -275,6 +276,99 @@ int mlstm_chunkwise_bwd(int B, int H, int T, int d_qk, int d_v, int num_blocks, 
   b.dbias = dbias;
   b.dC0 = dC0;
   b.dn0 = dn0;
+  if (g_ev0) (void)hipEventRecord(g_ev0, st);
+  e = mlstm::launch_bwd(dt, b, st);
+  if (g_ev1) (void)hipEventRecord(g_ev1, st);
+  if (e != hipSuccess) return fail(MLSTM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t retention_chunkwise_bwd_workspace_bytes(int B, int H, int T, int d_k, int d_v, int chunk, mlstm_dtype dt) {
+  BwdPlan bp;
+  if (plan_bwd(B, H, T, d_k, d_v, 1, chunk, dt, &bp, true) != MLSTM_OK) return 0;
+  return bp.bytes;
+}
+
+int retention_chunkwise_bwd(int B, int H, int T, int d_k, int d_v, int chunk, mlstm_dtype dt, const void* q,
+                            const void* k, const void* v, const float* gamma, const float* S0, const void* dout,
+                            void* dq, void* dk, void* dv, float* dS0, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  BwdPlan bp;
+  const int rc = plan_bwd(B, H, T, d_k, d_v, 1, chunk, dt, &bp, true);
+  if (rc != MLSTM_OK) return rc;
+  if (!q || !k || !v || !dout) return fail(MLSTM_E_NULL, "q, k, v and dout are required");
+  if (!dq || !dk || !dv) return fail(MLSTM_E_NULL, "dq, dk and dv are required");
+  if (!workspace) return fail(MLSTM_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", bp.bytes);
+  if (workspace_bytes < bp.bytes)
+    return fail(MLSTM_E_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, bp.bytes);
+  if ((size_t)workspace & 255) return fail(MLSTM_E_WORKSPACE, "workspace must be 256-byte aligned");
+  const Plan& pl = bp.fwd;
+  char* ws = static_cast<char*>(workspace);
+  mlstm::ChunkParams p{};  // the forward's state passes only
+  p.B = B;
+  p.H = H;
+  p.T = T;
+  p.DV = d_v;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.ret_gamma = gamma;
+  p.has_init = S0 ? 1 : 0;
+  p.C0 = S0;
+  p.h = nullptr;
+  p.NC = pl.NC;
+  p.G = pl.G;
+  p.NS = pl.NS;
+  p.nslices = pl.nslices;
+  p.ws_state = reinterpret_cast<float*>(ws);
+  p.ws_scal = reinterpret_cast<float*>(ws + pl.off_scal);
+  p.ws_min = reinterpret_cast<float*>(ws + pl.off_min);
+  const size_t gsz = align256((size_t)B * H * pl.NC * pl.L * sizeof(float));
+  p.ws_ga = reinterpret_cast<float*>(ws + pl.off_g);
+  p.ws_gg = reinterpret_cast<float*>(ws + pl.off_g + gsz);
+  p.ws_gb = reinterpret_cast<float*>(ws + pl.off_g + 2 * gsz);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = pl.var.launch(p, st, nullptr, nullptr);
+  if (e != hipSuccess) return fail(MLSTM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  mlstm::BwdParams b{};
+  b.B = B;
+  b.H = H;
+  b.T = T;
+  b.DQK = d_k;
+  b.DV = d_v;
+  b.NC = pl.NC;
+  b.G = pl.G;
+  b.NS = pl.NS;
+  b.ret = 1;
+  b.sc_nst = pl.nstate;
+  b.q = q;
+  b.k = k;
+  b.v = v;
+  b.dh = dout;
+  b.has_init = p.has_init;
+  b.sc_state = p.ws_state;
+  b.sc_min = p.ws_min;
+  b.ws_state = reinterpret_cast<float*>(ws + bp.off_cst);
+  b.ws_min = reinterpret_cast<float*>(ws + bp.off_cmin);
+  b.ws_ga = p.ws_ga;
+  b.ws_gg = p.ws_gg;
+  b.ws_gb = p.ws_gb;
+  b.wsP = ws + bp.off_P;
+  b.wsPt = ws + bp.off_Pt;
+  b.wsD = ws + bp.off_D;
+  b.wsDt = ws + bp.off_Dt;
+  b.ws_rden = reinterpret_cast<float*>(ws + bp.off_rden);
+  b.ws_dz = reinterpret_cast<float*>(ws + bp.off_dz);
+  b.ws_dbias = reinterpret_cast<float*>(ws + bp.off_db);
+  b.ws_ctot = reinterpret_cast<float*>(ws + bp.off_dbh);
+  b.ws_U = reinterpret_cast<float*>(ws + bp.off_U);
+  b.ws_qdq = reinterpret_cast<float*>(ws + bp.off_qdq);
+  b.ws_kdki = reinterpret_cast<float*>(ws + bp.off_kdki);
+  b.ws_kdk = reinterpret_cast<float*>(ws + bp.off_kdk);
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  b.dC0 = dS0;
   if (g_ev0) (void)hipEventRecord(g_ev0, st);
   e = mlstm::launch_bwd(dt, b, st);
   if (g_ev1) (void)hipEventRecord(g_ev1, st);

@@ -1,7 +1,9 @@
 // Chunkwise backward pass of the mLSTM recurrence (vector normaliser, one
 // memory block, chunks of 64 tokens): gradients of sum(dh * h) with respect to
 // q, k, v, the gate preactivations, the output gate, the normaliser bias and
-// the initial state.
+// the initial state.  Retention runs through the same kernels (p.ret): gates
+// i = 1, f = gamma_h make the stabiliser exactly 0 and the weights below
+// powers of gamma; with no normaliser dz~ = 0 and den~ = 1.
 //
 // The forward's state passes (gates, pass 1, pass 2) leave in the workspace
 // the superchunk start states and the chunk-local gate logs a_j, g_j, b_j (log2
@@ -237,14 +239,14 @@ __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
   // n~[64 dt + r] lives in thread 4 r of the lead work-group
   float nn = 0.f;
   const bool has = p.has_init || sc > 0;
-  const float* S0 = p.sc_state + ((size_t)bh * p.NS + sc) * NST;
+  const float* S0 = p.sc_state + ((size_t)bh * p.NS + sc) * p.sc_nst;
   if (has) {
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       const float4 u = *reinterpret_cast<const float4*>(S0 + toff + (size_t)16 * n * p.DV);
       acc[n] = f32x4{u.x, u.y, u.z, u.w};
     }
-    if (lead) nn = S0[(size_t)DQK * p.DV + dt * 64 + r];
+    if (lead && !p.ret) nn = S0[(size_t)DQK * p.DV + dt * 64 + r];
   }
   float m = p.sc_min[(size_t)bh * p.NS + sc];  // meaningful in threads below 64
   const int cb = sc * p.G, ce = min(p.NC, cb + p.G);
@@ -316,7 +318,9 @@ __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
 // with the very P, D and dn~ that D' and the dq/dk/dv products use: where the
 // denominator nearly cancels the direct term, rounding h (or any operand) on
 // one side only would leave the cancellation residue in the gradient.
-template <typename T, int DQK>
+// RET (retention): no normaliser, so den~ = 1 and dz~ = 0, and the readout
+// (needed only for dz~ and d o_pre) is not recomputed.
+template <typename T, int DQK, bool RET>
 __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
   constexpr int LD = BT<T>::LD;
   constexpr int LDQ = DQK + 16 / (int)sizeof(T);
@@ -412,11 +416,16 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
   }
   __syncthreads();
   if (tid < BL) {
-    const float bias = p.bias ? p.bias[hd] : 0.f;
-    const float z = srow[tid] + sal[tid] * sqn[tid] + bias * sem[tid];
-    const float den = fmaxf(fabsf(z), sem[tid]);
-    sden[tid] = 1.f / den;
-    ssg[tid] = fabsf(z) > sem[tid] ? (z > 0.f ? 1.f : -1.f) : 0.f;
+    if constexpr (RET) {
+      sden[tid] = 1.f;
+      ssg[tid] = 0.f;
+    } else {
+      const float bias = p.bias ? p.bias[hd] : 0.f;
+      const float z = srow[tid] + sal[tid] * sqn[tid] + bias * sem[tid];
+      const float den = fmaxf(fabsf(z), sem[tid]);
+      sden[tid] = 1.f / den;
+      ssg[tid] = fabsf(z) > sem[tid] ? (z > 0.f ? 1.f : -1.f) : 0.f;
+    }
   }
   __syncthreads();
 
@@ -443,7 +452,8 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
     if (p.o_pre) load16f<T>(ro, off, x);
   };
   load_slice(0);
-  if (has_state) ld16(Sp + (size_t)r * p.DV + c0, sv);
+  const bool readout = has_state && !RET;
+  if (readout) ld16(Sp + (size_t)r * p.DV + c0, sv);
   for (int cs = 0; cs < NCS; ++cs) {
     if (p.o_pre) {
 #pragma unroll
@@ -464,7 +474,7 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
     f32x4 accI[4], accN[4];
     zero_acc(accI);
     zero_acc(accN);
-    if (has_state) {
+    if (readout) {
       for (int ds = 0; ds < NDS; ++ds) {
         if (ds > 0) __syncthreads();  // previous tile consumed
         st_row16<T>(sSt, r, c0, sv);
@@ -987,14 +997,19 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   const unsigned nch = BH * (unsigned)p.NC;
   hipLaunchKernelGGL((bwd_chunk_states_kernel<T, DQK>), dim3(BH * p.NS * (DQK / 64) * (p.DV / 64)), dim3(256), 0,
                      stream, p);
-  hipLaunchKernelGGL((bwd_scores_kernel<T, DQK>), dim3(nch), dim3(256), 0, stream, p);
+  if (p.ret)
+    hipLaunchKernelGGL((bwd_scores_kernel<T, DQK, true>), dim3(nch), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((bwd_scores_kernel<T, DQK, false>), dim3(nch), dim3(256), 0, stream, p);
   hipLaunchKernelGGL((bwd_dq_kernel<T, DQK>), dim3(nch * (DQK / 64)), dim3(256), 0, stream, p);
   const size_t NST = (size_t)DQK * p.DV + DQK;
   hipLaunchKernelGGL(bwd_scan_kernel, dim3((unsigned)((NST / 4 + 255) / 256), BH), dim3(256), 0, stream, p, DQK);
   hipLaunchKernelGGL((bwd_dkv_kernel<T, DQK>), dim3(nch * (DQK / 64 + p.DV / 64)), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL(bwd_gate_total_kernel, dim3(nch), dim3(64), 0, stream, p, DQK / 64);
-  hipLaunchKernelGGL((bwd_gate_kernel<T>), dim3(nch), dim3(64), 0, stream, p);
-  if (p.dbias) hipLaunchKernelGGL(bwd_bias_kernel, dim3(1), dim3(256), 0, stream, p);
+  if (!p.ret) {  // retention has no gates or normaliser to differentiate
+    hipLaunchKernelGGL(bwd_gate_total_kernel, dim3(nch), dim3(64), 0, stream, p, DQK / 64);
+    hipLaunchKernelGGL((bwd_gate_kernel<T>), dim3(nch), dim3(64), 0, stream, p);
+    if (p.dbias) hipLaunchKernelGGL(bwd_bias_kernel, dim3(1), dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -97,6 +97,8 @@ bool step_supported(int dqk, int dv, int nb);
 // 64 tokens), after the forward plan's state passes ran.
 struct BwdParams {
   int B, H, T, DQK, DV, NC, G, NS;
+  int ret;        // retention: no gates, no normaliser
+  size_t sc_nst;  // floats per superchunk state slot of the forward plan
   const void* q;
   const void* k;
   const void* v;

@@ -166,3 +166,36 @@ def test_bwd_multichunk_superchunks(gpu, monkeypatch, G, dtype):
                      with_o=True, bias="uniform")
     out, ref = run_bwd(x, gpu, seed=2500 + G, state=_state(1, 2, 64, 128, 2600 + G))
     check(out, ref, TOL[x.q.dtype])
+
+
+@pytest.mark.parametrize("dtype,B,H,T,dk,dv,with_state", [("f32", 1, 3, 150, 64, 64, True),
+                                                          ("bf16", 2, 4, 200, 64, 128, False),
+                                                          ("bf16", 1, 2, 300, 128, 128, True)])
+def test_retention_bwd(gpu, dtype, B, H, T, dk, dv, with_state):
+    from linear_recurrent_sequence_mlstm_amd.workloads import retention_inputs
+    q, k, v = retention_inputs(B, H, T, dk, dv, seed=2700 + T, dtype=dtype)
+    do = grad_output((B, H, T, dv), seed=2800 + T, dtype=dtype)
+    S0 = torch.randn(B, H, dk, dv, generator=torch.Generator().manual_seed(2900)) * 0.3 if with_state else None
+    out = mlstm.retention_chunkwise_bwd(q.to(gpu), k.to(gpu), v.to(gpu), do.to(gpu),
+                                        S0=None if S0 is None else S0.to(gpu))
+    torch.cuda.synchronize()
+    ref = oracle.retention_bwd(q, k, v, do, None, S0)
+    errs = {nm: slice_err(cpu(out[nm]), ref[nm]) for nm in ("dq", "dk", "dv", "dS0")}
+    print(errs, flush=True)
+    tol = TOL[q.dtype]
+    assert all(e < tol for e in errs.values()), errs
+
+
+def test_retention_bwd_msr_T2048_full(gpu):
+    """The RetNet multi-scale retention workload at full size (B=8, H=4, d=64,
+    T=2048, bf16), every gradient against the oracle."""
+    q, k, v = workload("retnet_msr_T2048")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    do = grad_output((B, H, T, dv), seed=3001, scale=1 / 8)
+    out = mlstm.retention_chunkwise_bwd(q.to(gpu), k.to(gpu), v.to(gpu), do.to(gpu))
+    torch.cuda.synchronize()
+    ref = oracle.retention_bwd(q, k, v, do)
+    errs = {nm: slice_err(cpu(out[nm]), ref[nm]) for nm in ("dq", "dk", "dv", "dS0")}
+    print(errs, flush=True)
+    assert all(e < TOL[torch.bfloat16] for e in errs.values()), errs
