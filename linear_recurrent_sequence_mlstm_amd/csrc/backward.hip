@@ -326,15 +326,13 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
   constexpr int LDQ = DQK + 16 / (int)sizeof(T);
   constexpr unsigned ES = sizeof(T);
   __shared__ __attribute__((aligned(16))) T sQ[BL * LDQ];  // Q, token-major
-  __shared__ __attribute__((aligned(16))) T sX[BL * LD];   // K slices, then dN slices  [j][.]
+  __shared__ __attribute__((aligned(16))) T sX[BL * LD];   // K, dN, S~ tiles  [j][d], [j][c], [d][c]
   __shared__ __attribute__((aligned(16))) T sY[BL * LD];   // V slices                  [l][c]
   __shared__ __attribute__((aligned(16))) T sP[BL * LD];   // P                         [j][l]
-  __shared__ __attribute__((aligned(16))) T sSt[BL * LD];  // S~ tiles                  [d][c]
-  // bf16: S~ - bf16(S~), so that the state enters the readout to ~2^-16
-  // (the initial state is exact fp32 input)
-  __shared__ __attribute__((aligned(16))) T sSl[sizeof(T) == 2 ? BL * LD : 8];
-  // bf16: dn~ - bf16(dn~), likewise for D and dh . h (a near-cancelling
-  // dn~ . (v_l - y_j) must not see dn~ rounded)
+  // bf16 lo parts x - bf16(x) of dn~ and then of the S~ tiles: D, dh . h and
+  // the readout see dn~ and the state to ~2^-16 (a near-cancelling
+  // dn~ . (v_l - y_j) must not see dn~ rounded; the initial state is exact
+  // fp32 input)
   __shared__ __attribute__((aligned(16))) T sXl[sizeof(T) == 2 ? BL * LD : 8];
   __shared__ float sa[BL], sM[BL], sal[BL], sem[BL], sw[BL];
   __shared__ float sqn[BL], srow[BL], sden[BL], ssg[BL], sdz[BL];
@@ -471,39 +469,46 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
       st_row16<T>(sXl, r, c0, g);
     }
     if (cs + 1 < NCS) load_slice(cs + 1);
+    __syncthreads();
     f32x4 accI[4], accN[4];
     zero_acc(accI);
     zero_acc(accN);
+    mma64x<T, false, false>(accD, sX, LD, sY, LD, w, lane);  // sum_c dn~_jc v_lc
+    if constexpr (sizeof(T) == 2) mma64x<T, false, false>(accD, sXl, LD, sY, LD, w, lane);
+    mma64x<T, false, true>(accN, sP, LD, sY, LD, w, lane);  // sum_l P_jl v_lc
+    // this lane's dn~ values, so that sX / sXl can hold the S~ tiles next
+    float dnv[4][4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 16 * w + 4 * lg + i, col = 16 * n + lr;
+        dnv[n][i] = to_f32(sX[j * LD + col]);
+        if constexpr (sizeof(T) == 2) dnv[n][i] += to_f32(sXl[j * LD + col]);
+      }
     if (readout) {
       for (int ds = 0; ds < NDS; ++ds) {
-        if (ds > 0) __syncthreads();  // previous tile consumed
-        st_row16<T>(sSt, r, c0, sv);
+        __syncthreads();  // sX / sXl are free (dn~ read, previous tile consumed)
+        st_row16<T>(sX, r, c0, sv);
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) sv[e] -= to_f32(from_f32<T>(sv[e]));
-          st_row16<T>(sSl, r, c0, sv);
+          st_row16<T>(sXl, r, c0, sv);
         }
         if (ds + 1 < NDS) ld16(Sp + (size_t)((ds + 1) * 64 + r) * p.DV + cs * 64 + c0, sv);
         else if (cs + 1 < NCS) ld16(Sp + (size_t)r * p.DV + (cs + 1) * 64 + c0, sv);
         __syncthreads();
-        mma64x<T, false, true>(accI, sQ + ds * 64, LDQ, sSt, LD, w, lane);  // sum_d q_jd S~_dc
-        if constexpr (sizeof(T) == 2) mma64x<T, false, true>(accI, sQ + ds * 64, LDQ, sSl, LD, w, lane);
+        mma64x<T, false, true>(accI, sQ + ds * 64, LDQ, sX, LD, w, lane);  // sum_d q_jd S~_dc
+        if constexpr (sizeof(T) == 2) mma64x<T, false, true>(accI, sQ + ds * 64, LDQ, sXl, LD, w, lane);
       }
-    } else {
-      __syncthreads();
     }
-    mma64x<T, false, false>(accD, sX, LD, sY, LD, w, lane);  // sum_c dn~_jc v_lc
-    if constexpr (sizeof(T) == 2) mma64x<T, false, false>(accD, sXl, LD, sY, LD, w, lane);
-    mma64x<T, false, true>(accN, sP, LD, sY, LD, w, lane);  // sum_l P_jl v_lc
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       const int col = 16 * n + lr;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 16 * w + 4 * lg + i;
-        float dnv = to_f32(sX[j * LD + col]);
-        if constexpr (sizeof(T) == 2) dnv += to_f32(sXl[j * LD + col]);
-        sint[i] += dnv * accI[n][i];
+        sint[i] += dnv[n][i] * accI[n][i];
         if (p.o_pre && t0 + j < p.T) {
           const size_t e = (size_t)(t0 + j) * p.DV + cs * 64 + col;
           const float y = (sal[j] * accI[n][i] + accN[n][i]) * sden[j];
@@ -609,16 +614,16 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   constexpr int LD = BT<T>::LD;
   constexpr unsigned ES = sizeof(T);
   constexpr int NDT = DQK / 64;
-  __shared__ __attribute__((aligned(16))) T sA[BL * LD];  // D', then dN slices     [j][.]
-  __shared__ __attribute__((aligned(16))) T sB[BL * LD];  // K tile, then S~ slices [l][d], [d][c]
-  __shared__ __attribute__((aligned(16))) T sC[BL * LD];  // alpha dN slices        [j][c]
-  __shared__ __attribute__((aligned(16))) T sQ[BL * LD];  // Q of the tile          [j][d]
-  // bf16 lo parts, x - bf16(x), of S~, dN and alpha dN: dq's S~ dn~ and the
-  // local backward state then see dn~ as the scores kernel does (hi + lo), so
-  // the near-cancellation of dn~ . v against dz~ holds in them too
+  // alpha_j is per row of dq and per contraction index of U, so one tile of
+  // alpha dN serves both: the inter part of dq is alpha_j sum_c dN_jc S~_dc.
+  __shared__ __attribute__((aligned(16))) T sA[BL * LD];  // D', then alpha dN slices [j][.]
+  __shared__ __attribute__((aligned(16))) T sB[BL * LD];  // K tile, then S~ slices  [l][d], [d][c]
+  __shared__ __attribute__((aligned(16))) T sQ[BL * LD];  // Q of the tile           [j][d]
+  // bf16 lo parts, x - bf16(x), of S~ and alpha dN: dq's S~ dn~ and the local
+  // backward state then see dn~ as the scores kernel does (hi + lo), so the
+  // near-cancellation of dn~ . v against dz~ holds in them too
   __shared__ __attribute__((aligned(16))) T sBl[sizeof(T) == 2 ? BL * LD : 8];
   __shared__ __attribute__((aligned(16))) T sAl[sizeof(T) == 2 ? BL * LD : 8];
-  __shared__ __attribute__((aligned(16))) T sCl[sizeof(T) == 2 ? BL * LD : 8];
   __shared__ float sa[BL], sM[BL], sal[BL], sem[BL], sw[BL], sden[BL], sdz[BL], snp[64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -683,34 +688,31 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) g[e] = dn_of(g[e], 1.f, rden);
     }
-    __syncthreads();  // previous slice's operands are consumed
+#pragma unroll
+    for (int e = 0; e < 16; ++e) g[e] *= alr;  // alpha_j dn~_jc
+    __syncthreads();  // previous slice's operands (and D') are consumed
     st_row16<T>(sA, r, c0, g);
     st_row16<T>(sB, r, c0, sv);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) x[e] = g[e] * alr;
-    st_row16<T>(sC, r, c0, x);
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         sv[e] -= to_f32(from_f32<T>(sv[e]));
         g[e] -= to_f32(from_f32<T>(g[e]));
-        x[e] -= to_f32(from_f32<T>(x[e]));
       }
       st_row16<T>(sBl, r, c0, sv);
       st_row16<T>(sAl, r, c0, g);
-      st_row16<T>(sCl, r, c0, x);
     }
     if (cs + 1 < NCS) load_slice(cs + 1);
     __syncthreads();
-    mma64x<T, false, false>(accx, sA, LD, sB, LD, w, lane);  // sum_c dN_jc S~_dc
+    mma64x<T, false, false>(accx, sA, LD, sB, LD, w, lane);  // sum_c alpha_j dN_jc S~_dc
     if constexpr (sizeof(T) == 2) {
       mma64x<T, false, false>(accx, sA, LD, sBl, LD, w, lane);
       mma64x<T, false, false>(accx, sAl, LD, sB, LD, w, lane);
     }
     f32x4 u[4];
     zero_acc(u);
-    mma64x<T, true, true>(u, sQ, LD, sC, LD, w, lane);  // U_dc = sum_j q_jd alpha_j dN_jc
-    if constexpr (sizeof(T) == 2) mma64x<T, true, true>(u, sQ, LD, sCl, LD, w, lane);
+    mma64x<T, true, true>(u, sQ, LD, sA, LD, w, lane);  // U_dc = sum_j q_jd alpha_j dN_jc
+    if constexpr (sizeof(T) == 2) mma64x<T, true, true>(u, sQ, LD, sAl, LD, w, lane);
 #pragma unroll
     for (int n = 0; n < 4; ++n)
 #pragma unroll
@@ -730,7 +732,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = 16 * w + 4 * lg + i;
-      const float v = acc[n][i] + sal[j] * (accx[n][i] + sdz[j] * snp[d]);
+      const float v = acc[n][i] + accx[n][i] + sal[j] * sdz[j] * snp[d];
       if (t0 + j < p.T) dqw[(size_t)(t0 + j) * DQK + dt * 64 + d] = from_f32<T>(v);
     }
   }
