@@ -217,6 +217,9 @@ __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
   constexpr int NDT = DQK / 64;
   __shared__ __attribute__((aligned(16))) T sK[BL * LD];  // w . K, token-major [l][d]
   __shared__ __attribute__((aligned(16))) T sV[BL * LD];  // V, token-major     [l][c]
+  // bf16: w . K - bf16(w . K), so that the chunk states carry w . K to ~2^-16
+  // (the backward's cancellations amplify state errors at long lengths)
+  __shared__ __attribute__((aligned(16))) T sKl[sizeof(T) == 2 ? BL * LD : 8];
   __shared__ float sw[BL];
   __shared__ float sdec;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -290,6 +293,11 @@ __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
     for (int e = 0; e < 16; ++e) kx[e] *= wr;
     st_row16<T>(sK, r, c0, kx);
     st_row16<T>(sV, r, c0, vx);
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) kx[e] -= to_f32(from_f32<T>(kx[e]));
+      st_row16<T>(sKl, r, c0, kx);
+    }
     if (c + 2 < ce) {
       load16f<T>(rk, ((unsigned)((c + 1) * BL + r) * DQK + dt * 64 + c0) * ES, kx);
       load16f<T>(rv, ((unsigned)((c + 1) * BL + r) * p.DV + ct * 64 + c0) * ES, vx);
@@ -301,10 +309,14 @@ __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[n][i] *= dec;
     mma64x<T, true, true>(acc, sV, LD, sK, LD, w, lane);  // S~^T += V^T (w . K)
+    if constexpr (sizeof(T) == 2) mma64x<T, true, true>(acc, sV, LD, sKl, LD, w, lane);
     if (lead) {  // n~[64 dt + r] += sum_l w_l k_l, four threads per row
       float a = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) a += to_f32(sK[(16 * (tid & 3) + e) * LD + r]);
+      for (int e = 0; e < 16; ++e) {
+        a += to_f32(sK[(16 * (tid & 3) + e) * LD + r]);
+        if constexpr (sizeof(T) == 2) a += to_f32(sKl[(16 * (tid & 3) + e) * LD + r]);
+      }
       a += __shfl_xor(a, 1, 64);
       a += __shfl_xor(a, 2, 64);
       nn = dec * nn + a;
