@@ -122,6 +122,16 @@ __device__ __forceinline__ void mma64x(f32x4 (&acc)[4], const T* A, int lda, con
   }
 }
 
+// Work-groups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  This bijection of [0, n) gives each XCD a contiguous range of logical
+// indices, so that tiles which read the same data (the tiles of one chunk,
+// or of one superchunk) share an L2: block b runs on XCD b % 8 and takes
+// logical index start(b % 8) + b / 8.
+__device__ __forceinline__ int xcd_local(int b, int n) {
+  const int x = b & 7, q = n >> 3, r = n & 7;
+  return x * q + (x < r ? x : r) + (b >> 3);
+}
+
 // dn~ = o dh / den~ for one element (the same expression in every kernel, so
 // that each rounds it identically)
 __device__ __forceinline__ float dn_of(float dh, float o, float rden) { return (dh * o) * rden; }
@@ -226,9 +236,10 @@ __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   const int NVT = p.DV / 64;
-  const int ct = blockIdx.x % NVT;
-  const int dt = (blockIdx.x / NVT) % NDT;
-  const int bs = blockIdx.x / (NVT * NDT);
+  const int bid = xcd_local((int)blockIdx.x, (int)gridDim.x);
+  const int ct = bid % NVT;
+  const int dt = (bid / NVT) % NDT;
+  const int bs = bid / (NVT * NDT);
   const int bh = bs / p.NS, sc = bs % p.NS;
   const int r = tid >> 2, c0 = 16 * (tid & 3);
   const size_t NST = (size_t)DQK * p.DV + DQK;
@@ -640,8 +651,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  const int dt = blockIdx.x % NDT;
-  const int bc = blockIdx.x / NDT;
+  const int bid = xcd_local((int)blockIdx.x, (int)gridDim.x);
+  const int dt = bid % NDT;
+  const int bc = bid / NDT;
   const int bh = bc / p.NC, c = bc % p.NC;
   const int r = tid >> 2, c0 = 16 * (tid & 3);
   const int t0 = c * BL;
@@ -821,8 +833,9 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   const int NVT = p.DV / 64;
-  const int tile = blockIdx.x % (NDT + NVT);
-  const int bc = blockIdx.x / (NDT + NVT);
+  const int bid = xcd_local((int)blockIdx.x, (int)gridDim.x);
+  const int tile = bid % (NDT + NVT);
+  const int bc = bid / (NDT + NVT);
   const int bh = bc / p.NC, c = bc % p.NC;
   const int r = tid >> 2, c0 = 16 * (tid & 3);
   const int t0 = c * BL;
