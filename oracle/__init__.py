@@ -67,7 +67,7 @@ def _load(path: str | None = None):
     lib.oracle_mlstm_step.restype = i
     lib.oracle_retention_fwd.argtypes = [i, i, i, i, i] + [P] * 7
     lib.oracle_retention_fwd.restype = i
-    lib.oracle_mlstm_bwd.argtypes = [i, i, i, i, i] + [P] * 20
+    lib.oracle_mlstm_bwd.argtypes = [i, i, i, i, i, i] + [P] * 20
     lib.oracle_mlstm_bwd.restype = i
     lib.oracle_retention_bwd.argtypes = [i, i, i, i, i] + [P] * 10
     lib.oracle_retention_bwd.restype = i
@@ -199,9 +199,9 @@ def retention_fwd(q, k, v, gamma=None, S0=None, lib=None):
 
 
 def mlstm_bwd(q, k, v, i_pre, f_pre, dh, o_pre=None, bias=None, C0=None, n0=None,
-              m0=None, lib=None):
+              m0=None, lib=None, num_blocks=1):
     """Gradients of sum(dh * h) for the mLSTM sequence form (vector
-    normaliser, one memory block), h = mlstm_fwd(q, k, v, ...)[0].  Shapes as
+    normaliser; num_blocks memory blocks), h = mlstm_fwd(q, k, v, ...)[0].  Shapes as
     in mlstm_fwd; dh [B,H,T,dv].  Returns a dict of float64 arrays: dq, dk,
     dv, di (i_pre), df (f_pre), do (o_pre; None without o_pre), dbias [H],
     dC0 [B,H,dqk,dv] and dn0 [B,H,dqk] (gradients of the stabilised initial
@@ -211,15 +211,17 @@ def mlstm_bwd(q, k, v, i_pre, f_pre, dh, o_pre=None, bias=None, C0=None, n0=None
     B, H, T, dqk = q.shape
     dv = v.shape[-1]
     assert k.shape == q.shape and v.shape == (B, H, T, dv) and g.shape == v.shape
+    nb = int(num_blocks)
+    cshape = (B, H, dqk, dv) if nb == 1 else (B, H, nb, dqk // nb, dv // nb)
     if c0 is not None:
-        c0 = np.ascontiguousarray(c0.reshape(B, H, dqk, dv))
+        c0 = np.ascontiguousarray(c0.reshape(cshape))
     out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v),
                di=np.zeros((B, H, T)), df=np.zeros((B, H, T)),
                do=np.zeros_like(v) if op is not None else None,
-               dbias=np.zeros(H), dC0=np.zeros((B, H, dqk, dv)),
+               dbias=np.zeros(H), dC0=np.zeros(cshape),
                dn0=np.zeros((B, H, dqk)))
     rc = (lib or _load()).oracle_mlstm_bwd(
-        B, H, T, dqk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(ip), _ptr(fp), _ptr(op),
+        B, H, T, dqk, dv, nb, _ptr(q), _ptr(k), _ptr(v), _ptr(ip), _ptr(fp), _ptr(op),
         _ptr(bs), _ptr(c0), _ptr(nn0), _ptr(mm0), _ptr(g), _ptr(out["dq"]),
         _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["di"]), _ptr(out["df"]),
         _ptr(out["do"]), _ptr(out["dbias"]), _ptr(out["dC0"]), _ptr(out["dn0"]))

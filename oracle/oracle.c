@@ -291,19 +291,25 @@ int oracle_retention_fwd(int B, int H, int T, int dk, int dv, const double* q,
  * recomputed per segment of SEG steps from a saved state at each segment start
  * (checkpoints), so memory stays O((T/SEG + SEG) d_qk d_v).
  *
+ * With nb memory blocks (the block-diagonal memory of the "Edifice.Recurrent.
+ * XLSTMv2" page, "Key Improvements" item 1) the state and G are block-diagonal
+ * [nb][d_qk/nb][d_v/nb]: every product above runs per block, while n~, g and
+ * the denominator stay per head.
  * dh [B,H,T,d_v] in; outputs (any may be NULL): dq, dk [B,H,T,d_qk]; dv, do_pre
- * [B,H,T,d_v]; di, df [B,H,T]; dbias [H] (summed over B); dC0 [B,H,d_qk,d_v];
- * dn0 [B,H,d_qk].  Returns 0, -1 for bad sizes, -2 when out of memory.
+ * [B,H,T,d_v]; di, df [B,H,T]; dbias [H] (summed over B); dC0
+ * [B,H,nb,d_qk/nb,d_v/nb]; dn0 [B,H,d_qk].  Returns 0, -1 for bad sizes, -2 when out of memory.
  */
-int oracle_mlstm_bwd(int B, int H, int T, int dqk, int dv, const double* q,
+int oracle_mlstm_bwd(int B, int H, int T, int dqk, int dv, int nb, const double* q,
                      const double* k, const double* v, const double* i_pre,
                      const double* f_pre, const double* o_pre, const double* bias,
                      const double* C0, const double* n0, const double* m0,
                      const double* dh, double* dq, double* dk, double* dvo,
                      double* di, double* df, double* do_pre, double* dbias,
                      double* dC0, double* dn0) {
-  if (B < 0 || H < 0 || T < 0 || dqk <= 0 || dv <= 0) return -1;
-  const size_t csz = (size_t)dqk * dv;
+  if (B < 0 || H < 0 || T < 0 || dqk <= 0 || dv <= 0 || nb <= 0) return -1;
+  if (dqk % nb || dv % nb) return -1;
+  const int dqkb = dqk / nb, dvb = dv / nb;
+  const size_t csz = (size_t)dqk * dv / nb; /* [nb][dqkb][dvb] */
   const size_t ssz = csz + (size_t)dqk + 1; /* one saved state: S~, n~, m */
   const long BH = (long)B * H;
   int SEG = 1;
@@ -342,7 +348,7 @@ int oracle_mlstm_bwd(int B, int H, int T, int dqk, int dv, const double* q,
       memcpy(cur, ckpt + (size_t)s * ssz, ssz * sizeof(double));
       for (int t = s * SEG; t < T && t < (s + 1) * SEG; ++t) {
         const size_t tok = (size_t)bh * T + t;
-        cell_step(dqk, dv, 1, q + tok * dqk, k + tok * dqk, v + tok * dv, i_pre[tok],
+        cell_step(dqk, dv, nb, q + tok * dqk, k + tok * dqk, v + tok * dv, i_pre[tok],
                   f_pre[tok], o_pre ? o_pre + tok * dv : NULL, bs, 1, 0.0, cur,
                   cur + csz, cur + csz + dqk, hbuf);
       }
@@ -356,7 +362,7 @@ int oracle_mlstm_bwd(int B, int H, int T, int dqk, int dv, const double* q,
         const size_t tok = (size_t)bh * T + t;
         double* nxt = seg + (size_t)(t - t0 + 1) * ssz;
         memcpy(nxt, seg + (size_t)(t - t0) * ssz, ssz * sizeof(double));
-        cell_step(dqk, dv, 1, q + tok * dqk, k + tok * dqk, v + tok * dv, i_pre[tok],
+        cell_step(dqk, dv, nb, q + tok * dqk, k + tok * dqk, v + tok * dv, i_pre[tok],
                   f_pre[tok], o_pre ? o_pre + tok * dv : NULL, bs, 1, 0.0, nxt,
                   nxt + csz, nxt + csz + dqk, hbuf);
       }
@@ -379,8 +385,10 @@ int oracle_mlstm_bwd(int B, int H, int T, int dqk, int dv, const double* q,
         const double den = fmax(fabs(zt), fl);
         double sdy = 0.0; /* (o * dh) . y */
         for (int c = 0; c < dv; ++c) {
+          const int b = c / dvb, cc = c % dvb;
+          const double* Sb = St + (size_t)b * dqkb * dvb;
           double num = 0.0;
-          for (int r = 0; r < dqk; ++r) num += St[(size_t)r * dv + c] * qt[r];
+          for (int r = 0; r < dqkb; ++r) num += Sb[(size_t)r * dvb + cc] * qt[b * dqkb + r];
           const double y = num / den;
           const double o = o_pre ? sigmoid(o_pre[tok * dv + c]) : 1.0;
           if (do_pre && o_pre) do_pre[tok * dv + c] = dht[c] * y * o * (1.0 - o);
@@ -389,39 +397,47 @@ int oracle_mlstm_bwd(int B, int H, int T, int dqk, int dv, const double* q,
         }
         const double dz = fabs(zt) > fl ? -sdy / den * (zt > 0 ? 1.0 : -1.0) : 0.0;
         dbias_acc += dz * fl;
-        /* dq_t = S~_t dn + n~_t dz */
+        /* dq_t = S~_t dn + n~_t dz (the matrix per block, n~ over the head) */
         if (dq)
-          for (int r = 0; r < dqk; ++r) {
-            double a = nt[r] * dz;
-            for (int c = 0; c < dv; ++c) a += St[(size_t)r * dv + c] * dn[c];
-            dq[tok * dqk + r] = a;
+          for (int d = 0; d < dqk; ++d) {
+            const int b = d / dqkb, r = d % dqkb;
+            const double* Sr = St + (size_t)b * dqkb * dvb + (size_t)r * dvb;
+            double a = nt[d] * dz;
+            for (int cc = 0; cc < dvb; ++cc) a += Sr[cc] * dn[b * dvb + cc];
+            dq[tok * dqk + d] = a;
           }
-        /* total gradients of the state at t */
-        for (int r = 0; r < dqk; ++r) {
-          for (int c = 0; c < dv; ++c) G[(size_t)r * dv + c] += qt[r] * dn[c];
-          g[r] += qt[r] * dz;
+        /* total gradients of the state at t (block-diagonal, like the state) */
+        for (int d = 0; d < dqk; ++d) {
+          const int b = d / dqkb, r = d % dqkb;
+          double* Gr = G + (size_t)b * dqkb * dvb + (size_t)r * dvb;
+          for (int cc = 0; cc < dvb; ++cc) Gr[cc] += qt[d] * dn[b * dvb + cc];
+          g[d] += qt[d] * dz;
         }
-        /* through S~_t = f' S~_{t-1} + i' k v^T */
+        /* through S~_t = f' S~_{t-1} + i' k v^T (per block) */
         const double lf = log_sigmoid(f_pre[tok]);
         const double fdec = exp(lf + mp - mt), iw = exp(i_pre[tok] - mt);
         double kGv = 0.0, kg = 0.0, dlf = 0.0;
-        for (int r = 0; r < dqk; ++r) {
-          double a = 0.0;
-          for (int c = 0; c < dv; ++c) a += G[(size_t)r * dv + c] * vt[c];
-          Gv[r] = a;
-          kGv += kt[r] * a;
-          kg += kt[r] * g[r];
-          double b = np_[r] * g[r];
-          for (int c = 0; c < dv; ++c) b += G[(size_t)r * dv + c] * Sp[(size_t)r * dv + c];
-          dlf += b;
+        for (int d = 0; d < dqk; ++d) {
+          const int b = d / dqkb, r = d % dqkb;
+          const size_t ro = (size_t)b * dqkb * dvb + (size_t)r * dvb;
+          double a = 0.0, bb = np_[d] * g[d];
+          for (int cc = 0; cc < dvb; ++cc) {
+            a += G[ro + cc] * vt[b * dvb + cc];
+            bb += G[ro + cc] * Sp[ro + cc];
+          }
+          Gv[d] = a;
+          kGv += kt[d] * a;
+          kg += kt[d] * g[d];
+          dlf += bb;
         }
         dlf *= fdec;
         if (dk)
-          for (int r = 0; r < dqk; ++r) dk[tok * dqk + r] = iw * (Gv[r] + g[r]);
+          for (int d = 0; d < dqk; ++d) dk[tok * dqk + d] = iw * (Gv[d] + g[d]);
         if (dvo)
           for (int c = 0; c < dv; ++c) {
+            const int b = c / dvb, cc = c % dvb;
             double a = 0.0;
-            for (int r = 0; r < dqk; ++r) a += G[(size_t)r * dv + c] * kt[r];
+            for (int r = 0; r < dqkb; ++r) a += G[(size_t)b * dqkb * dvb + (size_t)r * dvb + cc] * kt[b * dqkb + r];
             dvo[tok * dv + c] = iw * a;
           }
         if (di) di[tok] = iw * (kGv + kg);

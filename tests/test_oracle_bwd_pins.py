@@ -163,3 +163,31 @@ def test_retention_bwd_pin_parallel_form_autograd():
     (out * torch.from_numpy(do)).sum().backward()
     for t, nm in ((tq, "dq"), (tk, "dk"), (tv, "dv")):
         assert _relerr(g[nm], t.grad.numpy()) < 1e-10, nm
+
+
+def test_bwd_pin_finite_differences_block_diagonal():
+    """Two memory blocks (the XLSTMv2 page's block-diagonal memory): the
+    gradient of every input and of the block-diagonal initial state against
+    central finite differences of the forward oracle with num_blocks=2."""
+    a, dh = _case(31, 1, 2, 8, 4, 6, kscale=3.0)
+    B, H, dqk, dv, nb = 1, 2, 4, 6, 2
+    a["C0"] = np.random.default_rng(32).standard_normal((B, H, nb, dqk // nb, dv // nb)) * 0.3
+
+    def fwd(a):
+        return oracle.mlstm_fwd(a["q"], a["k"], a["v"], a["i_pre"], a["f_pre"], a["o_pre"], a["bias"],
+                                a["C0"], a["n0"], a["m0"], num_blocks=nb)[0]
+
+    g = oracle.mlstm_bwd(dh=dh, num_blocks=nb, **a)
+    eps = 1e-6
+    for name, gname in GRAD_OF.items():
+        x = a[name]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            lp = np.sum(dh * fwd(a))
+            x[idx] = keep - eps
+            lm = np.sum(dh * fwd(a))
+            x[idx] = keep
+            fd[idx] = (lp - lm) / (2 * eps)
+        assert _relerr(g[gname], fd) < 1e-6, name
