@@ -269,13 +269,15 @@ size_t mlstm_chunkwise_bwd_workspace_bytes(int B, int H, int T, int d_qk, int d_
  *   do_pre   [B,H,T,d_v] dtype dt: gradient of o_pre; required exactly when
  *                  o_pre is given, else NULL;
  *   dbias    [H] fp32 or NULL: gradient of norm_bias, summed over the batch;
- *   dC0 [B,H,d_qk,d_v], dn0 [B,H,d_qk] fp32 or NULL: gradients of the
- *                  stabilised initial state C0, n0 (also for a zero state).
+ *   dC0 [B,H,nb,d_qk/nb,d_v/nb], dn0 [B,H,d_qk] fp32 or NULL: gradients of
+ *                  the stabilised initial state C0, n0 (also for a zero state).
  *                  The gradient of m0 is <dC0, C0> + <dn0, n0>.
  * The final state gets no incoming gradient (the loss is taken on h only).
- * Requires num_blocks = 1, chunk = 64, d_v a multiple of 64 and d_qk in
- * {64, 128, 256} (bf16) or 64 (fp32); other shapes return
- * MLSTM_E_UNSUPPORTED.  workspace: at least mlstm_chunkwise_bwd_workspace_bytes
+ * Requires chunk = 64 and either num_blocks = 1 with d_v a multiple of 64 and
+ * d_qk in {64, 128, 256} (bf16) or 64 (fp32), or num_blocks = 2 with
+ * d_qk = d_v = 64 (the block-diagonal memory of the "Edifice.Recurrent.XLSTMv2"
+ * page, "Key Improvements" item 1: one numerator per block, the normaliser
+ * over the head); other shapes return MLSTM_E_UNSUPPORTED.  workspace: at least mlstm_chunkwise_bwd_workspace_bytes
  * bytes, 256-byte aligned (it holds the start state of every chunk and the
  * backward state at every chunk end, fp32: 2 (d_qk d_v + d_qk) 4 bytes per
  * chunk and batch*head).  Enqueues the forward's state passes and eight

@@ -303,12 +303,12 @@ def retention_step(q, k, v, S, gamma=None, out=None):
 
 
 def chunkwise_bwd(q, k, v, i_pre, f_pre, dh, o_pre=None, bias=None, state=None, chunk=64,
-                  state_grad=True, workspace=None):
+                  state_grad=True, workspace=None, num_blocks=1):
     """mlstm_chunkwise_bwd: gradients of sum(dh * h) for h = chunkwise_fwd(q, k,
-    v, i_pre, f_pre, o_pre, bias, state) (vector normaliser, one memory block).
+    v, i_pre, f_pre, o_pre, bias, state, num_blocks) (vector normaliser).
     Returns a dict with dq, dk, dv, di (i_pre), df (f_pre), do (o_pre, or
     None), dbias ([H] fp32, or None without bias) and, with state_grad, dC0
-    [B,H,1,dqk,dv] and dn0 [B,H,dqk] (fp32)."""
+    [B,H,nb,dqk/nb,dv/nb] and dn0 [B,H,dqk] (fp32)."""
     B, H, T, dqk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
@@ -322,25 +322,26 @@ def chunkwise_bwd(q, k, v, i_pre, f_pre, dh, o_pre=None, bias=None, state=None, 
     _need(f_pre, "f_pre", (B, H, T), dt, dev)
     _need(o_pre, "o_pre", (B, H, T, dv), dt, dev)
     _need(bias, "bias", (H,), torch.float32, dev)
+    nb = int(num_blocks)
+    cshape = (B, H, nb, dqk // nb, dv // nb)
     C0 = n0 = m0 = None
     if state is not None:
         C0, n0, m0 = state
-        for t, nm, shp in zip((C0, n0, m0), ("C0", "n0", "m0"),
-                              ((B, H, 1, dqk, dv), (B, H, dqk), (B, H))):
+        for t, nm, shp in zip((C0, n0, m0), ("C0", "n0", "m0"), (cshape, (B, H, dqk), (B, H))):
             _need(t, nm, shp, torch.float32, dev)
     out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                di=torch.empty_like(i_pre), df=torch.empty_like(f_pre),
                do=torch.empty_like(o_pre) if o_pre is not None else None,
                dbias=torch.empty(H, dtype=torch.float32, device=dev) if bias is not None else None,
-               dC0=torch.empty(B, H, 1, dqk, dv, dtype=torch.float32, device=dev) if state_grad else None,
+               dC0=torch.empty(cshape, dtype=torch.float32, device=dev) if state_grad else None,
                dn0=torch.empty(B, H, dqk, dtype=torch.float32, device=dev) if state_grad else None)
     L = lib()
-    nbytes = L.mlstm_chunkwise_bwd_workspace_bytes(B, H, T, dqk, dv, 1, chunk, _DT[dt])
+    nbytes = L.mlstm_chunkwise_bwd_workspace_bytes(B, H, T, dqk, dv, nb, chunk, _DT[dt])
     if nbytes == 0:
-        _check(L.mlstm_chunkwise_bwd(B, H, T, dqk, dv, 1, chunk, _DT[dt], *([None] * 20), None, 0, None),
+        _check(L.mlstm_chunkwise_bwd(B, H, T, dqk, dv, nb, chunk, _DT[dt], *([None] * 20), None, 0, None),
                "mlstm_chunkwise_bwd")
     ws = _workspace(nbytes, dev, workspace)
-    rc = L.mlstm_chunkwise_bwd(B, H, T, dqk, dv, 1, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre),
+    rc = L.mlstm_chunkwise_bwd(B, H, T, dqk, dv, nb, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre),
                                _ptr(f_pre), _ptr(o_pre), _ptr(bias), _ptr(C0), _ptr(n0), _ptr(m0),
                                _ptr(dh), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["di"]),
                                _ptr(out["df"]), _ptr(out["do"]), _ptr(out["dbias"]), _ptr(out["dC0"]),

@@ -131,9 +131,10 @@ struct BwdPlan {
 int plan_bwd(int B, int H, int T, int dqk, int dv, int nb, int chunk, int dt, BwdPlan* bp, bool ret = false) {
   const int rc = plan_chunkwise(B, H, T, dqk, dv, nb, chunk, dt, ret, &bp->fwd);
   if (rc != MLSTM_OK) return rc;
-  if (nb != 1) return fail(MLSTM_E_UNSUPPORTED, "the backward pass takes num_blocks = 1 (got %d)", nb);
+  if (nb != 1 && !(nb == 2 && dqk == 64 && dv == 64 && !ret))
+    return fail(MLSTM_E_UNSUPPORTED, "the backward pass takes num_blocks = 1, or 2 with d_qk = d_v = 64 (got %d)", nb);
   if (chunk != 64) return fail(MLSTM_E_UNSUPPORTED, "the backward pass takes chunk = 64 (got %d)", chunk);
-  if (!mlstm::bwd_supported(dt, dqk, dv))
+  if (!mlstm::bwd_supported(dt, dqk, dv, nb))
     return fail(MLSTM_E_UNSUPPORTED, "no backward kernel for dtype=%s d_qk=%d d_v=%d", dt ? "bf16" : "fp32", dqk,
                 dv);
   const size_t BH = (size_t)B * H, NC = bp->fwd.NC, NCL = NC * 64, es = dt ? 2 : 4;
@@ -144,7 +145,7 @@ int plan_bwd(int B, int H, int T, int dqk, int dv, int nb, int chunk, int dt, Bw
   o += align256(BH * NC * 4);
   bp->off_U = o;
   o += align256(BH * NC * ((size_t)dqk * dv + dqk) * 4);
-  const size_t tile = align256(BH * NC * 64 * 64 * es);
+  const size_t tile = align256(BH * NC * nb * 64 * 64 * es);  // one 64 x 64 per chunk and memory block
   bp->off_P = o;
   bp->off_Pt = o + tile;
   bp->off_D = o + 2 * tile;
@@ -239,6 +240,7 @@ int mlstm_chunkwise_bwd(int B, int H, int T, int d_qk, int d_v, int num_blocks, 
   b.NC = pl.NC;
   b.G = pl.G;
   b.NS = pl.NS;
+  b.NB = num_blocks;
   b.sc_nst = pl.nstate;
   b.q = q;
   b.k = k;
@@ -339,6 +341,7 @@ int retention_chunkwise_bwd(int B, int H, int T, int d_k, int d_v, int chunk, ml
   b.NC = pl.NC;
   b.G = pl.G;
   b.NS = pl.NS;
+  b.NB = 1;
   b.ret = 1;
   b.sc_nst = pl.nstate;
   b.q = q;

@@ -105,12 +105,12 @@ __device__ __forceinline__ float frag_krows(const float* t, int ld, int col0, in
 // columns.  A (rows m, contraction k): AR ? stored [k][m] : stored [m][k];
 // B (contraction k, columns n): BR ? stored [k][n] : stored [n][k].
 // acc[n][i] is row 16 w + 4 lg + i, column 16 n + lr.
-template <typename T, bool AR, bool BR>
+template <typename T, bool AR, bool BR, int KB = 0, int KE = 64>
 __device__ __forceinline__ void mma64x(f32x4 (&acc)[4], const T* A, int lda, const T* B, int ldb, int w, int lane) {
   constexpr int K = Mma<T>::K;
   const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
-  for (int k0 = 0; k0 < 64; k0 += K) {
+  for (int k0 = KB; k0 < KE; k0 += K) {
     const typename Mma<T>::frag a =
         AR ? frag_krows(A, lda, 16 * w, k0, lg, lr) : frag_kcols(A, lda, 16 * w + lr, k0, lg, lr);
 #pragma unroll
@@ -131,6 +131,24 @@ __device__ __forceinline__ int xcd_local(int b, int n) {
   const int x = b & 7, q = n >> 3, r = n & 7;
   return x * q + (x < r ? x : r) + (b >> 3);
 }
+
+// Block-diagonal memory (NB = 2 blocks of a 64-wide head): the contraction
+// over a 64-wide index split at 32, one product per block.
+template <typename T, bool AR, bool BR, int NB>
+__device__ __forceinline__ void mma64x_blocks(f32x4 (&acc)[NB][4], const T* A, int lda, const T* B, int ldb, int w,
+                                              int lane) {
+  static_assert(NB == 1 || NB == 2, "one or two memory blocks");
+  if constexpr (NB == 1) {
+    mma64x<T, AR, BR>(acc[0], A, lda, B, ldb, w, lane);
+  } else {
+    mma64x<T, AR, BR, 0, 32>(acc[0], A, lda, B, ldb, w, lane);
+    mma64x<T, AR, BR, 32, 64>(acc[1], A, lda, B, ldb, w, lane);
+  }
+}
+// Output column tile n (columns 16 n .. 16 n + 15 of a 64-wide tile) lies in
+// memory block n * NB / 4; rows of wave w in block w * NB / 4.
+template <int NB>
+__device__ __forceinline__ constexpr int col_block(int n) { return n * NB / 4; }
 
 // dn~ = o dh / den~ for one element (the same expression in every kernel, so
 // that each rounds it identically)
@@ -220,8 +238,9 @@ __device__ __forceinline__ void load_chunk_gates(const BwdParams& p, int bh, int
 //   m <- b_L + M_L,  with M_L = max(m, g_L) and w_l = 2^{a_l - M_L}
 // (the forward's state update; K and V of the next chunk load during the
 // current one's product).
-template <typename T, int DQK>
+template <typename T, int DQK, int NB>
 __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
+  static_assert(NB == 1 || DQK == 64, "two blocks on 64-wide heads only");
   constexpr int LD = BT<T>::LD;
   constexpr unsigned ES = sizeof(T);
   constexpr int NDT = DQK / 64;
@@ -257,10 +276,18 @@ __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
   if (has) {
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-      const float4 u = *reinterpret_cast<const float4*>(S0 + toff + (size_t)16 * n * p.DV);
-      acc[n] = f32x4{u.x, u.y, u.z, u.w};
+      if constexpr (NB == 1) {
+        const float4 u = *reinterpret_cast<const float4*>(S0 + toff + (size_t)16 * n * p.DV);
+        acc[n] = f32x4{u.x, u.y, u.z, u.w};
+      } else if (col_block<NB>(n) == col_block<NB>(w)) {
+        // block layout [NB][32][32]: d = 16 n + lr, c = 16 w + 4 lg + i, same block bb
+        const int bb = col_block<NB>(n);
+        const float4 u = *reinterpret_cast<const float4*>(S0 + (size_t)bb * 1024 + (16 * n + lr - 32 * bb) * 32 +
+                                                          16 * w + 4 * lg - 32 * bb);
+        acc[n] = f32x4{u.x, u.y, u.z, u.w};
+      }
     }
-    if (lead && !p.ret) nn = S0[(size_t)DQK * p.DV + dt * 64 + r];
+    if (lead && !p.ret) nn = S0[p.sc_nst - DQK + dt * 64 + r];
   }
   float m = p.sc_min[(size_t)bh * p.NS + sc];  // meaningful in threads below 64
   const int cb = sc * p.G, ce = min(p.NC, cb + p.G);
@@ -321,6 +348,11 @@ __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
       for (int i = 0; i < 4; ++i) acc[n][i] *= dec;
     mma64x<T, true, true>(acc, sV, LD, sK, LD, w, lane);  // S~^T += V^T (w . K)
     if constexpr (sizeof(T) == 2) mma64x<T, true, true>(acc, sV, LD, sKl, LD, w, lane);
+    if constexpr (NB > 1) {  // the memory is block-diagonal
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        if (col_block<NB>(n) != col_block<NB>(w)) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     if (lead) {  // n~[64 dt + r] += sum_l w_l k_l, four threads per row
       float a = 0.f;
 #pragma unroll
@@ -343,15 +375,16 @@ __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
 // one side only would leave the cancellation residue in the gradient.
 // RET (retention): no normaliser, so den~ = 1 and dz~ = 0, and the readout
 // (needed only for dz~ and d o_pre) is not recomputed.
-template <typename T, int DQK, bool RET>
+template <typename T, int DQK, bool RET, int NB>
 __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
+  static_assert(NB == 1 || DQK == 64, "two blocks on 64-wide heads only");
   constexpr int LD = BT<T>::LD;
   constexpr int LDQ = DQK + 16 / (int)sizeof(T);
   constexpr unsigned ES = sizeof(T);
   __shared__ __attribute__((aligned(16))) T sQ[BL * LDQ];  // Q, token-major
   __shared__ __attribute__((aligned(16))) T sX[BL * LD];   // K, dN, S~ tiles  [j][d], [j][c], [d][c]
   __shared__ __attribute__((aligned(16))) T sY[BL * LD];   // V slices                  [l][c]
-  __shared__ __attribute__((aligned(16))) T sP[BL * LD];   // P                         [j][l]
+  __shared__ __attribute__((aligned(16))) T sP[NB][BL * LD];  // P of each memory block   [j][l]
   // bf16 lo parts x - bf16(x) of dn~ and then of the S~ tiles: D, dh . h and
   // the readout see dn~ and the state to ~2^-16 (a near-cancelling
   // dn~ . (v_l - y_j) must not see dn~ rounded; the initial state is exact
@@ -376,8 +409,9 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
   const auto rk = make_rsrc(static_cast<const T*>(p.k) + (size_t)bh * p.T * DQK, (unsigned)(p.T * DQK) * ES);
 
   // S = Q K^T over feature slices of 64 (Q kept whole); q_j . n~_prev alongside
-  f32x4 accP[4];
-  zero_acc(accP);
+  f32x4 accP[NB][4];  // per memory block: E . (Q_b K_b^T)
+#pragma unroll
+  for (int b = 0; b < NB; ++b) zero_acc(accP[b]);
   float qn = 0.f;
   for (int ds = 0; ds < DQK / 64; ++ds) {
     float x[16], y[16];
@@ -404,7 +438,7 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
     }
     st_row16<T>(sX, r, c0, y);
     __syncthreads();
-    mma64x<T, false, false>(accP, sQ + ds * 64, LDQ, sX, LD, w, lane);
+    mma64x_blocks<T, false, false, NB>(accP, sQ + ds * 64, LDQ, sX, LD, w, lane);
   }
   qn += __shfl_xor(qn, 1, 64);
   qn += __shfl_xor(qn, 2, 64);
@@ -412,9 +446,9 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
 
   // P = E . S (kept in fp32 registers), its row sums; P and P^T to the
   // workspace, P to LDS for the readout
-  T* Pw = static_cast<T*>(p.wsP) + ((size_t)bh * p.NC + c) * BL * BL;
-  T* Ptw = static_cast<T*>(p.wsPt) + ((size_t)bh * p.NC + c) * BL * BL;
-  float rs[4] = {0.f, 0.f, 0.f, 0.f};
+  T* Pw = static_cast<T*>(p.wsP) + ((size_t)bh * p.NC + c) * NB * BL * BL;
+  T* Ptw = static_cast<T*>(p.wsPt) + ((size_t)bh * p.NC + c) * NB * BL * BL;
+  float rs[4] = {0.f, 0.f, 0.f, 0.f};  // the normaliser sums over the whole head
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int l = 16 * n + lr;
@@ -422,12 +456,18 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
     for (int i = 0; i < 4; ++i) {
       const int j = 16 * w + 4 * lg + i;
       const float e = l <= j ? exp2_fast(sa[l] - sM[j]) : 0.f;
-      accP[n][i] *= e;
-      rs[i] += accP[n][i];
-      Pw[j * BL + l] = from_f32<T>(accP[n][i]);
-      sP[j * LD + l] = from_f32<T>(accP[n][i]);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        accP[b][n][i] *= e;
+        rs[i] += accP[b][n][i];
+        Pw[b * BL * BL + j * BL + l] = from_f32<T>(accP[b][n][i]);
+        sP[b][j * LD + l] = from_f32<T>(accP[b][n][i]);
+      }
     }
-    store4f(Ptw + l * BL + 16 * w + 4 * lg, accP[n][0], accP[n][1], accP[n][2], accP[n][3]);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      store4f(Ptw + b * BL * BL + l * BL + 16 * w + 4 * lg, accP[b][n][0], accP[b][n][1], accP[b][n][2],
+              accP[b][n][3]);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -458,8 +498,9 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
                             p.o_pre ? (unsigned)(p.T * p.DV) * ES : 0u);
   T* dow = p.d_o ? static_cast<T*>(p.d_o) + (size_t)bh * p.T * p.DV : nullptr;
   const float rden = sden[r];
-  f32x4 accD[4];
-  zero_acc(accD);
+  f32x4 accD[NB][4];  // per memory block: dN_b V_b^T
+#pragma unroll
+  for (int b = 0; b < NB; ++b) zero_acc(accD[b]);
   float sint[4] = {0.f, 0.f, 0.f, 0.f};  // rows 16 w + 4 lg + i: dn~ . (Q S~) partials
   // Global loads run one step ahead: slice cs + 1's dh, o_pre, v and the next
   // S~ tile are in flight while the current ones are multiplied.
@@ -496,9 +537,19 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
     f32x4 accI[4], accN[4];
     zero_acc(accI);
     zero_acc(accN);
-    mma64x<T, false, false>(accD, sX, LD, sY, LD, w, lane);  // sum_c dn~_jc v_lc
-    if constexpr (sizeof(T) == 2) mma64x<T, false, false>(accD, sXl, LD, sY, LD, w, lane);
-    mma64x<T, false, true>(accN, sP, LD, sY, LD, w, lane);  // sum_l P_jl v_lc
+    mma64x_blocks<T, false, false, NB>(accD, sX, LD, sY, LD, w, lane);  // sum_c dn~_jc v_lc
+    if constexpr (sizeof(T) == 2) mma64x_blocks<T, false, false, NB>(accD, sXl, LD, sY, LD, w, lane);
+    if constexpr (NB == 1) {
+      mma64x<T, false, true>(accN, sP[0], LD, sY, LD, w, lane);  // sum_l P_jl v_lc
+    } else {  // output column c takes the P of its block
+      f32x4 t1[4];
+      zero_acc(t1);
+      mma64x<T, false, true>(accN, sP[0], LD, sY, LD, w, lane);
+      mma64x<T, false, true>(t1, sP[1], LD, sY, LD, w, lane);
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        if (col_block<NB>(n) == 1) accN[n] = t1[n];
+    }
     // this lane's dn~ values, so that sX / sXl can hold the S~ tiles next
     float dnv[4][4];
 #pragma unroll
@@ -547,7 +598,9 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
   for (int i = 0; i < 4; ++i) {
     float a = 0.f, b = sint[i];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) a += accP[n][i] * accD[n][i];
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) a += accP[b][n][i] * accD[b][n][i];
     const int j = 16 * w + 4 * lg + i;
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1) {
@@ -570,7 +623,9 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
     for (int n = 0; n < 4; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float x = (accD[n][i] + sdz[16 * w + 4 * lg + i]) * accP[n][i];
+        float x = 0.f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) x += (accD[b][n][i] + sdz[16 * w + 4 * lg + i]) * accP[b][n][i];
         rsum[i] += x;
         csum[n] += x;
       }
@@ -613,27 +668,32 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
     if (tid == 0) p.ws_dbias[(size_t)bh * p.NC + c] = bsum;
   }
 
-  // D' = E . (dN V^T + dz~) and its transpose
-  T* Dw = static_cast<T*>(p.wsD) + ((size_t)bh * p.NC + c) * BL * BL;
-  T* Dtw = static_cast<T*>(p.wsDt) + ((size_t)bh * p.NC + c) * BL * BL;
+  // D' = E . (dN V^T + dz~) per memory block, and its transpose
+  T* Dw = static_cast<T*>(p.wsD) + ((size_t)bh * p.NC + c) * NB * BL * BL;
+  T* Dtw = static_cast<T*>(p.wsDt) + ((size_t)bh * p.NC + c) * NB * BL * BL;
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int l = 16 * n + lr;
-    float dv4[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = 16 * w + 4 * lg + i;
-      const float e = l <= j ? exp2_fast(sa[l] - sM[j]) : 0.f;
-      dv4[i] = e * (accD[n][i] + sdz[j]);
-      Dw[j * BL + l] = from_f32<T>(dv4[i]);
+    for (int b = 0; b < NB; ++b) {
+      float dv4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 16 * w + 4 * lg + i;
+        const float e = l <= j ? exp2_fast(sa[l] - sM[j]) : 0.f;
+        dv4[i] = e * (accD[b][n][i] + sdz[j]);
+        Dw[b * BL * BL + j * BL + l] = from_f32<T>(dv4[i]);
+      }
+      store4f(Dtw + b * BL * BL + l * BL + 16 * w + 4 * lg, dv4[0], dv4[1], dv4[2], dv4[3]);
     }
-    store4f(Dtw + l * BL + 16 * w + 4 * lg, dv4[0], dv4[1], dv4[2], dv4[3]);
   }
 }
 
 // ---------------------------------------------------------------- kernel 2
-template <typename T, int DQK>
+template <typename T, int DQK, int NB>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
+  static_assert(NB == 1 || DQK == 64, "two blocks on 64-wide heads only");
+  __shared__ __attribute__((aligned(16))) T sA2[NB > 1 ? BL * BT<T>::LD : 8];  // D' of block 1
   constexpr int LD = BT<T>::LD;
   constexpr unsigned ES = sizeof(T);
   constexpr int NDT = DQK / 64;
@@ -673,18 +733,31 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     float x[16], y[16], d[16];
     load16f<T>(rq, ((unsigned)(t0 + r) * DQK + dt * 64 + c0) * ES, x);
     load16f<T>(rk, ((unsigned)(t0 + r) * DQK + dt * 64 + c0) * ES, y);
-    const T* Dw = static_cast<const T*>(p.wsD) + ((size_t)bh * p.NC + c) * BL * BL;
+    const T* Dw = static_cast<const T*>(p.wsD) + ((size_t)bh * p.NC + c) * NB * BL * BL;
 #pragma unroll
     for (int e = 0; e < 16; ++e) d[e] = to_f32(Dw[r * BL + c0 + e]);
     st_row16<T>(sQ, r, c0, x);
     st_row16<T>(sB, r, c0, y);
     st_row16<T>(sA, r, c0, d);
+    if constexpr (NB > 1) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) d[e] = to_f32(Dw[BL * BL + r * BL + c0 + e]);
+      st_row16<T>(sA2, r, c0, d);
+    }
   }
   __syncthreads();
   f32x4 acc[4], accx[4];
   zero_acc(acc);
   zero_acc(accx);
   mma64x<T, false, true>(acc, sA, LD, sB, LD, w, lane);  // sum_l D'_jl k_l
+  if constexpr (NB > 1) {  // feature column d takes the D' of its block
+    f32x4 t1[4];
+    zero_acc(t1);
+    mma64x<T, false, true>(t1, sA2, LD, sB, LD, w, lane);
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+      if (col_block<NB>(n) == 1) acc[n] = t1[n];
+  }
 
   const auto rdh = make_rsrc(static_cast<const T*>(p.dh) + (size_t)bh * p.T * p.DV, (unsigned)(p.T * p.DV) * ES);
   const auto ro = make_rsrc(p.o_pre ? static_cast<const T*>(p.o_pre) + (size_t)bh * p.T * p.DV : nullptr,
@@ -737,6 +810,11 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     zero_acc(u);
     mma64x<T, true, true>(u, sQ, LD, sA, LD, w, lane);  // U_dc = sum_j q_jd alpha_j dN_jc
     if constexpr (sizeof(T) == 2) mma64x<T, true, true>(u, sQ, LD, sAl, LD, w, lane);
+    if constexpr (NB > 1) {  // the memory (and its gradient) is block-diagonal
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        if (col_block<NB>(n) != col_block<NB>(w)) u[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int n = 0; n < 4; ++n)
 #pragma unroll
@@ -809,7 +887,16 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p, int DQK) {
     for (int i = 0; i < 4; ++i) {
       const size_t e = e0 + i;
       if (e < CS) {
-        if (p.dC0) p.dC0[(size_t)bh * CS + e] = g4[i];
+        if (p.dC0) {
+          if (p.NB == 1) {
+            p.dC0[(size_t)bh * CS + e] = g4[i];
+          } else {  // [nb][d_qk/nb][d_v/nb]; off-diagonal entries are zero
+            const int d = (int)(e / p.DV), cc = (int)(e % p.DV);
+            const int bq = DQK / p.NB, bv = p.DV / p.NB, b = d / bq;
+            if (cc / bv == b)
+              p.dC0[(size_t)bh * (CS / p.NB) + (size_t)b * bq * bv + (size_t)(d % bq) * bv + cc % bv] = g4[i];
+          }
+        }
       } else if (e < NST) {
         if (p.dn0) p.dn0[(size_t)bh * DQK + (e - CS)] = g4[i];
       }
@@ -818,8 +905,10 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p, int DQK) {
 }
 
 // ---------------------------------------------------------------- kernel 4
-template <typename T, int DQK>
+template <typename T, int DQK, int NB>
 __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
+  static_assert(NB == 1 || DQK == 64, "two blocks on 64-wide heads only");
+  __shared__ __attribute__((aligned(16))) T sA2[NB > 1 ? BL * BT<T>::LD : 8];  // D'^T or P^T of block 1
   constexpr int LD = BT<T>::LD;
   constexpr unsigned ES = sizeof(T);
   constexpr int NDT = DQK / 64;
@@ -856,15 +945,28 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
       float x[16], y[16], d[16];
       load16f<T>(rq, ((unsigned)(t0 + r) * DQK + dt * 64 + c0) * ES, x);
       load16f<T>(rk, ((unsigned)(t0 + r) * DQK + dt * 64 + c0) * ES, y);
-      const T* Dt = static_cast<const T*>(p.wsDt) + ((size_t)bh * p.NC + c) * BL * BL;
+      const T* Dt = static_cast<const T*>(p.wsDt) + ((size_t)bh * p.NC + c) * NB * BL * BL;
 #pragma unroll
       for (int e = 0; e < 16; ++e) d[e] = to_f32(Dt[r * BL + c0 + e]);
       st_row16<T>(sA, r, c0, d);
+      if constexpr (NB > 1) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) d[e] = to_f32(Dt[BL * BL + r * BL + c0 + e]);
+        st_row16<T>(sA2, r, c0, d);
+      }
       st_row16<T>(sB, r, c0, x);  // Q [l][d]
       st_row16<T>(sK, r, c0, y);
     }
     __syncthreads();
     mma64x<T, false, true>(acc, sA, LD, sB, LD, w, lane);  // sum_l D'_lj q_ld
+    if constexpr (NB > 1) {  // feature column d takes the D' of its block
+      f32x4 t1[4];
+      zero_acc(t1);
+      mma64x<T, false, true>(t1, sA2, LD, sB, LD, w, lane);
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        if (col_block<NB>(n) == 1) acc[n] = t1[n];
+    }
     const int NCS = p.DV / 64;
     float vv[16], sv[16];  // one slice ahead
     load16f<T>(rv, ((unsigned)(t0 + r) * p.DV + c0) * ES, vv);
@@ -925,14 +1027,27 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) g[e] = dn_of(g[e], 1.f, rden);
       }
-      const T* Pt = static_cast<const T*>(p.wsPt) + ((size_t)bh * p.NC + c) * BL * BL;
+      const T* Pt = static_cast<const T*>(p.wsPt) + ((size_t)bh * p.NC + c) * NB * BL * BL;
 #pragma unroll
       for (int e = 0; e < 16; ++e) d[e] = to_f32(Pt[r * BL + c0 + e]);
       st_row16<T>(sA, r, c0, d);
+      if constexpr (NB > 1) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) d[e] = to_f32(Pt[BL * BL + r * BL + c0 + e]);
+        st_row16<T>(sA2, r, c0, d);
+      }
       st_row16<T>(sB, r, c0, g);  // dN [l][c]
     }
     __syncthreads();
     mma64x<T, false, true>(acc, sA, LD, sB, LD, w, lane);  // sum_l P_lj dn~_lc
+    if constexpr (NB > 1) {  // value column c takes the P of its block
+      f32x4 t1[4];
+      zero_acc(t1);
+      mma64x<T, false, true>(t1, sA2, LD, sB, LD, w, lane);
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        if (col_block<NB>(n) == 1) acc[n] = t1[n];
+    }
     float y[16], sv[16];  // one feature slice ahead
     load16f<T>(rk, ((unsigned)(t0 + r) * DQK + c0) * ES, y);
     ld16(Gc + (size_t)r * p.DV + ct * 64 + c0, sv);
@@ -1018,20 +1133,20 @@ __global__ void bwd_bias_kernel(BwdParams p) {
   }
 }
 
-template <typename T, int DQK>
+template <typename T, int DQK, int NB = 1>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   const unsigned BH = (unsigned)(p.B * p.H);
   const unsigned nch = BH * (unsigned)p.NC;
-  hipLaunchKernelGGL((bwd_chunk_states_kernel<T, DQK>), dim3(BH * p.NS * (DQK / 64) * (p.DV / 64)), dim3(256), 0,
+  hipLaunchKernelGGL((bwd_chunk_states_kernel<T, DQK, NB>), dim3(BH * p.NS * (DQK / 64) * (p.DV / 64)), dim3(256), 0,
                      stream, p);
   if (p.ret)
-    hipLaunchKernelGGL((bwd_scores_kernel<T, DQK, true>), dim3(nch), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_scores_kernel<T, DQK, true, NB>), dim3(nch), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((bwd_scores_kernel<T, DQK, false>), dim3(nch), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL((bwd_dq_kernel<T, DQK>), dim3(nch * (DQK / 64)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_scores_kernel<T, DQK, false, NB>), dim3(nch), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, DQK, NB>), dim3(nch * (DQK / 64)), dim3(256), 0, stream, p);
   const size_t NST = (size_t)DQK * p.DV + DQK;
   hipLaunchKernelGGL(bwd_scan_kernel, dim3((unsigned)((NST / 4 + 255) / 256), BH), dim3(256), 0, stream, p, DQK);
-  hipLaunchKernelGGL((bwd_dkv_kernel<T, DQK>), dim3(nch * (DQK / 64 + p.DV / 64)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dkv_kernel<T, DQK, NB>), dim3(nch * (DQK / 64 + p.DV / 64)), dim3(256), 0, stream, p);
   if (!p.ret) {  // retention has no gates or normaliser to differentiate
     hipLaunchKernelGGL(bwd_gate_total_kernel, dim3(nch), dim3(64), 0, stream, p, DQK / 64);
     hipLaunchKernelGGL((bwd_gate_kernel<T>), dim3(nch), dim3(64), 0, stream, p);
@@ -1042,13 +1157,19 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
 
 }  // namespace
 
-bool bwd_supported(int dtype, int dqk, int dv) {
+bool bwd_supported(int dtype, int dqk, int dv, int nb) {
   if (dv % 64) return false;
+  if (nb == 2) return dqk == 64 && dv == 64;  // two 32-wide blocks of a 64-wide head
+  if (nb != 1) return false;
   if (dtype == 1) return dqk == 64 || dqk == 128 || dqk == 256;
   return dqk == 64;
 }
 
 hipError_t launch_bwd(int dtype, const BwdParams& p, hipStream_t stream) {
+  if (p.NB == 2) {
+    if (p.DQK != 64 || p.DV != 64 || p.ret) return hipErrorInvalidValue;
+    return dtype == 1 ? launch_bwd_t<__bf16, 64, 2>(p, stream) : launch_bwd_t<float, 64, 2>(p, stream);
+  }
   if (dtype == 1) {
     if (p.DQK == 64) return launch_bwd_t<__bf16, 64>(p, stream);
     if (p.DQK == 128) return launch_bwd_t<__bf16, 128>(p, stream);

@@ -97,6 +97,7 @@ bool step_supported(int dqk, int dv, int nb);
 // 64 tokens), after the forward plan's state passes ran.
 struct BwdParams {
   int B, H, T, DQK, DV, NC, G, NS;
+  int NB;         // memory blocks (1, or 2 on 64-wide heads)
   int ret;        // retention: no gates, no normaliser
   size_t sc_nst;  // floats per superchunk state slot of the forward plan
   const void* q;
@@ -136,7 +137,7 @@ struct BwdParams {
   float* dC0;
   float* dn0;
 };
-bool bwd_supported(int dtype, int dqk, int dv);
+bool bwd_supported(int dtype, int dqk, int dv, int nb);
 hipError_t launch_bwd(int dtype, const BwdParams& p, hipStream_t stream);
 
 }  // namespace mlstm
