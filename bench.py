@@ -19,9 +19,9 @@ with a fresh bf16 token per step; it reports achieved HBM GB/s.
 fused; xLSTM-v2 block-diagonal B=4 H=4 d=64 nb=2 T=65536, also with per-block
 denominators; the 7B prefill with an output gate, and with the scalar
 normaliser), the retention decode step on the RetNet shape, and the backward
-passes of the 7B prefill and of the RetNet workloads: tokens/s per call and
-its algorithmic bytes against HBM (``backward`` runs the two backward
-passes alone).
+passes of the 7B prefill, the RetNet and the xLSTM-v2 block-diagonal
+workloads: tokens/s per call and its algorithmic bytes against HBM
+(``backward`` runs the backward passes alone).
 
 ``roofline`` is measured live: HIP events recorded by the library right before
 and after its main kernel (mlstm_set_profile_events) give that kernel's
@@ -301,6 +301,30 @@ def bench_variants(torch, mlstm, workload, args, dev, only_backward=False):
     out.append(dict(workload="retnet_msr_T2048_backward", B=B, H=H, T=T, d_k=dk, d_v=dv, **r, bytes=byts,
                     flops=flops, tokens=B * T))
     del rsets, douts, ws
+
+    # block-diagonal backward on the xLSTM-v2 workload (B=4, H=4, d=64, nb=2, T=65536)
+    x = workload("xlstm2_blockdiag_T65536")
+    B, H, T, dqk = x.q.shape
+    dv = x.v.shape[-1]
+    nb = x.num_blocks
+    bsets = [x.to(dev), x.to(dev)]
+    dhs = [grad_output((B, H, T, dv), seed=7200 + i).to(dev) for i in range(len(bsets))]
+    ws = torch.empty(mlstm.lib().mlstm_chunkwise_bwd_workspace_bytes(B, H, T, dqk, dv, nb, 64, mlstm.BF16),
+                     dtype=torch.uint8, device=dev)
+
+    def call_bd(i):
+        g = bsets[i]
+        mlstm.chunkwise_bwd(g.q, g.k, g.v, g.i_pre, g.f_pre, dhs[i], g.o_pre, g.bias, workspace=ws,
+                            num_blocks=nb)
+
+    r = timed(call_bd, len(bsets), nb_steps, nb_steps)
+    byts, flops = backward_work(B, H, T, dqk, dv)
+    # block-diagonal: the six state-sized products are nb times smaller
+    byts -= B * H * (dqk * dv - dqk * dv // nb) * 4
+    flops -= B * H * T * 12 * (dqk * dv - dqk * dv // nb)
+    out.append(dict(workload="xlstm2_blockdiag_T65536_backward", B=B, H=H, T=T, d_qk=dqk, d_v=dv, num_blocks=nb,
+                    **r, bytes=byts, flops=flops, tokens=B * T))
+    del bsets, dhs, ws
     if only_backward:
         return out
 

@@ -843,6 +843,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 // ---------------------------------------------------------------- kernel 3
 // Thread = 4 consecutive entries of the backward state; chunks in reverse,
 // in windows of SW whose local states are all loaded before any is replaced.
+template <int SW>
 __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p, int DQK) {
   const int bh = blockIdx.y;
   const size_t NST = (size_t)DQK * p.DV + DQK;
@@ -852,7 +853,6 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p, int DQK) {
   const float* gg = p.ws_gg + (size_t)bh * p.NC * BL;
   const float* mn = p.ws_min + (size_t)bh * p.NC;
   float4 G = make_float4(0.f, 0.f, 0.f, 0.f);
-  constexpr int SW = 8;
   for (int c1 = p.NC - 1; c1 >= 0; c1 -= SW) {
     float4 u[SW];
     float dec[SW];
@@ -1123,14 +1123,22 @@ __global__ __launch_bounds__(64) void bwd_gate_kernel(BwdParams p) {
   (void)tg;
 }
 
-// d bias_h = sum over the batch and the chunks of the bias partials
-__global__ void bwd_bias_kernel(BwdParams p) {
-  for (int hd = threadIdx.x; hd < p.H; hd += blockDim.x) {
-    float a = 0.f;
-    for (int b = 0; b < p.B; ++b)
-      for (int c = 0; c < p.NC; ++c) a += p.ws_dbias[((size_t)b * p.H + hd) * p.NC + c];
-    p.dbias[hd] = a;
+// d bias_h = sum over the batch and the chunks of the bias partials: one
+// work-group per head, a strided sum per thread, then a tree over the group.
+__global__ __launch_bounds__(256) void bwd_bias_kernel(BwdParams p) {
+  __shared__ float sred[4];
+  const int hd = blockIdx.x, tid = threadIdx.x;
+  float a = 0.f;
+  const int n = p.B * p.NC;
+  for (int e = tid; e < n; e += 256) {
+    const int b = e / p.NC, c = e % p.NC;
+    a += p.ws_dbias[((size_t)b * p.H + hd) * p.NC + c];
   }
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) a += __shfl_xor(a, d, 64);
+  if ((tid & 63) == 0) sred[tid >> 6] = a;
+  __syncthreads();
+  if (tid == 0) p.dbias[hd] = sred[0] + sred[1] + sred[2] + sred[3];
 }
 
 template <typename T, int DQK, int NB = 1>
@@ -1145,12 +1153,18 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_scores_kernel<T, DQK, false, NB>), dim3(nch), dim3(256), 0, stream, p);
   hipLaunchKernelGGL((bwd_dq_kernel<T, DQK, NB>), dim3(nch * (DQK / 64)), dim3(256), 0, stream, p);
   const size_t NST = (size_t)DQK * p.DV + DQK;
-  hipLaunchKernelGGL(bwd_scan_kernel, dim3((unsigned)((NST / 4 + 255) / 256), BH), dim3(256), 0, stream, p, DQK);
+  // long sequences of small states leave few work-groups for a long chain:
+  // keep more chunks' loads in flight per step of it
+  const dim3 gs((unsigned)((NST / 4 + 255) / 256), BH);
+  if (p.NC >= 256)
+    hipLaunchKernelGGL(bwd_scan_kernel<32>, gs, dim3(256), 0, stream, p, DQK);
+  else
+    hipLaunchKernelGGL(bwd_scan_kernel<8>, gs, dim3(256), 0, stream, p, DQK);
   hipLaunchKernelGGL((bwd_dkv_kernel<T, DQK, NB>), dim3(nch * (DQK / 64 + p.DV / 64)), dim3(256), 0, stream, p);
   if (!p.ret) {  // retention has no gates or normaliser to differentiate
     hipLaunchKernelGGL(bwd_gate_total_kernel, dim3(nch), dim3(64), 0, stream, p, DQK / 64);
     hipLaunchKernelGGL((bwd_gate_kernel<T>), dim3(nch), dim3(64), 0, stream, p);
-    if (p.dbias) hipLaunchKernelGGL(bwd_bias_kernel, dim3(1), dim3(256), 0, stream, p);
+    if (p.dbias) hipLaunchKernelGGL(bwd_bias_kernel, dim3((unsigned)p.H), dim3(256), 0, stream, p);
   }
   return hipGetLastError();
 }
