@@ -124,7 +124,7 @@ int launch(const Plan& pl, mlstm::ChunkParams& p, void* workspace, size_t worksp
 // the backward's own arrays.
 struct BwdPlan {
   Plan fwd;
-  size_t off_cst, off_cmin, off_U, off_P, off_Pt, off_D, off_Dt, off_rden, off_dz, off_db, off_dbh, off_qdq, off_kdki,
+  size_t off_carry, off_segdec, nseg, off_cst, off_cmin, off_U, off_P, off_Pt, off_D, off_Dt, off_rden, off_dz, off_db, off_dbh, off_qdq, off_kdki,
       off_kdk, bytes;
 };
 
@@ -165,6 +165,13 @@ int plan_bwd(int B, int H, int T, int dqk, int dv, int nb, int chunk, int dt, Bw
   o += align256(BH * NCL * 4);
   bp->off_kdk = o;
   o += align256(BH * NCL * (dqk / 64) * 4);
+  // two-level backward scan for long sequences (256 chunks or more): segment
+  // totals / carries, one state per 32 chunks
+  bp->nseg = NC >= 256 ? (NC + 31) / 32 : 0;
+  bp->off_carry = o;
+  o += align256(BH * bp->nseg * ((size_t)dqk * dv + dqk) * 4);
+  bp->off_segdec = o;
+  o += align256(BH * bp->nseg * 4);
   bp->bytes = o;
   return MLSTM_OK;
 }
@@ -269,6 +276,9 @@ int mlstm_chunkwise_bwd(int B, int H, int T, int d_qk, int d_v, int num_blocks, 
   b.ws_qdq = reinterpret_cast<float*>(ws + bp.off_qdq);
   b.ws_kdki = reinterpret_cast<float*>(ws + bp.off_kdki);
   b.ws_kdk = reinterpret_cast<float*>(ws + bp.off_kdk);
+  b.NSEG = (int)bp.nseg;
+  b.ws_carry = bp.nseg ? reinterpret_cast<float*>(ws + bp.off_carry) : nullptr;
+  b.ws_segdec = bp.nseg ? reinterpret_cast<float*>(ws + bp.off_segdec) : nullptr;
   b.dq = dq;
   b.dk = dk;
   b.dv = dv;
@@ -368,6 +378,9 @@ int retention_chunkwise_bwd(int B, int H, int T, int d_k, int d_v, int chunk, ml
   b.ws_qdq = reinterpret_cast<float*>(ws + bp.off_qdq);
   b.ws_kdki = reinterpret_cast<float*>(ws + bp.off_kdki);
   b.ws_kdk = reinterpret_cast<float*>(ws + bp.off_kdk);
+  b.NSEG = (int)bp.nseg;
+  b.ws_carry = bp.nseg ? reinterpret_cast<float*>(ws + bp.off_carry) : nullptr;
+  b.ws_segdec = bp.nseg ? reinterpret_cast<float*>(ws + bp.off_segdec) : nullptr;
   b.dq = dq;
   b.dk = dk;
   b.dv = dv;

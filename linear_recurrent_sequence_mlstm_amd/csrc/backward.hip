@@ -843,6 +843,31 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 // ---------------------------------------------------------------- kernel 3
 // Thread = 4 consecutive entries of the backward state; chunks in reverse,
 // in windows of SW whose local states are all loaded before any is replaced.
+// dC0, dn0 from the backward state before the first chunk (entries e0 .. e0+3
+// of the flattened [S~ | n~] state, full layout); dC0 in the memory's block layout.
+__device__ __forceinline__ void store_init_grad(const BwdParams& p, int DQK, int bh, size_t e0, float4 G) {
+  const size_t CS = (size_t)DQK * p.DV, NST = CS + DQK;
+  const float g4[4] = {G.x, G.y, G.z, G.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const size_t e = e0 + i;
+    if (e < CS) {
+      if (p.dC0) {
+        if (p.NB == 1) {
+          p.dC0[(size_t)bh * CS + e] = g4[i];
+        } else {  // [nb][d_qk/nb][d_v/nb]; off-diagonal entries are zero
+          const int d = (int)(e / p.DV), cc = (int)(e % p.DV);
+          const int bq = DQK / p.NB, bv = p.DV / p.NB, b = d / bq;
+          if (cc / bv == b)
+            p.dC0[(size_t)bh * (CS / p.NB) + (size_t)b * bq * bv + (size_t)(d % bq) * bv + cc % bv] = g4[i];
+        }
+      }
+    } else if (e < NST) {
+      if (p.dn0) p.dn0[(size_t)bh * DQK + (e - CS)] = g4[i];
+    }
+  }
+}
+
 template <int SW>
 __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p, int DQK) {
   const int bh = blockIdx.y;
@@ -880,27 +905,100 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p, int DQK) {
       }
     }
   }
-  if (active) {
-    const size_t CS = (size_t)DQK * p.DV;
-    const float g4[4] = {G.x, G.y, G.z, G.w};
+  if (active) store_init_grad(p, DQK, bh, e0, G);
+}
+
+// Two-level form of the same scan for long sequences (many chunks, few
+// work-groups per chain): segments of SEG chunks run their local scans in
+// parallel (bwd_scan_local_kernel: every slot gets the segment-local
+// G_c, and the segment's local total goes to ws_carry), a short chain over
+// the segments turns the totals into the carry entering each segment's end
+// (bwd_scan_carry_kernel, which also writes dC0, dn0), and a second parallel
+// pass adds each carry, decayed to the chunk, to the segment's slots
+// (bwd_scan_apply_kernel).
+constexpr int SEG = 32;
+
+__device__ __forceinline__ float chunk_decay(const BwdParams& p, int bh, int c) {
+  const float mp = p.ws_min[(size_t)bh * p.NC + c];
+  return exp2_fast(mp - fmaxf(mp, p.ws_gg[(size_t)bh * p.NC * BL + (size_t)c * BL + BL - 1]));
+}
+
+__global__ __launch_bounds__(256) void bwd_scan_local_kernel(BwdParams p, int DQK) {
+  const int bh = blockIdx.y, sg = blockIdx.z;
+  const size_t NST = (size_t)DQK * p.DV + DQK;
+  const size_t e0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e0 >= NST) return;
+  float* base = p.ws_U + (size_t)bh * p.NC * NST;
+  const int cb = sg * SEG, ce = min(p.NC, cb + SEG);
+  float4 G = make_float4(0.f, 0.f, 0.f, 0.f);
+  float fs = 1.f;  // decay over the whole segment
+  for (int c = ce - 1; c >= cb; --c) {
+    const float4 u = *reinterpret_cast<const float4*>(base + (size_t)c * NST + e0);
+    *reinterpret_cast<float4*>(base + (size_t)c * NST + e0) = G;
+    const float f = c == p.NC - 1 ? 0.f : chunk_decay(p, bh, c);
+    fs *= f;
+    G.x = f * G.x + u.x;
+    G.y = f * G.y + u.y;
+    G.z = f * G.z + u.z;
+    G.w = f * G.w + u.w;
+  }
+  *reinterpret_cast<float4*>(p.ws_carry + ((size_t)bh * p.NSEG + sg) * NST + e0) = G;
+  if (e0 == 0) p.ws_segdec[(size_t)bh * p.NSEG + sg] = fs;
+}
+
+__global__ __launch_bounds__(256) void bwd_scan_carry_kernel(BwdParams p, int DQK) {
+  const int bh = blockIdx.y;
+  const size_t NST = (size_t)DQK * p.DV + DQK;
+  const size_t e0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e0 >= NST) return;
+  float4 G = make_float4(0.f, 0.f, 0.f, 0.f);  // entering the end of segment sg
+  constexpr int W = 8;  // segments whose totals load together
+  for (int s1 = p.NSEG - 1; s1 >= 0; s1 -= W) {
+    float4 tot[W];
+    float f[W];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t e = e0 + i;
-      if (e < CS) {
-        if (p.dC0) {
-          if (p.NB == 1) {
-            p.dC0[(size_t)bh * CS + e] = g4[i];
-          } else {  // [nb][d_qk/nb][d_v/nb]; off-diagonal entries are zero
-            const int d = (int)(e / p.DV), cc = (int)(e % p.DV);
-            const int bq = DQK / p.NB, bv = p.DV / p.NB, b = d / bq;
-            if (cc / bv == b)
-              p.dC0[(size_t)bh * (CS / p.NB) + (size_t)b * bq * bv + (size_t)(d % bq) * bv + cc % bv] = g4[i];
-          }
-        }
-      } else if (e < NST) {
-        if (p.dn0) p.dn0[(size_t)bh * DQK + (e - CS)] = g4[i];
+    for (int j = 0; j < W; ++j) {
+      const int sg = s1 - j;
+      tot[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      f[j] = 0.f;
+      if (sg >= 0) {
+        tot[j] = *reinterpret_cast<const float4*>(p.ws_carry + ((size_t)bh * p.NSEG + sg) * NST + e0);
+        f[j] = p.ws_segdec[(size_t)bh * p.NSEG + sg];
       }
     }
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      const int sg = s1 - j;
+      if (sg >= 0) {
+        *reinterpret_cast<float4*>(p.ws_carry + ((size_t)bh * p.NSEG + sg) * NST + e0) = G;
+        G.x = f[j] * G.x + tot[j].x;
+        G.y = f[j] * G.y + tot[j].y;
+        G.z = f[j] * G.z + tot[j].z;
+        G.w = f[j] * G.w + tot[j].w;
+      }
+    }
+  }
+  store_init_grad(p, DQK, bh, e0, G);
+}
+
+__global__ __launch_bounds__(256) void bwd_scan_apply_kernel(BwdParams p, int DQK) {
+  const int bh = blockIdx.y, sg = blockIdx.z;
+  const size_t NST = (size_t)DQK * p.DV + DQK;
+  const size_t e0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e0 >= NST || sg == p.NSEG - 1) return;  // nothing enters the last segment
+  float* base = p.ws_U + (size_t)bh * p.NC * NST;
+  const float4 C = *reinterpret_cast<const float4*>(p.ws_carry + ((size_t)bh * p.NSEG + sg) * NST + e0);
+  const int cb = sg * SEG, ce = min(p.NC, cb + SEG);
+  float r = 1.f;  // decay from the end of chunk c to the end of the segment
+  for (int c = ce - 1; c >= cb; --c) {
+    float4* slot = reinterpret_cast<float4*>(base + (size_t)c * NST + e0);
+    float4 g = *slot;
+    g.x += r * C.x;
+    g.y += r * C.y;
+    g.z += r * C.z;
+    g.w += r * C.w;
+    *slot = g;
+    r *= chunk_decay(p, bh, c);
   }
 }
 
@@ -1155,11 +1253,15 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   const size_t NST = (size_t)DQK * p.DV + DQK;
   // long sequences of small states leave few work-groups for a long chain:
   // keep more chunks' loads in flight per step of it
-  const dim3 gs((unsigned)((NST / 4 + 255) / 256), BH);
-  if (p.NC >= 256)
-    hipLaunchKernelGGL(bwd_scan_kernel<32>, gs, dim3(256), 0, stream, p, DQK);
-  else
-    hipLaunchKernelGGL(bwd_scan_kernel<8>, gs, dim3(256), 0, stream, p, DQK);
+  const unsigned ge = (unsigned)((NST / 4 + 255) / 256);
+  if (p.ws_carry && p.NSEG > 1) {  // two-level scan (long sequences)
+    const dim3 g3(ge, BH, (unsigned)p.NSEG);
+    hipLaunchKernelGGL(bwd_scan_local_kernel, g3, dim3(256), 0, stream, p, DQK);
+    hipLaunchKernelGGL(bwd_scan_carry_kernel, dim3(ge, BH), dim3(256), 0, stream, p, DQK);
+    hipLaunchKernelGGL(bwd_scan_apply_kernel, g3, dim3(256), 0, stream, p, DQK);
+  } else {
+    hipLaunchKernelGGL(bwd_scan_kernel<8>, dim3(ge, BH), dim3(256), 0, stream, p, DQK);
+  }
   hipLaunchKernelGGL((bwd_dkv_kernel<T, DQK, NB>), dim3(nch * (DQK / 64 + p.DV / 64)), dim3(256), 0, stream, p);
   if (!p.ret) {  // retention has no gates or normaliser to differentiate
     hipLaunchKernelGGL(bwd_gate_total_kernel, dim3(nch), dim3(64), 0, stream, p, DQK / 64);

@@ -242,3 +242,51 @@ def test_bwd_block_diagonal(gpu, monkeypatch, dtype, T, init, G):
         part[:, :, a:a + 16] = dh[:, :, a:a + 16]
         scale += np.abs(oracle.mlstm_bwd(*args, part, x.o_pre, x.bias, *sargs, num_blocks=nb)["dbias"])
     check(out, ref, TOL[dt], dbias_scale=scale)
+
+
+def near_floor(x, state, band=2e-2):
+    """[B,H,T] mask of tokens whose |n.q + bias| lies within a relative band of
+    the denominator floor 1 (by the oracle, stepping through the sequence):
+    there the gradient jumps, and a bf16 run may take the other branch."""
+    B, H, T, dqk = x.q.shape
+    dv = x.v.shape[-1]
+    q, k, v, ip, fp = (cpu(t) for t in (x.q, x.k, x.v, x.i_pre, x.f_pre))
+    op = cpu(x.o_pre)
+    bs = cpu(x.bias)
+    if state is None:
+        C, n, m = np.zeros((B, H, 1, dqk, dv)), np.zeros((B, H, dqk)), np.zeros((B, H))
+    else:
+        C, n, m = (t.double().numpy().copy() for t in state)
+    mask = np.zeros((B, H, T), dtype=bool)
+    for t in range(T):
+        oracle.mlstm_step(q[:, :, t], k[:, :, t], v[:, :, t], ip[:, :, t], fp[:, :, t], C, n, m,
+                          None if op is None else op[:, :, t], bs)
+        z = np.einsum("bhd,bhd->bh", n, q[:, :, t]) * np.exp(m)
+        if bs is not None:
+            z = z + bs[None, :]
+        mask[:, :, t] = np.abs(np.abs(z) - 1) < band
+    return mask
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_long_sequence_two_level_scan(gpu, dtype):
+    """257 chunks (T = 16421, ragged): the backward chunk scan runs in two
+    levels (segments of 32 chunks, the last one a single chunk), with an
+    initial state whose gradient comes out of the segment carries.  dh is
+    zero at tokens within 2% of the denominator floor, as in the full 7B
+    test (the gradient jumps there)."""
+    B, H, T = 1, 2, 256 * 64 + 37
+    x = mlstm_inputs(B, H, T, 64, 64, seed=3400, dtype=dtype, k_scale=1 / 8, f_mix=True, with_o=True,
+                     bias="uniform")
+    st = _state(B, H, 64, 64, 3402)
+    mask = near_floor(x, st)
+    dh = grad_output((B, H, T, 64), seed=3401, dtype=dtype)
+    dh[torch.from_numpy(mask)] = 0
+    print("tokens near the floor (dh zeroed): %d of %d" % (int(mask.sum()), mask.size), flush=True)
+    g = x.to(gpu)
+    out = mlstm.chunkwise_bwd(g.q, g.k, g.v, g.i_pre, g.f_pre, dh.to(gpu), g.o_pre, g.bias,
+                              state=tuple(t.to(gpu) for t in st))
+    torch.cuda.synchronize()
+    ref = oracle.mlstm_bwd(x.q, x.k, x.v, x.i_pre, x.f_pre, dh, x.o_pre, x.bias, st[0].reshape(B, H, 64, 64),
+                           st[1], st[2])
+    check(out, ref, TOL[x.q.dtype])
