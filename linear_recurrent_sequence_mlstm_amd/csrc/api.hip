@@ -124,7 +124,7 @@ int launch(const Plan& pl, mlstm::ChunkParams& p, void* workspace, size_t worksp
 // the backward's own arrays.
 struct BwdPlan {
   Plan fwd;
-  size_t off_carry, off_segdec, nseg, off_cst, off_cmin, off_U, off_P, off_Pt, off_D, off_Dt, off_rden, off_dz, off_db, off_dbh, off_qdq, off_kdki,
+  size_t off_carry, off_segdec, nseg, off_cst, off_cmin, off_U, off_Pt, off_Dt, off_rden, off_dz, off_db, off_dbh, off_qdq, off_kdki,
       off_kdk, bytes;
 };
 
@@ -146,11 +146,9 @@ int plan_bwd(int B, int H, int T, int dqk, int dv, int nb, int chunk, int dt, Bw
   bp->off_U = o;
   o += align256(BH * NC * ((size_t)dqk * dv + dqk) * 4);
   const size_t tile = align256(BH * NC * nb * 64 * 64 * es);  // one 64 x 64 per chunk and memory block
-  bp->off_P = o;
-  bp->off_Pt = o + tile;
-  bp->off_D = o + 2 * tile;
-  bp->off_Dt = o + 3 * tile;
-  o += 4 * tile;
+  bp->off_Pt = o;
+  bp->off_Dt = o + tile;
+  o += 2 * tile;
   bp->off_rden = o;
   o += align256(BH * NCL * 4);
   bp->off_dz = o;
@@ -264,9 +262,7 @@ int mlstm_chunkwise_bwd(int B, int H, int T, int d_qk, int d_v, int num_blocks, 
   b.ws_ga = p.ws_ga;
   b.ws_gg = p.ws_gg;
   b.ws_gb = p.ws_gb;
-  b.wsP = ws + bp.off_P;
   b.wsPt = ws + bp.off_Pt;
-  b.wsD = ws + bp.off_D;
   b.wsDt = ws + bp.off_Dt;
   b.ws_rden = reinterpret_cast<float*>(ws + bp.off_rden);
   b.ws_dz = reinterpret_cast<float*>(ws + bp.off_dz);
@@ -366,9 +362,7 @@ int retention_chunkwise_bwd(int B, int H, int T, int d_k, int d_v, int chunk, ml
   b.ws_ga = p.ws_ga;
   b.ws_gg = p.ws_gg;
   b.ws_gb = p.ws_gb;
-  b.wsP = ws + bp.off_P;
   b.wsPt = ws + bp.off_Pt;
-  b.wsD = ws + bp.off_D;
   b.wsDt = ws + bp.off_Dt;
   b.ws_rden = reinterpret_cast<float*>(ws + bp.off_rden);
   b.ws_dz = reinterpret_cast<float*>(ws + bp.off_dz);

@@ -446,7 +446,6 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
 
   // P = E . S (kept in fp32 registers), its row sums; P and P^T to the
   // workspace, P to LDS for the readout
-  T* Pw = static_cast<T*>(p.wsP) + ((size_t)bh * p.NC + c) * NB * BL * BL;
   T* Ptw = static_cast<T*>(p.wsPt) + ((size_t)bh * p.NC + c) * NB * BL * BL;
   float rs[4] = {0.f, 0.f, 0.f, 0.f};  // the normaliser sums over the whole head
 #pragma unroll
@@ -460,7 +459,6 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
       for (int b = 0; b < NB; ++b) {
         accP[b][n][i] *= e;
         rs[i] += accP[b][n][i];
-        Pw[b * BL * BL + j * BL + l] = from_f32<T>(accP[b][n][i]);
         sP[b][j * LD + l] = from_f32<T>(accP[b][n][i]);
       }
     }
@@ -668,8 +666,8 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
     if (tid == 0) p.ws_dbias[(size_t)bh * p.NC + c] = bsum;
   }
 
-  // D' = E . (dN V^T + dz~) per memory block, and its transpose
-  T* Dw = static_cast<T*>(p.wsD) + ((size_t)bh * p.NC + c) * NB * BL * BL;
+  // D' = E . (dN V^T + dz~) per memory block, stored transposed (dq and dk
+  // both read D'^T: dq with transposing LDS reads)
   T* Dtw = static_cast<T*>(p.wsDt) + ((size_t)bh * p.NC + c) * NB * BL * BL;
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
@@ -682,7 +680,6 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
         const int j = 16 * w + 4 * lg + i;
         const float e = l <= j ? exp2_fast(sa[l] - sM[j]) : 0.f;
         dv4[i] = e * (accD[b][n][i] + sdz[j]);
-        Dw[b * BL * BL + j * BL + l] = from_f32<T>(dv4[i]);
       }
       store4f(Dtw + b * BL * BL + l * BL + 16 * w + 4 * lg, dv4[0], dv4[1], dv4[2], dv4[3]);
     }
@@ -699,7 +696,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   constexpr int NDT = DQK / 64;
   // alpha_j is per row of dq and per contraction index of U, so one tile of
   // alpha dN serves both: the inter part of dq is alpha_j sum_c dN_jc S~_dc.
-  __shared__ __attribute__((aligned(16))) T sA[BL * LD];  // D', then alpha dN slices [j][.]
+  __shared__ __attribute__((aligned(16))) T sA[BL * LD];  // D'^T [l][j], then alpha dN slices [j][c]
   __shared__ __attribute__((aligned(16))) T sB[BL * LD];  // K tile, then S~ slices  [l][d], [d][c]
   __shared__ __attribute__((aligned(16))) T sQ[BL * LD];  // Q of the tile           [j][d]
   // bf16 lo parts, x - bf16(x), of S~ and alpha dN: dq's S~ dn~ and the local
@@ -733,7 +730,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     float x[16], y[16], d[16];
     load16f<T>(rq, ((unsigned)(t0 + r) * DQK + dt * 64 + c0) * ES, x);
     load16f<T>(rk, ((unsigned)(t0 + r) * DQK + dt * 64 + c0) * ES, y);
-    const T* Dw = static_cast<const T*>(p.wsD) + ((size_t)bh * p.NC + c) * NB * BL * BL;
+    const T* Dw = static_cast<const T*>(p.wsDt) + ((size_t)bh * p.NC + c) * NB * BL * BL;  // D'^T [l][j]
 #pragma unroll
     for (int e = 0; e < 16; ++e) d[e] = to_f32(Dw[r * BL + c0 + e]);
     st_row16<T>(sQ, r, c0, x);
@@ -749,11 +746,11 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   f32x4 acc[4], accx[4];
   zero_acc(acc);
   zero_acc(accx);
-  mma64x<T, false, true>(acc, sA, LD, sB, LD, w, lane);  // sum_l D'_jl k_l
+  mma64x<T, true, true>(acc, sA, LD, sB, LD, w, lane);  // sum_l D'_jl k_l (D' held transposed)
   if constexpr (NB > 1) {  // feature column d takes the D' of its block
     f32x4 t1[4];
     zero_acc(t1);
-    mma64x<T, false, true>(t1, sA2, LD, sB, LD, w, lane);
+    mma64x<T, true, true>(t1, sA2, LD, sB, LD, w, lane);
 #pragma unroll
     for (int n = 0; n < 4; ++n)
       if (col_block<NB>(n) == 1) acc[n] = t1[n];

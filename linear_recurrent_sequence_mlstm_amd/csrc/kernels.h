@@ -115,10 +115,8 @@ struct BwdParams {
   const float* ws_ga;     // [B*H][NC*64] a_j, prefix maxima g_j, b_j (log2)
   const float* ws_gg;
   const float* ws_gb;
-  void* wsP;   // [B*H][NC][64][64] E.(Q K^T), and transposed
-  void* wsPt;
-  void* wsD;   // [B*H][NC][64][64] D', and transposed
-  void* wsDt;
+  void* wsPt;  // [B*H][NC][NB][64][64] (E.(Q_b K_b^T))^T
+  void* wsDt;  // [B*H][NC][NB][64][64] D'_b^T
   float* ws_rden;     // [B*H][NC*64] 1 / den~
   float* ws_dz;       // [B*H][NC*64] dz~
   float* ws_dbias;    // [B*H][NC] bias partials of the chunks
