@@ -140,9 +140,20 @@ def retention_workspace_bytes(B, H, T, dk, dv, chunk=64, dtype=torch.bfloat16) -
 
 
 def _workspace(nbytes, device, workspace):
-    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
-        return workspace
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    """The caller's workspace (a contiguous tensor on `device`, any dtype, at
+    least nbytes long) or a fresh one; returns (tensor, its size in bytes)."""
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor):
+            raise TypeError("workspace must be a torch.Tensor")
+        if workspace.device != device:
+            raise ValueError("workspace is on %s, expected %s" % (workspace.device, device))
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        size = workspace.numel() * workspace.element_size()
+        if size >= nbytes:
+            return workspace, size
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    return ws, ws.numel()
 
 
 # normaliser readings of the _ex entry points (MLSTM_NORM_* in mlstm.h)
@@ -195,11 +206,11 @@ def chunkwise_fwd(q, k, v, i_pre, f_pre, o_pre=None, bias=None, state=None, num_
     if nbytes == 0:
         _check(L.mlstm_chunkwise_fwd(B, H, T, dqk, dv, nb, chunk, _DT[dt], *([None] * 13),
                                      None, None, 0, None), "mlstm_chunkwise_fwd")
-    ws = _workspace(nbytes, dev, workspace)
+    ws, wsb = _workspace(nbytes, dev, workspace)
     rc = L.mlstm_chunkwise_fwd_ex(B, H, T, dqk, dv, nb, chunk, _DT[dt], mode, _ptr(q), _ptr(k), _ptr(v),
                                   _ptr(i_pre), _ptr(f_pre), _ptr(o_pre), _ptr(bias), _ptr(C0), _ptr(n0),
                                   _ptr(m0), _ptr(Co), _ptr(no), _ptr(mo), _ptr(h), _ptr(ws),
-                                  ws.numel(), _stream(dev))
+                                  wsb, _stream(dev))
     _check(rc, "mlstm_chunkwise_fwd_ex")
     return h, ((Co, no, mo) if return_state else None)
 
@@ -262,7 +273,7 @@ def retention_chunkwise_fwd(q, k, v, gamma=None, S0=None, chunk=64, return_state
     if nbytes == 0:
         _check(L.retention_chunkwise_fwd(B, H, T, dk, dv, chunk, _DT[dt], *([None] * 7), None, 0, None),
                "retention_chunkwise_fwd")
-    ws = _workspace(nbytes, dev, workspace)
+    ws, wsb = _workspace(nbytes, dev, workspace)
     if groupnorm is not None:
         gw, gb, eps = groupnorm
         _need(gw, "gn_weight", (H * dv,), torch.float32, dev)
@@ -270,12 +281,12 @@ def retention_chunkwise_fwd(q, k, v, gamma=None, S0=None, chunk=64, return_state
         rc = L.retention_chunkwise_groupnorm_fwd(B, H, T, dk, dv, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v),
                                                  _ptr(gamma), _ptr(S0), _ptr(S_out if return_state else None),
                                                  _ptr(gw), _ptr(gb), float(eps), _ptr(out), _ptr(ws),
-                                                 ws.numel(), _stream(dev))
+                                                 wsb, _stream(dev))
         _check(rc, "retention_chunkwise_groupnorm_fwd")
         return out, (S_out if return_state else None)
     rc = L.retention_chunkwise_fwd(B, H, T, dk, dv, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v),
                                    _ptr(gamma), _ptr(S0), _ptr(S_out if return_state else None),
-                                   _ptr(out), _ptr(ws), ws.numel(), _stream(dev))
+                                   _ptr(out), _ptr(ws), wsb, _stream(dev))
     _check(rc, "retention_chunkwise_fwd")
     return out, (S_out if return_state else None)
 
@@ -340,12 +351,12 @@ def chunkwise_bwd(q, k, v, i_pre, f_pre, dh, o_pre=None, bias=None, state=None, 
     if nbytes == 0:
         _check(L.mlstm_chunkwise_bwd(B, H, T, dqk, dv, nb, chunk, _DT[dt], *([None] * 20), None, 0, None),
                "mlstm_chunkwise_bwd")
-    ws = _workspace(nbytes, dev, workspace)
+    ws, wsb = _workspace(nbytes, dev, workspace)
     rc = L.mlstm_chunkwise_bwd(B, H, T, dqk, dv, nb, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre),
                                _ptr(f_pre), _ptr(o_pre), _ptr(bias), _ptr(C0), _ptr(n0), _ptr(m0),
                                _ptr(dh), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["di"]),
                                _ptr(out["df"]), _ptr(out["do"]), _ptr(out["dbias"]), _ptr(out["dC0"]),
-                               _ptr(out["dn0"]), _ptr(ws), ws.numel(), _stream(dev))
+                               _ptr(out["dn0"]), _ptr(ws), wsb, _stream(dev))
     _check(rc, "mlstm_chunkwise_bwd")
     return out
 
@@ -372,9 +383,9 @@ def retention_chunkwise_bwd(q, k, v, dout, gamma=None, S0=None, chunk=64, state_
     if nbytes == 0:
         _check(L.retention_chunkwise_bwd(B, H, T, dk, dv, chunk, _DT[dt], *([None] * 10), None, 0, None),
                "retention_chunkwise_bwd")
-    ws = _workspace(nbytes, dev, workspace)
+    ws, wsb = _workspace(nbytes, dev, workspace)
     rc = L.retention_chunkwise_bwd(B, H, T, dk, dv, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
                                    _ptr(S0), _ptr(dout), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
-                                   _ptr(out["dS0"]), _ptr(ws), ws.numel(), _stream(dev))
+                                   _ptr(out["dS0"]), _ptr(ws), wsb, _stream(dev))
     _check(rc, "retention_chunkwise_bwd")
     return out

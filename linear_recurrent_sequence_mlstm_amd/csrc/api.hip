@@ -56,8 +56,13 @@ int plan_chunkwise(int B, int H, int T, int dqk, int dv, int nb, int chunk, int 
                 dqk, dv, nb);
   if (dqk % nb || dv % nb)
     return fail(MLSTM_E_SHAPE, "d_qk=%d and d_v=%d must be multiples of num_blocks=%d", dqk, dv, nb);
-  if ((long long)T * (dqk > dv ? dqk : dv) >= (1LL << 31))
-    return fail(MLSTM_E_SHAPE, "T * d too large (%d x %d)", T, dqk > dv ? dqk : dv);
+  // The kernels address one (batch, head) of q, k, v, h, o_pre, dh and the
+  // gradients through buffer resources with 32-bit byte offsets (and a signed
+  // 32-bit scalar part): that slice must stay below 2^31 bytes.
+  const long long es = dt == MLSTM_BF16 ? 2 : 4;
+  if ((long long)T * (dqk > dv ? dqk : dv) * es >= (1LL << 31))
+    return fail(MLSTM_E_SHAPE, "one (batch, head) of T x d = %d x %d %s elements exceeds 2^31 bytes", T,
+                dqk > dv ? dqk : dv, dt == MLSTM_BF16 ? "bf16" : "fp32");
   if ((long long)B * H >= (1LL << 24)) return fail(MLSTM_E_SHAPE, "B * H too large");
   if (chunk != 16 && chunk != 32 && chunk != 64)
     return fail(MLSTM_E_SHAPE, "chunk must be 16, 32 or 64 (got %d)", chunk);

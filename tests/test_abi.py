@@ -114,3 +114,36 @@ def test_retention_validation():
     assert L.retention_chunkwise_fwd(1, 1, 10, 256, 64, 64, 1, *p, BOGUS, BOGUS, 1 << 30, None) == E_UNSUPPORTED
     assert L.retention_chunkwise_fwd(1, 1, 10, 64, 64, 64, 1, None, BOGUS, BOGUS, None, None, None,
                                      BOGUS, BOGUS, 1 << 30, None) == E_NULL
+
+
+@pytest.mark.parametrize("dt,T,d", [(0, 1 << 24, 64), (1, 1 << 24, 64), (1, 1 << 22, 512), (0, (1 << 23) + 5, 64)])
+def test_slice_bytes_limit(dt, T, d):
+    """One (batch, head) of a tensor is addressed with 32-bit byte offsets: a
+    slice of 2^31 bytes or more is rejected (forward, workspace queries and
+    backward) before anything runs, instead of wrapping."""
+    L = _lib.lib()
+    assert _fwd(T=T, dqk=64, dv=d, dt=dt) == E_SHAPE
+    assert "2^31" in _lib.last_error()
+    assert L.mlstm_chunkwise_workspace_bytes(1, 2, T, 64, d, 1, 64, dt) == 0
+    assert L.mlstm_chunkwise_bwd_workspace_bytes(1, 2, T, 64, d, 1, 64, dt) == 0
+    assert L.retention_chunkwise_workspace_bytes(1, 2, T, 64, d, 64, dt) == 0
+    # just below the limit the same shape family plans normally
+    Tok = ((1 << 31) // (d * (2 if dt else 4))) - 64
+    assert L.mlstm_chunkwise_workspace_bytes(1, 2, Tok, 64, d, 1, 64, dt) > 0
+
+
+def test_workspace_argument_checks():
+    """A caller's workspace must be a contiguous tensor on the call's device;
+    its size counts in bytes whatever its dtype (no GPU needed: the checks
+    raise before anything is allocated)."""
+    import torch
+    dev = torch.device("cuda:0")
+    with pytest.raises(ValueError, match="workspace is on"):
+        _lib._workspace(1024, dev, torch.empty(4096, dtype=torch.uint8))
+    with pytest.raises(TypeError):
+        _lib._workspace(1024, dev, object())
+    cpu = torch.device("cpu")
+    ws, n = _lib._workspace(1024, cpu, torch.empty(512, dtype=torch.float32))
+    assert n == 2048 and ws.dtype == torch.float32
+    with pytest.raises(ValueError, match="contiguous"):
+        _lib._workspace(16, cpu, torch.empty(64, 2)[:, 0])
