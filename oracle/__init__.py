@@ -21,8 +21,10 @@ Parity status of each function (what pins it is listed in the tests):
   groupnorm        pinned (torch's group_norm in fp64; zero mean and
                    var/(var+eps) variance of every normalised row)
   mlstm_bwd        pinned (central finite differences of mlstm_fwd for every
-                   input; torch autograd through an unstabilised fp64
-                   recurrence written in the test)
+                   input, also with a loss on the final state; torch autograd
+                   through an unstabilised fp64 recurrence written in the
+                   test; a split run chained through the state gradients;
+                   the per-token bias terms against their closed form)
   retention_bwd    pinned (central finite differences of retention_fwd;
                    torch autograd through the decay-matrix parallel form)
 """
@@ -67,7 +69,7 @@ def _load(path: str | None = None):
     lib.oracle_mlstm_step.restype = i
     lib.oracle_retention_fwd.argtypes = [i, i, i, i, i] + [P] * 7
     lib.oracle_retention_fwd.restype = i
-    lib.oracle_mlstm_bwd.argtypes = [i, i, i, i, i, i] + [P] * 20
+    lib.oracle_mlstm_bwd.argtypes = [i, i, i, i, i, i] + [P] * 23
     lib.oracle_mlstm_bwd.restype = i
     lib.oracle_retention_bwd.argtypes = [i, i, i, i, i] + [P] * 10
     lib.oracle_retention_bwd.restype = i
@@ -199,15 +201,17 @@ def retention_fwd(q, k, v, gamma=None, S0=None, lib=None):
 
 
 def mlstm_bwd(q, k, v, i_pre, f_pre, dh, o_pre=None, bias=None, C0=None, n0=None,
-              m0=None, lib=None, num_blocks=1):
+              m0=None, lib=None, num_blocks=1, dCT=None, dnT=None):
     """Gradients of sum(dh * h) for the mLSTM sequence form (vector
     normaliser; num_blocks memory blocks), h = mlstm_fwd(q, k, v, ...)[0].  Shapes as
-    in mlstm_fwd; dh [B,H,T,dv].  Returns a dict of float64 arrays: dq, dk,
-    dv, di (i_pre), df (f_pre), do (o_pre; None without o_pre), dbias [H],
-    dC0 [B,H,dqk,dv] and dn0 [B,H,dqk] (gradients of the stabilised initial
-    state, zero-state runs included)."""
+    in mlstm_fwd; dh [B,H,T,dv].  dCT (shaped as C0), dnT [B,H,dqk]: optional
+    gradient arriving at the stabilised final state (S~_T, n~_T at fixed m_T).
+    Returns a dict of float64 arrays: dq, dk, dv, di (i_pre), df (f_pre), do
+    (o_pre; None without o_pre), dbias [H], dbias_t [B,H,T] (the per-token
+    terms of dbias), dC0 [B,H,dqk,dv] and dn0 [B,H,dqk] (gradients of the
+    stabilised initial state, zero-state runs included)."""
     q, k, v, ip, fp, g = map(_f64, (q, k, v, i_pre, f_pre, dh))
-    op, bs, c0, nn0, mm0 = map(_f64, (o_pre, bias, C0, n0, m0))
+    op, bs, c0, nn0, mm0, dct, dnt = map(_f64, (o_pre, bias, C0, n0, m0, dCT, dnT))
     B, H, T, dqk = q.shape
     dv = v.shape[-1]
     assert k.shape == q.shape and v.shape == (B, H, T, dv) and g.shape == v.shape
@@ -215,16 +219,20 @@ def mlstm_bwd(q, k, v, i_pre, f_pre, dh, o_pre=None, bias=None, C0=None, n0=None
     cshape = (B, H, dqk, dv) if nb == 1 else (B, H, nb, dqk // nb, dv // nb)
     if c0 is not None:
         c0 = np.ascontiguousarray(c0.reshape(cshape))
+    if dct is not None:
+        dct = np.ascontiguousarray(dct.reshape(cshape))
+    if dnt is not None:
+        assert dnt.shape == (B, H, dqk)
     out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v),
                di=np.zeros((B, H, T)), df=np.zeros((B, H, T)),
                do=np.zeros_like(v) if op is not None else None,
-               dbias=np.zeros(H), dC0=np.zeros(cshape),
+               dbias=np.zeros(H), dbias_t=np.zeros((B, H, T)), dC0=np.zeros(cshape),
                dn0=np.zeros((B, H, dqk)))
     rc = (lib or _load()).oracle_mlstm_bwd(
         B, H, T, dqk, dv, nb, _ptr(q), _ptr(k), _ptr(v), _ptr(ip), _ptr(fp), _ptr(op),
-        _ptr(bs), _ptr(c0), _ptr(nn0), _ptr(mm0), _ptr(g), _ptr(out["dq"]),
+        _ptr(bs), _ptr(c0), _ptr(nn0), _ptr(mm0), _ptr(g), _ptr(dct), _ptr(dnt), _ptr(out["dq"]),
         _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["di"]), _ptr(out["df"]),
-        _ptr(out["do"]), _ptr(out["dbias"]), _ptr(out["dC0"]), _ptr(out["dn0"]))
+        _ptr(out["do"]), _ptr(out["dbias"]), _ptr(out["dbias_t"]), _ptr(out["dC0"]), _ptr(out["dn0"]))
     if rc != 0:
         raise ValueError("oracle_mlstm_bwd failed with %d" % rc)
     return out

@@ -295,17 +295,28 @@ int oracle_retention_fwd(int B, int H, int T, int dk, int dv, const double* q,
  * XLSTMv2" page, "Key Improvements" item 1) the state and G are block-diagonal
  * [nb][d_qk/nb][d_v/nb]: every product above runs per block, while n~, g and
  * the denominator stay per head.
+ * Gradient flowing into the final state (optional): dCT [B,H,nb,d_qk/nb,d_v/nb]
+ * and dnT [B,H,d_qk] are the gradients of the loss with respect to the
+ * stabilised final state S~_T, n~_T at fixed m_T, i.e. e^{m_T} times the
+ * gradients with respect to the true final C_T, n_T.  They start the reverse
+ * sweep as G~ and g~ (NULL: zero).  This is the reading under which the
+ * downstream loss depends on the final state only through the true state (as
+ * a continuation of the recurrence does, its outputs being independent of
+ * the stabiliser); no derivative of the stabiliser itself appears.  A second
+ * call's dC0, dn0 (for the same m) are exactly the first call's dCT, dnT.
  * dh [B,H,T,d_v] in; outputs (any may be NULL): dq, dk [B,H,T,d_qk]; dv, do_pre
- * [B,H,T,d_v]; di, df [B,H,T]; dbias [H] (summed over B); dC0
+ * [B,H,T,d_v]; di, df [B,H,T]; dbias [H] (summed over B); dbias_t [B,H,T]
+ * (the per-token terms dz_t of that sum, in true units); dC0
  * [B,H,nb,d_qk/nb,d_v/nb]; dn0 [B,H,d_qk].  Returns 0, -1 for bad sizes, -2 when out of memory.
  */
 int oracle_mlstm_bwd(int B, int H, int T, int dqk, int dv, int nb, const double* q,
                      const double* k, const double* v, const double* i_pre,
                      const double* f_pre, const double* o_pre, const double* bias,
                      const double* C0, const double* n0, const double* m0,
-                     const double* dh, double* dq, double* dk, double* dvo,
+                     const double* dh, const double* dCT, const double* dnT,
+                     double* dq, double* dk, double* dvo,
                      double* di, double* df, double* do_pre, double* dbias,
-                     double* dC0, double* dn0) {
+                     double* dbias_t, double* dC0, double* dn0) {
   if (B < 0 || H < 0 || T < 0 || dqk <= 0 || dv <= 0 || nb <= 0) return -1;
   if (dqk % nb || dv % nb) return -1;
   const int dqkb = dqk / nb, dvb = dv / nb;
@@ -336,6 +347,9 @@ int oracle_mlstm_bwd(int B, int H, int T, int dqk, int dv, int nb, const double*
       bad = 1;
       continue;
     }
+    /* the gradient arriving at the final state */
+    if (dCT) memcpy(G, dCT + bh * csz, csz * sizeof(double));
+    if (dnT) memcpy(g, dnT + bh * dqk, (size_t)dqk * sizeof(double));
     /* forward sweep: the state at every segment start */
     double* s0 = ckpt;
     if (C0) memcpy(s0, C0 + bh * csz, csz * sizeof(double));
@@ -397,6 +411,7 @@ int oracle_mlstm_bwd(int B, int H, int T, int dqk, int dv, int nb, const double*
         }
         const double dz = fabs(zt) > fl ? -sdy / den * (zt > 0 ? 1.0 : -1.0) : 0.0;
         dbias_acc += dz * fl;
+        if (dbias_t) dbias_t[tok] = dz * fl;
         /* dq_t = S~_t dn + n~_t dz (the matrix per block, n~ over the head) */
         if (dq)
           for (int d = 0; d < dqk; ++d) {

@@ -191,3 +191,137 @@ def test_bwd_pin_finite_differences_block_diagonal():
             x[idx] = keep
             fd[idx] = (lp - lm) / (2 * eps)
         assert _relerr(g[gname], fd) < 1e-6, name
+
+
+def _fwd_state(a, nb=1):
+    """h and the final stabilised state (C, n, m) of the forward oracle."""
+    B, H, T, dqk = a["q"].shape
+    dv = a["v"].shape[-1]
+    C0 = None if a["C0"] is None else a["C0"].reshape(B, H, nb, dqk // nb, dv // nb)
+    return oracle.mlstm_fwd(a["q"], a["k"], a["v"], a["i_pre"], a["f_pre"], a["o_pre"], a["bias"], C0,
+                            a["n0"], a["m0"], num_blocks=nb)
+
+
+def test_bwd_pin_final_state_gradient_finite_differences():
+    """A gradient arriving at the final state: the loss
+    L = sum dh * h + e^{m_T - m_ref} (<dC_T, S~_T> + <dn_T, n~_T>)
+    is the loss on the true final state (C_T = S~_T e^{m_T}) scaled by the
+    constant e^{-m_ref}, a smooth function of the inputs however the
+    stabiliser moves; its central finite differences pin every gradient of
+    oracle.mlstm_bwd(..., dCT, dnT)."""
+    a, dh = _case(41, 1, 2, 9, 4, 3, kscale=3.0)
+    rng = np.random.default_rng(42)
+    B, H, dqk, dv = 1, 2, 4, 3
+    dCT = rng.standard_normal((B, H, dqk, dv))
+    dnT = rng.standard_normal((B, H, dqk))
+    _, _, _, m_ref = _fwd_state(a)
+    m_ref = m_ref.copy()
+
+    def loss(a):
+        h, C, n, m = _fwd_state(a)
+        s = np.exp(m - m_ref)
+        return (np.sum(dh * h) + np.sum(s[..., None, None] * dCT * C.reshape(B, H, dqk, dv))
+                + np.sum(s[..., None] * dnT * n))
+
+    g = oracle.mlstm_bwd(dh=dh, dCT=dCT, dnT=dnT, **a)
+    g0 = oracle.mlstm_bwd(dh=dh, **a)
+    assert _relerr(g["dk"], g0["dk"]) > 1e-3  # the final-state term is not negligible here
+    eps = 1e-6
+    for name, gname in GRAD_OF.items():
+        x = a[name]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            lp = loss(a)
+            x[idx] = keep - eps
+            lm = loss(a)
+            x[idx] = keep
+            fd[idx] = (lp - lm) / (2 * eps)
+        assert _relerr(g[gname], fd) < 1e-6, name
+
+
+@pytest.mark.parametrize("T,init", [(1, True), (23, False), (50, True)])
+def test_bwd_pin_final_state_gradient_autograd(T, init):
+    """The same loss through torch autograd on the unstabilised recurrence of
+    this file: the final-state term is <dC_T e^{-m_T}, C_T> + <dn_T e^{-m_T}, n_T>
+    in true units (m_T from the forward oracle, a constant)."""
+    a, dh = _case(200 + T, 2, 2, T, 8, 6, init=init, kscale=2.0)
+    rng = np.random.default_rng(300 + T)
+    dCT = rng.standard_normal((2, 2, 8, 6))
+    dnT = rng.standard_normal((2, 2, 8))
+    g = oracle.mlstm_bwd(dh=dh, dCT=dCT, dnT=dnT, **a)
+    _, _, _, mT = _fwd_state(a)
+    t = {n: (None if x is None else torch.tensor(x, requires_grad=True)) for n, x in a.items()}
+    h, _, CT, nT = _torch_h_state(t)
+    s = torch.from_numpy(np.exp(-mT))
+    L = ((h * torch.from_numpy(dh)).sum() + (s[..., None, None] * torch.from_numpy(dCT) * CT).sum()
+         + (s[..., None] * torch.from_numpy(dnT) * nT).sum())
+    L.backward()
+    for name, gname in GRAD_OF.items():
+        if t[name] is None or name == "m0":
+            continue
+        assert _relerr(g[gname], t[name].grad.numpy()) < 1e-10, (name, T)
+
+
+def _torch_h_state(t):
+    """_torch_h that also returns the final true state (C_T, n_T)."""
+    q, k, v, ip, fp = t["q"], t["k"], t["v"], t["i_pre"], t["f_pre"]
+    B, H, T, dqk = q.shape
+    dv = v.shape[-1]
+    if t["C0"] is not None:
+        C = t["C0"] * torch.exp(t["m0"])[..., None, None]
+        n = t["n0"] * torch.exp(t["m0"])[..., None]
+    else:
+        C = torch.zeros(B, H, dqk, dv, dtype=torch.float64)
+        n = torch.zeros(B, H, dqk, dtype=torch.float64)
+    bias = t["bias"] if t["bias"] is not None else torch.zeros(H, dtype=torch.float64)
+    hs = []
+    for s in range(T):
+        f = torch.sigmoid(fp[:, :, s])[..., None]
+        i = torch.exp(ip[:, :, s])[..., None]
+        C = f[..., None] * C + (i * k[:, :, s])[..., :, None] * v[:, :, s][..., None, :]
+        n = f * n + i * k[:, :, s]
+        num = (C * q[:, :, s][..., :, None]).sum(-2)
+        z = (n * q[:, :, s]).sum(-1) + bias
+        den = torch.clamp(z.abs(), min=1.0)
+        o = torch.sigmoid(t["o_pre"][:, :, s]) if t["o_pre"] is not None else 1.0
+        hs.append(o * num / den[..., None])
+    return torch.stack(hs, 2), None, C, n
+
+
+def test_bwd_pin_split_chaining():
+    """Backward of a split run: the second part's initial-state gradients,
+    passed as the first part's final-state gradients, give the gradients of
+    the whole run (the state carry of the forward, run backwards)."""
+    a, dh = _case(51, 2, 2, 30, 6, 5, kscale=2.0)
+    T1 = 13
+    full = oracle.mlstm_bwd(dh=dh, **a)
+    part = lambda x, lo, hi: None if x is None else x[:, :, lo:hi]
+    seq = ("q", "k", "v", "i_pre", "f_pre", "o_pre")
+    a1 = dict(a, **{n: part(a[n], 0, T1) for n in seq})
+    _, C1, n1, m1 = _fwd_state(a1)
+    a2 = dict(a, **{n: part(a[n], T1, 30) for n in seq}, C0=C1.reshape(2, 2, 6, 5), n0=n1, m0=m1)
+    g2 = oracle.mlstm_bwd(dh=dh[:, :, T1:], **a2)
+    g1 = oracle.mlstm_bwd(dh=dh[:, :, :T1], dCT=g2["dC0"], dnT=g2["dn0"], **a1)
+    for nm in ("dq", "dk", "dv", "di", "df", "do"):
+        got = np.concatenate([g1[nm], g2[nm]], axis=2)
+        assert _relerr(got, full[nm]) < 1e-11, nm
+    assert _relerr(g1["dbias"] + g2["dbias"], full["dbias"]) < 1e-11
+    assert _relerr(g1["dC0"], full["dC0"]) < 1e-11 and _relerr(g1["dn0"], full["dn0"]) < 1e-11
+
+
+def test_bwd_pin_bias_terms():
+    """The per-token terms of the bias gradient: where |z_t| > 1 (z_t = n_t . q_t
+    + bias in true units), h_t = o * num / |z_t|, so d(dh_t . h_t)/d bias =
+    -(dh_t . h_t) sign(z_t) / |z_t|, else 0; h and z from the unstabilised
+    recurrence of this file.  Their sum over the batch and tokens is dbias."""
+    a, dh = _case(61, 2, 3, 40, 8, 6, kscale=3.0)
+    g = oracle.mlstm_bwd(dh=dh, **a)
+    t = {n: (None if x is None else torch.from_numpy(x)) for n, x in a.items()}
+    h, z = _torch_h(t)
+    h, z = h.numpy(), z.numpy()
+    assert (np.abs(z) > 1).any() and (np.abs(z) < 1).any()
+    ref = np.where(np.abs(z) > 1, -np.sum(dh * h, axis=-1) * np.sign(z) / np.abs(z), 0.0)
+    assert _relerr(g["dbias_t"], ref) < 1e-10
+    assert _relerr(g["dbias_t"].sum(axis=(0, 2)), g["dbias"]) < 1e-12
