@@ -57,9 +57,7 @@ def run_bwd(x, dev, seed, state=None):
     return out, ref
 
 
-def check(out, ref, tol, dbias_scale=None):
-    """dbias_scale ([H], optional): judge the bias gradient, a sum over every
-    token, against the magnitude of its terms rather than its own size."""
+def check(out, ref, tol):
     errs = {}
     for name in ("dq", "dk", "dv", "di", "df", "do", "dC0", "dn0"):
         if out.get(name) is None:
@@ -67,10 +65,7 @@ def check(out, ref, tol, dbias_scale=None):
         r = ref[name] if name != "dC0" else ref[name].reshape(out[name].shape)
         errs[name] = slice_err(cpu(out[name]), r)
     if out.get("dbias") is not None:
-        if dbias_scale is None:
-            errs["dbias"] = slice_err(cpu(out["dbias"]), ref["dbias"], lead=1)
-        else:
-            errs["dbias"] = float(np.abs(cpu(out["dbias"]) - ref["dbias"]).max() / np.max(dbias_scale))
+        errs["dbias"] = slice_err(cpu(out["dbias"]), ref["dbias"], lead=1)
     print({k: "%.2e" % v for k, v in errs.items()}, flush=True)
     bad = {k: v for k, v in errs.items() if not v < tol}
     assert not bad, bad
@@ -107,58 +102,31 @@ def test_bwd_xlstm7b_head_shape(gpu):
     check(out, ref, TOL[torch.bfloat16])
 
 
-def test_bwd_xlstm7b_full_T8192_window(gpu):
+def test_bwd_xlstm7b_full_T8192(gpu):
     """The 7B prefill workload at full size (B=1, H=8, T=8192: the launch
-    configuration bench.py times), dh non-zero on the last W = 320 tokens
-    only.  Window tokens: every gradient against the oracle's backward over
-    the window, started from the oracle's own state after the first T - W
-    tokens.  Prefix tokens: dq is exactly zero, and the last prefix token's dk
-    and dv follow from the window's initial-state gradient
-    (dk = i' (dC0 v + dn0), dv = i' dC0^T k with i' = e^{i_pre - m}).
+    configuration bench.py times), dh non-zero on every token except those
+    near the denominator floor, every gradient over the whole sequence
+    against the oracle's backward.
 
     The gradient jumps where |n.q + bias| crosses the floor 1 (the max in the
     denominator), and the GPU's states differ from fp64 by about 2e-3, so a
     token within that distance of the floor may take the other branch.  At
-    tokens whose margin ||z| / floor - 1| (from the oracle, stepping through
-    the window) is below 2e-2, dh is set to zero: there dh . h = 0, so dz~ = 0
-    on both sides whichever branch each takes."""
+    tokens whose margin ||z| - 1| (z from the oracle) is below 2e-2, dh is
+    set to zero: there dh . h = 0, so dz~ = 0 on both sides whichever branch
+    each takes (about 0.6 % of the tokens here)."""
     x = workload("xlstm7b_prefill_T8192")
     B, H, T, dqk = x.q.shape
     dv = x.v.shape[-1]
-    W = 320
-    cut = lambda t, a, b: t[:, :, a:b].contiguous()
-    _, C, n, m = oracle.mlstm_fwd(*(cut(t, 0, T - W) for t in (x.q, x.k, x.v, x.i_pre, x.f_pre)))
-    # margins to the denominator floor over the window
-    Cs, ns, ms = C.copy(), n.copy(), m.copy()
-    qn, kn, vn, ipn, fpn = (cpu(t) for t in (x.q, x.k, x.v, x.i_pre, x.f_pre))
-    near = np.zeros((B, H, W), dtype=bool)
-    for s in range(W):
-        t = T - W + s
-        oracle.mlstm_step(qn[:, :, t], kn[:, :, t], vn[:, :, t], ipn[:, :, t], fpn[:, :, t], Cs, ns, ms)
-        z = np.einsum("bhd,bhd->bh", ns, qn[:, :, t])
-        near[:, :, s] = np.abs(np.abs(z) * np.exp(ms) - 1) < 2e-2
     dh = grad_output((B, H, T, dv), seed=2006)
-    dh[:, :, :T - W] = 0
-    dh[:, :, T - W:][torch.from_numpy(near)] = 0
-    print("window tokens near the floor (dh zeroed): %d of %d" % (int(near.sum()), near.size), flush=True)
+    z = oracle.mlstm_bwd(x.q, x.k, x.v, x.i_pre, x.f_pre, dh)["z"]
+    near = np.abs(np.abs(z) - 1) < 2e-2
+    dh[torch.from_numpy(near)] = 0
+    print("tokens near the floor (dh zeroed): %d of %d" % (int(near.sum()), near.size), flush=True)
     g = x.to(gpu)
     out = mlstm.chunkwise_bwd(g.q, g.k, g.v, g.i_pre, g.f_pre, dh.to(gpu))
     torch.cuda.synchronize()
-    win = [cut(t, T - W, T) for t in (x.q, x.k, x.v, x.i_pre, x.f_pre)]
-    ref = oracle.mlstm_bwd(*win, cut(dh, T - W, T), C0=C.reshape(B, H, dqk, dv), n0=n, m0=m)
-    errs = {nm: slice_err(cpu(out[nm])[:, :, T - W:], ref[nm]) for nm in ("dq", "dk", "dv", "di", "df")}
-    print({k: "%.2e" % v for k, v in errs.items()}, flush=True)
-    assert all(v < TOL[torch.bfloat16] for v in errs.values()), errs
-    assert float(out["dq"][:, :, :T - W].abs().max()) == 0.0
-    t = T - W - 1
-    iw = np.exp(ipn[:, :, t] - m)  # e^{i_pre - m} with m after token t
-    dC0 = ref["dC0"]
-    dk_ref = iw[..., None] * (np.einsum("bhdc,bhc->bhd", dC0, vn[:, :, t]) + ref["dn0"])
-    dv_ref = iw[..., None] * np.einsum("bhdc,bhd->bhc", dC0, kn[:, :, t])
-    e_k = slice_err(cpu(out["dk"])[:, :, t], dk_ref)
-    e_v = slice_err(cpu(out["dv"])[:, :, t], dv_ref)
-    print("last prefix token: dk %.2e dv %.2e" % (e_k, e_v), flush=True)
-    assert e_k < TOL[torch.bfloat16] and e_v < TOL[torch.bfloat16], (e_k, e_v)
+    ref = oracle.mlstm_bwd(x.q, x.k, x.v, x.i_pre, x.f_pre, dh)
+    check(out, ref, TOL[torch.bfloat16])
 
 
 @pytest.mark.parametrize("G,dtype", [(2, "bf16"), (3, "bf16"), (3, "f32")])
@@ -206,17 +174,22 @@ def test_retention_bwd_msr_T2048_full(gpu):
     assert all(e < TOL[torch.bfloat16] for e in errs.values()), errs
 
 
-@pytest.mark.parametrize("dtype,T,init,G", [("f32", 150, True, 0), ("bf16", 200, False, 0),
-                                            ("bf16", 7 * 64 - 5, True, 3)])
-def test_bwd_block_diagonal(gpu, monkeypatch, dtype, T, init, G):
+@pytest.mark.parametrize("dtype,T,init,G,plain", [("f32", 150, True, 0, True), ("bf16", 200, False, 0, True),
+                                                  ("bf16", 7 * 64 - 5, True, 3, False)])
+def test_bwd_block_diagonal(gpu, monkeypatch, dtype, T, init, G, plain):
     """Two memory blocks (d_qk = d_v = 64, 32 x 32 blocks) with the xLSTM-v2
     workload's distributions: k / 8, forget mixture, uniform bias; an initial
     block-diagonal state; superchunks of 3 chunks in the last case.
 
-    The bias gradient is a sum over all tokens whose terms cancel (by about
-    85x in the last case), so it is judged against the magnitude of its
-    terms: the sum of |oracle dbias| over 16-token ranges of dh (dbias is
-    linear in dh).  Every other gradient is judged as elsewhere."""
+    The bias gradient is the sum over the batch and every token of per-token
+    terms dz_t (oracle's dbias_t).  With each term computed to a relative
+    accuracy e, the sum is accurate to e * sum |dz_t|, the forward-error bound
+    of a sum; where the terms cancel, that is far larger than e * |dbias|
+    (here sum |dz_t| / |dbias| is 12 and 7 in the fp32 case, 21 and 6 in the
+    first bf16 case, about 300 in the last).  So the bias gradient is judged
+    against tol * sum |dz_t| in every case, and the two better-conditioned
+    cases are also held to the plain normwise bar, tol * |dbias|.  Every
+    other gradient is judged as elsewhere."""
     if G:
         monkeypatch.setenv("MLSTM_SUPERCHUNK_CHUNKS", str(G))
     B, H, nb = 2, 2, 2
@@ -233,15 +206,19 @@ def test_bwd_block_diagonal(gpu, monkeypatch, dtype, T, init, G):
     out = mlstm.chunkwise_bwd(gx.q, gx.k, gx.v, gx.i_pre, gx.f_pre, dh.to(gpu), gx.o_pre, gx.bias,
                               state=None if st is None else tuple(t.to(gpu) for t in st), num_blocks=nb)
     torch.cuda.synchronize()
-    args = (x.q, x.k, x.v, x.i_pre, x.f_pre)
     sargs = st if st is not None else (None, None, None)
-    ref = oracle.mlstm_bwd(*args, dh, x.o_pre, x.bias, *sargs, num_blocks=nb)
-    scale = np.zeros(H)
-    for a in range(0, T, 16):
-        part = torch.zeros_like(dh)
-        part[:, :, a:a + 16] = dh[:, :, a:a + 16]
-        scale += np.abs(oracle.mlstm_bwd(*args, part, x.o_pre, x.bias, *sargs, num_blocks=nb)["dbias"])
-    check(out, ref, TOL[dt], dbias_scale=scale)
+    ref = oracle.mlstm_bwd(x.q, x.k, x.v, x.i_pre, x.f_pre, dh, x.o_pre, x.bias, *sargs, num_blocks=nb)
+    db, dbr = cpu(out["dbias"]), ref["dbias"]
+    terms = np.abs(ref["dbias_t"]).sum(axis=(0, 2))
+    e_sum = float((np.abs(db - dbr) / terms).max())
+    e_plain = slice_err(db, dbr, lead=1)
+    print("dbias: %.2e of sum |dz_t|, %.2e of |dbias| (sum |dz_t| / |dbias| = %s)"
+          % (e_sum, e_plain, np.round(terms / np.abs(dbr), 1)), flush=True)
+    assert e_sum < TOL[dt], e_sum
+    if plain:
+        assert e_plain < TOL[dt], e_plain
+    out = dict(out, dbias=None)  # judged above
+    check(out, ref, TOL[dt])
 
 
 def near_floor(x, state, band=2e-2):
