@@ -69,9 +69,9 @@ def _load(path: str | None = None):
     lib.oracle_mlstm_step.restype = i
     lib.oracle_retention_fwd.argtypes = [i, i, i, i, i] + [P] * 7
     lib.oracle_retention_fwd.restype = i
-    lib.oracle_mlstm_bwd.argtypes = [i, i, i, i, i, i] + [P] * 23
+    lib.oracle_mlstm_bwd.argtypes = [i, i, i, i, i, i] + [P] * 24
     lib.oracle_mlstm_bwd.restype = i
-    lib.oracle_retention_bwd.argtypes = [i, i, i, i, i] + [P] * 10
+    lib.oracle_retention_bwd.argtypes = [i, i, i, i, i] + [P] * 11
     lib.oracle_retention_bwd.restype = i
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i
@@ -208,8 +208,9 @@ def mlstm_bwd(q, k, v, i_pre, f_pre, dh, o_pre=None, bias=None, C0=None, n0=None
     gradient arriving at the stabilised final state (S~_T, n~_T at fixed m_T).
     Returns a dict of float64 arrays: dq, dk, dv, di (i_pre), df (f_pre), do
     (o_pre; None without o_pre), dbias [H], dbias_t [B,H,T] (the per-token
-    terms of dbias), dC0 [B,H,dqk,dv] and dn0 [B,H,dqk] (gradients of the
-    stabilised initial state, zero-state runs included)."""
+    terms of dbias), z [B,H,T] (n_t . q_t + bias in true units: the gradient
+    jumps where |z| crosses 1), dC0 [B,H,dqk,dv] and dn0 [B,H,dqk]
+    (gradients of the stabilised initial state, zero-state runs included)."""
     q, k, v, ip, fp, g = map(_f64, (q, k, v, i_pre, f_pre, dh))
     op, bs, c0, nn0, mm0, dct, dnt = map(_f64, (o_pre, bias, C0, n0, m0, dCT, dnT))
     B, H, T, dqk = q.shape
@@ -226,27 +227,29 @@ def mlstm_bwd(q, k, v, i_pre, f_pre, dh, o_pre=None, bias=None, C0=None, n0=None
     out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v),
                di=np.zeros((B, H, T)), df=np.zeros((B, H, T)),
                do=np.zeros_like(v) if op is not None else None,
-               dbias=np.zeros(H), dbias_t=np.zeros((B, H, T)), dC0=np.zeros(cshape),
+               dbias=np.zeros(H), dbias_t=np.zeros((B, H, T)), z=np.zeros((B, H, T)), dC0=np.zeros(cshape),
                dn0=np.zeros((B, H, dqk)))
     rc = (lib or _load()).oracle_mlstm_bwd(
         B, H, T, dqk, dv, nb, _ptr(q), _ptr(k), _ptr(v), _ptr(ip), _ptr(fp), _ptr(op),
         _ptr(bs), _ptr(c0), _ptr(nn0), _ptr(mm0), _ptr(g), _ptr(dct), _ptr(dnt), _ptr(out["dq"]),
         _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["di"]), _ptr(out["df"]),
-        _ptr(out["do"]), _ptr(out["dbias"]), _ptr(out["dbias_t"]), _ptr(out["dC0"]), _ptr(out["dn0"]))
+        _ptr(out["do"]), _ptr(out["dbias"]), _ptr(out["dbias_t"]), _ptr(out["z"]), _ptr(out["dC0"]), _ptr(out["dn0"]))
     if rc != 0:
         raise ValueError("oracle_mlstm_bwd failed with %d" % rc)
     return out
 
 
-def retention_bwd(q, k, v, dout, gamma=None, S0=None, lib=None):
-    """Gradients of sum(dout * out) for out = retention_fwd(q, k, v, gamma,
-    S0)[0].  Returns a dict of float64 arrays dq, dk, dv and dS0 [B,H,dk,dv]."""
-    q, k, v, g, s0, go = map(_f64, (q, k, v, gamma, S0, dout))
+def retention_bwd(q, k, v, dout, gamma=None, S0=None, lib=None, dS_T=None):
+    """Gradients of sum(dout * out) (+ <dS_T, S_T> with the optional gradient
+    dS_T [B,H,dk,dv] arriving at the final state) for out, S_T =
+    retention_fwd(q, k, v, gamma, S0).  Returns a dict of float64 arrays dq,
+    dk, dv and dS0 [B,H,dk,dv]."""
+    q, k, v, g, s0, go, dst = map(_f64, (q, k, v, gamma, S0, dout, dS_T))
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v), dS0=np.zeros((B, H, dk, dv)))
     rc = (lib or _load()).oracle_retention_bwd(
-        B, H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(go), _ptr(out["dq"]),
+        B, H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(go), _ptr(dst), _ptr(out["dq"]),
         _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dS0"]))
     if rc != 0:
         raise ValueError("oracle_retention_bwd failed with %d" % rc)

@@ -306,7 +306,9 @@ int oracle_retention_fwd(int B, int H, int T, int dk, int dv, const double* q,
  * call's dC0, dn0 (for the same m) are exactly the first call's dCT, dnT.
  * dh [B,H,T,d_v] in; outputs (any may be NULL): dq, dk [B,H,T,d_qk]; dv, do_pre
  * [B,H,T,d_v]; di, df [B,H,T]; dbias [H] (summed over B); dbias_t [B,H,T]
- * (the per-token terms dz_t of that sum, in true units); dC0
+ * (the per-token terms dz_t of that sum, in true units); z_t [B,H,T] (the
+ * normaliser argument n_t . q_t + bias in true units, whose |.| meets the
+ * floor 1 where the gradient jumps); dC0
  * [B,H,nb,d_qk/nb,d_v/nb]; dn0 [B,H,d_qk].  Returns 0, -1 for bad sizes, -2 when out of memory.
  */
 int oracle_mlstm_bwd(int B, int H, int T, int dqk, int dv, int nb, const double* q,
@@ -316,7 +318,7 @@ int oracle_mlstm_bwd(int B, int H, int T, int dqk, int dv, int nb, const double*
                      const double* dh, const double* dCT, const double* dnT,
                      double* dq, double* dk, double* dvo,
                      double* di, double* df, double* do_pre, double* dbias,
-                     double* dbias_t, double* dC0, double* dn0) {
+                     double* dbias_t, double* z_t, double* dC0, double* dn0) {
   if (B < 0 || H < 0 || T < 0 || dqk <= 0 || dv <= 0 || nb <= 0) return -1;
   if (dqk % nb || dv % nb) return -1;
   const int dqkb = dqk / nb, dvb = dv / nb;
@@ -412,6 +414,7 @@ int oracle_mlstm_bwd(int B, int H, int T, int dqk, int dv, int nb, const double*
         const double dz = fabs(zt) > fl ? -sdy / den * (zt > 0 ? 1.0 : -1.0) : 0.0;
         dbias_acc += dz * fl;
         if (dbias_t) dbias_t[tok] = dz * fl;
+        if (z_t) z_t[tok] = zt / fl;
         /* dq_t = S~_t dn + n~_t dz (the matrix per block, n~ over the head) */
         if (dq)
           for (int d = 0; d < dqk; ++d) {
@@ -490,8 +493,8 @@ int oracle_mlstm_bwd(int B, int H, int T, int dqk, int dv, int nb, const double*
  */
 int oracle_retention_bwd(int B, int H, int T, int dk, int dv, const double* q,
                          const double* k, const double* v, const double* gamma,
-                         const double* S0, const double* dout, double* dq,
-                         double* dk_out, double* dv_out, double* dS0) {
+                         const double* S0, const double* dout, const double* dST,
+                         double* dq, double* dk_out, double* dv_out, double* dS0) {
   if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0) return -1;
   const size_t ssz = (size_t)dk * dv;
   const long BH = (long)B * H;
@@ -523,16 +526,20 @@ int oracle_retention_bwd(int B, int H, int T, int dk, int dv, const double* q,
           dq[tok * dk + r] = a;
         }
     }
-    /* reverse sweep: G_t = gamma G_{t+1} + q_t dout_t^T (S reused as G) */
-    memset(S, 0, ssz * sizeof(double));
+    /* reverse sweep: G_t = gamma G_{t+1} + q_t dout_t^T (S reused as G),
+     * starting from the gradient arriving at the final state, G_{T-1} =
+     * dS_T + q_{T-1} dout_{T-1}^T */
+    if (dST) memcpy(S, dST + bh * ssz, ssz * sizeof(double));
+    else memset(S, 0, ssz * sizeof(double));
     for (int t = T - 1; t >= 0; --t) {
       const size_t tok = (size_t)bh * T + t;
       const double* qt = q + tok * dk;
       const double* kt = k + tok * dk;
       const double* vt = v + tok * dv;
       const double* gt = dout + tok * dv;
+      const double gd = t == T - 1 ? 1.0 : g; /* G_{t+1} decays into G_t */
       for (int r = 0; r < dk; ++r)
-        for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] = g * S[(size_t)r * dv + c] + qt[r] * gt[c];
+        for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] = gd * S[(size_t)r * dv + c] + qt[r] * gt[c];
       if (dk_out)
         for (int r = 0; r < dk; ++r) {
           double a = 0.0;

@@ -315,7 +315,8 @@ def test_bwd_pin_bias_terms():
     """The per-token terms of the bias gradient: where |z_t| > 1 (z_t = n_t . q_t
     + bias in true units), h_t = o * num / |z_t|, so d(dh_t . h_t)/d bias =
     -(dh_t . h_t) sign(z_t) / |z_t|, else 0; h and z from the unstabilised
-    recurrence of this file.  Their sum over the batch and tokens is dbias."""
+    recurrence of this file.  Their sum over the batch and tokens is dbias,
+    and the oracle's reported z is that recurrence's z."""
     a, dh = _case(61, 2, 3, 40, 8, 6, kscale=3.0)
     g = oracle.mlstm_bwd(dh=dh, **a)
     t = {n: (None if x is None else torch.from_numpy(x)) for n, x in a.items()}
@@ -325,3 +326,35 @@ def test_bwd_pin_bias_terms():
     ref = np.where(np.abs(z) > 1, -np.sum(dh * h, axis=-1) * np.sign(z) / np.abs(z), 0.0)
     assert _relerr(g["dbias_t"], ref) < 1e-10
     assert _relerr(g["dbias_t"].sum(axis=(0, 2)), g["dbias"]) < 1e-12
+    assert _relerr(g["z"], z) < 1e-12
+
+
+def test_retention_bwd_pin_final_state_finite_differences():
+    """Retention with a gradient arriving at the final state: central finite
+    differences of sum(dout * out) + <dS_T, S_T> (S_T from the forward)."""
+    rng = np.random.default_rng(23)
+    B, H, T, dk, dv = 1, 2, 7, 3, 4
+    a = dict(q=rng.standard_normal((B, H, T, dk)), k=rng.standard_normal((B, H, T, dk)),
+             v=rng.standard_normal((B, H, T, dv)), S0=rng.standard_normal((B, H, dk, dv)))
+    gamma = np.array([0.9, 0.7])
+    do = rng.standard_normal((B, H, T, dv))
+    dST = rng.standard_normal((B, H, dk, dv))
+
+    def loss():
+        out, S = oracle.retention_fwd(a["q"], a["k"], a["v"], gamma, a["S0"])
+        return np.sum(do * out) + np.sum(dST * S)
+
+    g = oracle.retention_bwd(a["q"], a["k"], a["v"], do, gamma, a["S0"], dS_T=dST)
+    eps = 1e-6
+    for name, gname in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("S0", "dS0")):
+        x = a[name]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            lp = loss()
+            x[idx] = keep - eps
+            lm = loss()
+            x[idx] = keep
+            fd[idx] = (lp - lm) / (2 * eps)
+        assert _relerr(g[gname], fd) < 1e-7, name
