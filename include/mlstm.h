@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MLSTM_ABI_VERSION 1
+#define MLSTM_ABI_VERSION 2
 
 typedef enum { MLSTM_F32 = 0, MLSTM_BF16 = 1 } mlstm_dtype;
 
@@ -263,6 +263,15 @@ size_t mlstm_chunkwise_bwd_workspace_bytes(int B, int H, int T, int d_qk, int d_
  *   q, k, v, i_pre, f_pre, o_pre, norm_bias, C0, n0, m0   as passed to the
  *                  forward (o_pre, norm_bias, C0, n0, m0 may be NULL);
  *   dh       [B,H,T,d_v]  gradient of the loss with respect to h (dtype dt);
+ *   dC_T [B,H,nb,d_qk/nb,d_v/nb], dn_T [B,H,d_qk] fp32 or NULL (zero): the
+ *                  gradient arriving at the final stabilised state (C_out,
+ *                  n_out of the forward) at fixed m_out, i.e. e^{m_T} times
+ *                  the gradient with respect to the true final C_T, n_T.  The
+ *                  loss is taken to depend on the final state only through
+ *                  the true state, as a continuation of the recurrence does
+ *                  (its outputs do not depend on the stabiliser), so m_out
+ *                  gets no gradient of its own.  A following call's dC0, dn0
+ *                  are exactly this call's dC_T, dn_T, so calls chain;
  *   dq, dk   [B,H,T,d_qk], dv [B,H,T,d_v], di_pre, df_pre [B,H,T]  outputs,
  *                  dtype dt (gradients of q, k, v and of the gate
  *                  preactivations i_pre, f_pre);
@@ -272,7 +281,6 @@ size_t mlstm_chunkwise_bwd_workspace_bytes(int B, int H, int T, int d_qk, int d_
  *   dC0 [B,H,nb,d_qk/nb,d_v/nb], dn0 [B,H,d_qk] fp32 or NULL: gradients of
  *                  the stabilised initial state C0, n0 (also for a zero state).
  *                  The gradient of m0 is <dC0, C0> + <dn0, n0>.
- * The final state gets no incoming gradient (the loss is taken on h only).
  * Requires chunk = 64 and either num_blocks = 1 with d_v a multiple of 64 and
  * d_qk in {64, 128, 256} (bf16) or 64 (fp32), or num_blocks = 2 with
  * d_qk = d_v = 64 (the block-diagonal memory of the "Edifice.Recurrent.XLSTMv2"
@@ -289,10 +297,10 @@ int mlstm_chunkwise_bwd(int B, int H, int T, int d_qk, int d_v, int num_blocks,
                         const void* v, const void* i_pre, const void* f_pre,
                         const void* o_pre, const float* norm_bias,
                         const float* C0, const float* n0, const float* m0,
-                        const void* dh, void* dq, void* dk,
-                        void* dv, void* di_pre, void* df_pre, void* do_pre,
-                        float* dbias, float* dC0, float* dn0, void* workspace,
-                        size_t workspace_bytes, void* stream);
+                        const void* dh, const float* dC_T, const float* dn_T,
+                        void* dq, void* dk, void* dv, void* di_pre, void* df_pre,
+                        void* do_pre, float* dbias, float* dC0, float* dn0,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace size in bytes for retention_chunkwise_bwd (0 for arguments it
  * does not take, with the error message set). */
@@ -306,9 +314,11 @@ size_t retention_chunkwise_bwd_workspace_bytes(int B, int H, int T, int d_k, int
  * ("Triple Paradigm": parallel mode is the training mode); this is the
  * gradient of the same function, computed chunkwise:
  *     dq_t = S_t dout_t,  dk_t = G_t v_t,  dv_t = G_t^T k_t,
- *     G_t = gamma_h G_{t+1} + q_t dout_t^T,  dS0 = gamma_h G_0.
+ *     G_t = gamma_h G_{t+1} + q_t dout_t^T,  G_T = dS_T,  dS0 = gamma_h G_0.
  *   q, k [B,H,T,d_k]; v, dout [B,H,T,d_v] (dtype dt); gamma [H] fp32 or NULL
  *   (1 - 2^(-5-h)); S0 [B,H,d_k,d_v] fp32 or NULL (zero);
+ *   dS_T [B,H,d_k,d_v] fp32 or NULL (zero): gradient arriving at the final
+ *   state S_out (a following call's dS0), so that calls chain;
  *   dq, dk [B,H,T,d_k], dv [B,H,T,d_v] outputs, dtype dt;
  *   dS0 [B,H,d_k,d_v] fp32 or NULL: gradient of S0 (also for a zero S0).
  * Requires chunk = 64, d_v a multiple of 64 and d_k in {64, 128} (bf16) or 64
@@ -320,9 +330,9 @@ size_t retention_chunkwise_bwd_workspace_bytes(int B, int H, int T, int d_k, int
 int retention_chunkwise_bwd(int B, int H, int T, int d_k, int d_v, int chunk,
                             mlstm_dtype dt, const void* q, const void* k,
                             const void* v, const float* gamma, const float* S0,
-                            const void* dout, void* dq, void* dk, void* dv,
-                            float* dS0, void* workspace, size_t workspace_bytes,
-                            void* stream);
+                            const void* dout, const float* dS_T, void* dq, void* dk,
+                            void* dv, float* dS0, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

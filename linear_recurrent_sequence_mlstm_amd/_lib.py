@@ -71,12 +71,12 @@ def lib():
     L.retention_step.restype = i
     L.mlstm_chunkwise_bwd_workspace_bytes.argtypes = [i] * 8
     L.mlstm_chunkwise_bwd_workspace_bytes.restype = sz
-    L.mlstm_chunkwise_bwd.argtypes = ([i] * 8 + [vp] * 6 + [fp] * 4 + [vp] + [vp] * 6 + [fp] * 3 +
+    L.mlstm_chunkwise_bwd.argtypes = ([i] * 8 + [vp] * 6 + [fp] * 4 + [vp] + [fp] * 2 + [vp] * 6 + [fp] * 3 +
                                       [vp, sz, vp])
     L.mlstm_chunkwise_bwd.restype = i
     L.retention_chunkwise_bwd_workspace_bytes.argtypes = [i] * 7
     L.retention_chunkwise_bwd_workspace_bytes.restype = sz
-    L.retention_chunkwise_bwd.argtypes = [i] * 7 + [vp] * 3 + [fp] * 2 + [vp] * 4 + [fp] + [vp, sz, vp]
+    L.retention_chunkwise_bwd.argtypes = [i] * 7 + [vp] * 3 + [fp] * 2 + [vp] + [fp] + [vp] * 3 + [fp] + [vp, sz, vp]
     L.retention_chunkwise_bwd.restype = i
     _lib = L
     return L
@@ -314,12 +314,14 @@ def retention_step(q, k, v, S, gamma=None, out=None):
 
 
 def chunkwise_bwd(q, k, v, i_pre, f_pre, dh, o_pre=None, bias=None, state=None, chunk=64,
-                  state_grad=True, workspace=None, num_blocks=1):
+                  state_grad=True, workspace=None, num_blocks=1, final_grad=None):
     """mlstm_chunkwise_bwd: gradients of sum(dh * h) for h = chunkwise_fwd(q, k,
     v, i_pre, f_pre, o_pre, bias, state, num_blocks) (vector normaliser).
-    Returns a dict with dq, dk, dv, di (i_pre), df (f_pre), do (o_pre, or
-    None), dbias ([H] fp32, or None without bias) and, with state_grad, dC0
-    [B,H,nb,dqk/nb,dv/nb] and dn0 [B,H,dqk] (fp32)."""
+    final_grad = (dC_T [B,H,nb,dqk/nb,dv/nb] or None, dn_T [B,H,dqk] or None),
+    fp32: gradient arriving at the final stabilised state (a following call's
+    dC0, dn0).  Returns a dict with dq, dk, dv, di (i_pre), df (f_pre), do
+    (o_pre, or None), dbias ([H] fp32, or None without bias) and, with
+    state_grad, dC0 [B,H,nb,dqk/nb,dv/nb] and dn0 [B,H,dqk] (fp32)."""
     B, H, T, dqk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
@@ -340,6 +342,11 @@ def chunkwise_bwd(q, k, v, i_pre, f_pre, dh, o_pre=None, bias=None, state=None, 
         C0, n0, m0 = state
         for t, nm, shp in zip((C0, n0, m0), ("C0", "n0", "m0"), (cshape, (B, H, dqk), (B, H))):
             _need(t, nm, shp, torch.float32, dev)
+    dCT = dnT = None
+    if final_grad is not None:
+        dCT, dnT = final_grad
+        _need(dCT, "dC_T", cshape, torch.float32, dev)
+        _need(dnT, "dn_T", (B, H, dqk), torch.float32, dev)
     out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                di=torch.empty_like(i_pre), df=torch.empty_like(f_pre),
                do=torch.empty_like(o_pre) if o_pre is not None else None,
@@ -349,21 +356,24 @@ def chunkwise_bwd(q, k, v, i_pre, f_pre, dh, o_pre=None, bias=None, state=None, 
     L = lib()
     nbytes = L.mlstm_chunkwise_bwd_workspace_bytes(B, H, T, dqk, dv, nb, chunk, _DT[dt])
     if nbytes == 0:
-        _check(L.mlstm_chunkwise_bwd(B, H, T, dqk, dv, nb, chunk, _DT[dt], *([None] * 20), None, 0, None),
+        _check(L.mlstm_chunkwise_bwd(B, H, T, dqk, dv, nb, chunk, _DT[dt], *([None] * 22), None, 0, None),
                "mlstm_chunkwise_bwd")
     ws, wsb = _workspace(nbytes, dev, workspace)
     rc = L.mlstm_chunkwise_bwd(B, H, T, dqk, dv, nb, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre),
                                _ptr(f_pre), _ptr(o_pre), _ptr(bias), _ptr(C0), _ptr(n0), _ptr(m0),
-                               _ptr(dh), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["di"]),
+                               _ptr(dh), _ptr(dCT), _ptr(dnT), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                               _ptr(out["di"]),
                                _ptr(out["df"]), _ptr(out["do"]), _ptr(out["dbias"]), _ptr(out["dC0"]),
                                _ptr(out["dn0"]), _ptr(ws), wsb, _stream(dev))
     _check(rc, "mlstm_chunkwise_bwd")
     return out
 
 
-def retention_chunkwise_bwd(q, k, v, dout, gamma=None, S0=None, chunk=64, state_grad=True, workspace=None):
+def retention_chunkwise_bwd(q, k, v, dout, gamma=None, S0=None, chunk=64, state_grad=True, workspace=None,
+                            dS_T=None):
     """retention_chunkwise_bwd: gradients of sum(dout * out) for out =
-    retention_chunkwise_fwd(q, k, v, gamma, S0).  Returns a dict with dq, dk,
+    retention_chunkwise_fwd(q, k, v, gamma, S0); dS_T [B,H,dk,dv] fp32 or
+    None: gradient arriving at the final state.  Returns a dict with dq, dk,
     dv and, with state_grad, dS0 [B,H,dk,dv] fp32."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -376,16 +386,17 @@ def retention_chunkwise_bwd(q, k, v, dout, gamma=None, S0=None, chunk=64, state_
     _need(dout, "dout", (B, H, T, dv), dt, dev)
     _need(gamma, "gamma", (H,), torch.float32, dev)
     _need(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    _need(dS_T, "dS_T", (B, H, dk, dv), torch.float32, dev)
     out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                dS0=torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev) if state_grad else None)
     L = lib()
     nbytes = L.retention_chunkwise_bwd_workspace_bytes(B, H, T, dk, dv, chunk, _DT[dt])
     if nbytes == 0:
-        _check(L.retention_chunkwise_bwd(B, H, T, dk, dv, chunk, _DT[dt], *([None] * 10), None, 0, None),
+        _check(L.retention_chunkwise_bwd(B, H, T, dk, dv, chunk, _DT[dt], *([None] * 11), None, 0, None),
                "retention_chunkwise_bwd")
     ws, wsb = _workspace(nbytes, dev, workspace)
     rc = L.retention_chunkwise_bwd(B, H, T, dk, dv, chunk, _DT[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
-                                   _ptr(S0), _ptr(dout), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                   _ptr(S0), _ptr(dout), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
                                    _ptr(out["dS0"]), _ptr(ws), wsb, _stream(dev))
     _check(rc, "retention_chunkwise_bwd")
     return out

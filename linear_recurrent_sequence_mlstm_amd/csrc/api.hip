@@ -130,7 +130,7 @@ int launch(const Plan& pl, mlstm::ChunkParams& p, void* workspace, size_t worksp
 struct BwdPlan {
   Plan fwd;
   size_t off_carry, off_segdec, nseg, off_cst, off_cmin, off_U, off_Pt, off_Dt, off_rden, off_dz, off_db, off_dbh, off_qdq, off_kdki,
-      off_kdk, bytes;
+      off_kdk, off_cT, bytes;
 };
 
 int plan_bwd(int B, int H, int T, int dqk, int dv, int nb, int chunk, int dt, BwdPlan* bp, bool ret = false) {
@@ -175,6 +175,9 @@ int plan_bwd(int B, int H, int T, int dqk, int dv, int nb, int chunk, int dt, Bw
   o += align256(BH * bp->nseg * ((size_t)dqk * dv + dqk) * 4);
   bp->off_segdec = o;
   o += align256(BH * bp->nseg * 4);
+  // partials of <dC_T, S~_T> + <dn_T, n~_T>, one per 64 x 64 state tile
+  bp->off_cT = o;
+  o += align256(BH * (size_t)(dqk / 64 > 0 ? dqk / 64 : 1) * (dv / 64 > 0 ? dv / 64 : 1) * 4);
   bp->bytes = o;
   return MLSTM_OK;
 }
@@ -193,9 +196,9 @@ size_t mlstm_chunkwise_bwd_workspace_bytes(int B, int H, int T, int d_qk, int d_
 int mlstm_chunkwise_bwd(int B, int H, int T, int d_qk, int d_v, int num_blocks, int chunk, mlstm_dtype dt,
                         const void* q, const void* k, const void* v, const void* i_pre, const void* f_pre,
                         const void* o_pre, const float* norm_bias, const float* C0, const float* n0,
-                        const float* m0, const void* dh, void* dq, void* dk, void* dv,
-                        void* di_pre, void* df_pre, void* do_pre, float* dbias, float* dC0, float* dn0,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        const float* m0, const void* dh, const float* dC_T, const float* dn_T, void* dq,
+                        void* dk, void* dv, void* di_pre, void* df_pre, void* do_pre, float* dbias, float* dC0,
+                        float* dn0, void* workspace, size_t workspace_bytes, void* stream) {
   BwdPlan bp;
   const int rc = plan_bwd(B, H, T, d_qk, d_v, num_blocks, chunk, dt, &bp);
   if (rc != MLSTM_OK) return rc;
@@ -289,6 +292,9 @@ int mlstm_chunkwise_bwd(int B, int H, int T, int d_qk, int d_v, int num_blocks, 
   b.dbias = dbias;
   b.dC0 = dC0;
   b.dn0 = dn0;
+  b.dCT = dC_T;
+  b.dnT = dn_T;
+  b.ws_cT = (dC_T || dn_T) ? reinterpret_cast<float*>(ws + bp.off_cT) : nullptr;
   if (g_ev0) (void)hipEventRecord(g_ev0, st);
   e = mlstm::launch_bwd(dt, b, st);
   if (g_ev1) (void)hipEventRecord(g_ev1, st);
@@ -304,8 +310,8 @@ size_t retention_chunkwise_bwd_workspace_bytes(int B, int H, int T, int d_k, int
 
 int retention_chunkwise_bwd(int B, int H, int T, int d_k, int d_v, int chunk, mlstm_dtype dt, const void* q,
                             const void* k, const void* v, const float* gamma, const float* S0, const void* dout,
-                            void* dq, void* dk, void* dv, float* dS0, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+                            const float* dS_T, void* dq, void* dk, void* dv, float* dS0, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   BwdPlan bp;
   const int rc = plan_bwd(B, H, T, d_k, d_v, 1, chunk, dt, &bp, true);
   if (rc != MLSTM_OK) return rc;
@@ -384,6 +390,7 @@ int retention_chunkwise_bwd(int B, int H, int T, int d_k, int d_v, int chunk, ml
   b.dk = dk;
   b.dv = dv;
   b.dC0 = dS0;
+  b.dCT = dS_T;  // retention has no gates: the walk needs no final-state dot product
   if (g_ev0) (void)hipEventRecord(g_ev0, st);
   e = mlstm::launch_bwd(dt, b, st);
   if (g_ev1) (void)hipEventRecord(g_ev1, st);

@@ -18,14 +18,19 @@
 //   dk_j = sum_l D'_lj q_l + w_j (G_c v_j + g_c),
 //   dv_j = sum_l E_lj (q_l . k_j) dn~_l + w_j G_c^T k_j,
 // with (G_c, g_c) the backward state at the end of chunk c from the reverse
-// chunk scan  G_{c-1} = 2^{m_prev - M_L} G_c + sum_j alpha_j q_j [dn~_j, dz~_j]^T.
-// q and k enter h only through e^{F_t} q_t and e^{i_t - F_t} k_t (F the
-// cumulative log forget gate), so d i_pre_t = k_t . dk_t and d log f_t is the
-// reverse cumulative sum of q_s . dq_s - k_s . dk_s over s >= t.
+// chunk scan  G_{c-1} = 2^{m_prev - M_L} G_c + sum_j alpha_j q_j [dn~_j, dz~_j]^T,
+// which starts from the gradient arriving at the final state (dC_T, dn_T;
+// zero without one).
+// q and k enter h and the final state only through e^{F_t} q_t, e^{i_t - F_t} k_t
+// and the factor e^{F_T} of the final state (F the cumulative log forget
+// gate), so d i_pre_t = k_t . dk_t and d log f_t is the reverse cumulative
+// sum of q_s . dq_s - k_s . dk_s over s >= t plus the constant
+// <dC_T, S~_T> + <dn_T, n~_T>.
 //
 // Kernels (all on the caller's stream, after the forward's state passes):
 //   bwd_chunk_states_kernel  per (batch*head, superchunk, 64 x 64 state tile):
-//                      every chunk's start state.
+//                      every chunk's start state (and, with a final-state
+//                      gradient, the final state's share of <dC_T, S~_T>).
 //   bwd_scores_kernel  per (batch*head, chunk): Q K^T, the denominators, the
 //                      readout (recomputed), dN V^T; writes P = E.(Q K^T) and
 //                      D' (and transposes), 1/den~, dz~, d o_pre and a bias
@@ -291,6 +296,9 @@ __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
   }
   float m = p.sc_min[(size_t)bh * p.NS + sc];  // meaningful in threads below 64
   const int cb = sc * p.G, ce = min(p.NC, cb + p.G);
+  // with a gradient arriving at the final state, the last superchunk's walk
+  // also applies its last chunk, and iteration ce holds the final state
+  const int cend = (p.ws_cT && sc == p.NS - 1) ? ce + 1 : ce;
   const auto rk = make_rsrc(static_cast<const T*>(p.k) + (size_t)bh * p.T * DQK, (unsigned)(p.T * DQK) * ES);
   const auto rv = make_rsrc(static_cast<const T*>(p.v) + (size_t)bh * p.T * p.DV, (unsigned)(p.T * p.DV) * ES);
   float kx[16], vx[16];
@@ -304,21 +312,50 @@ __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
     gL = p.ws_gg[tg + BL - 1];
     bL = p.ws_gb[tg + BL - 1];
   }
-  for (int c = cb; c < ce; ++c) {
+  for (int c = cb; c < cend; ++c) {
+    if (c == ce) {
+      // the final state: this tile's share of <dC_T, S~_T> (+ <dn_T, n~_T>)
+      float a = 0.f;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int d = dt * 64 + 16 * n + lr, cc = ct * 64 + 16 * w + 4 * lg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float g;
+          if constexpr (NB == 1) {
+            g = p.dCT ? p.dCT[(size_t)bh * DQK * p.DV + (size_t)d * p.DV + cc + i] : 0.f;
+          } else {  // block layout [NB][32][32]; off-diagonal entries are zero
+            const int bb = d / 32;
+            g = (p.dCT && (cc + i) / 32 == bb)
+                    ? p.dCT[(size_t)bh * 2048 + bb * 1024 + (d - 32 * bb) * 32 + (cc + i - 32 * bb)]
+                    : 0.f;
+          }
+          a += g * acc[n][i];
+        }
+      }
+      if (lead && (tid & 3) == 0 && p.dnT) a += nn * p.dnT[(size_t)bh * DQK + dt * 64 + r];
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) a += __shfl_xor(a, d, 64);
+      __syncthreads();  // sw is free
+      if (lane == 0) sw[w] = a;
+      __syncthreads();
+      if (tid == 0) p.ws_cT[(size_t)bh * NDT * NVT + dt * NVT + ct] = sw[0] + sw[1] + sw[2] + sw[3];
+      break;
+    }
     float* St = p.ws_state + ((size_t)bh * p.NC + c) * NST;
 #pragma unroll
     for (int n = 0; n < 4; ++n)
       *reinterpret_cast<float4*>(St + toff + (size_t)16 * n * p.DV) = make_float4(acc[n][0], acc[n][1], acc[n][2], acc[n][3]);
     if (lead && (tid & 3) == 0) St[(size_t)DQK * p.DV + dt * 64 + r] = nn;
     if (lead && dt == 0 && tid == 0) p.ws_min[(size_t)bh * p.NC + c] = m;
-    if (c + 1 == ce) break;  // the next superchunk starts from its own start state
+    if (c + 1 == cend) break;  // the next superchunk starts from its own start state
     __syncthreads();  // previous chunk's operands are consumed
     if (tid < BL) {
       const float ML = fmaxf(m, gL);
       sw[tid] = exp2_fast(ga - ML);
       if (tid == 0) sdec = exp2_fast(m - ML);
       m = bL + ML;
-      if (c + 2 < ce) {
+      if (c + 2 < cend) {
         const size_t tg = (size_t)bh * NCL + (size_t)(c + 1) * BL;
         ga = p.ws_ga[tg + tid];
         gL = p.ws_gg[tg + BL - 1];
@@ -336,7 +373,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
       for (int e = 0; e < 16; ++e) kx[e] -= to_f32(from_f32<T>(kx[e]));
       st_row16<T>(sKl, r, c0, kx);
     }
-    if (c + 2 < ce) {
+    if (c + 2 < cend) {
       load16f<T>(rk, ((unsigned)((c + 1) * BL + r) * DQK + dt * 64 + c0) * ES, kx);
       load16f<T>(rv, ((unsigned)((c + 1) * BL + r) * p.DV + ct * 64 + c0) * ES, vx);
     }
@@ -865,6 +902,32 @@ __device__ __forceinline__ void store_init_grad(const BwdParams& p, int DQK, int
   }
 }
 
+// The gradient arriving at the final state for entries e0 .. e0+3 of the
+// flattened [S~ | n~] state (full layout; dC_T in the memory's block layout,
+// zero off the diagonal blocks); zero without one.
+__device__ __forceinline__ float4 load_final_grad(const BwdParams& p, int DQK, int bh, size_t e0) {
+  const size_t CS = (size_t)DQK * p.DV, NST = CS + DQK;
+  float g4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const size_t e = e0 + i;
+    if (e < CS) {
+      if (p.dCT) {
+        if (p.NB == 1) {
+          g4[i] = p.dCT[(size_t)bh * CS + e];
+        } else {
+          const int d = (int)(e / p.DV), cc = (int)(e % p.DV);
+          const int bq = DQK / p.NB, bv = p.DV / p.NB, b = d / bq;
+          if (cc / bv == b) g4[i] = p.dCT[(size_t)bh * (CS / p.NB) + (size_t)b * bq * bv + (size_t)(d % bq) * bv + cc % bv];
+        }
+      }
+    } else if (e < NST) {
+      if (p.dnT) g4[i] = p.dnT[(size_t)bh * DQK + (e - CS)];
+    }
+  }
+  return make_float4(g4[0], g4[1], g4[2], g4[3]);
+}
+
 template <int SW>
 __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p, int DQK) {
   const int bh = blockIdx.y;
@@ -874,7 +937,7 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p, int DQK) {
   float* base = p.ws_U + (size_t)bh * p.NC * NST;
   const float* gg = p.ws_gg + (size_t)bh * p.NC * BL;
   const float* mn = p.ws_min + (size_t)bh * p.NC;
-  float4 G = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 G = active ? load_final_grad(p, DQK, bh, e0) : make_float4(0.f, 0.f, 0.f, 0.f);
   for (int c1 = p.NC - 1; c1 >= 0; c1 -= SW) {
     float4 u[SW];
     float dec[SW];
@@ -894,7 +957,7 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p, int DQK) {
       const int c = c1 - j;
       if (c >= 0) {
         if (active) *reinterpret_cast<float4*>(base + (size_t)c * NST + e0) = G;
-        const float f = c == p.NC - 1 ? 0.f : dec[j];
+        const float f = dec[j];
         G.x = f * G.x + u[j].x;
         G.y = f * G.y + u[j].y;
         G.z = f * G.z + u[j].z;
@@ -932,7 +995,7 @@ __global__ __launch_bounds__(256) void bwd_scan_local_kernel(BwdParams p, int DQ
   for (int c = ce - 1; c >= cb; --c) {
     const float4 u = *reinterpret_cast<const float4*>(base + (size_t)c * NST + e0);
     *reinterpret_cast<float4*>(base + (size_t)c * NST + e0) = G;
-    const float f = c == p.NC - 1 ? 0.f : chunk_decay(p, bh, c);
+    const float f = chunk_decay(p, bh, c);
     fs *= f;
     G.x = f * G.x + u.x;
     G.y = f * G.y + u.y;
@@ -948,7 +1011,7 @@ __global__ __launch_bounds__(256) void bwd_scan_carry_kernel(BwdParams p, int DQ
   const size_t NST = (size_t)DQK * p.DV + DQK;
   const size_t e0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e0 >= NST) return;
-  float4 G = make_float4(0.f, 0.f, 0.f, 0.f);  // entering the end of segment sg
+  float4 G = load_final_grad(p, DQK, bh, e0);  // entering the end of segment sg
   constexpr int W = 8;  // segments whose totals load together
   for (int s1 = p.NSEG - 1; s1 >= 0; s1 -= W) {
     float4 tot[W];
@@ -982,7 +1045,8 @@ __global__ __launch_bounds__(256) void bwd_scan_apply_kernel(BwdParams p, int DQ
   const int bh = blockIdx.y, sg = blockIdx.z;
   const size_t NST = (size_t)DQK * p.DV + DQK;
   const size_t e0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (e0 >= NST || sg == p.NSEG - 1) return;  // nothing enters the last segment
+  // only a final-state gradient enters the last segment
+  if (e0 >= NST || (sg == p.NSEG - 1 && !p.dCT && !p.dnT)) return;
   float* base = p.ws_U + (size_t)bh * p.NC * NST;
   const float4 C = *reinterpret_cast<const float4*>(p.ws_carry + ((size_t)bh * p.NSEG + sg) * NST + e0);
   const int cb = sg * SEG, ce = min(p.NC, cb + SEG);
@@ -1191,12 +1255,15 @@ __global__ __launch_bounds__(64) void bwd_gate_total_kernel(BwdParams p, int NDT
 }
 
 template <typename T>
-__global__ __launch_bounds__(64) void bwd_gate_kernel(BwdParams p) {
+__global__ __launch_bounds__(64) void bwd_gate_kernel(BwdParams p, int NCT) {
   const int lane = threadIdx.x;
   const int bh = blockIdx.x / p.NC, c = blockIdx.x % p.NC;
   const size_t tg = (size_t)bh * p.NC * BL + (size_t)c * BL + lane;
   float carry = 0.f;
   for (int c2 = c + 1 + lane; c2 < p.NC; c2 += 64) carry += p.ws_ctot[(size_t)bh * p.NC + c2];
+  // <dC_T, S~_T> + <dn_T, n~_T> from the walk's tile partials
+  if (p.ws_cT)
+    for (int i = lane; i < NCT; i += 64) carry += p.ws_cT[(size_t)bh * NCT + i];
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) carry += __shfl_xor(carry, d, 64);
   // suffix sum within the chunk: lane 63 - l takes token l
@@ -1262,7 +1329,7 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_dkv_kernel<T, DQK, NB>), dim3(nch * (DQK / 64 + p.DV / 64)), dim3(256), 0, stream, p);
   if (!p.ret) {  // retention has no gates or normaliser to differentiate
     hipLaunchKernelGGL(bwd_gate_total_kernel, dim3(nch), dim3(64), 0, stream, p, DQK / 64);
-    hipLaunchKernelGGL((bwd_gate_kernel<T>), dim3(nch), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((bwd_gate_kernel<T>), dim3(nch), dim3(64), 0, stream, p, (DQK / 64) * (p.DV / 64));
     if (p.dbias) hipLaunchKernelGGL(bwd_bias_kernel, dim3((unsigned)p.H), dim3(256), 0, stream, p);
   }
   return hipGetLastError();

@@ -137,6 +137,12 @@ struct BwdParams {
   float* dbias;
   float* dC0;
   float* dn0;
+  // gradient arriving at the stabilised final state (S~_T, n~_T at fixed
+  // m_T), layouts of dC0 / dn0, or null; ws_cT [B*H][(d_qk/64)(d_v/64)]
+  // receives the walk tiles' partials of <dC_T, S~_T> + <dn_T, n~_T>
+  const float* dCT;
+  const float* dnT;
+  float* ws_cT;
 };
 bool bwd_supported(int dtype, int dqk, int dv, int nb);
 hipError_t launch_bwd(int dtype, const BwdParams& p, hipStream_t stream);

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert _lib.abi_version() == 1
+    assert _lib.abi_version() == 2
 
 
 BOGUS = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first

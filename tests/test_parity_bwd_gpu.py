@@ -267,3 +267,112 @@ def test_bwd_long_sequence_two_level_scan(gpu, dtype):
     ref = oracle.mlstm_bwd(x.q, x.k, x.v, x.i_pre, x.f_pre, dh, x.o_pre, x.bias, st[0].reshape(B, H, 64, 64),
                            st[1], st[2])
     check(out, ref, TOL[x.q.dtype])
+
+
+def _final_grad(B, H, dqk, dv, seed, nb=1, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(B, H, nb, dqk // nb, dv // nb, generator=g) * scale,
+            torch.randn(B, H, dqk, generator=g) * scale)
+
+
+@pytest.mark.parametrize("dtype,T,dqk,dv,nb,init,G", [("f32", 150, 64, 64, 1, True, 0),
+                                                      ("bf16", 200, 64, 128, 1, False, 0),
+                                                      ("bf16", 7 * 64 - 9, 64, 128, 1, True, 3),
+                                                      ("bf16", 160, 256, 512, 1, False, 0),
+                                                      ("f32", 150, 64, 64, 2, True, 0),
+                                                      ("bf16", 300, 64, 64, 2, False, 2)])
+def test_bwd_final_state_gradient(gpu, monkeypatch, dtype, T, dqk, dv, nb, init, G):
+    """A gradient arriving at the final stabilised state (dC_T, dn_T at fixed
+    m_T) on top of dh: every gradient against the oracle's backward with the
+    same final-state gradient; one and two memory blocks, superchunks of
+    several chunks."""
+    if G:
+        monkeypatch.setenv("MLSTM_SUPERCHUNK_CHUNKS", str(G))
+    B, H = 2, 2
+    x = mlstm_inputs(B, H, T, dqk, dv, seed=3500 + T + dqk, dtype=dtype, nb=nb, k_scale=dqk ** -0.5,
+                     f_mix=True, with_o=True, bias="uniform")
+    dh = grad_output((B, H, T, dv), seed=3600 + T, dtype=dtype)
+    dCT, dnT = _final_grad(B, H, dqk, dv, 3700 + T, nb)
+    st = None
+    if init:
+        g = torch.Generator().manual_seed(3800 + T)
+        st = (torch.randn(B, H, nb, dqk // nb, dv // nb, generator=g) * 0.3,
+              torch.randn(B, H, dqk, generator=g) * 0.3, torch.rand(B, H, generator=g) * 4 - 2)
+    gx = x.to(gpu)
+    out = mlstm.chunkwise_bwd(gx.q, gx.k, gx.v, gx.i_pre, gx.f_pre, dh.to(gpu), gx.o_pre, gx.bias,
+                              state=None if st is None else tuple(t.to(gpu) for t in st), num_blocks=nb,
+                              final_grad=(dCT.to(gpu), dnT.to(gpu)))
+    torch.cuda.synchronize()
+    sargs = st if st is not None else (None, None, None)
+    ref = oracle.mlstm_bwd(x.q, x.k, x.v, x.i_pre, x.f_pre, dh, x.o_pre, x.bias, *sargs, num_blocks=nb,
+                           dCT=dCT, dnT=dnT)
+    # The bias gradient does not depend on the final-state gradient; its
+    # terms cancel by about 140x in the fp32 case, so it is judged against the
+    # sum of their magnitudes (the bar of the block-diagonal tests)
+    terms = np.abs(ref["dbias_t"]).sum(axis=(0, 2))
+    e = float((np.abs(cpu(out["dbias"]) - ref["dbias"]) / terms).max())
+    print("dbias: %.2e of sum |dz_t| (sum |dz_t| / |dbias| = %s)" % (e, np.round(terms / np.abs(ref["dbias"]), 1)))
+    assert e < TOL[x.q.dtype], e
+    check(dict(out, dbias=None), ref, TOL[x.q.dtype])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_final_state_gradient_two_level_scan(gpu, dtype):
+    """A final-state gradient with 257 chunks (the two-level chunk scan: it
+    enters the carry of the last segment)."""
+    B, H, T = 1, 2, 256 * 64 + 37
+    x = mlstm_inputs(B, H, T, 64, 64, seed=3900, dtype=dtype, k_scale=1 / 8, f_mix=True, with_o=True,
+                     bias="uniform")
+    st = _state(B, H, 64, 64, 3902)
+    mask = near_floor(x, st)
+    dh = grad_output((B, H, T, 64), seed=3901, dtype=dtype)
+    dh[torch.from_numpy(mask)] = 0
+    dCT, dnT = _final_grad(B, H, 64, 64, 3903)
+    g = x.to(gpu)
+    out = mlstm.chunkwise_bwd(g.q, g.k, g.v, g.i_pre, g.f_pre, dh.to(gpu), g.o_pre, g.bias,
+                              state=tuple(t.to(gpu) for t in st), final_grad=(dCT.to(gpu), dnT.to(gpu)))
+    torch.cuda.synchronize()
+    ref = oracle.mlstm_bwd(x.q, x.k, x.v, x.i_pre, x.f_pre, dh, x.o_pre, x.bias, st[0].reshape(B, H, 64, 64),
+                           st[1], st[2], dCT=dCT, dnT=dnT)
+    check(out, ref, TOL[x.q.dtype])
+
+
+def test_bwd_chained_calls(gpu):
+    """Training across two calls: the forward of the first part hands its
+    final state to the second; the second's backward returns dC0, dn0, which
+    enter the first's backward as the final-state gradient.  The gradients of
+    both parts together equal the oracle's backward of the whole sequence
+    (the split-run test of the forward, run backwards)."""
+    B, H, T, T1 = 1, 2, 700, 320
+    x = mlstm_inputs(B, H, T, 64, 128, seed=4000, dtype="bf16", k_scale=1 / 8, f_mix=True, with_o=True,
+                     bias="uniform")
+    dh = grad_output((B, H, T, 128), seed=4001)
+    g = x.to(gpu)
+    cut = lambda t, a, b: None if t is None else t[:, :, a:b].contiguous()
+    part1 = [cut(t, 0, T1) for t in (g.q, g.k, g.v, g.i_pre, g.f_pre)]
+    part2 = [cut(t, T1, T) for t in (g.q, g.k, g.v, g.i_pre, g.f_pre)]
+    _, st1 = mlstm.chunkwise_fwd(*part1, cut(g.o_pre, 0, T1), g.bias)
+    g2 = mlstm.chunkwise_bwd(*part2, dh[:, :, T1:].contiguous().to(gpu), cut(g.o_pre, T1, T), g.bias, state=st1)
+    g1 = mlstm.chunkwise_bwd(*part1, dh[:, :, :T1].contiguous().to(gpu), cut(g.o_pre, 0, T1), g.bias,
+                             final_grad=(g2["dC0"], g2["dn0"]))
+    torch.cuda.synchronize()
+    ref = oracle.mlstm_bwd(x.q, x.k, x.v, x.i_pre, x.f_pre, dh, x.o_pre, x.bias)
+    out = {nm: torch.cat([g1[nm], g2[nm]], dim=2) for nm in ("dq", "dk", "dv", "di", "df", "do")}
+    out["dbias"] = g1["dbias"] + g2["dbias"]
+    out["dC0"], out["dn0"] = g1["dC0"], g1["dn0"]
+    check(out, ref, TOL[torch.bfloat16])
+
+
+@pytest.mark.parametrize("dtype,T,dk,dv", [("f32", 150, 64, 64), ("bf16", 300, 128, 128)])
+def test_retention_bwd_final_state_gradient(gpu, dtype, T, dk, dv):
+    from linear_recurrent_sequence_mlstm_amd.workloads import retention_inputs
+    B, H = 2, 3
+    q, k, v = retention_inputs(B, H, T, dk, dv, seed=4100 + T, dtype=dtype)
+    do = grad_output((B, H, T, dv), seed=4200 + T, dtype=dtype)
+    dST = torch.randn(B, H, dk, dv, generator=torch.Generator().manual_seed(4300))
+    out = mlstm.retention_chunkwise_bwd(q.to(gpu), k.to(gpu), v.to(gpu), do.to(gpu), dS_T=dST.to(gpu))
+    torch.cuda.synchronize()
+    ref = oracle.retention_bwd(q, k, v, do, None, None, dS_T=dST)
+    errs = {nm: slice_err(cpu(out[nm]), ref[nm]) for nm in ("dq", "dk", "dv", "dS0")}
+    print(errs, flush=True)
+    assert all(e < TOL[q.dtype] for e in errs.values()), errs
