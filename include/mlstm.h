@@ -158,6 +158,36 @@ int mlstm_chunkwise_fwd_ex(int B, int H, int T, int d_qk, int d_v, int num_block
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mlstm_chunkwise_fwd_ex without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Its kernels use a scratch array
+ * that the library holds in device memory: one copy of
+ * mlstm_noalloc_scratch_bytes() bytes (64 MiB) per GPU, created when the
+ * library's code loads on that GPU and kept until the process ends.  This
+ * call allocates nothing: no hipMalloc, hipFree or allocating library
+ * routine.  Its first call on a device looks the array's address up once
+ * (hipGetSymbolAddress) with that device current.  A call whose
+ * mlstm_chunkwise_workspace_bytes(...) exceeds the scratch size returns
+ * MLSTM_E_WORKSPACE before anything runs.  Every call on one GPU uses the
+ * same array and leaves its contents behind (nothing in it needs to start at
+ * zero): calls that overlap on one GPU (on different streams, or from
+ * different threads without ordering) race and must not be made.  Arguments,
+ * outputs and supported shapes are those of mlstm_chunkwise_fwd_ex.
+ */
+int mlstm_chunkwise_fwd_noalloc(int B, int H, int T, int d_qk, int d_v,
+                                int num_blocks, int chunk, mlstm_dtype dt,
+                                int norm_mode, const void* q, const void* k,
+                                const void* v, const void* i_pre,
+                                const void* f_pre, const void* o_pre,
+                                const float* norm_bias, const float* C0,
+                                const float* n0, const float* m0,
+                                float* C_out, float* n_out, float* m_out,
+                                void* h, void* stream);
+
+/* Size in bytes of the per-GPU scratch array of mlstm_chunkwise_fwd_noalloc. */
+size_t mlstm_noalloc_scratch_bytes(void);
+
+/*
  * Fused single-token decode step on every (b, h); the fp32 state is updated
  * IN PLACE and the readout uses the updated state.
  *   q, k  [B,H,d_qk]; v [B,H,d_v]; i_pre, f_pre [B,H]; o_pre [B,H,d_v] or

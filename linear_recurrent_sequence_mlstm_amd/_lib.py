@@ -27,7 +27,8 @@ EXPORTS = ("mlstm_abi_version", "mlstm_last_error", "mlstm_set_profile_events",
            "retention_chunkwise_workspace_bytes",
            "retention_chunkwise_fwd", "retention_chunkwise_groupnorm_fwd", "retention_step",
            "mlstm_chunkwise_bwd_workspace_bytes", "mlstm_chunkwise_bwd",
-           "retention_chunkwise_bwd_workspace_bytes", "retention_chunkwise_bwd")
+           "retention_chunkwise_bwd_workspace_bytes", "retention_chunkwise_bwd",
+           "mlstm_chunkwise_fwd_noalloc", "mlstm_noalloc_scratch_bytes")
 
 
 def library_path() -> str:
@@ -58,6 +59,10 @@ def lib():
     L.mlstm_step.restype = i
     L.mlstm_chunkwise_fwd_ex.argtypes = [i] * 9 + [vp] * 6 + [fp] * 7 + [vp, vp, sz, vp]
     L.mlstm_chunkwise_fwd_ex.restype = i
+    L.mlstm_chunkwise_fwd_noalloc.argtypes = [i] * 9 + [vp] * 6 + [fp] * 7 + [vp, vp]
+    L.mlstm_chunkwise_fwd_noalloc.restype = i
+    L.mlstm_noalloc_scratch_bytes.argtypes = []
+    L.mlstm_noalloc_scratch_bytes.restype = sz
     L.mlstm_step_ex.argtypes = [i] * 7 + [vp] * 6 + [fp] * 4 + [vp, vp]
     L.mlstm_step_ex.restype = i
     L.retention_chunkwise_workspace_bytes.argtypes = [i] * 6 + [i]
@@ -213,6 +218,43 @@ def chunkwise_fwd(q, k, v, i_pre, f_pre, o_pre=None, bias=None, state=None, num_
                                   wsb, _stream(dev))
     _check(rc, "mlstm_chunkwise_fwd_ex")
     return h, ((Co, no, mo) if return_state else None)
+
+
+def chunkwise_fwd_noalloc(q, k, v, i_pre, f_pre, h, state_out, o_pre=None, bias=None, state=None, num_blocks=1,
+                          chunk=64, norm_mode="vector"):
+    """mlstm_chunkwise_fwd_noalloc: chunkwise_fwd into caller-given outputs h
+    [B,H,T,dv] and state_out = (C, n, m) (or None), using the library's
+    per-GPU scratch array instead of a workspace; nothing is allocated."""
+    mode = NORM_MODES[norm_mode]
+    B, H, T, dqk = q.shape
+    dv = v.shape[-1]
+    nb = int(num_blocks)
+    dev, dt = q.device, q.dtype
+    if dt not in _DT:
+        raise TypeError("unsupported dtype %s" % dt)
+    _need(k, "k", (B, H, T, dqk), dt, dev)
+    _need(v, "v", (B, H, T, dv), dt, dev)
+    _need(i_pre, "i_pre", (B, H, T), dt, dev)
+    _need(f_pre, "f_pre", (B, H, T), dt, dev)
+    _need(o_pre, "o_pre", (B, H, T, dv), dt, dev)
+    _need(bias, "bias", (H,), torch.float32, dev)
+    _need(h, "h", (B, H, T, dv), dt, dev)
+    scalar_n = mode == NORM_MODES["scalar"]
+    sshape = ((B, H, nb, dqk // nb, dv // nb), (B, H) if scalar_n else (B, H, dqk), (B, H))
+    C0 = n0 = m0 = Co = no = mo = None
+    if state is not None:
+        C0, n0, m0 = state
+        for t, nm, shp in zip((C0, n0, m0), ("C0", "n0", "m0"), sshape):
+            _need(t, nm, shp, torch.float32, dev)
+    if state_out is not None:
+        Co, no, mo = state_out
+        for t, nm, shp in zip((Co, no, mo), ("C_out", "n_out", "m_out"), sshape):
+            _need(t, nm, shp, torch.float32, dev)
+    rc = lib().mlstm_chunkwise_fwd_noalloc(B, H, T, dqk, dv, nb, chunk, _DT[dt], mode, _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(i_pre), _ptr(f_pre), _ptr(o_pre), _ptr(bias), _ptr(C0), _ptr(n0),
+                                           _ptr(m0), _ptr(Co), _ptr(no), _ptr(mo), _ptr(h), _stream(dev))
+    _check(rc, "mlstm_chunkwise_fwd_noalloc")
+    return h
 
 
 def step(q, k, v, i_pre, f_pre, C, n, m, o_pre=None, bias=None, num_blocks=1, h=None,

@@ -8,8 +8,18 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/mlstm.h"
 #include "kernels.h"
+
+// Scratch of mlstm_chunkwise_fwd_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  In host code `scratch` names a host
+// stand-in, never the device memory: the device address comes from
+// hipGetSymbolAddress (per device, see scratch_ptr) and only that address is
+// handed to kernels.
+static constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -180,6 +190,86 @@ int plan_bwd(int B, int H, int T, int dqk, int dv, int nb, int chunk, int dt, Bw
   o += align256(BH * (size_t)(dqk / 64 > 0 ? dqk / 64 : 1) * (dv / 64 > 0 ? dv / 64 : 1) * 4);
   bp->bytes = o;
   return MLSTM_OK;
+}
+
+}  // namespace
+
+namespace {
+
+// The device address of this device's copy of `scratch`, looked up once per
+// device (with that device current, as the caller's stream requires).
+int scratch_ptr(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MLSTM_E_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MLSTM_E_HIP, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MLSTM_E_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return MLSTM_OK;
+}
+
+// Shared by mlstm_chunkwise_fwd(_ex) (the caller's workspace) and
+// mlstm_chunkwise_fwd_noalloc (this device's scratch array).
+int chunkwise_fwd_impl(int B, int H, int T, int d_qk, int d_v, int num_blocks, int chunk, mlstm_dtype dt,
+                              int norm_mode, const void* q, const void* k, const void* v, const void* i_pre,
+                              const void* f_pre, const void* o_pre, const float* norm_bias, const float* C0,
+                              const float* n0, const float* m0, float* C_out, float* n_out, float* m_out, void* h,
+                              void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
+  if (norm_mode != MLSTM_NORM_VECTOR && norm_mode != MLSTM_NORM_SCALAR && norm_mode != MLSTM_NORM_BLOCK)
+    return fail(MLSTM_E_UNSUPPORTED, "unknown norm_mode %d", norm_mode);
+  Plan pl;
+  const int rc = plan_chunkwise(B, H, T, d_qk, d_v, num_blocks, chunk, dt, false, &pl);
+  if (rc != MLSTM_OK) return rc;
+  if (!q || !k || !v || !i_pre || !f_pre || !h)
+    return fail(MLSTM_E_NULL, "q, k, v, i_pre, f_pre and h are required");
+  if (noalloc) {
+    if (pl.bytes > kScratchBytes)
+      return fail(MLSTM_E_WORKSPACE, "this call needs %zu bytes of scratch; the no-allocation entry point holds %zu",
+                  pl.bytes, kScratchBytes);
+    const int rs = scratch_ptr(&workspace);
+    if (rs != MLSTM_OK) return rs;
+    workspace_bytes = kScratchBytes;
+  }
+  if (norm_mode == MLSTM_NORM_SCALAR) {
+    if (!pl.var.launch_scalar_norm) return fail(MLSTM_E_UNSUPPORTED, "no scalar-normaliser kernel");
+    pl.var.launch = pl.var.launch_scalar_norm;  // same plan and workspace
+  }
+  if (norm_mode == MLSTM_NORM_BLOCK && num_blocks > 1) {  // one block: the vector normaliser
+    if (!pl.var.launch_block_norm) return fail(MLSTM_E_UNSUPPORTED, "no per-block-normaliser kernel");
+    pl.var.launch = pl.var.launch_block_norm;
+  }
+  mlstm::ChunkParams p{};
+  p.B = B;
+  p.H = H;
+  p.T = T;
+  p.DV = d_v;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.i_pre = i_pre;
+  p.f_pre = f_pre;
+  p.o_pre = o_pre;
+  p.bias = norm_bias;
+  p.ret_gamma = nullptr;
+  p.has_init = (C0 || n0 || m0) ? 1 : 0;
+  p.C0 = C0;
+  p.n0 = n0;
+  p.m0 = m0;
+  p.h = h;
+  p.C_out = C_out;
+  p.n_out = n_out;
+  p.m_out = m_out;
+  return launch(pl, p, workspace, workspace_bytes, stream);
 }
 
 }  // namespace
@@ -438,44 +528,22 @@ int mlstm_chunkwise_fwd_ex(int B, int H, int T, int d_qk, int d_v, int num_block
                            const void* f_pre, const void* o_pre, const float* norm_bias, const float* C0,
                            const float* n0, const float* m0, float* C_out, float* n_out, float* m_out, void* h,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  if (norm_mode != MLSTM_NORM_VECTOR && norm_mode != MLSTM_NORM_SCALAR && norm_mode != MLSTM_NORM_BLOCK)
-    return fail(MLSTM_E_UNSUPPORTED, "unknown norm_mode %d", norm_mode);
-  Plan pl;
-  const int rc = plan_chunkwise(B, H, T, d_qk, d_v, num_blocks, chunk, dt, false, &pl);
-  if (rc != MLSTM_OK) return rc;
-  if (!q || !k || !v || !i_pre || !f_pre || !h)
-    return fail(MLSTM_E_NULL, "q, k, v, i_pre, f_pre and h are required");
-  if (norm_mode == MLSTM_NORM_SCALAR) {
-    if (!pl.var.launch_scalar_norm) return fail(MLSTM_E_UNSUPPORTED, "no scalar-normaliser kernel");
-    pl.var.launch = pl.var.launch_scalar_norm;  // same plan and workspace
-  }
-  if (norm_mode == MLSTM_NORM_BLOCK && num_blocks > 1) {  // one block: the vector normaliser
-    if (!pl.var.launch_block_norm) return fail(MLSTM_E_UNSUPPORTED, "no per-block-normaliser kernel");
-    pl.var.launch = pl.var.launch_block_norm;
-  }
-  mlstm::ChunkParams p{};
-  p.B = B;
-  p.H = H;
-  p.T = T;
-  p.DV = d_v;
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.i_pre = i_pre;
-  p.f_pre = f_pre;
-  p.o_pre = o_pre;
-  p.bias = norm_bias;
-  p.ret_gamma = nullptr;
-  p.has_init = (C0 || n0 || m0) ? 1 : 0;
-  p.C0 = C0;
-  p.n0 = n0;
-  p.m0 = m0;
-  p.h = h;
-  p.C_out = C_out;
-  p.n_out = n_out;
-  p.m_out = m_out;
-  return launch(pl, p, workspace, workspace_bytes, stream);
+  return chunkwise_fwd_impl(B, H, T, d_qk, d_v, num_blocks, chunk, dt, norm_mode, q, k, v, i_pre, f_pre, o_pre,
+                            norm_bias, C0, n0, m0, C_out, n_out, m_out, h, workspace, workspace_bytes, stream,
+                            false);
 }
+
+int mlstm_chunkwise_fwd_noalloc(int B, int H, int T, int d_qk, int d_v, int num_blocks, int chunk, mlstm_dtype dt,
+                                int norm_mode, const void* q, const void* k, const void* v, const void* i_pre,
+                                const void* f_pre, const void* o_pre, const float* norm_bias, const float* C0,
+                                const float* n0, const float* m0, float* C_out, float* n_out, float* m_out,
+                                void* h, void* stream) {
+  return chunkwise_fwd_impl(B, H, T, d_qk, d_v, num_blocks, chunk, dt, norm_mode, q, k, v, i_pre, f_pre, o_pre,
+                            norm_bias, C0, n0, m0, C_out, n_out, m_out, h, nullptr, 0, stream, true);
+}
+
+size_t mlstm_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
 
 int retention_chunkwise_fwd(int B, int H, int T, int d_k, int d_v, int chunk, mlstm_dtype dt, const void* q,
                             const void* k, const void* v, const float* gamma, const float* S0, float* S_out,

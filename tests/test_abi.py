@@ -147,3 +147,21 @@ def test_workspace_argument_checks():
     assert n == 2048 and ws.dtype == torch.float32
     with pytest.raises(ValueError, match="contiguous"):
         _lib._workspace(16, cpu, torch.empty(64, 2)[:, 0])
+
+
+def test_noalloc_rejects_beyond_its_scratch():
+    """The no-allocation forward holds a fixed scratch array: a call that
+    needs more is rejected before anything runs (no GPU needed), and invalid
+    arguments get the same codes as the workspace entry point."""
+    L = _lib.lib()
+    cap = L.mlstm_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    p = [BOGUS] * 6 + [None] * 7
+    need = L.mlstm_chunkwise_workspace_bytes(4, 8, 8192, 256, 512, 1, 64, 1)
+    assert need > cap
+    assert L.mlstm_chunkwise_fwd_noalloc(4, 8, 8192, 256, 512, 1, 64, 1, 0, *p, BOGUS, None) == E_WORKSPACE
+    assert "scratch" in _lib.last_error()
+    assert L.mlstm_chunkwise_workspace_bytes(1, 8, 8192, 256, 512, 1, 64, 1) <= cap  # the 7B prefill fits
+    assert L.mlstm_chunkwise_fwd_noalloc(1, 2, 64, 96, 64, 1, 64, 1, 0, *p, BOGUS, None) == E_UNSUPPORTED
+    assert L.mlstm_chunkwise_fwd_noalloc(1, 2, 64, 64, 64, 1, 64, 1, 0, *p, None, None) == E_NULL
+    assert L.mlstm_chunkwise_fwd_noalloc(1, 2, 64, 64, 64, 1, 64, 1, 9, *p, BOGUS, None) == E_UNSUPPORTED
