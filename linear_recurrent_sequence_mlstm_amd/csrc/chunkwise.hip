@@ -973,6 +973,482 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   }
 }
 
+// Pass 3, wave-specialised form for the xLSTM-7B head shape (bf16, d_qk = 256,
+// one memory block, chunks of 64 tokens, 128 d_v columns per work-group).
+// Same arithmetic as chunk_kernel, split by role so that the MFMA pipes of
+// every SIMD see one wave that streams products while another wave on the same
+// SIMD does the loads, scores, normaliser and gate work:
+//   state waves 0..3  own all 256 state rows x 32 columns each (fp32, in MFMA
+//                     accumulator registers): readout S~^T q, P V, outputs,
+//                     state update.  No exchange between waves.
+//   helper waves 4..7 stage the next chunk (global loads into registers,
+//                     then LDS), compute the chunk's causal score tiles with
+//                     their decay factors (P to LDS, fp32 row sums for the
+//                     denominator), n~ . q_j (hi + lo bf16 rows of n~, fused
+//                     with the score tile (0, j)), the n~ update and the gate
+//                     vectors of the next chunk (the m_prev chain).
+// K and V are double-buffered in LDS (the next chunk's go into the other
+// buffer while the state waves update from the current one), as are the
+// gate vectors and n~, so a chunk needs two work-group barriers:
+//   A: the chunk's Q, K, V, gate vectors and n~ are in LDS;
+//      state waves: readout; helpers: scores, n~ . q, P and den partials.
+//   B: P and the denominators are in LDS, Q is free;
+//      state waves: P V, outputs, update; helpers: the next chunk's Q, K, V
+//      and gate vectors into LDS, n~ of this chunk, then the loads of the
+//      chunk after.
+template <bool HAS_O, bool SN>
+__global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
+  using T = __bf16;
+  using M = Mma<T>;
+  typedef typename M::frag frag;
+  constexpr int DQK = 256, L = 64, W = 128, WC = 32, CT = 2, NT = 16, NJT = 4, NKL = 2;
+  constexpr int K = M::K, KL = M::KL;
+  constexpr int VE = 8;  // bf16 elements per 16 bytes
+  constexpr int QS = DQK + lds_pad_res(DQK, 2, MLSTM_P3_QRES);
+  constexpr int KST = DQK + lds_pad_res(DQK, 2, MLSTM_P3_QRES);  // two K buffers: the smaller padding
+  constexpr int VS = W + lds_row_pad(W, 2);
+  constexpr int PS = L + 8;
+  constexpr unsigned ES = 2;
+  constexpr int NTQK = NJT * (NJT + 1) / 2;  // causal score tiles
+
+  __shared__ __attribute__((aligned(16))) T sQ[L * QS];
+  __shared__ __attribute__((aligned(16))) T sK[2][L * KST];
+  __shared__ __attribute__((aligned(16))) T sV[2][L * VS];
+  __shared__ __attribute__((aligned(16))) T sP[L * PS];
+  __shared__ __attribute__((aligned(16))) T sNh[2][2 * DQK];  // n~ as hi / lo bf16 rows, two sets
+  __shared__ float sNf[2][DQK];
+  __shared__ float sA2b[2][L], sM2b[2][L], sRSb[2][L], sCLb[2][L], sBTb[2][L], sWb[2][L];
+  __shared__ float sDenPart[NJT * L];
+  __shared__ float sDenInter[L];
+  __shared__ float sAlphab[2];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool state_wave = w < 4;
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int BH = p.B * p.H;
+  const int idx = blockIdx.x;
+  const int bh = __builtin_amdgcn_readfirstlane(idx % BH);
+  const int slice = __builtin_amdgcn_readfirstlane((idx / BH) % p.nslices);
+  const int sc = __builtin_amdgcn_readfirstlane((idx / BH) / p.nslices);
+  const int hd = __builtin_amdgcn_readfirstlane(bh % p.H);
+  const int T_ = p.T, DV = p.DV;
+  const size_t CS = (size_t)DQK * DV;
+  const size_t NSTATE = CS + DQK;
+  const int c_begin = sc * p.G;
+  const int c_end = min(c_begin + p.G, p.NC);
+
+  const auto rq = make_rsrc(static_cast<const T*>(p.q) + (size_t)bh * T_ * DQK, (unsigned)T_ * DQK * ES);
+  const auto rk = make_rsrc(static_cast<const T*>(p.k) + (size_t)bh * T_ * DQK, (unsigned)T_ * DQK * ES);
+  const auto rv = make_rsrc(static_cast<const T*>(p.v) + (size_t)bh * T_ * DV, (unsigned)T_ * DV * ES);
+  const size_t NCL = (size_t)p.NC * L;
+  const auto rga_r = make_rsrc(p.ws_ga + (size_t)bh * NCL, (unsigned)NCL * 4u);
+  const auto rgg_r = make_rsrc(p.ws_gg + (size_t)bh * NCL, (unsigned)NCL * 4u);
+  const auto rgb_r = make_rsrc(p.ws_gb + (size_t)bh * NCL, (unsigned)NCL * 4u);
+  const auto ro = make_rsrc(HAS_O ? static_cast<const T*>(p.o_pre) + (size_t)bh * T_ * DV : nullptr,
+                            HAS_O ? (unsigned)T_ * DV * ES : 0u);
+  const auto rh = make_rsrc(static_cast<T*>(p.h) + (size_t)bh * T_ * DV, (unsigned)T_ * DV * ES);
+  const float bias = p.bias ? p.bias[hd] : 0.f;
+  const float* Sin = (sc > 0 || p.has_init) ? p.ws_state + ((size_t)bh * p.NS + sc) * NSTATE : nullptr;
+
+  // n~ into set s: fp32 and as the hi / lo rows of the den tile
+  auto put_n = [&](int s, int r, float x) __attribute__((always_inline)) {
+    sNf[s][r] = x;
+    const T hi = (T)x;
+    sNh[s][r] = hi;
+    sNh[s][DQK + r] = (T)(x - (float)hi);
+  };
+  for (int r = tid; r < DQK; r += 512) put_n(0, r, Sin ? Sin[CS + r] : 0.f);
+  for (int e = tid; e < L * PS; e += 512) sP[e] = (T)0.f;  // masked tiles are never written
+  for (int e = tid; e < NJT * L; e += 512) sDenPart[e] = 0.f;
+
+  // ------------------------------------------------------------ helper waves
+  // Staging: helper thread ht of 256 holds 16-byte units ht + 256 it of the
+  // next chunk's Q (8), K (8) and V slice (4) between their loads and their
+  // LDS stores.
+  const int ht = tid - 256;
+  const int hw = w - 4;  // helper index
+  Vec16<T> gq[8], gk[8], gv[4];
+  unsigned rga = 0, rgg = 0, rgb = 0;  // chunk-local gate logs of the next chunk (helper 0)
+  float m_prev = p.ws_min[(size_t)bh * p.NS + sc];  // stabiliser chain, kept by helper 0
+
+  auto h_load = [&](int c) __attribute__((always_inline)) {
+    const unsigned t0 = (unsigned)c * L;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int u = ht + it * 256;
+      const unsigned j = u >> 5, col = (u & 31) * VE;
+      gq[it] = bload16<T>(rq, ((t0 + j) * DQK + col) * ES);
+      gk[it] = bload16<T>(rk, ((t0 + j) * DQK + col) * ES);
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int u = ht + it * 256;
+      const unsigned j = u >> 4, col = (u & 15) * VE;
+      gv[it] = bload16<T>(rv, ((t0 + j) * DV + slice * W + col) * ES);
+    }
+    if (hw == 0) {
+      const unsigned o = (t0 + (unsigned)lane) * 4u;
+      rga = bload1_raw<float>(rga_r, o);
+      rgg = bload1_raw<float>(rgg_r, o);
+      rgb = bload1_raw<float>(rgb_r, o);
+    }
+  };
+  auto h_store = [&](int kv) __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int u = ht + it * 256;
+      const int j = u >> 5, col = (u & 31) * VE;
+      *reinterpret_cast<uint4*>(&sQ[j * QS + col]) = *reinterpret_cast<const uint4*>(gq[it].v);
+      *reinterpret_cast<uint4*>(&sK[kv][j * KST + col]) = *reinterpret_cast<const uint4*>(gk[it].v);
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int u = ht + it * 256;
+      const int j = u >> 4, col = (u & 15) * VE;
+      *reinterpret_cast<uint4*>(&sV[kv][j * VS + col]) = *reinterpret_cast<const uint4*>(gv[it].v);
+    }
+  };
+  // gate vectors of the loaded chunk into set gb (helper 0, one lane per token)
+  auto h_gates = [&](int gb) __attribute__((always_inline)) {
+    const float a = __uint_as_float(rga), g = __uint_as_float(rgg), b = __uint_as_float(rgb);
+    const float Mj = fmaxf(m_prev, g);
+    const float gL = __uint_as_float(__builtin_amdgcn_readlane(rgg, L - 1));
+    const float bL = __uint_as_float(__builtin_amdgcn_readlane(rgb, L - 1));
+    const float ML = fmaxf(m_prev, gL);
+    const float mj = b + Mj;
+    const float cl = exp2_fast(-mj);
+    sA2b[gb][lane] = a;
+    sM2b[gb][lane] = Mj;
+    sRSb[gb][lane] = exp2_fast(m_prev - Mj);
+    sCLb[gb][lane] = cl;
+    sBTb[gb][lane] = bias * cl;
+    sWb[gb][lane] = exp2_fast(a - ML);
+    if (lane == 0) sAlphab[gb] = m_prev - ML;
+    m_prev = bL + ML;
+  };
+
+  // ------------------------------------------------------------- state waves
+  // Wave s owns columns [32 s, 32 s + 32) of the slice and every state row,
+  // rows stored in perm_row order so that the accumulators are the readout's
+  // A operand.
+  // The two roles run separate loops with the same two barriers per chunk
+  // (their registers never live at the same time).
+  if (state_wave) {
+  const int sw = w;
+  const int wcol0 = slice * W + sw * WC;  // first global d_v column of this state wave
+  f32x4 st[NT][CT];
+  const int soff = perm_row_lane<T>(lg) * DV + wcol0 + lr;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[nt][ct][i] = Sin ? Sin[soff + perm_row_uni<T>(nt, i) * DV + ct * 16] : 0.f;
+  float sig = 0.f;  // the registers hold S~ / 2^sig (lazy decay)
+  const int vcol = sw * WC + 4 * (lr & 3);  // transposing-read source column of V^T (+ 16 ct)
+  const int kcol = 8 * (lr & 3);            // ... of K^T (+ perm part per tile)
+  for (int c = c_begin; c < c_end; ++c) {
+    const int t0 = c * L;
+    const int pb = (c - c_begin) & 1;  // buffer / set of this chunk
+    const bool need_update = c + 1 < c_end || (sc == p.NS - 1);
+    __syncthreads();  // A
+    {
+      // output-gate values of this wave's outputs, issued now so that the
+      // readout hides their latency
+      Raw4<T> oraw[HAS_O ? NJT : 1][HAS_O ? CT : 1];
+      if constexpr (HAS_O) {
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            oraw[jt][ct] = bload4_raw<T>(ro, ((unsigned)(t0 + jt * 16 + lr) * DV + wcol0 + ct * 16 + 4 * lg) * ES);
+      }
+      // readout of the state at the chunk start: acc[jt][ct] = S~[:, c]^T q_j
+      f32x4 acc[NJT][CT];
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[jt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // n~ . q_j of query tile sw alongside: rows 0 (hi) and 1 (lo) of an A
+      // tile of n~ times this wave's Q fragments of that tile
+      f32x4 pn = {0.f, 0.f, 0.f, 0.f};
+      const T* nh = sNh[pb];
+#pragma unroll
+      for (int kk = 0; kk < DQK / K; ++kk) {
+        frag qf[NJT];
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt) qf[jt] = M::load(&sQ[(jt * 16 + lr) * QS + kk * K + KL * lg]);
+        frag nf = M::zero();
+        if constexpr (!SN) {
+          const frag f = M::load(&nh[(lr & 1) * DQK + kk * K + KL * lg]);
+          nf = lr < 2 ? f : M::zero();
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const frag sf = StateFrag<T, NT, CT>::get(st, kk, ct);
+#pragma unroll
+          for (int jt = 0; jt < NJT; ++jt) acc[jt][ct] = M::mma(sf, qf[jt], acc[jt][ct]);
+        }
+        if constexpr (!SN) {
+          frag qs = qf[0];
+#pragma unroll
+          for (int jt = 1; jt < NJT; ++jt) qs = sw == jt ? qf[jt] : qs;  // wave-uniform select
+          pn = M::mma(nf, qs, pn);
+        }
+      }
+      if constexpr (SN) {  // the inter part of the denominator is n~ itself
+        if (sw == 0) sDenInter[lane] = sNf[pb][0];
+      } else {
+        if (lg == 0) sDenInter[sw * 16 + lr] = pn[0] + pn[1];
+      }
+      __syncthreads();  // B
+      const float* sA2 = sA2b[pb];
+      const float* sRS = sRSb[pb];
+      const float* sCL = sCLb[pb];
+      const float* sBT = sBTb[pb];
+      const float* sW = sWb[pb];
+      const T* sVc = sV[pb];
+      frag vf[CT][NKL];  // V^T fragments of this wave's columns
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int kb = 0; kb < NKL; ++kb) vf[ct][kb] = frag_rows(sVc, VS, kb * K, lg, lr, vcol + ct * 16);
+      // P V, combine, outputs
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) {
+        f32x4 o_acc[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) o_acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKL; ++kb) {
+          if (kb * K <= jt * 16 + 15) {
+            const frag pf = M::load(&sP[(jt * 16 + lr) * PS + kb * K + KL * lg]);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) o_acc[ct] = M::mma(vf[ct][kb], pf, o_acc[ct]);
+          }
+        }
+        const int j = jt * 16 + lr;
+        const float rs = sRS[j];
+        const float rs_state = rs * exp2_fast(sig);
+        float den = rs * sDenInter[j] + sBT[j];
+#pragma unroll
+        for (int t = 0; t < NJT; ++t) den += sDenPart[t * L + j];
+        const float inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), sCL[j]));
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          float o[4] = {1.f, 1.f, 1.f, 1.f};
+          if constexpr (HAS_O) {
+            raw4_to_f32<T>(oraw[jt][ct], o);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = sigmoidf_(o[i]);
+          }
+          float hv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hv[i] = o[i] * (o_acc[ct][i] + rs_state * acc[jt][ct][i]) * inv;
+          // rows past T fall outside the output buffer and are dropped
+          bstore4<T>(rh, ((unsigned)(t0 + j) * DV + wcol0 + ct * 16 + 4 * lg) * ES, hv[0], hv[1], hv[2], hv[3]);
+        }
+      }
+      // state update: S^ <- S^ + 2^{-sig'} (w . K)^T V (the chunk's decay is
+      // folded into sig; rescaled once sig drops below -64)
+      if (need_update) {
+        const float la = sAlphab[pb];
+        const float sig_new = sig + la;
+        const bool rescale = sig_new < -64.f;  // wave-uniform, rare
+        const float wscale = exp2_fast(rescale ? 0.f : -sig_new);
+        frag wv[CT][NKL];
+#pragma unroll
+        for (int kb = 0; kb < NKL; ++kb) {
+          float wls[KL];
+#pragma unroll
+          for (int e = 0; e < KL; ++e) wls[e] = sW[kb * K + krow<T>(lg, e)] * wscale;
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) wv[ct][kb] = scale_frag(vf[ct][kb], wls);
+        }
+        if (rescale) {
+          const float f = exp2_fast(sig_new);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) st[nt][ct] *= f;
+          sig = 0.f;
+        } else {
+          sig = sig_new;
+        }
+        const T* sKc = sK[pb];
+        // pairs of row tiles; the next pair's K^T fragments are read while
+        // the current pair multiplies.  n~ gets sum_l w_l k_l: row tile nt
+        // is summed by wave nt % 4 (with the unscaled w)
+        constexpr int NG = NKL * NT / 2;
+        frag ka[2][2];
+        auto load_g = [&](int g, int b) __attribute__((always_inline)) {
+          const int kb = g / (NT / 2), nt0 = (g % (NT / 2)) * 2;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int nt = nt0 + q;
+            ka[b][q] = frag_rows(sKc, KST, kb * K, lg, lr, kcol + (nt >> 1) * 32 + (nt & 1) * 4);
+          }
+        };
+        float dn[NT / 4];
+#pragma unroll
+        for (int q = 0; q < NT / 4; ++q) dn[q] = 0.f;
+        load_g(0, 0);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          if (g + 1 < NG) load_g(g + 1, (g + 1) & 1);
+          const int kb = g / (NT / 2), nt0 = (g % (NT / 2)) * 2;
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) st[nt0 + q][ct] = M::mma(ka[g & 1][q], wv[ct][kb], st[nt0 + q][ct]);
+          if constexpr (!SN) {
+            // this wave's tile among nt0, nt0 + 1 (if any): wave-uniform
+            const int q = sw - (nt0 & 3);
+            if (q == 0 || q == 1) {
+              const frag kq = q == 0 ? ka[g & 1][0] : ka[g & 1][1];
+#pragma unroll
+              for (int e = 0; e < KL; ++e) dn[nt0 / 4] += sW[kb * K + krow<T>(lg, e)] * (float)kq[e];
+            }
+          }
+        }
+        const float alpha = exp2_fast(la);
+        if constexpr (SN) {
+          if (sw == 0) {
+            float x = sW[lane];
+#pragma unroll
+            for (int d = 32; d > 0; d >>= 1) x += __shfl_xor(x, d, 64);
+            if (lane == 0) put_n(pb ^ 1, 0, alpha * sNf[pb][0] + x);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < NT / 4; ++q) {
+            const float x = sum_lane_groups(dn[q]);
+            const int r = perm_row<T>(4 * q + sw, lr);
+            if (lg == 0) put_n(pb ^ 1, r, alpha * sNf[pb][r] + x);
+          }
+        }
+      }
+      (void)sA2;
+    }
+  }
+  __syncthreads();
+  if (sc == p.NS - 1 && p.C_out) {
+    float* Sdst = p.C_out + (size_t)bh * CS;
+    const float f = exp2_fast(sig);
+    int so = soff;
+    asm volatile("" : "+v"(so));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Sdst[so + perm_row_uni<T>(nt, i) * DV + ct * 16] = st[nt][ct][i] * f;
+  }
+  } else {
+  // ------------------------------------------------------------ helper waves
+  // prime: the first chunk in LDS, the second one's loads in flight
+  h_load(c_begin);
+  h_store(0);
+  if (hw == 0) h_gates(0);
+  if (c_begin + 1 < c_end) h_load(c_begin + 1);
+  for (int c = c_begin; c < c_end; ++c) {
+    const int pb = (c - c_begin) & 1;  // buffer / set of this chunk
+    const bool more = c + 1 < c_end;
+    const bool need_update = more || (sc == p.NS - 1);
+    __syncthreads();  // A
+    {
+      const float* sA2 = sA2b[pb];
+      const float* sM2 = sM2b[pb];
+      const T* sKc = sK[pb];
+      // score tiles (key tile lt, query tile jt): the k-th tile of helper hw
+      // is k 4 + hw for even k, k 4 + 3 - hw for odd k; the first is (0, hw),
+      // which also sums n~ . q_j of query tile hw
+      auto tile_of = [](int ti, int& lt, int& jt) __attribute__((always_inline)) {
+        lt = 0;
+        jt = ti;
+        int rem = NJT;
+        while (jt >= rem) {
+          jt -= rem;
+          ++lt;
+          --rem;
+        }
+        jt += lt;
+      };
+      auto scores = [&](auto nuc) __attribute__((always_inline)) {
+        constexpr int NU = decltype(nuc)::value;
+        int lt[NU], jt[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) tile_of(u * 4 + ((u & 1) ? 3 - hw : hw), lt[u], jt[u]);
+        float fac[NU][4];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const int j = jt[u] * 16 + lr;
+          const float m2 = sM2[j];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int l = lt[u] * 16 + 4 * lg + i;
+            fac[u][i] = (l <= j) ? exp2_fast(sA2[l] - m2) : 0.f;
+          }
+        }
+        f32x4 pt[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) pt[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // fragments of k-block kb + 1 are read while those of kb multiply
+        frag kf[2][NU], qj[2][NU];
+        auto load_kb = [&](int kb, int b) __attribute__((always_inline)) {
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            kf[b][u] = M::load(&sKc[(lt[u] * 16 + lr) * KST + kb * K + KL * lg]);
+            qj[b][u] = M::load(&sQ[(jt[u] * 16 + lr) * QS + kb * K + KL * lg]);
+          }
+        };
+        load_kb(0, 0);
+#pragma unroll
+        for (int kb = 0; kb < DQK / K; ++kb) {
+          if (kb + 1 < DQK / K) load_kb(kb + 1, (kb + 1) & 1);
+#pragma unroll
+          for (int u = 0; u < NU; ++u) pt[u] = M::mma(kf[kb & 1][u], qj[kb & 1][u], pt[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const int j = jt[u] * 16 + lr;
+          float x[4], dsum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[i] = pt[u][i] * fac[u][i];
+            dsum += SN ? fac[u][i] : x[i];
+          }
+          store4f(&sP[j * PS + kpos4<T>(lt[u] * 16 + 4 * lg)], x[0], x[1], x[2], x[3]);
+          const float ds = sum_lane_groups(dsum);
+          if (lg == 0) sDenPart[lt[u] * L + j] = ds;
+        }
+      };
+      if (hw < 2) scores(std::integral_constant<int, 3>{});
+      else scores(std::integral_constant<int, 2>{});
+      __syncthreads();  // B
+      if (more) {
+        h_store(pb ^ 1);  // Q, K, V of the next chunk (loaded during the previous one)
+        if (hw == 0) h_gates(pb ^ 1);
+      }
+      if (c + 2 < c_end) h_load(c + 2);  // the chunk after: in flight during the rest
+    }
+  }
+  __syncthreads();
+  if (slice == 0 && sc == p.NS - 1) {
+    const int s_end = (c_end - c_begin) & 1;  // set holding n~ after the last chunk
+    if (p.n_out) {
+      if constexpr (SN) {
+        if (ht == 0) p.n_out[bh] = sNf[s_end][0];
+      } else {
+        for (int r = ht; r < DQK; r += 256) p.n_out[(size_t)bh * DQK + r] = sNf[s_end][r];
+      }
+    }
+    if (w == 4 && lane == 0 && p.m_out) p.m_out[bh] = m_prev * kLn2;
+  }
+  }
+}
+
 // s_waitcnt with only a vmcnt limit (gfx9 encoding, expcnt and lgkmcnt left
 // at their no-wait maxima).
 template <int N>
@@ -1609,7 +2085,16 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
   if (!p.h) return hipGetLastError();  // state passes only (the backward's recompute)
   dim3 g3((unsigned)(BH * p.nslices * p.NS));
   if (ev0) (void)hipEventRecord(ev0, stream);
-  if constexpr (GN)
+  // the xLSTM-7B head shape (d_qk 256, one memory block, 128-column slices):
+  // the wave-specialised form of pass 3
+  constexpr bool WS = std::is_same<T, __bf16>::value && DQK == 256 && NB == 1 && WC * NCG == 128 && L == 64 &&
+                      !RET && !GN && !PB;
+  if constexpr (WS) {
+    if (p.o_pre)
+      hipLaunchKernelGGL((chunk_kernel_ws<true, SN>), g3, dim3(512), 0, stream, p);
+    else
+      hipLaunchKernelGGL((chunk_kernel_ws<false, SN>), g3, dim3(512), 0, stream, p);
+  } else if constexpr (GN)
     hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, false, true>), g3, dim3(NTH), 0, stream, p);
   else if (!RET && p.o_pre)
     hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, !RET, false, SN, PB>), g3, dim3(NTH), 0,
