@@ -29,10 +29,11 @@ achieved = algorithmic bytes (or flops) per call / that time.  Its
 ``main_kernel`` part gives the same for the per-chunk output kernel alone,
 from events the library records right before and after it
 (mlstm_set_profile_events).  ``traffic`` sums the committed rocprofv3
-FETCH_SIZE / WRITE_SIZE readings of the call's kernels.  The decode and
-variant legs run before the prefill leg, so that the prefill's warm-up and
-timed steps find the GPU at its steady clocks.  ``cpu_baseline`` times the
-fp64 CPU oracle on the host cores on a bounded sample of the same workload.
+FETCH_SIZE / WRITE_SIZE readings of the call's kernels.  The variant and
+decode legs run before the prefill leg (the decode leg right before it), so
+that the prefill's warm-up and timed steps find the GPU at its steady
+clocks.  ``cpu_baseline`` times the fp64 CPU oracle on the host cores on a
+bounded sample of the same workload.
 """
 import argparse
 import hashlib
@@ -138,7 +139,9 @@ class _KernelEvents:
                 self.hip.hipEventDestroy(e)
 
 
-def bench_prefill(torch, mlstm, x, args, dev):
+def prepare_prefill(torch, mlstm, x, dev):
+    """Device buffers of the prefill leg: four input sets with the same
+    values, their outputs, the final state and the workspace."""
     spec = dict(B=1, H=8, T=8192, dqk=256, dv=512)
     sets = [x.to(dev)]
     for _ in range(3):  # distinct buffers with the same values
@@ -150,6 +153,12 @@ def bench_prefill(torch, mlstm, x, args, dev):
     st = (torch.empty(B, H, 1, dqk, dv, device=dev), torch.empty(B, H, dqk, device=dev),
           torch.empty(B, H, device=dev))
     ws = torch.empty(mlstm.chunkwise_workspace_bytes(B, H, T, dqk, dv), dtype=torch.uint8, device=dev)
+    return dict(spec=spec, sets=sets, hs=hs, st=st, ws=ws)
+
+
+def bench_prefill(torch, mlstm, prep, args, dev):
+    spec, sets, hs, st, ws = (prep[k] for k in ("spec", "sets", "hs", "st", "ws"))
+    B, H, T, dqk, dv = (spec[k] for k in ("B", "H", "T", "dqk", "dv"))
 
     def call(i):
         g = sets[i % len(sets)]
@@ -525,7 +534,8 @@ def main():
     if args.only:
         print("bench: only %s" % args.only, file=sys.stderr, flush=True)
         if args.only == "prefill":
-            r = bench_prefill(torch, mlstm, workload("xlstm7b_prefill_T8192"), args, dev)
+            r = bench_prefill(torch, mlstm, prepare_prefill(torch, mlstm, workload("xlstm7b_prefill_T8192"), dev),
+                              args, dev)
             r.pop("spec")
         elif args.only == "decode":
             r = bench_decode(torch, mlstm, workload, args, dev)
@@ -537,21 +547,24 @@ def main():
             r = copy_calibration(torch, dev)
         print(json.dumps(dict(leg=args.only, **r)))
         return
-    # The decode and variant legs run first: the headline prefill leg then
-    # starts on a GPU that has been busy for about a second (steady clocks),
-    # as in continuous service, instead of on one that just woke up.  Its W
-    # warm-up and K timed steps are unchanged.
-    print("bench: decode xlstm7b_decode_B256 steps=%d" % args.decode_steps, file=sys.stderr, flush=True)
-    dc = bench_decode(torch, mlstm, workload, args, dev)
+    # The prefill's buffers are set up first and the decode leg (45 ms of
+    # continuous GPU work) runs right before the prefill leg, so that the
+    # prefill's warm-up and timed steps find the GPU at its steady clocks:
+    # after a host-side pause of a few milliseconds this GPU needs about 20 ms
+    # of work to return to them (measured: pass 3 of the prefill takes ~100 us
+    # per call for its first 50 calls after a 1 s pause, 86 us after that).
+    x = workload("xlstm7b_prefill_T8192")
+    prep = prepare_prefill(torch, mlstm, x, dev)
     var = []
     if args.variant_steps > 0:
         print("bench: retention and block-diagonal workloads, %d calls each" % args.variant_steps,
               file=sys.stderr, flush=True)
         var = bench_variants(torch, mlstm, workload, args, dev)
+    print("bench: decode xlstm7b_decode_B256 steps=%d" % args.decode_steps, file=sys.stderr, flush=True)
+    dc = bench_decode(torch, mlstm, workload, args, dev)
     print("bench: prefill xlstm7b_prefill_T8192 steps=%d warmup=%d" % (args.steps, args.warmup),
           file=sys.stderr, flush=True)
-    x = workload("xlstm7b_prefill_T8192")
-    pf = bench_prefill(torch, mlstm, x, args, dev)
+    pf = bench_prefill(torch, mlstm, prep, args, dev)
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
