@@ -79,7 +79,11 @@ def source_sha(*names):
 
 
 # the launches of one prefill call, in order
-PREFILL_KERNELS = ("local_state_kernel", "superchunk_scan_kernel", "chunk_kernel")
+PREFILL_KERNELS = ("local_state_kernel", "superchunk_scan_kernel", "chunk_kernel_ws")
+# the launches of one backward call of the 7B workload (the forward's state
+# passes, then the backward kernels)
+BACKWARD_KERNELS = ("bwd_chunk_states_kernel", "bwd_scores_kernel", "bwd_dq_kernel", "bwd_scan_kernel",
+                    "bwd_dkv_kernel", "bwd_gate_total_kernel", "bwd_gate_kernel")
 
 
 def traffic_from_profiles(kernels, sha):
@@ -493,15 +497,20 @@ def cpu_baseline(x, sample_tokens):
 
 
 def variant_line(v):
-    """One retention / block-diagonal record: throughput of the whole call
-    and the HBM and MFMA rooflines of its algorithmic work."""
+    """One retention / block-diagonal / backward record: throughput of the
+    whole call and the HBM and MFMA rooflines of its algorithmic work."""
     s = v["call_ms"] * 1e-3
     gbs = v["bytes"] / s / 1e9
     keep = {k: v[k] for k in v if k not in ("call_ms", "kernel_ms", "wall_ms", "bytes", "flops", "tokens")}
+    traffic = None
+    if v["workload"] == "xlstm7b_prefill_T8192_backward":
+        fwd = traffic_from_profiles(PREFILL_KERNELS[:2], source_sha("chunkwise.hip", "common.h"))
+        bwd = traffic_from_profiles(BACKWARD_KERNELS, source_sha("backward.hip", "chunkwise.hip", "common.h"))
+        traffic = None if fwd is None or bwd is None else fwd + bwd
     return dict(keep, value=v["tokens"] / s, unit="tokens/s", ms_per_call=v["call_ms"],
                 wall_ms_per_call=v["wall_ms"], main_kernel_ms=v["kernel_ms"],
                 roofline=dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
-                              traffic=None, kernel="whole call (all launches)",
+                              traffic=traffic, kernel="whole call (all launches)",
                               mfma_frac=v["flops"] / s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                               algorithmic_bytes=v["bytes"], algorithmic_flops=v["flops"]))
 
