@@ -119,11 +119,20 @@ constexpr int lds_pad_res(int row_elems, int esize, int res) {
 #ifndef MLSTM_P1_ROWS
 #define MLSTM_P1_ROWS 256  // most state rows of a bf16 pass-1 tile
 #endif
+#ifndef MLSTM_P1_STAGES
+#define MLSTM_P1_STAGES 4  // LDS ring stages of pass 1 (3 to 6; loads run stages-1 k-steps ahead)
+#endif
 #ifndef MLSTM_P3_QRES
 #define MLSTM_P3_QRES 8
 #endif
 #ifndef MLSTM_P3_KRES
 #define MLSTM_P3_KRES 24
+#endif
+#ifndef MLSTM_P3_UPD
+#define MLSTM_P3_UPD 1  // K^T fragment groups read ahead in the 7B pass-3 state update
+#endif
+#ifndef MLSTM_P3_SCD
+#define MLSTM_P3_SCD 1  // k-blocks of score fragments read ahead in the 7B pass-3 helpers
 #endif
 
 template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool GN = false, bool PB = false>
@@ -979,23 +988,27 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
 // every SIMD see one wave that streams products while another wave on the same
 // SIMD does the loads, scores, normaliser and gate work:
 //   state waves 0..3  own all 256 state rows x 32 columns each (fp32, in MFMA
-//                     accumulator registers): readout S~^T q, P V, outputs,
-//                     state update.  No exchange between waves.
+//                     accumulator registers): readout S~^T q and n~ . q (hi +
+//                     lo bf16 rows of n~), P V, outputs, state update, and
+//                     the n~ update of 64 features each (by MFMA, w as hi +
+//                     lo bf16).  No exchange between waves.
 //   helper waves 4..7 stage the next chunk (global loads into registers,
 //                     then LDS), compute the chunk's causal score tiles with
 //                     their decay factors (P to LDS, fp32 row sums for the
-//                     denominator), n~ . q_j (hi + lo bf16 rows of n~, fused
-//                     with the score tile (0, j)), the n~ update and the gate
-//                     vectors of the next chunk (the m_prev chain).
+//                     denominator) and the gate vectors of the next chunk
+//                     (the m_prev chain).
 // K and V are double-buffered in LDS (the next chunk's go into the other
 // buffer while the state waves update from the current one), as are the
 // gate vectors and n~, so a chunk needs two work-group barriers:
 //   A: the chunk's Q, K, V, gate vectors and n~ are in LDS;
-//      state waves: readout; helpers: scores, n~ . q, P and den partials.
+//      state waves: readout, n~ . q; helpers: scores, P and den partials.
 //   B: P and the denominators are in LDS, Q is free;
-//      state waves: P V, outputs, update; helpers: the next chunk's Q, K, V
-//      and gate vectors into LDS, n~ of this chunk, then the loads of the
+//      state waves: P V, outputs, update, n~ of the next chunk; helpers: the
+//      next chunk's Q, K, V and gate vectors into LDS, then the loads of the
 //      chunk after.
+// The wave-uniform choices (which query tile a state wave takes n~ . q for,
+// which features it updates) are address offsets, never register selects,
+// and no LDS read is waited for inside a product loop.
 template <bool HAS_O, bool SN>
 __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
   using T = __bf16;
@@ -1016,8 +1029,9 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
   __shared__ __attribute__((aligned(16))) T sV[2][L * VS];
   __shared__ __attribute__((aligned(16))) T sP[L * PS];
   __shared__ __attribute__((aligned(16))) T sNh[2][2 * DQK];  // n~ as hi / lo bf16 rows, two sets
-  __shared__ float sNf[2][DQK];
-  __shared__ float sA2b[2][L], sM2b[2][L], sRSb[2][L], sCLb[2][L], sBTb[2][L], sWb[2][L];
+  __shared__ __attribute__((aligned(16))) float sNf[2][DQK];
+  __shared__ float sA2b[2][L], sM2b[2][L], sRSb[2][L], sCLb[2][L], sBTb[2][L];
+  __shared__ __attribute__((aligned(16))) float sWb[2][L];
   __shared__ float sDenPart[NJT * L];
   __shared__ float sDenInter[L];
   __shared__ float sAlphab[2];
@@ -1109,6 +1123,62 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
       *reinterpret_cast<uint4*>(&sV[kv][j * VS + col]) = *reinterpret_cast<const uint4*>(gv[it].v);
     }
   };
+  // n~ of the next chunk into set pb ^ 1: alpha n~ + sum_l w_l k_l over the
+  // 64 features [fw, fw + 64), by MFMA: K^T fragments of buffer pb times an
+  // all-columns B operand of w (its hi and lo bf16 parts, wk = w at this
+  // lane's fragment tokens krow(lg, 0..7) of each k-block), 4 MFMAs per
+  // 16-feature tile.  Two tiles at a time: their reads are issued first,
+  // then 8 MFMAs of 2 independent chains; the lanes of column 0 store 4
+  // features each.
+  auto n_update = [&](int pb, int fw, const float (&wk)[2][KL], float alpha) __attribute__((always_inline)) {
+    const T* sKc = sK[pb];
+    frag whi[NKL], wlo[NKL];
+#pragma unroll
+    for (int kb = 0; kb < NKL; ++kb)
+#pragma unroll
+      for (int e = 0; e < KL; ++e) {
+        const T hi = (T)wk[kb][e];
+        whi[kb][e] = hi;
+        wlo[kb][e] = (T)(wk[kb][e] - (float)hi);
+      }
+#pragma unroll
+    for (int t0 = 0; t0 < 4; t0 += 2) {
+      frag ka[2][NKL];
+      float4 nold[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int kb = 0; kb < NKL; ++kb)
+          ka[t][kb] = frag_rows(sKc, KST, kb * K, lg, lr, fw + 16 * (t0 + t) + 4 * (lr & 3));
+        nold[t] = *reinterpret_cast<const float4*>(&sNf[pb][fw + 16 * (t0 + t) + 4 * lg]);
+      }
+      f32x4 d[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int kb = 0; kb < NKL; ++kb) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) d[t] = M::mma(ka[t][kb], whi[kb], d[t]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) d[t] = M::mma(ka[t][kb], wlo[kb], d[t]);
+      }
+      if (lr == 0) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int r = fw + 16 * (t0 + t) + 4 * lg;  // features r .. r + 3
+          const float x[4] = {alpha * nold[t].x + d[t][0], alpha * nold[t].y + d[t][1], alpha * nold[t].z + d[t][2],
+                              alpha * nold[t].w + d[t][3]};
+          *reinterpret_cast<float4*>(&sNf[pb ^ 1][r]) = make_float4(x[0], x[1], x[2], x[3]);
+          T hi[4], lo[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hi[i] = (T)x[i];
+            lo[i] = (T)(x[i] - (float)hi[i]);
+          }
+          *reinterpret_cast<uint2*>(&sNh[pb ^ 1][r]) = *reinterpret_cast<const uint2*>(hi);
+          *reinterpret_cast<uint2*>(&sNh[pb ^ 1][DQK + r]) = *reinterpret_cast<const uint2*>(lo);
+        }
+      }
+    }
+  };
   // gate vectors of the loaded chunk into set gb (helper 0, one lane per token)
   auto h_gates = [&](int gb) __attribute__((always_inline)) {
     const float a = __uint_as_float(rga), g = __uint_as_float(rgg), b = __uint_as_float(rgb);
@@ -1170,32 +1240,25 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
       for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) acc[jt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // n~ . q_j of query tile sw alongside: rows 0 (hi) and 1 (lo) of an A
-      // tile of n~ times this wave's Q fragments of that tile
+      // n~ . q_j of query tile sw alongside: the A rows alternate the hi and
+      // lo bf16 parts of n~ (only output rows 0 and 1 are used), B is this
+      // wave's query tile read once more at a wave-uniform offset (no
+      // register selects)
       f32x4 pn = {0.f, 0.f, 0.f, 0.f};
-      const T* nh = sNh[pb];
+      const T* nhl = &sNh[pb][(lr & 1) * DQK + KL * lg];
+      const T* qsw = &sQ[(sw * 16 + lr) * QS + KL * lg];
 #pragma unroll
       for (int kk = 0; kk < DQK / K; ++kk) {
         frag qf[NJT];
 #pragma unroll
         for (int jt = 0; jt < NJT; ++jt) qf[jt] = M::load(&sQ[(jt * 16 + lr) * QS + kk * K + KL * lg]);
-        frag nf = M::zero();
-        if constexpr (!SN) {
-          const frag f = M::load(&nh[(lr & 1) * DQK + kk * K + KL * lg]);
-          nf = lr < 2 ? f : M::zero();
-        }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const frag sf = StateFrag<T, NT, CT>::get(st, kk, ct);
 #pragma unroll
           for (int jt = 0; jt < NJT; ++jt) acc[jt][ct] = M::mma(sf, qf[jt], acc[jt][ct]);
         }
-        if constexpr (!SN) {
-          frag qs = qf[0];
-#pragma unroll
-          for (int jt = 1; jt < NJT; ++jt) qs = sw == jt ? qf[jt] : qs;  // wave-uniform select
-          pn = M::mma(nf, qs, pn);
-        }
+        if constexpr (!SN) pn = M::mma(M::load(nhl + kk * K), M::load(qsw + kk * K), pn);
       }
       if constexpr (SN) {  // the inter part of the denominator is n~ itself
         if (sw == 0) sDenInter[lane] = sNf[pb][0];
@@ -1257,12 +1320,18 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
         const float sig_new = sig + la;
         const bool rescale = sig_new < -64.f;  // wave-uniform, rare
         const float wscale = exp2_fast(rescale ? 0.f : -sig_new);
+        // w of this lane's fragment rows
+        float wk[NKL][KL];
+#pragma unroll
+        for (int kb = 0; kb < NKL; ++kb)
+#pragma unroll
+          for (int e = 0; e < KL; ++e) wk[kb][e] = sW[kb * K + krow<T>(lg, e)];
         frag wv[CT][NKL];
 #pragma unroll
         for (int kb = 0; kb < NKL; ++kb) {
           float wls[KL];
 #pragma unroll
-          for (int e = 0; e < KL; ++e) wls[e] = sW[kb * K + krow<T>(lg, e)] * wscale;
+          for (int e = 0; e < KL; ++e) wls[e] = wk[kb][e] * wscale;
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) wv[ct][kb] = scale_frag(vf[ct][kb], wls);
         }
@@ -1277,11 +1346,11 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
           sig = sig_new;
         }
         const T* sKc = sK[pb];
-        // pairs of row tiles; the next pair's K^T fragments are read while
-        // the current pair multiplies.  n~ gets sum_l w_l k_l: row tile nt
-        // is summed by wave nt % 4 (with the unscaled w)
+        // pairs of row tiles; the K^T fragments of the next UD pairs are
+        // read while the current pair multiplies
         constexpr int NG = NKL * NT / 2;
-        frag ka[2][2];
+        constexpr int UD = MLSTM_P3_UPD, UB = UD + 1;
+        frag ka[UB][2];
         auto load_g = [&](int g, int b) __attribute__((always_inline)) {
           const int kb = g / (NT / 2), nt0 = (g % (NT / 2)) * 2;
 #pragma unroll
@@ -1290,28 +1359,18 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
             ka[b][q] = frag_rows(sKc, KST, kb * K, lg, lr, kcol + (nt >> 1) * 32 + (nt & 1) * 4);
           }
         };
-        float dn[NT / 4];
 #pragma unroll
-        for (int q = 0; q < NT / 4; ++q) dn[q] = 0.f;
-        load_g(0, 0);
+        for (int g = 0; g < UD; ++g) load_g(g, g);
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-          if (g + 1 < NG) load_g(g + 1, (g + 1) & 1);
+          if (g + UD < NG) load_g(g + UD, (g + UD) % UB);
           const int kb = g / (NT / 2), nt0 = (g % (NT / 2)) * 2;
 #pragma unroll
           for (int q = 0; q < 2; ++q)
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) st[nt0 + q][ct] = M::mma(ka[g & 1][q], wv[ct][kb], st[nt0 + q][ct]);
-          if constexpr (!SN) {
-            // this wave's tile among nt0, nt0 + 1 (if any): wave-uniform
-            const int q = sw - (nt0 & 3);
-            if (q == 0 || q == 1) {
-              const frag kq = q == 0 ? ka[g & 1][0] : ka[g & 1][1];
-#pragma unroll
-              for (int e = 0; e < KL; ++e) dn[nt0 / 4] += sW[kb * K + krow<T>(lg, e)] * (float)kq[e];
-            }
-          }
+            for (int ct = 0; ct < CT; ++ct) st[nt0 + q][ct] = M::mma(ka[g % UB][q], wv[ct][kb], st[nt0 + q][ct]);
         }
+        // n~ of the next chunk: features [64 sw, 64 sw + 64) from this wave
         const float alpha = exp2_fast(la);
         if constexpr (SN) {
           if (sw == 0) {
@@ -1321,12 +1380,7 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
             if (lane == 0) put_n(pb ^ 1, 0, alpha * sNf[pb][0] + x);
           }
         } else {
-#pragma unroll
-          for (int q = 0; q < NT / 4; ++q) {
-            const float x = sum_lane_groups(dn[q]);
-            const int r = perm_row<T>(4 * q + sw, lr);
-            if (lg == 0) put_n(pb ^ 1, r, alpha * sNf[pb][r] + x);
-          }
+          n_update(pb, 64 * sw, wk, alpha);
         }
       }
       (void)sA2;
@@ -1394,8 +1448,10 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
         f32x4 pt[NU];
 #pragma unroll
         for (int u = 0; u < NU; ++u) pt[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // fragments of k-block kb + 1 are read while those of kb multiply
-        frag kf[2][NU], qj[2][NU];
+        // fragments of k-blocks kb + 1 .. kb + SD are read while those of kb
+        // multiply
+        constexpr int SD = MLSTM_P3_SCD, SB = SD + 1;
+        frag kf[SB][NU], qj[SB][NU];
         auto load_kb = [&](int kb, int b) __attribute__((always_inline)) {
 #pragma unroll
           for (int u = 0; u < NU; ++u) {
@@ -1403,12 +1459,13 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
             qj[b][u] = M::load(&sQ[(jt[u] * 16 + lr) * QS + kb * K + KL * lg]);
           }
         };
-        load_kb(0, 0);
+#pragma unroll
+        for (int kb = 0; kb < SD; ++kb) load_kb(kb, kb);
 #pragma unroll
         for (int kb = 0; kb < DQK / K; ++kb) {
-          if (kb + 1 < DQK / K) load_kb(kb + 1, (kb + 1) & 1);
+          if (kb + SD < DQK / K) load_kb(kb + SD, (kb + SD) % SB);
 #pragma unroll
-          for (int u = 0; u < NU; ++u) pt[u] = M::mma(kf[kb & 1][u], qj[kb & 1][u], pt[u]);
+          for (int u = 0; u < NU; ++u) pt[u] = M::mma(kf[kb % SB][u], qj[kb % SB][u], pt[u]);
         }
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
@@ -1703,12 +1760,16 @@ __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
   constexpr bool BF = sizeof(T) == 2;
   static_assert(L % KS == 0, "superchunks of whole k-steps");
 
-  // ring of 4 stages (separate arrays, so that the compiler's own wait
+  // ring of NSTG stages (separate arrays, so that the compiler's own wait
   // tracking tells their loads apart) and w of the superchunk
+  constexpr int NSTG = MLSTM_P1_STAGES;
+  static_assert(NSTG >= 3 && NSTG <= 6, "ring stages");
   __shared__ __attribute__((aligned(1024))) unsigned char ring0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char ring1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char ring2[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char ring3[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring3[NSTG > 3 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring4[NSTG > 4 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring5[NSTG > 5 ? C::STAGE : 16];
   __shared__ __attribute__((aligned(16))) float sw[C::GLMAX];
   __shared__ float stot[16];
   __shared__ float smax[NWP];
@@ -1717,7 +1778,9 @@ __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
     if constexpr (b == 0) return ring0;
     else if constexpr (b == 1) return ring1;
     else if constexpr (b == 2) return ring2;
-    else return ring3;
+    else if constexpr (b == 3) return ring3;
+    else if constexpr (b == 4) return ring4;
+    else return ring5;
   };
 
   const int tid = threadIdx.x;
@@ -1795,20 +1858,24 @@ __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
   };
   constexpr int NV = JA;  // vm operations of one step of one wave
 
-  // gate inputs, then the first four steps in flight, then w of the
+  // gate inputs, then the first NSTG steps in flight, then w of the
   // superchunk into LDS (the gate loads are issued first, so waiting for
   // them does not wait for the ring)
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
   {
     GateRegs<NWP> r;
     gate_loads<T, RET, NWP>(p, L, bh, sc, w, lane, r);
     issue(0, I0{});
     issue(1, I1{});
     issue(2, I2{});
-    issue(3, I3{});
+    if constexpr (NSTG > 3) issue(3, I3{});
+    if constexpr (NSTG > 4) issue(4, I4{});
+    if constexpr (NSTG > 5) issue(5, I5{});
     gate_compute<T, RET, NWP, false, true>(p, L, bh, sc, w, lane, tid, r, sw, stot, smax);
   }
 
@@ -1874,45 +1941,64 @@ __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
     }
   };
 
-  // ---- Software pipeline over k-steps, stage of step c = c % 4.  Step 0's
-  // fragments are in registers before the loop.  Iteration c: once this
+  // ---- Software pipeline over k-steps, stage of step c = c % NSTG.  Step
+  // 0's fragments are in registers before the loop.  Iteration c: once this
   // wave's loads of step c + 1 have landed, a barrier publishes that stage
   // (and guarantees every wave has read step c's stage into registers, so
-  // step c + 4 can go into it), then step c + 1's fragments are read while
-  // the MFMAs of step c run, and scaled by w after them.  Steps past the end
-  // (the loop runs in groups of 4) only issue and wait.
+  // step c + NSTG can go into it), then step c + 1's fragments are read
+  // while the MFMAs of step c run, and scaled by w after them.  Steps past
+  // the end (the loop runs in groups of NSTG) only issue and wait.
   StepFrags F0, F1;
-  wait_vmcnt<3 * NV>();  // step 0 landed
+  wait_vmcnt<(NSTG - 1) * NV>();  // step 0 landed
   lds_barrier();
   load_step(I0{}, F0);
   scale_step(0, F0);
   // body<true>: steps c and c + 1 both exist (no branch, so the next step's
   // fragment reads can overlap this step's MFMAs); body<false>: the last
-  // group of 4, where either may be past the end.
+  // group of NSTG, where either may be past the end.
   auto body = [&](auto fullc, int c, auto bidx, StepFrags& cur, StepFrags& nxt) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(fullc)::value;
     constexpr int b = decltype(bidx)::value;
-    using B1 = std::integral_constant<int, (b + 1) % 4>;
-    wait_vmcnt<2 * NV>();
+    using B1 = std::integral_constant<int, (b + 1) % NSTG>;
+    wait_vmcnt<(NSTG - 2) * NV>();
     lds_barrier();
-    issue(c + 4, bidx);
+    issue(c + NSTG, bidx);
     if (FULL || c + 1 < NSTEP) load_step(B1{}, nxt);
     if (FULL || c < NSTEP) mma_step(cur);
     if (FULL || c + 1 < NSTEP) scale_step(c + 1, nxt);
   };
+  // one group of NSTG steps; the fragment sets alternate, so a group of odd
+  // size starts on the set the previous group did not
+  auto group = [&](auto fullc, int c, auto odd) __attribute__((always_inline)) {
+    constexpr bool O = decltype(odd)::value;
+    StepFrags& A = O ? F1 : F0;
+    StepFrags& B = O ? F0 : F1;
+    body(fullc, c, I0{}, A, B);
+    body(fullc, c + 1, I1{}, B, A);
+    body(fullc, c + 2, I2{}, A, B);
+    if constexpr (NSTG > 3) body(fullc, c + 3, I3{}, B, A);
+    if constexpr (NSTG > 4) body(fullc, c + 4, I4{}, A, B);
+    if constexpr (NSTG > 5) body(fullc, c + 5, I5{}, B, A);
+  };
   using Full = std::true_type;
   using Tail = std::false_type;
   int c = 0;
-  for (; c + 4 < NSTEP; c += 4) {
-    body(Full{}, c, I0{}, F0, F1);
-    body(Full{}, c + 1, I1{}, F1, F0);
-    body(Full{}, c + 2, I2{}, F0, F1);
-    body(Full{}, c + 3, I3{}, F1, F0);
+  if constexpr (NSTG % 2 == 0) {
+    for (; c + NSTG < NSTEP; c += NSTG) group(Full{}, c, std::false_type{});
+    group(Tail{}, c, std::false_type{});
+  } else {
+    // odd ring: two groups per loop trip keep the fragment sets in step
+    for (; c + 2 * NSTG < NSTEP; c += 2 * NSTG) {
+      group(Full{}, c, std::false_type{});
+      group(Full{}, c + NSTG, std::true_type{});
+    }
+    if (c + NSTG < NSTEP) {
+      group(Full{}, c, std::false_type{});
+      group(Tail{}, c + NSTG, std::true_type{});
+    } else {
+      group(Tail{}, c, std::false_type{});
+    }
   }
-  body(Tail{}, c, I0{}, F0, F1);
-  body(Tail{}, c + 1, I1{}, F1, F0);
-  body(Tail{}, c + 2, I2{}, F0, F1);
-  body(Tail{}, c + 3, I3{}, F1, F0);
   wait_vmcnt<0>();  // no load into the ring in flight past this point
 
   // ---- outputs: slot sc + 1 of the workspace holds superchunk sc's local state
