@@ -1030,7 +1030,8 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
   __shared__ __attribute__((aligned(16))) T sP[L * PS];
   __shared__ __attribute__((aligned(16))) T sNh[2][2 * DQK];  // n~ as hi / lo bf16 rows, two sets
   __shared__ __attribute__((aligned(16))) float sNf[2][DQK];
-  __shared__ float sA2b[2][L], sM2b[2][L], sRSb[2][L], sCLb[2][L], sBTb[2][L];
+  __shared__ __attribute__((aligned(16))) float sA2b[2][L];
+  __shared__ float sM2b[2][L], sRSb[2][L], sCLb[2][L], sBTb[2][L];
   __shared__ __attribute__((aligned(16))) float sWb[2][L];
   __shared__ float sDenPart[NJT * L];
   __shared__ float sDenInter[L];
@@ -1277,6 +1278,29 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int kb = 0; kb < NKL; ++kb) vf[ct][kb] = frag_rows(sVc, VS, kb * K, lg, lr, vcol + ct * 16);
+      // the normaliser of this lane's tokens, every read first
+      float rsj[NJT], invj[NJT];
+      {
+        float d_in[NJT], d_bt[NJT], d_cl[NJT], d_pt[NJT][NJT];
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt) {
+          const int j = jt * 16 + lr;
+          rsj[jt] = sRS[j];
+          d_in[jt] = sDenInter[j];
+          d_bt[jt] = sBT[j];
+          d_cl[jt] = sCL[j];
+#pragma unroll
+          for (int t = 0; t < NJT; ++t) d_pt[jt][t] = sDenPart[t * L + j];
+        }
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt) {
+          float den = rsj[jt] * d_in[jt] + d_bt[jt];
+#pragma unroll
+          for (int t = 0; t < NJT; ++t) den += d_pt[jt][t];
+          invj[jt] = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), d_cl[jt]));
+        }
+      }
+      const float sig_scale = exp2_fast(sig);
       // P V, combine, outputs
 #pragma unroll
       for (int jt = 0; jt < NJT; ++jt) {
@@ -1292,12 +1316,8 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
           }
         }
         const int j = jt * 16 + lr;
-        const float rs = sRS[j];
-        const float rs_state = rs * exp2_fast(sig);
-        float den = rs * sDenInter[j] + sBT[j];
-#pragma unroll
-        for (int t = 0; t < NJT; ++t) den += sDenPart[t * L + j];
-        const float inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), sCL[j]));
+        const float rs_state = rsj[jt] * sig_scale;
+        const float inv = invj[jt];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           float o[4] = {1.f, 1.f, 1.f, 1.f};
@@ -1434,15 +1454,26 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
         int lt[NU], jt[NU];
 #pragma unroll
         for (int u = 0; u < NU; ++u) tile_of(u * 4 + ((u & 1) ? 3 - hw : hw), lt[u], jt[u]);
+        // decay factors 2^(a_l - M_j) of this lane's 4 tokens l per tile:
+        // every read first (unconditional, 16-byte), then the masked exps
         float fac[NU][4];
+        {
+          float m2[NU];
+          float4 a4[NU];
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          const int j = jt[u] * 16 + lr;
-          const float m2 = sM2[j];
+          for (int u = 0; u < NU; ++u) {
+            m2[u] = sM2[jt[u] * 16 + lr];
+            a4[u] = *reinterpret_cast<const float4*>(&sA2[lt[u] * 16 + 4 * lg]);
+          }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int l = lt[u] * 16 + 4 * lg + i;
-            fac[u][i] = (l <= j) ? exp2_fast(sA2[l] - m2) : 0.f;
+          for (int u = 0; u < NU; ++u) {
+            const int j = jt[u] * 16 + lr;
+            const float av[4] = {a4[u].x, a4[u].y, a4[u].z, a4[u].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int l = lt[u] * 16 + 4 * lg + i;
+              fac[u][i] = (l <= j) ? exp2_fast(av[i] - m2[u]) : 0.f;
+            }
           }
         }
         f32x4 pt[NU];
