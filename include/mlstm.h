@@ -235,18 +235,33 @@ int retention_chunkwise_fwd(int B, int H, int T, int d_k, int d_v, int chunk,
                             size_t workspace_bytes, void* stream);
 
 /*
+ * Workspace size in bytes for retention_chunkwise_groupnorm_fwd: that of
+ * retention_chunkwise_fwd, plus B*H*T*d_v fp32 when d_v is wider than one
+ * work-group (0, with the error message set, for arguments it does not take).
+ */
+size_t retention_chunkwise_groupnorm_workspace_bytes(int B, int H, int T, int d_k,
+                                                     int d_v, int chunk,
+                                                     mlstm_dtype dt);
+
+/*
  * retention_chunkwise_fwd with the per-head group norm of the "Multi-Scale
- * Retention (MSR)" section of the "Edifice.Attention.RetNet" page fused into
- * the output write: each output row of each head is normalised over its d_v
+ * Retention (MSR)" section of the "Edifice.Attention.RetNet" page applied to
+ * the outputs: each output row of each head is normalised over its d_v
  * channels,
  *     out = (y - mean(y)) / sqrt(var(y) + gn_eps) * gn_weight + gn_bias
  * with y the retention output, mean and (biased) variance over the row, and
  * per-channel gn_weight, gn_bias [H*d_v] fp32 (NULL: 1 and 0), as a group
  * norm with one group per head over the H*d_v channels.  Statistics are
- * taken in fp32 before rounding to dt.  Same arguments, workspace and
- * S0/S_out as retention_chunkwise_fwd; gn_eps > 0.  Requires d_v = 64 for
- * d_k = 64 and d_v = 128 for d_k = 128 (one work-group holds a whole row);
- * other shapes return MLSTM_E_UNSUPPORTED.
+ * taken in fp32 before rounding to dt.  Same arguments and S0/S_out as
+ * retention_chunkwise_fwd; gn_eps > 0; the workspace size comes from
+ * retention_chunkwise_groupnorm_workspace_bytes.  Requires d_v a multiple of
+ * W, the d_v width one work-group holds (64 for d_k = 64, 128 for d_k = 128).
+ * With d_v = W the norm is applied in the output write.  With d_v > W the
+ * output pass writes the unnormalised rows in fp32 to the workspace and one
+ * more kernel normalises them into out (the same arithmetic, at the cost of
+ * one fp32 write and read of the outputs).  Other shapes return
+ * MLSTM_E_UNSUPPORTED; more than 2^33 output rows (B*H*T) return
+ * MLSTM_E_SHAPE.
  */
 int retention_chunkwise_groupnorm_fwd(int B, int H, int T, int d_k, int d_v,
                                       int chunk, mlstm_dtype dt, const void* q,

@@ -25,7 +25,8 @@ EXPORTS = ("mlstm_abi_version", "mlstm_last_error", "mlstm_set_profile_events",
            "mlstm_chunkwise_workspace_bytes",
            "mlstm_chunkwise_fwd", "mlstm_chunkwise_fwd_ex", "mlstm_step", "mlstm_step_ex",
            "retention_chunkwise_workspace_bytes",
-           "retention_chunkwise_fwd", "retention_chunkwise_groupnorm_fwd", "retention_step",
+           "retention_chunkwise_fwd", "retention_chunkwise_groupnorm_workspace_bytes",
+           "retention_chunkwise_groupnorm_fwd", "retention_step",
            "mlstm_chunkwise_bwd_workspace_bytes", "mlstm_chunkwise_bwd",
            "retention_chunkwise_bwd_workspace_bytes", "retention_chunkwise_bwd",
            "mlstm_chunkwise_fwd_noalloc", "mlstm_noalloc_scratch_bytes")
@@ -69,6 +70,8 @@ def lib():
     L.retention_chunkwise_workspace_bytes.restype = sz
     L.retention_chunkwise_fwd.argtypes = [i] * 7 + [vp] * 3 + [fp] * 3 + [vp, vp, sz, vp]
     L.retention_chunkwise_fwd.restype = i
+    L.retention_chunkwise_groupnorm_workspace_bytes.argtypes = [i] * 6 + [i]
+    L.retention_chunkwise_groupnorm_workspace_bytes.restype = sz
     L.retention_chunkwise_groupnorm_fwd.argtypes = ([i] * 7 + [vp] * 3 + [fp] * 5 + [ctypes.c_float] +
                                                     [vp, vp, sz, vp])
     L.retention_chunkwise_groupnorm_fwd.restype = i
@@ -292,8 +295,8 @@ def retention_chunkwise_fwd(q, k, v, gamma=None, S0=None, chunk=64, return_state
                             S_out=None, workspace=None, groupnorm=None):
     """retention_chunkwise_fwd.  q,k [B,H,T,dk]; v [B,H,T,dv]; gamma [H] fp32
     or None (1 - 2^(-5-h)); S0 [B,H,dk,dv] fp32 or None.  Returns (out, S).
-    groupnorm = (weight [H*dv] or None, bias [H*dv] or None, eps) fuses the
-    per-head group norm of the outputs (retention_chunkwise_groupnorm_fwd)."""
+    groupnorm = (weight [H*dv] or None, bias [H*dv] or None, eps) applies the
+    per-head group norm to the outputs (retention_chunkwise_groupnorm_fwd)."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
@@ -311,10 +314,17 @@ def retention_chunkwise_fwd(q, k, v, gamma=None, S0=None, chunk=64, return_state
     if return_state:
         _need(S_out, "S_out", (B, H, dk, dv), torch.float32, dev)
     L = lib()
-    nbytes = L.retention_chunkwise_workspace_bytes(B, H, T, dk, dv, chunk, _DT[dt])
+    if groupnorm is None:
+        nbytes = L.retention_chunkwise_workspace_bytes(B, H, T, dk, dv, chunk, _DT[dt])
+    else:
+        nbytes = L.retention_chunkwise_groupnorm_workspace_bytes(B, H, T, dk, dv, chunk, _DT[dt])
     if nbytes == 0:
-        _check(L.retention_chunkwise_fwd(B, H, T, dk, dv, chunk, _DT[dt], *([None] * 7), None, 0, None),
-               "retention_chunkwise_fwd")
+        if groupnorm is None:
+            rc = L.retention_chunkwise_fwd(B, H, T, dk, dv, chunk, _DT[dt], *([None] * 7), None, 0, None)
+        else:
+            rc = L.retention_chunkwise_groupnorm_fwd(B, H, T, dk, dv, chunk, _DT[dt], *([None] * 8), None,
+                                                     ctypes.c_float(1.0), None, None, 0, None)
+        _check(rc, "retention_chunkwise_fwd")
     ws, wsb = _workspace(nbytes, dev, workspace)
     if groupnorm is not None:
         gw, gb, eps = groupnorm

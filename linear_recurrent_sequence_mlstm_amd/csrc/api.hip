@@ -568,21 +568,56 @@ int retention_chunkwise_fwd(int B, int H, int T, int d_k, int d_v, int chunk, ml
   return launch(pl, p, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Group-norm plan: the retention plan; a head wider than the fused variant's
+// work-group (d_v = nslices x W) adds an fp32 [B*H*T][d_v] array of
+// unnormalised outputs after the retention workspace.
+int plan_groupnorm(int B, int H, int T, int d_k, int d_v, int chunk, mlstm_dtype dt, Plan* pl,
+                   size_t* gn_off) {
+  const int rc = plan_chunkwise(B, H, T, d_k, d_v, 1, chunk, dt, true, pl);
+  if (rc != MLSTM_OK) return rc;
+  mlstm::ChunkVariant gv;
+  if (!mlstm::find_retention_groupnorm_variant(dt, d_k, chunk, &gv) || d_v % gv.w)
+    return fail(MLSTM_E_UNSUPPORTED, "group norm needs d_v a multiple of %d for d_k=%d (got d_v=%d)",
+                mlstm::find_retention_groupnorm_variant(dt, d_k, chunk, &gv) ? gv.w : 0, d_k, d_v);
+  pl->var.launch = gv.launch;  // same plan as without the norm
+  if ((long long)B * H * T >= (1LL << 33))
+    return fail(MLSTM_E_SHAPE, "B * H * T = %lld output rows is too many for the group norm",
+                (long long)B * H * T);
+  *gn_off = 0;
+  if (d_v > gv.w) {
+    *gn_off = pl->bytes;
+    pl->bytes += align256((size_t)B * H * T * d_v * sizeof(float));
+  }
+  return MLSTM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t retention_chunkwise_groupnorm_workspace_bytes(int B, int H, int T, int d_k, int d_v, int chunk,
+                                                     mlstm_dtype dt) {
+  Plan pl;
+  size_t gn_off;
+  if (plan_groupnorm(B, H, T, d_k, d_v, chunk, dt, &pl, &gn_off) != MLSTM_OK) return 0;
+  return pl.bytes;
+}
+
 int retention_chunkwise_groupnorm_fwd(int B, int H, int T, int d_k, int d_v, int chunk, mlstm_dtype dt,
                                       const void* q, const void* k, const void* v, const float* gamma,
                                       const float* S0, float* S_out, const float* gn_weight,
                                       const float* gn_bias, float gn_eps, void* out, void* workspace,
                                       size_t workspace_bytes, void* stream) {
   Plan pl;
-  const int rc = plan_chunkwise(B, H, T, d_k, d_v, 1, chunk, dt, true, &pl);
+  size_t gn_off;
+  const int rc = plan_groupnorm(B, H, T, d_k, d_v, chunk, dt, &pl, &gn_off);
   if (rc != MLSTM_OK) return rc;
-  mlstm::ChunkVariant gv;
-  if (!mlstm::find_retention_groupnorm_variant(dt, d_k, chunk, &gv) || d_v != gv.w)
-    return fail(MLSTM_E_UNSUPPORTED, "fused group norm needs d_v = %d for d_k=%d (got d_v=%d)",
-                mlstm::find_retention_groupnorm_variant(dt, d_k, chunk, &gv) ? gv.w : 0, d_k, d_v);
   if (!(gn_eps > 0.f)) return fail(MLSTM_E_SHAPE, "gn_eps must be positive (got %g)", (double)gn_eps);
   if (!q || !k || !v || !out) return fail(MLSTM_E_NULL, "q, k, v and out are required");
-  pl.var.launch = gv.launch;  // same plan and workspace as without the norm
   mlstm::ChunkParams p{};
   p.B = B;
   p.H = H;
@@ -599,6 +634,7 @@ int retention_chunkwise_groupnorm_fwd(int B, int H, int T, int d_k, int d_v, int
   p.gn_w = gn_weight;
   p.gn_b = gn_bias;
   p.gn_eps = gn_eps;
+  p.gn_ws = gn_off ? reinterpret_cast<float*>(static_cast<char*>(workspace) + gn_off) : nullptr;
   return launch(pl, p, workspace, workspace_bytes, stream);
 }
 

@@ -516,8 +516,21 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
       // work-group holds the whole row, W = d_v): a group of UR consecutive
       // lanes owns a row, 4 fp32 values per lane; mean, then the biased
       // variance of the centred values; y = (x - mean) rsqrt(var + eps) w + b.
+      // A head wider than the work-group (gn_ws set) leaves its fp32 rows in
+      // gn_ws for the row pass instead.
       constexpr int UR = W / 4;
       static_assert((UR & (UR - 1)) == 0 && UR <= 64 && NTH % UR == 0, "row groups of lanes");
+      if (p.gn_ws) {  // work-group-uniform
+#pragma unroll
+        for (int u0 = 0; u0 < L * UR; u0 += NTH) {
+          const int u = u0 + tid;
+          const int j = u / UR, cu = u % UR;
+          if (tc + j < T_)
+            *reinterpret_cast<f32x4*>(&p.gn_ws[((size_t)bh * T_ + tc + j) * DV + slice * W + cu * 4]) =
+                *reinterpret_cast<const f32x4*>(&sH[j * HS + cu * 4]);
+        }
+        return;
+      }
 #pragma unroll
       for (int u0 = 0; u0 < L * UR; u0 += NTH) {
         const int u = u0 + tid;
@@ -1537,6 +1550,41 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
   }
 }
 
+// Row pass of the group norm for heads wider than a pass-3 work-group: one
+// wave per output row (b, h, t) of d_v fp32 values in gn_ws; mean, then the
+// biased variance of the centred values, then y = (x - mean) rsqrt(var + eps)
+// w + b into h in the output dtype (the arithmetic of the fused form).
+template <typename T>
+__global__ __launch_bounds__(256) void groupnorm_rows_kernel(const float* __restrict__ x, T* __restrict__ y,
+                                                             long long rows, int T_, int H, int DV,
+                                                             const float* __restrict__ gw,
+                                                             const float* __restrict__ gb, float eps) {
+  const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;  // wave-uniform
+  const int lane = threadIdx.x & 63;
+  const int hd = (int)((r / T_) % H);
+  const float* xr = x + r * DV;
+  float sm = 0.f;
+  for (int c = lane; c < DV; c += 64) sm += xr[c];
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) sm += __shfl_xor(sm, d, 64);
+  const float mean = sm / (float)DV;
+  float sq = 0.f;
+  for (int c = lane; c < DV; c += 64) {
+    const float dx = xr[c] - mean;
+    sq += dx * dx;
+  }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) sq += __shfl_xor(sq, d, 64);
+  const float rstd = rsqrtf(sq / (float)DV + eps);
+  T* yr = y + r * DV;
+  for (int c = lane; c < DV; c += 64) {
+    const float wv = gw ? gw[(size_t)hd * DV + c] : 1.f;
+    const float bv = gb ? gb[(size_t)hd * DV + c] : 0.f;
+    yr[c] = (T)((xr[c] - mean) * rstd * wv + bv);
+  }
+}
+
 // s_waitcnt with only a vmcnt limit (gfx9 encoding, expcnt and lgkmcnt left
 // at their no-wait maxima).
 template <int N>
@@ -2211,8 +2259,14 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
       hipLaunchKernelGGL((chunk_kernel_ws<true, SN>), g3, dim3(512), 0, stream, p);
     else
       hipLaunchKernelGGL((chunk_kernel_ws<false, SN>), g3, dim3(512), 0, stream, p);
-  } else if constexpr (GN)
+  } else if constexpr (GN) {
     hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, false, true>), g3, dim3(NTH), 0, stream, p);
+    if (p.gn_ws) {
+      const long long rows = (long long)BH * p.T;
+      hipLaunchKernelGGL((groupnorm_rows_kernel<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
+                         p.gn_ws, static_cast<T*>(p.h), rows, p.T, p.H, p.DV, p.gn_w, p.gn_b, p.gn_eps);
+    }
+  }
   else if (!RET && p.o_pre)
     hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, !RET, false, SN, PB>), g3, dim3(NTH), 0,
                        stream, p);

@@ -36,6 +36,10 @@ struct ChunkParams {
   const float* gn_w;
   const float* gn_b;
   float gn_eps;
+  // group norm of a head whose d_v spans several work-groups: pass 3 writes
+  // the unnormalised outputs here in fp32 ([B*H*T][d_v]) and a row pass
+  // normalises them into h (null: the work-group holds the whole row)
+  float* gn_ws;
 };
 
 struct ScanParams {

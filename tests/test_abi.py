@@ -102,10 +102,21 @@ def test_retention_groupnorm_validation():
     f = ctypes.c_float
     args = lambda dv=64, eps=1e-5, q=BOGUS: [1, 1, 10, 64, dv, 64, 1, q, BOGUS, BOGUS, None, None, None,
                                             None, None, f(eps), BOGUS, BOGUS, 1 << 30, None]
-    assert L.retention_chunkwise_groupnorm_fwd(*args(dv=128)) == E_UNSUPPORTED  # d_v must be 64 at d_k 64
+    assert L.retention_chunkwise_groupnorm_fwd(*args(dv=96)) == E_UNSUPPORTED  # d_v a multiple of 64 at d_k 64
     assert L.retention_chunkwise_groupnorm_fwd(*args(eps=0.0)) == E_SHAPE
     assert L.retention_chunkwise_groupnorm_fwd(*args(q=None)) == E_NULL
     assert _lib.last_error() != ""
+    # heads wider than one work-group need room for their fp32 rows: the
+    # workspace grows by exactly B*H*T*d_v*4 bytes (256-aligned), and a call
+    # with only the plain retention workspace is rejected before any launch
+    plain = L.retention_chunkwise_workspace_bytes(2, 3, 100, 64, 256, 64, 1)
+    gn = L.retention_chunkwise_groupnorm_workspace_bytes(2, 3, 100, 64, 256, 64, 1)
+    assert plain > 0 and gn == plain + ((2 * 3 * 100 * 256 * 4 + 255) // 256) * 256
+    assert L.retention_chunkwise_groupnorm_workspace_bytes(2, 3, 100, 64, 64, 64, 1) == \
+        L.retention_chunkwise_workspace_bytes(2, 3, 100, 64, 64, 64, 1)
+    assert L.retention_chunkwise_groupnorm_workspace_bytes(2, 3, 100, 64, 96, 64, 1) == 0
+    wide = [2, 3, 100, 64, 256, 64, 1, BOGUS, BOGUS, BOGUS, None, None, None, None, None, f(1e-5), BOGUS]
+    assert L.retention_chunkwise_groupnorm_fwd(*wide, BOGUS, plain, None) == E_WORKSPACE
 
 
 def test_retention_validation():

@@ -292,17 +292,20 @@ def test_retention_custom_gamma_fp32(gpu):
     assert slice_err(cpu(S), ref_S) < TOL[torch.float32]
 
 
-@pytest.mark.parametrize("B,H,T,dk,dtype,with_state,affine", [
-    (8, 4, 2048, 64, "bf16", False, True),   # the RetNet workload's shape
-    (2, 3, 130, 64, "bf16", True, False),    # ragged tail, initial state
-    (1, 2, 100, 64, "f32", True, True),
-    (2, 2, 200, 128, "bf16", False, True),
+@pytest.mark.parametrize("B,H,T,dk,dv,dtype,with_state,affine", [
+    (8, 4, 2048, 64, 64, "bf16", False, True),   # the RetNet workload's shape
+    (2, 3, 130, 64, 64, "bf16", True, False),    # ragged tail, initial state
+    (1, 2, 100, 64, 64, "f32", True, True),
+    (2, 2, 200, 128, 128, "bf16", False, True),
+    # heads wider than one work-group: fp32 rows through the workspace, then
+    # the row pass (d_v = 2 d_k, the value width RetNet uses; 4 slices)
+    (2, 3, 333, 64, 128, "bf16", True, True),
+    (1, 2, 150, 64, 256, "f32", False, True),
+    (2, 2, 200, 128, 512, "bf16", True, False),
 ])
-def test_retention_groupnorm(gpu, B, H, T, dk, dtype, with_state, affine):
-    """Retention with the per-head group norm fused into the output write
-    against the oracle's retention followed by its group norm; the final
-    state is unaffected by the norm."""
-    dv = dk
+def test_retention_groupnorm(gpu, B, H, T, dk, dv, dtype, with_state, affine):
+    """Retention with the per-head group norm against the oracle's retention
+    followed by its group norm; the final state is unaffected by the norm."""
     q, k, v = retention_inputs(B, H, T, dk, dv, seed=31, dtype=dtype)
     g = torch.Generator().manual_seed(6)
     S0 = torch.randn(B, H, dk, dv, generator=g) * 0.1 if with_state else None
