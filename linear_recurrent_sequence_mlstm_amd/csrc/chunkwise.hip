@@ -1238,16 +1238,6 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
     const bool need_update = c + 1 < c_end || (sc == p.NS - 1);
     __syncthreads();  // A
     {
-      // output-gate values of this wave's outputs, issued now so that the
-      // readout hides their latency
-      Raw4<T> oraw[HAS_O ? NJT : 1][HAS_O ? CT : 1];
-      if constexpr (HAS_O) {
-#pragma unroll
-        for (int jt = 0; jt < NJT; ++jt)
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct)
-            oraw[jt][ct] = bload4_raw<T>(ro, ((unsigned)(t0 + jt * 16 + lr) * DV + wcol0 + ct * 16 + 4 * lg) * ES);
-      }
       // readout of the state at the chunk start: acc[jt][ct] = S~[:, c]^T q_j
       f32x4 acc[NJT][CT];
 #pragma unroll
@@ -1278,6 +1268,16 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
         if (sw == 0) sDenInter[lane] = sNf[pb][0];
       } else {
         if (lg == 0) sDenInter[sw * 16 + lr] = pn[0] + pn[1];
+      }
+      // output-gate values of this wave's outputs, issued after the readout
+      // (not live across it) so that the wait at barrier B hides their latency
+      Raw4<T> oraw[HAS_O ? NJT : 1][HAS_O ? CT : 1];
+      if constexpr (HAS_O) {
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            oraw[jt][ct] = bload4_raw<T>(ro, ((unsigned)(t0 + jt * 16 + lr) * DV + wcol0 + ct * 16 + 4 * lg) * ES);
       }
       __syncthreads();  // B
       const float* sA2 = sA2b[pb];

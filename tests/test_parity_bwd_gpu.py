@@ -7,6 +7,8 @@ oracle in fp64).  Metric as for the forward: per (batch, head)
 slice, max |g - g_ref| / max |g_ref|, the largest over slices; 1e-4 for fp32,
 2e-2 for bf16 inputs (the bias gradient: over heads).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -376,3 +378,62 @@ def test_retention_bwd_final_state_gradient(gpu, dtype, T, dk, dv):
     errs = {nm: slice_err(cpu(out[nm]), ref[nm]) for nm in ("dq", "dk", "dv", "dS0")}
     print(errs, flush=True)
     assert all(e < TOL[q.dtype] for e in errs.values()), errs
+
+
+def test_bwd_tokens_at_the_denominator_floor_fp32(gpu):
+    """Every token placed within 0.5e-3 .. 1.5e-3 of the denominator floor
+    |n.q + bias| = 1, half of them just above it and half just below, with
+    both signs of n.q + bias and dh on every token.  The derivative of
+    max(|z|, 1) switches at the floor; in fp32 the GPU's z is within about
+    1e-6 of the oracle's, so every token falls on the same side on both and
+    every gradient is compared, none masked.
+
+    q_t is built from the inputs' own true-space normaliser
+    n_t = sigmoid(f~_t) n_{t-1} + exp(i~_t) k_t (q does not enter n): its
+    component along n_t sets z_t to the target, the orthogonal part is
+    random."""
+    B, H, T, dqk, dv = 2, 2, 150, 64, 64
+    x = mlstm_inputs(B, H, T, dqk, dv, seed=2500, dtype="f32", k_scale=1 / 8, with_o=True, bias="uniform")
+    k = x.k.double()
+    f = torch.sigmoid(x.f_pre.double())
+    i = torch.exp(x.i_pre.double())
+    bias = x.bias.double()[None, :]
+    g = torch.Generator().manual_seed(2501)
+    side = torch.where(torch.rand(B, H, T, generator=g) < 0.5, -1.0, 1.0).double()
+    sgn = torch.where(torch.rand(B, H, T, generator=g) < 0.5, -1.0, 1.0).double()
+    off = (0.5e-3 + 1e-3 * torch.rand(B, H, T, generator=g)).double()
+    r = torch.randn(B, H, T, dqk, generator=g).double() * 0.3
+    n = torch.zeros(B, H, dqk, dtype=torch.float64)
+    q = torch.empty(B, H, T, dqk, dtype=torch.float64)
+    for t in range(T):
+        n = f[..., t, None] * n + i[..., t, None] * k[..., t, :]
+        nn = (n * n).sum(-1, keepdim=True)
+        z = sgn[..., t] * (1 + side[..., t] * off[..., t])
+        rt = r[..., t, :] - (r[..., t, :] * n).sum(-1, keepdim=True) / nn * n
+        q[..., t, :] = ((z - bias) / nn[..., 0])[..., None] * n + rt
+    x = dataclasses.replace(x, q=q.float().contiguous())
+    # the tokens really sit where intended (oracle forward, fp64)
+    z_ref = np.einsum("bhtd,bhtd->bht", np.asarray(oracle_n(x)), cpu(x.q)) + cpu(x.bias)[None, :, None]
+    dist = np.abs(np.abs(z_ref) - 1)
+    assert dist.min() > 4e-4 and dist.max() < 1.6e-3
+    assert (np.abs(z_ref) > 1).mean() > 0.3 and (np.abs(z_ref) < 1).mean() > 0.3
+    out, ref = run_bwd(x, gpu, seed=2502)
+    db, dbr = cpu(out["dbias"]), ref["dbias"]
+    terms = np.abs(ref["dbias_t"]).sum(axis=(0, 2))
+    e_sum = float((np.abs(db - dbr) / terms).max())
+    print("dbias: %.2e of sum |dz_t|" % e_sum, flush=True)
+    assert e_sum < TOL[torch.float32], e_sum
+    check(dict(out, dbias=None), ref, TOL[torch.float32])
+
+
+def oracle_n(x):
+    """True-space normaliser n_t of every token, from the oracle's forward:
+    ñ_t e^{m_t}, one token at a time (the oracle reports the final state, so
+    run it on every prefix length)."""
+    B, H, T, dqk = x.q.shape
+    out = np.empty((B, H, T, dqk))
+    for t in range(T):
+        _, _, nt, mt = oracle.mlstm_fwd(x.q[:, :, :t + 1], x.k[:, :, :t + 1], x.v[:, :, :t + 1],
+                                        x.i_pre[:, :, :t + 1], x.f_pre[:, :, :t + 1], None, x.bias)
+        out[:, :, t] = nt * np.exp(mt)[..., None]
+    return out

@@ -83,3 +83,32 @@ def test_xlstm7b_decode_128_steps_sampled(gpu):
     assert slice_err(cpu(got), ref[0]) < TOL[torch.bfloat16]
     st = (C[bi.to(gpu), hi.to(gpu)][None], n[bi.to(gpu), hi.to(gpu)][None], m[bi.to(gpu), hi.to(gpu)][None])
     check_state(st, ref[1:], TOL[torch.bfloat16])
+
+
+def test_xlstm7b_decode_all_sequences_first_8_steps(gpu):
+    """The same decode workload on every one of its 2048 (batch, head)
+    sequences: h at each of the first 8 steps and the whole 1 GiB state after
+    them, against the oracle run on all sequences."""
+    d = workload("xlstm7b_decode_B256")
+    S8 = 8
+    _, B, H, dqk = d.q.shape
+    dv = d.v.shape[-1]
+    g = d.to(gpu)
+    C = torch.zeros(B, H, 1, dqk, dv, device=gpu)
+    n = torch.zeros(B, H, dqk, device=gpu)
+    m = torch.zeros(B, H, device=gpu)
+    hs = []
+    for s in range(S8):
+        h = torch.empty(B, H, dv, dtype=torch.bfloat16, device=gpu)
+        mlstm.step(g.q[s], g.k[s], g.v[s], g.i_pre[s], g.f_pre[s], C, n, m, bias=g.bias, h=h)
+        hs.append(h)
+    torch.cuda.synchronize()
+    # every (batch, head) as one of B*H heads of a single batch: [1, B*H, S, d]
+    got = torch.stack(hs, dim=2).reshape(1, B * H, S8, dv)
+    seq = lambda t: t[:S8].permute(1, 2, 0, 3).reshape(1, B * H, S8, -1).contiguous()
+    seq_g = lambda t: t[:S8].permute(1, 2, 0).reshape(1, B * H, S8).contiguous()
+    bias = None if d.bias is None else d.bias.repeat(B).contiguous()
+    ref = oracle.mlstm_fwd(seq(d.q), seq(d.k), seq(d.v), seq_g(d.i_pre), seq_g(d.f_pre), None, bias)
+    assert slice_err(cpu(got), ref[0]) < TOL[torch.bfloat16]
+    st = (C.reshape(1, B * H, 1, dqk, dv), n.reshape(1, B * H, dqk), m.reshape(1, B * H))
+    check_state(st, ref[1:], TOL[torch.bfloat16])
