@@ -244,7 +244,8 @@ __device__ __forceinline__ void load_chunk_gates(const BwdParams& p, int bh, int
 // (the forward's state update; K and V of the next chunk load during the
 // current one's product).
 template <typename T, int DQK, int NB>
-__global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
+// four waves per SIMD (108 registers, no spills; 2 % of the 7B backward)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void bwd_chunk_states_kernel(BwdParams p) {
   static_assert(NB == 1 || DQK == 64, "two blocks on 64-wide heads only");
   constexpr int LD = BT<T>::LD;
   constexpr unsigned ES = sizeof(T);
@@ -413,7 +414,11 @@ __global__ __launch_bounds__(256) void bwd_chunk_states_kernel(BwdParams p) {
 // RET (retention): no normaliser, so den~ = 1 and dz~ = 0, and the readout
 // (needed only for dz~ and d o_pre) is not recomputed.
 template <typename T, int DQK, bool RET, int NB>
-__global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
+// Two waves per SIMD (two work-groups per CU where the LDS allows): left to
+// itself the compiler spends about 300 registers and runs one; the cap costs
+// a few spills at the widest shapes and measured 10 % on the two-block
+// backward, 3 % at the 7B head shape.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_scores_kernel(BwdParams p) {
   static_assert(NB == 1 || DQK == 64, "two blocks on 64-wide heads only");
   constexpr int LD = BT<T>::LD;
   constexpr int LDQ = DQK + 16 / (int)sizeof(T);
@@ -725,7 +730,9 @@ __global__ __launch_bounds__(256) void bwd_scores_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- kernel 2
 template <typename T, int DQK, int NB>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
+// three waves per SIMD where the LDS allows (162 registers at d_qk = 256, no
+// spills; 2 % of the 7B backward)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void bwd_dq_kernel(BwdParams p) {
   static_assert(NB == 1 || DQK == 64, "two blocks on 64-wide heads only");
   __shared__ __attribute__((aligned(16))) T sA2[NB > 1 ? BL * BT<T>::LD : 8];  // D' of block 1
   constexpr int LD = BT<T>::LD;
