@@ -560,8 +560,8 @@ def main():
     # continuous GPU work) runs right before the prefill leg, so that the
     # prefill's warm-up and timed steps find the GPU at its steady clocks:
     # after a host-side pause of a few milliseconds this GPU needs about 20 ms
-    # of work to return to them (measured: pass 3 of the prefill takes ~100 us
-    # per call for its first 50 calls after a 1 s pause, 86 us after that).
+    # of work to return to them (measured: pass 3 of the prefill takes about
+    # 15 % longer for its first 50 calls after a 1 s pause than after them).
     x = workload("xlstm7b_prefill_T8192")
     prep = prepare_prefill(torch, mlstm, x, dev)
     var = []
