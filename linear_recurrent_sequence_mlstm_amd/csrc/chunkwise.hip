@@ -1900,11 +1900,12 @@ __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
 
   // per-lane byte offsets of the loaded units relative to the step's first
   // token (the token part goes into the scalar offset); pad slots point past
-  // any buffer end.  Every wave issues exactly JA loads per step on every
-  // path, also past the last step (clamped to it; those stages are never
-  // read), so that the vm counter advances identically on all paths and the
-  // waits name exact counts; a wave with fewer than JA instructions in the
-  // stage repeats its previous one (same bytes to the same slot).
+  // any buffer end.  The NI load instructions of a stage are dealt to the
+  // waves in turn: waves w < NI mod NWP issue JA of them, the others JA - 1
+  // (when NWP does not divide NI).  Every wave issues its loads of a step on
+  // every path, also past the last step (clamped to it; those stages are
+  // never read), so that its vm counter advances the same way on all paths
+  // and its waits name exact counts.
   unsigned voff[JA];
 #pragma unroll
   for (int j = 0; j < JA; ++j) {
@@ -1916,10 +1917,10 @@ __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
     } else if (i < C::NI) {
       const int unit = (i - C::NIK) * 64 + lane, row = unit / C::UV, cu = unit % C::UV;
       if (row < KS && cu < TC / VE) voff[j] = (unsigned)(row * DV + c0 + cu * VE) * ES;
-    } else {
-      voff[j] = voff[j - 1];
     }
   }
+  // whether this wave issues JA loads per step (else JA - 1)
+  const bool full_ja = (C::NI % NWP) == 0 || w < C::NI % NWP;
   auto issue = [&](int s_, auto bidx) __attribute__((always_inline)) {
     unsigned char* st = stage_ptr(bidx);
     const int s = min(s_, NSTEP - 1);
@@ -1928,14 +1929,18 @@ __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
     const int sv = __builtin_amdgcn_readfirstlane((int)(t0 * DV * ES));
 #pragma unroll
     for (int j = 0; j < JA; ++j) {
-      const int i0 = w + NWP * j;  // wave-uniform
-      const int i = i0 < C::NI ? i0 : i0 - NWP;
+      const int i = w + NWP * j;  // wave-uniform
       const bool isk = i < C::NIK;
-      dma16_to_lds(isk ? rk : rv, st + i * 1024, voff[j], isk ? sk : sv);
+      if (j < JA - 1 || full_ja) dma16_to_lds(isk ? rk : rv, st + i * 1024, voff[j], isk ? sk : sv);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  constexpr int NV = JA;  // vm operations of one step of one wave
+  // s_waitcnt until at most N steps of this wave's loads are in flight
+  auto wait_steps = [&](auto nc) __attribute__((always_inline)) {
+    constexpr int N = decltype(nc)::value;
+    if (full_ja) wait_vmcnt<N * JA>();
+    else wait_vmcnt<N * (JA - 1)>();
+  };
 
   // gate inputs, then the first NSTG steps in flight, then w of the
   // superchunk into LDS (the gate loads are issued first, so waiting for
@@ -2028,7 +2033,7 @@ __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
   // while the MFMAs of step c run, and scaled by w after them.  Steps past
   // the end (the loop runs in groups of NSTG) only issue and wait.
   StepFrags F0, F1;
-  wait_vmcnt<(NSTG - 1) * NV>();  // step 0 landed
+  wait_steps(std::integral_constant<int, NSTG - 1>{});  // step 0 landed
   lds_barrier();
   load_step(I0{}, F0);
   scale_step(0, F0);
@@ -2039,7 +2044,7 @@ __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
     constexpr bool FULL = decltype(fullc)::value;
     constexpr int b = decltype(bidx)::value;
     using B1 = std::integral_constant<int, (b + 1) % NSTG>;
-    wait_vmcnt<(NSTG - 2) * NV>();
+    wait_steps(std::integral_constant<int, NSTG - 2>{});
     lds_barrier();
     issue(c + NSTG, bidx);
     if (FULL || c + 1 < NSTEP) load_step(B1{}, nxt);
