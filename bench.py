@@ -386,6 +386,23 @@ def bench_variants(torch, mlstm, workload, args, dev, only_backward=False):
     S = torch.zeros(B, H, dk, dv, device=dev)
     o = torch.empty(B, H, dv, dtype=q.dtype, device=dev)
     r = timed(lambda i: mlstm.retention_step(*toks[i], S, out=o), D, D, D, chunkwise=False)
+    # the same D steps captured once in a HIP graph and replayed (what a
+    # serving loop that captures its decode steps sees: no host enqueue per
+    # step); GPU time per step over 5 replays
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(D):
+            mlstm.retention_step(*toks[i], S, out=o)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    r["graph_ms_per_step"] = e0.elapsed_time(e1) / (5 * D)
+    del graph
     byts = 2 * B * H * dk * dv * 4 + B * H * (2 * dk + 2 * dv) * 2
     out.append(dict(workload="retnet_msr_decode_B8", B=B, H=H, d_k=dk, d_v=dv, steps=D, **r, bytes=byts,
                     flops=B * H * 4 * dk * dv, tokens=B))
