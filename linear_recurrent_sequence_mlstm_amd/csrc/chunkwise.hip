@@ -293,7 +293,8 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   __shared__ float sNf[RET ? 4 : DQK];
   // gate vectors, two sets: wave 0 fills the next chunk's while the other
   // waves still read the current chunk's
-  __shared__ float sA2b[2][L], sM2b[2][L], sRSb[2][L], sCLb[2][L], sBTb[2][L], sWb[2][L];
+  __shared__ __attribute__((aligned(16))) float sA2b[2][L];
+  __shared__ float sM2b[2][L], sRSb[2][L], sCLb[2][L], sBTb[2][L], sWb[2][L];
   __shared__ float sDenPart[NDB * NJT * L];
   __shared__ float sDenInter[NDB * L];
   __shared__ float sAlphab[2];
@@ -621,10 +622,10 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
         jt += lt;
       };
       auto tile_idx = [&](int k) __attribute__((always_inline)) { return k * NW + ((k & 1) ? NW - 1 - w : w); };
-      // rows 0 (hi) and 1 (lo) of the n~ tile; zero in rows 2..15
+      // A rows alternate the hi and lo parts of n~ (only output rows 0 and 1
+      // are used, so no select zeroes the others)
       auto n_frag = [&](int kb) __attribute__((always_inline)) {
-        const frag f = M::load(&sNh[(lr & 1) * DQK + kb * K + KL * lg]);
-        return lr < 2 ? f : M::zero();
+        return M::load(&sNh[(lr & 1) * DQK + kb * K + KL * lg]);
       };
       auto scores = [&](auto nuc, auto wnc) __attribute__((always_inline)) {
         constexpr int NU = decltype(nuc)::value;
@@ -632,16 +633,26 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
         int lt[NU], jt[NU];
 #pragma unroll
         for (int u = 0; u < NU; ++u) tile_of(tile_idx(u), lt[u], jt[u]);
-        // decay factors of the tiles first: they do not wait for the MFMAs
+        // decay factors of the tiles first: they do not wait for the MFMAs;
+        // every read first (unconditional, 16-byte), then the masked exps
         float fac[NU][4];
+        {
+          float m2[NU];
+          float4 a4[NU];
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          const int j = jt[u] * 16 + lr;
-          const float m2 = sM2[j];
+          for (int u = 0; u < NU; ++u) {
+            m2[u] = sM2[jt[u] * 16 + lr];
+            a4[u] = *reinterpret_cast<const float4*>(&sA2[lt[u] * 16 + 4 * lg]);
+          }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int l = lt[u] * 16 + 4 * lg + i;
-            fac[u][i] = (l <= j) ? exp2_fast(sA2[l] - m2) : 0.f;
+          for (int u = 0; u < NU; ++u) {
+            const int j = jt[u] * 16 + lr;
+            const float av[4] = {a4[u].x, a4[u].y, a4[u].z, a4[u].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int l = lt[u] * 16 + 4 * lg + i;
+              fac[u][i] = (l <= j) ? exp2_fast(av[i] - m2[u]) : 0.f;
+            }
           }
         }
         f32x4 pt[NU][NB];
@@ -908,10 +919,25 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
         }
       }
       if constexpr (VN && !NFRAG) {
-        for (int r = tid; r < DQK; r += NTH) {
-          float x = alpha * sNf[r];
-          for (int l = 0; l < L; ++l) x += sW[l] * to_f32(sK[l * KST + r]);
-          put_n(r, x);
+        // PPF adjacent lanes per feature, each summing L / PPF tokens with its
+        // reads issued together; the partial sums meet by xor shuffles
+        constexpr int PPF = NTH >= DQK ? (NTH / DQK > 8 ? 8 : NTH / DQK) : 1;
+        constexpr int LP = L / PPF;
+        static_assert(L % PPF == 0 && (PPF & (PPF - 1)) == 0, "token parts");
+        const int part = tid % PPF;
+        for (int r = tid / PPF; r < DQK; r += NTH / PPF) {
+          float kv[LP], wl[LP];
+#pragma unroll
+          for (int l = 0; l < LP; ++l) {
+            kv[l] = to_f32(sK[(part * LP + l) * KST + r]);
+            wl[l] = sW[part * LP + l];
+          }
+          float x = 0.f;
+#pragma unroll
+          for (int l = 0; l < LP; ++l) x += wl[l] * kv[l];
+#pragma unroll
+          for (int d = 1; d < PPF; d <<= 1) x += __shfl_xor(x, d, 64);
+          if (part == 0) put_n(r, alpha * sNf[r] + x);
         }
       }
       if constexpr (SN) {  // n~ <- alpha n~ + sum_l w_l, summed by the last wave
