@@ -805,6 +805,36 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
       // accumulators they select) are compile-time constants
       auto phase_c = [&](auto rgc) __attribute__((always_inline)) {
         constexpr int RG = decltype(rgc)::value;
+        // the normaliser of this lane's tokens of every tile, every read first
+        const int db = PB ? blk : 0;  // this wave's columns lie in block blk
+        float rsv[JPW], invv[JPW];
+        {
+          float d_in[JPW], d_bt[JPW], d_cl[JPW], d_pt[JPW][NJT];
+#pragma unroll
+          for (int jj = 0; jj < JPW; ++jj) {
+            const int j = C::jt_of(RG, jj) * 16 + lr;
+            rsv[jj] = sRS[j];
+            if constexpr (!RET) {
+              d_in[jj] = sDenInter[db * L + j];
+              d_bt[jj] = sBT[j];
+              d_cl[jj] = sCL[j];
+#pragma unroll
+              for (int t = 0; t < NJT; ++t) d_pt[jj][t] = sDenPart[(db * NJT + t) * L + j];
+            }
+          }
+#pragma unroll
+          for (int jj = 0; jj < JPW; ++jj) {
+            if constexpr (RET) {
+              invv[jj] = 1.f;
+            } else {
+              float den = rsv[jj] * d_in[jj] + d_bt[jj];
+#pragma unroll
+              for (int t = 0; t < NJT; ++t) den += d_pt[jj][t];
+              invv[jj] = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), d_cl[jj]));
+            }
+          }
+        }
+        const float sig_scale = exp2_fast(sig);
 #pragma unroll
         for (int jj = 0; jj < JPW; ++jj) {
           const int jt = C::jt_of(RG, jj);  // compile-time after unrolling
@@ -822,24 +852,14 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
             }
           }
           const int j = jt * 16 + lr;
-          const float rs = sRS[j];
-          const float rs_state = rs * exp2_fast(sig);
+          const float rs_state = rsv[jj] * sig_scale;
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) {
             f32x4 a = acc[jt][ct];
             if constexpr (XCH) a += sX[((cg * NJT + jt) * CT + ct) * 64 + lane];
             o_acc[ct] += rs_state * a;
           }
-          float inv;
-          if constexpr (RET) {
-            inv = 1.f;
-          } else {
-            const int db = PB ? blk : 0;  // this wave's columns lie in block blk
-            float den = rs * sDenInter[db * L + j] + sBT[j];
-#pragma unroll
-            for (int t = 0; t < NJT; ++t) den += sDenPart[(db * NJT + t) * L + j];
-            inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), sCL[j]));
-          }
+          const float inv = invv[jj];
           // rows past T fall outside the output buffer and are dropped
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) {
