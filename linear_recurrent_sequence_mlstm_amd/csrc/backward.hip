@@ -490,13 +490,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   // workspace, P to LDS for the readout
   T* Ptw = static_cast<T*>(p.wsPt) + ((size_t)bh * p.NC + c) * NB * BL * BL;
   float rs[4] = {0.f, 0.f, 0.f, 0.f};  // the normaliser sums over the whole head
+  // the gate logs of this lane's tokens l and j, read in one batch
+  float saL[4], smJ[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) saL[n] = sa[16 * n + lr];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) smJ[i] = sM[16 * w + 4 * lg + i];
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int l = 16 * n + lr;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = 16 * w + 4 * lg + i;
-      const float e = l <= j ? exp2_fast(sa[l] - sM[j]) : 0.f;
+      const float e = l <= j ? exp2_fast(saL[n] - smJ[i]) : 0.f;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         accP[b][n][i] *= e;
@@ -711,6 +717,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   // D' = E . (dN V^T + dz~) per memory block, stored transposed (dq and dk
   // both read D'^T: dq with transposing LDS reads)
   T* Dtw = static_cast<T*>(p.wsDt) + ((size_t)bh * p.NC + c) * NB * BL * BL;
+  float saL2[4], smJ2[4], dzJ[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) saL2[n] = sa[16 * n + lr];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    smJ2[i] = sM[16 * w + 4 * lg + i];
+    dzJ[i] = sdz[16 * w + 4 * lg + i];
+  }
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int l = 16 * n + lr;
@@ -720,8 +734,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 16 * w + 4 * lg + i;
-        const float e = l <= j ? exp2_fast(sa[l] - sM[j]) : 0.f;
-        dv4[i] = e * (accD[b][n][i] + sdz[j]);
+        const float e = l <= j ? exp2_fast(saL2[n] - smJ2[i]) : 0.f;
+        dv4[i] = e * (accD[b][n][i] + dzJ[i]);
       }
       store4f(Dtw + b * BL * BL + l * BL + 16 * w + 4 * lg, dv4[0], dv4[1], dv4[2], dv4[3]);
     }
