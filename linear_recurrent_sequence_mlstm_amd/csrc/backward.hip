@@ -215,6 +215,11 @@ __device__ __forceinline__ void st_row16(T* s, int r, int c0, const float (&x)[1
           make_float4(x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]);
   }
 }
+// x from lane (lr + N) mod 16 of the same row of 16 lanes (DPP row_ror:N)
+template <int N>
+__device__ __forceinline__ float dpp_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x120 + N, 0xF, 0xF, false));
+}
 // Stabiliser quantities of one chunk into LDS (threads 0..63): a_j, M_j,
 // alpha_j, e^{-m_j}, w_j; returns nothing, sets *sdec to 2^{m_prev - M_L}.
 __device__ __forceinline__ void load_chunk_gates(const BwdParams& p, int bh, int c, int tid, float* sa, float* sM,
@@ -1256,17 +1261,337 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
   }
 }
 
+// dk and dv of one chunk in one work-group of 8 waves (bf16, d_qk = 64 NDT,
+// one memory block).  G_c is read from memory once, in 64 x 64 blocks (feature
+// block a inner, value-column block b outer).  Each block is staged in LDS as
+// its hi and lo bf16 parts and serves both products:
+//   waves 0..3, dk: wave w takes token strips 2 (w >> 1) and 2 (w >> 1) + 1
+//     (16 rows each) and feature columns [32 (w & 1), +32) of every feature
+//     block: dk_inter[., a] += V[., b] G[a, b]^T (hi and lo parts), and at the
+//     end dk = D'^T Q + w (dk_inter + g_c) and the rows' partials of k . dk;
+//   waves 4..7, dv: wave w takes token strip s = w - 4: dv[s, b] += K[s, a] G[a, b]
+//     (hi part) over the feature blocks, plus P^T dN[:, b]; value block b is
+//     complete, and stored, when its inner loop over a ends.
+// The G blocks are loaded NDT ahead into registers, with one barrier per block
+// (two LDS buffers).  The V and dN column blocks are double-buffered too and load
+// one outer step ahead.  Q, K and D'^T stay in LDS for the whole chunk.
+template <int NDT>
+__global__ __launch_bounds__(512) void bwd_dkv_chunk_kernel(BwdParams p) {
+  using T = __bf16;
+  using M = Mma<T>;
+  typedef typename M::frag frag;
+  constexpr int DQK = 64 * NDT;
+  constexpr int PF = NDT;         // G blocks in flight (register slots)
+  constexpr int QLD = DQK + 8;    // row stride of sQ, sK (bf16)
+  constexpr int GLD = BT<T>::LD;  // row stride of the 64 x 64 blocks
+  constexpr unsigned ES = 2;
+  static_assert(NDT >= 2 && (NDT & (NDT - 1)) == 0, "feature blocks: a power of two, at least 2");
+  __shared__ __attribute__((aligned(16))) T sQ[BL * QLD];
+  __shared__ __attribute__((aligned(16))) T sK[BL * QLD];
+  __shared__ __attribute__((aligned(16))) T sGh[2][BL * GLD];
+  __shared__ __attribute__((aligned(16))) T sGl[2][BL * GLD];
+  __shared__ __attribute__((aligned(16))) T sV[2][BL * GLD];
+  __shared__ __attribute__((aligned(16))) T sN[2][BL * GLD];
+  __shared__ __attribute__((aligned(16))) T sDt[BL * GLD];
+  __shared__ float sa[BL], sM[BL], sal[BL], sem[BL], sw[BL], sg[DQK];
+  __shared__ float skd[2][BL];  // k . dk partials of the two feature halves
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const bool dk_wave = w < 4;
+  const int s = w & 3;                  // dv waves: token strip
+  const int sp = (w >> 1) & 1, fh = w & 1;  // dk waves: strip pair, feature half
+  const int bh = (int)blockIdx.x / p.NC, c = (int)blockIdx.x % p.NC;
+  const int t0 = c * BL;
+  const int DV = p.DV, NVT = DV / 64, NIT = NDT * NVT;
+  const size_t NST = (size_t)DQK * DV + DQK;
+  const int r = tid >> 3, c8 = 8 * (tid & 7);  // staging of a 64 x 64 block: row, 8 columns
+  load_chunk_gates(p, bh, c, tid, sa, sM, sal, sem, sw);
+  const float* Gc = p.ws_U + ((size_t)bh * p.NC + c) * NST;  // G_c, then g_c
+  if (tid < DQK) sg[tid] = Gc[(size_t)DQK * DV + tid];
+  const float rden = p.ws_rden[(size_t)bh * p.NC * BL + (size_t)c * BL + r];
+  const bool has_o = p.o_pre != nullptr;
+  const auto rG = make_rsrc(Gc, (unsigned)(DQK * DV) * 4u);
+  const auto rq = make_rsrc(static_cast<const T*>(p.q) + (size_t)bh * p.T * DQK, (unsigned)(p.T * DQK) * ES);
+  const auto rk = make_rsrc(static_cast<const T*>(p.k) + (size_t)bh * p.T * DQK, (unsigned)(p.T * DQK) * ES);
+  const auto rv = make_rsrc(static_cast<const T*>(p.v) + (size_t)bh * p.T * DV, (unsigned)(p.T * DV) * ES);
+  const auto rdh = make_rsrc(static_cast<const T*>(p.dh) + (size_t)bh * p.T * DV, (unsigned)(p.T * DV) * ES);
+  const auto ro = make_rsrc(has_o ? static_cast<const T*>(p.o_pre) + (size_t)bh * p.T * DV : nullptr,
+                            has_o ? (unsigned)(p.T * DV) * ES : 0u);
+  // outputs: 16-byte stores through descriptors that end at token T (rows past it are dropped)
+  const auto rdk = make_rsrc(static_cast<T*>(p.dk) + (size_t)bh * p.T * DQK, (unsigned)(p.T * DQK) * ES);
+  const auto rdv = make_rsrc(static_cast<T*>(p.dv) + (size_t)bh * p.T * DV, (unsigned)(p.T * DV) * ES);
+  const size_t tile0 = ((size_t)bh * p.NC + c) * BL * BL;  // this chunk's D'^T and P^T tiles
+  const auto rdt = make_rsrc(static_cast<const T*>(p.wsDt) + tile0, (unsigned)(BL * BL) * ES);
+  const auto rpt = make_rsrc(static_cast<const T*>(p.wsPt) + tile0, (unsigned)(BL * BL) * ES);
+  // Every load below is issued unconditionally, so that the compiler counts
+  // the same loads in flight on every path and waits only for the one it
+  // needs; a load with nothing to fetch goes through a zero-size descriptor
+  // (reads zero, touches no memory).
+  const auto rnone = make_rsrc(nullptr, 0u);
+
+  // G block i (a = i % NDT, b = i / NDT): this thread's 8 floats (zero past the last block)
+  u32x4 gr[PF][2];
+  auto g_load = [&](int i, u32x4(&dst)[2]) __attribute__((always_inline)) {
+    const int b = i / NDT, a = i % NDT;
+    const auto rg = i < NIT ? rG : rnone;
+    const unsigned off = ((unsigned)(64 * a + r) * DV + 64 * b + c8) * 4u;
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0);
+    dst[1] = __builtin_amdgcn_raw_buffer_load_b128(rg, off + 16, 0, 0);
+  };
+  // ... into LDS buffer buf as hi = bf16(G) and lo = bf16(G - hi)
+  auto g_store = [&](int buf, const u32x4(&src)[2]) __attribute__((always_inline)) {
+    u32x4 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x0 = __uint_as_float(src[e >> 1][2 * (e & 1)]);
+      const float x1 = __uint_as_float(src[e >> 1][2 * (e & 1) + 1]);
+      hi[e] = pack_bf16x2(x0, x1);
+      lo[e] = pack_bf16x2(x0 - __uint_as_float(hi[e] << 16), x1 - __uint_as_float(hi[e] & 0xffff0000u));
+    }
+    *reinterpret_cast<u32x4*>(&sGh[buf][r * GLD + c8]) = hi;
+    *reinterpret_cast<u32x4*>(&sGl[buf][r * GLD + c8]) = lo;
+  };
+  // value-column block b of V and of dh (and o_pre): this thread's 8
+  // elements (zero past the last block)
+  u32x4 nh, no, nv;
+  auto nv_load = [&](int b) __attribute__((always_inline)) {
+    const bool in = b < NVT;
+    const unsigned off = ((unsigned)(t0 + r) * DV + 64 * b + c8) * ES;
+    nh = __builtin_amdgcn_raw_buffer_load_b128(in ? rdh : rnone, off, 0, 0);
+    no = __builtin_amdgcn_raw_buffer_load_b128(in ? ro : rnone, off, 0, 0);
+    nv = __builtin_amdgcn_raw_buffer_load_b128(in ? rv : rnone, off, 0, 0);
+  };
+  // ... into LDS buffer buf: V as loaded, dN = o dh / den~ rounded to bf16
+  auto nv_store = [&](int buf) __attribute__((always_inline)) {
+    u32x4 dn;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float g0 = __uint_as_float(nh[e] << 16), g1 = __uint_as_float(nh[e] & 0xffff0000u);
+      if (has_o) {
+        g0 = dn_of(g0, sigmoidf_(__uint_as_float(no[e] << 16)), rden);
+        g1 = dn_of(g1, sigmoidf_(__uint_as_float(no[e] & 0xffff0000u)), rden);
+      } else {
+        g0 = dn_of(g0, 1.f, rden);
+        g1 = dn_of(g1, 1.f, rden);
+      }
+      dn[e] = pack_bf16x2(g0, g1);
+    }
+    *reinterpret_cast<u32x4*>(&sN[buf][r * GLD + c8]) = dn;
+    *reinterpret_cast<u32x4*>(&sV[buf][r * GLD + c8]) = nv;
+  };
+
+  // prologue: Q, K, D'^T, P^T rows, the first G blocks, V and dN of block 0
+  // in flight together
+  frag afr[2];  // dv waves: P^T rows 16 s + lr along the tokens l (k order of frag_krows)
+  {
+    u32x4 qr[NDT], kr[NDT];
+#pragma unroll
+    for (int it = 0; it < NDT; ++it) {
+      const int u = tid + 512 * it, row = u / (DQK / 8), col = (u % (DQK / 8)) * 8;
+      const unsigned off = ((unsigned)(t0 + row) * DQK + col) * ES;
+      qr[it] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+      kr[it] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+    }
+    const u32x4 dtr = __builtin_amdgcn_raw_buffer_load_b128(rdt, (unsigned)(r * BL + c8) * ES, 0, 0);
+    u32x2 pr[2][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        pr[kk][h] = __builtin_amdgcn_raw_buffer_load_b64(rpt, (unsigned)((16 * s + lr) * BL + 32 * kk + 16 * h + 4 * lg) * ES,
+                                                         0, 0);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) g_load(i, gr[i]);
+    nv_load(0);
+#pragma unroll
+    for (int it = 0; it < NDT; ++it) {
+      const int u = tid + 512 * it, row = u / (DQK / 8), col = (u % (DQK / 8)) * 8;
+      *reinterpret_cast<u32x4*>(&sQ[row * QLD + col]) = qr[it];
+      *reinterpret_cast<u32x4*>(&sK[row * QLD + col]) = kr[it];
+    }
+    *reinterpret_cast<u32x4*>(&sDt[r * GLD + c8]) = dtr;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x4 lo4 = __builtin_bit_cast(bf16x4, pr[kk][0]);
+      const bf16x4 hi4 = __builtin_bit_cast(bf16x4, pr[kk][1]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        afr[kk][e] = lo4[e];
+        afr[kk][4 + e] = hi4[e];
+      }
+    }
+    g_store(0, gr[0]);
+    nv_store(0);
+  }
+  // dk waves: acc[a][2 ms + nn] = V G^T of feature block a, rows of strip
+  // 2 sp + ms, columns 16 (2 fh + nn) + lr; dv waves: acc[0] = K G and
+  // acc[1] = P^T dN of the current value block
+  f32x4 acc[NDT][4];
+#pragma unroll
+  for (int a = 0; a < NDT; ++a) zero_acc(acc[a]);
+  frag vfr[2][2];  // dk waves: V rows of the two strips, current value block
+  for (int b = 0; b < NVT; ++b) {
+#pragma unroll
+    for (int a = 0; a < NDT; ++a) {
+      const int i = b * NDT + a;
+      __syncthreads();
+      // (the last block's store is skipped: its buffer stages dk afterwards;
+      // after the last value block nv_store writes zeros nobody reads)
+      if (i + 1 < NIT) g_store((a + 1) & 1, gr[(a + 1) % PF]);
+      if (a == NDT - 1) nv_store((b + 1) & 1);
+      if (a == 0) nv_load(b + 1);
+      g_load(i + PF, gr[a]);
+      const T* gh = sGh[a & 1];
+      if (dk_wave) {
+        const T* gl = sGl[a & 1];
+        if (a == 0) {
+#pragma unroll
+          for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+              vfr[ms][kk] =
+                  *reinterpret_cast<const frag*>(&sV[b & 1][(16 * (2 * sp + ms) + lr) * GLD + 32 * kk + 8 * lg]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int nn = 0; nn < 2; ++nn) {
+            const int o = (16 * (2 * fh + nn) + lr) * GLD + 32 * kk + 8 * lg;  // G rows d, k = value column
+            const frag bh_ = *reinterpret_cast<const frag*>(gh + o);
+            const frag bl_ = *reinterpret_cast<const frag*>(gl + o);
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms) {
+              acc[a][2 * ms + nn] = M::mma(vfr[ms][kk], bh_, acc[a][2 * ms + nn]);
+              acc[a][2 * ms + nn] = M::mma(vfr[ms][kk], bl_, acc[a][2 * ms + nn]);
+            }
+          }
+      } else {
+        if (a == 0) {
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+              acc[1][n] = M::mma(afr[kk], frag_krows(sN[b & 1], GLD, 16 * n, 32 * kk, lg, lr), acc[1][n]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const frag ka = frag_kcols(sK, QLD, 16 * s + lr, 64 * a + 32 * kk, lg, lr);
+#pragma unroll
+          for (int n = 0; n < 4; ++n) acc[0][n] = M::mma(ka, frag_krows(gh, GLD, 16 * n, 32 * kk, lg, lr), acc[0][n]);
+        }
+        if (a == NDT - 1) {
+          // dv_j = sum_l P_lj dn~_l + w_j G_c^T k_j, value block b: staged in
+          // this wave's 16 rows of sN[b & 1] (read only at a = 0, rewritten
+          // one value block later), then stored as 16-byte row pieces
+          T* st = sN[b & 1];
+          float wj[4];
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) wj[ii] = sw[16 * s + 4 * lg + ii];
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+              st[(16 * s + 4 * lg + ii) * GLD + 16 * n + lr] = from_f32<T>(acc[1][n][ii] + wj[ii] * acc[0][n][ii]);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int row = 16 * s + 8 * h + (lane >> 3), col = 8 * (lane & 7);
+            const u32x4 u = *reinterpret_cast<const u32x4*>(&st[row * GLD + col]);
+            __builtin_amdgcn_raw_buffer_store_b128(u, rdv, ((unsigned)(t0 + row) * DV + 64 * b + col) * ES, 0, 0);
+          }
+          zero_acc(acc[0]);
+          zero_acc(acc[1]);
+        }
+      }
+    }
+  }
+  if (dk_wave) {
+    // dk_j = sum_l D'_lj q_l + w_j (G_c v_j + g_c); k_j . w_j (G_c v_j + g_c)
+    // over this wave's 32 features of each feature block.  dk is staged in
+    // this wave's 32 x 32 corner of sGh[0] (no longer read: the last block
+    // sits in sGh[1]), then stored as 16-byte row pieces.
+    T* st = sGh[0];
+    float wj[2][4];
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) wj[ms][ii] = sw[16 * (2 * sp + ms) + 4 * lg + ii];
+    float kd[2][4] = {};  // k_j . x_j over this lane's features of every block
+    frag dfr[2][2];       // D'^T rows of the two strips
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) dfr[ms][kk] = frag_kcols(sDt, GLD, 16 * (2 * sp + ms) + lr, 32 * kk, lg, lr);
+#pragma unroll
+    for (int a = 0; a < NDT; ++a) {
+      f32x4 t[4];
+      zero_acc(t);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int nn = 0; nn < 2; ++nn) {
+          const frag qb = frag_krows(sQ, QLD, 64 * a + 16 * (2 * fh + nn), 32 * kk, lg, lr);
+#pragma unroll
+          for (int ms = 0; ms < 2; ++ms) t[2 * ms + nn] = M::mma(dfr[ms][kk], qb, t[2 * ms + nn]);
+        }
+      float gd[2];
+      T kv[2][2][4];
+#pragma unroll
+      for (int nn = 0; nn < 2; ++nn) {
+        const int d = 64 * a + 16 * (2 * fh + nn) + lr;
+        gd[nn] = sg[d];
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) kv[ms][nn][ii] = sK[(16 * (2 * sp + ms) + 4 * lg + ii) * QLD + d];
+      }
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+        for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int j = 16 * (2 * sp + ms) + 4 * lg + ii;
+            const float x = wj[ms][ii] * (acc[a][2 * ms + nn][ii] + gd[nn]);
+            st[j * GLD + 32 * fh + 16 * nn + lr] = from_f32<T>(t[2 * ms + nn][ii] + x);
+            kd[ms][ii] += to_f32(kv[ms][nn][ii]) * x;
+          }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 32 * sp + 16 * h + (lane >> 2), col = 32 * fh + 8 * (lane & 3);
+        const u32x4 u = *reinterpret_cast<const u32x4*>(&st[row * GLD + col]);
+        __builtin_amdgcn_raw_buffer_store_b128(u, rdk, ((unsigned)(t0 + row) * DQK + 64 * a + col) * ES, 0, 0);
+      }
+    }
+    // row sums over the 16 lanes lr (DPP rotations within rows of 16)
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        kd[ms][ii] += dpp_ror<8>(kd[ms][ii]);
+        kd[ms][ii] += dpp_ror<4>(kd[ms][ii]);
+        kd[ms][ii] += dpp_ror<2>(kd[ms][ii]);
+        kd[ms][ii] += dpp_ror<1>(kd[ms][ii]);
+        if (lr == 0) skd[fh][16 * (2 * sp + ms) + 4 * lg + ii] = kd[ms][ii];
+      }
+  }
+  __syncthreads();
+  // the rest of k . dk, one slot per token (the launcher passes 1 slot)
+  if (tid < BL) p.ws_kdk[(size_t)bh * p.NC * BL + (size_t)c * BL + tid] = skd[0][tid] + skd[1][tid];
+}
+
 // ---------------------------------------------------------------- kernel 5
 // d i_pre_t = k_t . dk_t; d log f_t = sum_{s >= t} (q_s . dq_s - k_s . dk_s);
 // d f_pre = d log f * sigmoid(-f_pre).  Two passes over (batch*head, chunk)
 // work-groups of one wave: the chunk totals of q.dq - k.dk, then each chunk's
 // in-chunk suffix sums plus the totals of the chunks after it.
-__global__ __launch_bounds__(64) void bwd_gate_total_kernel(BwdParams p, int NDT) {
+// slots: partials of k . dk per token that the dk kernel left in ws_kdk.
+__global__ __launch_bounds__(64) void bwd_gate_total_kernel(BwdParams p, int slots) {
   const int lane = threadIdx.x;
   const int bh = blockIdx.x / p.NC, c = blockIdx.x % p.NC;
   const size_t tg = (size_t)bh * p.NC * BL + (size_t)c * BL + lane;
   float kdk = p.ws_kdki[tg];
-  for (int d = 0; d < NDT; ++d) kdk += p.ws_kdk[tg * NDT + d];
+  for (int d = 0; d < slots; ++d) kdk += p.ws_kdk[tg * slots + d];
   float dF = c * BL + lane < p.T ? p.ws_qdq[tg] - kdk : 0.f;
   p.ws_kdki[tg] = kdk;  // k . dk, complete
   p.ws_qdq[tg] = dF;    // q . dq - k . dk
@@ -1347,9 +1672,16 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   } else {
     hipLaunchKernelGGL(bwd_scan_kernel<8>, dim3(ge, BH), dim3(256), 0, stream, p, DQK);
   }
-  hipLaunchKernelGGL((bwd_dkv_kernel<T, DQK, NB>), dim3(nch * (DQK / 64 + p.DV / 64)), dim3(256), 0, stream, p);
+  // slots per token of the k . dk partials the dk kernel leaves
+  int kdk_slots = DQK / 64;
+  if constexpr (sizeof(T) == 2 && NB == 1 && DQK == 256) {
+    hipLaunchKernelGGL((bwd_dkv_chunk_kernel<DQK / 64>), dim3(nch), dim3(512), 0, stream, p);
+    kdk_slots = 1;
+  } else {
+    hipLaunchKernelGGL((bwd_dkv_kernel<T, DQK, NB>), dim3(nch * (DQK / 64 + p.DV / 64)), dim3(256), 0, stream, p);
+  }
   if (!p.ret) {  // retention has no gates or normaliser to differentiate
-    hipLaunchKernelGGL(bwd_gate_total_kernel, dim3(nch), dim3(64), 0, stream, p, DQK / 64);
+    hipLaunchKernelGGL(bwd_gate_total_kernel, dim3(nch), dim3(64), 0, stream, p, kdk_slots);
     hipLaunchKernelGGL((bwd_gate_kernel<T>), dim3(nch), dim3(64), 0, stream, p, (DQK / 64) * (p.DV / 64));
     if (p.dbias) hipLaunchKernelGGL(bwd_bias_kernel, dim3((unsigned)p.H), dim3(256), 0, stream, p);
   }

@@ -131,7 +131,7 @@ struct BwdParams {
   int NSEG;           // segments of 32 chunks of the two-level scan
   float* ws_qdq;      // [B*H][NC*64] q . dq
   float* ws_kdki;     // [B*H][NC*64] in-chunk part of k . dk
-  float* ws_kdk;      // [B*H][NC*64][d_qk/64] partials of the rest of k . dk
+  float* ws_kdk;      // [B*H][NC*64][d_qk/64 or 1] partials of the rest of k . dk
   void* dq;
   void* dk;
   void* dv;

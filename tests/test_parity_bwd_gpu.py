@@ -87,7 +87,9 @@ def test_bwd_fp32_state_bias_ragged(gpu):
 
 
 @pytest.mark.parametrize("dqk,dv,T,with_o,init", [(64, 128, 200, True, False), (128, 128, 256, False, True),
-                                                  (64, 64, 1, True, True), (64, 192, 64, False, False)])
+                                                  (64, 64, 1, True, True), (64, 192, 64, False, False),
+                                                  (256, 128, 100, True, True), (256, 384, 130, False, False),
+                                                  (256, 128, 1, True, False)])
 def test_bwd_bf16(gpu, dqk, dv, T, with_o, init):
     x = mlstm_inputs(2, 2, T, dqk, dv, seed=2100 + T + dqk, dtype="bf16", k_scale=dqk ** -0.5,
                      f_mix=True, with_o=with_o, bias="uniform")
