@@ -437,6 +437,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   // dn~ . (v_l - y_j) must not see dn~ rounded; the initial state is exact
   // fp32 input)
   __shared__ __attribute__((aligned(16))) T sXl[sizeof(T) == 2 ? BL * LD : 8];
+  // o_pre of the current d_v slice, as loaded (exact in T), unpadded [j][c]:
+  // the d o_pre tile reads it in the MFMA layout
+  __shared__ __attribute__((aligned(16))) T sO[RET ? 8 : BL * 64];
   __shared__ float sa[BL], sM[BL], sal[BL], sem[BL], sw[BL];
   __shared__ float sqn[BL], srow[BL], sden[BL], ssg[BL], sdz[BL];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -547,14 +550,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   const auto rdh = make_rsrc(static_cast<const T*>(p.dh) + (size_t)bh * p.T * p.DV, (unsigned)(p.T * p.DV) * ES);
   const auto ro = make_rsrc(p.o_pre ? static_cast<const T*>(p.o_pre) + (size_t)bh * p.T * p.DV : nullptr,
                             p.o_pre ? (unsigned)(p.T * p.DV) * ES : 0u);
-  T* dow = p.d_o ? static_cast<T*>(p.d_o) + (size_t)bh * p.T * p.DV : nullptr;
+  const auto rdo = make_rsrc(p.d_o ? static_cast<T*>(p.d_o) + (size_t)bh * p.T * p.DV : nullptr,
+                             p.d_o ? (unsigned)(p.T * p.DV) * ES : 0u);
+  const bool has_o = !RET && p.o_pre;
   const float rden = sden[r];
   f32x4 accD[NB][4];  // per memory block: dN_b V_b^T
 #pragma unroll
   for (int b = 0; b < NB; ++b) zero_acc(accD[b]);
   float sint[4] = {0.f, 0.f, 0.f, 0.f};  // rows 16 w + 4 lg + i: dn~ . (Q S~) partials
   // Global loads run one step ahead: slice cs + 1's dh, o_pre, v and the next
-  // S~ tile are in flight while the current ones are multiplied.
+  // S~ tile are in flight while the current ones are multiplied.  They are
+  // issued on every path (the last step reloads its own slice and tile), so
+  // that the compiler counts the same loads in flight everywhere and waits
+  // only for the ones it needs.
   const int NCS = p.DV / 64;
   constexpr int NDS = DQK / 64;
   float g[16], x[16], vv[16], sv[16];
@@ -562,11 +570,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     const unsigned off = ((unsigned)(t0 + r) * p.DV + cs * 64 + c0) * ES;
     load16f<T>(rdh, off, g);
     load16f<T>(rv, off, vv);
-    if (p.o_pre) load16f<T>(ro, off, x);
+    load16f<T>(ro, off, x);  // zeros without o_pre
   };
   load_slice(0);
   const bool readout = has_state && !RET;
-  if (readout) ld16(Sp + (size_t)r * p.DV + c0, sv);
+  ld16(Sp + (size_t)r * p.DV + c0, sv);  // (unused without a readout)
   for (int cs = 0; cs < NCS; ++cs) {
     if (p.o_pre) {
 #pragma unroll
@@ -583,7 +591,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       for (int e = 0; e < 16; ++e) g[e] -= to_f32(from_f32<T>(g[e]));
       st_row16<T>(sXl, r, c0, g);
     }
-    if (cs + 1 < NCS) load_slice(cs + 1);
+    if constexpr (!RET) {
+      if (has_o) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) store4f(sO + r * 64 + c0 + 4 * h, x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]);
+      }
+    }
+    load_slice(cs + 1 < NCS ? cs + 1 : cs);
     __syncthreads();
     f32x4 accI[4], accN[4];
     zero_acc(accI);
@@ -620,27 +634,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
           for (int e = 0; e < 16; ++e) sv[e] -= to_f32(from_f32<T>(sv[e]));
           st_row16<T>(sXl, r, c0, sv);
         }
-        if (ds + 1 < NDS) ld16(Sp + (size_t)((ds + 1) * 64 + r) * p.DV + cs * 64 + c0, sv);
-        else if (cs + 1 < NCS) ld16(Sp + (size_t)r * p.DV + (cs + 1) * 64 + c0, sv);
+        {  // the next S~ tile
+          const bool more = ds + 1 < NDS;
+          const int nds = more ? ds + 1 : 0, ncs = more ? cs : (cs + 1 < NCS ? cs + 1 : cs);
+          ld16(Sp + (size_t)(nds * 64 + r) * p.DV + ncs * 64 + c0, sv);
+        }
         __syncthreads();
         mma64x<T, false, true>(accI, sQ + ds * 64, LDQ, sX, LD, w, lane);  // sum_d q_jd S~_dc
         if constexpr (sizeof(T) == 2) mma64x<T, false, true>(accI, sQ + ds * 64, LDQ, sXl, LD, w, lane);
       }
     }
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int col = 16 * n + lr;
+    for (int n = 0; n < 4; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = 16 * w + 4 * lg + i;
-        sint[i] += dnv[n][i] * accI[n][i];
-        if (p.o_pre && t0 + j < p.T) {
-          const size_t e = (size_t)(t0 + j) * p.DV + cs * 64 + col;
-          const float y = (sal[j] * accI[n][i] + accN[n][i]) * sden[j];
-          const float o = sigmoidf_(to_f32(static_cast<const T*>(p.o_pre)[(size_t)bh * p.T * p.DV + e]));
-          const float g = to_f32(static_cast<const T*>(p.dh)[(size_t)bh * p.T * p.DV + e]);
-          dow[e] = from_f32<T>(g * y * (o * (1.f - o)));
-        }
+      for (int i = 0; i < 4; ++i) sint[i] += dnv[n][i] * accI[n][i];
+    if constexpr (!RET) {
+      // d o_pre = dh h~ sigma'(o_pre) with h~ = num~ / den~ and dn~ = sigma(o) dh / den~:
+      // d o_pre = dn~ num~ sigma(-o_pre), num~ = alpha Q S~ + P V (rows past T are dropped)
+      if (has_o) {
+        float alj[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) alj[i] = sal[16 * w + 4 * lg + i];
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = 16 * w + 4 * lg + i, col = 16 * n + lr;
+            const float o = to_f32(sO[j * 64 + col]);
+            const float d = dnv[n][i] * (alj[i] * accI[n][i] + accN[n][i]) * sigmoidf_(-o);
+            bstore1<T>(rdo, ((unsigned)(t0 + j) * p.DV + cs * 64 + col) * ES, d);
+          }
       }
     }
   }

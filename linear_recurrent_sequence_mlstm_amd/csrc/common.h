@@ -206,6 +206,15 @@ __device__ __forceinline__ void raw4_to_f32(const Raw4<T>& r, float (&x)[4]) {
     for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(r.v[i]);
   }
 }
+// One element converted to T and stored through a buffer resource (a store
+// past its end is dropped).
+template <typename T>
+__device__ __forceinline__ void bstore1(__amdgpu_buffer_rsrc_t r, unsigned byte_off, float a) {
+  if constexpr (sizeof(T) == 2)
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)a), r, byte_off, 0, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), r, byte_off, 0, 0);
+}
 // Four consecutive elements converted to T and stored through a buffer
 // resource (stores past its end are dropped).
 template <typename T>
