@@ -813,20 +813,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   const auto rq = make_rsrc(static_cast<const T*>(p.q) + (size_t)bh * p.T * DQK, (unsigned)(p.T * DQK) * ES);
   const auto rk = make_rsrc(static_cast<const T*>(p.k) + (size_t)bh * p.T * DQK, (unsigned)(p.T * DQK) * ES);
   {
-    float x[16], y[16], d[16];
+    float x[16], y[16], d[16], d2[16];
     load16f<T>(rq, ((unsigned)(t0 + r) * DQK + dt * 64 + c0) * ES, x);
     load16f<T>(rk, ((unsigned)(t0 + r) * DQK + dt * 64 + c0) * ES, y);
-    const T* Dw = static_cast<const T*>(p.wsDt) + ((size_t)bh * p.NC + c) * NB * BL * BL;  // D'^T [l][j]
-#pragma unroll
-    for (int e = 0; e < 16; ++e) d[e] = to_f32(Dw[r * BL + c0 + e]);
+    // D'^T [l][j] of each memory block
+    const auto rD = make_rsrc(static_cast<const T*>(p.wsDt) + ((size_t)bh * p.NC + c) * NB * BL * BL,
+                              (unsigned)(NB * BL * BL) * ES);
+    load16f<T>(rD, (unsigned)(r * BL + c0) * ES, d);
+    if constexpr (NB > 1) load16f<T>(rD, (unsigned)(BL * BL + r * BL + c0) * ES, d2);
     st_row16<T>(sQ, r, c0, x);
     st_row16<T>(sB, r, c0, y);
     st_row16<T>(sA, r, c0, d);
-    if constexpr (NB > 1) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) d[e] = to_f32(Dw[BL * BL + r * BL + c0 + e]);
-      st_row16<T>(sA2, r, c0, d);
-    }
+    if constexpr (NB > 1) st_row16<T>(sA2, r, c0, d2);
   }
   __syncthreads();
   f32x4 acc[4], accx[4];
@@ -848,17 +846,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   float* Uw = p.ws_U + ((size_t)bh * p.NC + c) * NST;
   const float rden = sden[r], alr = sal[r];
   const int NCS = p.DV / 64;
-  float g[16], x[16], sv[16];  // one slice ahead (see the scores kernel)
+  // S~ rows [64 dt, 64 dt + 64) of the chunk's start state (zeros without one)
+  const auto rS = make_rsrc(Sp + (size_t)dt * 64 * p.DV, has_state ? (unsigned)(64 * p.DV) * 4u : 0u);
+  // one slice ahead (see the scores kernel), issued on every path: the last
+  // step reloads its own slice
+  float g[16], x[16], sv[16];
   auto load_slice = [&](int cs) {
     const unsigned off = ((unsigned)(t0 + r) * p.DV + cs * 64 + c0) * ES;
     load16f<T>(rdh, off, g);
-    if (p.o_pre) load16f<T>(ro, off, x);
-    if (has_state) ld16(Sp + (size_t)(dt * 64 + r) * p.DV + cs * 64 + c0, sv);
+    load16f<T>(ro, off, x);  // zeros without o_pre
+    load16f<float>(rS, (unsigned)(r * p.DV + cs * 64 + c0) * 4u, sv);
   };
-  if (!has_state) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sv[e] = 0.f;
-  }
   load_slice(0);
   for (int cs = 0; cs < NCS; ++cs) {
     if (p.o_pre) {
@@ -882,17 +880,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
       st_row16<T>(sBl, r, c0, sv);
       st_row16<T>(sAl, r, c0, g);
     }
-    if (cs + 1 < NCS) load_slice(cs + 1);
+    load_slice(cs + 1 < NCS ? cs + 1 : cs);
     __syncthreads();
     mma64x<T, false, false>(accx, sA, LD, sB, LD, w, lane);  // sum_c alpha_j dN_jc S~_dc
     if constexpr (sizeof(T) == 2) {
       mma64x<T, false, false>(accx, sA, LD, sBl, LD, w, lane);
       mma64x<T, false, false>(accx, sAl, LD, sB, LD, w, lane);
     }
+    // U_dc = sum_j q_jd alpha_j dN_jc, held transposed (u[n][i] = U[16 n + lr][16 w + 4 lg + i])
+    // so that each lane stores 4 consecutive columns at once
     f32x4 u[4];
     zero_acc(u);
-    mma64x<T, true, true>(u, sQ, LD, sA, LD, w, lane);  // U_dc = sum_j q_jd alpha_j dN_jc
-    if constexpr (sizeof(T) == 2) mma64x<T, true, true>(u, sQ, LD, sAl, LD, w, lane);
+    mma64x<T, true, true>(u, sA, LD, sQ, LD, w, lane);
+    if constexpr (sizeof(T) == 2) mma64x<T, true, true>(u, sAl, LD, sQ, LD, w, lane);
     if constexpr (NB > 1) {  // the memory (and its gradient) is block-diagonal
 #pragma unroll
       for (int n = 0; n < 4; ++n)
@@ -900,17 +900,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     }
 #pragma unroll
     for (int n = 0; n < 4; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        Uw[(size_t)(dt * 64 + 16 * w + 4 * lg + i) * p.DV + cs * 64 + 16 * n + lr] = u[n][i];
+      *reinterpret_cast<float4*>(Uw + (size_t)(dt * 64 + 16 * n + lr) * p.DV + cs * 64 + 16 * w + 4 * lg) =
+          make_float4(u[n][0], u[n][1], u[n][2], u[n][3]);
   }
   if (tid < 64) {  // normaliser column: sum_j q_jd alpha_j dz~_j
     float a = 0.f;
     for (int j = 0; j < BL; ++j) a += to_f32(sQ[j * LD + tid]) * sal[j] * sdz[j];
     Uw[(size_t)DQK * p.DV + dt * 64 + tid] = a;
   }
-  // dq = intra + alpha (S~ dn~ + n~ dz~); q . dq partial
-  T* dqw = static_cast<T*>(p.dq) + (size_t)bh * p.T * DQK;
+  // dq = intra + alpha (S~ dn~ + n~ dz~) (rows past T are dropped)
+  const auto rdq = make_rsrc(static_cast<T*>(p.dq) + (size_t)bh * p.T * DQK, (unsigned)(p.T * DQK) * ES);
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int d = 16 * n + lr;
@@ -918,7 +917,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     for (int i = 0; i < 4; ++i) {
       const int j = 16 * w + 4 * lg + i;
       const float v = acc[n][i] + accx[n][i] + sal[j] * sdz[j] * snp[d];
-      if (t0 + j < p.T) dqw[(size_t)(t0 + j) * DQK + dt * 64 + d] = from_f32<T>(v);
+      bstore1<T>(rdq, ((unsigned)(t0 + j) * DQK + dt * 64 + d) * ES, v);
     }
   }
 }
