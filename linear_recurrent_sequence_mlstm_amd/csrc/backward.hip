@@ -1141,6 +1141,13 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
   const auto rq = make_rsrc(static_cast<const T*>(p.q) + (size_t)bh * p.T * DQK, (unsigned)(p.T * DQK) * ES);
   const auto rk = make_rsrc(static_cast<const T*>(p.k) + (size_t)bh * p.T * DQK, (unsigned)(p.T * DQK) * ES);
   const auto rv = make_rsrc(static_cast<const T*>(p.v) + (size_t)bh * p.T * p.DV, (unsigned)(p.T * p.DV) * ES);
+  // G_c; a load through rnone reads zeros and touches no memory: the next
+  // slice's loads are issued on every path, so that the compiler counts the
+  // same loads in flight everywhere
+  const auto rG = make_rsrc(Gc, (unsigned)(DQK * p.DV) * 4u);
+  const auto rnone = make_rsrc(nullptr, 0u);
+  // this chunk's D'^T and P^T tiles of each memory block
+  const size_t tile0 = ((size_t)bh * p.NC + c) * NB * BL * BL;
   f32x4 acc[4], accx[4];
   zero_acc(acc);
   zero_acc(accx);
@@ -1148,19 +1155,19 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
     // dk_j = sum_l D'_lj q_l + w_j (G_c v_j + g_c), features [64 dt, 64 dt + 64)
     const int dt = tile;
     if (tid < 64) sg[tid] = Gc[(size_t)DQK * p.DV + dt * 64 + tid];
+    const int NCS = p.DV / 64;
+    float vv[16], sv[16];  // V and G slices, one ahead (the first in flight with Q, K, D'^T)
     {
-      float x[16], y[16], d[16];
+      float x[16], y[16], d[16], d2[16];
       load16f<T>(rq, ((unsigned)(t0 + r) * DQK + dt * 64 + c0) * ES, x);
       load16f<T>(rk, ((unsigned)(t0 + r) * DQK + dt * 64 + c0) * ES, y);
-      const T* Dt = static_cast<const T*>(p.wsDt) + ((size_t)bh * p.NC + c) * NB * BL * BL;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) d[e] = to_f32(Dt[r * BL + c0 + e]);
+      const auto rD = make_rsrc(static_cast<const T*>(p.wsDt) + tile0, (unsigned)(NB * BL * BL) * ES);
+      load16f<T>(rD, (unsigned)(r * BL + c0) * ES, d);
+      if constexpr (NB > 1) load16f<T>(rD, (unsigned)(BL * BL + r * BL + c0) * ES, d2);
+      load16f<T>(rv, ((unsigned)(t0 + r) * p.DV + c0) * ES, vv);
+      load16f<float>(rG, (unsigned)((dt * 64 + r) * p.DV + c0) * 4u, sv);
       st_row16<T>(sA, r, c0, d);
-      if constexpr (NB > 1) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) d[e] = to_f32(Dt[BL * BL + r * BL + c0 + e]);
-        st_row16<T>(sA2, r, c0, d);
-      }
+      if constexpr (NB > 1) st_row16<T>(sA2, r, c0, d2);
       st_row16<T>(sB, r, c0, x);  // Q [l][d]
       st_row16<T>(sK, r, c0, y);
     }
@@ -1174,10 +1181,6 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
       for (int n = 0; n < 4; ++n)
         if (col_block<NB>(n) == 1) acc[n] = t1[n];
     }
-    const int NCS = p.DV / 64;
-    float vv[16], sv[16];  // one slice ahead
-    load16f<T>(rv, ((unsigned)(t0 + r) * p.DV + c0) * ES, vv);
-    ld16(Gc + (size_t)(dt * 64 + r) * p.DV + c0, sv);
     for (int cs = 0; cs < NCS; ++cs) {
       __syncthreads();
       st_row16<T>(sA, r, c0, vv);
@@ -1187,15 +1190,17 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
         for (int e = 0; e < 16; ++e) sv[e] -= to_f32(from_f32<T>(sv[e]));
         st_row16<T>(sBl, r, c0, sv);
       }
-      if (cs + 1 < NCS) {
-        load16f<T>(rv, ((unsigned)(t0 + r) * p.DV + (cs + 1) * 64 + c0) * ES, vv);
-        ld16(Gc + (size_t)(dt * 64 + r) * p.DV + (cs + 1) * 64 + c0, sv);
+      {
+        const bool more = cs + 1 < NCS;
+        load16f<T>(more ? rv : rnone, ((unsigned)(t0 + r) * p.DV + (cs + 1) * 64 + c0) * ES, vv);
+        load16f<float>(more ? rG : rnone, (unsigned)((dt * 64 + r) * p.DV + (cs + 1) * 64 + c0) * 4u, sv);
       }
       __syncthreads();
       mma64x<T, false, false>(accx, sA, LD, sB, LD, w, lane);  // sum_c v_jc G_dc
       if constexpr (sizeof(T) == 2) mma64x<T, false, false>(accx, sA, LD, sBl, LD, w, lane);
     }
-    T* dkw = static_cast<T*>(p.dk) + (size_t)bh * p.T * DQK;
+    // (rows past T are dropped by the descriptor)
+    const auto rdk = make_rsrc(static_cast<T*>(p.dk) + (size_t)bh * p.T * DQK, (unsigned)(p.T * DQK) * ES);
     float kd[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
@@ -1204,15 +1209,16 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
       for (int i = 0; i < 4; ++i) {
         const int j = 16 * w + 4 * lg + i;
         const float x = sw[j] * (accx[n][i] + sg[d]);
-        const float v = acc[n][i] + x;
-        if (t0 + j < p.T) dkw[(size_t)(t0 + j) * DQK + dt * 64 + d] = from_f32<T>(v);
+        bstore1<T>(rdk, ((unsigned)(t0 + j) * DQK + dt * 64 + d) * ES, acc[n][i] + x);
         kd[i] += to_f32(sK[j * LD + d]) * x;  // w_j k_j . (G_c v_j + g_c)
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int d = 1; d < 16; d <<= 1) kd[i] += __shfl_xor(kd[i], d, 64);
+    for (int i = 0; i < 4; ++i) {  // row sums over the 16 lanes lr
+      kd[i] += dpp_ror<8>(kd[i]);
+      kd[i] += dpp_ror<4>(kd[i]);
+      kd[i] += dpp_ror<2>(kd[i]);
+      kd[i] += dpp_ror<1>(kd[i]);
       if (lr == 0) p.ws_kdk[((size_t)bh * p.NC * BL + (size_t)c * BL + 16 * w + 4 * lg + i) * NDT + dt] = kd[i];
     }
   } else {
@@ -1221,28 +1227,27 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
     const auto rdh = make_rsrc(static_cast<const T*>(p.dh) + (size_t)bh * p.T * p.DV, (unsigned)(p.T * p.DV) * ES);
     const auto ro = make_rsrc(p.o_pre ? static_cast<const T*>(p.o_pre) + (size_t)bh * p.T * p.DV : nullptr,
                               p.o_pre ? (unsigned)(p.T * p.DV) * ES : 0u);
+    float y[16], sv[16];  // K and G slices, one ahead (the first in flight with dh, P^T)
     {
       const float rden = p.ws_rden[(size_t)bh * p.NC * BL + (size_t)c * BL + r];
-      float g[16], x[16], d[16];
+      float g[16], x[16], d[16], d2[16];
       const unsigned off = ((unsigned)(t0 + r) * p.DV + ct * 64 + c0) * ES;
       load16f<T>(rdh, off, g);
+      load16f<T>(ro, off, x);  // zeros without o_pre
+      const auto rP = make_rsrc(static_cast<const T*>(p.wsPt) + tile0, (unsigned)(NB * BL * BL) * ES);
+      load16f<T>(rP, (unsigned)(r * BL + c0) * ES, d);
+      if constexpr (NB > 1) load16f<T>(rP, (unsigned)(BL * BL + r * BL + c0) * ES, d2);
+      load16f<T>(rk, ((unsigned)(t0 + r) * DQK + c0) * ES, y);
+      load16f<float>(rG, (unsigned)(r * p.DV + ct * 64 + c0) * 4u, sv);
       if (p.o_pre) {
-        load16f<T>(ro, off, x);
 #pragma unroll
         for (int e = 0; e < 16; ++e) g[e] = dn_of(g[e], sigmoidf_(x[e]), rden);
       } else {
 #pragma unroll
         for (int e = 0; e < 16; ++e) g[e] = dn_of(g[e], 1.f, rden);
       }
-      const T* Pt = static_cast<const T*>(p.wsPt) + ((size_t)bh * p.NC + c) * NB * BL * BL;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) d[e] = to_f32(Pt[r * BL + c0 + e]);
       st_row16<T>(sA, r, c0, d);
-      if constexpr (NB > 1) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) d[e] = to_f32(Pt[BL * BL + r * BL + c0 + e]);
-        st_row16<T>(sA2, r, c0, d);
-      }
+      if constexpr (NB > 1) st_row16<T>(sA2, r, c0, d2);
       st_row16<T>(sB, r, c0, g);  // dN [l][c]
     }
     __syncthreads();
@@ -1255,29 +1260,27 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
       for (int n = 0; n < 4; ++n)
         if (col_block<NB>(n) == 1) acc[n] = t1[n];
     }
-    float y[16], sv[16];  // one feature slice ahead
-    load16f<T>(rk, ((unsigned)(t0 + r) * DQK + c0) * ES, y);
-    ld16(Gc + (size_t)r * p.DV + ct * 64 + c0, sv);
     for (int ds = 0; ds < NDT; ++ds) {
       __syncthreads();
       st_row16<T>(sA, r, c0, y);
       st_row16<T>(sB, r, c0, sv);  // G [d][c]
-      if (ds + 1 < NDT) {
-        load16f<T>(rk, ((unsigned)(t0 + r) * DQK + (ds + 1) * 64 + c0) * ES, y);
-        ld16(Gc + (size_t)((ds + 1) * 64 + r) * p.DV + ct * 64 + c0, sv);
+      {
+        const bool more = ds + 1 < NDT;
+        load16f<T>(more ? rk : rnone, ((unsigned)(t0 + r) * DQK + (ds + 1) * 64 + c0) * ES, y);
+        load16f<float>(more ? rG : rnone, (unsigned)(((ds + 1) * 64 + r) * p.DV + ct * 64 + c0) * 4u, sv);
       }
       __syncthreads();
       mma64x<T, false, true>(accx, sA, LD, sB, LD, w, lane);  // sum_d k_jd G_dc
     }
-    T* dvw = static_cast<T*>(p.dv) + (size_t)bh * p.T * p.DV;
+    // (rows past T are dropped by the descriptor)
+    const auto rdv = make_rsrc(static_cast<T*>(p.dv) + (size_t)bh * p.T * p.DV, (unsigned)(p.T * p.DV) * ES);
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       const int col = 16 * n + lr;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 16 * w + 4 * lg + i;
-        const float v = acc[n][i] + sw[j] * accx[n][i];
-        if (t0 + j < p.T) dvw[(size_t)(t0 + j) * p.DV + ct * 64 + col] = from_f32<T>(v);
+        bstore1<T>(rdv, ((unsigned)(t0 + j) * p.DV + ct * 64 + col) * ES, acc[n][i] + sw[j] * accx[n][i]);
       }
     }
   }
