@@ -83,7 +83,7 @@ PREFILL_KERNELS = ("local_state_kernel", "superchunk_scan_kernel", "chunk_kernel
 # the launches of one backward call of the 7B workload (the forward's state
 # passes, then the backward kernels)
 BACKWARD_KERNELS = ("bwd_chunk_states_kernel", "bwd_scores_kernel", "bwd_dq_kernel", "bwd_scan_kernel",
-                    "bwd_dkv_kernel", "bwd_gate_total_kernel", "bwd_gate_kernel")
+                    "bwd_dkv_chunk_kernel", "bwd_gate_total_kernel", "bwd_gate_kernel")
 
 
 def traffic_from_profiles(kernels, sha):
