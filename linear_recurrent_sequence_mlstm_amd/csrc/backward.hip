@@ -420,9 +420,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
 // (needed only for dz~ and d o_pre) is not recomputed.
 template <typename T, int DQK, bool RET, int NB>
 // Two waves per SIMD (two work-groups per CU where the LDS allows): left to
-// itself the compiler spends about 300 registers and runs one; the cap
-// measured 10 % on the two-block backward, 3 % at the 7B head shape, and
-// spills nothing.
+// itself the compiler spends about 300 registers and runs one; the cap costs
+// a few spills at the widest shapes and measured 10 % on the two-block
+// backward, 3 % at the 7B head shape.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_scores_kernel(BwdParams p) {
   static_assert(NB == 1 || DQK == 64, "two blocks on 64-wide heads only");
   constexpr int LD = BT<T>::LD;
