@@ -187,6 +187,36 @@ __device__ __forceinline__ void load16f(__amdgpu_buffer_rsrc_t r, unsigned byte_
   }
 }
 
+// 16 consecutive elements of type S as loaded (raw words), to be unpacked
+// later by unpack16f: a prefetch kept in this form is not waited for until
+// its values are used.
+template <typename S>
+struct Raw16 {
+  u32x4 u[sizeof(S) == 2 ? 2 : 4];
+};
+template <typename S>
+__device__ __forceinline__ void load16raw(__amdgpu_buffer_rsrc_t r, unsigned byte_off, Raw16<S>& x) {
+#pragma unroll
+  for (int h = 0; h < (sizeof(S) == 2 ? 2 : 4); ++h) x.u[h] = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off + 16 * h, 0, 0);
+}
+template <typename S>
+__device__ __forceinline__ void unpack16f(const Raw16<S>& x, float (&y)[16]) {
+  if constexpr (sizeof(S) == 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[8 * h + 2 * e] = __uint_as_float(x.u[h][e] << 16);
+        y[8 * h + 2 * e + 1] = __uint_as_float(x.u[h][e] & 0xffff0000u);
+      }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[4 * h + e] = __uint_as_float(x.u[h][e]);
+  }
+}
+
 // 16 consecutive fp32 values (in bounds).
 __device__ __forceinline__ void ld16(const float* src, float (&x)[16]) {
 #pragma unroll
@@ -307,17 +337,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
   const int cend = (p.ws_cT && sc == p.NS - 1) ? ce + 1 : ce;
   const auto rk = make_rsrc(static_cast<const T*>(p.k) + (size_t)bh * p.T * DQK, (unsigned)(p.T * DQK) * ES);
   const auto rv = make_rsrc(static_cast<const T*>(p.v) + (size_t)bh * p.T * p.DV, (unsigned)(p.T * p.DV) * ES);
-  float kx[16], vx[16];
-  load16f<T>(rk, ((unsigned)(cb * BL + r) * DQK + dt * 64 + c0) * ES, kx);
-  load16f<T>(rv, ((unsigned)(cb * BL + r) * p.DV + ct * 64 + c0) * ES, vx);
-  // gate logs of the chunk to update next, one chunk ahead
-  float ga = 0.f, gL = 0.f, bL = 0.f;
-  if (tid < BL) {
-    const size_t tg = (size_t)bh * NCL + (size_t)cb * BL;
-    ga = p.ws_ga[tg + tid];
+  const auto rnone = make_rsrc(nullptr, 0u);
+  // The chunk to update next: its K and V slices (raw, unpacked when staged)
+  // and gate logs load one chunk ahead, on every path and in every wave, so
+  // that the compiler waits for them alone and not for the state stores
+  // issued after them (a load past the walk goes through rnone: zeros).
+  Raw16<T> kraw, vraw;
+  float ga, gL, bL;
+  auto load_next = [&](int cc) __attribute__((always_inline)) {
+    const bool in = cc + 1 < cend;
+    load16raw<T>(in ? rk : rnone, ((unsigned)(cc * BL + r) * DQK + dt * 64 + c0) * ES, kraw);
+    load16raw<T>(in ? rv : rnone, ((unsigned)(cc * BL + r) * p.DV + ct * 64 + c0) * ES, vraw);
+    const size_t tg = (size_t)bh * NCL + (size_t)min(cc, p.NC - 1) * BL;
+    ga = p.ws_ga[tg + (tid & (BL - 1))];
     gL = p.ws_gg[tg + BL - 1];
     bL = p.ws_gb[tg + BL - 1];
-  }
+  };
+  load_next(cb);
   for (int c = cb; c < cend; ++c) {
     if (c == ce) {
       // the final state: this tile's share of <dC_T, S~_T> (+ <dn_T, n~_T>)
@@ -356,20 +392,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
     if (lead && dt == 0 && tid == 0) p.ws_min[(size_t)bh * p.NC + c] = m;
     if (c + 1 == cend) break;  // the next superchunk starts from its own start state
     __syncthreads();  // previous chunk's operands are consumed
+    const float ML = fmaxf(m, gL);
     if (tid < BL) {
-      const float ML = fmaxf(m, gL);
       sw[tid] = exp2_fast(ga - ML);
       if (tid == 0) sdec = exp2_fast(m - ML);
-      m = bL + ML;
-      if (c + 2 < cend) {
-        const size_t tg = (size_t)bh * NCL + (size_t)(c + 1) * BL;
-        ga = p.ws_ga[tg + tid];
-        gL = p.ws_gg[tg + BL - 1];
-        bL = p.ws_gb[tg + BL - 1];
-      }
     }
+    m = bL + ML;
     __syncthreads();
     const float wr = sw[r];
+    float kx[16], vx[16];
+    unpack16f<T>(kraw, kx);
+    unpack16f<T>(vraw, vx);
+    load_next(c + 1);
 #pragma unroll
     for (int e = 0; e < 16; ++e) kx[e] *= wr;
     st_row16<T>(sK, r, c0, kx);
@@ -378,10 +412,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
 #pragma unroll
       for (int e = 0; e < 16; ++e) kx[e] -= to_f32(from_f32<T>(kx[e]));
       st_row16<T>(sKl, r, c0, kx);
-    }
-    if (c + 2 < cend) {
-      load16f<T>(rk, ((unsigned)((c + 1) * BL + r) * DQK + dt * 64 + c0) * ES, kx);
-      load16f<T>(rv, ((unsigned)((c + 1) * BL + r) * p.DV + ct * 64 + c0) * ES, vx);
     }
     __syncthreads();
     const float dec = sdec;
