@@ -354,8 +354,10 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
 
   // ---------------------------------------------------------------- state in
   f32x4 st[NT][CT];
-  const float* Sin = nullptr;
-  if (sc > 0 || p.has_init) Sin = p.ws_state + ((size_t)bh * p.NS + sc) * NSTATE;
+  // the start state through a descriptor that is empty when there is none
+  // (reads zero): the loads need no branch and go out back to back
+  const bool has_in = sc > 0 || p.has_init;
+  const auto rSin = make_rsrc(p.ws_state + ((size_t)bh * p.NS + sc) * NSTATE, has_in ? (unsigned)(NSTATE * 4) : 0u);
   // state element (nt, ct, i) of this lane sits at soff + (uni(nt,i)*DVB + ct*16)
   const int soff = blk * DQKB * DVB + (rrow0 + perm_row_lane<T>(lg)) * DVB + wcl0 + lr;
 #pragma unroll
@@ -364,7 +366,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        st[nt][ct][i] = Sin ? Sin[soff + perm_row_uni<T>(nt, i) * DVB + ct * 16] : 0.f;
+        st[nt][ct][i] = bload1<float>(rSin, (unsigned)(soff + perm_row_uni<T>(nt, i) * DVB + ct * 16) * 4u);
   // n~ in fp32 and as the hi/lo rows of the den tile
   auto put_n = [&](int r, float x) __attribute__((always_inline)) {
     sNf[r] = x;
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
     sNh[DQK + r] = from_f32<T>(x - to_f32(hi));
   };
   if constexpr (!RET) {
-    for (int r = tid; r < DQK; r += NTH) put_n(r, Sin ? Sin[CS + r] : 0.f);
+    for (int r = tid; r < DQK; r += NTH) put_n(r, bload1<float>(rSin, (unsigned)(CS + r) * 4u));
   }
   // masked (l > j) tiles of P and their den partials are never written
   for (int e = tid; e < NB * L * PS; e += NTH) sP[e] = from_f32<T>(0.f);
@@ -1123,7 +1125,10 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
                             HAS_O ? (unsigned)T_ * DV * ES : 0u);
   const auto rh = make_rsrc(static_cast<T*>(p.h) + (size_t)bh * T_ * DV, (unsigned)T_ * DV * ES);
   const float bias = p.bias ? p.bias[hd] : 0.f;
-  const float* Sin = (sc > 0 || p.has_init) ? p.ws_state + ((size_t)bh * p.NS + sc) * NSTATE : nullptr;
+  // the start state through a descriptor that is empty when there is none
+  // (reads zero): the loads need no branch and go out back to back
+  const bool has_in = sc > 0 || p.has_init;
+  const auto rSin = make_rsrc(p.ws_state + ((size_t)bh * p.NS + sc) * NSTATE, has_in ? (unsigned)(NSTATE * 4) : 0u);
 
   // n~ into set s: fp32 and as the hi / lo rows of the den tile
   auto put_n = [&](int s, int r, float x) __attribute__((always_inline)) {
@@ -1132,7 +1137,7 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
     sNh[s][r] = hi;
     sNh[s][DQK + r] = (T)(x - (float)hi);
   };
-  for (int r = tid; r < DQK; r += 512) put_n(0, r, Sin ? Sin[CS + r] : 0.f);
+  for (int r = tid; r < DQK; r += 512) put_n(0, r, bload1<float>(rSin, (unsigned)(CS + r) * 4u));
   for (int e = tid; e < L * PS; e += 512) sP[e] = (T)0.f;  // masked tiles are never written
   for (int e = tid; e < NJT * L; e += 512) sDenPart[e] = 0.f;
 
@@ -1274,7 +1279,7 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st[nt][ct][i] = Sin ? Sin[soff + perm_row_uni<T>(nt, i) * DV + ct * 16] : 0.f;
+      for (int i = 0; i < 4; ++i) st[nt][ct][i] = bload1<float>(rSin, (unsigned)(soff + perm_row_uni<T>(nt, i) * DV + ct * 16) * 4u);
   float sig = 0.f;  // the registers hold S~ / 2^sig (lazy decay)
   const int vcol = sw * WC + 4 * (lr & 3);  // transposing-read source column of V^T (+ 16 ct)
   const int kcol = 8 * (lr & 3);            // ... of K^T (+ perm part per tile)
