@@ -160,7 +160,16 @@ def prepare_prefill(torch, mlstm, x, dev):
     return dict(spec=spec, sets=sets, hs=hs, st=st, ws=ws)
 
 
-def bench_prefill(torch, mlstm, prep, args, dev):
+def prefill_events(torch, K):
+    """The prefill leg's events: K pairs around the main kernel and the two
+    around the timed steps.  Made ahead of time (before the decode leg in
+    the full run): creating them takes the host longer than the warm-up's GPU
+    work, and the idle GPU would lower its clocks right before the timed
+    steps."""
+    return dict(kev=_KernelEvents(K), e0=torch.cuda.Event(enable_timing=True), e1=torch.cuda.Event(enable_timing=True))
+
+
+def bench_prefill(torch, mlstm, prep, args, dev, events=None):
     spec, sets, hs, st, ws = (prep[k] for k in ("spec", "sets", "hs", "st", "ws"))
     B, H, T, dqk, dv = (spec[k] for k in ("B", "H", "T", "dqk", "dv"))
 
@@ -169,23 +178,29 @@ def bench_prefill(torch, mlstm, prep, args, dev):
         mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, h=hs[i % len(sets)],
                             state_out=st, workspace=ws)
 
+    K = args.steps
+    ev = events or prefill_events(torch, K)
+    kev, e0, e1 = ev["kev"], ev["e0"], ev["e1"]  # kev: around the main kernel, in a second loop of K calls
+    L = mlstm.lib()
     for i in range(args.warmup):
         call(i)
-    K = args.steps
-    kev = _KernelEvents(K)  # around the main kernel of every timed step
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    L = mlstm.lib()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record()
     for i in range(K):
-        L.mlstm_set_profile_events(*kev.pairs[i])
         call(i)
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    mlstm.set_profile_events()
     step_ms = e0.elapsed_time(e1) / K
+    # the main kernel's time: the same K calls again, each with the library's
+    # events around pass 3 (kept out of the timed steps: a pair of event
+    # records costs about 2.5 us of GPU time per call)
+    for i in range(K):
+        L.mlstm_set_profile_events(*kev.pairs[i])
+        call(i)
+    torch.cuda.synchronize()
+    mlstm.set_profile_events()
     kern_ms = kev.mean_ms()
     kev.close()
     byts, flops = prefill_work(B, H, T, dqk, dv)
@@ -193,7 +208,9 @@ def bench_prefill(torch, mlstm, prep, args, dev):
                 tokens=B * T)
 
 
-def bench_decode(torch, mlstm, workload, args, dev):
+def bench_decode(torch, mlstm, workload, args, dev, finish_later=False):
+    """The decode leg; with finish_later, returns a function that reads its
+    events out afterwards, so that the next leg starts on a busy GPU."""
     d = workload("xlstm7b_decode_B256", steps=args.decode_steps).to(dev)
     S, B, H, dqk = d.q.shape
     dv = d.v.shape[-1]
@@ -205,11 +222,11 @@ def bench_decode(torch, mlstm, workload, args, dev):
     def call(s):
         mlstm.step(d.q[s], d.k[s], d.v[s], d.i_pre[s], d.f_pre[s], C, n, m, bias=d.bias, h=h)
 
+    ev = _KernelEvents(S)  # around every step (both launches of a step); made before the warm-up
     for s in range(min(args.warmup, S)):
         call(s)
     for t in (C, n, m):
         t.zero_()
-    ev = _KernelEvents(S)  # around every step (both launches of a step)
     stream = torch.cuda.current_stream(dev).cuda_stream
     rec = ev.hip.hipEventRecord
     torch.cuda.synchronize()
@@ -220,10 +237,14 @@ def bench_decode(torch, mlstm, workload, args, dev):
         rec(ev.pairs[s][1], ev.ct.c_void_p(stream))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = ev.mean_ms()
-    ev.close()
-    byts, flops = decode_work(B, H, dqk, dv)
-    return dict(B=B, H=H, dqk=dqk, dv=dv, S=S, wall=wall, step_ms=step_ms, bytes=byts, flops=flops)
+
+    def finish():
+        step_ms = ev.mean_ms()
+        ev.close()
+        byts, flops = decode_work(B, H, dqk, dv)
+        return dict(B=B, H=H, dqk=dqk, dv=dv, S=S, wall=wall, step_ms=step_ms, bytes=byts, flops=flops)
+
+    return finish if finish_later else finish()
 
 
 def retention_work(B, H, T, dk, dv, L=64):
@@ -268,12 +289,13 @@ def bench_variants(torch, mlstm, workload, args, dev, only_backward=False):
     stream = torch.cuda.current_stream(dev).cuda_stream
 
     def timed(call, nsets, K, W, chunkwise=True):
-        # chunkwise calls also record the library's events around pass 3
-        for i in range(W):
-            call(i % nsets)
+        # chunkwise calls also record the library's events around pass 3;
+        # the events exist before the warm-up (see bench_prefill)
         ev = _KernelEvents(K)
         kev = _KernelEvents(K) if chunkwise else None
         rec = ev.hip.hipEventRecord
+        for i in range(W):
+            call(i % nsets)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
@@ -573,12 +595,13 @@ def main():
             r = copy_calibration(torch, dev)
         print(json.dumps(dict(leg=args.only, **r)))
         return
-    # The prefill's buffers are set up first and the decode leg (45 ms of
-    # continuous GPU work) runs right before the prefill leg, so that the
-    # prefill's warm-up and timed steps find the GPU at its steady clocks:
-    # after a host-side pause of a few milliseconds this GPU needs about 20 ms
-    # of work to return to them (measured: pass 3 of the prefill takes about
-    # 15 % longer for its first 50 calls after a 1 s pause than after them).
+    # The prefill's buffers and events are set up first and the decode leg (45
+    # ms of continuous GPU work) runs right before the prefill leg, its events
+    # read only afterwards, so that the prefill's warm-up and timed steps find
+    # the GPU at its steady clocks: after a host-side pause of a few
+    # milliseconds this GPU needs about 20 ms of work to return to them
+    # (measured: pass 3 of the prefill takes about 15 % longer for its first 50
+    # calls after a 1 s pause than after them).
     x = workload("xlstm7b_prefill_T8192")
     prep = prepare_prefill(torch, mlstm, x, dev)
     var = []
@@ -586,11 +609,12 @@ def main():
         print("bench: retention and block-diagonal workloads, %d calls each" % args.variant_steps,
               file=sys.stderr, flush=True)
         var = bench_variants(torch, mlstm, workload, args, dev)
-    print("bench: decode xlstm7b_decode_B256 steps=%d" % args.decode_steps, file=sys.stderr, flush=True)
-    dc = bench_decode(torch, mlstm, workload, args, dev)
-    print("bench: prefill xlstm7b_prefill_T8192 steps=%d warmup=%d" % (args.steps, args.warmup),
-          file=sys.stderr, flush=True)
-    pf = bench_prefill(torch, mlstm, prep, args, dev)
+    pf_events = prefill_events(torch, args.steps)
+    print("bench: decode xlstm7b_decode_B256 steps=%d, then prefill xlstm7b_prefill_T8192 steps=%d warmup=%d"
+          % (args.decode_steps, args.steps, args.warmup), file=sys.stderr, flush=True)
+    dc_finish = bench_decode(torch, mlstm, workload, args, dev, finish_later=True)
+    pf = bench_prefill(torch, mlstm, prep, args, dev, events=pf_events)
+    dc = dc_finish()
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
