@@ -80,10 +80,6 @@ def source_sha(*names):
 
 # the launches of one prefill call, in order
 PREFILL_KERNELS = ("local_state_kernel", "superchunk_scan_kernel", "chunk_kernel_ws")
-# the launches of one backward call of the 7B workload (the forward's state
-# passes, then the backward kernels)
-BACKWARD_KERNELS = ("bwd_chunk_states_kernel", "bwd_scores_kernel", "bwd_dq_kernel", "bwd_scan_kernel",
-                    "bwd_dkv_chunk_kernel", "bwd_gate_total_kernel", "bwd_gate_kernel")
 
 
 def traffic_from_profiles(kernels, sha):
@@ -103,6 +99,28 @@ def traffic_from_profiles(kernels, sha):
             return None
         tot += rec.get("bytes_per_launch")
     return tot
+
+
+def workload_traffic(name):
+    """HBM bytes of one whole call of a variant workload (every launch of it)
+    from the committed rocprofv3 counter summary, taken in a run of that
+    workload alone; None when missing or when the kernels' sources changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get("workloads", {}).get(name)
+    except (OSError, ValueError):
+        return None
+    if name.endswith("_backward"):
+        sha = source_sha("backward.hip", "chunkwise.hip", "common.h")
+    elif "decode" in name:
+        sha = source_sha("step.hip", "common.h")
+    else:
+        sha = source_sha("chunkwise.hip", "common.h")
+    if not rec or rec.get("source_sha") != sha:
+        return None
+    return rec.get("bytes_per_call")
 
 
 class _KernelEvents:
@@ -283,8 +301,14 @@ def bench_variants(torch, mlstm, workload, args, dev, only_backward=False):
     """The retention and block-diagonal workloads through the same chunkwise
     kernels: fence-free events around every call (all launches of it) and
     the library's events around its main kernel.  Enough distinct input sets
-    rotate that the inputs do not stay in the 256 MB Infinity Cache."""
+    rotate that the inputs do not stay in the 256 MB Infinity Cache.
+    ``args.variant`` (a list of workload names, or None for all) limits the
+    leg to those workloads, so that a counter run sees one workload only."""
     out = []
+    pick = getattr(args, "variant", None)
+
+    def want(*names):
+        return pick is None or any(n in pick for n in names)
     L = mlstm.lib()
     stream = torch.cuda.current_stream(dev).cuda_stream
 
@@ -313,191 +337,206 @@ def bench_variants(torch, mlstm, workload, args, dev, only_backward=False):
             kev.close()
         return r
 
-    # backward pass of the 7B prefill workload (state passes recomputed,
-    # gradients of all inputs and of the initial state); the library's events
-    # bracket its six backward kernels
     from linear_recurrent_sequence_mlstm_amd.workloads import grad_output
-    x = workload("xlstm7b_prefill_T8192")
-    B, H, T, dqk = x.q.shape
-    dv = x.v.shape[-1]
-    sets = [x.to(dev), x.to(dev)]
-    dhs = [grad_output((B, H, T, dv), seed=7000 + i).to(dev) for i in range(len(sets))]
-    ws = torch.empty(mlstm.lib().mlstm_chunkwise_bwd_workspace_bytes(B, H, T, dqk, dv, 1, 64, mlstm.BF16),
-                     dtype=torch.uint8, device=dev)
+    nb_steps = max(1, args.variant_steps // 4)  # timed calls of each backward workload
+    if want("xlstm7b_prefill_T8192_backward"):
+        # backward pass of the 7B prefill workload (state passes recomputed,
+        # gradients of all inputs and of the initial state); the library's events
+        # bracket its six backward kernels
+        x = workload("xlstm7b_prefill_T8192")
+        B, H, T, dqk = x.q.shape
+        dv = x.v.shape[-1]
+        sets = [x.to(dev), x.to(dev)]
+        dhs = [grad_output((B, H, T, dv), seed=7000 + i).to(dev) for i in range(len(sets))]
+        ws = torch.empty(mlstm.lib().mlstm_chunkwise_bwd_workspace_bytes(B, H, T, dqk, dv, 1, 64, mlstm.BF16),
+                         dtype=torch.uint8, device=dev)
 
-    def call_bwd(i):
-        g = sets[i]
-        mlstm.chunkwise_bwd(g.q, g.k, g.v, g.i_pre, g.f_pre, dhs[i], None, g.bias, workspace=ws)
+        def call_bwd(i):
+            g = sets[i]
+            mlstm.chunkwise_bwd(g.q, g.k, g.v, g.i_pre, g.f_pre, dhs[i], None, g.bias, workspace=ws)
 
-    nb_steps = max(1, args.variant_steps // 4)
-    r = timed(call_bwd, len(sets), nb_steps, nb_steps)
-    byts, flops = backward_work(B, H, T, dqk, dv)
-    out.append(dict(workload="xlstm7b_prefill_T8192_backward", B=B, H=H, T=T, d_qk=dqk, d_v=dv, **r,
-                    bytes=byts, flops=flops, tokens=B * T))
-    del sets, dhs, ws
+        r = timed(call_bwd, len(sets), nb_steps, nb_steps)
+        byts, flops = backward_work(B, H, T, dqk, dv)
+        out.append(dict(workload="xlstm7b_prefill_T8192_backward", B=B, H=H, T=T, d_qk=dqk, d_v=dv, **r,
+                        bytes=byts, flops=flops, tokens=B * T))
+        del sets, dhs, ws
 
-    # retention backward on the RetNet workload (B=8, H=4, d=64, T=2048)
-    q, k, v = workload("retnet_msr_T2048")
-    B, H, T, dk = q.shape
-    dv = v.shape[-1]
-    rsets = [tuple(t.to(dev) for t in (q, k, v)) for _ in range(4)]
-    douts = [grad_output((B, H, T, dv), seed=7100 + i, scale=1 / 8).to(dev) for i in range(len(rsets))]
-    ws = torch.empty(mlstm.lib().retention_chunkwise_bwd_workspace_bytes(B, H, T, dk, dv, 64, mlstm.BF16),
-                     dtype=torch.uint8, device=dev)
-    r = timed(lambda i: mlstm.retention_chunkwise_bwd(*rsets[i], douts[i], workspace=ws), len(rsets),
-              args.variant_steps, args.variant_steps)
-    byts, flops = retention_backward_work(B, H, T, dk, dv)
-    out.append(dict(workload="retnet_msr_T2048_backward", B=B, H=H, T=T, d_k=dk, d_v=dv, **r, bytes=byts,
-                    flops=flops, tokens=B * T))
-    del rsets, douts, ws
+    if want("retnet_msr_T2048_backward"):
+        # retention backward on the RetNet workload (B=8, H=4, d=64, T=2048)
+        q, k, v = workload("retnet_msr_T2048")
+        B, H, T, dk = q.shape
+        dv = v.shape[-1]
+        rsets = [tuple(t.to(dev) for t in (q, k, v)) for _ in range(4)]
+        douts = [grad_output((B, H, T, dv), seed=7100 + i, scale=1 / 8).to(dev) for i in range(len(rsets))]
+        ws = torch.empty(mlstm.lib().retention_chunkwise_bwd_workspace_bytes(B, H, T, dk, dv, 64, mlstm.BF16),
+                         dtype=torch.uint8, device=dev)
+        r = timed(lambda i: mlstm.retention_chunkwise_bwd(*rsets[i], douts[i], workspace=ws), len(rsets),
+                  args.variant_steps, args.variant_steps)
+        byts, flops = retention_backward_work(B, H, T, dk, dv)
+        out.append(dict(workload="retnet_msr_T2048_backward", B=B, H=H, T=T, d_k=dk, d_v=dv, **r, bytes=byts,
+                        flops=flops, tokens=B * T))
+        del rsets, douts, ws
 
-    # block-diagonal backward on the xLSTM-v2 workload (B=4, H=4, d=64, nb=2, T=65536)
-    x = workload("xlstm2_blockdiag_T65536")
-    B, H, T, dqk = x.q.shape
-    dv = x.v.shape[-1]
-    nb = x.num_blocks
-    bsets = [x.to(dev), x.to(dev)]
-    dhs = [grad_output((B, H, T, dv), seed=7200 + i).to(dev) for i in range(len(bsets))]
-    ws = torch.empty(mlstm.lib().mlstm_chunkwise_bwd_workspace_bytes(B, H, T, dqk, dv, nb, 64, mlstm.BF16),
-                     dtype=torch.uint8, device=dev)
+    if want("xlstm2_blockdiag_T65536_backward"):
+        # block-diagonal backward on the xLSTM-v2 workload (B=4, H=4, d=64, nb=2, T=65536)
+        x = workload("xlstm2_blockdiag_T65536")
+        B, H, T, dqk = x.q.shape
+        dv = x.v.shape[-1]
+        nb = x.num_blocks
+        bsets = [x.to(dev), x.to(dev)]
+        dhs = [grad_output((B, H, T, dv), seed=7200 + i).to(dev) for i in range(len(bsets))]
+        ws = torch.empty(mlstm.lib().mlstm_chunkwise_bwd_workspace_bytes(B, H, T, dqk, dv, nb, 64, mlstm.BF16),
+                         dtype=torch.uint8, device=dev)
 
-    def call_bd(i):
-        g = bsets[i]
-        mlstm.chunkwise_bwd(g.q, g.k, g.v, g.i_pre, g.f_pre, dhs[i], g.o_pre, g.bias, workspace=ws,
-                            num_blocks=nb)
+        def call_bd(i):
+            g = bsets[i]
+            mlstm.chunkwise_bwd(g.q, g.k, g.v, g.i_pre, g.f_pre, dhs[i], g.o_pre, g.bias, workspace=ws,
+                                num_blocks=nb)
 
-    r = timed(call_bd, len(bsets), nb_steps, nb_steps)
-    byts, flops = backward_work(B, H, T, dqk, dv)
-    # block-diagonal: the six state-sized products are nb times smaller
-    byts -= B * H * (dqk * dv - dqk * dv // nb) * 4
-    flops -= B * H * T * 12 * (dqk * dv - dqk * dv // nb)
-    out.append(dict(workload="xlstm2_blockdiag_T65536_backward", B=B, H=H, T=T, d_qk=dqk, d_v=dv, num_blocks=nb,
-                    **r, bytes=byts, flops=flops, tokens=B * T))
-    del bsets, dhs, ws
+        r = timed(call_bd, len(bsets), nb_steps, nb_steps)
+        byts, flops = backward_work(B, H, T, dqk, dv)
+        # block-diagonal: the six state-sized products are nb times smaller
+        byts -= B * H * (dqk * dv - dqk * dv // nb) * 4
+        flops -= B * H * T * 12 * (dqk * dv - dqk * dv // nb)
+        out.append(dict(workload="xlstm2_blockdiag_T65536_backward", B=B, H=H, T=T, d_qk=dqk, d_v=dv, num_blocks=nb,
+                        **r, bytes=byts, flops=flops, tokens=B * T))
+        del bsets, dhs, ws
     if only_backward:
         return out
 
-    # RetNet multi-scale retention: B=8, H=4, d=64, T=2048 (34 MB per call)
-    q, k, v = workload("retnet_msr_T2048")
-    B, H, T, dk = q.shape
-    dv = v.shape[-1]
-    sets = [tuple(t.to(dev) for t in (q, k, v)) for _ in range(8)]
-    outs = [torch.empty(B, H, T, dv, dtype=q.dtype, device=dev) for _ in sets]
-    S = torch.empty(B, H, dk, dv, device=dev)
-    ws = torch.empty(mlstm.retention_workspace_bytes(B, H, T, dk, dv), dtype=torch.uint8, device=dev)
-    r = timed(lambda i: mlstm.retention_chunkwise_fwd(*sets[i], out=outs[i], S_out=S, workspace=ws),
-              len(sets), args.variant_steps, args.variant_steps)
-    byts, flops = retention_work(B, H, T, dk, dv)
-    out.append(dict(workload="retnet_msr_T2048", B=B, H=H, T=T, d_k=dk, d_v=dv, **r, bytes=byts, flops=flops,
-                    tokens=B * T))
-    # the same with the per-head group norm fused into the output write
-    gw = torch.ones(H * dv, device=dev)
-    gb = torch.zeros(H * dv, device=dev)
-    r = timed(lambda i: mlstm.retention_chunkwise_fwd(*sets[i], out=outs[i], S_out=S, workspace=ws,
-                                                      groupnorm=(gw, gb, 1e-5)),
-              len(sets), args.variant_steps, args.variant_steps)
-    out.append(dict(workload="retnet_msr_T2048_groupnorm", B=B, H=H, T=T, d_k=dk, d_v=dv, **r,
-                    bytes=byts + 2 * H * dv * 4, flops=flops, tokens=B * T))
-    del sets, outs, S, ws, gw, gb
+    if want("retnet_msr_T2048", "retnet_msr_T2048_groupnorm"):
+        # RetNet multi-scale retention: B=8, H=4, d=64, T=2048 (34 MB per call)
+        q, k, v = workload("retnet_msr_T2048")
+        B, H, T, dk = q.shape
+        dv = v.shape[-1]
+        sets = [tuple(t.to(dev) for t in (q, k, v)) for _ in range(8)]
+        outs = [torch.empty(B, H, T, dv, dtype=q.dtype, device=dev) for _ in sets]
+        S = torch.empty(B, H, dk, dv, device=dev)
+        ws = torch.empty(mlstm.retention_workspace_bytes(B, H, T, dk, dv), dtype=torch.uint8, device=dev)
+        byts, flops = retention_work(B, H, T, dk, dv)
+        if want("retnet_msr_T2048"):
+            r = timed(lambda i: mlstm.retention_chunkwise_fwd(*sets[i], out=outs[i], S_out=S, workspace=ws),
+                      len(sets), args.variant_steps, args.variant_steps)
+            out.append(dict(workload="retnet_msr_T2048", B=B, H=H, T=T, d_k=dk, d_v=dv, **r, bytes=byts,
+                            flops=flops, tokens=B * T))
+        # the same with the per-head group norm fused into the output write
+        gw = torch.ones(H * dv, device=dev)
+        gb = torch.zeros(H * dv, device=dev)
+        if want("retnet_msr_T2048_groupnorm"):
+            r = timed(lambda i: mlstm.retention_chunkwise_fwd(*sets[i], out=outs[i], S_out=S, workspace=ws,
+                                                              groupnorm=(gw, gb, 1e-5)),
+                      len(sets), args.variant_steps, args.variant_steps)
+            out.append(dict(workload="retnet_msr_T2048_groupnorm", B=B, H=H, T=T, d_k=dk, d_v=dv, **r,
+                            bytes=byts + 2 * H * dv * 4, flops=flops, tokens=B * T))
+        del sets, outs, S, ws, gw, gb
 
-    # retention decode on the same workload: its first D tokens, one call
-    # of retention_step each, state updated in place
-    D = min(128, T)
-    q, k, v = workload("retnet_msr_T2048")
-    toks = [tuple(t[:, :, s].contiguous().to(dev) for t in (q, k, v)) for s in range(D)]
-    S = torch.zeros(B, H, dk, dv, device=dev)
-    o = torch.empty(B, H, dv, dtype=q.dtype, device=dev)
-    r = timed(lambda i: mlstm.retention_step(*toks[i], S, out=o), D, D, D, chunkwise=False)
-    # the same D steps captured once in a HIP graph and replayed (what a
-    # serving loop that captures its decode steps sees: no host enqueue per
-    # step); GPU time per step over 5 replays
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(D):
-            mlstm.retention_step(*toks[i], S, out=o)
-    graph.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
+    if want("retnet_msr_decode_B8"):
+        # retention decode on the same workload: its first D tokens, one call
+        # of retention_step each, state updated in place
+        q, k, v = workload("retnet_msr_T2048")
+        B, H, T, dk = q.shape
+        dv = v.shape[-1]
+        D = min(128, T)
+        toks = [tuple(t[:, :, s].contiguous().to(dev) for t in (q, k, v)) for s in range(D)]
+        S = torch.zeros(B, H, dk, dv, device=dev)
+        o = torch.empty(B, H, dv, dtype=q.dtype, device=dev)
+        r = timed(lambda i: mlstm.retention_step(*toks[i], S, out=o), D, D, D, chunkwise=False)
+        # the same D steps captured once in a HIP graph and replayed (what a
+        # serving loop that captures its decode steps sees: no host enqueue per
+        # step); GPU time per step over 5 replays
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(D):
+                mlstm.retention_step(*toks[i], S, out=o)
         graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    r["graph_ms_per_step"] = e0.elapsed_time(e1) / (5 * D)
-    del graph
-    byts = 2 * B * H * dk * dv * 4 + B * H * (2 * dk + 2 * dv) * 2
-    out.append(dict(workload="retnet_msr_decode_B8", B=B, H=H, d_k=dk, d_v=dv, steps=D, **r, bytes=byts,
-                    flops=B * H * 4 * dk * dv, tokens=B))
-    del toks, S, o
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        r["graph_ms_per_step"] = e0.elapsed_time(e1) / (5 * D)
+        del graph
+        byts = 2 * B * H * dk * dv * 4 + B * H * (2 * dk + 2 * dv) * 2
+        out.append(dict(workload="retnet_msr_decode_B8", B=B, H=H, d_k=dk, d_v=dv, steps=D, **r, bytes=byts,
+                        flops=B * H * 4 * dk * dv, tokens=B))
+        del toks, S, o
 
-    # the 7B prefill with an output gate o = sigmoid(o_pre) [B,H,T,d_v] read too
-    x = workload("xlstm7b_prefill_T8192", with_o=True)
-    B, H, T, dqk = x.q.shape
-    dv = x.v.shape[-1]
-    sets = [x.to(dev), x.to(dev)]
-    hs = [torch.empty(B, H, T, dv, dtype=x.q.dtype, device=dev) for _ in sets]
-    st = (torch.empty(B, H, 1, dqk, dv, device=dev), torch.empty(B, H, dqk, device=dev),
-          torch.empty(B, H, device=dev))
-    ws = torch.empty(mlstm.chunkwise_workspace_bytes(B, H, T, dqk, dv), dtype=torch.uint8, device=dev)
+    if want("xlstm7b_prefill_T8192_with_o", "xlstm7b_prefill_T8192_scalar_norm"):
+        # the 7B prefill with an output gate o = sigmoid(o_pre) [B,H,T,d_v] read too
+        x = workload("xlstm7b_prefill_T8192", with_o=True)
+        B, H, T, dqk = x.q.shape
+        dv = x.v.shape[-1]
+        sets = [x.to(dev), x.to(dev)]
+        hs = [torch.empty(B, H, T, dv, dtype=x.q.dtype, device=dev) for _ in sets]
+        st = (torch.empty(B, H, 1, dqk, dv, device=dev), torch.empty(B, H, dqk, device=dev),
+              torch.empty(B, H, device=dev))
+        ws = torch.empty(mlstm.chunkwise_workspace_bytes(B, H, T, dqk, dv), dtype=torch.uint8, device=dev)
 
-    def call_o(i):
-        g = sets[i]
-        mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, h=hs[i], state_out=st,
-                            workspace=ws)
+        def call_o(i):
+            g = sets[i]
+            mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, h=hs[i], state_out=st,
+                                workspace=ws)
 
-    r = timed(call_o, len(sets), args.variant_steps, args.variant_steps)
-    byts, flops = prefill_work(B, H, T, dqk, dv)
-    byts += B * H * T * dv * 2
-    out.append(dict(workload="xlstm7b_prefill_T8192_with_o", B=B, H=H, T=T, d_qk=dqk, d_v=dv, **r,
-                    bytes=byts, flops=flops, tokens=B * T))
+        if want("xlstm7b_prefill_T8192_with_o"):
+            r = timed(call_o, len(sets), args.variant_steps, args.variant_steps)
+            byts, flops = prefill_work(B, H, T, dqk, dv)
+            byts += B * H * T * dv * 2
+            out.append(dict(workload="xlstm7b_prefill_T8192_with_o", B=B, H=H, T=T, d_qk=dqk, d_v=dv, **r,
+                            bytes=byts, flops=flops, tokens=B * T))
 
-    # the same workload (no output gate) with the scalar normaliser reading
-    st_s = (st[0], torch.empty(B, H, device=dev), st[2])
+        # the same workload (no output gate) with the scalar normaliser reading
+        st_s = (st[0], torch.empty(B, H, device=dev), st[2])
 
-    def call_s(i):
-        g = sets[i]
-        mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, None, g.bias, h=hs[i], state_out=st_s, workspace=ws,
-                            norm_mode="scalar")
+        def call_s(i):
+            g = sets[i]
+            mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, None, g.bias, h=hs[i], state_out=st_s, workspace=ws,
+                                norm_mode="scalar")
 
-    r = timed(call_s, len(sets), args.variant_steps, args.variant_steps)
-    byts, flops = prefill_work(B, H, T, dqk, dv)
-    out.append(dict(workload="xlstm7b_prefill_T8192_scalar_norm", B=B, H=H, T=T, d_qk=dqk, d_v=dv, **r,
-                    bytes=byts - B * H * (dqk - 1) * 4, flops=flops, tokens=B * T))
-    del sets, hs, st, st_s, ws
+        if want("xlstm7b_prefill_T8192_scalar_norm"):
+            r = timed(call_s, len(sets), args.variant_steps, args.variant_steps)
+            byts, flops = prefill_work(B, H, T, dqk, dv)
+            out.append(dict(workload="xlstm7b_prefill_T8192_scalar_norm", B=B, H=H, T=T, d_qk=dqk, d_v=dv, **r,
+                            bytes=byts - B * H * (dqk - 1) * 4, flops=flops, tokens=B * T))
+        del sets, hs, st, st_s, ws
 
-    # xLSTM-v2 block-diagonal: B=4, H=4, d=64, nb=2, T=65536 (541 MB per call)
-    x = workload("xlstm2_blockdiag_T65536")
-    B, H, T, dqk = x.q.shape
-    dv = x.v.shape[-1]
-    sets = [x.to(dev), x.to(dev)]
-    hs = [torch.empty(B, H, T, dv, dtype=x.q.dtype, device=dev) for _ in sets]
-    nb = x.num_blocks
-    st = (torch.empty(B, H, nb, dqk // nb, dv // nb, device=dev), torch.empty(B, H, dqk, device=dev),
-          torch.empty(B, H, device=dev))
-    ws = torch.empty(mlstm.chunkwise_workspace_bytes(B, H, T, dqk, dv, nb), dtype=torch.uint8, device=dev)
+    if want("xlstm2_blockdiag_T65536", "xlstm2_blockdiag_T65536_block_norm"):
+        # xLSTM-v2 block-diagonal: B=4, H=4, d=64, nb=2, T=65536 (541 MB per call)
+        x = workload("xlstm2_blockdiag_T65536")
+        B, H, T, dqk = x.q.shape
+        dv = x.v.shape[-1]
+        sets = [x.to(dev), x.to(dev)]
+        hs = [torch.empty(B, H, T, dv, dtype=x.q.dtype, device=dev) for _ in sets]
+        nb = x.num_blocks
+        st = (torch.empty(B, H, nb, dqk // nb, dv // nb, device=dev), torch.empty(B, H, dqk, device=dev),
+              torch.empty(B, H, device=dev))
+        ws = torch.empty(mlstm.chunkwise_workspace_bytes(B, H, T, dqk, dv, nb), dtype=torch.uint8, device=dev)
 
-    def call(i):
-        g = sets[i]
-        mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, num_blocks=nb, h=hs[i],
-                            state_out=st, workspace=ws)
+        def call(i):
+            g = sets[i]
+            mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, num_blocks=nb, h=hs[i],
+                                state_out=st, workspace=ws)
 
-    r = timed(call, len(sets), args.variant_steps, args.variant_steps)
-    byts, flops = prefill_work(B, H, T, dqk, dv)
-    # block-diagonal: the state and its products are nb times smaller
-    byts -= B * H * (dqk * dv - dqk * dv // nb) * 4
-    flops -= B * H * T * 4 * (dqk * dv - dqk * dv // nb)
-    out.append(dict(workload="xlstm2_blockdiag_T65536", B=B, H=H, T=T, d_qk=dqk, d_v=dv, num_blocks=nb, **r,
-                    bytes=byts, flops=flops, tokens=B * T))
+        byts, flops = prefill_work(B, H, T, dqk, dv)
+        # block-diagonal: the state and its products are nb times smaller
+        byts -= B * H * (dqk * dv - dqk * dv // nb) * 4
+        flops -= B * H * T * 4 * (dqk * dv - dqk * dv // nb)
+        if want("xlstm2_blockdiag_T65536"):
+            r = timed(call, len(sets), args.variant_steps, args.variant_steps)
+            out.append(dict(workload="xlstm2_blockdiag_T65536", B=B, H=H, T=T, d_qk=dqk, d_v=dv, num_blocks=nb, **r,
+                            bytes=byts, flops=flops, tokens=B * T))
 
-    # the same with one denominator per memory block
-    def call_b(i):
-        g = sets[i]
-        mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, num_blocks=nb, h=hs[i],
-                            state_out=st, workspace=ws, norm_mode="block")
+        # the same with one denominator per memory block
+        def call_b(i):
+            g = sets[i]
+            mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, num_blocks=nb, h=hs[i],
+                                state_out=st, workspace=ws, norm_mode="block")
 
-    r = timed(call_b, len(sets), args.variant_steps, args.variant_steps)
-    out.append(dict(workload="xlstm2_blockdiag_T65536_block_norm", B=B, H=H, T=T, d_qk=dqk, d_v=dv,
-                    num_blocks=nb, **r, bytes=byts, flops=flops, tokens=B * T))
+        if want("xlstm2_blockdiag_T65536_block_norm"):
+            r = timed(call_b, len(sets), args.variant_steps, args.variant_steps)
+            out.append(dict(workload="xlstm2_blockdiag_T65536_block_norm", B=B, H=H, T=T, d_qk=dqk, d_v=dv,
+                            num_blocks=nb, **r, bytes=byts, flops=flops, tokens=B * T))
     return out
 
 
@@ -541,11 +580,7 @@ def variant_line(v):
     s = v["call_ms"] * 1e-3
     gbs = v["bytes"] / s / 1e9
     keep = {k: v[k] for k in v if k not in ("call_ms", "kernel_ms", "wall_ms", "bytes", "flops", "tokens")}
-    traffic = None
-    if v["workload"] == "xlstm7b_prefill_T8192_backward":
-        fwd = traffic_from_profiles(PREFILL_KERNELS[:2], source_sha("chunkwise.hip", "common.h"))
-        bwd = traffic_from_profiles(BACKWARD_KERNELS, source_sha("backward.hip", "chunkwise.hip", "common.h"))
-        traffic = None if fwd is None or bwd is None else fwd + bwd
+    traffic = workload_traffic(v["workload"])
     return dict(keep, value=v["tokens"] / s, unit="tokens/s", ms_per_call=v["call_ms"],
                 wall_ms_per_call=v["wall_ms"], main_kernel_ms=v["kernel_ms"],
                 roofline=dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
@@ -566,6 +601,8 @@ def main():
                     help="timed calls of the retention and block-diagonal workloads (0: skip them)")
     ap.add_argument("--only", choices=("prefill", "decode", "copy", "variants", "backward"),
                     help="run one leg alone and print its raw figures (for profiler runs)")
+    ap.add_argument("--variant", action="append",
+                    help="with --only variants: run only this workload (repeatable; for counter runs)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -134,6 +134,13 @@ constexpr int lds_pad_res(int row_elems, int esize, int res) {
 #ifndef MLSTM_P3_SCD
 #define MLSTM_P3_SCD 1  // k-blocks of score fragments read ahead in the 7B pass-3 helpers
 #endif
+#ifndef MLSTM_P3_PRIO
+// wave priorities in the 7B pass 3: 0 none; 1 helpers raised while they form
+// the score tiles (the longer role before barrier B: their MFMAs then issue
+// ahead of the readout's); 2 that, and the state waves raised above the
+// helpers' staging after barrier B; 3 state waves raised only
+#define MLSTM_P3_PRIO 1
+#endif
 
 template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool GN = false, bool PB = false>
 struct ChunkCfg {
@@ -1270,6 +1277,7 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
   // The two roles run separate loops with the same two barriers per chunk
   // (their registers never live at the same time).
   if (state_wave) {
+  if constexpr (MLSTM_P3_PRIO >= 2) __builtin_amdgcn_s_setprio(1);
   const int sw = w;
   const int wcol0 = slice * W + sw * WC;  // first global d_v column of this state wave
   f32x4 st[NT][CT];
@@ -1495,6 +1503,7 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
     const bool more = c + 1 < c_end;
     const bool need_update = more || (sc == p.NS - 1);
     __syncthreads();  // A
+    if constexpr (MLSTM_P3_PRIO == 1 || MLSTM_P3_PRIO == 2) __builtin_amdgcn_s_setprio(2);
     {
       const float* sA2 = sA2b[pb];
       const float* sM2 = sM2b[pb];
@@ -1578,6 +1587,7 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
       };
       if (hw < 2) scores(std::integral_constant<int, 3>{});
       else scores(std::integral_constant<int, 2>{});
+      if constexpr (MLSTM_P3_PRIO == 1 || MLSTM_P3_PRIO == 2) __builtin_amdgcn_s_setprio(0);
       __syncthreads();  // B
       if (more) {
         h_store(pb ^ 1);  // Q, K, V of the next chunk (loaded during the previous one)
