@@ -501,6 +501,29 @@ def bench_variants(torch, mlstm, workload, args, dev, only_backward=False):
                             bytes=byts - B * H * (dqk - 1) * 4, flops=flops, tokens=B * T))
         del sets, hs, st, st_s, ws
 
+    if want("xlstm7b_prefill_T64_from_state"):
+        # a short call: 64 tokens of the 7B head shape continuing from a
+        # carried state (one superchunk, so one launch), state updated in place
+        # into a second set of buffers
+        x = workload("xlstm7b_prefill_T8192")
+        T = 64
+        B, H, _, dqk = x.q.shape
+        dv = x.v.shape[-1]
+        sl = [t[:, :, :T].contiguous().to(dev) for t in (x.q, x.k, x.v, x.i_pre, x.f_pre)]
+        g = torch.Generator().manual_seed(64)
+        st0 = (torch.randn(B, H, 1, dqk, dv, generator=g).mul_(0.3).to(dev),
+               torch.randn(B, H, dqk, generator=g).mul_(0.3).to(dev), torch.zeros(B, H, device=dev))
+        st1 = tuple(torch.empty_like(t) for t in st0)
+        h = torch.empty(B, H, T, dv, dtype=x.q.dtype, device=dev)
+        ws = torch.empty(mlstm.chunkwise_workspace_bytes(B, H, T, dqk, dv), dtype=torch.uint8, device=dev)
+        r = timed(lambda i: mlstm.chunkwise_fwd(*sl, None, None, state=st0, state_out=st1, h=h, workspace=ws),
+                  1, args.variant_steps, args.variant_steps)
+        byts, flops = prefill_work(B, H, T, dqk, dv)
+        byts += B * H * (dqk * dv + dqk + 1) * 4  # the initial state read
+        out.append(dict(workload="xlstm7b_prefill_T64_from_state", B=B, H=H, T=T, d_qk=dqk, d_v=dv, **r,
+                        bytes=byts, flops=flops, tokens=B * T))
+        del sl, st0, st1, h, ws
+
     if want("xlstm2_blockdiag_T65536", "xlstm2_blockdiag_T65536_block_norm"):
         # xLSTM-v2 block-diagonal: B=4, H=4, d=64, nb=2, T=65536 (541 MB per call)
         x = workload("xlstm2_blockdiag_T65536")

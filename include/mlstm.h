@@ -114,6 +114,10 @@ size_t mlstm_chunkwise_workspace_bytes(int B, int H, int T, int d_qk, int d_v,
  * fp32 {(64,1),(64,2)}.  d_v must be a multiple of 128 when d_qk/num_blocks
  * >= 128 (bf16), else of 64, and d_v/num_blocks a multiple of 32 resp. 16.
  * Any T >= 1.  Other combinations return MLSTM_E_UNSUPPORTED.
+ * A call whose plan has one superchunk (T <= chunk always; longer T when
+ * B*H fills the GPU) is one kernel launch that reads C0/n0/m0 directly (the
+ * parallel form of a short sequence); otherwise three launches.  The results
+ * are the same bit for bit either way.
  */
 int mlstm_chunkwise_fwd(int B, int H, int T, int d_qk, int d_v, int num_blocks,
                         int chunk, mlstm_dtype dt, const void* q, const void* k,

@@ -130,6 +130,12 @@ int launch(const Plan& pl, mlstm::ChunkParams& p, void* workspace, size_t worksp
   p.ws_ga = reinterpret_cast<float*>(ws + pl.off_g);
   p.ws_gg = reinterpret_cast<float*>(ws + pl.off_g + gsz);
   p.ws_gb = reinterpret_cast<float*>(ws + pl.off_g + 2 * gsz);
+  // A plan of one superchunk runs as pass 3 alone, straight from the caller's
+  // initial state: one launch instead of three.  Not when the final n~ or m
+  // overwrites an initial-state array that the other d_v slices of the head
+  // still read (each slice reads and rewrites only its own columns of C).
+  const bool clobbers = pl.nslices > 1 && ((p.n_out && p.n_out == p.n0) || (p.m_out && p.m_out == p.m0));
+  p.direct = (pl.NS == 1 && !clobbers) ? 1 : 0;
   const hipError_t e = pl.var.launch(p, static_cast<hipStream_t>(stream), g_ev0, g_ev1);
   if (e != hipSuccess) return fail(MLSTM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

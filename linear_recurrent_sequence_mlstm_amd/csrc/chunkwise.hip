@@ -255,6 +255,34 @@ __device__ __forceinline__ float frag_rows(const float* tile, int RS, int kb0, i
   return tile[(kb0 + lg) * RS + ccol];
 }
 
+// inclusive scans over lanes in segments of SEG = 16, 32 or 64 lanes: row
+// shifts inside rows of 16, then row broadcasts.  update_dpp with bound_ctrl
+// off hands lanes without a source (and lanes of rows outside the row mask)
+// the `old` operand, here the identity (checked on MI355X).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_or(float x, float identity) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(x), CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ float seg_scan_sum(float x, int seg) {
+  x += dpp_or<0x111, 0xF>(x, 0.f);                  // row_shr:1
+  x += dpp_or<0x112, 0xF>(x, 0.f);                  // row_shr:2
+  x += dpp_or<0x114, 0xF>(x, 0.f);                  // row_shr:4
+  x += dpp_or<0x118, 0xF>(x, 0.f);                  // row_shr:8
+  if (seg >= 32) x += dpp_or<0x142, 0xA>(x, 0.f);  // row_bcast:15 into rows 1, 3
+  if (seg >= 64) x += dpp_or<0x143, 0xC>(x, 0.f);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+__device__ __forceinline__ float seg_scan_max(float x, int seg) {
+  x = fmaxf(x, dpp_or<0x111, 0xF>(x, -INFINITY));
+  x = fmaxf(x, dpp_or<0x112, 0xF>(x, -INFINITY));
+  x = fmaxf(x, dpp_or<0x114, 0xF>(x, -INFINITY));
+  x = fmaxf(x, dpp_or<0x118, 0xF>(x, -INFINITY));
+  if (seg >= 32) x = fmaxf(x, dpp_or<0x142, 0xA>(x, -INFINITY));
+  if (seg >= 64) x = fmaxf(x, dpp_or<0x143, 0xC>(x, -INFINITY));
+  return x;
+}
+
 // Pass 3: per (batch*head, superchunk, d_v slice), the chunks of the
 // superchunk in order from its start state: readout, outputs, update.
 //
@@ -344,6 +372,10 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   const auto rga_r = make_rsrc(p.ws_ga + (size_t)bh * NCL, (unsigned)NCL * 4u);
   const auto rgg_r = make_rsrc(p.ws_gg + (size_t)bh * NCL, (unsigned)NCL * 4u);
   const auto rgb_r = make_rsrc(p.ws_gb + (size_t)bh * NCL, (unsigned)NCL * 4u);
+  // ... or, in a direct call, the gate preactivations themselves
+  const bool dg = p.direct && !RET;
+  const auto ri_d = make_rsrc(dg ? static_cast<const T*>(p.i_pre) + (size_t)bh * T_ : nullptr, dg ? (unsigned)T_ * ES : 0u);
+  const auto rf_d = make_rsrc(dg ? static_cast<const T*>(p.f_pre) + (size_t)bh * T_ : nullptr, dg ? (unsigned)T_ * ES : 0u);
   constexpr bool has_o = HAS_O;  // output gate present (o_pre not null)
   const auto ro = make_rsrc(has_o ? static_cast<const T*>(p.o_pre) + (size_t)bh * T_ * DV : nullptr,
                             has_o ? (unsigned)T_ * DV * ES : 0u);
@@ -363,8 +395,15 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   f32x4 st[NT][CT];
   // the start state through a descriptor that is empty when there is none
   // (reads zero): the loads need no branch and go out back to back
-  const bool has_in = sc > 0 || p.has_init;
-  const auto rSin = make_rsrc(p.ws_state + ((size_t)bh * p.NS + sc) * NSTATE, has_in ? (unsigned)(NSTATE * 4) : 0u);
+  // (a direct call reads the caller's C0 and n0, a planned one its slot of
+  // superchunk start states, whose n~ follows the matrix)
+  const bool has_in = p.direct ? p.C0 != nullptr : (sc > 0 || p.has_init);
+  const float* sbase = p.direct ? (p.C0 ? p.C0 + (size_t)bh * CS : nullptr) : p.ws_state + ((size_t)bh * p.NS + sc) * NSTATE;
+  const auto rSin = make_rsrc(sbase, has_in ? (unsigned)((p.direct ? CS : NSTATE) * 4) : 0u);
+  constexpr int NN = SN ? 1 : DQK;  // entries of a caller's n0 per (batch, head)
+  const bool has_n = p.direct ? p.n0 != nullptr : has_in;
+  const float* nbase = p.direct ? (p.n0 ? p.n0 + (size_t)bh * NN : nullptr) : sbase + CS;
+  const auto rNin = make_rsrc(nbase, has_n ? (unsigned)((p.direct ? NN : DQK) * 4) : 0u);
   // state element (nt, ct, i) of this lane sits at soff + (uni(nt,i)*DVB + ct*16)
   const int soff = blk * DQKB * DVB + (rrow0 + perm_row_lane<T>(lg)) * DVB + wcl0 + lr;
 #pragma unroll
@@ -382,7 +421,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
     sNh[DQK + r] = from_f32<T>(x - to_f32(hi));
   };
   if constexpr (!RET) {
-    for (int r = tid; r < DQK; r += NTH) put_n(r, bload1<float>(rSin, (unsigned)(CS + r) * 4u));
+    for (int r = tid; r < DQK; r += NTH) put_n(r, bload1<float>(rNin, (unsigned)r * 4u));
   }
   // masked (l > j) tiles of P and their den partials are never written
   for (int e = tid; e < NB * L * PS; e += NTH) sP[e] = from_f32<T>(0.f);
@@ -393,7 +432,9 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   // 2^{sig}.  When sig drops below -64 the registers are rescaled once.
   float sig = 0.f;
   // stabiliser carried by wave 0 (log2 units)
-  float m_prev = p.ws_min[(size_t)bh * p.NS + sc];
+  float m_prev = p.direct ? ((!RET && p.m0) ? p.m0[bh] * kLog2e : 0.f) : p.ws_min[(size_t)bh * p.NS + sc];
+  float ret_lg2 = 0.f;  // retention: log2 gamma_h (direct calls form the gate logs here)
+  if constexpr (RET) ret_lg2 = log2f(p.ret_gamma ? p.ret_gamma[hd] : 1.f - exp2f(-5.f - (float)hd));
 
   // ------------------------------------------------------ staging registers
   // All global loads are unconditional buffer loads (units past the end of a
@@ -404,6 +445,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   Vec16<T> rgk[C::QIT];
   Vec16<T> rgv[C::VIT];
   unsigned rga = 0, rgg = 0, rgb = 0;  // chunk-local gate logs of the next chunk (raw fp32)
+  unsigned rgt = 0;                    // ... and its first token (direct calls: i, f in rga, rgg)
 
   auto load_q = [&](int c) __attribute__((always_inline)) {
     const unsigned t0 = (unsigned)c * L;
@@ -429,7 +471,12 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
       const unsigned j = u / (W / VE), col = (u % (W / VE)) * VE;
       rgv[it] = bload16<T>(rv, ((t0 + j) * DV + slice * W + col) * ES);
     }
-    {
+    rgt = t0;
+    if (p.direct) {
+      const unsigned t = t0 + (unsigned)(lane & (L - 1));
+      rga = __float_as_uint(bload1<T>(ri_d, t * ES));
+      rgg = __float_as_uint(bload1<T>(rf_d, t * ES));
+    } else {
       const unsigned o = (t0 + (unsigned)(lane & (L - 1))) * 4u;
       rga = bload1_raw<float>(rga_r, o);
       rgg = bload1_raw<float>(rgg_r, o);
@@ -480,10 +527,26 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   // chunk-local logs b_j, a_j, g_j of the gate pass: only the chain through
   // m_prev is left here.
   auto gates = [&](int gb) __attribute__((always_inline)) {
-    const float a = __uint_as_float(rga), g = __uint_as_float(rgg), b = __uint_as_float(rgb);
+    float a = __uint_as_float(rga), g = __uint_as_float(rgg), b = __uint_as_float(rgb);
+    if (p.direct) {
+      // the gate pass's chunk-local logs, formed here: tokens past T count
+      // as f = 1, i = 0
+      const bool valid = rgt + (unsigned)(lane & (L - 1)) < (unsigned)T_;
+      float lf2, li;
+      if constexpr (RET) {
+        lf2 = valid ? ret_lg2 : 0.f;
+        li = valid ? 0.f : -INFINITY;
+      } else {
+        lf2 = valid ? log2_sigmoid(__uint_as_float(rgg)) : 0.f;
+        li = valid ? __uint_as_float(rga) * kLog2e : -INFINITY;
+      }
+      b = seg_scan_sum(lf2, L);
+      a = li - b;
+      g = seg_scan_max(a, L);
+    }
     const float Mj = fmaxf(m_prev, g);
-    const float gL = __uint_as_float(__builtin_amdgcn_readlane(rgg, L - 1));
-    const float bL = __uint_as_float(__builtin_amdgcn_readlane(rgb, L - 1));
+    const float gL = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(g), L - 1));
+    const float bL = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(b), L - 1));
     const float ML = fmaxf(m_prev, gL);
     if (lane < L) {
       const float mj = b + Mj;
@@ -1134,8 +1197,20 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
   const float bias = p.bias ? p.bias[hd] : 0.f;
   // the start state through a descriptor that is empty when there is none
   // (reads zero): the loads need no branch and go out back to back
-  const bool has_in = sc > 0 || p.has_init;
-  const auto rSin = make_rsrc(p.ws_state + ((size_t)bh * p.NS + sc) * NSTATE, has_in ? (unsigned)(NSTATE * 4) : 0u);
+  // (a direct call reads the caller's C0 and n0, a planned one its slot of
+  // superchunk start states, whose n~ follows the matrix)
+  const bool has_in = p.direct ? p.C0 != nullptr : (sc > 0 || p.has_init);
+  const float* sbase = p.direct ? (p.C0 ? p.C0 + (size_t)bh * CS : nullptr) : p.ws_state + ((size_t)bh * p.NS + sc) * NSTATE;
+  const auto rSin = make_rsrc(sbase, has_in ? (unsigned)((p.direct ? CS : NSTATE) * 4) : 0u);
+  constexpr int NN = SN ? 1 : DQK;  // entries of a caller's n0 per (batch, head)
+  const bool has_n = p.direct ? p.n0 != nullptr : has_in;
+  const float* nbase = p.direct ? (p.n0 ? p.n0 + (size_t)bh * NN : nullptr) : sbase + CS;
+  const auto rNin = make_rsrc(nbase, has_n ? (unsigned)((p.direct ? NN : DQK) * 4) : 0u);
+  // the gate preactivations, read by a direct call (helper 0)
+  const auto ri_d = make_rsrc(p.direct ? static_cast<const T*>(p.i_pre) + (size_t)bh * T_ : nullptr,
+                              p.direct ? (unsigned)T_ * ES : 0u);
+  const auto rf_d = make_rsrc(p.direct ? static_cast<const T*>(p.f_pre) + (size_t)bh * T_ : nullptr,
+                              p.direct ? (unsigned)T_ * ES : 0u);
 
   // n~ into set s: fp32 and as the hi / lo rows of the den tile
   auto put_n = [&](int s, int r, float x) __attribute__((always_inline)) {
@@ -1144,7 +1219,7 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
     sNh[s][r] = hi;
     sNh[s][DQK + r] = (T)(x - (float)hi);
   };
-  for (int r = tid; r < DQK; r += 512) put_n(0, r, bload1<float>(rSin, (unsigned)(CS + r) * 4u));
+  for (int r = tid; r < DQK; r += 512) put_n(0, r, bload1<float>(rNin, (unsigned)r * 4u));
   for (int e = tid; e < L * PS; e += 512) sP[e] = (T)0.f;  // masked tiles are never written
   for (int e = tid; e < NJT * L; e += 512) sDenPart[e] = 0.f;
 
@@ -1156,7 +1231,9 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
   const int hw = w - 4;  // helper index
   Vec16<T> gq[8], gk[8], gv[4];
   unsigned rga = 0, rgg = 0, rgb = 0;  // chunk-local gate logs of the next chunk (helper 0)
-  float m_prev = p.ws_min[(size_t)bh * p.NS + sc];  // stabiliser chain, kept by helper 0
+  // stabiliser chain, kept by helper 0
+  float m_prev = p.direct ? (p.m0 ? p.m0[bh] * kLog2e : 0.f) : p.ws_min[(size_t)bh * p.NS + sc];
+  unsigned rgt = 0;  // first token of the loaded chunk (direct calls: i, f in rga, rgg)
 
   auto h_load = [&](int c) __attribute__((always_inline)) {
     const unsigned t0 = (unsigned)c * L;
@@ -1174,10 +1251,16 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
       gv[it] = bload16<T>(rv, ((t0 + j) * DV + slice * W + col) * ES);
     }
     if (hw == 0) {
-      const unsigned o = (t0 + (unsigned)lane) * 4u;
-      rga = bload1_raw<float>(rga_r, o);
-      rgg = bload1_raw<float>(rgg_r, o);
-      rgb = bload1_raw<float>(rgb_r, o);
+      rgt = t0;
+      if (p.direct) {
+        rga = __float_as_uint(bload1<T>(ri_d, (t0 + (unsigned)lane) * ES));
+        rgg = __float_as_uint(bload1<T>(rf_d, (t0 + (unsigned)lane) * ES));
+      } else {
+        const unsigned o = (t0 + (unsigned)lane) * 4u;
+        rga = bload1_raw<float>(rga_r, o);
+        rgg = bload1_raw<float>(rgg_r, o);
+        rgb = bload1_raw<float>(rgb_r, o);
+      }
     }
   };
   auto h_store = [&](int kv) __attribute__((always_inline)) {
@@ -1253,10 +1336,20 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
   };
   // gate vectors of the loaded chunk into set gb (helper 0, one lane per token)
   auto h_gates = [&](int gb) __attribute__((always_inline)) {
-    const float a = __uint_as_float(rga), g = __uint_as_float(rgg), b = __uint_as_float(rgb);
+    float a = __uint_as_float(rga), g = __uint_as_float(rgg), b = __uint_as_float(rgb);
+    if (p.direct) {
+      // the gate pass's chunk-local logs, formed here: tokens past T count
+      // as f = 1, i = 0
+      const bool valid = rgt + (unsigned)lane < (unsigned)T_;
+      const float lf2 = valid ? log2_sigmoid(__uint_as_float(rgg)) : 0.f;
+      const float li = valid ? __uint_as_float(rga) * kLog2e : -INFINITY;
+      b = seg_scan_sum(lf2, L);
+      a = li - b;
+      g = seg_scan_max(a, L);
+    }
     const float Mj = fmaxf(m_prev, g);
-    const float gL = __uint_as_float(__builtin_amdgcn_readlane(rgg, L - 1));
-    const float bL = __uint_as_float(__builtin_amdgcn_readlane(rgb, L - 1));
+    const float gL = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(g), L - 1));
+    const float bL = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(b), L - 1));
     const float ML = fmaxf(m_prev, gL);
     const float mj = b + Mj;
     const float cl = exp2_fast(-mj);
@@ -1678,34 +1771,6 @@ __device__ __forceinline__ void lds_barrier() {
 // work-group computes w_t of its own superchunk (a few KB of gate inputs,
 // read by each tile) while its first k-steps are in flight.  With one
 // superchunk a stand-alone kernel writes the chunk-local arrays.
-
-// inclusive scans over lanes in segments of SEG = 16, 32 or 64 lanes: row
-// shifts inside rows of 16, then row broadcasts.  update_dpp with bound_ctrl
-// off hands lanes without a source (and lanes of rows outside the row mask)
-// the `old` operand, here the identity (checked on MI355X).
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_or(float x, float identity) {
-  return __int_as_float(
-      __builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(x), CTRL, ROWS, 0xF, false));
-}
-__device__ __forceinline__ float seg_scan_sum(float x, int seg) {
-  x += dpp_or<0x111, 0xF>(x, 0.f);                  // row_shr:1
-  x += dpp_or<0x112, 0xF>(x, 0.f);                  // row_shr:2
-  x += dpp_or<0x114, 0xF>(x, 0.f);                  // row_shr:4
-  x += dpp_or<0x118, 0xF>(x, 0.f);                  // row_shr:8
-  if (seg >= 32) x += dpp_or<0x142, 0xA>(x, 0.f);  // row_bcast:15 into rows 1, 3
-  if (seg >= 64) x += dpp_or<0x143, 0xC>(x, 0.f);  // row_bcast:31 into rows 2, 3
-  return x;
-}
-__device__ __forceinline__ float seg_scan_max(float x, int seg) {
-  x = fmaxf(x, dpp_or<0x111, 0xF>(x, -INFINITY));
-  x = fmaxf(x, dpp_or<0x112, 0xF>(x, -INFINITY));
-  x = fmaxf(x, dpp_or<0x114, 0xF>(x, -INFINITY));
-  x = fmaxf(x, dpp_or<0x118, 0xF>(x, -INFINITY));
-  if (seg >= 32) x = fmaxf(x, dpp_or<0x142, 0xA>(x, -INFINITY));
-  if (seg >= 64) x = fmaxf(x, dpp_or<0x143, 0xC>(x, -INFINITY));
-  return x;
-}
 
 // Gate inputs of one superchunk for wave w of NWG: 64-token groups w, w + NWG, ...
 template <int NWG>
@@ -2271,7 +2336,10 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
   constexpr int NTH = 64 * NCG * NRG;
   const int BH = p.B * p.H;
   const size_t CS = (size_t)DQK * p.DV / NB;
-  if (p.NS == 1)
+  if (p.direct) {
+    // one superchunk, run as pass 3 alone (it reads C0 / n0 / m0 and forms
+    // the gate logs itself)
+  } else if (p.NS == 1)
     hipLaunchKernelGGL((superchunk_gate_kernel<T, RET>), dim3((unsigned)BH), dim3(256), 0, stream, p, L);
   else {
     // pass 1 tiles: TR rows x TC columns of one memory block.  bf16 tiles
@@ -2312,7 +2380,7 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
   s.scalar_n = SN ? 1 : 0;
   const size_t nstate = CS + (RET ? 0 : DQK);
   dim3 g2((unsigned)((nstate / 4 + 255) / 256), (unsigned)BH);
-  hipLaunchKernelGGL((superchunk_scan_kernel<RET>), g2, dim3(256), 0, stream, s);
+  if (!p.direct) hipLaunchKernelGGL((superchunk_scan_kernel<RET>), g2, dim3(256), 0, stream, s);
   if (!p.h) return hipGetLastError();  // state passes only (the backward's recompute)
   dim3 g3((unsigned)(BH * p.nslices * p.NS));
   if (ev0) (void)hipEventRecord(ev0, stream);

@@ -24,6 +24,10 @@ struct ChunkParams {
   float* ws_gg;            //   forget-gate sums b_j (gate pass -> pass 3)
   float* ws_gb;
   int has_init;
+  // one-superchunk plan run as pass 3 alone: it takes its start state from
+  // C0 / n0 / m0 (null: zero) and forms the chunk-local gate logs from i_pre,
+  // f_pre itself, so the gate pass and pass 2 are not launched
+  int direct;
   const float* C0;
   const float* n0;
   const float* m0;
@@ -50,6 +54,10 @@ struct ScanParams {
   float* ws_scal;
   float* ws_min;
   int has_init;
+  // one-superchunk plan run as pass 3 alone: it takes its start state from
+  // C0 / n0 / m0 (null: zero) and forms the chunk-local gate logs from i_pre,
+  // f_pre itself, so the gate pass and pass 2 are not launched
+  int direct;
   const float* C0;
   const float* n0;
   const float* m0;

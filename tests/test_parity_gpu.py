@@ -136,6 +136,47 @@ def test_chunkwise_initial_state_and_split_run(gpu, dqk, dv, nb):
     check_state(st_alias, ref[1:], TOL[torch.bfloat16])
 
 
+@pytest.mark.parametrize("T", [1, 37, 64])
+@pytest.mark.parametrize("dqk,dv,nb,dtype,with_o,norm_mode", [
+    (256, 512, 1, "bf16", False, "vector"), (256, 512, 1, "bf16", True, "vector"),
+    (256, 512, 1, "bf16", False, "scalar"), (64, 256, 1, "bf16", True, "vector"),
+    (128, 256, 1, "bf16", False, "vector"), (64, 64, 2, "bf16", True, "vector"), (64, 128, 1, "f32", True, "vector")])
+def test_short_call_single_launch(gpu, T, dqk, dv, nb, dtype, with_o, norm_mode):
+    """A call of one chunk (one superchunk) runs as pass 3 alone, from the
+    caller's initial state, forming the gate logs itself.  Against the oracle,
+    and bit for bit against the three-launch plan, which an in-place call on
+    a head wider than one work-group's d_v slice takes (its final n~ and m
+    overwrite arrays the other slices still read)."""
+    B, H = 2, 3
+    x = mlstm_inputs(B, H, T, dqk, dv, seed=60 + T, dtype=dtype, nb=nb, k_scale=dqk ** -0.5, f_mix=True,
+                     with_o=with_o, bias="uniform")
+    rng = np.random.default_rng(61 + T)
+    scalar = norm_mode == "scalar"
+    C0 = rng.standard_normal((B, H, nb, dqk // nb, dv // nb)) * 0.3
+    n0 = rng.standard_normal((B, H) if scalar else (B, H, dqk)) * 0.3
+    m0 = rng.uniform(-2, 2, (B, H))
+    ref = oracle.mlstm_fwd(x.q, x.k, x.v, x.i_pre, x.f_pre, x.o_pre, x.bias, C0, n0, m0, num_blocks=nb,
+                           norm_mode=norm_mode)
+    g = x.to(gpu)
+    st0 = tuple(torch.tensor(a, dtype=torch.float32, device=gpu) for a in (C0, n0, m0))
+    h1, st1 = mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, state=st0, num_blocks=nb,
+                                  norm_mode=norm_mode)
+    st_alias = tuple(t.clone() for t in st0)
+    h2, _ = mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, state=st_alias,
+                                state_out=st_alias, num_blocks=nb, norm_mode=norm_mode)
+    torch.cuda.synchronize()
+    tol = TOL[g.q.dtype]
+    assert slice_err(cpu(h1), ref[0]) < tol
+    C, n, m = (cpu(t) for t in st1)
+    assert np.max(np.abs(m - ref[3])) < 1e-4
+    sc = np.exp(m - ref[3])
+    assert slice_err(C * sc[:, :, None, None, None], ref[1]) < tol
+    assert slice_err(n * (sc if scalar else sc[:, :, None]), ref[2]) < tol
+    assert torch.equal(h1, h2)
+    for a, b in zip(st1, st_alias):
+        assert torch.equal(a, b)
+
+
 def test_chunkwise_deterministic_and_writes_every_output(gpu):
     x = mlstm_inputs(1, 4, 1234, 256, 512, seed=5, dtype="bf16", k_scale=1 / 16).to(gpu)
     outs = []
