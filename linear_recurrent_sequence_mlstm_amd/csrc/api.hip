@@ -145,7 +145,7 @@ int launch(const Plan& pl, mlstm::ChunkParams& p, void* workspace, size_t worksp
 // the backward's own arrays.
 struct BwdPlan {
   Plan fwd;
-  size_t off_carry, off_segdec, nseg, off_cst, off_cmin, off_U, off_Pt, off_Dt, off_rden, off_dz, off_db, off_dbh, off_qdq, off_kdki,
+  size_t off_carry, off_segdec, off_rdec, nseg, off_cst, off_cmin, off_U, off_Pt, off_Dt, off_rden, off_dz, off_db, off_dbh, off_qdq, off_kdki,
       off_kdk, off_cT, bytes;
 };
 
@@ -191,6 +191,8 @@ int plan_bwd(int B, int H, int T, int dqk, int dv, int nb, int chunk, int dt, Bw
   o += align256(BH * bp->nseg * ((size_t)dqk * dv + dqk) * 4);
   bp->off_segdec = o;
   o += align256(BH * bp->nseg * 4);
+  bp->off_rdec = o;  // per chunk, with the two-level scan only
+  o += align256(BH * (bp->nseg ? NC : 0) * 4);
   // partials of <dC_T, S~_T> + <dn_T, n~_T>, one per 64 x 64 state tile
   bp->off_cT = o;
   o += align256(BH * (size_t)(dqk / 64 > 0 ? dqk / 64 : 1) * (dv / 64 > 0 ? dv / 64 : 1) * 4);
@@ -379,6 +381,7 @@ int mlstm_chunkwise_bwd(int B, int H, int T, int d_qk, int d_v, int num_blocks, 
   b.NSEG = (int)bp.nseg;
   b.ws_carry = bp.nseg ? reinterpret_cast<float*>(ws + bp.off_carry) : nullptr;
   b.ws_segdec = bp.nseg ? reinterpret_cast<float*>(ws + bp.off_segdec) : nullptr;
+  b.ws_rdec = bp.nseg ? reinterpret_cast<float*>(ws + bp.off_rdec) : nullptr;
   b.dq = dq;
   b.dk = dk;
   b.dv = dv;
@@ -482,6 +485,7 @@ int retention_chunkwise_bwd(int B, int H, int T, int d_k, int d_v, int chunk, ml
   b.NSEG = (int)bp.nseg;
   b.ws_carry = bp.nseg ? reinterpret_cast<float*>(ws + bp.off_carry) : nullptr;
   b.ws_segdec = bp.nseg ? reinterpret_cast<float*>(ws + bp.off_segdec) : nullptr;
+  b.ws_rdec = bp.nseg ? reinterpret_cast<float*>(ws + bp.off_rdec) : nullptr;
   b.dq = dq;
   b.dk = dk;
   b.dv = dv;

@@ -1070,9 +1070,11 @@ __global__ __launch_bounds__(256) void bwd_scan_local_kernel(BwdParams p, int DQ
   const int cb = sg * SEG, ce = min(p.NC, cb + SEG);
   float4 G = make_float4(0.f, 0.f, 0.f, 0.f);
   float fs = 1.f;  // decay over the whole segment
+  const bool rec = blockIdx.x == 0 && threadIdx.x == 0;  // records r_c for the dk/dv pass
   for (int c = ce - 1; c >= cb; --c) {
     const float4 u = *reinterpret_cast<const float4*>(base + (size_t)c * NST + e0);
     *reinterpret_cast<float4*>(base + (size_t)c * NST + e0) = G;
+    if (rec) p.ws_rdec[(size_t)bh * p.NC + c] = fs;  // decay from the end of chunk c to the segment's end
     const float f = chunk_decay(p, bh, c);
     fs *= f;
     G.x = f * G.x + u.x;
@@ -1142,7 +1144,11 @@ __global__ __launch_bounds__(256) void bwd_scan_apply_kernel(BwdParams p, int DQ
 }
 
 // ---------------------------------------------------------------- kernel 4
-template <typename T, int DQK, int NB>
+// FC: after a two-level scan without its apply pass, the slots hold the
+// segment-local states G'_c; G_c = G'_c + r_c C_s (C_s: the state entering the
+// end of segment s, r_c: the decay from the end of chunk c to there) is
+// formed as the slices load.
+template <typename T, int DQK, int NB, bool FC = false>
 __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
   static_assert(NB == 1 || DQK == 64, "two blocks on 64-wide heads only");
   __shared__ __attribute__((aligned(16))) T sA2[NB > 1 ? BL * BT<T>::LD : 8];  // D'^T or P^T of block 1
@@ -1176,6 +1182,16 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
   // same loads in flight everywhere
   const auto rG = make_rsrc(Gc, (unsigned)(DQK * p.DV) * 4u);
   const auto rnone = make_rsrc(nullptr, 0u);
+  const float* Cs = FC ? p.ws_carry + ((size_t)bh * p.NSEG + c / SEG) * NST : nullptr;
+  const auto rC = make_rsrc(Cs, FC ? (unsigned)(DQK * p.DV) * 4u : 0u);
+  const float rc = FC ? p.ws_rdec[(size_t)bh * p.NC + c] : 0.f;
+  float cv[FC ? 16 : 1];  // the carry's slice beside each G slice
+  auto add_carry = [&](float (&g)[16]) __attribute__((always_inline)) {
+    if constexpr (FC) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) g[e] += rc * cv[e];
+    }
+  };
   // this chunk's D'^T and P^T tiles of each memory block
   const size_t tile0 = ((size_t)bh * p.NC + c) * NB * BL * BL;
   f32x4 acc[4], accx[4];
@@ -1184,7 +1200,8 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
   if (tile < NDT) {
     // dk_j = sum_l D'_lj q_l + w_j (G_c v_j + g_c), features [64 dt, 64 dt + 64)
     const int dt = tile;
-    if (tid < 64) sg[tid] = Gc[(size_t)DQK * p.DV + dt * 64 + tid];
+    if (tid < 64)
+      sg[tid] = Gc[(size_t)DQK * p.DV + dt * 64 + tid] + (FC ? rc * Cs[(size_t)DQK * p.DV + dt * 64 + tid] : 0.f);
     const int NCS = p.DV / 64;
     float vv[16], sv[16];  // V and G slices, one ahead (the first in flight with Q, K, D'^T)
     {
@@ -1196,6 +1213,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
       if constexpr (NB > 1) load16f<T>(rD, (unsigned)(BL * BL + r * BL + c0) * ES, d2);
       load16f<T>(rv, ((unsigned)(t0 + r) * p.DV + c0) * ES, vv);
       load16f<float>(rG, (unsigned)((dt * 64 + r) * p.DV + c0) * 4u, sv);
+      if constexpr (FC) load16f<float>(rC, (unsigned)((dt * 64 + r) * p.DV + c0) * 4u, cv);
       st_row16<T>(sA, r, c0, d);
       if constexpr (NB > 1) st_row16<T>(sA2, r, c0, d2);
       st_row16<T>(sB, r, c0, x);  // Q [l][d]
@@ -1214,6 +1232,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
     for (int cs = 0; cs < NCS; ++cs) {
       __syncthreads();
       st_row16<T>(sA, r, c0, vv);
+      add_carry(sv);
       st_row16<T>(sB, r, c0, sv);
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -1224,6 +1243,8 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
         const bool more = cs + 1 < NCS;
         load16f<T>(more ? rv : rnone, ((unsigned)(t0 + r) * p.DV + (cs + 1) * 64 + c0) * ES, vv);
         load16f<float>(more ? rG : rnone, (unsigned)((dt * 64 + r) * p.DV + (cs + 1) * 64 + c0) * 4u, sv);
+        if constexpr (FC)
+          load16f<float>(more ? rC : rnone, (unsigned)((dt * 64 + r) * p.DV + (cs + 1) * 64 + c0) * 4u, cv);
       }
       __syncthreads();
       mma64x<T, false, false>(accx, sA, LD, sB, LD, w, lane);  // sum_c v_jc G_dc
@@ -1269,6 +1290,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
       if constexpr (NB > 1) load16f<T>(rP, (unsigned)(BL * BL + r * BL + c0) * ES, d2);
       load16f<T>(rk, ((unsigned)(t0 + r) * DQK + c0) * ES, y);
       load16f<float>(rG, (unsigned)(r * p.DV + ct * 64 + c0) * 4u, sv);
+      if constexpr (FC) load16f<float>(rC, (unsigned)(r * p.DV + ct * 64 + c0) * 4u, cv);
       if (p.o_pre) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) g[e] = dn_of(g[e], sigmoidf_(x[e]), rden);
@@ -1293,11 +1315,14 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
     for (int ds = 0; ds < NDT; ++ds) {
       __syncthreads();
       st_row16<T>(sA, r, c0, y);
+      add_carry(sv);
       st_row16<T>(sB, r, c0, sv);  // G [d][c]
       {
         const bool more = ds + 1 < NDT;
         load16f<T>(more ? rk : rnone, ((unsigned)(t0 + r) * DQK + (ds + 1) * 64 + c0) * ES, y);
         load16f<float>(more ? rG : rnone, (unsigned)(((ds + 1) * 64 + r) * p.DV + ct * 64 + c0) * 4u, sv);
+        if constexpr (FC)
+          load16f<float>(more ? rC : rnone, (unsigned)(((ds + 1) * 64 + r) * p.DV + ct * 64 + c0) * 4u, cv);
       }
       __syncthreads();
       mma64x<T, false, true>(accx, sA, LD, sB, LD, w, lane);  // sum_d k_jd G_dc
@@ -1719,11 +1744,16 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   // long sequences of small states leave few work-groups for a long chain:
   // keep more chunks' loads in flight per step of it
   const unsigned ge = (unsigned)((NST / 4 + 255) / 256);
-  if (p.ws_carry && p.NSEG > 1) {  // two-level scan (long sequences)
+  // the 7B head shape has its own dk/dv kernel, which reads finished states
+  constexpr bool CHUNK_DKV = sizeof(T) == 2 && NB == 1 && DQK == 256;
+  const bool two_level = p.ws_carry && p.NSEG > 1;
+  if (two_level) {  // two-level scan (long sequences)
     const dim3 g3(ge, BH, (unsigned)p.NSEG);
     hipLaunchKernelGGL(bwd_scan_local_kernel, g3, dim3(256), 0, stream, p, DQK);
     hipLaunchKernelGGL(bwd_scan_carry_kernel, dim3(ge, BH), dim3(256), 0, stream, p, DQK);
-    hipLaunchKernelGGL(bwd_scan_apply_kernel, g3, dim3(256), 0, stream, p, DQK);
+    // the generic dk/dv kernel adds the decayed carries as it loads the
+    // states (no apply pass over them)
+    if (CHUNK_DKV) hipLaunchKernelGGL(bwd_scan_apply_kernel, g3, dim3(256), 0, stream, p, DQK);
   } else {
     hipLaunchKernelGGL(bwd_scan_kernel<8>, dim3(ge, BH), dim3(256), 0, stream, p, DQK);
   }
@@ -1733,7 +1763,11 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_dkv_chunk_kernel<DQK / 64>), dim3(nch), dim3(512), 0, stream, p);
     kdk_slots = 1;
   } else {
-    hipLaunchKernelGGL((bwd_dkv_kernel<T, DQK, NB>), dim3(nch * (DQK / 64 + p.DV / 64)), dim3(256), 0, stream, p);
+    const dim3 gk(nch * (DQK / 64 + p.DV / 64));
+    if (two_level)
+      hipLaunchKernelGGL((bwd_dkv_kernel<T, DQK, NB, true>), gk, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((bwd_dkv_kernel<T, DQK, NB, false>), gk, dim3(256), 0, stream, p);
   }
   if (!p.ret) {  // retention has no gates or normaliser to differentiate
     hipLaunchKernelGGL(bwd_gate_total_kernel, dim3(nch), dim3(64), 0, stream, p, kdk_slots);

@@ -137,6 +137,7 @@ struct BwdParams {
   float* ws_carry;    // [B*H][NSEG][d_qk d_v + d_qk] segment totals / carries (two-level scan), or null
   float* ws_segdec;   // [B*H][NSEG] decay over each segment (two-level scan)
   int NSEG;           // segments of 32 chunks of the two-level scan
+  float* ws_rdec;     // [B*H][NC] decay from the end of chunk c to the end of its segment (two-level scan)
   float* ws_qdq;      // [B*H][NC*64] q . dq
   float* ws_kdki;     // [B*H][NC*64] in-chunk part of k . dk
   float* ws_kdk;      // [B*H][NC*64][d_qk/64 or 1] partials of the rest of k . dk
