@@ -298,7 +298,7 @@ __device__ __forceinline__ float seg_scan_max(float x, int seg) {
 // PB: one denominator per memory block, |n~_b . q_b + ...| over the block's
 // features (NB > 1).
 template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET, bool HAS_O, bool GN = false,
-          bool SN = false, bool PB = false>
+          bool SN = false, bool PB = false, bool DIR = false>
 __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   using C = ChunkCfg<T, DQK, NB, WC, NRG, NCG, L, GN, PB>;
   using M = Mma<T>;
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   const auto rgg_r = make_rsrc(p.ws_gg + (size_t)bh * NCL, (unsigned)NCL * 4u);
   const auto rgb_r = make_rsrc(p.ws_gb + (size_t)bh * NCL, (unsigned)NCL * 4u);
   // ... or, in a direct call, the gate preactivations themselves
-  const bool dg = p.direct && !RET;
+  constexpr bool dg = DIR && !RET;
   const auto ri_d = make_rsrc(dg ? static_cast<const T*>(p.i_pre) + (size_t)bh * T_ : nullptr, dg ? (unsigned)T_ * ES : 0u);
   const auto rf_d = make_rsrc(dg ? static_cast<const T*>(p.f_pre) + (size_t)bh * T_ : nullptr, dg ? (unsigned)T_ * ES : 0u);
   constexpr bool has_o = HAS_O;  // output gate present (o_pre not null)
@@ -397,13 +397,13 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   // (reads zero): the loads need no branch and go out back to back
   // (a direct call reads the caller's C0 and n0, a planned one its slot of
   // superchunk start states, whose n~ follows the matrix)
-  const bool has_in = p.direct ? p.C0 != nullptr : (sc > 0 || p.has_init);
-  const float* sbase = p.direct ? (p.C0 ? p.C0 + (size_t)bh * CS : nullptr) : p.ws_state + ((size_t)bh * p.NS + sc) * NSTATE;
-  const auto rSin = make_rsrc(sbase, has_in ? (unsigned)((p.direct ? CS : NSTATE) * 4) : 0u);
+  const bool has_in = DIR ? p.C0 != nullptr : (sc > 0 || p.has_init);
+  const float* sbase = DIR ? (p.C0 ? p.C0 + (size_t)bh * CS : nullptr) : p.ws_state + ((size_t)bh * p.NS + sc) * NSTATE;
+  const auto rSin = make_rsrc(sbase, has_in ? (unsigned)((DIR ? CS : NSTATE) * 4) : 0u);
   constexpr int NN = SN ? 1 : DQK;  // entries of a caller's n0 per (batch, head)
-  const bool has_n = p.direct ? p.n0 != nullptr : has_in;
-  const float* nbase = p.direct ? (p.n0 ? p.n0 + (size_t)bh * NN : nullptr) : sbase + CS;
-  const auto rNin = make_rsrc(nbase, has_n ? (unsigned)((p.direct ? NN : DQK) * 4) : 0u);
+  const bool has_n = DIR ? p.n0 != nullptr : has_in;
+  const float* nbase = DIR ? (p.n0 ? p.n0 + (size_t)bh * NN : nullptr) : sbase + CS;
+  const auto rNin = make_rsrc(nbase, has_n ? (unsigned)((DIR ? NN : DQK) * 4) : 0u);
   // state element (nt, ct, i) of this lane sits at soff + (uni(nt,i)*DVB + ct*16)
   const int soff = blk * DQKB * DVB + (rrow0 + perm_row_lane<T>(lg)) * DVB + wcl0 + lr;
 #pragma unroll
@@ -421,7 +421,11 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
     sNh[DQK + r] = from_f32<T>(x - to_f32(hi));
   };
   if constexpr (!RET) {
-    for (int r = tid; r < DQK; r += NTH) put_n(r, bload1<float>(rNin, (unsigned)r * 4u));
+    if constexpr (DIR) {
+      for (int r = tid; r < DQK; r += NTH) put_n(r, bload1<float>(rNin, (unsigned)r * 4u));
+    } else {
+      for (int r = tid; r < DQK; r += NTH) put_n(r, bload1<float>(rSin, (unsigned)(CS + r) * 4u));
+    }
   }
   // masked (l > j) tiles of P and their den partials are never written
   for (int e = tid; e < NB * L * PS; e += NTH) sP[e] = from_f32<T>(0.f);
@@ -432,7 +436,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   // 2^{sig}.  When sig drops below -64 the registers are rescaled once.
   float sig = 0.f;
   // stabiliser carried by wave 0 (log2 units)
-  float m_prev = p.direct ? ((!RET && p.m0) ? p.m0[bh] * kLog2e : 0.f) : p.ws_min[(size_t)bh * p.NS + sc];
+  float m_prev = DIR ? ((!RET && p.m0) ? p.m0[bh] * kLog2e : 0.f) : p.ws_min[(size_t)bh * p.NS + sc];
   float ret_lg2 = 0.f;  // retention: log2 gamma_h (direct calls form the gate logs here)
   if constexpr (RET) ret_lg2 = log2f(p.ret_gamma ? p.ret_gamma[hd] : 1.f - exp2f(-5.f - (float)hd));
 
@@ -472,7 +476,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
       rgv[it] = bload16<T>(rv, ((t0 + j) * DV + slice * W + col) * ES);
     }
     rgt = t0;
-    if (p.direct) {
+    if constexpr (DIR) {
       const unsigned t = t0 + (unsigned)(lane & (L - 1));
       rga = __float_as_uint(bload1<T>(ri_d, t * ES));
       rgg = __float_as_uint(bload1<T>(rf_d, t * ES));
@@ -528,7 +532,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   // m_prev is left here.
   auto gates = [&](int gb) __attribute__((always_inline)) {
     float a = __uint_as_float(rga), g = __uint_as_float(rgg), b = __uint_as_float(rgb);
-    if (p.direct) {
+    if constexpr (DIR) {
       // the gate pass's chunk-local logs, formed here: tokens past T count
       // as f = 1, i = 0
       const bool valid = rgt + (unsigned)(lane & (L - 1)) < (unsigned)T_;
@@ -1140,7 +1144,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
 // The wave-uniform choices (which query tile a state wave takes n~ . q for,
 // which features it updates) are address offsets, never register selects,
 // and no LDS read is waited for inside a product loop.
-template <bool HAS_O, bool SN>
+template <bool HAS_O, bool SN, bool DIR = false>
 __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
   using T = __bf16;
   using M = Mma<T>;
@@ -1199,18 +1203,18 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
   // (reads zero): the loads need no branch and go out back to back
   // (a direct call reads the caller's C0 and n0, a planned one its slot of
   // superchunk start states, whose n~ follows the matrix)
-  const bool has_in = p.direct ? p.C0 != nullptr : (sc > 0 || p.has_init);
-  const float* sbase = p.direct ? (p.C0 ? p.C0 + (size_t)bh * CS : nullptr) : p.ws_state + ((size_t)bh * p.NS + sc) * NSTATE;
-  const auto rSin = make_rsrc(sbase, has_in ? (unsigned)((p.direct ? CS : NSTATE) * 4) : 0u);
+  const bool has_in = DIR ? p.C0 != nullptr : (sc > 0 || p.has_init);
+  const float* sbase = DIR ? (p.C0 ? p.C0 + (size_t)bh * CS : nullptr) : p.ws_state + ((size_t)bh * p.NS + sc) * NSTATE;
+  const auto rSin = make_rsrc(sbase, has_in ? (unsigned)((DIR ? CS : NSTATE) * 4) : 0u);
   constexpr int NN = SN ? 1 : DQK;  // entries of a caller's n0 per (batch, head)
-  const bool has_n = p.direct ? p.n0 != nullptr : has_in;
-  const float* nbase = p.direct ? (p.n0 ? p.n0 + (size_t)bh * NN : nullptr) : sbase + CS;
-  const auto rNin = make_rsrc(nbase, has_n ? (unsigned)((p.direct ? NN : DQK) * 4) : 0u);
+  const bool has_n = DIR ? p.n0 != nullptr : has_in;
+  const float* nbase = DIR ? (p.n0 ? p.n0 + (size_t)bh * NN : nullptr) : sbase + CS;
+  const auto rNin = make_rsrc(nbase, has_n ? (unsigned)((DIR ? NN : DQK) * 4) : 0u);
   // the gate preactivations, read by a direct call (helper 0)
-  const auto ri_d = make_rsrc(p.direct ? static_cast<const T*>(p.i_pre) + (size_t)bh * T_ : nullptr,
-                              p.direct ? (unsigned)T_ * ES : 0u);
-  const auto rf_d = make_rsrc(p.direct ? static_cast<const T*>(p.f_pre) + (size_t)bh * T_ : nullptr,
-                              p.direct ? (unsigned)T_ * ES : 0u);
+  const auto ri_d = make_rsrc(DIR ? static_cast<const T*>(p.i_pre) + (size_t)bh * T_ : nullptr,
+                              DIR ? (unsigned)T_ * ES : 0u);
+  const auto rf_d = make_rsrc(DIR ? static_cast<const T*>(p.f_pre) + (size_t)bh * T_ : nullptr,
+                              DIR ? (unsigned)T_ * ES : 0u);
 
   // n~ into set s: fp32 and as the hi / lo rows of the den tile
   auto put_n = [&](int s, int r, float x) __attribute__((always_inline)) {
@@ -1219,7 +1223,11 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
     sNh[s][r] = hi;
     sNh[s][DQK + r] = (T)(x - (float)hi);
   };
-  for (int r = tid; r < DQK; r += 512) put_n(0, r, bload1<float>(rNin, (unsigned)r * 4u));
+  if constexpr (DIR) {
+    for (int r = tid; r < DQK; r += 512) put_n(0, r, bload1<float>(rNin, (unsigned)r * 4u));
+  } else {
+    for (int r = tid; r < DQK; r += 512) put_n(0, r, bload1<float>(rSin, (unsigned)(CS + r) * 4u));
+  }
   for (int e = tid; e < L * PS; e += 512) sP[e] = (T)0.f;  // masked tiles are never written
   for (int e = tid; e < NJT * L; e += 512) sDenPart[e] = 0.f;
 
@@ -1232,7 +1240,7 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
   Vec16<T> gq[8], gk[8], gv[4];
   unsigned rga = 0, rgg = 0, rgb = 0;  // chunk-local gate logs of the next chunk (helper 0)
   // stabiliser chain, kept by helper 0
-  float m_prev = p.direct ? (p.m0 ? p.m0[bh] * kLog2e : 0.f) : p.ws_min[(size_t)bh * p.NS + sc];
+  float m_prev = DIR ? (p.m0 ? p.m0[bh] * kLog2e : 0.f) : p.ws_min[(size_t)bh * p.NS + sc];
   unsigned rgt = 0;  // first token of the loaded chunk (direct calls: i, f in rga, rgg)
 
   auto h_load = [&](int c) __attribute__((always_inline)) {
@@ -1252,7 +1260,7 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
     }
     if (hw == 0) {
       rgt = t0;
-      if (p.direct) {
+      if constexpr (DIR) {
         rga = __float_as_uint(bload1<T>(ri_d, (t0 + (unsigned)lane) * ES));
         rgg = __float_as_uint(bload1<T>(rf_d, (t0 + (unsigned)lane) * ES));
       } else {
@@ -1337,7 +1345,7 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
   // gate vectors of the loaded chunk into set gb (helper 0, one lane per token)
   auto h_gates = [&](int gb) __attribute__((always_inline)) {
     float a = __uint_as_float(rga), g = __uint_as_float(rgg), b = __uint_as_float(rgb);
-    if (p.direct) {
+    if constexpr (DIR) {
       // the gate pass's chunk-local logs, formed here: tokens past T count
       // as f = 1, i = 0
       const bool valid = rgt + (unsigned)lane < (unsigned)T_;
@@ -2388,25 +2396,34 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
   // the wave-specialised form of pass 3
   constexpr bool WS = std::is_same<T, __bf16>::value && DQK == 256 && NB == 1 && WC * NCG == 128 && L == 64 &&
                       !RET && !GN && !PB;
-  if constexpr (WS) {
-    if (p.o_pre)
-      hipLaunchKernelGGL((chunk_kernel_ws<true, SN>), g3, dim3(512), 0, stream, p);
+  // DIR: a direct call (one superchunk, no gate pass or pass 2), a separate
+  // instantiation so that the planned kernels carry no branch on it
+  auto pass3 = [&](auto dir) {
+    constexpr bool DIR = decltype(dir)::value;
+    if constexpr (WS) {
+      if (p.o_pre)
+        hipLaunchKernelGGL((chunk_kernel_ws<true, SN, DIR>), g3, dim3(512), 0, stream, p);
+      else
+        hipLaunchKernelGGL((chunk_kernel_ws<false, SN, DIR>), g3, dim3(512), 0, stream, p);
+    } else if constexpr (GN) {
+      hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, false, true, false, false, DIR>), g3,
+                         dim3(NTH), 0, stream, p);
+      if (p.gn_ws) {
+        const long long rows = (long long)BH * p.T;
+        hipLaunchKernelGGL((groupnorm_rows_kernel<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
+                           p.gn_ws, static_cast<T*>(p.h), rows, p.T, p.H, p.DV, p.gn_w, p.gn_b, p.gn_eps);
+      }
+    } else if (!RET && p.o_pre)
+      hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, !RET, false, SN, PB, DIR>), g3, dim3(NTH),
+                         0, stream, p);
     else
-      hipLaunchKernelGGL((chunk_kernel_ws<false, SN>), g3, dim3(512), 0, stream, p);
-  } else if constexpr (GN) {
-    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, false, true>), g3, dim3(NTH), 0, stream, p);
-    if (p.gn_ws) {
-      const long long rows = (long long)BH * p.T;
-      hipLaunchKernelGGL((groupnorm_rows_kernel<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
-                         p.gn_ws, static_cast<T*>(p.h), rows, p.T, p.H, p.DV, p.gn_w, p.gn_b, p.gn_eps);
-    }
-  }
-  else if (!RET && p.o_pre)
-    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, !RET, false, SN, PB>), g3, dim3(NTH), 0,
-                       stream, p);
+      hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, false, false, SN, PB, DIR>), g3,
+                         dim3(NTH), 0, stream, p);
+  };
+  if (p.direct)
+    pass3(std::true_type{});
   else
-    hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, false, false, SN, PB>), g3, dim3(NTH), 0,
-                       stream, p);
+    pass3(std::false_type{});
   const hipError_t e = hipGetLastError();
   if (ev1) (void)hipEventRecord(ev1, stream);
   return e;
