@@ -149,7 +149,9 @@ def retention_workspace_bytes(B, H, T, dk, dv, chunk=64, dtype=torch.bfloat16) -
 
 def _workspace(nbytes, device, workspace):
     """The caller's workspace (a contiguous tensor on `device`, any dtype, at
-    least nbytes long) or a fresh one; returns (tensor, its size in bytes)."""
+    least nbytes long) or, without one, a fresh one; returns (tensor, its size
+    in bytes).  A caller's workspace that is too small raises: a caller that
+    passes one does not expect the call to allocate."""
     if workspace is not None:
         if not isinstance(workspace, torch.Tensor):
             raise TypeError("workspace must be a torch.Tensor")
@@ -158,8 +160,9 @@ def _workspace(nbytes, device, workspace):
         if not workspace.is_contiguous():
             raise ValueError("workspace must be contiguous")
         size = workspace.numel() * workspace.element_size()
-        if size >= nbytes:
-            return workspace, size
+        if size < nbytes:
+            raise ValueError("workspace holds %d bytes, the call needs %d" % (size, nbytes))
+        return workspace, size
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
     return ws, ws.numel()
 

@@ -176,3 +176,24 @@ def test_noalloc_rejects_beyond_its_scratch():
     assert L.mlstm_chunkwise_fwd_noalloc(1, 2, 64, 96, 64, 1, 64, 1, 0, *p, BOGUS, None) == E_UNSUPPORTED
     assert L.mlstm_chunkwise_fwd_noalloc(1, 2, 64, 64, 64, 1, 64, 1, 0, *p, None, None) == E_NULL
     assert L.mlstm_chunkwise_fwd_noalloc(1, 2, 64, 64, 64, 1, 64, 1, 9, *p, BOGUS, None) == E_UNSUPPORTED
+
+
+def test_binding_workspace_checks():
+    """A caller's workspace is used as given or rejected, never replaced: too
+    small, on another device, or not contiguous raises (host-side, no GPU)."""
+    import torch
+    from linear_recurrent_sequence_mlstm_amd._lib import _workspace
+    cpu = torch.device("cpu")
+    ws = torch.empty(1000, dtype=torch.uint8)
+    got, n = _workspace(1000, cpu, ws)
+    assert got is ws and n == 1000
+    got, n = _workspace(3000, cpu, torch.empty(1000, dtype=torch.float32))  # any dtype, counted in bytes
+    assert n == 4000
+    with pytest.raises(ValueError):
+        _workspace(1001, cpu, ws)
+    with pytest.raises(ValueError):
+        _workspace(10, cpu, torch.empty(40, dtype=torch.uint8)[::2])
+    with pytest.raises(TypeError):
+        _workspace(10, cpu, bytearray(100))
+    fresh, n = _workspace(10, cpu, None)
+    assert n >= 256
