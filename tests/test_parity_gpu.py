@@ -177,6 +177,33 @@ def test_short_call_single_launch(gpu, T, dqk, dv, nb, dtype, with_o, norm_mode)
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("chunk,T", [(16, 9), (16, 16), (32, 29), (32, 32)])
+def test_short_call_single_launch_small_chunks(gpu, chunk, T):
+    """Direct calls with fp32 chunks of 16 and 32 tokens (the gate wave's
+    lanes repeat the chunk's tokens; the scans run per segment): against the
+    oracle and bit for bit against the three-launch plan (in place, two d_v
+    slices)."""
+    B, H, dqk, dv = 2, 3, 64, 128
+    x = mlstm_inputs(B, H, T, dqk, dv, seed=80 + T, dtype="f32", k_scale=1 / 8, f_mix=True, with_o=True,
+                     bias="uniform")
+    rng = np.random.default_rng(81 + T)
+    C0, n0, m0 = rng.standard_normal((B, H, 1, dqk, dv)) * 0.3, rng.standard_normal((B, H, dqk)) * 0.3, \
+        rng.uniform(-2, 2, (B, H))
+    ref = oracle.mlstm_fwd(x.q, x.k, x.v, x.i_pre, x.f_pre, x.o_pre, x.bias, C0, n0, m0)
+    g = x.to(gpu)
+    st0 = tuple(torch.tensor(a, dtype=torch.float32, device=gpu) for a in (C0, n0, m0))
+    h1, st1 = mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, state=st0, chunk=chunk)
+    st_alias = tuple(t.clone() for t in st0)
+    h2, _ = mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, state=st_alias,
+                                state_out=st_alias, chunk=chunk)
+    torch.cuda.synchronize()
+    assert slice_err(cpu(h1), ref[0]) < TOL[torch.float32]
+    check_state(st1, ref[1:], TOL[torch.float32])
+    assert torch.equal(h1, h2)
+    for a, b in zip(st1, st_alias):
+        assert torch.equal(a, b)
+
+
 def test_chunkwise_deterministic_and_writes_every_output(gpu):
     x = mlstm_inputs(1, 4, 1234, 256, 512, seed=5, dtype="bf16", k_scale=1 / 16).to(gpu)
     outs = []
