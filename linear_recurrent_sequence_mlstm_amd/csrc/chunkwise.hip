@@ -298,7 +298,7 @@ __device__ __forceinline__ float seg_scan_max(float x, int seg) {
 // PB: one denominator per memory block, |n~_b . q_b + ...| over the block's
 // features (NB > 1).
 template <typename T, int DQK, int NB, int WC, int NRG, int NCG, int L, bool RET, bool HAS_O, bool GN = false,
-          bool SN = false, bool PB = false, bool DIR = false>
+          bool SN = false, bool PB = false, bool DIR = false, bool FS = false>
 __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   using C = ChunkCfg<T, DQK, NB, WC, NRG, NCG, L, GN, PB>;
   using M = Mma<T>;
@@ -396,14 +396,16 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   // the start state through a descriptor that is empty when there is none
   // (reads zero): the loads need no branch and go out back to back
   // (a direct call reads the caller's C0 and n0, a planned one its slot of
-  // superchunk start states, whose n~ follows the matrix)
-  const bool has_in = DIR ? p.C0 != nullptr : (sc > 0 || p.has_init);
-  const float* sbase = DIR ? (p.C0 ? p.C0 + (size_t)bh * CS : nullptr) : p.ws_state + ((size_t)bh * p.NS + sc) * NSTATE;
-  const auto rSin = make_rsrc(sbase, has_in ? (unsigned)((DIR ? CS : NSTATE) * 4) : 0u);
+  // superchunk start states, whose n~ follows the matrix; FS starts from the
+  // caller's state too and composes it below)
+  constexpr bool CALLER = DIR || FS;
+  const bool has_in = CALLER ? p.C0 != nullptr : (sc > 0 || p.has_init);
+  const float* sbase = CALLER ? (p.C0 ? p.C0 + (size_t)bh * CS : nullptr) : p.ws_state + ((size_t)bh * p.NS + sc) * NSTATE;
+  const auto rSin = make_rsrc(sbase, has_in ? (unsigned)((CALLER ? CS : NSTATE) * 4) : 0u);
   constexpr int NN = SN ? 1 : DQK;  // entries of a caller's n0 per (batch, head)
-  const bool has_n = DIR ? p.n0 != nullptr : has_in;
-  const float* nbase = DIR ? (p.n0 ? p.n0 + (size_t)bh * NN : nullptr) : sbase + CS;
-  const auto rNin = make_rsrc(nbase, has_n ? (unsigned)((DIR ? NN : DQK) * 4) : 0u);
+  const bool has_n = CALLER ? p.n0 != nullptr : has_in;
+  const float* nbase = CALLER ? (p.n0 ? p.n0 + (size_t)bh * NN : nullptr) : sbase + CS;
+  const auto rNin = make_rsrc(nbase, has_n ? (unsigned)((CALLER ? NN : DQK) * 4) : 0u);
   // state element (nt, ct, i) of this lane sits at soff + (uni(nt,i)*DVB + ct*16)
   const int soff = blk * DQKB * DVB + (rrow0 + perm_row_lane<T>(lg)) * DVB + wcl0 + lr;
 #pragma unroll
@@ -420,8 +422,65 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
     sNh[r] = hi;
     sNh[DQK + r] = from_f32<T>(x - to_f32(hi));
   };
+  // FS: pass 2 folded in.  This superchunk's start state is the scan of the
+  // local states of superchunks 0 .. sc-1 (pass 1's slots 1 .. sc, with
+  // their log2 decay A and scale mu) from the caller's state, in pass 2's
+  // arithmetic: m' = max(A + m, mu), S = 2^{A+m-m'} S + 2^{mu-m'} dS.  All
+  // FS_J slots load first (past sc they repeat slot sc and are not used), so
+  // their latencies overlap.
+  constexpr int FS_J = FS ? 7 : 1;
+  float fs_m = (!RET && p.m0) ? p.m0[bh] * kLog2e : 0.f;
+  float fs_fa[FS_J], fs_fb[FS_J];
+  if constexpr (FS) {
+    const auto rLoc = make_rsrc(p.ws_state + (size_t)bh * p.NS * NSTATE, (unsigned)(p.NS * NSTATE * 4));
+    float dl[FS_J][NT][CT][4];
+#pragma unroll
+    for (int j = 0; j < FS_J; ++j) {
+      const unsigned slot = (unsigned)min(j + 1, sc) * (unsigned)NSTATE;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            dl[j][nt][ct][i] =
+                bload1<float>(rLoc, (slot + (unsigned)(soff + perm_row_uni<T>(nt, i) * DVB + ct * 16)) * 4u);
+    }
+#pragma unroll
+    for (int j = 0; j < FS_J; ++j) {
+      fs_fa[j] = 1.f;
+      fs_fb[j] = 0.f;
+      if (j < sc) {  // work-group-uniform
+        const float A = p.ws_scal[((size_t)bh * p.NS + j) * 2 + 0];
+        const float mu = p.ws_scal[((size_t)bh * p.NS + j) * 2 + 1];
+        const float mn = fmaxf(A + fs_m, mu);
+        fs_fa[j] = exp2_fast(A + fs_m - mn);
+        fs_fb[j] = exp2_fast(mu - mn);
+        fs_m = mn;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st[nt][ct][i] = fs_fa[j] * st[nt][ct][i] + fs_fb[j] * dl[j][nt][ct][i];
+      }
+    }
+  }
   if constexpr (!RET) {
-    if constexpr (DIR) {
+    if constexpr (FS) {
+      const auto rLoc = make_rsrc(p.ws_state + (size_t)bh * p.NS * NSTATE, (unsigned)(p.NS * NSTATE * 4));
+      for (int r = tid; r < DQK; r += NTH) {
+        float x = bload1<float>(rNin, (unsigned)r * 4u);
+        float dn[FS_J];
+#pragma unroll
+        for (int j = 0; j < FS_J; ++j)
+          dn[j] = bload1<float>(rLoc, ((unsigned)min(j + 1, sc) * (unsigned)NSTATE + (unsigned)(CS + r)) * 4u);
+#pragma unroll
+        for (int j = 0; j < FS_J; ++j)
+          if (j < sc) x = fs_fa[j] * x + fs_fb[j] * dn[j];
+        put_n(r, x);
+      }
+    } else if constexpr (DIR) {
       for (int r = tid; r < DQK; r += NTH) put_n(r, bload1<float>(rNin, (unsigned)r * 4u));
     } else {
       for (int r = tid; r < DQK; r += NTH) put_n(r, bload1<float>(rSin, (unsigned)(CS + r) * 4u));
@@ -436,7 +495,7 @@ __global__ __launch_bounds__(64 * NCG * NRG) void chunk_kernel(ChunkParams p) {
   // 2^{sig}.  When sig drops below -64 the registers are rescaled once.
   float sig = 0.f;
   // stabiliser carried by wave 0 (log2 units)
-  float m_prev = DIR ? ((!RET && p.m0) ? p.m0[bh] * kLog2e : 0.f) : p.ws_min[(size_t)bh * p.NS + sc];
+  float m_prev = FS ? fs_m : DIR ? ((!RET && p.m0) ? p.m0[bh] * kLog2e : 0.f) : p.ws_min[(size_t)bh * p.NS + sc];
   float ret_lg2 = 0.f;  // retention: log2 gamma_h (direct calls form the gate logs here)
   if constexpr (RET) ret_lg2 = log2f(p.ret_gamma ? p.ret_gamma[hd] : 1.f - exp2f(-5.f - (float)hd));
 
@@ -2374,6 +2433,10 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
     else
       hipLaunchKernelGGL((local_state_kernel<T, DQK, NBC, TR, 32, L, RET, NWP, NB, SN>), g1, b1, 0, stream, p);
   }
+  // the xLSTM-7B head shape (d_qk 256, one memory block, 128-column slices):
+  // the wave-specialised form of pass 3
+  constexpr bool WSK = std::is_same<T, __bf16>::value && DQK == 256 && NB == 1 && WC * NCG == 128 && L == 64 &&
+                       !RET && !GN && !PB;
   ScanParams s;
   s.NS = p.NS;
   s.CS = CS;
@@ -2388,25 +2451,28 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
   s.scalar_n = SN ? 1 : 0;
   const size_t nstate = CS + (RET ? 0 : DQK);
   dim3 g2((unsigned)((nstate / 4 + 255) / 256), (unsigned)BH);
-  if (!p.direct) hipLaunchKernelGGL((superchunk_scan_kernel<RET>), g2, dim3(256), 0, stream, s);
+  // fuse_scan: pass 3 composes the start states (a forward call only; the
+  // backward's recompute, h = NULL, needs pass 2's slots)
+  // (heads of 64 features only: a wider one's state exceeds the fused limit)
+  constexpr bool FSK = !WSK && DQK == 64;
+  const bool fs = FSK && p.fuse_scan && p.h;
+  if (!p.direct && !fs) hipLaunchKernelGGL((superchunk_scan_kernel<RET>), g2, dim3(256), 0, stream, s);
   if (!p.h) return hipGetLastError();  // state passes only (the backward's recompute)
   dim3 g3((unsigned)(BH * p.nslices * p.NS));
   if (ev0) (void)hipEventRecord(ev0, stream);
-  // the xLSTM-7B head shape (d_qk 256, one memory block, 128-column slices):
-  // the wave-specialised form of pass 3
-  constexpr bool WS = std::is_same<T, __bf16>::value && DQK == 256 && NB == 1 && WC * NCG == 128 && L == 64 &&
-                      !RET && !GN && !PB;
+  constexpr bool WS = WSK;
   // DIR: a direct call (one superchunk, no gate pass or pass 2), a separate
   // instantiation so that the planned kernels carry no branch on it
-  auto pass3 = [&](auto dir) {
+  auto pass3 = [&](auto dir, auto fsc) {
     constexpr bool DIR = decltype(dir)::value;
+    constexpr bool FS = decltype(fsc)::value && FSK;  // generic kernel, 64-wide heads
     if constexpr (WS) {
       if (p.o_pre)
         hipLaunchKernelGGL((chunk_kernel_ws<true, SN, DIR>), g3, dim3(512), 0, stream, p);
       else
         hipLaunchKernelGGL((chunk_kernel_ws<false, SN, DIR>), g3, dim3(512), 0, stream, p);
     } else if constexpr (GN) {
-      hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, false, true, false, false, DIR>), g3,
+      hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, false, true, false, false, DIR, FS>), g3,
                          dim3(NTH), 0, stream, p);
       if (p.gn_ws) {
         const long long rows = (long long)BH * p.T;
@@ -2414,16 +2480,18 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
                            p.gn_ws, static_cast<T*>(p.h), rows, p.T, p.H, p.DV, p.gn_w, p.gn_b, p.gn_eps);
       }
     } else if (!RET && p.o_pre)
-      hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, !RET, false, SN, PB, DIR>), g3, dim3(NTH),
-                         0, stream, p);
+      hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, !RET, false, SN, PB, DIR, FS>), g3,
+                         dim3(NTH), 0, stream, p);
     else
-      hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, false, false, SN, PB, DIR>), g3,
+      hipLaunchKernelGGL((chunk_kernel<T, DQK, NB, WC, NRG, NCG, L, RET, false, false, SN, PB, DIR, FS>), g3,
                          dim3(NTH), 0, stream, p);
   };
   if (p.direct)
-    pass3(std::true_type{});
+    pass3(std::true_type{}, std::false_type{});
+  else if (fs)
+    pass3(std::false_type{}, std::integral_constant<bool, FSK>{});
   else
-    pass3(std::false_type{});
+    pass3(std::false_type{}, std::false_type{});
   const hipError_t e = hipGetLastError();
   if (ev1) (void)hipEventRecord(ev1, stream);
   return e;

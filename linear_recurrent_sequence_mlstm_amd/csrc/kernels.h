@@ -28,6 +28,10 @@ struct ChunkParams {
   // C0 / n0 / m0 (null: zero) and forms the chunk-local gate logs from i_pre,
   // f_pre itself, so the gate pass and pass 2 are not launched
   int direct;
+  // few superchunks of a small state: pass 3 composes its start state from
+  // pass 1's local states itself (pass 2's arithmetic), so pass 2 is not
+  // launched
+  int fuse_scan;
   const float* C0;
   const float* n0;
   const float* m0;
@@ -54,10 +58,6 @@ struct ScanParams {
   float* ws_scal;
   float* ws_min;
   int has_init;
-  // one-superchunk plan run as pass 3 alone: it takes its start state from
-  // C0 / n0 / m0 (null: zero) and forms the chunk-local gate logs from i_pre,
-  // f_pre itself, so the gate pass and pass 2 are not launched
-  int direct;
   const float* C0;
   const float* n0;
   const float* m0;
