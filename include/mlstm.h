@@ -30,10 +30,15 @@
  *   - Tensor pointers are DEVICE pointers to contiguous row-major arrays.
  *   - q, k, v, gate preactivations, o_pre and outputs h use the call's dtype;
  *     states (C, n, m, S), norm_bias and gamma are always fp32.
- *   - The caller owns every buffer.  The library allocates no memory and keeps
- *     no pointer after returning.  Work is enqueued on `stream` (a
- *     hipStream_t; NULL = default stream) and the call returns without
- *     synchronising.
+ *   - The caller owns every buffer.  No call allocates memory, and no
+ *     compute call keeps a pointer after returning.  Work is enqueued on
+ *     `stream` (a hipStream_t; NULL = default stream) and the call returns
+ *     without synchronising.
+ *   - State the library holds: per calling thread, the last error message
+ *     and the two events of mlstm_set_profile_events (until it is called with
+ *     NULL, NULL); per GPU, the 64 MiB device array that only
+ *     mlstm_chunkwise_fwd_noalloc uses (module memory, part of the library's
+ *     code object on that device, held until the process ends).
  *   - Return value: 0 on success, a negative MLSTM_E_* code otherwise.  All
  *     argument checks happen before anything is enqueued, so on error no
  *     output has been touched.  mlstm_last_error() describes the last error of
