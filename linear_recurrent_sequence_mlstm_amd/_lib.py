@@ -117,11 +117,18 @@ def _check(rc: int, what: str):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: ctypes turns it into the void* argument without an object
+    return None if t is None else t.data_ptr()
 
 
 def _need(t, name, shape, dtype, device):
     if t is None:
+        return
+    # the common case in one expression (a call checks about a dozen tensors,
+    # and these checks dominated the host time of a short call); any failure
+    # falls through to the checks below, which name what is wrong
+    if isinstance(t, torch.Tensor) and t.dtype is dtype and t.shape == shape and t.is_contiguous() \
+            and t.device == device:
         return
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
@@ -135,8 +142,14 @@ def _need(t, name, shape, dtype, device):
         raise ValueError("%s must be contiguous" % name)
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    """The current stream of `device` as a raw hipStream_t (an int)."""
+    if _raw_stream is not None:
+        return _raw_stream(device.index if device.index is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def chunkwise_workspace_bytes(B, H, T, dqk, dv, num_blocks=1, chunk=64, dtype=torch.bfloat16) -> int:
