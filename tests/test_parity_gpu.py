@@ -474,3 +474,23 @@ def test_step_matches_chunkwise(gpu):
     torch.cuda.synchronize()
     full = torch.cat([h, torch.stack(hs, dim=2)], dim=2)
     assert slice_err(cpu(full), ref[0]) < TOL[torch.bfloat16]
+
+
+def test_binding_rejects_bad_tensors(gpu):
+    """The binding's one-expression check of the common case falls through
+    to the specific errors: a tensor on the host, of another dtype, not
+    contiguous or of the wrong shape is refused before anything reaches the
+    library."""
+    x = mlstm_inputs(1, 2, 16, 64, 64, seed=90, dtype="bf16", k_scale=1 / 8).to(gpu)
+    good = dict(q=x.q, k=x.k, v=x.v, i_pre=x.i_pre, f_pre=x.f_pre)
+    mlstm.chunkwise_fwd(**good)  # accepted
+    torch.cuda.synchronize()
+    bad = [
+        (dict(good, k=x.k.cpu()), ValueError),                          # host tensor
+        (dict(good, v=x.v.float()), TypeError),                         # dtype
+        (dict(good, q=x.q.transpose(2, 3).contiguous().transpose(2, 3)), ValueError),  # not contiguous
+        (dict(good, i_pre=x.i_pre[:, :, :8].contiguous()), ValueError),  # shape
+    ]
+    for kw, err in bad:
+        with pytest.raises(err):
+            mlstm.chunkwise_fwd(**kw)
