@@ -1,0 +1,128 @@
+"""GPU parity over a seeded sweep of small random configurations.
+
+Each case draws a dtype, head shape, number of memory blocks, normaliser
+reading, length, chunk length, batch and heads, and whether an initial state,
+an output gate, a bias and an in-place final state are given.  The plan then
+takes whichever path it takes for that case (one launch for one superchunk,
+pass 2 folded into pass 3 for a few superchunks of a small state, or the
+three launches), and the outputs and final state are compared with the fp64
+oracle on the same inputs.  A second sweep does the same for retention
+calls (head shape, chunk length, per-head or default decays, initial state,
+in-place final state).  Bars: 1e-4 for fp32, 2e-2 for bf16, per (batch,
+head) slice as in the other parity tests.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_recurrent_sequence_mlstm_amd import _lib as mlstm
+from linear_recurrent_sequence_mlstm_amd.workloads import mlstm_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+# (dtype, d_qk, num_blocks, admissible d_v)
+SHAPES = [("bf16", 64, 1, (64, 128, 192)), ("bf16", 64, 2, (64, 128)), ("bf16", 128, 1, (128, 256)),
+          ("bf16", 256, 1, (128, 512)), ("bf16", 256, 2, (256,)), ("f32", 64, 1, (64, 128)),
+          ("f32", 64, 2, (64,))]
+
+
+def _cases(n=28, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt, dqk, nb, dvs = SHAPES[i % len(SHAPES)]
+        dv = int(rng.choice(dvs))
+        big = dqk * dv >= 256 * 256
+        T = int(rng.integers(1, 300 if big else 1200))
+        chunk = 64 if dt == "bf16" or nb > 1 else int(rng.choice([16, 32, 64]))  # fp32 two-block kernels: 64
+        mode = str(rng.choice(["vector", "scalar", "block"] if nb > 1 else ["vector", "scalar"]))
+        out.append(dict(dt=dt, dqk=dqk, nb=nb, dv=dv, T=T, chunk=chunk, mode=mode,
+                        B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)), init=bool(rng.random() < 0.6),
+                        with_o=bool(rng.random() < 0.5), in_place=bool(rng.random() < 0.3), seed=5000 + i))
+    return out
+
+
+def _slice_err(got, ref):
+    g = np.asarray(got, dtype=np.float64).reshape(got.shape[0] * got.shape[1], -1)
+    r = np.asarray(ref, dtype=np.float64).reshape(g.shape)
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    return float((np.abs(g - r).max(axis=1) / np.maximum(np.abs(r).max(axis=1), 1e-30)).max())
+
+
+@pytest.mark.parametrize("case", _cases(), ids=lambda c: "%s_d%dx%d_nb%d_%s_T%d_L%d_B%dH%d%s%s%s" % (
+    c["dt"], c["dqk"], c["dv"], c["nb"], c["mode"], c["T"], c["chunk"], c["B"], c["H"],
+    "_state" if c["init"] else "", "_o" if c["with_o"] else "", "_inplace" if c["in_place"] else ""))
+def test_random_configuration(gpu, case):
+    c = case
+    B, H, T, dqk, dv, nb = c["B"], c["H"], c["T"], c["dqk"], c["dv"], c["nb"]
+    x = mlstm_inputs(B, H, T, dqk, dv, seed=c["seed"], dtype=c["dt"], nb=nb, k_scale=dqk ** -0.5, f_mix=True,
+                     with_o=c["with_o"], bias="uniform", chunk=c["chunk"])
+    scalar = c["mode"] == "scalar"
+    st = None
+    if c["init"]:
+        rng = np.random.default_rng(c["seed"] + 1)
+        st = (rng.standard_normal((B, H, nb, dqk // nb, dv // nb)) * 0.3,
+              rng.standard_normal((B, H) if scalar else (B, H, dqk)) * 0.3, rng.uniform(-2, 2, (B, H)))
+    ref = oracle.mlstm_fwd(x.q, x.k, x.v, x.i_pre, x.f_pre, x.o_pre, x.bias, *(st or (None, None, None)),
+                           num_blocks=nb, norm_mode=c["mode"])
+    g = x.to(gpu)
+    gst = None if st is None else tuple(torch.tensor(a, dtype=torch.float32, device=gpu) for a in st)
+    kw = dict(num_blocks=nb, chunk=c["chunk"], norm_mode=c["mode"])
+    if c["in_place"] and gst is not None:
+        h, out = mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, state=gst, state_out=gst,
+                                     **kw)
+        out = gst
+    else:
+        h, out = mlstm.chunkwise_fwd(g.q, g.k, g.v, g.i_pre, g.f_pre, g.o_pre, g.bias, state=gst, **kw)
+    torch.cuda.synchronize()
+    tol = TOL[c["dt"]]
+    assert _slice_err(h.double().cpu().numpy(), ref[0]) < tol
+    C, n, m = (t.double().cpu().numpy() for t in out)
+    assert np.max(np.abs(m - ref[3])) < 1e-4
+    sc = np.exp(m - ref[3])
+    assert _slice_err(C * sc[:, :, None, None, None], ref[1]) < tol
+    assert _slice_err((n * sc) if scalar else (n * sc[:, :, None]), ref[2]) < tol
+
+
+# retention: (dtype, d_k, admissible d_v, admissible chunks)
+RSHAPES = [("bf16", 64, (64, 128, 256), (32, 64)), ("bf16", 128, (128, 256), (64,)), ("f32", 64, (64, 128), (64,))]
+
+
+def _rcases(n=12, seed=2025):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt, dk, dvs, chunks = RSHAPES[i % len(RSHAPES)]
+        out.append(dict(dt=dt, dk=dk, dv=int(rng.choice(dvs)), chunk=int(rng.choice(chunks)),
+                        T=int(rng.integers(1, 1500)), B=int(rng.integers(1, 3)), H=int(rng.integers(1, 5)),
+                        init=bool(rng.random() < 0.6), custom_gamma=bool(rng.random() < 0.4),
+                        in_place=bool(rng.random() < 0.3), seed=6000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _rcases(), ids=lambda c: "%s_d%dx%d_T%d_L%d_B%dH%d%s%s%s" % (
+    c["dt"], c["dk"], c["dv"], c["T"], c["chunk"], c["B"], c["H"], "_state" if c["init"] else "",
+    "_gamma" if c["custom_gamma"] else "", "_inplace" if c["in_place"] else ""))
+def test_random_retention_configuration(gpu, case):
+    c = case
+    B, H, T, dk, dv = c["B"], c["H"], c["T"], c["dk"], c["dv"]
+    g = torch.Generator().manual_seed(c["seed"])
+    dt = torch.bfloat16 if c["dt"] == "bf16" else torch.float32
+    q, k, v = (torch.randn(B, H, T, d, generator=g).div_(8).to(dt) for d in (dk, dk, dv))
+    gamma = (1 - torch.rand(H, generator=g) * 0.1).float() if c["custom_gamma"] else None
+    S0 = (torch.randn(B, H, dk, dv, generator=g) * 0.3).float() if c["init"] else None
+    ref_o, ref_S = oracle.retention_fwd(q, k, v, gamma, S0)
+    d = torch.device(gpu)
+    gg = None if gamma is None else gamma.to(d)
+    gS = None if S0 is None else S0.to(d)
+    if c["in_place"] and gS is not None:
+        o, _ = mlstm.retention_chunkwise_fwd(q.to(d), k.to(d), v.to(d), gg, gS, chunk=c["chunk"], S_out=gS)
+        S = gS
+    else:
+        o, S = mlstm.retention_chunkwise_fwd(q.to(d), k.to(d), v.to(d), gg, gS, chunk=c["chunk"])
+    torch.cuda.synchronize()
+    tol = TOL[c["dt"]]
+    assert _slice_err(o.double().cpu().numpy(), ref_o) < tol
+    assert _slice_err(S.double().cpu().numpy(), ref_S) < tol
