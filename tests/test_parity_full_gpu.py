@@ -112,3 +112,43 @@ def test_xlstm7b_decode_all_sequences_first_8_steps(gpu):
     assert slice_err(cpu(got), ref[0]) < TOL[torch.bfloat16]
     st = (C.reshape(1, B * H, 1, dqk, dv), n.reshape(1, B * H, dqk), m.reshape(1, B * H))
     check_state(st, ref[1:], TOL[torch.bfloat16])
+
+
+@pytest.mark.parametrize("dt,dqk,dv", [(torch.bfloat16, 256, 512), (torch.float32, 64, 64)],
+                         ids=["bf16_256x512", "f32_64x64"])
+def test_largest_admissible_slice_sampled(gpu, dt, dqk, dv):
+    """One (batch, head) as long as the boundary admits: T x max(d_qk, d_v)
+    elements just under 2^31 bytes, and T not a multiple of the chunk.  A
+    forget preactivation of -80 at a few tokens erases the memory there (the
+    old state is scaled by sigma(-80) < 1e-34), so the oracle can follow the
+    window after each such token from a zero state.  Compared: the outputs
+    in every window, and the final state after the last one.  The windows sit
+    at the start, across superchunk boundaries, across the 2^30-byte mark of
+    the widest tensor, far into the sequence and at its ragged end."""
+    es = 2 if dt == torch.bfloat16 else 4
+    d = max(dqk, dv)
+    T = (1 << 31) // (d * es) - 64 - 23
+    W = 320
+    dev = torch.device(gpu)
+    g = torch.Generator(device=dev).manual_seed(7001 + dqk)
+    q = torch.randn(1, 1, T, dqk, generator=g, device=dev).to(dt)
+    k = (torch.randn(1, 1, T, dqk, generator=g, device=dev) * dqk ** -0.5).to(dt)
+    v = torch.randn(1, 1, T, dv, generator=g, device=dev).to(dt)
+    i_pre = torch.randn(1, 1, T, generator=g, device=dev).to(dt)
+    f_pre = (torch.randn(1, 1, T, generator=g, device=dev) + 3.0).to(dt)
+    bias = torch.tensor([0.3], device=dev)
+    starts = [0, 1024 - 100, (1 << 30) // (d * es) - 150, 1024 * 1500 - 37, T - W]
+    for r in starts[1:]:
+        f_pre[0, 0, r] = -80.0
+    print("T=%d d_qk=%d d_v=%s windows at %s" % (T, dqk, dv, starts), flush=True)
+    h, st = mlstm.chunkwise_fwd(q, k, v, i_pre, f_pre, None, bias,
+                                state_out=(torch.empty(1, 1, 1, dqk, dv, device=dev),
+                                           torch.empty(1, 1, dqk, device=dev), torch.empty(1, 1, device=dev)))
+    torch.cuda.synchronize()
+    b = cpu(bias)
+    for r in starts:
+        w = slice(r, r + W)
+        ref = oracle.mlstm_fwd(cpu(q[:, :, w]), cpu(k[:, :, w]), cpu(v[:, :, w]), cpu(i_pre[:, :, w]),
+                               cpu(f_pre[:, :, w]), None, b)
+        assert slice_err(cpu(h[:, :, w]), ref[0]) < TOL[dt], r
+    check_state(st, ref[1:], TOL[dt])
