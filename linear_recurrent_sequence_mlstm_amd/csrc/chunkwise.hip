@@ -1489,14 +1489,15 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
         if (lg == 0) sDenInter[sw * 16 + lr] = pn[0] + pn[1];
       }
       // output-gate values of this wave's outputs, issued after the readout
-      // (not live across it) so that the wait at barrier B hides their latency
-      Raw4<T> oraw[HAS_O ? NJT : 1][HAS_O ? CT : 1];
+      // (not live across it) so that the wait at barrier B hides their
+      // latency: 16 bytes per lane in the column order of the output stores
+      // below, swapped back into the MFMA layout where they are used
+      u32x4 oq[HAS_O ? NJT : 1];
       if constexpr (HAS_O) {
 #pragma unroll
         for (int jt = 0; jt < NJT; ++jt)
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct)
-            oraw[jt][ct] = bload4_raw<T>(ro, ((unsigned)(t0 + jt * 16 + lr) * DV + wcol0 + ct * 16 + 4 * lg) * ES);
+          oq[jt] = __builtin_amdgcn_raw_buffer_load_b128(
+              ro, ((unsigned)(t0 + jt * 16 + lr) * DV + wcol0 + ((lg & 1) << 4) + ((lg >> 1) << 3)) * ES, 0, 0);
       }
       __syncthreads();  // B
       const float* sA2 = sA2b[pb];
@@ -1550,20 +1551,37 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
         const int j = jt * 16 + lr;
         const float rs_state = rsj[jt] * sig_scale;
         const float inv = invj[jt];
+        unsigned pk[CT][2];  // this lane's 4 outputs of each column tile, as bf16 pairs
+        Raw4<T> oraw[CT];
+        if constexpr (HAS_O) {
+          const auto y0 = __builtin_amdgcn_permlane16_swap(oq[jt][0], oq[jt][2], false, false);
+          const auto y1 = __builtin_amdgcn_permlane16_swap(oq[jt][1], oq[jt][3], false, false);
+          oraw[0].v = u32x2{y0[0], y1[0]};
+          oraw[1].v = u32x2{y0[1], y1[1]};
+        }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           float o[4] = {1.f, 1.f, 1.f, 1.f};
           if constexpr (HAS_O) {
-            raw4_to_f32<T>(oraw[jt][ct], o);
+            raw4_to_f32<T>(oraw[ct], o);
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = sigmoidf_(o[i]);
           }
           float hv[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) hv[i] = o[i] * (o_acc[ct][i] + rs_state * acc[jt][ct][i]) * inv;
-          // rows past T fall outside the output buffer and are dropped
-          bstore4<T>(rh, ((unsigned)(t0 + j) * DV + wcol0 + ct * 16 + 4 * lg) * ES, hv[0], hv[1], hv[2], hv[3]);
+          pk[ct][0] = pack_bf16x2(hv[0], hv[1]);
+          pk[ct][1] = pack_bf16x2(hv[2], hv[3]);
         }
+        // 16-lane group g holds columns 4g..4g+3 of both tiles; swapping the
+        // odd groups' tile 0 with the even groups' tile 1 gives each lane 8
+        // adjacent columns (groups 0..3: 0-7, 16-23, 8-15, 24-31), one
+        // 16-byte store (rows past T fall outside the buffer and are dropped)
+        const auto x0 = __builtin_amdgcn_permlane16_swap(pk[0][0], pk[1][0], false, false);
+        const auto x1 = __builtin_amdgcn_permlane16_swap(pk[0][1], pk[1][1], false, false);
+        const u32x4 hq = {x0[0], x1[0], x0[1], x1[1]};
+        __builtin_amdgcn_raw_buffer_store_b128(
+            hq, rh, ((unsigned)(t0 + j) * DV + wcol0 + ((lg & 1) << 4) + ((lg >> 1) << 3)) * ES, 0, 0);
       }
       // state update: S^ <- S^ + 2^{-sig'} (w . K)^T V (the chunk's decay is
       // folded into sig; rescaled once sig drops below -64)
