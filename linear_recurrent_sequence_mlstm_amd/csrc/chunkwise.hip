@@ -65,6 +65,20 @@ __device__ __forceinline__ constexpr int perm_row_uni(int nt, int i) {
   return sizeof(T) == 2 ? (nt >> 1) * 32 + (nt & 1) * 4 + i : nt * 16 + i * 4;
 }
 
+// Superchunk start states of the 7B head shape (bf16, d_qk = 256, d_v a
+// multiple of 128, one memory block) are kept in the order the pass-3 state
+// waves hold them: for each group of 32 columns (one state wave of one
+// slice), each of its 32 (row tile, column tile) pairs, each lane, the four
+// rows of that lane's accumulator.  Pass 1 then stores a lane's 4 rows as
+// one 16-byte store, and pass 3 reads each lane's 128 values as 32 16-byte
+// loads that cover 1 KB per wave.  Index of the float4 holding rows
+// r0 .. r0 + 3 (r0 a multiple of 4) of column c:
+__device__ __forceinline__ unsigned ws_perm4(int r0, int c) {
+  const int nt = 2 * (r0 >> 5) + ((r0 >> 2) & 1);  // inverse of perm_row<bf16>
+  const int lg = (r0 >> 3) & 3;
+  return (unsigned)((((c >> 5) * 32 + nt * 2 + ((c >> 4) & 1)) * 64 + (c & 15) + 16 * lg) * 4);
+}
+
 // Readout A operand (rows = columns of d_v, k = features kk*K .. +K-1 of the
 // block) taken from the accumulator tiles of the state.
 template <typename T, int NT, int CT>
@@ -1447,7 +1461,18 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st[nt][ct][i] = bload1<float>(rSin, (unsigned)(soff + perm_row_uni<T>(nt, i) * DV + ct * 16) * 4u);
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (DIR) st[nt][ct][i] = bload1<float>(rSin, (unsigned)(soff + perm_row_uni<T>(nt, i) * DV + ct * 16) * 4u);
+      }
+  if constexpr (!DIR) {
+    // a slot of pass 2 in the register order: one 16-byte load per tile
+    const unsigned so4 = (unsigned)(((wcol0 >> 5) * 32 * 64 + lane) * 16);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        st[nt][ct] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rSin, so4 + (unsigned)((nt * 2 + ct) * 64 * 16), 0, 0));
+  }
   float sig = 0.f;  // the registers hold S~ / 2^sig (lazy decay)
   const int vcol = sw * WC + 4 * (lr & 3);  // transposing-read source column of V^T (+ 16 ct)
   const int kcol = 8 * (lr & 3);            // ... of K^T (+ perm part per tile)
@@ -2298,6 +2323,18 @@ __global__ __launch_bounds__(64 * NWP) void local_state_kernel(ChunkParams p) {
 
   // ---- outputs: slot sc + 1 of the workspace holds superchunk sc's local state
   float* dst = p.ws_state + ((size_t)bh * p.NS + sc + 1) * NSTATE;
+  constexpr bool PERM_OK = sizeof(T) == 2 && DQK == 256 && NB == 1 && NBS == 1;
+  if (PERM_OK && p.perm_state) {
+    // the register order of pass 3: a lane's 4 rows are one float4
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NTc; ++nt) {
+        const int r0 = rt * TR + wr * (TR / WR) + mt * 16 + 4 * lg;
+        const int cl = ctl * TC + wcw * (TC / WCW) + nt * 16 + lr;
+        *reinterpret_cast<f32x4*>(dst + ws_perm4(r0, cl)) = acc[mt][nt];
+      }
+  } else
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -2365,7 +2402,14 @@ __global__ __launch_bounds__(256) void superchunk_scan_kernel(ScanParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const size_t e = e0 + i;
-      if (e < p.CS) x[i] = p.C0 ? p.C0[(size_t)bh * p.CS + e] : 0.f;
+      if (p.perm && e < p.CS) {
+        // gather rows r0 + i of column c (inverse of ws_perm4)
+        const int DV = (int)(p.CS / p.DQK);
+        const int lane = (int)((e0 >> 2) & 63), q = (int)((e0 >> 8) & 31), nt = q >> 1;
+        const int c = (int)(e0 >> 13) * 32 + (q & 1) * 16 + (lane & 15);
+        const int r = 32 * (nt >> 1) + 8 * (lane >> 4) + 4 * (nt & 1) + i;
+        x[i] = p.C0 ? p.C0[(size_t)bh * p.CS + (size_t)r * DV + c] : 0.f;
+      } else if (e < p.CS) x[i] = p.C0 ? p.C0[(size_t)bh * p.CS + e] : 0.f;
       else if (p.scalar_n) x[i] = (p.n0 && e == p.CS) ? p.n0[bh] : 0.f;  // n0 [B,H]
       else x[i] = p.n0 ? p.n0[(size_t)bh * p.DQK + (e - p.CS)] : 0.f;
     }
@@ -2421,6 +2465,13 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
   constexpr int NTH = 64 * NCG * NRG;
   const int BH = p.B * p.H;
   const size_t CS = (size_t)DQK * p.DV / NB;
+  // the xLSTM-7B head shape (d_qk 256, one memory block, 128-column slices):
+  // the wave-specialised form of pass 3
+  constexpr bool WSK = std::is_same<T, __bf16>::value && DQK == 256 && NB == 1 && WC * NCG == 128 && L == 64 &&
+                       !RET && !GN && !PB;
+  // the planned 7B-shape pass 3 reads the superchunk slots in its register
+  // order (not a state-passes-only call: the backward reads them in order)
+  p.perm_state = (WSK && p.h && !p.direct) ? 1 : 0;
   if (p.direct) {
     // one superchunk, run as pass 3 alone (it reads C0 / n0 / m0 and forms
     // the gate logs itself)
@@ -2451,10 +2502,6 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
     else
       hipLaunchKernelGGL((local_state_kernel<T, DQK, NBC, TR, 32, L, RET, NWP, NB, SN>), g1, b1, 0, stream, p);
   }
-  // the xLSTM-7B head shape (d_qk 256, one memory block, 128-column slices):
-  // the wave-specialised form of pass 3
-  constexpr bool WSK = std::is_same<T, __bf16>::value && DQK == 256 && NB == 1 && WC * NCG == 128 && L == 64 &&
-                       !RET && !GN && !PB;
   ScanParams s;
   s.NS = p.NS;
   s.CS = CS;
@@ -2467,6 +2514,7 @@ hipError_t launch_chunkwise(ChunkParams p, hipStream_t stream, hipEvent_t ev0, h
   s.n0 = p.n0;
   s.m0 = p.m0;
   s.scalar_n = SN ? 1 : 0;
+  s.perm = p.perm_state;
   const size_t nstate = CS + (RET ? 0 : DQK);
   dim3 g2((unsigned)((nstate / 4 + 255) / 256), (unsigned)BH);
   // fuse_scan: pass 3 composes the start states (a forward call only; the

@@ -32,6 +32,9 @@ struct ChunkParams {
   // pass 1's local states itself (pass 2's arithmetic), so pass 2 is not
   // launched
   int fuse_scan;
+  // superchunk state slots in the register order of the 7B-shape pass 3
+  // (set by the launcher; the slots' d_qk entries of n~ stay in order)
+  int perm_state;
   const float* C0;
   const float* n0;
   const float* m0;
@@ -62,6 +65,7 @@ struct ScanParams {
   const float* n0;
   const float* m0;
   int scalar_n;  // n0 is [B,H] (scalar normaliser)
+  int perm;      // the slots use the 7B-shape pass 3 register order (C0 is gathered into it)
 };
 
 // ev0/ev1 (may be null) are recorded right before / after the main kernel.
