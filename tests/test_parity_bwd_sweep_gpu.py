@@ -6,7 +6,9 @@ oracle's step-by-step backward on the same inputs, with the bars of the other
 backward tests: per (batch, head) slice 1e-4 for fp32 and 2e-2 for bf16, the
 bias gradient against the same bar times the sum of its per-token terms
 (the forward-error bound of a sum whose terms cancel), and dh set to zero at
-tokens within 2 % of the denominator floor, where the gradient jumps.
+tokens within 2 % of the denominator floor, where the gradient jumps.  A
+second sweep does the same for the retention backward (head shape, length,
+per-head or default decays, initial state, final-state gradient).
 """
 import numpy as np
 import pytest
@@ -16,7 +18,7 @@ import oracle
 from linear_recurrent_sequence_mlstm_amd import _lib as mlstm
 from linear_recurrent_sequence_mlstm_amd.workloads import grad_output, mlstm_inputs
 
-from test_parity_bwd_gpu import TOL, check, cpu, near_floor
+from test_parity_bwd_gpu import TOL, check, cpu, near_floor, slice_err
 
 pytestmark = pytest.mark.gpu
 
@@ -76,3 +78,43 @@ def test_random_backward_configuration(gpu, monkeypatch, case):
     print("near-floor tokens %d of %d; dbias %.2e of sum |dz_t|" % (int(mask.sum()), mask.size, e), flush=True)
     assert e < tol, e
     check(dict(out, dbias=None), ref, tol)
+
+
+# retention backward: (dtype, d_k, admissible d_v)
+RSHAPES = [("f32", 64, (64, 128)), ("bf16", 64, (64, 128, 256)), ("bf16", 128, (128, 256))]
+
+
+def _rcases(n=9, seed=2027):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt, dk, dvs = RSHAPES[i % len(RSHAPES)]
+        out.append(dict(dt=dt, dk=dk, dv=int(rng.choice(dvs)), T=int(rng.integers(1, 700)),
+                        B=int(rng.integers(1, 3)), H=int(rng.integers(1, 5)), init=bool(rng.random() < 0.5),
+                        gamma=bool(rng.random() < 0.4), final=bool(rng.random() < 0.4), seed=9000 + 10 * i))
+    return out
+
+
+@pytest.mark.parametrize("case", _rcases(), ids=lambda c: "%s_d%dx%d_T%d_B%dH%d%s%s%s" % (
+    c["dt"], c["dk"], c["dv"], c["T"], c["B"], c["H"], "_state" if c["init"] else "",
+    "_gamma" if c["gamma"] else "", "_final" if c["final"] else ""))
+def test_random_retention_backward_configuration(gpu, case):
+    from linear_recurrent_sequence_mlstm_amd.workloads import retention_inputs
+    c = case
+    B, H, T, dk, dv, s = c["B"], c["H"], c["T"], c["dk"], c["dv"], c["seed"]
+    q, k, v = retention_inputs(B, H, T, dk, dv, seed=s, dtype=c["dt"])
+    do = grad_output((B, H, T, dv), seed=s + 1, dtype=c["dt"])
+    g = torch.Generator().manual_seed(s + 2)
+    gamma = (1 - torch.rand(H, generator=g) * 0.1).float() if c["gamma"] else None
+    S0 = torch.randn(B, H, dk, dv, generator=g) * 0.3 if c["init"] else None
+    dST = torch.randn(B, H, dk, dv, generator=g) if c["final"] else None
+    dev = torch.device(gpu)
+    out = mlstm.retention_chunkwise_bwd(q.to(dev), k.to(dev), v.to(dev), do.to(dev),
+                                        None if gamma is None else gamma.to(dev),
+                                        None if S0 is None else S0.to(dev),
+                                        dS_T=None if dST is None else dST.to(dev))
+    torch.cuda.synchronize()
+    ref = oracle.retention_bwd(q, k, v, do, gamma, S0, dS_T=dST)
+    errs = {nm: slice_err(cpu(out[nm]), ref[nm]) for nm in ("dq", "dk", "dv", "dS0")}
+    print(errs, flush=True)
+    assert all(e < TOL[q.dtype] for e in errs.values()), errs
