@@ -8,7 +8,8 @@ pass 2 folded into pass 3 for a few superchunks of a small state, or the
 three launches), and the outputs and final state are compared with the fp64
 oracle on the same inputs.  A second sweep does the same for retention
 calls (head shape, chunk length, per-head or default decays, initial state,
-in-place final state).  Bars: 1e-4 for fp32, 2e-2 for bf16, per (batch,
+in-place final state), and a third for decode steps (dtype, head shape,
+memory blocks, normaliser reading, random or zero state, output gate, bias).  Bars: 1e-4 for fp32, 2e-2 for bf16, per (batch,
 head) slice as in the other parity tests.
 """
 import numpy as np
@@ -126,3 +127,59 @@ def test_random_retention_configuration(gpu, case):
     tol = TOL[c["dt"]]
     assert _slice_err(o.double().cpu().numpy(), ref_o) < tol
     assert _slice_err(S.double().cpu().numpy(), ref_S) < tol
+
+
+# decode steps: (dtype, d_qk, num_blocks, admissible d_v)
+DSHAPES = [("bf16", 64, 1, (64, 128)), ("f32", 64, 1, (64, 128)), ("bf16", 64, 2, (64, 128)),
+           ("bf16", 128, 1, (128, 256)), ("bf16", 256, 1, (256, 512)), ("f32", 128, 2, (128,))]
+
+
+def _dcases(n=12, seed=2028):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt, dqk, nb, dvs = DSHAPES[i % len(DSHAPES)]
+        mode = str(rng.choice(["vector", "scalar", "block"] if nb > 1 else ["vector", "scalar"]))
+        out.append(dict(dt=dt, dqk=dqk, nb=nb, dv=int(rng.choice(dvs)), mode=mode, B=int(rng.integers(1, 5)),
+                        H=int(rng.integers(1, 4)), init=bool(rng.random() < 0.6), with_o=bool(rng.random() < 0.5),
+                        bias=bool(rng.random() < 0.7), seed=7000 + 10 * i))
+    return out
+
+
+@pytest.mark.parametrize("case", _dcases(), ids=lambda c: "%s_d%dx%d_nb%d_%s_B%dH%d%s%s%s" % (
+    c["dt"], c["dqk"], c["dv"], c["nb"], c["mode"], c["B"], c["H"], "_state" if c["init"] else "",
+    "_o" if c["with_o"] else "", "_bias" if c["bias"] else ""))
+def test_random_decode_configuration(gpu, case):
+    """Six decode steps from a random (or zero) state: every step's outputs
+    and the final state against the oracle's step."""
+    from linear_recurrent_sequence_mlstm_amd.workloads import decode_inputs
+    c = case
+    B, H, dqk, dv, nb, S = c["B"], c["H"], c["dqk"], c["dv"], c["nb"], 6
+    scalar = c["mode"] == "scalar"
+    x = decode_inputs(S, B, H, dqk, dv, seed=c["seed"], dtype=c["dt"], nb=nb, k_scale=dqk ** -0.5,
+                      with_o=c["with_o"], bias="uniform" if c["bias"] else None)
+    rng = np.random.default_rng(c["seed"] + 1)
+    nshape = (B, H) if scalar else (B, H, dqk)
+    if c["init"]:
+        Cr = rng.standard_normal((B, H, nb, dqk // nb, dv // nb)) * 0.3
+        nr = rng.standard_normal(nshape) * 0.3
+        mr = rng.uniform(-2, 2, (B, H))
+    else:
+        Cr, nr, mr = np.zeros((B, H, nb, dqk // nb, dv // nb)), np.zeros(nshape), np.zeros((B, H))
+    C, n, m = (torch.tensor(a, dtype=torch.float32, device=gpu) for a in (Cr, nr, mr))
+    g = x.to(gpu)
+    tol = TOL[c["dt"]]
+    for s in range(S):
+        h = mlstm.step(g.q[s], g.k[s], g.v[s], g.i_pre[s], g.f_pre[s], C, n, m,
+                       o_pre=None if g.o_pre is None else g.o_pre[s], bias=g.bias, num_blocks=nb,
+                       norm_mode=c["mode"])
+        hr = oracle.mlstm_step(x.q[s], x.k[s], x.v[s], x.i_pre[s], x.f_pre[s], Cr, nr, mr,
+                               o_pre=None if x.o_pre is None else x.o_pre[s], bias=x.bias, num_blocks=nb,
+                               norm_mode=c["mode"])
+        torch.cuda.synchronize()
+        assert _slice_err(h.double().cpu().numpy(), hr) < tol, s
+    Cg, ng, mg = (t.double().cpu().numpy() for t in (C, n, m))
+    assert np.max(np.abs(mg - mr)) < 1e-4
+    sc = np.exp(mg - mr)
+    assert _slice_err(Cg * sc[:, :, None, None, None], Cr) < tol
+    assert _slice_err((ng * sc) if scalar else (ng * sc[:, :, None]), nr) < tol
