@@ -1456,15 +1456,15 @@ __global__ __launch_bounds__(512) void chunk_kernel_ws(ChunkParams p) {
   const int wcol0 = slice * W + sw * WC;  // first global d_v column of this state wave
   f32x4 st[NT][CT];
   const int soff = perm_row_lane<T>(lg) * DV + wcol0 + lr;
+  if constexpr (DIR) {
+    // the caller's C0 in its own order
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (DIR) st[nt][ct][i] = bload1<float>(rSin, (unsigned)(soff + perm_row_uni<T>(nt, i) * DV + ct * 16) * 4u);
-      }
-  if constexpr (!DIR) {
+        for (int i = 0; i < 4; ++i) st[nt][ct][i] = bload1<float>(rSin, (unsigned)(soff + perm_row_uni<T>(nt, i) * DV + ct * 16) * 4u);
+  } else {
     // a slot of pass 2 in the register order: one 16-byte load per tile
     const unsigned so4 = (unsigned)(((wcol0 >> 5) * 32 * 64 + lane) * 16);
 #pragma unroll
